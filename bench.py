@@ -1,0 +1,230 @@
+"""Benchmark of the chunkwise mLSTM forward pass on one MI355X.
+
+A step is one full forward pass (inter-chunk states, then the intra-chunk
+parallel stage) over one batch of synthetic inputs that are already resident
+in GPU memory.  Default workload: 7B-shaped heads, bf16 inputs, B=8 NH=8
+S=8192 DHQK=256 DHV=512 chunk=256, exponential input gate, fp32 H.
+
+Prints ONE JSON line: throughput (tokens/s = B*S per step), the roofline
+figures of the dominant kernel measured with HIP events on the launch stream,
+and a CPU baseline: the float64 recurrent oracle timed on a bounded sample of
+the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+METRIC = "mLSTM chunkwise fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 7B-shaped heads"
+
+
+def _oracle_head(args):
+    """One head of the recurrent oracle on a sequence prefix (CPU baseline)."""
+    name, b, h, S = args
+    import numpy as np
+    from oracle import recurrent_fw
+    from workloads import WORKLOADS, head_inputs
+    w = WORKLOADS[name]
+    x = head_inputs(w, b, h)
+    t0 = time.perf_counter()
+    kw = {}
+    if "C0" in x and w.gate == "exp":
+        kw = dict(C0=x["C0"], n0=x["n0"], m0=x["m0"])
+    elif "C0" in x:
+        kw = dict(C0=x["C0"])
+    recurrent_fw(*[x[k][:S].astype(np.float64) for k in ("q", "k", "v", "i", "f")], gate=w.gate, **kw)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(name: str, budget_s: float) -> dict:
+    """Time the float64 recurrent oracle on a bounded sample of the workload.
+
+    Heads are spread over a process pool (one BLAS thread per worker).  The
+    sample is n_heads full-length heads (or a prefix of one head when a
+    single head exceeds the budget); tokens/s counts NH heads per token."""
+    from workloads import WORKLOADS
+    w = WORKLOADS[name]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # probe the per-step cost on a short prefix
+    probe_steps = min(w.S, 256)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        dt = pool.map(_oracle_head, [(name, 0, 0, probe_steps)])[0]
+        per_step = dt / probe_steps
+        head_s = per_step * w.S
+        if head_s * 1.0 <= budget_s * cores:
+            n_heads = int(max(1, min(w.BH, (budget_s * cores) // head_s)))
+            n_heads = max(1, (n_heads // cores) * cores) if n_heads >= cores else n_heads
+            steps = w.S
+        else:
+            n_heads = 1
+            steps = int(max(probe_steps, budget_s / per_step))
+        heads = [(i // w.NH, i % w.NH) for i in range(n_heads)]
+        t0 = time.perf_counter()
+        pool.map(_oracle_head, [(name, b, h, steps) for (b, h) in heads])
+        wall = time.perf_counter() - t0
+    tokens = n_heads * steps / w.NH
+    used = min(cores, n_heads)
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": (f"float64 recurrent oracle, {n_heads} of {w.BH} heads x {steps} of {w.S} steps "
+                       f"({w.name}), {used} worker processes with 1 BLAS thread each; "
+                       f"tokens/s counts {w.NH} heads per token; wall {wall:.1f} s")}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_7b_s8192")
+    ap.add_argument("--precision", default="split", choices=["split", "f16"])
+    ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import xlstm_mlstm_chunkwise_amd as mt
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    mt.lib()  # fail loudly if the HIP library is missing
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    x = make_inputs(w)
+    qd = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+
+    def up(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+
+    q, k, v = up(x["q"], qd), up(x["k"], qd), up(x["v"], qd)
+    i_pre, f_pre = up(x["i"], torch.float32), up(x["f"], torch.float32)
+    sig = w.gate == "sig"
+    C0 = up(x["C0"], torch.float32) if "C0" in x else None
+    n0 = up(x["n0"], torch.float32) if ("n0" in x and not sig) else None
+    m0 = up(x["m0"], torch.float32) if ("m0" in x and not sig) else None
+    del x
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    h_dtype = torch.bfloat16 if args.h_dtype == "bf16" else torch.float32
+    H = torch.empty((w.B, w.NH, w.S, w.DHV), dtype=h_dtype, device=dev)
+    desc = mt.make_desc(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk,
+                        qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
+                        h_dtype=mt.MLSTM_BF16 if args.h_dtype == "bf16" else mt.MLSTM_F32,
+                        gate=w.gate, precision=args.precision, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv)
+    ws = torch.empty(mt.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kw = dict(chunk_size=w.chunk, gate=w.gate, h_dtype=h_dtype, precision=args.precision,
+              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, workspace=ws, out=H)
+
+    def step():
+        return mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations: the same two launches, issued through the stage
+    # entry points with events between them on the launch stream.
+    import ctypes
+    Nc = mt.num_chunks(desc)
+    L = mt.lib()
+    Cst = torch.empty((w.B, w.NH, Nc + 1, w.DHQK, w.DHV), dtype=torch.float32, device=dev)
+    nst = None if sig else torch.empty((w.B, w.NH, Nc + 1, w.DHQK), dtype=torch.float32, device=dev)
+    mst = None if sig else torch.empty((w.B, w.NH, Nc + 1), dtype=torch.float32, device=dev)
+    del ws
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def p(t):
+        return None if t is None else t.data_ptr()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for it in range(args.steps):
+        ev[it][0].record(stream)
+        st = L.mlstm_fw_states(ctypes.byref(desc), p(k), p(v), p(i_pre), p(f_pre), p(C0), p(n0), p(m0),
+                               p(Cst), p(nst), p(mst), None, None, None, sptr)
+        ev[it][1].record(stream)
+        st2 = L.mlstm_fw_hintra(ctypes.byref(desc), p(q), p(k), p(v), p(i_pre), p(f_pre), p(Cst), p(nst),
+                                p(mst), p(H), None, None, sptr)
+        ev[it][2].record(stream)
+        if st or st2:
+            raise mt.MlstmError(st or st2, "stage call")
+    torch.cuda.synchronize()
+    t_states = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_hintra = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    del Cst, nst, mst
+
+    tokens = w.B * w.S
+    flops = mt.flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # algorithmic FLOPs of each stage: states = K^T.V (2 DK DV per token-head);
+    # intra = Q.C + causal Q.K^T and P.V
+    per_th_states = 2.0 * w.DHQK * w.DHV
+    per_th_intra = 2.0 * w.DHQK * w.DHV + (w.chunk + 1) * (w.DHQK + w.DHV)
+    f_states = w.BH * w.S * per_th_states
+    f_intra = w.BH * w.S * per_th_intra
+    dominant = "hintra" if t_hintra >= t_states else "states"
+    t_dom, f_dom = (t_hintra, f_intra) if dominant == "hintra" else (t_states, f_states)
+    ach = f_dom / (t_dom * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16x2-mfma/fp32-acc" if args.precision == "split" else "fp16-mfma/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
+                   "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
+                   "precision": args.precision},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "wall_ms_per_step": wall_ms,
+        "kernels_ms": {"states": t_states, "hintra": t_hintra},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * mlstm_tfla.h - C ABI of the MI355X (gfx950) chunkwise mLSTM forward pass.
+ *
+ * What is computed.  The forward pass of the mLSTM cell (matrix memory C
+ * updated by an outer product, exponential input gate, normaliser n and
+ * max-state stabiliser m; "xLSTM: the NX-AI repository behind the extended
+ * LSTM architecture", section "Exponential gating, matrix memory, and why the
+ * kernels decide everything"), evaluated in the chunkwise-parallel form with a
+ * second level of tiling inside each chunk ("Tiled Flash Linear Attention:
+ * More Efficient Linear RNN and xLSTM Kernels", abstract).  Per head, with
+ * s = qk_scale, lf_t = log sigmoid(f_t):
+ *
+ *   exp gate:  m_t = max(lf_t + m_{t-1}, i_t)
+ *              C_t = e^{lf_t + m_{t-1} - m_t} C_{t-1} + e^{i_t - m_t} k_t v_t^T
+ *              n_t = e^{lf_t + m_{t-1} - m_t} n_{t-1} + e^{i_t - m_t} k_t
+ *              h_t = s C_t^T q_t / (max(|s n_t . q_t|, e^{-m_t}) + eps)
+ *   sig gate:  C_t = sigmoid(f_t) C_{t-1} + sigmoid(i_t) k_t v_t^T
+ *              h_t = s C_t^T q_t                      (no n, no m)
+ *
+ * The two-stage split (an inter-chunk recurrence that materialises the state
+ * entering every chunk, then an intra-chunk parallel stage that reads those
+ * states) follows the parallel-stage interface listed on the
+ * "flash-xlstm-exp 0.1.0" page (section "Usage": Q, K, V, input and forget
+ * gates, per-chunk C/n/m states and chunk_size in; H plus per-row n and m
+ * out).  mlstm_chunkwise_fw runs both stages.
+ *
+ * Conventions for every entry point.
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) on
+ *     the current HIP device; sizes are element counts implied by the
+ *     descriptor.  Tensors are contiguous, row-major:
+ *        Q, K      (B, NH, S, DHQK)   qkv_dtype
+ *        V         (B, NH, S, DHV)    qkv_dtype
+ *        i_pre     (B, NH, S)         float32   input-gate pre-activation
+ *        f_pre     (B, NH, S)         float32   forget-gate pre-activation
+ *        C0, C_out (B, NH, DHQK, DHV) float32   (rows follow k, columns v)
+ *        n0, n_out (B, NH, DHQK)      float32   exp gate only
+ *        m0, m_out (B, NH)            float32   exp gate only
+ *        H         (B, NH, S, DHV)    h_dtype
+ *     Q, K, V and H must be 16-byte aligned; everything else 4-byte aligned.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates no device memory and keeps no mutable global state.  Inputs
+ *     are never written.  Outputs must not alias inputs.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Results are ready when the stream has finished.
+ *   - Every call validates all arguments on the host before it launches
+ *     anything and returns a status code; nothing is launched when the status
+ *     is not MLSTM_OK.  A failed launch returns MLSTM_E_HIP.
+ *   - Readings where the method leaves a step open: the scale s multiplies
+ *     the query at readout (states are built from raw k, v); the forget gate
+ *     applies at every step including the first; m starts at m0 (0 if m0 is
+ *     NULL); eps is added after the max.
+ */
+#ifndef MLSTM_TFLA_H
+#define MLSTM_TFLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLSTM_ABI_VERSION 1
+
+typedef enum {
+  MLSTM_OK = 0,
+  MLSTM_E_NULLPTR = 1,     /* a required pointer is NULL                       */
+  MLSTM_E_SHAPE = 2,       /* B, NH, S, DHQK or DHV out of the supported set   */
+  MLSTM_E_CHUNK = 3,       /* chunk_size or tile sizes unsupported             */
+  MLSTM_E_DTYPE = 4,       /* unknown dtype code                               */
+  MLSTM_E_UNSUPPORTED = 5, /* a combination the library does not implement    */
+  MLSTM_E_WORKSPACE = 6,   /* workspace missing or smaller than required       */
+  MLSTM_E_HIP = 7,         /* a HIP launch or runtime call failed              */
+  MLSTM_E_ALIGN = 8,       /* a pointer violates its alignment requirement     */
+  MLSTM_E_ARG = 9          /* other invalid argument (gate, precision, eps...) */
+} mlstm_status_t;
+
+typedef enum { MLSTM_F32 = 0, MLSTM_BF16 = 1 } mlstm_dtype_t;
+typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
+
+/* Operand precision of the three contractions whose left operand is
+ * computed on the fly (P = scores x decay in P.V, the carried state C in
+ * Q.C, and the gated keys in K^T.V).  Inputs Q, K, V are converted to fp16
+ * for the matrix cores (exact for bf16 values of magnitude in
+ * [2^-14, 65504]; smaller ones keep an absolute error below 2^-25).
+ *   MLSTM_PREC_SPLIT: the computed operand is carried as an fp16 hi + lo
+ *                     pair (about 21 significant bits, two MFMA passes).
+ *   MLSTM_PREC_F16:   one fp16 rounding of the computed operand (one pass).
+ * Ignored for float32 inputs, which use fp32 matrix-core instructions. */
+typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1 } mlstm_prec_t;
+
+typedef struct {
+  int32_t B, NH;       /* batch, heads: >= 1                                   */
+  int32_t S;           /* sequence length: >= 0, need not divide chunk_size   */
+  int32_t DHQK, DHV;   /* head dims: multiples of 64, at most 512 (float32
+                          inputs: DHQK at most 256)                           */
+  int32_t chunk_size;  /* L: power of two, 64..1024                           */
+  int32_t qkv_dtype;   /* mlstm_dtype_t of Q, K, V                             */
+  int32_t h_dtype;     /* mlstm_dtype_t of H                                   */
+  int32_t gate;        /* mlstm_gate_t                                         */
+  int32_t precision;   /* mlstm_prec_t                                         */
+  float qk_scale;      /* s; <= 0 selects 1/sqrt(DHQK)                         */
+  float eps;           /* >= 0, added to the normaliser after the max          */
+  int32_t tile_lq;     /* rows of the intra-chunk output tile; 0 = library    */
+  int32_t tile_lkv;    /* key rows per intra-chunk step; 0 = library          */
+  int32_t reserved[4]; /* must be zero                                        */
+} mlstm_fw_desc_t;
+
+/* ABI version of the loaded library (MLSTM_ABI_VERSION). */
+int mlstm_abi_version(void);
+
+/* Static text for a status code ("ok", "null pointer", ...). */
+const char* mlstm_status_str(int status);
+
+/* Host-only check of a descriptor (no pointers, no device calls).  Returns
+ * MLSTM_OK or the first error found. */
+int mlstm_fw_validate(const mlstm_fw_desc_t* desc);
+
+/* Number of chunks N_c = ceil(S / chunk_size) for a valid descriptor, else
+ * -1. */
+int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
+
+/* Bytes of device workspace that mlstm_chunkwise_fw needs for `desc`: the
+ * per-chunk states (B, NH, N_c + 1, DHQK, DHV), (B, NH, N_c + 1, DHQK) and
+ * (B, NH, N_c + 1) in float32, each region 256-byte aligned.  Returns 0 for an
+ * invalid descriptor. */
+size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
+
+/* Full forward pass: states then H (both stages of the chunkwise form).
+ *   C0, n0, m0   may be NULL: zero initial state (m0 = 0).  For the sig gate
+ *                n0 and m0 must be NULL.
+ *   C_out, n_out, m_out  may be NULL: that final state is not written.  For
+ *                the sig gate n_out and m_out must be NULL.  The final state
+ *                follows the stabiliser convention above: the true memory is
+ *                C_out * e^{m_out}.
+ *   workspace    device buffer of at least mlstm_fw_workspace_bytes(desc)
+ *                bytes, 256-byte aligned; it may be NULL only when that size
+ *                is 0.  Its contents on return are the chunk states, laid out
+ *                as described for mlstm_fw_states.
+ * With S == 0 the call only copies the initial state to the outputs. */
+int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
+                       const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre,
+                       const float* C0, const float* n0, const float* m0,
+                       void* H,
+                       float* C_out, float* n_out, float* m_out,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Stage one, the inter-chunk recurrence: for every head, the stabilised state
+ * entering each chunk c = 0..N_c-1 and the final state (index N_c):
+ *   C_states (B, NH, N_c + 1, DHQK, DHV) float32
+ *   n_states (B, NH, N_c + 1, DHQK)      float32  (exp gate; NULL for sig)
+ *   m_states (B, NH, N_c + 1)            float32  (exp gate; NULL for sig)
+ * Entry 0 holds the initial state.  C_out/n_out/m_out as for
+ * mlstm_chunkwise_fw.  Q is not read. */
+int mlstm_fw_states(const mlstm_fw_desc_t* desc,
+                    const void* K, const void* V,
+                    const float* i_pre, const float* f_pre,
+                    const float* C0, const float* n0, const float* m0,
+                    float* C_states, float* n_states, float* m_states,
+                    float* C_out, float* n_out, float* m_out,
+                    void* stream);
+
+/* Stage two, the intra-chunk parallel pass: H from Q, K, V, the gates and the
+ * states written by mlstm_fw_states (only entries 0..N_c-1 are read).
+ * Optional per-row outputs (NULL = not written; exp gate only):
+ *   m_rows   (B, NH, S) float32: the max-state m_t
+ *   den_rows (B, NH, S) float32: the stabilised normaliser s n_t . q_t before
+ *            the max with e^{-m_t} */
+int mlstm_fw_hintra(const mlstm_fw_desc_t* desc,
+                    const void* Q, const void* K, const void* V,
+                    const float* i_pre, const float* f_pre,
+                    const float* C_states, const float* n_states,
+                    const float* m_states,
+                    void* H, float* m_rows, float* den_rows,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_TFLA_H */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before any device work.
+
+No test here launches a kernel: every call is one that validation refuses,
+so these run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import xlstm_mlstm_chunkwise_amd as mt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlstm_tfla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlstm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "mlstm_chunkwise_fw" in names and "mlstm_fw_states" in names and "mlstm_fw_hintra" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", mt.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = mt.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_abi_version_and_status_strings():
+    assert mt.abi_version() == 1
+    assert mt.status_str(0) == "ok"
+    for code in range(1, 10):
+        assert mt.status_str(code) not in ("ok", "unknown status")
+    assert mt.status_str(999) == "unknown status"
+
+
+def test_desc_layout_matches_header():
+    # 14 int/float fields plus reserved[4], all 4 bytes
+    assert ctypes.sizeof(mt.FwDesc) == 18 * 4
+
+
+def _desc(**kw):
+    base = dict(B=2, NH=3, S=1000, DHQK=128, DHV=64, chunk_size=128)
+    base.update({k: kw.pop(k) for k in list(kw) if k in base})
+    return mt.make_desc(base["B"], base["NH"], base["S"], base["DHQK"], base["DHV"],
+                        base["chunk_size"], **kw)
+
+
+def test_valid_descriptor_and_workspace_size():
+    d = _desc()
+    assert mt.validate(d) == 0
+    Nc = (1000 + 127) // 128
+    assert mt.num_chunks(d) == Nc
+    def r256(x):
+        return (x + 255) // 256 * 256
+    BH = 6
+    expect = r256(BH * (Nc + 1) * 128 * 64 * 4) + r256(BH * (Nc + 1) * 128 * 4) + r256(BH * (Nc + 1) * 4)
+    assert mt.workspace_bytes(d) == expect
+    ds = _desc(gate="sig")
+    assert mt.workspace_bytes(ds) == r256(BH * (Nc + 1) * 128 * 64 * 4)
+    assert mt.validate(_desc(S=0)) == 0
+    assert mt.num_chunks(_desc(S=0)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 2), (dict(NH=-1), 2), (dict(S=-5), 2),
+    (dict(DHQK=96), 2), (dict(DHQK=1024), 2), (dict(DHV=32), 2), (dict(DHV=576), 2),
+    (dict(chunk_size=96), 3), (dict(chunk_size=32), 3), (dict(chunk_size=2048), 3),
+    (dict(tile_lq=48), 3), (dict(tile_lkv=256), 3),
+    (dict(qkv_dtype=7), 4), (dict(h_dtype=-1), 4),
+    (dict(gate=2), 9), (dict(precision=5), 9), (dict(eps=-1.0), 9), (dict(eps=float("nan")), 9),
+    (dict(qk_scale=float("inf")), 9),
+    (dict(qkv_dtype=mt.MLSTM_F32, DHQK=512), 5),
+])
+def test_validation_errors(kw, code):
+    d = _desc(**kw)
+    assert mt.validate(d) == code
+    assert mt.workspace_bytes(d) == 0
+    assert mt.num_chunks(d) == -1
+
+
+def test_reserved_fields_must_be_zero():
+    d = _desc()
+    d.reserved[2] = 1
+    assert mt.validate(d) == 9
+
+
+def _fw(desc, **ptrs):
+    names = ["Q", "K", "V", "i", "f", "C0", "n0", "m0", "H", "C_out", "n_out", "m_out"]
+    vals = [ptrs.get(n, 4096) for n in names]
+    ws = ptrs.get("ws", 1 << 20)
+    ws_bytes = ptrs.get("ws_bytes", mt.workspace_bytes(desc) if desc is not None else 0)
+    return mt.lib().mlstm_chunkwise_fw(ctypes.byref(desc) if desc is not None else None, *vals, ws, ws_bytes, None)
+
+
+def test_entry_points_refuse_before_launch():
+    lib = mt.lib()
+    d = _desc()
+    assert _fw(None) == 1
+    assert _fw(d, Q=None) == 1
+    assert _fw(d, H=None) == 1
+    assert _fw(d, K=4096 + 8) == 8           # Q/K/V/H need 16-byte alignment
+    assert _fw(d, i=4096 + 2) == 8
+    assert _fw(d, ws=None) == 6
+    assert _fw(d, ws_bytes=mt.workspace_bytes(d) - 1) == 6
+    assert _fw(d, ws=(1 << 20) + 64) == 6    # workspace needs 256-byte alignment
+    ds = _desc(gate="sig")
+    assert _fw(ds, C0=None, n0=4096, m0=None, n_out=None, m_out=None) == 5
+    assert _fw(ds, C0=None, n0=None, m0=None, n_out=None, m_out=4096) == 5
+    bad = _desc(DHQK=100)
+    assert _fw(bad) == 2
+    # stage calls
+    args = [4096] * 13
+    assert lib.mlstm_fw_states(ctypes.byref(d), *args[:7], None, *args[8:], None) == 1   # C_states NULL
+    assert lib.mlstm_fw_states(ctypes.byref(ds), *args[:8], 4096, None, None, None, None, None) == 5
+    assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), None, 4096, 4096, 4096, None, None, None) == 1
+    assert lib.mlstm_fw_hintra(ctypes.byref(ds), *([4096] * 6), None, None, 4096, 4096, None, None) == 5
+
+
+def test_flops_formula():
+    # 7B-shaped heads, S=8192, chunk 256: 378.4 GFLOP
+    f = mt.flops(8, 8, 8192, 256, 512, 256)
+    assert abs(f / 1e9 - 378.4) < 0.1

@@ -1,0 +1,293 @@
+"""MI355X (gfx950) chunkwise mLSTM forward pass: Python binding of libmlstm_tfla.so.
+
+The binding only marshals arguments: it allocates outputs and workspace with
+PyTorch (device memory), passes raw device pointers and the current HIP
+stream to the C ABI declared in include/mlstm_tfla.h, and turns a non-zero
+status into an exception.  Every step of the computation runs in the HIP
+kernels; there is no other code path.  If the shared library is missing the
+import of the functions below fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmlstm_tfla.so")
+
+MLSTM_F32, MLSTM_BF16 = 0, 1
+MLSTM_GATE_EXP, MLSTM_GATE_SIG = 0, 1
+MLSTM_PREC_SPLIT, MLSTM_PREC_F16 = 0, 1
+_PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16}
+_GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
+
+STATUS_NAMES = {
+    0: "MLSTM_OK", 1: "MLSTM_E_NULLPTR", 2: "MLSTM_E_SHAPE", 3: "MLSTM_E_CHUNK",
+    4: "MLSTM_E_DTYPE", 5: "MLSTM_E_UNSUPPORTED", 6: "MLSTM_E_WORKSPACE",
+    7: "MLSTM_E_HIP", 8: "MLSTM_E_ALIGN", 9: "MLSTM_E_ARG",
+}
+
+
+class MlstmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+class FwDesc(ctypes.Structure):
+    """Mirror of mlstm_fw_desc_t."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("NH", ctypes.c_int32), ("S", ctypes.c_int32),
+        ("DHQK", ctypes.c_int32), ("DHV", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32), ("h_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
+        ("precision", ctypes.c_int32), ("qk_scale", ctypes.c_float), ("eps", ctypes.c_float),
+        ("tile_lq", ctypes.c_int32), ("tile_lkv", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
+    ]
+
+
+_lib = None
+_SYMBOLS = {
+    "mlstm_abi_version": (ctypes.c_int, []),
+    "mlstm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "mlstm_fw_validate": (ctypes.c_int, [ctypes.POINTER(FwDesc)]),
+    "mlstm_fw_num_chunks": (ctypes.c_int64, [ctypes.POINTER(FwDesc)]),
+    "mlstm_fw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
+    "mlstm_chunkwise_fw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12
+                           + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
+    "mlstm_fw_hintra": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmlstm_tfla.so (built in-tree by xlstm_mlstm_chunkwise_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with `python -m xlstm_mlstm_chunkwise_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (restype, argtypes) in _SYMBOLS.items():
+            fn = getattr(handle, name)
+            fn.restype = restype
+            fn.argtypes = argtypes
+        _lib = handle
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().mlstm_abi_version()
+
+
+def status_str(status: int) -> str:
+    return lib().mlstm_status_str(status).decode()
+
+
+def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=MLSTM_F32,
+              gate="exp", precision="split", qk_scale=0.0, eps=0.0, tile_lq=0, tile_lkv=0) -> FwDesc:
+    d = FwDesc()
+    d.B, d.NH, d.S, d.DHQK, d.DHV, d.chunk_size = B, NH, S, DHQK, DHV, chunk_size
+    d.qkv_dtype, d.h_dtype = qkv_dtype, h_dtype
+    d.gate = _GATE[gate] if isinstance(gate, str) else gate
+    d.precision = _PREC[precision] if isinstance(precision, str) else precision
+    d.qk_scale, d.eps = qk_scale, eps
+    d.tile_lq, d.tile_lkv = tile_lq, tile_lkv
+    return d
+
+
+def validate(desc: FwDesc) -> int:
+    return lib().mlstm_fw_validate(ctypes.byref(desc))
+
+
+def workspace_bytes(desc: FwDesc) -> int:
+    return lib().mlstm_fw_workspace_bytes(ctypes.byref(desc))
+
+
+def num_chunks(desc: FwDesc) -> int:
+    return lib().mlstm_fw_num_chunks(ctypes.byref(desc))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (device memory and streams only)
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MLSTM_BF16
+    if t.dtype == torch.float32:
+        return MLSTM_F32
+    raise TypeError(f"Q/K/V must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype=None):
+    if t is None:
+        return
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv):
+    torch = _torch()
+    B, NH, S, DK = q.shape
+    DV = v.shape[-1]
+    hcode = MLSTM_BF16 if h_dtype == torch.bfloat16 else MLSTM_F32
+    return make_desc(B, NH, S, DK, DV, chunk_size, qkv_dtype=_dtype_code(q), h_dtype=hcode,
+                     gate=gate, precision=precision,
+                     qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps),
+                     tile_lq=tile_lq, tile_lkv=tile_lkv)
+
+
+def _check_inputs(q, k, v, i_pre, f_pre):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("Q must be (B, NH, S, DHQK)")
+    B, NH, S, DK = q.shape
+    DV = v.shape[-1]
+    _check(q, "Q", (B, NH, S, DK))
+    _check(k, "K", (B, NH, S, DK), q.dtype)
+    _check(v, "V", (B, NH, S, DV), q.dtype)
+    _check(i_pre, "i_pre", (B, NH, S), torch.float32)
+    _check(f_pre, "f_pre", (B, NH, S), torch.float32)
+    return B, NH, S, DK, DV
+
+
+def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
+                       gate: str = "exp", h_dtype=None, precision: str = "split",
+                       qk_scale: Optional[float] = None, eps: float = 0.0,
+                       tile_lq: int = 0, tile_lkv: int = 0, workspace=None,
+                       return_final_state: bool = True, out=None):
+    """Chunkwise mLSTM forward pass on the GPU.
+
+    q, k: (B, NH, S, DHQK); v: (B, NH, S, DHV), bfloat16 or float32;
+    i_pre, f_pre: (B, NH, S) float32; C0 (B, NH, DHQK, DHV), n0 (B, NH, DHQK),
+    m0 (B, NH) float32 or None (zero state).  Returns (H, C, n, m); n and m
+    are None for gate="sig", and the final state is None when
+    return_final_state is False.  H is float32 unless h_dtype says otherwise.
+    """
+    torch = _torch()
+    B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
+    h_dtype = torch.float32 if h_dtype is None else h_dtype
+    _check(C0, "C0", (B, NH, DK, DV), torch.float32)
+    _check(n0, "n0", (B, NH, DK), torch.float32)
+    _check(m0, "m0", (B, NH), torch.float32)
+    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv)
+    st = validate(desc)
+    if st:
+        raise MlstmError(st, "mlstm_chunkwise_fw")
+    dev = q.device
+    H = out if out is not None else torch.empty((B, NH, S, DV), dtype=h_dtype, device=dev)
+    _check(H, "H", (B, NH, S, DV), h_dtype)
+    sig = gate == "sig"
+    C_out = n_out = m_out = None
+    if return_final_state:
+        C_out = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=dev)
+        if not sig:
+            n_out = torch.empty((B, NH, DK), dtype=torch.float32, device=dev)
+            m_out = torch.empty((B, NH), dtype=torch.float32, device=dev)
+    need = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {need}")
+    st = lib().mlstm_chunkwise_fw(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre),
+        _ptr(C0), _ptr(n0), _ptr(m0), _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_chunkwise_fw")
+    return H, C_out, n_out, m_out
+
+
+def mlstm_fw_states(k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
+                    gate: str = "exp", precision: str = "split", return_final_state: bool = True):
+    """Stage one alone: returns (C_states, n_states, m_states, C, n, m) with the
+    state entering every chunk plus the final state at index N_c."""
+    torch = _torch()
+    B, NH, S, DK, DV = _check_inputs(k, k, v, i_pre, f_pre)
+    desc = _desc_for(k, v, chunk_size, gate, torch.float32, precision, None, 0.0, 0, 0)
+    st = validate(desc)
+    if st:
+        raise MlstmError(st, "mlstm_fw_states")
+    _check(C0, "C0", (B, NH, DK, DV), torch.float32)
+    _check(n0, "n0", (B, NH, DK), torch.float32)
+    _check(m0, "m0", (B, NH), torch.float32)
+    Nc = num_chunks(desc)
+    dev = k.device
+    sig = gate == "sig"
+    Cst = torch.empty((B, NH, Nc + 1, DK, DV), dtype=torch.float32, device=dev)
+    nst = None if sig else torch.empty((B, NH, Nc + 1, DK), dtype=torch.float32, device=dev)
+    mst = None if sig else torch.empty((B, NH, Nc + 1), dtype=torch.float32, device=dev)
+    C_out = n_out = m_out = None
+    if return_final_state:
+        C_out = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=dev)
+        if not sig:
+            n_out = torch.empty((B, NH, DK), dtype=torch.float32, device=dev)
+            m_out = torch.empty((B, NH), dtype=torch.float32, device=dev)
+    st = lib().mlstm_fw_states(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
+        _ptr(Cst), _ptr(nst), _ptr(mst), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_fw_states")
+    return Cst, nst, mst, C_out, n_out, m_out
+
+
+def mlstm_fw_hintra(q, k, v, i_pre, f_pre, C_states, n_states=None, m_states=None, *,
+                    chunk_size: int, gate: str = "exp", h_dtype=None, precision: str = "split",
+                    qk_scale: Optional[float] = None, eps: float = 0.0,
+                    tile_lq: int = 0, tile_lkv: int = 0, return_rows: bool = False):
+    """Stage two alone: H (and, with return_rows, per-row m and stabilised
+    normaliser) from the chunk states of mlstm_fw_states."""
+    torch = _torch()
+    B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
+    h_dtype = torch.float32 if h_dtype is None else h_dtype
+    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv)
+    st = validate(desc)
+    if st:
+        raise MlstmError(st, "mlstm_fw_hintra")
+    Nc = num_chunks(desc)
+    _check(C_states, "C_states", (B, NH, Nc + 1, DK, DV), torch.float32)
+    _check(n_states, "n_states", (B, NH, Nc + 1, DK), torch.float32)
+    _check(m_states, "m_states", (B, NH, Nc + 1), torch.float32)
+    dev = q.device
+    H = torch.empty((B, NH, S, DV), dtype=h_dtype, device=dev)
+    m_rows = den_rows = None
+    if return_rows and gate == "exp":
+        m_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
+        den_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
+    st = lib().mlstm_fw_hintra(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C_states),
+        _ptr(n_states), _ptr(m_states), _ptr(H), _ptr(m_rows), _ptr(den_rows), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_fw_hintra")
+    if return_rows:
+        return H, m_rows, den_rows
+    return H
+
+
+def flops(B, NH, S, DHQK, DHV, chunk_size) -> float:
+    """Algorithmic matrix-core FLOPs of one forward pass, causal lower triangle
+    only: per token 4*DHQK*DHV (Q.C and K^T.V) + (L+1)*(DHQK+DHV) (Q.K^T and P.V)."""
+    return float(B) * NH * S * (4.0 * DHQK * DHV + (chunk_size + 1) * (DHQK + DHV))

@@ -1,0 +1,241 @@
+// C ABI of the chunkwise mLSTM forward pass: argument validation, workspace
+// layout and launch of the two stages.  See include/mlstm_tfla.h for the
+// contract of every entry point.
+#include <math.h>
+#include <initializer_list>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "mlstm_tfla.h"
+
+namespace {
+
+using mlstm::HintraParams;
+using mlstm::StatesParams;
+
+constexpr int kMaxChunk = 1024;
+constexpr int kMinChunk = 64;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int validate_desc(const mlstm_fw_desc_t* d) {
+  if (!d) return MLSTM_E_NULLPTR;
+  for (int i = 0; i < 4; ++i)
+    if (d->reserved[i] != 0) return MLSTM_E_ARG;
+  if (d->qkv_dtype != MLSTM_F32 && d->qkv_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
+  if (d->h_dtype != MLSTM_F32 && d->h_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
+  if (d->gate != MLSTM_GATE_EXP && d->gate != MLSTM_GATE_SIG) return MLSTM_E_ARG;
+  if (d->precision != MLSTM_PREC_SPLIT && d->precision != MLSTM_PREC_F16) return MLSTM_E_ARG;
+  if (!isfinite(d->qk_scale) || !isfinite(d->eps) || d->eps < 0.0f) return MLSTM_E_ARG;
+  if (d->B < 1 || d->NH < 1 || d->S < 0) return MLSTM_E_SHAPE;
+  const bool dk_ok = d->DHQK == 64 || d->DHQK == 128 || d->DHQK == 256 || d->DHQK == 512;
+  if (!dk_ok) return MLSTM_E_SHAPE;
+  if (d->DHV < 64 || d->DHV > 512 || d->DHV % 64 != 0) return MLSTM_E_SHAPE;
+  if (d->qkv_dtype == MLSTM_F32 && d->DHQK > 256) return MLSTM_E_UNSUPPORTED;
+  if (!is_pow2(d->chunk_size) || d->chunk_size < kMinChunk || d->chunk_size > kMaxChunk) return MLSTM_E_CHUNK;
+  if (d->tile_lq != 0 && d->tile_lq != 64 && d->tile_lq != 128) return MLSTM_E_CHUNK;
+  if (d->tile_lkv != 0 && d->tile_lkv != 64 && d->tile_lkv != 128) return MLSTM_E_CHUNK;
+  if (d->tile_lq > d->chunk_size || d->tile_lkv > d->chunk_size) return MLSTM_E_CHUNK;
+  // 128-key tiles hold 128 full key rows in LDS: DHQK <= 256 (<= 128 for float32).
+  if (d->tile_lkv == 128 && d->DHQK > (d->qkv_dtype == MLSTM_F32 ? 128 : 256)) return MLSTM_E_UNSUPPORTED;
+  // Grid and index limits.
+  const int64_t BH = (int64_t)d->B * d->NH;
+  const int64_t Nc = ((int64_t)d->S + d->chunk_size - 1) / d->chunk_size;
+  if (BH > (1 << 30)) return MLSTM_E_SHAPE;
+  if (BH * Nc * (d->chunk_size / 64) > 0x7fffffffLL) return MLSTM_E_SHAPE;  // grid.x bound
+  if ((int64_t)d->S * (int64_t)d->DHV > (1LL << 40)) return MLSTM_E_SHAPE;
+  return MLSTM_OK;
+}
+
+struct WsLayout {
+  size_t c_off, n_off, m_off, total;
+};
+
+WsLayout ws_layout(const mlstm_fw_desc_t* d) {
+  const size_t BH = (size_t)d->B * d->NH;
+  const size_t Nc1 = (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
+  WsLayout w;
+  w.c_off = 0;
+  size_t off = round_up(BH * Nc1 * d->DHQK * d->DHV * sizeof(float), 256);
+  w.n_off = off;
+  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * sizeof(float), 256);
+  w.m_off = off;
+  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * sizeof(float), 256);
+  w.total = off;
+  return w;
+}
+
+int check_sig_nulls(const mlstm_fw_desc_t* d, const void* a, const void* b, const void* c, const void* e) {
+  if (d->gate == MLSTM_GATE_SIG && (a || b || c || e)) return MLSTM_E_UNSUPPORTED;
+  return MLSTM_OK;
+}
+
+int check_f32_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return MLSTM_E_ALIGN;
+  return MLSTM_OK;
+}
+
+float resolve_scale(const mlstm_fw_desc_t* d) {
+  return d->qk_scale > 0.0f ? d->qk_scale : 1.0f / sqrtf((float)d->DHQK);
+}
+
+int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const float* i_pre, const float* f_pre,
+               const float* C0, const float* n0, const float* m0, float* Cst, float* nst, float* mst,
+               float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+  StatesParams p;
+  p.K = K;
+  p.V = V;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.m0 = m0;
+  p.C_states = Cst;
+  p.n_states = nst;
+  p.m_states = mst;
+  p.C_out = C_out;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  p.BH = d->B * d->NH;
+  p.S = d->S;
+  p.DK = d->DHQK;
+  p.DV = d->DHV;
+  p.L = d->chunk_size;
+  p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  const bool bf16 = d->qkv_dtype == MLSTM_BF16;
+  const hipError_t e = mlstm::launch_states(p, bf16, d->gate == MLSTM_GATE_SIG,
+                                            bf16 && d->precision == MLSTM_PREC_SPLIT, stream);
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
+               const float* f_pre, const float* Cst, const float* nst, const float* mst, void* H,
+               float* m_rows, float* den_rows, hipStream_t stream) {
+  if (d->S == 0) return MLSTM_OK;
+  HintraParams p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.C_states = Cst;
+  p.n_states = nst;
+  p.m_states = mst;
+  p.H = H;
+  p.m_rows = m_rows;
+  p.den_rows = den_rows;
+  p.scale = resolve_scale(d);
+  p.eps = d->eps;
+  p.BH = d->B * d->NH;
+  p.S = d->S;
+  p.DK = d->DHQK;
+  p.DV = d->DHV;
+  p.L = d->chunk_size;
+  p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  p.h_bf16 = d->h_dtype == MLSTM_BF16;
+  p.tile_lq = d->tile_lq ? d->tile_lq : 64;
+  p.tile_lkv = d->tile_lkv ? d->tile_lkv : 64;
+  const bool bf16 = d->qkv_dtype == MLSTM_BF16;
+  const hipError_t e = mlstm::launch_hintra(p, bf16, d->gate == MLSTM_GATE_SIG,
+                                            bf16 && d->precision == MLSTM_PREC_SPLIT, stream);
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_abi_version(void) { return MLSTM_ABI_VERSION; }
+
+const char* mlstm_status_str(int status) {
+  switch (status) {
+    case MLSTM_OK: return "ok";
+    case MLSTM_E_NULLPTR: return "null pointer";
+    case MLSTM_E_SHAPE: return "unsupported shape";
+    case MLSTM_E_CHUNK: return "unsupported chunk or tile size";
+    case MLSTM_E_DTYPE: return "unknown dtype";
+    case MLSTM_E_UNSUPPORTED: return "unsupported combination";
+    case MLSTM_E_WORKSPACE: return "workspace missing or too small";
+    case MLSTM_E_HIP: return "HIP launch failed";
+    case MLSTM_E_ALIGN: return "misaligned pointer";
+    case MLSTM_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int mlstm_fw_validate(const mlstm_fw_desc_t* desc) { return validate_desc(desc); }
+
+int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc) {
+  if (validate_desc(desc) != MLSTM_OK) return -1;
+  return ((int64_t)desc->S + desc->chunk_size - 1) / desc->chunk_size;
+}
+
+size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc) {
+  if (validate_desc(desc) != MLSTM_OK) return 0;
+  return ws_layout(desc).total;
+}
+
+int mlstm_fw_states(const mlstm_fw_desc_t* desc, const void* K, const void* V, const float* i_pre,
+                    const float* f_pre, const float* C0, const float* n0, const float* m0, float* C_states,
+                    float* n_states, float* m_states, float* C_out, float* n_out, float* m_out,
+                    void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
+  if (!C_states) return MLSTM_E_NULLPTR;
+  if (desc->gate == MLSTM_GATE_EXP && (!n_states || !m_states)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
+  if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
+  if ((K && !aligned(K, 16)) || (V && !aligned(V, 16)) || !aligned(C_states, 16)) return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, n_states, m_states, C_out, n_out, m_out})) != MLSTM_OK)
+    return st;
+  return run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, C_states, n_states, m_states, C_out, n_out, m_out,
+                    static_cast<hipStream_t>(stream));
+}
+
+int mlstm_fw_hintra(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                    const float* f_pre, const float* C_states, const float* n_states, const float* m_states,
+                    void* H, float* m_rows, float* den_rows, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H || !C_states)) return MLSTM_E_NULLPTR;
+  if (desc->S > 0 && desc->gate == MLSTM_GATE_EXP && (!n_states || !m_states)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n_states, m_states, m_rows, den_rows)) != MLSTM_OK) return st;
+  if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)) ||
+      (C_states && !aligned(C_states, 16)))
+    return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, n_states, m_states, m_rows, den_rows})) != MLSTM_OK) return st;
+  return run_hintra(desc, Q, K, V, i_pre, f_pre, C_states, n_states, m_states, H, m_rows, den_rows,
+                    static_cast<hipStream_t>(stream));
+}
+
+int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       void* H, float* C_out, float* n_out, float* m_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
+  if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
+    return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, C_out, n_out, m_out})) != MLSTM_OK) return st;
+  const WsLayout w = ws_layout(desc);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MLSTM_E_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* Cst = reinterpret_cast<float*>(ws + w.c_off);
+  float* nst = desc->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
+  float* mst = desc->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, Cst, nst, mst, C_out, n_out, m_out, s);
+  if (st != MLSTM_OK) return st;
+  return run_hintra(desc, Q, K, V, i_pre, f_pre, Cst, nst, mst, H, nullptr, nullptr, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Launch interface between the C ABI (api.hip) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlstm {
+
+struct StatesParams {
+  const void* K;
+  const void* V;
+  const float* i_pre;
+  const float* f_pre;
+  const float* C0;  // may be null (zero state)
+  const float* n0;  // may be null
+  const float* m0;  // may be null
+  float* C_states;  // (BH, Nc + 1, DK, DV), required
+  float* n_states;  // (BH, Nc + 1, DK), exp gate
+  float* m_states;  // (BH, Nc + 1), exp gate
+  float* C_out;     // may be null
+  float* n_out;
+  float* m_out;
+  int BH, S, DK, DV, L, Nc;
+};
+
+struct HintraParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* i_pre;
+  const float* f_pre;
+  const float* C_states;
+  const float* n_states;
+  const float* m_states;
+  void* H;
+  float* m_rows;    // may be null
+  float* den_rows;  // may be null
+  float scale;
+  float eps;
+  int BH, S, DK, DV, L, Nc;
+  int h_bf16;    // 1: H is bf16, 0: float32
+  int tile_lq;   // rows per workgroup: 64 or 128
+  int tile_lkv;  // keys per step: 64 or 128
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
+hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
+
+}  // namespace mlstm
