@@ -155,14 +155,11 @@ def main(argv=None) -> int:
     ms = e0.elapsed_time(e1) / args.steps
 
     # Per-kernel durations: the same two launches, issued through the stage
-    # entry points with events between them on the launch stream.
+    # entry points (on the same workspace) with events between them on the
+    # launch stream.
     import ctypes
-    Nc = mt.num_chunks(desc)
     L = mt.lib()
-    Cst = torch.empty((w.B, w.NH, Nc + 1, w.DHQK, w.DHV), dtype=torch.float32, device=dev)
-    nst = None if sig else torch.empty((w.B, w.NH, Nc + 1, w.DHQK), dtype=torch.float32, device=dev)
-    mst = None if sig else torch.empty((w.B, w.NH, Nc + 1), dtype=torch.float32, device=dev)
-    del ws
+    ws_bytes = ws.numel()
     sptr = ctypes.c_void_p(stream.cuda_stream)
 
     def p(t):
@@ -172,17 +169,16 @@ def main(argv=None) -> int:
     for it in range(args.steps):
         ev[it][0].record(stream)
         st = L.mlstm_fw_states(ctypes.byref(desc), p(k), p(v), p(i_pre), p(f_pre), p(C0), p(n0), p(m0),
-                               p(Cst), p(nst), p(mst), None, None, None, sptr)
+                               p(ws), ws_bytes, None, None, None, sptr)
         ev[it][1].record(stream)
-        st2 = L.mlstm_fw_hintra(ctypes.byref(desc), p(q), p(k), p(v), p(i_pre), p(f_pre), p(Cst), p(nst),
-                                p(mst), p(H), None, None, sptr)
+        st2 = L.mlstm_fw_hintra(ctypes.byref(desc), p(q), p(k), p(v), p(i_pre), p(f_pre), p(ws), ws_bytes,
+                                p(H), None, None, sptr)
         ev[it][2].record(stream)
         if st or st2:
             raise mt.MlstmError(st or st2, "stage call")
     torch.cuda.synchronize()
     t_states = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     t_hintra = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    del Cst, nst, mst
 
     tokens = w.B * w.S
     flops = mt.flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)

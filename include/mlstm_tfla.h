@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 1
+#define MLSTM_ABI_VERSION 2
 
 typedef enum {
   MLSTM_OK = 0,
@@ -120,13 +120,16 @@ int mlstm_fw_validate(const mlstm_fw_desc_t* desc);
  * -1. */
 int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
 
-/* Bytes of device workspace that mlstm_chunkwise_fw needs for `desc`: the
- * per-chunk states (B, NH, N_c + 1, DHQK, DHV), (B, NH, N_c + 1, DHQK) and
- * (B, NH, N_c + 1) in float32, each region 256-byte aligned.  Returns 0 for an
- * invalid descriptor. */
+/* Bytes of device workspace that the forward pass needs for `desc`: the
+ * stabilised state entering every chunk plus the final state, i.e. N_c + 1
+ * states per head of DHQK x DHV values (4 bytes each), DHQK normaliser values
+ * and one max-state (exp gate), each region 256-byte aligned.  Returns 0 for
+ * an invalid descriptor.  The storage order of the states inside the
+ * workspace belongs to the library (it is the operand order of the kernels
+ * that read it); mlstm_fw_unpack_states returns them as plain float32. */
 size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
 
-/* Full forward pass: states then H (both stages of the chunkwise form).
+/* Full forward pass: stage one (states) then stage two (H) on `workspace`.
  *   C0, n0, m0   may be NULL: zero initial state (m0 = 0).  For the sig gate
  *                n0 and m0 must be NULL.
  *   C_out, n_out, m_out  may be NULL: that final state is not written.  For
@@ -135,8 +138,8 @@ size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
  *                C_out * e^{m_out}.
  *   workspace    device buffer of at least mlstm_fw_workspace_bytes(desc)
  *                bytes, 256-byte aligned; it may be NULL only when that size
- *                is 0.  Its contents on return are the chunk states, laid out
- *                as described for mlstm_fw_states.
+ *                is 0.  On return it holds the chunk states (see
+ *                mlstm_fw_unpack_states).
  * With S == 0 the call only copies the initial state to the outputs. */
 int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        const void* Q, const void* K, const void* V,
@@ -147,23 +150,20 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* Stage one, the inter-chunk recurrence: for every head, the stabilised state
- * entering each chunk c = 0..N_c-1 and the final state (index N_c):
- *   C_states (B, NH, N_c + 1, DHQK, DHV) float32
- *   n_states (B, NH, N_c + 1, DHQK)      float32  (exp gate; NULL for sig)
- *   m_states (B, NH, N_c + 1)            float32  (exp gate; NULL for sig)
- * Entry 0 holds the initial state.  C_out/n_out/m_out as for
- * mlstm_chunkwise_fw.  Q is not read. */
+/* Stage one, the inter-chunk recurrence: writes into `workspace` the
+ * stabilised state entering each chunk c = 0..N_c-1 (entry 0 is the initial
+ * state) and the final state (entry N_c).  Arguments as for
+ * mlstm_chunkwise_fw; Q is not needed. */
 int mlstm_fw_states(const mlstm_fw_desc_t* desc,
                     const void* K, const void* V,
                     const float* i_pre, const float* f_pre,
                     const float* C0, const float* n0, const float* m0,
-                    float* C_states, float* n_states, float* m_states,
+                    void* workspace, size_t workspace_bytes,
                     float* C_out, float* n_out, float* m_out,
                     void* stream);
 
 /* Stage two, the intra-chunk parallel pass: H from Q, K, V, the gates and the
- * states written by mlstm_fw_states (only entries 0..N_c-1 are read).
+ * chunk states that mlstm_fw_states left in `workspace` (same descriptor).
  * Optional per-row outputs (NULL = not written; exp gate only):
  *   m_rows   (B, NH, S) float32: the max-state m_t
  *   den_rows (B, NH, S) float32: the stabilised normaliser s n_t . q_t before
@@ -171,10 +171,20 @@ int mlstm_fw_states(const mlstm_fw_desc_t* desc,
 int mlstm_fw_hintra(const mlstm_fw_desc_t* desc,
                     const void* Q, const void* K, const void* V,
                     const float* i_pre, const float* f_pre,
-                    const float* C_states, const float* n_states,
-                    const float* m_states,
+                    const void* workspace, size_t workspace_bytes,
                     void* H, float* m_rows, float* den_rows,
                     void* stream);
+
+/* The chunk states held in `workspace`, as float32:
+ *   C_states (B, NH, N_c + 1, DHQK, DHV)   (may be NULL)
+ *   n_states (B, NH, N_c + 1, DHQK)        (exp gate; may be NULL)
+ *   m_states (B, NH, N_c + 1)              (exp gate; may be NULL)
+ * Entry c is the state entering chunk c; entry N_c the final state.  For the
+ * sig gate n_states and m_states must be NULL. */
+int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc,
+                           const void* workspace, size_t workspace_bytes,
+                           float* C_states, float* n_states, float* m_states,
+                           void* stream);
 
 #ifdef __cplusplus
 }

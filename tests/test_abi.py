@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert "mlstm_chunkwise_fw" in names and "mlstm_fw_states" in names and "mlstm_fw_hintra" in names
+    for n in ("mlstm_chunkwise_fw", "mlstm_fw_states", "mlstm_fw_hintra", "mlstm_fw_unpack_states"):
+        assert n in names
     out = subprocess.run(["nm", "-D", "--defined-only", mt.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 1
+    assert mt.abi_version() == 2
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -120,11 +121,16 @@ def test_entry_points_refuse_before_launch():
     bad = _desc(DHQK=100)
     assert _fw(bad) == 2
     # stage calls
-    args = [4096] * 13
-    assert lib.mlstm_fw_states(ctypes.byref(d), *args[:7], None, *args[8:], None) == 1   # C_states NULL
-    assert lib.mlstm_fw_states(ctypes.byref(ds), *args[:8], 4096, None, None, None, None, None) == 5
-    assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), None, 4096, 4096, 4096, None, None, None) == 1
-    assert lib.mlstm_fw_hintra(ctypes.byref(ds), *([4096] * 6), None, None, 4096, 4096, None, None) == 5
+    wsb = mt.workspace_bytes(d)
+    assert lib.mlstm_fw_states(ctypes.byref(d), *([4096] * 7), None, wsb, None, None, None, None) == 6
+    assert lib.mlstm_fw_states(ctypes.byref(d), None, *([4096] * 6), 1 << 20, wsb, None, None, None, None) == 1
+    assert lib.mlstm_fw_states(ctypes.byref(ds), *([4096] * 5), 4096, None, 1 << 20, wsb, None, None, None,
+                               None) == 5
+    assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), 1 << 20, wsb, None, None, None, None) == 1
+    assert lib.mlstm_fw_hintra(ctypes.byref(ds), *([4096] * 5), 1 << 20, wsb, 4096, 4096, None, None) == 5
+    assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), 1 << 20, wsb - 1, 4096, None, None, None) == 6
+    assert lib.mlstm_fw_unpack_states(ctypes.byref(ds), 1 << 20, wsb, None, 4096, None, None) == 5
+    assert lib.mlstm_fw_unpack_states(ctypes.byref(d), None, wsb, 4096, None, None, None) == 6
 
 
 def test_flops_formula():

@@ -110,6 +110,13 @@ SMALL = [
     ("bf16_short", dict(B=1, NH=2, S=5, DHQK=64, DHV=64, chunk=64)),
     ("bf16_one", dict(B=1, NH=1, S=1, DHQK=64, DHV=64, chunk=1024)),
     ("bf16_l1024", dict(B=1, NH=1, S=1500, DHQK=128, DHV=128, chunk=1024, init_state=True)),
+    # shapes served by the wide-tile intra-chunk kernel (DHV >= 256, DHQK 128 or 256)
+    ("wide_exp_d128_v256", dict(B=1, NH=2, S=300, DHQK=128, DHV=256, chunk=128)),
+    ("wide_exp_d256_v512_init", dict(B=1, NH=1, S=333, DHQK=256, DHV=512, chunk=64, init_state=True)),
+    ("wide_sig_d256_v256", dict(gate="sig", B=1, NH=2, S=260, DHQK=256, DHV=256, chunk=256)),
+    ("wide_exp_tq128", dict(B=1, NH=1, S=700, DHQK=256, DHV=512, chunk=256, tile_lq=128, tile_lkv=128)),
+    ("wide_sig_tq128_init", dict(gate="sig", B=1, NH=1, S=450, DHQK=128, DHV=512, chunk=512, tile_lq=128,
+                                 init_state=True)),
 ]
 
 
@@ -174,44 +181,65 @@ def test_bf16_h_output(mt):
     _compare(w, gpu, ref, "bf16 H", h_bf16=True)
 
 
-def test_stage_states_match_oracle_chunk_states(mt):
-    w = _small_workload(dict(B=1, NH=2, S=450, DHQK=128, DHV=128, chunk=128, init_state=True))
+@pytest.mark.parametrize("shape", [dict(DHQK=128, DHV=128, chunk=128), dict(DHQK=256, DHV=512, chunk=128),
+                                   dict(DHQK=128, DHV=256, chunk=64, gate="sig")],
+                         ids=["rowmajor_states", "packed_states", "packed_states_sig"])
+def test_stage_states_match_oracle_chunk_states(mt, shape):
+    """Stage one's chunk states (unpacked to float32) against the oracle's."""
+    gate = shape.pop("gate", "exp")
+    w = _small_workload(dict(B=1, NH=2, S=450, init_state=True, gate=gate, **shape))
     x = make_inputs(w)
     k, v = _to_dev(x["k"], torch.bfloat16), _to_dev(x["v"], torch.bfloat16)
+    q = _to_dev(x["q"], torch.bfloat16)
     i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
-    C0, n0, m0 = (_to_dev(x[n], torch.float32) for n in ("C0", "n0", "m0"))
-    Cst, nst, mst, C, n, m = mt.mlstm_fw_states(k, v, i_pre, f_pre, C0, n0, m0, chunk_size=128)
+    C0 = _to_dev(x["C0"], torch.float32)
+    n0 = m0 = None
+    if gate == "exp":
+        n0, m0 = _to_dev(x["n0"], torch.float32), _to_dev(x["m0"], torch.float32)
+    ws, C, n, m = mt.mlstm_fw_states(k, v, i_pre, f_pre, C0, n0, m0, chunk_size=w.chunk, gate=gate)
+    Cst, nst, mst = mt.unpack_states(q, v, ws, chunk_size=w.chunk, gate=gate)
     torch.cuda.synchronize()
-    Cst, nst, mst = (t.cpu().numpy() for t in (Cst, nst, mst))
+    Cst = Cst.cpu().numpy()
     for h in range(2):
         args = [x[nm][0, h].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
-        Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][0, h], x["n0"][0, h], x["m0"][0, h],
-                                                     chunk_size=128, return_states=True)
+        if gate == "exp":
+            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][0, h], x["n0"][0, h], x["m0"][0, h],
+                                                         chunk_size=w.chunk, return_states=True)
+        else:
+            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][0, h], gate="sig",
+                                                         chunk_size=w.chunk, return_states=True)
         Nc = Cs.shape[0]
-        ref_C = np.concatenate([Cs, Cr[None]], axis=0)
-        ref_n = np.concatenate([ns, nr[None]], axis=0)
-        ref_M = np.concatenate([Ms, [mr]], axis=0)
         assert Cst.shape[2] == Nc + 1
-        np.testing.assert_allclose(mst[0, h], ref_M, atol=TOL_M["bf16"], rtol=0)
+        ref_C = np.concatenate([Cs, Cr[None]], axis=0)
         scale = max(1.0, np.abs(ref_C).max())
         assert np.abs(Cst[0, h] - ref_C).max() / scale <= TOL_C["bf16"]
-        assert np.abs(nst[0, h] - ref_n).max() / max(1.0, np.abs(ref_n).max()) <= TOL_C["bf16"]
+        assert np.abs(C.cpu().numpy()[0, h] - Cr).max() / max(1.0, np.abs(Cr).max()) <= TOL_C["bf16"]
+        if gate == "exp":
+            ref_n = np.concatenate([ns, nr[None]], axis=0)
+            ref_M = np.concatenate([Ms, [mr]], axis=0)
+            np.testing.assert_allclose(mst.cpu().numpy()[0, h], ref_M, atol=TOL_M["bf16"], rtol=0)
+            assert np.abs(nst.cpu().numpy()[0, h] - ref_n).max() / max(1.0, np.abs(ref_n).max()) <= TOL_C["bf16"]
 
 
-def test_hintra_rows_match_recurrent_rows(mt):
-    w = _small_workload(dict(qkv_dtype="f32", B=1, NH=1, S=190, DHQK=64, DHV=64, chunk=64))
+@pytest.mark.parametrize("wide", [False, True], ids=["generic", "wide"])
+def test_hintra_rows_match_recurrent_rows(mt, wide):
+    if wide:
+        w = _small_workload(dict(B=1, NH=1, S=190, DHQK=128, DHV=256, chunk=64))
+        dt, tol = torch.bfloat16, 2e-2
+    else:
+        w = _small_workload(dict(qkv_dtype="f32", B=1, NH=1, S=190, DHQK=64, DHV=64, chunk=64))
+        dt, tol = torch.float32, 1e-4
     x = make_inputs(w)
-    q, k, v = (_to_dev(x[n], torch.float32) for n in ("q", "k", "v"))
+    q, k, v = (_to_dev(x[n], dt) for n in ("q", "k", "v"))
     i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
-    Cst, nst, mst, *_ = mt.mlstm_fw_states(k, v, i_pre, f_pre, chunk_size=64)
-    H, m_rows, den_rows = mt.mlstm_fw_hintra(q, k, v, i_pre, f_pre, Cst, nst, mst, chunk_size=64,
-                                             return_rows=True)
+    ws, *_ = mt.mlstm_fw_states(k, v, i_pre, f_pre, chunk_size=64)
+    H, m_rows, den_rows = mt.mlstm_fw_hintra(q, k, v, i_pre, f_pre, ws, chunk_size=64, return_rows=True)
     torch.cuda.synchronize()
     args = [x[nm][0, 0].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
     Hr, _, _, _, rm, rden = recurrent_fw(*args, return_rows=True)
-    np.testing.assert_allclose(H.cpu().numpy()[0, 0], Hr, atol=1e-4, rtol=0)
+    np.testing.assert_allclose(H.cpu().numpy()[0, 0], Hr, atol=tol, rtol=0)
     np.testing.assert_allclose(m_rows.cpu().numpy()[0, 0], rm, atol=1e-5, rtol=0)
-    np.testing.assert_allclose(den_rows.cpu().numpy()[0, 0], rden, atol=1e-4, rtol=1e-5)
+    np.testing.assert_allclose(den_rows.cpu().numpy()[0, 0], rden, atol=1e-4, rtol=1e-4)
 
 
 def test_empty_sequence_copies_initial_state(mt):

@@ -10,7 +10,6 @@ import of the functions below fails with an error that says how to build it.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -57,8 +56,12 @@ _SYMBOLS = {
     "mlstm_fw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_fw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-    "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
-    "mlstm_fw_hintra": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12),
+    "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 8
+                        + [ctypes.c_size_t] + [ctypes.c_void_p] * 4),
+    "mlstm_fw_hintra": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 6
+                        + [ctypes.c_size_t] + [ctypes.c_void_p] * 4),
+    "mlstm_fw_unpack_states": (ctypes.c_int, [ctypes.POINTER(FwDesc), ctypes.c_void_p, ctypes.c_size_t]
+                               + [ctypes.c_void_p] * 4),
 }
 
 
@@ -221,25 +224,34 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     return H, C_out, n_out, m_out
 
 
+def _workspace(desc, workspace, dev):
+    torch = _torch()
+    need = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {need}")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def mlstm_fw_states(k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
-                    gate: str = "exp", precision: str = "split", return_final_state: bool = True):
-    """Stage one alone: returns (C_states, n_states, m_states, C, n, m) with the
-    state entering every chunk plus the final state at index N_c."""
+                    gate: str = "exp", precision: str = "split", tile_lq: int = 0, tile_lkv: int = 0,
+                    workspace=None, return_final_state: bool = True):
+    """Stage one alone.  Returns (workspace, C, n, m): the workspace now holds
+    the chunk states (read them with unpack_states); C, n, m are the final
+    state (None where not requested or not defined for the gate)."""
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(k, k, v, i_pre, f_pre)
-    desc = _desc_for(k, v, chunk_size, gate, torch.float32, precision, None, 0.0, 0, 0)
+    desc = _desc_for(k, v, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_fw_states")
     _check(C0, "C0", (B, NH, DK, DV), torch.float32)
     _check(n0, "n0", (B, NH, DK), torch.float32)
     _check(m0, "m0", (B, NH), torch.float32)
-    Nc = num_chunks(desc)
     dev = k.device
     sig = gate == "sig"
-    Cst = torch.empty((B, NH, Nc + 1, DK, DV), dtype=torch.float32, device=dev)
-    nst = None if sig else torch.empty((B, NH, Nc + 1, DK), dtype=torch.float32, device=dev)
-    mst = None if sig else torch.empty((B, NH, Nc + 1), dtype=torch.float32, device=dev)
+    workspace, ws_bytes = _workspace(desc, workspace, dev)
     C_out = n_out = m_out = None
     if return_final_state:
         C_out = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=dev)
@@ -248,18 +260,18 @@ def mlstm_fw_states(k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size
             m_out = torch.empty((B, NH), dtype=torch.float32, device=dev)
     st = lib().mlstm_fw_states(
         ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
-        _ptr(Cst), _ptr(nst), _ptr(mst), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
+        _ptr(workspace), ws_bytes, _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
     if st:
         raise MlstmError(st, "mlstm_fw_states")
-    return Cst, nst, mst, C_out, n_out, m_out
+    return workspace, C_out, n_out, m_out
 
 
-def mlstm_fw_hintra(q, k, v, i_pre, f_pre, C_states, n_states=None, m_states=None, *,
-                    chunk_size: int, gate: str = "exp", h_dtype=None, precision: str = "split",
-                    qk_scale: Optional[float] = None, eps: float = 0.0,
-                    tile_lq: int = 0, tile_lkv: int = 0, return_rows: bool = False):
-    """Stage two alone: H (and, with return_rows, per-row m and stabilised
-    normaliser) from the chunk states of mlstm_fw_states."""
+def mlstm_fw_hintra(q, k, v, i_pre, f_pre, workspace, *, chunk_size: int, gate: str = "exp",
+                    h_dtype=None, precision: str = "split", qk_scale: Optional[float] = None,
+                    eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, return_rows: bool = False):
+    """Stage two alone: H (and, with return_rows, the per-row m and stabilised
+    normaliser) from the chunk states that mlstm_fw_states left in workspace.
+    The descriptor arguments must match the ones given to mlstm_fw_states."""
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
     h_dtype = torch.float32 if h_dtype is None else h_dtype
@@ -267,24 +279,48 @@ def mlstm_fw_hintra(q, k, v, i_pre, f_pre, C_states, n_states=None, m_states=Non
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_fw_hintra")
-    Nc = num_chunks(desc)
-    _check(C_states, "C_states", (B, NH, Nc + 1, DK, DV), torch.float32)
-    _check(n_states, "n_states", (B, NH, Nc + 1, DK), torch.float32)
-    _check(m_states, "m_states", (B, NH, Nc + 1), torch.float32)
     dev = q.device
+    workspace, ws_bytes = _workspace(desc, workspace, dev)
     H = torch.empty((B, NH, S, DV), dtype=h_dtype, device=dev)
     m_rows = den_rows = None
     if return_rows and gate == "exp":
         m_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
         den_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
     st = lib().mlstm_fw_hintra(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C_states),
-        _ptr(n_states), _ptr(m_states), _ptr(H), _ptr(m_rows), _ptr(den_rows), _stream())
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(workspace), ws_bytes,
+        _ptr(H), _ptr(m_rows), _ptr(den_rows), _stream())
     if st:
         raise MlstmError(st, "mlstm_fw_hintra")
     if return_rows:
         return H, m_rows, den_rows
     return H
+
+
+def unpack_states(q_like, v_like, workspace, *, chunk_size: int, gate: str = "exp",
+                  precision: str = "split", tile_lq: int = 0, tile_lkv: int = 0):
+    """The chunk states in workspace as float32 tensors (C_states, n_states,
+    m_states) of shapes (B, NH, N_c+1, DHQK, DHV), (B, NH, N_c+1, DHQK),
+    (B, NH, N_c+1); entry c is the state entering chunk c.  q_like / v_like
+    only supply the shapes and the input dtype."""
+    torch = _torch()
+    desc = _desc_for(q_like, v_like, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv)
+    st = validate(desc)
+    if st:
+        raise MlstmError(st, "mlstm_fw_unpack_states")
+    B, NH, S, DK = q_like.shape
+    DV = v_like.shape[-1]
+    Nc = num_chunks(desc)
+    dev = q_like.device
+    sig = gate == "sig"
+    Cst = torch.empty((B, NH, Nc + 1, DK, DV), dtype=torch.float32, device=dev)
+    nst = None if sig else torch.empty((B, NH, Nc + 1, DK), dtype=torch.float32, device=dev)
+    mst = None if sig else torch.empty((B, NH, Nc + 1), dtype=torch.float32, device=dev)
+    st = lib().mlstm_fw_unpack_states(ctypes.byref(desc), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _ptr(Cst), _ptr(nst), _ptr(mst), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_fw_unpack_states")
+    return Cst, nst, mst
 
 
 def flops(B, NH, S, DHQK, DHV, chunk_size) -> float:

@@ -84,9 +84,40 @@ float resolve_scale(const mlstm_fw_desc_t* d) {
   return d->qk_scale > 0.0f ? d->qk_scale : 1.0f / sqrtf((float)d->DHQK);
 }
 
+// The wide kernels (bf16 inputs, large head dims) keep the chunk states in
+// the packed fragment layout; every other shape uses float32 row-major
+// states.  Both layouts take the same number of bytes.
+bool packed_layout(const mlstm_fw_desc_t* d) {
+  const int tq = d->tile_lq ? d->tile_lq : 64;
+  return mlstm::hintra_wide_supported(d->DHQK, d->DHV, d->chunk_size, tq, d->qkv_dtype == MLSTM_BF16);
+}
+
+struct WsPtrs {
+  float* C;
+  float* n;
+  float* m;
+};
+
+WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
+  const WsLayout w = ws_layout(d);
+  char* ws = static_cast<char*>(workspace);
+  WsPtrs r;
+  r.C = reinterpret_cast<float*>(ws + w.c_off);
+  r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
+  r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
+  return r;
+}
+
+int check_workspace(const mlstm_fw_desc_t* d, const void* workspace, size_t workspace_bytes) {
+  const WsLayout w = ws_layout(d);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MLSTM_E_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  return MLSTM_OK;
+}
+
 int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const float* i_pre, const float* f_pre,
-               const float* C0, const float* n0, const float* m0, float* Cst, float* nst, float* mst,
-               float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+               const float* C0, const float* n0, const float* m0, const WsPtrs& ws, float* C_out, float* n_out,
+               float* m_out, hipStream_t stream) {
   StatesParams p;
   p.K = K;
   p.V = V;
@@ -95,9 +126,9 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   p.C0 = C0;
   p.n0 = n0;
   p.m0 = m0;
-  p.C_states = Cst;
-  p.n_states = nst;
-  p.m_states = mst;
+  p.C_states = ws.C;
+  p.n_states = ws.n;
+  p.m_states = ws.m;
   p.C_out = C_out;
   p.n_out = n_out;
   p.m_out = m_out;
@@ -108,14 +139,16 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   p.L = d->chunk_size;
   p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
-  const hipError_t e = mlstm::launch_states(p, bf16, d->gate == MLSTM_GATE_SIG,
-                                            bf16 && d->precision == MLSTM_PREC_SPLIT, stream);
+  const bool sig = d->gate == MLSTM_GATE_SIG;
+  const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
+  const hipError_t e = packed_layout(d) ? mlstm::launch_states_wide(p, sig, split, stream)
+                                        : mlstm::launch_states(p, bf16, sig, split, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
 int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
-               const float* f_pre, const float* Cst, const float* nst, const float* mst, void* H,
-               float* m_rows, float* den_rows, hipStream_t stream) {
+               const float* f_pre, const WsPtrs& ws, void* H, float* m_rows, float* den_rows,
+               hipStream_t stream) {
   if (d->S == 0) return MLSTM_OK;
   HintraParams p;
   p.Q = Q;
@@ -123,9 +156,9 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   p.V = V;
   p.i_pre = i_pre;
   p.f_pre = f_pre;
-  p.C_states = Cst;
-  p.n_states = nst;
-  p.m_states = mst;
+  p.C_states = ws.C;
+  p.n_states = ws.n;
+  p.m_states = ws.m;
   p.H = H;
   p.m_rows = m_rows;
   p.den_rows = den_rows;
@@ -141,8 +174,10 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   p.tile_lq = d->tile_lq ? d->tile_lq : 64;
   p.tile_lkv = d->tile_lkv ? d->tile_lkv : 64;
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
-  const hipError_t e = mlstm::launch_hintra(p, bf16, d->gate == MLSTM_GATE_SIG,
-                                            bf16 && d->precision == MLSTM_PREC_SPLIT, stream);
+  const bool sig = d->gate == MLSTM_GATE_SIG;
+  const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
+  const hipError_t e = packed_layout(d) ? mlstm::launch_hintra_wide(p, sig, split, stream)
+                                        : mlstm::launch_hintra(p, bf16, sig, split, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
@@ -181,37 +216,58 @@ size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc) {
 }
 
 int mlstm_fw_states(const mlstm_fw_desc_t* desc, const void* K, const void* V, const float* i_pre,
-                    const float* f_pre, const float* C0, const float* n0, const float* m0, float* C_states,
-                    float* n_states, float* m_states, float* C_out, float* n_out, float* m_out,
-                    void* stream) {
+                    const float* f_pre, const float* C0, const float* n0, const float* m0, void* workspace,
+                    size_t workspace_bytes, float* C_out, float* n_out, float* m_out, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
   if (desc->S > 0 && (!K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
-  if (!C_states) return MLSTM_E_NULLPTR;
-  if (desc->gate == MLSTM_GATE_EXP && (!n_states || !m_states)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
-  if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
-  if ((K && !aligned(K, 16)) || (V && !aligned(V, 16)) || !aligned(C_states, 16)) return MLSTM_E_ALIGN;
-  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, n_states, m_states, C_out, n_out, m_out})) != MLSTM_OK)
-    return st;
-  return run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, C_states, n_states, m_states, C_out, n_out, m_out,
+  if ((K && !aligned(K, 16)) || (V && !aligned(V, 16))) return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, C_out, n_out, m_out})) != MLSTM_OK) return st;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  return run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws_ptrs(desc, workspace), C_out, n_out, m_out,
                     static_cast<hipStream_t>(stream));
 }
 
 int mlstm_fw_hintra(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
-                    const float* f_pre, const float* C_states, const float* n_states, const float* m_states,
-                    void* H, float* m_rows, float* den_rows, void* stream) {
+                    const float* f_pre, const void* workspace, size_t workspace_bytes, void* H, float* m_rows,
+                    float* den_rows, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H || !C_states)) return MLSTM_E_NULLPTR;
-  if (desc->S > 0 && desc->gate == MLSTM_GATE_EXP && (!n_states || !m_states)) return MLSTM_E_NULLPTR;
-  if ((st = check_sig_nulls(desc, n_states, m_states, m_rows, den_rows)) != MLSTM_OK) return st;
-  if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)) ||
-      (C_states && !aligned(C_states, 16)))
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, m_rows, den_rows, nullptr, nullptr)) != MLSTM_OK) return st;
+  if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
     return MLSTM_E_ALIGN;
-  if ((st = check_f32_ptrs({i_pre, f_pre, n_states, m_states, m_rows, den_rows})) != MLSTM_OK) return st;
-  return run_hintra(desc, Q, K, V, i_pre, f_pre, C_states, n_states, m_states, H, m_rows, den_rows,
-                    static_cast<hipStream_t>(stream));
+  if ((st = check_f32_ptrs({i_pre, f_pre, m_rows, den_rows})) != MLSTM_OK) return st;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  return run_hintra(desc, Q, K, V, i_pre, f_pre, ws_ptrs(desc, const_cast<void*>(workspace)), H, m_rows,
+                    den_rows, static_cast<hipStream_t>(stream));
+}
+
+int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, size_t workspace_bytes,
+                           float* C_states, float* n_states, float* m_states, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
+  if ((st = check_f32_ptrs({C_states, n_states, m_states})) != MLSTM_OK) return st;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  const WsPtrs ws = ws_ptrs(desc, const_cast<void*>(workspace));
+  const long long n = (long long)desc->B * desc->NH * (mlstm_fw_num_chunks(desc) + 1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (C_states) {
+    if (packed_layout(desc)) {
+      e = mlstm::launch_unpack_states(ws.C, C_states, n, desc->DHQK, desc->DHV, s);
+    } else {
+      e = hipMemcpyAsync(C_states, ws.C, (size_t)n * desc->DHQK * desc->DHV * sizeof(float),
+                         hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (e == hipSuccess && n_states)
+    e = hipMemcpyAsync(n_states, ws.n, (size_t)n * desc->DHQK * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && m_states)
+    e = hipMemcpyAsync(m_states, ws.m, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
 int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
@@ -225,17 +281,12 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
     return MLSTM_E_ALIGN;
   if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, C_out, n_out, m_out})) != MLSTM_OK) return st;
-  const WsLayout w = ws_layout(desc);
-  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MLSTM_E_WORKSPACE;
-  if (workspace && !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  float* Cst = reinterpret_cast<float*>(ws + w.c_off);
-  float* nst = desc->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
-  float* mst = desc->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  const WsPtrs ws = ws_ptrs(desc, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, Cst, nst, mst, C_out, n_out, m_out, s);
+  st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
   if (st != MLSTM_OK) return st;
-  return run_hintra(desc, Q, K, V, i_pre, f_pre, Cst, nst, mst, H, nullptr, nullptr, s);
+  return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);
 }
 
 }  // extern "C"

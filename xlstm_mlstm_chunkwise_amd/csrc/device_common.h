@@ -251,4 +251,92 @@ __device__ __forceinline__ float block_reduce(float x, float* scratch) {
   return r;
 }
 
+
+// ---------------------------------------------------------------------------
+// 32x32x16 fp16 matrix-core tiles (v_mfma_f32_32x32x16_f16).
+// A fragment: lane l holds A[row l % 32][k 8 * (l / 32) + e], e = 0..7.
+// B fragment: lane l holds B[k 8 * (l / 32) + e][col l % 32].
+// Accumulator: lane l register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float16_t mma32(const half8_t& a, const half8_t& b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element e = 0..3 from address a_{i/4 + 4e} + (i % 4),
+// where a_j is the address supplied by lane j of the group.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4_t lds_read_tr16(const _Float16* p) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+  return __builtin_bit_cast(half4_t, v);
+}
+
+// Fragment whose contraction axis runs down the rows of a row-major LDS
+// matrix X (row stride ld elements): lane l gets X[k0 + 8 * (l / 32) + e][c0 + l % 32],
+// e = 0..7.  Serves as a B fragment (rows = k, columns = n) and as an A
+// fragment of the transposed matrix (columns of X = rows of A).
+__device__ __forceinline__ half8_t frag_tr(const _Float16* X, int ld, int k0, int c0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const _Float16* base = X + (k0 + 8 * (grp >> 1) + (j >> 2)) * ld + c0 + 16 * (grp & 1) + 4 * (j & 3);
+  const half4_t lo = lds_read_tr16(base);
+  const half4_t hi = lds_read_tr16(base + 4 * ld);
+  half8_t f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+// Fragment whose contraction axis runs along a row of a row-major LDS matrix:
+// lane l gets X[r0 + l % 32][k0 + 8 * (l / 32) + e] (one 16-byte read).
+__device__ __forceinline__ half8_t frag_row(const _Float16* X, int ld, int r0, int k0, int lane) {
+  return *reinterpret_cast<const half8_t*>(X + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
+}
+
+// bf16 x 8 (16 bytes) -> fp16 x 8.
+__device__ __forceinline__ half8_t bf16x8_to_f16x8(uint4 u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  half8_t f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = static_cast<_Float16>(__uint_as_float(w[e] << 16));
+    f[2 * e + 1] = static_cast<_Float16>(__uint_as_float(w[e] & 0xffff0000u));
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// Packed chunk-state layout shared by the wide states and intra-chunk kernels.
+// One state (DK x DV) is stored as (DK/16) x (DV/32) fragments of a 16-row k
+// step and a 32-column block; each fragment is a hi plane then a lo plane of
+// 64 lanes x 8 fp16 values (2 x 1 KiB).  Lane l holds column 32*nb + l % 32;
+// slot e holds row 16*kk + (e < 4 ? 4*(l/32) + e : 8 + 4*(l/32) + e - 4), the
+// row order of a 32x32 accumulator half.  hi + lo reproduces the float32
+// state to about 22 significant bits.
+__device__ __forceinline__ size_t pack_frag_offset(int kk, int nb, int plane, int DV) {
+  return ((size_t)(kk * (DV / 32) + nb) * 2 + plane) * 512;
+}
+
+__device__ __forceinline__ float unpack_state_elem(const _Float16* P, int k, int v, int DV) {
+  const int kk = k >> 4, kr = k & 15, nb = v >> 5, col = v & 31;
+  const int h = (kr & 7) >> 2;
+  const int e = (kr < 8 ? 0 : 4) + (kr & 3);
+  const int lane = 32 * h + col;
+  const float hi = static_cast<float>(P[pack_frag_offset(kk, nb, 0, DV) + lane * 8 + e]);
+  const float lo = static_cast<float>(P[pack_frag_offset(kk, nb, 1, DV) + lane * 8 + e]);
+  return hi + lo;
+}
+
+// 4 bf16 (8 bytes) -> 4 fp16.
+__device__ __forceinline__ half4_t bf16x4_to_f16x4(uint2 u) {
+  half4_t f;
+  f[0] = static_cast<_Float16>(__uint_as_float(u.x << 16));
+  f[1] = static_cast<_Float16>(__uint_as_float(u.x & 0xffff0000u));
+  f[2] = static_cast<_Float16>(__uint_as_float(u.y << 16));
+  f[3] = static_cast<_Float16>(__uint_as_float(u.y & 0xffff0000u));
+  return f;
+}
+
 }  // namespace mlstm

@@ -47,4 +47,16 @@ struct HintraParams {
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 
+// Wide-tile intra-chunk kernel (bf16 inputs, large head dims): whether it
+// covers a shape, and its launch.
+bool hintra_wide_supported(int DK, int DV, int L, int tile_lq, bool bf16_inputs);
+hipError_t launch_hintra_wide(const HintraParams& p, bool sig, bool split, hipStream_t stream);
+
+// Wide-tile states kernel: writes the chunk states in the packed fragment
+// layout read by the wide intra-chunk kernel.
+hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream);
+// Packed states (n_states x DK x DV) -> float32.
+hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
+                                hipStream_t stream);
+
 }  // namespace mlstm

@@ -1,0 +1,300 @@
+// Inter-chunk recurrence, wide-tile version for bf16 inputs (gfx950).
+//
+// Same recurrence as states_kernel.hip (TFLA abstract: chunkwise-parallel
+// form with states carried between chunks):
+//   M' = max(g + M, max_t a_t),  a_t = g - b_t + i_t
+//   C' = e^{g + M - M'} C + sum_t e^{a_t - M'} k_t v_t^T,   n' likewise
+//   (sigmoid gate: C' = e^{g} C + sum_t e^{g - b_t + log sigmoid(i_t)} k_t v_t^T)
+// Organisation:
+//   * one workgroup (4 waves) keeps a TK x TV tile of C in 32x32x16 fp16
+//     matrix-core accumulators for the whole sequence (TK = TV = 64 or 128);
+//   * each 64-step time block stages the gated keys as fp16 hi + lo planes and
+//     the values as fp16, both row-major in LDS, and reads them transposed
+//     with ds_read_b64_tr_b16 (the contraction runs over time, down the rows);
+//   * the state entering every chunk is written in the packed layout the
+//     intra-chunk kernel consumes (see pack_offset): for every 16-row k step
+//     and 32-column block, 64 lanes x 8 fp16 values, hi plane then lo plane.
+//     The lane and slot order is the accumulator's own, so the writes are
+//     plain 16-byte stores.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mlstm {
+namespace {
+
+constexpr int kMaxL = 1024;
+constexpr int kTT = 64;  // time steps per LDS stage
+
+template <int TK, int TV, bool SIG, bool SPLIT>
+__global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) {
+  constexpr int WR = TK / 2, WCOL = TV / 2;      // wave tile
+  constexpr int RB = WR / 32, CB = WCOL / 32;    // 32x32 blocks per wave
+  constexpr int LDK = TK + 8, LDV = TV + 8;
+  constexpr int KSEG = TK / 8, VSEG = TV / 8;    // 16-byte segments per row
+  constexpr int KPT = kTT * KSEG / 256, VPT = kTT * VSEG / 256;
+  static_assert(kTT * KSEG % 256 == 0 && kTT * VSEG % 256 == 0, "staging split");
+
+  __shared__ float s_w[kMaxL];
+  __shared__ float s_red[4];
+  __shared__ float s_g;
+  __shared__ float s_np[256 / KSEG][TK];
+  __shared__ __align__(16) _Float16 s_kh[kTT * LDK];
+  __shared__ __align__(16) _Float16 s_kl[kTT * LDK];
+  __shared__ __align__(16) _Float16 s_v[kTT * LDV];
+
+  const int NTK = p.DK / TK, NTV = p.DV / TV;
+  const int bid = blockIdx.x;
+  const int bh = bid % p.BH;
+  const int kt = (bid / p.BH) % NTK;
+  const int vt = bid / (p.BH * NTK);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int S = p.S, DK = p.DK, DV = p.DV, L = p.L, Nc = p.Nc;
+  const int wr0 = (wave >> 1) * WR, wc0 = (wave & 1) * WCOL;  // inside the tile
+  const uint16_t* K = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK + kt * TK;
+  const uint16_t* V = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV + vt * TV;
+  const float* ig = p.i_pre + (size_t)bh * S;
+  const float* fg = p.f_pre + (size_t)bh * S;
+  const bool own_n = !SIG && vt == 0;
+  const int nseg = tid % KSEG;     // this thread's key segment while staging
+  const int nrow = tid / KSEG;     // and its first time row
+
+  float16_t acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const int vcol = vt * TV + wc0 + 32 * cb + l32;
+        acc[rb][cb][r] = p.C0 ? p.C0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] : 0.0f;
+      }
+  float nreg = 0.0f;  // n for key row kt*TK + tid (tid < TK), own_n only
+  if (own_n && tid < TK && p.n0) nreg = p.n0[(size_t)bh * DK + kt * TK + tid];
+  float M = 0.0f;
+  if (!SIG && p.m0) M = p.m0[bh];
+
+  uint4 kpre[KPT], vpre[VPT];
+  auto load_kv = [&](int t0, int tb, int Lc) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int t = nrow + i * (256 / KSEG);
+      kpre[i] = (tb + t < Lc) ? *reinterpret_cast<const uint4*>(K + (size_t)(t0 + tb + t) * DK + nseg * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int idx = tid + i * 256;
+      const int t = idx / VSEG, sg = idx % VSEG;
+      vpre[i] = (tb + t < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(t0 + tb + t) * DV + sg * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  for (int c = 0; c <= Nc; ++c) {
+    // ---- state entering chunk c, packed hi/lo fragments
+    {
+      _Float16* P = reinterpret_cast<_Float16*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
+      const int NB = DV / 32;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
+          const int nblk = (vt * TV + wc0 + 32 * cb) / 32;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            half8_t hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = acc[rb][cb][8 * half + e];
+              const _Float16 hh = static_cast<_Float16>(x);
+              hi[e] = hh;
+              lo[e] = static_cast<_Float16>(x - static_cast<float>(hh));
+            }
+            const size_t blk = ((size_t)(2 * kblk + half) * NB + nblk) * 2;
+            *reinterpret_cast<half8_t*>(P + (blk + 0) * 512 + lane * 8) = hi;
+            *reinterpret_cast<half8_t*>(P + (blk + 1) * 512 + lane * 8) = lo;
+          }
+        }
+      if (own_n && tid < TK) p.n_states[((size_t)bh * (Nc + 1) + c) * DK + kt * TK + tid] = nreg;
+      if (!SIG && kt == 0 && vt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + c] = M;
+    }
+    if (c == Nc) break;
+
+    const int t0 = c * L;
+    const int Lc = min(L, S - t0);
+    load_kv(t0, 0, Lc);  // first time block, overlapped with the gates
+    // ---- gates
+    float b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = 4 * tid + e;
+      b[e] = pos < Lc ? log_sigmoid(fg[t0 + pos]) : 0.0f;
+    }
+    block_scan4<false, 4>(b, s_red);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * tid + e == Lc - 1) s_g = b[e];
+    __syncthreads();
+    const float gsum = s_g;
+    float a[4];
+    float amax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = 4 * tid + e;
+      if (pos < Lc) {
+        const float it = ig[t0 + pos];
+        a[e] = gsum - b[e] + (SIG ? log_sigmoid(it) : it);
+        amax = fmaxf(amax, a[e]);
+      } else {
+        a[e] = -INFINITY;
+      }
+    }
+    float decay;
+    if constexpr (SIG) {
+      decay = expf(gsum);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? expf(a[e]) : 0.0f;
+    } else {
+      amax = block_reduce<true, 4>(amax, s_red);
+      const float Mnew = fmaxf(gsum + M, amax);
+      decay = expf(gsum + M - Mnew);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? expf(a[e] - Mnew) : 0.0f;
+      M = Mnew;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[rb][cb] *= decay;
+    float np[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) np[e] = 0.0f;
+
+    for (int tb = 0; tb < Lc; tb += kTT) {
+      // stage gated keys (hi/lo) and values
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int t = nrow + i * (256 / KSEG);
+        const float w = s_w[tb + t];  // 0 beyond the chunk
+        const uint32_t ww[4] = {kpre[i].x, kpre[i].y, kpre[i].z, kpre[i].w};
+        half8_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __uint_as_float(ww[e] << 16) * w;
+          const float x1 = __uint_as_float(ww[e] & 0xffff0000u) * w;
+          np[2 * e] += x0;
+          np[2 * e + 1] += x1;
+          const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+          hi[2 * e] = h0;
+          hi[2 * e + 1] = h1;
+          lo[2 * e] = static_cast<_Float16>(x0 - static_cast<float>(h0));
+          lo[2 * e + 1] = static_cast<_Float16>(x1 - static_cast<float>(h1));
+        }
+        *reinterpret_cast<half8_t*>(s_kh + t * LDK + nseg * 8) = hi;
+        if constexpr (SPLIT) *reinterpret_cast<half8_t*>(s_kl + t * LDK + nseg * 8) = lo;
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int idx = tid + i * 256;
+        const int t = idx / VSEG, sg = idx % VSEG;
+        *reinterpret_cast<half8_t*>(s_v + t * LDV + sg * 8) = bf16x8_to_f16x8(vpre[i]);
+      }
+      if (tb + kTT < Lc) load_kv(t0, tb + kTT, Lc);
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kTT / 16; ++ks) {
+        if (tb + 16 * ks >= Lc) break;  // uniform: rest of the block is padding
+        half8_t ah[RB], al[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          ah[rb] = frag_tr(s_kh, LDK, 16 * ks, wr0 + 32 * rb, lane);
+          if constexpr (SPLIT) al[rb] = frag_tr(s_kl, LDK, 16 * ks, wr0 + 32 * rb, lane);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const half8_t bv = frag_tr(s_v, LDV, 16 * ks, wc0 + 32 * cb, lane);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][cb] = mma32(ah[rb], bv, acc[rb][cb]);
+            if constexpr (SPLIT) acc[rb][cb] = mma32(al[rb], bv, acc[rb][cb]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (own_n) {
+      // n' = decay n + sum_t w_t k_t: reduce the per-thread partial sums
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_np[nrow][nseg * 8 + e] = np[e];
+      __syncthreads();
+      if (tid < TK) {
+        float sacc = 0.0f;
+        for (int r = 0; r < 256 / KSEG; ++r) sacc += s_np[r][tid];
+        nreg = nreg * decay + sacc;
+      }
+      __syncthreads();
+    }
+  }
+
+  if (p.C_out) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const int vcol = vt * TV + wc0 + 32 * cb + l32;
+          p.C_out[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] = acc[rb][cb][r];
+        }
+  }
+  if (own_n && p.n_out && tid < TK) p.n_out[(size_t)bh * DK + kt * TK + tid] = nreg;
+  if (!SIG && p.m_out && kt == 0 && vt == 0 && tid == 0) p.m_out[bh] = M;
+}
+
+template <int T, bool SIG, bool SPLIT>
+hipError_t launch_t(const StatesParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)(p.BH * (p.DK / T) * (p.DV / T)));
+  hipLaunchKernelGGL((states_wide_kernel<T, T, SIG, SPLIT>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Packed state -> float32 (B, NH, N_c + 1, DK, DV).
+__global__ __launch_bounds__(256) void unpack_states_kernel(const _Float16* P, float* C, long long total, int DK,
+                                                            int DV) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long per = (long long)DK * DV;
+  const long long s = i / per;
+  const int k = (int)((i % per) / DV), v = (int)(i % DV);
+  C[i] = unpack_state_elem(P + s * per * 2, k, v, DV);
+}
+
+}  // namespace
+
+hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  // 128-wide tiles when they still give at least two workgroups per CU.
+  const bool big = (long long)p.BH * (p.DK / 128) * (p.DV / 128) >= 512;
+  if (big) {
+    if (sig) return split ? launch_t<128, true, true>(p, stream) : launch_t<128, true, false>(p, stream);
+    return split ? launch_t<128, false, true>(p, stream) : launch_t<128, false, false>(p, stream);
+  }
+  if (sig) return split ? launch_t<64, true, true>(p, stream) : launch_t<64, true, false>(p, stream);
+  return split ? launch_t<64, false, true>(p, stream) : launch_t<64, false, false>(p, stream);
+}
+
+hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
+                                hipStream_t stream) {
+  const long long total = n_states * DK * DV;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(unpack_states_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(packed), C, total, DK, DV);
+  return hipGetLastError();
+}
+
+}  // namespace mlstm
