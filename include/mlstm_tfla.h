@@ -78,16 +78,22 @@ typedef enum {
 typedef enum { MLSTM_F32 = 0, MLSTM_BF16 = 1 } mlstm_dtype_t;
 typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
 
-/* Operand precision of the three contractions whose left operand is
- * computed on the fly (P = scores x decay in P.V, the carried state C in
- * Q.C, and the gated keys in K^T.V).  Inputs Q, K, V are converted to fp16
- * for the matrix cores (exact for bf16 values of magnitude in
- * [2^-14, 65504]; smaller ones keep an absolute error below 2^-25).
+/* Arithmetic of the three contractions whose left operand is computed on the
+ * fly (P = scores x decay in P.V, the carried state C in Q.C, and the gated
+ * keys in K^T.V).  For bf16 inputs Q, K, V are converted to fp16 for the
+ * matrix cores (exact for bf16 values of magnitude in [2^-14, 65504];
+ * smaller ones keep an absolute error below 2^-25).
  *   MLSTM_PREC_SPLIT: the computed operand is carried as an fp16 hi + lo
- *                     pair (about 21 significant bits, two MFMA passes).
+ *                     pair (about 21 significant bits, two MFMA passes),
+ *                     fp32 accumulation.  Default.
  *   MLSTM_PREC_F16:   one fp16 rounding of the computed operand (one pass).
- * Ignored for float32 inputs, which use fp32 matrix-core instructions. */
-typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1 } mlstm_prec_t;
+ *   MLSTM_PREC_F64:   everything (gates, scores, contractions, chunk states)
+ *                     in fp64 on the vector units; for rows whose sums cancel
+ *                     too strongly for fp32 accumulation.  Workspace states
+ *                     take 8 bytes per value.
+ * SPLIT and F16 are the same for float32 inputs, which use fp32 matrix-core
+ * instructions. */
+typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } mlstm_prec_t;
 
 typedef struct {
   int32_t B, NH;       /* batch, heads: >= 1                                   */
@@ -122,8 +128,9 @@ int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
 
 /* Bytes of device workspace that the forward pass needs for `desc`: the
  * stabilised state entering every chunk plus the final state, i.e. N_c + 1
- * states per head of DHQK x DHV values (4 bytes each), DHQK normaliser values
- * and one max-state (exp gate), each region 256-byte aligned.  Returns 0 for
+ * states per head of DHQK x DHV values, DHQK normaliser values and one
+ * max-state (exp gate), each region 256-byte aligned; 4 bytes per value, 8
+ * with MLSTM_PREC_F64.  Returns 0 for
  * an invalid descriptor.  The storage order of the states inside the
  * workspace belongs to the library (it is the operand order of the kernels
  * that read it); mlstm_fw_unpack_states returns them as plain float32. */

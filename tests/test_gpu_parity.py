@@ -169,6 +169,48 @@ def test_workload_parity_full_size_sampled_heads(mt, name):
     print(f"[{name}] heads {len(heads)} max|dH|={worst:.3g}", flush=True)
 
 
+def test_f64_mode_full_size_bf16_s2048_d128(mt):
+    """The 2048/128 workload holds rows beyond float32 accumulation; the
+    float64 mode meets the 2e-2 bound on every head."""
+    w = WORKLOADS["bf16_s2048_d128"]
+    x = make_inputs(w)
+    gpu = _run_gpu(mt, w, x, precision="f64")
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.NH):
+            ref = _oracle(w, x, (b, h))
+            g = [None if o is None else o[b, h] for o in gpu]
+            worst = max(worst, _compare(w, g, ref, f"f64 head {(b, h)}"))
+    print(f"\n[bf16_s2048_d128 f64] heads {w.BH} max|dH|={worst:.3g}", flush=True)
+
+
+F64_SMALL = [
+    ("f64_bf16_exp", dict(B=1, NH=2, S=300, DHQK=128, DHV=128, chunk=128, init_state=True)),
+    ("f64_bf16_sig", dict(gate="sig", B=1, NH=2, S=200, DHQK=64, DHV=192, chunk=64)),
+    ("f64_f32_exp", dict(qkv_dtype="f32", B=2, NH=1, S=257, DHQK=64, DHV=64, chunk=256)),
+    ("f64_bf16_spikes", dict(B=1, NH=2, S=600, DHQK=128, DHV=128, chunk=128, i_dist=("normal", 0.0, 2.0),
+                            i_spike_prob=0.02)),
+]
+
+
+@pytest.mark.parametrize("name,over", F64_SMALL, ids=[s[0] for s in F64_SMALL])
+def test_f64_mode_small(mt, name, over):
+    """Float64 mode: H is stored as float32, so the bound is a few float32 ulps
+    of |H| (1e-6 + 2e-7 |H_ref|) instead of the float32-accumulation bounds."""
+    w = _small_workload(over)
+    x = make_inputs(w)
+    H, C, n, m = _run_gpu(mt, w, x, precision="f64")
+    for b in range(w.B):
+        for h in range(w.NH):
+            Hr, Cr, nr, mr = _oracle(w, x, (b, h), fn="recurrent")
+            err = np.abs(H[b, h] - Hr)
+            assert np.all(err <= 1e-6 + 2e-7 * np.abs(Hr)), f"{name}: max|dH| {err.max():.3g}"
+            assert np.abs(C[b, h] - Cr).max() <= 1e-6 * max(1.0, np.abs(Cr).max())
+            if w.gate == "exp":
+                assert abs(m[b, h] - mr) <= 1e-6
+                assert np.abs(n[b, h] - nr).max() <= 1e-6 * max(1.0, np.abs(nr).max())
+
+
 def test_bf16_h_output(mt):
     w = _small_workload(dict(B=1, NH=2, S=400, DHQK=128, DHV=128, chunk=128))
     x = make_inputs(w)

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libmlstm_tfla.so")
 
 MLSTM_F32, MLSTM_BF16 = 0, 1
 MLSTM_GATE_EXP, MLSTM_GATE_SIG = 0, 1
-MLSTM_PREC_SPLIT, MLSTM_PREC_F16 = 0, 1
-_PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16}
+MLSTM_PREC_SPLIT, MLSTM_PREC_F16, MLSTM_PREC_F64 = 0, 1, 2
+_PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16, "f64": MLSTM_PREC_F64}
 _GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
 
 STATUS_NAMES = {

@@ -29,7 +29,8 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   if (d->qkv_dtype != MLSTM_F32 && d->qkv_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
   if (d->h_dtype != MLSTM_F32 && d->h_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
   if (d->gate != MLSTM_GATE_EXP && d->gate != MLSTM_GATE_SIG) return MLSTM_E_ARG;
-  if (d->precision != MLSTM_PREC_SPLIT && d->precision != MLSTM_PREC_F16) return MLSTM_E_ARG;
+  if (d->precision != MLSTM_PREC_SPLIT && d->precision != MLSTM_PREC_F16 && d->precision != MLSTM_PREC_F64)
+    return MLSTM_E_ARG;
   if (!isfinite(d->qk_scale) || !isfinite(d->eps) || d->eps < 0.0f) return MLSTM_E_ARG;
   if (d->B < 1 || d->NH < 1 || d->S < 0) return MLSTM_E_SHAPE;
   const bool dk_ok = d->DHQK == 64 || d->DHQK == 128 || d->DHQK == 256 || d->DHQK == 512;
@@ -58,13 +59,14 @@ struct WsLayout {
 WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   const size_t BH = (size_t)d->B * d->NH;
   const size_t Nc1 = (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
+  const size_t el = d->precision == MLSTM_PREC_F64 ? sizeof(double) : sizeof(float);
   WsLayout w;
   w.c_off = 0;
-  size_t off = round_up(BH * Nc1 * d->DHQK * d->DHV * sizeof(float), 256);
+  size_t off = round_up(BH * Nc1 * d->DHQK * d->DHV * el, 256);
   w.n_off = off;
-  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * sizeof(float), 256);
+  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * el, 256);
   w.m_off = off;
-  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * sizeof(float), 256);
+  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * el, 256);
   w.total = off;
   return w;
 }
@@ -88,6 +90,7 @@ float resolve_scale(const mlstm_fw_desc_t* d) {
 // the packed fragment layout; every other shape uses float32 row-major
 // states.  Both layouts take the same number of bytes.
 bool packed_layout(const mlstm_fw_desc_t* d) {
+  if (d->precision == MLSTM_PREC_F64) return false;
   const int tq = d->tile_lq ? d->tile_lq : 64;
   return mlstm::hintra_wide_supported(d->DHQK, d->DHV, d->chunk_size, tq, d->qkv_dtype == MLSTM_BF16);
 }
@@ -141,8 +144,10 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
   const bool sig = d->gate == MLSTM_GATE_SIG;
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
-  const hipError_t e = packed_layout(d) ? mlstm::launch_states_wide(p, sig, split, stream)
-                                        : mlstm::launch_states(p, bf16, sig, split, stream);
+  hipError_t e;
+  if (d->precision == MLSTM_PREC_F64) e = mlstm::launch_states_f64(p, bf16, sig, stream);
+  else if (packed_layout(d)) e = mlstm::launch_states_wide(p, sig, split, stream);
+  else e = mlstm::launch_states(p, bf16, sig, split, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
@@ -176,8 +181,10 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
   const bool sig = d->gate == MLSTM_GATE_SIG;
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
-  const hipError_t e = packed_layout(d) ? mlstm::launch_hintra_wide(p, sig, split, stream)
-                                        : mlstm::launch_hintra(p, bf16, sig, split, stream);
+  hipError_t e;
+  if (d->precision == MLSTM_PREC_F64) e = mlstm::launch_hintra_f64(p, bf16, sig, stream);
+  else if (packed_layout(d)) e = mlstm::launch_hintra_wide(p, sig, split, stream);
+  else e = mlstm::launch_hintra(p, bf16, sig, split, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
@@ -255,6 +262,12 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, s
   const long long n = (long long)desc->B * desc->NH * (mlstm_fw_num_chunks(desc) + 1);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (desc->precision == MLSTM_PREC_F64) {
+    if (C_states) e = mlstm::launch_narrow_f64(ws.C, C_states, n * desc->DHQK * desc->DHV, s);
+    if (e == hipSuccess && n_states) e = mlstm::launch_narrow_f64(ws.n, n_states, n * desc->DHQK, s);
+    if (e == hipSuccess && m_states) e = mlstm::launch_narrow_f64(ws.m, m_states, n, s);
+    return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+  }
   if (C_states) {
     if (packed_layout(desc)) {
       e = mlstm::launch_unpack_states(ws.C, C_states, n, desc->DHQK, desc->DHV, s);

@@ -55,6 +55,10 @@ hipError_t launch_hintra_wide(const HintraParams& p, bool sig, bool split, hipSt
 // Wide-tile states kernel: writes the chunk states in the packed fragment
 // layout read by the wide intra-chunk kernel.
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream);
+// Float64 precision mode: both stages in fp64, states kept in fp64.
+hipError_t launch_states_f64(const StatesParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
+hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
+hipError_t launch_narrow_f64(const void* src, float* dst, long long n, hipStream_t stream);
 // Packed states (n_states x DK x DV) -> float32.
 hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
                                 hipStream_t stream);
