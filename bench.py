@@ -93,6 +93,9 @@ def main(argv=None) -> int:
     ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, --steps times (the "
+                         "reference reading for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -107,6 +110,19 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t) / args.steps
+        print(json.dumps({"copy_bytes": 4 * n, "steps": args.steps, "ms_per_copy": dt * 1e3,
+                          "GB/s (read+write)": 8 * n / dt / 1e9}), flush=True)
+        return 0
     mt.lib()  # fail loudly if the HIP library is missing
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)

@@ -311,22 +311,12 @@ __device__ __forceinline__ half8_t bf16x8_to_f16x8(uint4 u) {
 // Packed chunk-state layout shared by the wide states and intra-chunk kernels.
 // One state (DK x DV) is stored as (DK/16) x (DV/32) fragments of a 16-row k
 // step and a 32-column block; each fragment is a hi plane then a lo plane of
-// 64 lanes x 8 fp16 values (2 x 1 KiB).  Lane l holds column 32*nb + l % 32;
+// 64 lanes x 8 bf16 values (2 x 1 KiB).  Lane l holds column 32*nb + l % 32;
 // slot e holds row 16*kk + (e < 4 ? 4*(l/32) + e : 8 + 4*(l/32) + e - 4), the
 // row order of a 32x32 accumulator half.  hi + lo reproduces the float32
-// state to about 22 significant bits.
+// state to about 16 significant bits.
 __device__ __forceinline__ size_t pack_frag_offset(int kk, int nb, int plane, int DV) {
   return ((size_t)(kk * (DV / 32) + nb) * 2 + plane) * 512;
-}
-
-__device__ __forceinline__ float unpack_state_elem(const _Float16* P, int k, int v, int DV) {
-  const int kk = k >> 4, kr = k & 15, nb = v >> 5, col = v & 31;
-  const int h = (kr & 7) >> 2;
-  const int e = (kr < 8 ? 0 : 4) + (kr & 3);
-  const int lane = 32 * h + col;
-  const float hi = static_cast<float>(P[pack_frag_offset(kk, nb, 0, DV) + lane * 8 + e]);
-  const float lo = static_cast<float>(P[pack_frag_offset(kk, nb, 1, DV) + lane * 8 + e]);
-  return hi + lo;
 }
 
 // 4 bf16 (8 bytes) -> 4 fp16.
@@ -337,6 +327,66 @@ __device__ __forceinline__ half4_t bf16x4_to_f16x4(uint2 u) {
   f[2] = static_cast<_Float16>(__uint_as_float(u.y << 16));
   f[3] = static_cast<_Float16>(__uint_as_float(u.y & 0xffff0000u));
   return f;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 matrix-core operands (wide kernels).  Inputs Q, K, V feed the bf16
+// MFMAs unchanged; a value computed in float32 is carried as a bf16 hi + lo
+// pair (hi = RNE(x), lo = RNE(x - hi)), about 16 significant bits.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float16_t mma32b(const bf16x8_t& a, const bf16x8_t& b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mma16b(const bf16x8_t& a, const bf16x8_t& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 hi and lo words (low half = first value).
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  bf16x2_t h;
+  h[0] = static_cast<__bf16>(x0);
+  h[1] = static_cast<__bf16>(x1);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  bf16x2_t l;
+  l[0] = static_cast<__bf16>(x0 - h0);
+  l[1] = static_cast<__bf16>(x1 - h1);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+__device__ __forceinline__ uint32_t round_bf16x2(float x0, float x1) {
+  bf16x2_t h;
+  h[0] = static_cast<__bf16>(x0);
+  h[1] = static_cast<__bf16>(x1);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// 16-bit fragment helpers on raw storage (bit patterns only).
+__device__ __forceinline__ uint4 frag_tr_u(const uint16_t* X, int ld, int k0, int c0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const uint16_t* base = X + (k0 + 8 * (grp >> 1) + (j >> 2)) * ld + c0 + 16 * (grp & 1) + 4 * (j & 3);
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(base));
+  const short4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(base + 4 * ld));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+__device__ __forceinline__ uint4 frag_row_u(const uint16_t* X, int ld, int r0, int k0, int lane) {
+  return *reinterpret_cast<const uint4*>(X + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ float unpack_state_elem_bf16(const uint16_t* P, int k, int v, int DV) {
+  const int kk = k >> 4, kr = k & 15, nb = v >> 5, col = v & 31;
+  const int h = (kr & 7) >> 2;
+  const int e = (kr < 8 ? 0 : 4) + (kr & 3);
+  const int lane = 32 * h + col;
+  const float hi = bf16_to_f32(P[pack_frag_offset(kk, nb, 0, DV) + lane * 8 + e]);
+  const float lo = bf16_to_f32(P[pack_frag_offset(kk, nb, 1, DV) + lane * 8 + e]);
+  return hi + lo;
 }
 
 }  // namespace mlstm

@@ -5,15 +5,18 @@
 // the max-state), organised for the large head dimensions:
 //   * one workgroup (8 waves) computes TQ rows x all DV columns of H for one
 //     chunk of one head, so the score tile Q.K^T is formed once;
-//   * P.V and Q.C use 32x32x16 fp16 matrix-core tiles; each wave owns a
-//     64-row x (DV / (8 * 64 / TQ))-column block of H in accumulators;
+//   * all products run on bf16 matrix cores: Q, K, V enter unchanged, and each
+//     operand computed in float32 (P = s.S.decay, the chunk state C) is carried
+//     as a bf16 hi + lo pair, two MFMA passes;
+//   * P.V and Q.C use 32x32x16 tiles; each wave owns a 64-row x
+//     (DV / (8 * 64 / TQ))-column block of H in accumulators;
 //   * the chunk state C arrives packed in matrix-core fragment order (written
-//     so by the wide states kernel) and is loaded straight into registers;
+//     so by the wide states kernel) and is loaded straight into registers,
+//     several k steps ahead;
 //   * K and V are staged in LDS row-major; V is read back transposed with
 //     ds_read_b64_tr_b16 since the P.V contraction runs down its rows;
 //   * the score tile is computed transposed with 16x16x32 tiles (each wave
-//     16 rows), turned into P = s.S.decay, split into fp16 hi + lo planes and
-//     shared through LDS as the A operand of P.V.
+//     16 rows), turned into P, and shared through LDS as hi and lo planes.
 // Keys are taken 64 at a time.
 #include "device_common.h"
 #include "kernels.h"
@@ -30,7 +33,11 @@ struct Wide {
   static constexpr int NWC = NW / NWR;     // waves along columns
   static constexpr int WC = DV / NWC;      // columns per wave
   static constexpr int CB = WC / 32;       // 32-column blocks per wave
-  static constexpr int LDK = DK + 8, LDV = DV + 8, LDP = TKV + 8;
+  // Row strides (elements).  K and P are read along rows (16-byte reads, a
+  // stride of 4 banks mod 64 keeps 16 rows conflict-free); V is read down its
+  // rows with the transposing read (4 rows x 32 bytes per 16 lanes: a stride
+  // of 8 banks mod 64 keeps them apart).
+  static constexpr int LDK = DK + 8, LDV = DV + 16, LDP = TKV + 8;
   static constexpr int K_ELEMS = TKV * LDK;
   static constexpr int P_ELEMS = TQ * LDP;   // one plane
   static constexpr int V_ELEMS = TKV * LDV;
@@ -43,16 +50,17 @@ template <int DK, int DV, int TQ, bool SIG, bool SPLIT>
 __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) {
   typedef Wide<DK, DV, TQ> W;
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
+  constexpr int NKK = DK / 16;  // 32x32x16 steps over DK
 
   __shared__ float s_b2[kMaxL];
   __shared__ float s_u2[kMaxL];
   __shared__ float s_red[W::NW];
   __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ], s_row_den[TQ], s_den2[TQ];
   __shared__ float s_n[DK];
-  __shared__ __align__(16) _Float16 s_k[W::K_ELEMS];
-  __shared__ __align__(16) _Float16 s_ph[W::P_ELEMS];
-  __shared__ __align__(16) _Float16 s_pl[W::P_ELEMS];
-  __shared__ __align__(16) _Float16 s_v[W::V_ELEMS];
+  __shared__ __align__(16) uint16_t s_k[W::K_ELEMS];
+  __shared__ __align__(16) uint16_t s_ph[W::P_ELEMS];
+  __shared__ __align__(16) uint16_t s_pl[W::P_ELEMS];
+  __shared__ __align__(16) uint16_t s_v[W::V_ELEMS];
 
   const int NQT = p.L / TQ;
   // Workgroups are dealt round-robin to the 8 XCDs; remap so that the row
@@ -81,6 +89,34 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV;
   const float* ig = p.i_pre + (size_t)bh * S + t0;
   const float* fg = p.f_pre + (size_t)bh * S + t0;
+
+  // P.V / Q.C role: rows wr0 .. wr0+63, columns wc0 .. wc0+WC-1.
+  const int wr0 = (wave / W::NWC) * 64;
+  const int wc0 = (wave % W::NWC) * W::WC;
+
+  // ---- issue the first state / Q fragment loads before the gate math
+  const uint16_t* Pst = reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
+  constexpr int PD = W::CB >= 4 ? 1 : 3;  // k steps loaded ahead
+  uint4 bb[NKK][W::CB][2];
+  uint4 qa[NKK][2];
+  auto load_k = [&](int kk) {
+#pragma unroll
+    for (int cb = 0; cb < W::CB; ++cb) {
+      const int nb = (wc0 + 32 * cb) >> 5;
+      bb[kk][cb][0] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 0, DV) + lane * 8);
+      if constexpr (SPLIT) bb[kk][cb][1] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 1, DV) + lane * 8);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = row0 + wr0 + 32 * rb + l32;
+      const uint16_t* qp = Q + (size_t)row * DK + 16 * kk + 4 * h2;
+      const uint2 x0 = row < Lc ? *reinterpret_cast<const uint2*>(qp) : make_uint2(0, 0);
+      const uint2 x1 = row < Lc ? *reinterpret_cast<const uint2*>(qp + 8) : make_uint2(0, 0);
+      qa[kk][rb] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    }
+  };
+#pragma unroll
+  for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(kk);
 
   // ---- gates over chunk positions [0, kend): b (inclusive cumsum of log-forget),
   // u = input term - b (log2 units), prefix max of u.
@@ -146,33 +182,9 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const int sr = (TQ == 128) ? wave : (wave & 3);
   const int skb0 = (TQ == 128) ? 0 : 2 * (wave >> 2);
   const int srow = sr * 16 + l16;  // row of this lane in the transposed score tile
-  // Q rows as B fragments of K.Q^T (16x16x32): Q[srow][32 ks + 8 g4 + e]
-  half8_t qs[NKS];
-  {
-    const bool ok = row0 + srow < Lc;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 u = ok ? *reinterpret_cast<const uint4*>(Q + (size_t)(row0 + srow) * DK + 32 * ks + 8 * g4)
-                   : make_uint4(0, 0, 0, 0);
-      qs[ks] = bf16x8_to_f16x8(u);
-    }
-  }
-  float den_part = 0.0f;
-  if constexpr (!SIG) {
-    if (skb0 == 0) {
-      float d = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += static_cast<float>(qs[ks][e]) * s_n[32 * ks + 8 * g4 + e];
-      }
-      den_part = d * scale * s_row_w[srow];
-    }
-  }
+  const bool srow_ok = row0 + srow < Lc;
+  const uint16_t* qrow_ptr = Q + (size_t)(row0 + srow) * DK + 8 * g4;
 
-  // P.V / Q.C role: rows wr0 .. wr0+63, columns wc0 .. wc0+WC-1.
-  const int wr0 = (wave / W::NWC) * 64;
-  const int wc0 = (wave % W::NWC) * W::WC;
   float16_t acc[2][W::CB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -181,80 +193,56 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
-  // ---- inter-chunk term: acc = Q . C.  The state comes packed as matrix-core
-  // B fragments (hi and lo planes) and is read straight from memory, one k step
-  // ahead; the Q rows use the same contraction-slot order as the packed state.
-  {
-    const _Float16* Pst = reinterpret_cast<const _Float16*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
-    constexpr int NKK = DK / 16;
-    uint4 bcur[W::CB][2], bnext[W::CB][2];
-    uint2 qcur[2][2], qnext[2][2];
-    auto load_k = [&](int kk, uint4 (&bb)[W::CB][2], uint2 (&qq)[2][2]) {
+  // ---- inter-chunk term: acc = Q . C with the packed state fragments; the Q
+  // rows use the same contraction-slot order as the packed state.
 #pragma unroll
-      for (int cb = 0; cb < W::CB; ++cb) {
-        const int nb = (wc0 + 32 * cb) >> 5;
-        bb[cb][0] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 0, DV) + lane * 8);
-        if constexpr (SPLIT) bb[cb][1] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 1, DV) + lane * 8);
-      }
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (kk + PD < NKK) load_k(kk + PD);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = row0 + wr0 + 32 * rb + l32;
-        const uint16_t* qp = Q + (size_t)row * DK + 16 * kk + 4 * h2;
-        qq[rb][0] = row < Lc ? *reinterpret_cast<const uint2*>(qp) : make_uint2(0, 0);
-        qq[rb][1] = row < Lc ? *reinterpret_cast<const uint2*>(qp + 8) : make_uint2(0, 0);
-      }
-    };
-    load_k(0, bcur, qcur);
-#pragma unroll 2
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (kk + 1 < NKK) load_k(kk + 1, bnext, qnext);
-      half8_t a[2];
+    for (int cb = 0; cb < W::CB; ++cb) {
+      const bf16x8_t bh_ = as_bf16x8(bb[kk][cb][0]);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const half4_t lo4 = bf16x4_to_f16x4(qcur[rb][0]);
-        const half4_t hi4 = bf16x4_to_f16x4(qcur[rb][1]);
-        a[rb][0] = lo4[0]; a[rb][1] = lo4[1]; a[rb][2] = lo4[2]; a[rb][3] = lo4[3];
-        a[rb][4] = hi4[0]; a[rb][5] = hi4[1]; a[rb][6] = hi4[2]; a[rb][7] = hi4[3];
-      }
+      for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(as_bf16x8(qa[kk][rb]), bh_, acc[rb][cb]);
+      if constexpr (SPLIT) {
+        const bf16x8_t bl_ = as_bf16x8(bb[kk][cb][1]);
 #pragma unroll
-      for (int cb = 0; cb < W::CB; ++cb) {
-        const half8_t bh_ = __builtin_bit_cast(half8_t, bcur[cb][0]);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32(a[rb], bh_, acc[rb][cb]);
-        if constexpr (SPLIT) {
-          const half8_t bl_ = __builtin_bit_cast(half8_t, bcur[cb][1]);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32(a[rb], bl_, acc[rb][cb]);
-        }
-      }
-      if (kk + 1 < NKK) {
-#pragma unroll
-        for (int cb = 0; cb < W::CB; ++cb) {
-          bcur[cb][0] = bnext[cb][0];
-          bcur[cb][1] = bnext[cb][1];
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          qcur[rb][0] = qnext[rb][0];
-          qcur[rb][1] = qnext[rb][1];
-        }
+        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(as_bf16x8(qa[kk][rb]), bl_, acc[rb][cb]);
       }
     }
-    // scale row by e^{b + M - m} * s
+  }
+  // scale row by e^{b + M - m} * s
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float w = s_row_w[row] * scale;
+    for (int r = 0; r < 16; ++r) {
+      const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      const float w = s_row_w[row] * scale;
 #pragma unroll
-        for (int cb = 0; cb < W::CB; ++cb) acc[rb][cb][r] *= w;
+      for (int cb = 0; cb < W::CB; ++cb) acc[rb][cb][r] *= w;
+    }
+
+  // normaliser contribution of the state: s e^{b + M - m} q . n
+  float den_part = 0.0f;
+  if constexpr (!SIG) {
+    if (skb0 == 0 && srow_ok) {
+      float d = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 u = *reinterpret_cast<const uint4*>(qrow_ptr + 32 * ks);
+        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d += __uint_as_float(ww[e] << 16) * s_n[32 * ks + 8 * g4 + 2 * e];
+          d += __uint_as_float(ww[e] & 0xffff0000u) * s_n[32 * ks + 8 * g4 + 2 * e + 1];
+        }
       }
+      den_part = d * scale * s_row_w[srow];
+    }
   }
 
   // ---- intra-chunk term over key tiles [0, kend)
   const float r2 = s_row_r2[srow];
-  const int tau = row0 + srow;  // chunk row of this lane in the score tile
+  const int tau = row0 + srow;
   const int ntiles = (kend + W::TKV - 1) / W::TKV;
   // K and V tiles (64 rows) are prefetched into registers one tile ahead.
   constexpr int KPT = W::TKV * DK / 8 / W::NT;  // 16-byte K loads per thread
@@ -278,20 +266,25 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     }
   };
   if (ntiles > 0) load_kv(0);
+  // this lane's Q row as B fragments of the transposed score tile
+  uint4 qs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qs[ks] = srow_ok ? *reinterpret_cast<const uint4*>(qrow_ptr + 32 * ks) : make_uint4(0, 0, 0, 0);
+
   for (int j = 0; j < ntiles; ++j) {
     const int s0 = j * W::TKV;
-    // stage K rows (64 x DK) and V rows (64 x DV) as fp16, row-major
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * W::NT;
       const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-      *reinterpret_cast<half8_t*>(s_k + rr * W::LDK + cc) = bf16x8_to_f16x8(kpre[i]);
+      *reinterpret_cast<uint4*>(s_k + rr * W::LDK + cc) = kpre[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int idx = tid + i * W::NT;
       const int rr = idx / (DV / 8), cc = (idx % (DV / 8)) * 8;
-      *reinterpret_cast<half8_t*>(s_v + rr * W::LDV + cc) = bf16x8_to_f16x8(vpre[i]);
+      *reinterpret_cast<uint4*>(s_v + rr * W::LDV + cc) = vpre[i];
     }
     if (j + 1 < ntiles) load_kv(s0 + W::TKV);
     __syncthreads();
@@ -306,23 +299,28 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       if (live) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const half8_t a = *reinterpret_cast<const half8_t*>(s_k + (16 * sb + l16) * W::LDK + 32 * ks + 8 * g4);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qs[ks], sacc, 0, 0, 0);
+          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * sb + l16) * W::LDK + 32 * ks + 8 * g4);
+          sacc = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc);
         }
       }
-      half4_t ph, pl;
+      float val[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int sg = key0 + 4 * g4 + r;
-        float val = 0.0f;
-        if (live && sg <= tau && tau < kend) val = scale * sacc[r] * exp2f(r2 + s_u2[sg]);
-        den_part += val;
-        const _Float16 hh = static_cast<_Float16>(val);
-        ph[r] = hh;
-        pl[r] = static_cast<_Float16>(val - static_cast<float>(hh));
+        val[r] = 0.0f;
+        if (live && sg <= tau && tau < kend) val[r] = scale * sacc[r] * __builtin_amdgcn_exp2f(r2 + s_u2[sg]);
+        den_part += val[r];
       }
-      *reinterpret_cast<half4_t*>(s_ph + srow * W::LDP + 16 * sb + 4 * g4) = ph;
-      if constexpr (SPLIT) *reinterpret_cast<half4_t*>(s_pl + srow * W::LDP + 16 * sb + 4 * g4) = pl;
+      uint2 ph, pl;
+      if constexpr (SPLIT) {
+        split_bf16x2(val[0], val[1], ph.x, pl.x);
+        split_bf16x2(val[2], val[3], ph.y, pl.y);
+        *reinterpret_cast<uint2*>(s_pl + srow * W::LDP + 16 * sb + 4 * g4) = pl;
+      } else {
+        ph.x = round_bf16x2(val[0], val[1]);
+        ph.y = round_bf16x2(val[2], val[3]);
+      }
+      *reinterpret_cast<uint2*>(s_ph + srow * W::LDP + 16 * sb + 4 * g4) = ph;
     }
     __syncthreads();
 
@@ -331,19 +329,19 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     for (int kk = 0; kk < W::TKV / 16; ++kk) {
       const int key0 = s0 + 16 * kk;
       if (key0 > row0 + wr0 + 63 || key0 >= kend) continue;  // wave-uniform: all zero
-      half8_t ah[2], al[2];
+      uint4 ah[2], al[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        ah[rb] = frag_row(s_ph, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
-        if constexpr (SPLIT) al[rb] = frag_row(s_pl, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
+        ah[rb] = frag_row_u(s_ph, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
+        if constexpr (SPLIT) al[rb] = frag_row_u(s_pl, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
       }
 #pragma unroll
       for (int cb = 0; cb < W::CB; ++cb) {
-        const half8_t bv = frag_tr(s_v, W::LDV, 16 * kk, wc0 + 32 * cb, lane);
+        const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, W::LDV, 16 * kk, wc0 + 32 * cb, lane));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          acc[rb][cb] = mma32(ah[rb], bv, acc[rb][cb]);
-          if constexpr (SPLIT) acc[rb][cb] = mma32(al[rb], bv, acc[rb][cb]);
+          acc[rb][cb] = mma32b(as_bf16x8(ah[rb]), bv, acc[rb][cb]);
+          if constexpr (SPLIT) acc[rb][cb] = mma32b(as_bf16x8(al[rb]), bv, acc[rb][cb]);
         }
       }
     }
@@ -359,7 +357,13 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       else s_den2[srow] = den_part;
     }
     __syncthreads();
-    if (TQ != 128 && tid < TQ) s_row_den[tid] += s_den2[tid];
+    if (tid < TQ) {
+      float d = s_row_den[tid];
+      if (TQ != 128) d += s_den2[tid];
+      s_row_den[tid] = d;
+      // reciprocal of the normaliser, reused for every column of the row
+      s_den2[tid] = 1.0f / (fmaxf(fabsf(d), exp2f(-s_row_m2[tid])) + p.eps);
+    }
   }
   __syncthreads();
   float* Hf = static_cast<float*>(p.H);
@@ -372,12 +376,10 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
       const int t = row0 + row;
       if (t >= Lc) continue;
-      float norm = 1.0f;
-      if constexpr (!SIG) norm = fmaxf(fabsf(s_row_den[row]), exp2f(-s_row_m2[row])) + p.eps;
+      const float inv = SIG ? 1.0f : s_den2[row];
 #pragma unroll
       for (int cb = 0; cb < W::CB; ++cb) {
-        float hv = acc[rb][cb][r];
-        if constexpr (!SIG) hv = hv / norm;
+        const float hv = acc[rb][cb][r] * inv;
         const size_t off = hbase + (size_t)t * DV + wc0 + 32 * cb + l32;
         if (p.h_bf16) Hb[off] = f32_to_bf16(hv);
         else Hf[off] = hv;

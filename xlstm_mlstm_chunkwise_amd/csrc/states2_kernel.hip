@@ -6,14 +6,16 @@
 //   C' = e^{g + M - M'} C + sum_t e^{a_t - M'} k_t v_t^T,   n' likewise
 //   (sigmoid gate: C' = e^{g} C + sum_t e^{g - b_t + log sigmoid(i_t)} k_t v_t^T)
 // Organisation:
-//   * one workgroup (4 waves) keeps a TK x TV tile of C in 32x32x16 fp16
-//     matrix-core accumulators for the whole sequence (TK = TV = 64 or 128);
-//   * each 64-step time block stages the gated keys as fp16 hi + lo planes and
-//     the values as fp16, both row-major in LDS, and reads them transposed
-//     with ds_read_b64_tr_b16 (the contraction runs over time, down the rows);
+//   * one workgroup (4 waves) keeps a TK x TV tile of C in 32x32x16 bf16
+//     matrix-core accumulators (float32) for the whole sequence (TK = TV = 64
+//     or 128);
+//   * each 64-step time block stages the gated keys as bf16 hi + lo planes
+//     (computed in float32) and the values unchanged, both row-major in LDS,
+//     and reads them transposed with ds_read_b64_tr_b16 (the contraction runs
+//     over time, down the rows);
 //   * the state entering every chunk is written in the packed layout the
 //     intra-chunk kernel consumes (see pack_offset): for every 16-row k step
-//     and 32-column block, 64 lanes x 8 fp16 values, hi plane then lo plane.
+//     and 32-column block, 64 lanes x 8 bf16 values, hi plane then lo plane.
 //     The lane and slot order is the accumulator's own, so the writes are
 //     plain 16-byte stores.
 #include "device_common.h"
@@ -29,7 +31,8 @@ template <int TK, int TV, bool SIG, bool SPLIT>
 __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) {
   constexpr int WR = TK / 2, WCOL = TV / 2;      // wave tile
   constexpr int RB = WR / 32, CB = WCOL / 32;    // 32x32 blocks per wave
-  constexpr int LDK = TK + 8, LDV = TV + 8;
+  // row strides of 8 banks mod 64 keep the 4 rows of a transposing read apart
+  constexpr int LDK = TK + 16, LDV = TV + 16;
   constexpr int KSEG = TK / 8, VSEG = TV / 8;    // 16-byte segments per row
   constexpr int KPT = kTT * KSEG / 256, VPT = kTT * VSEG / 256;
   static_assert(kTT * KSEG % 256 == 0 && kTT * VSEG % 256 == 0, "staging split");
@@ -38,9 +41,9 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
   __shared__ float s_red[4];
   __shared__ float s_g;
   __shared__ float s_np[256 / KSEG][TK];
-  __shared__ __align__(16) _Float16 s_kh[kTT * LDK];
-  __shared__ __align__(16) _Float16 s_kl[kTT * LDK];
-  __shared__ __align__(16) _Float16 s_v[kTT * LDV];
+  __shared__ __align__(16) uint16_t s_kh[kTT * LDK];
+  __shared__ __align__(16) uint16_t s_kl[kTT * LDK];
+  __shared__ __align__(16) uint16_t s_v[kTT * LDV];
 
   const int NTK = p.DK / TK, NTV = p.DV / TV;
   const int bid = blockIdx.x;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
   for (int c = 0; c <= Nc; ++c) {
     // ---- state entering chunk c, packed hi/lo fragments
     {
-      _Float16* P = reinterpret_cast<_Float16*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
+      uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
       const int NB = DV / 32;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -105,17 +108,13 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
           const int nblk = (vt * TV + wc0 + 32 * cb) / 32;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            half8_t hi, lo;
+            uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = acc[rb][cb][8 * half + e];
-              const _Float16 hh = static_cast<_Float16>(x);
-              hi[e] = hh;
-              lo[e] = static_cast<_Float16>(x - static_cast<float>(hh));
-            }
+            for (int e = 0; e < 4; ++e)
+              split_bf16x2(acc[rb][cb][8 * half + 2 * e], acc[rb][cb][8 * half + 2 * e + 1], hi[e], lo[e]);
             const size_t blk = ((size_t)(2 * kblk + half) * NB + nblk) * 2;
-            *reinterpret_cast<half8_t*>(P + (blk + 0) * 512 + lane * 8) = hi;
-            *reinterpret_cast<half8_t*>(P + (blk + 1) * 512 + lane * 8) = lo;
+            *reinterpret_cast<uint4*>(P + (blk + 0) * 512 + lane * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4*>(P + (blk + 1) * 512 + lane * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
           }
         }
       if (own_n && tid < TK) p.n_states[((size_t)bh * (Nc + 1) + c) * DK + kt * TK + tid] = nreg;
@@ -181,46 +180,43 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
         const int t = nrow + i * (256 / KSEG);
         const float w = s_w[tb + t];  // 0 beyond the chunk
         const uint32_t ww[4] = {kpre[i].x, kpre[i].y, kpre[i].z, kpre[i].w};
-        half8_t hi, lo;
+        uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x0 = __uint_as_float(ww[e] << 16) * w;
           const float x1 = __uint_as_float(ww[e] & 0xffff0000u) * w;
           np[2 * e] += x0;
           np[2 * e + 1] += x1;
-          const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
-          hi[2 * e] = h0;
-          hi[2 * e + 1] = h1;
-          lo[2 * e] = static_cast<_Float16>(x0 - static_cast<float>(h0));
-          lo[2 * e + 1] = static_cast<_Float16>(x1 - static_cast<float>(h1));
+          if constexpr (SPLIT) split_bf16x2(x0, x1, hi[e], lo[e]);
+          else hi[e] = round_bf16x2(x0, x1);
         }
-        *reinterpret_cast<half8_t*>(s_kh + t * LDK + nseg * 8) = hi;
-        if constexpr (SPLIT) *reinterpret_cast<half8_t*>(s_kl + t * LDK + nseg * 8) = lo;
+        *reinterpret_cast<uint4*>(s_kh + t * LDK + nseg * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        if constexpr (SPLIT) *reinterpret_cast<uint4*>(s_kl + t * LDK + nseg * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
       }
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const int idx = tid + i * 256;
         const int t = idx / VSEG, sg = idx % VSEG;
-        *reinterpret_cast<half8_t*>(s_v + t * LDV + sg * 8) = bf16x8_to_f16x8(vpre[i]);
+        *reinterpret_cast<uint4*>(s_v + t * LDV + sg * 8) = vpre[i];
       }
       if (tb + kTT < Lc) load_kv(t0, tb + kTT, Lc);
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < kTT / 16; ++ks) {
         if (tb + 16 * ks >= Lc) break;  // uniform: rest of the block is padding
-        half8_t ah[RB], al[RB];
+        bf16x8_t ah[RB], al[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          ah[rb] = frag_tr(s_kh, LDK, 16 * ks, wr0 + 32 * rb, lane);
-          if constexpr (SPLIT) al[rb] = frag_tr(s_kl, LDK, 16 * ks, wr0 + 32 * rb, lane);
+          ah[rb] = as_bf16x8(frag_tr_u(s_kh, LDK, 16 * ks, wr0 + 32 * rb, lane));
+          if constexpr (SPLIT) al[rb] = as_bf16x8(frag_tr_u(s_kl, LDK, 16 * ks, wr0 + 32 * rb, lane));
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const half8_t bv = frag_tr(s_v, LDV, 16 * ks, wc0 + 32 * cb, lane);
+          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, LDV, 16 * ks, wc0 + 32 * cb, lane));
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            acc[rb][cb] = mma32(ah[rb], bv, acc[rb][cb]);
-            if constexpr (SPLIT) acc[rb][cb] = mma32(al[rb], bv, acc[rb][cb]);
+            acc[rb][cb] = mma32b(ah[rb], bv, acc[rb][cb]);
+            if constexpr (SPLIT) acc[rb][cb] = mma32b(al[rb], bv, acc[rb][cb]);
           }
         }
       }
@@ -264,14 +260,14 @@ hipError_t launch_t(const StatesParams& p, hipStream_t stream) {
 }
 
 // Packed state -> float32 (B, NH, N_c + 1, DK, DV).
-__global__ __launch_bounds__(256) void unpack_states_kernel(const _Float16* P, float* C, long long total, int DK,
+__global__ __launch_bounds__(256) void unpack_states_kernel(const uint16_t* P, float* C, long long total, int DK,
                                                             int DV) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const long long per = (long long)DK * DV;
   const long long s = i / per;
   const int k = (int)((i % per) / DV), v = (int)(i % DV);
-  C[i] = unpack_state_elem(P + s * per * 2, k, v, DV);
+  C[i] = unpack_state_elem_bf16(P + s * per * 2, k, v, DV);
 }
 
 }  // namespace
@@ -293,7 +289,7 @@ hipError_t launch_unpack_states(const void* packed, float* C, long long n_states
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(unpack_states_kernel, dim3(blocks), dim3(256), 0, stream,
-                     static_cast<const _Float16*>(packed), C, total, DK, DV);
+                     static_cast<const uint16_t*>(packed), C, total, DK, DV);
   return hipGetLastError();
 }
 
