@@ -91,6 +91,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="bf16_7b_s8192")
     ap.add_argument("--precision", default="split", choices=["split", "f16"])
     ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--tile-lq", type=int, default=None, help="override the workload's intra-chunk row tile")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -125,6 +126,8 @@ def main(argv=None) -> int:
         return 0
     mt.lib()  # fail loudly if the HIP library is missing
     w = WORKLOADS[args.workload]
+    if args.tile_lq is not None:
+        w = w.replace(tile_lq=args.tile_lq)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
@@ -223,7 +226,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
                    "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
-                   "precision": args.precision},
+                   "precision": args.precision, "tile_lq": w.tile_lq or 64},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "wall_ms_per_step": wall_ms,

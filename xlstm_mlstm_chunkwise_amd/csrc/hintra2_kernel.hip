@@ -3,13 +3,15 @@
 // Same arithmetic as hintra_kernel.hip (TFLA abstract: second level of
 // sequence tiling inside each chunk; mLSTM readout with the normaliser and
 // the max-state), organised for the large head dimensions:
-//   * one workgroup (8 waves) computes TQ rows x all DV columns of H for one
-//     chunk of one head, so the score tile Q.K^T is formed once;
+//   * one workgroup (8 waves) computes TQ rows x TV columns of H for one chunk
+//     of one head (TV = DV, or DV / 2 with 128-row tiles, which halves how
+//     often the chunk state is read at the cost of forming the score tile
+//     twice);
 //   * all products run on bf16 matrix cores: Q, K, V enter unchanged, and each
 //     operand computed in float32 (P = s.S.decay, the chunk state C) is carried
 //     as a bf16 hi + lo pair, two MFMA passes;
 //   * P.V and Q.C use 32x32x16 tiles; each wave owns a 64-row x
-//     (DV / (8 * 64 / TQ))-column block of H in accumulators;
+//     (TV / (8 * 64 / TQ))-column block of H in accumulators;
 //   * the chunk state C arrives packed in matrix-core fragment order (written
 //     so by the wide states kernel) and is loaded straight into registers,
 //     several k steps ahead;
@@ -26,29 +28,33 @@ namespace {
 
 constexpr int kMaxL = 1024;
 
-template <int DK, int DV, int TQ>
+template <int DK, int TV, int TQ>
 struct Wide {
   static constexpr int NW = 8, NT = 512, TKV = 64;
   static constexpr int NWR = TQ / 64;      // waves along rows (64 rows each)
   static constexpr int NWC = NW / NWR;     // waves along columns
-  static constexpr int WC = DV / NWC;      // columns per wave
+  static constexpr int WC = TV / NWC;      // columns per wave
   static constexpr int CB = WC / 32;       // 32-column blocks per wave
   // Row strides (elements).  K and P are read along rows (16-byte reads, a
   // stride of 4 banks mod 64 keeps 16 rows conflict-free); V is read down its
   // rows with the transposing read (4 rows x 32 bytes per 16 lanes: a stride
   // of 8 banks mod 64 keeps them apart).
-  static constexpr int LDK = DK + 8, LDV = DV + 16, LDP = TKV + 8;
+  static constexpr int LDK = DK + 8, LDV = TV + 16, LDP = TKV + 8, LDQ = DK + 8;
   static constexpr int K_ELEMS = TKV * LDK;
   static constexpr int P_ELEMS = TQ * LDP;   // one plane
   static constexpr int V_ELEMS = TKV * LDV;
+  static constexpr int Q_ELEMS = TQ * LDQ;   // shares the K/P/V space before the key loop
+  static constexpr int BUF_ELEMS = (K_ELEMS + 2 * P_ELEMS + V_ELEMS) > Q_ELEMS ? (K_ELEMS + 2 * P_ELEMS + V_ELEMS)
+                                                                                 : Q_ELEMS;
   static constexpr int SKB = (TQ == 128) ? 4 : 2;  // 16-key score blocks per wave
-  static_assert(CB >= 1 && WC % 32 == 0, "DV too small for this tile");
+  static_assert(CB >= 1 && WC % 32 == 0, "TV too small for this tile");
   static_assert(DK % 32 == 0, "DHQK must be a multiple of 32");
 };
 
-template <int DK, int DV, int TQ, bool SIG, bool SPLIT>
+template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT>
 __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) {
-  typedef Wide<DK, DV, TQ> W;
+  typedef Wide<DK, TV, TQ> W;
+  constexpr int NVT = DV / TV;
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
   constexpr int NKK = DK / 16;  // 32x32x16 steps over DK
 
@@ -57,18 +63,23 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   __shared__ float s_red[W::NW];
   __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ], s_row_den[TQ], s_den2[TQ];
   __shared__ float s_n[DK];
-  __shared__ __align__(16) uint16_t s_k[W::K_ELEMS];
-  __shared__ __align__(16) uint16_t s_ph[W::P_ELEMS];
-  __shared__ __align__(16) uint16_t s_pl[W::P_ELEMS];
-  __shared__ __align__(16) uint16_t s_v[W::V_ELEMS];
+  __shared__ __align__(16) uint16_t s_buf[W::BUF_ELEMS];
+  uint16_t* const s_k = s_buf;
+  uint16_t* const s_ph = s_buf + W::K_ELEMS;
+  uint16_t* const s_pl = s_ph + W::P_ELEMS;
+  uint16_t* const s_v = s_pl + W::P_ELEMS;
+  uint16_t* const s_q = s_buf;  // the Q tile, before the key loop
 
   const int NQT = p.L / TQ;
-  // Workgroups are dealt round-robin to the 8 XCDs; remap so that the row
-  // tiles of one chunk (which read the same state, keys and values) are
+  // Workgroups are dealt round-robin to the 8 XCDs; remap so that the tiles
+  // of one chunk (which read the same state, keys and values) are
   // consecutive on one XCD and share its L2.
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int vt = bid % NVT;
+  bid /= NVT;
+  const int v0 = vt * TV;
   const int qt = bid % NQT;
   bid /= NQT;
   const int c = bid % p.Nc;
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 
   const uint16_t* Q = static_cast<const uint16_t*>(p.Q) + ((size_t)bh * S + t0) * DK;
   const uint16_t* K = static_cast<const uint16_t*>(p.K) + ((size_t)bh * S + t0) * DK;
-  const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV;
+  const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV + v0;
   const float* ig = p.i_pre + (size_t)bh * S + t0;
   const float* fg = p.f_pre + (size_t)bh * S + t0;
 
@@ -94,25 +105,36 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const int wr0 = (wave / W::NWC) * 64;
   const int wc0 = (wave % W::NWC) * W::WC;
 
+  // Score-tile role of this wave: 16 rows (row block sr) x SKB key blocks.
+  const int sr = (TQ == 128) ? wave : (wave & 3);
+  const int skb0 = (TQ == 128) ? 0 : 2 * (wave >> 2);
+  const int srow = sr * 16 + l16;  // row of this lane in the transposed score tile
+  const bool srow_ok = row0 + srow < Lc;
+  // The Q tile (TQ x DK) is requested now, overlapping the gate math, and
+  // staged once in LDS for both the inter-chunk product and the score tile.
+  constexpr int QPT = TQ * DK / 8 / W::NT;  // 16-byte loads per thread
+  static_assert(TQ * DK / 8 % W::NT == 0, "Q tile split");
+  uint4 qpre[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + i * W::NT;
+    const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+    qpre[i] = (row0 + rr < Lc) ? *reinterpret_cast<const uint4*>(Q + (size_t)(row0 + rr) * DK + cc)
+                               : make_uint4(0, 0, 0, 0);
+  }
+  float mprev = 0.0f;
+  if constexpr (!SIG) mprev = p.m_states[(size_t)bh * (Nc + 1) + c];
+
   // ---- issue the first state / Q fragment loads before the gate math
   const uint16_t* Pst = reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
   constexpr int PD = W::CB >= 4 ? 1 : 3;  // k steps loaded ahead
   uint4 bb[NKK][W::CB][2];
-  uint4 qa[NKK][2];
   auto load_k = [&](int kk) {
 #pragma unroll
     for (int cb = 0; cb < W::CB; ++cb) {
-      const int nb = (wc0 + 32 * cb) >> 5;
+      const int nb = (v0 + wc0 + 32 * cb) >> 5;
       bb[kk][cb][0] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 0, DV) + lane * 8);
       if constexpr (SPLIT) bb[kk][cb][1] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 1, DV) + lane * 8);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = row0 + wr0 + 32 * rb + l32;
-      const uint16_t* qp = Q + (size_t)row * DK + 16 * kk + 4 * h2;
-      const uint2 x0 = row < Lc ? *reinterpret_cast<const uint2*>(qp) : make_uint2(0, 0);
-      const uint2 x1 = row < Lc ? *reinterpret_cast<const uint2*>(qp + 8) : make_uint2(0, 0);
-      qa[kk][rb] = make_uint4(x0.x, x0.y, x1.x, x1.y);
     }
   };
 #pragma unroll
@@ -159,7 +181,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           s_row_w[tid] = exp2f(b2);
           s_row_m2[tid] = 0.0f;
         } else {
-          const float M2 = p.m_states[(size_t)bh * (Nc + 1) + c] * kLog2e;
+          const float M2 = mprev * kLog2e;
           const float mx = fmaxf(M2, s_row_m2[tid]);
           s_row_r2[tid] = -mx;
           s_row_w[tid] = exp2f(M2 - mx);
@@ -175,15 +197,19 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       const float* nst = p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
       for (int k = tid; k < DK; k += W::NT) s_n[k] = nst[k];
     }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int idx = tid + i * W::NT;
+      const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+      *reinterpret_cast<uint4*>(s_q + rr * W::LDQ + cc) = qpre[i];
+    }
     __syncthreads();
   }
+  // this lane's Q row as B fragments of the transposed score tile
+  uint4 qs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qs[ks] = *reinterpret_cast<const uint4*>(s_q + srow * W::LDQ + 32 * ks + 8 * g4);
 
-  // Score-tile role of this wave: 16 rows (row block sr) x SKB key blocks.
-  const int sr = (TQ == 128) ? wave : (wave & 3);
-  const int skb0 = (TQ == 128) ? 0 : 2 * (wave >> 2);
-  const int srow = sr * 16 + l16;  // row of this lane in the transposed score tile
-  const bool srow_ok = row0 + srow < Lc;
-  const uint16_t* qrow_ptr = Q + (size_t)(row0 + srow) * DK + 8 * g4;
 
   float16_t acc[2][W::CB];
 #pragma unroll
@@ -198,18 +224,27 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     if (kk + PD < NKK) load_k(kk + PD);
+    bf16x8_t qa[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const uint16_t* qp = s_q + (wr0 + 32 * rb + l32) * W::LDQ + 16 * kk + 4 * h2;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(qp);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 8);
+      qa[rb] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+    }
 #pragma unroll
     for (int cb = 0; cb < W::CB; ++cb) {
       const bf16x8_t bh_ = as_bf16x8(bb[kk][cb][0]);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(as_bf16x8(qa[kk][rb]), bh_, acc[rb][cb]);
+      for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bh_, acc[rb][cb]);
       if constexpr (SPLIT) {
         const bf16x8_t bl_ = as_bf16x8(bb[kk][cb][1]);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(as_bf16x8(qa[kk][rb]), bl_, acc[rb][cb]);
+        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bl_, acc[rb][cb]);
       }
     }
   }
+  __syncthreads();  // the Q tile's LDS is reused for K, P and V below
   // scale row by e^{b + M - m} * s
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -228,7 +263,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       float d = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow_ptr + 32 * ks);
+        const uint4 u = qs[ks];
         const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -246,8 +281,8 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const int ntiles = (kend + W::TKV - 1) / W::TKV;
   // K and V tiles (64 rows) are prefetched into registers one tile ahead.
   constexpr int KPT = W::TKV * DK / 8 / W::NT;  // 16-byte K loads per thread
-  constexpr int VPT = W::TKV * DV / 8 / W::NT;  // 16-byte V loads per thread
-  static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * DV / 8 % W::NT == 0, "tile split");
+  constexpr int VPT = W::TKV * TV / 8 / W::NT;  // 16-byte V loads per thread
+  static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * TV / 8 % W::NT == 0, "tile split");
   uint4 kpre[KPT], vpre[VPT];
   auto load_kv = [&](int s0) {
 #pragma unroll
@@ -260,17 +295,12 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int idx = tid + i * W::NT;
-      const int rr = idx / (DV / 8), cc = (idx % (DV / 8)) * 8;
+      const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
       vpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc)
                                : make_uint4(0, 0, 0, 0);
     }
   };
   if (ntiles > 0) load_kv(0);
-  // this lane's Q row as B fragments of the transposed score tile
-  uint4 qs[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qs[ks] = srow_ok ? *reinterpret_cast<const uint4*>(qrow_ptr + 32 * ks) : make_uint4(0, 0, 0, 0);
 
   for (int j = 0; j < ntiles; ++j) {
     const int s0 = j * W::TKV;
@@ -283,7 +313,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int idx = tid + i * W::NT;
-      const int rr = idx / (DV / 8), cc = (idx % (DV / 8)) * 8;
+      const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
       *reinterpret_cast<uint4*>(s_v + rr * W::LDV + cc) = vpre[i];
     }
     if (j + 1 < ntiles) load_kv(s0 + W::TKV);
@@ -368,7 +398,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   __syncthreads();
   float* Hf = static_cast<float*>(p.H);
   uint16_t* Hb = static_cast<uint16_t*>(p.H);
-  const size_t hbase = ((size_t)bh * S + t0) * DV;
+  const size_t hbase = ((size_t)bh * S + t0) * DV + v0;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -387,7 +417,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     }
   }
   if constexpr (!SIG) {
-    if (tid < TQ && row0 + tid < Lc) {
+    if (vt == 0 && tid < TQ && row0 + tid < Lc) {
       const size_t ro = (size_t)bh * S + t0 + row0 + tid;
       if (p.m_rows) p.m_rows[ro] = s_row_m2[tid] * kLn2;
       if (p.den_rows) p.den_rows[ro] = s_row_den[tid];
@@ -395,17 +425,22 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   }
 }
 
-template <int DK, int DV, int TQ, bool SIG, bool SPLIT>
+template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT>
 hipError_t launch_t(const HintraParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)(p.BH * p.Nc * (p.L / TQ)));
-  hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
+  dim3 grid((unsigned)(p.BH * p.Nc * (p.L / TQ) * (DV / TV)));
+  hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
+// Tile choice: 64-row tiles span all DV columns; 128-row tiles span DV / 2
+// columns when DV = 512 (keeps 64 accumulators per lane).
 template <int DK, int DV, bool SIG, bool SPLIT>
 hipError_t launch_tq(const HintraParams& p, hipStream_t stream) {
-  if (p.tile_lq == 128) return launch_t<DK, DV, 128, SIG, SPLIT>(p, stream);
-  if constexpr (DV >= 256) return launch_t<DK, DV, 64, SIG, SPLIT>(p, stream);
+  if (p.tile_lq == 128) {
+    if constexpr (DV == 512) return launch_t<DK, DV, 128, 256, SIG, SPLIT>(p, stream);
+    else return launch_t<DK, DV, 128, DV, SIG, SPLIT>(p, stream);
+  }
+  if constexpr (DV >= 256) return launch_t<DK, DV, 64, DV, SIG, SPLIT>(p, stream);
   return hipErrorInvalidValue;
 }
 
