@@ -16,6 +16,7 @@ import argparse
 import json
 import multiprocessing as mp
 import os
+import re
 import sys
 import time
 
@@ -26,6 +27,63 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 METRIC = "mLSTM chunkwise fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 7B-shaped heads"
+CSRC = os.path.join(ROOT, "xlstm_mlstm_chunkwise_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def csrc_sha256() -> str:
+    """Hash of every kernel source file (name and bytes, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(w, h_bytes: int) -> dict:
+    """HBM bytes each stage must move at least once per launch.
+
+    states: reads K, V and both gate rows (plus the initial state when given)
+            and writes N_c + 1 chunk states of DHQK*DHV + DHQK + 1 values of
+            4 bytes (the packed hi/lo pair of a 16-bit type is 4 bytes too).
+    hintra: reads Q, K, V, the gates and the N_c states entering the chunks,
+            and writes H."""
+    el = 2 if w.qkv_dtype == "bf16" else 4
+    nc = -(-w.S // w.chunk)
+    per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
+    qk = w.BH * w.S * w.DHQK * el
+    vv = w.BH * w.S * w.DHV * el
+    gates = 2 * w.BH * w.S * 4
+    init = w.BH * per_state if w.init_state else 0
+    return {
+        "states": qk + vv + gates + init + w.BH * (nc + 1) * per_state,
+        "hintra": 2 * qk + vv + gates + w.BH * nc * per_state + w.BH * w.S * w.DHV * h_bytes,
+    }
+
+
+def recorded_traffic(workload: str, kernel: str, tile_lq) -> tuple:
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else (None, reason)."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    rec = {}
+    for line in open(path):
+        m = re.match(r"\s*traffic-record:\s*(.*)", line)
+        if m:
+            kv = dict(x.split("=", 1) for x in m.group(1).split())
+            if kv.get("kernel") == kernel and kv.get("tile_lq", "default") == str(tile_lq or "default"):
+                rec = kv
+    if not rec:
+        return None, "kernel not in counter summary"
+    if rec.get("source_sha256") != csrc_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    b = float(rec["fetch_kib"]) * 1024 * float(rec["fetch_scale"]) + \
+        float(rec["write_kib"]) * 1024 * float(rec["write_scale"])
+    return b, os.path.relpath(path, ROOT)
 
 
 def _oracle_head(args):
@@ -81,6 +139,17 @@ def cpu_baseline(name: str, budget_s: float) -> dict:
             "sample": (f"float64 recurrent oracle, {n_heads} of {w.BH} heads x {steps} of {w.S} steps "
                        f"({w.name}), {used} worker processes with 1 BLAS thread each; "
                        f"tokens/s counts {w.NH} heads per token; wall {wall:.1f} s")}
+
+
+def path_dtype(mt, desc, precision: str) -> str:
+    """Arithmetic of the kernels that run for `desc`: the 16-bit type of the
+    matrix-core operands (x2 when the computed operand is split hi + lo) and
+    the accumulation type."""
+    wide = mt.kernel_family(desc) == mt.MLSTM_FAMILY_WIDE
+    if desc.qkv_dtype == mt.MLSTM_F32:
+        return "f32-mfma/f32-acc"
+    t = "bf16" if wide else "f16"
+    return f"{t}x2-mfma/f32-acc" if precision == "split" else f"{t}-mfma/f32-acc"
 
 
 def main(argv=None) -> int:
@@ -202,15 +271,19 @@ def main(argv=None) -> int:
     tokens = w.B * w.S
     flops = mt.flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
     tflops = flops / (ms * 1e-3) / 1e12
+    # The dominant kernel is priced against HBM: its algorithmic bytes per
+    # launch over its mean launch time.  (Its FLOP/byte ratio sits far below
+    # the bf16 matrix-core ridge point of 2500/8 flop per byte.)
+    abytes = algorithmic_bytes(w, 2 if args.h_dtype == "bf16" else 4)
     # algorithmic FLOPs of each stage: states = K^T.V (2 DK DV per token-head);
     # intra = Q.C + causal Q.K^T and P.V
-    per_th_states = 2.0 * w.DHQK * w.DHV
-    per_th_intra = 2.0 * w.DHQK * w.DHV + (w.chunk + 1) * (w.DHQK + w.DHV)
-    f_states = w.BH * w.S * per_th_states
-    f_intra = w.BH * w.S * per_th_intra
+    f_stage = {"states": 2.0 * w.DHQK * w.DHV * w.BH * w.S,
+               "hintra": (2.0 * w.DHQK * w.DHV + (w.chunk + 1) * (w.DHQK + w.DHV)) * w.BH * w.S}
+    t_stage = {"states": t_states, "hintra": t_hintra}
     dominant = "hintra" if t_hintra >= t_states else "states"
-    t_dom, f_dom = (t_hintra, f_intra) if dominant == "hintra" else (t_states, f_states)
-    ach = f_dom / (t_dom * 1e-3) / 1e12
+    t_dom = t_stage[dominant]
+    ach = abytes[dominant] / (t_dom * 1e-3) / 1e9
+    traffic, traffic_src = recorded_traffic(w.name, dominant, args.tile_lq)
     out = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -222,7 +295,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16x2-mfma/fp32-acc" if args.precision == "split" else "fp16-mfma/fp32-acc",
+        "dtype": path_dtype(mt, desc, args.precision),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
                    "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
@@ -230,9 +303,12 @@ def main(argv=None) -> int:
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "wall_ms_per_step": wall_ms,
-        "kernels_ms": {"states": t_states, "hintra": t_hintra},
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None},
+        "kernels_ms": t_stage,
+        "kernels_GBps": {k: abytes[k] / (t_stage[k] * 1e-3) / 1e9 for k in t_stage},
+        "kernels_TFLOPs": {k: f_stage[k] / (t_stage[k] * 1e-3) / 1e12 for k in t_stage},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes": abytes[dominant], "traffic_source": traffic_src},
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)

@@ -80,13 +80,17 @@ typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
 
 /* Arithmetic of the three contractions whose left operand is computed on the
  * fly (P = scores x decay in P.V, the carried state C in Q.C, and the gated
- * keys in K^T.V).  For bf16 inputs Q, K, V are converted to fp16 for the
- * matrix cores (exact for bf16 values of magnitude in [2^-14, 65504];
- * smaller ones keep an absolute error below 2^-25).
- *   MLSTM_PREC_SPLIT: the computed operand is carried as an fp16 hi + lo
- *                     pair (about 21 significant bits, two MFMA passes),
- *                     fp32 accumulation.  Default.
- *   MLSTM_PREC_F16:   one fp16 rounding of the computed operand (one pass).
+ * keys in K^T.V).  With bf16 inputs the raw Q, K, V enter the matrix cores
+ * unchanged; the computed operand is rounded to nearest-even in one of two
+ * ways, and every product accumulates in fp32:
+ *   MLSTM_PREC_SPLIT: the operand is carried as a hi + lo pair of 16-bit
+ *                     values (two MFMA passes).  The head shapes with
+ *                     DHQK in {128, 256} and DHV in {256, 512} use bf16
+ *                     pairs (about 16 significant bits); the other shapes
+ *                     use fp16 pairs (about 21 bits, Q, K, V converted
+ *                     to fp16, which is exact for bf16 values of magnitude
+ *                     in [2^-14, 65504]).  Default.
+ *   MLSTM_PREC_F16:   a single 16-bit rounding of the operand (one pass).
  *   MLSTM_PREC_F64:   everything (gates, scores, contractions, chunk states)
  *                     in fp64 on the vector units; for rows whose sums cancel
  *                     too strongly for fp32 accumulation.  Workspace states
@@ -126,14 +130,31 @@ int mlstm_fw_validate(const mlstm_fw_desc_t* desc);
  * -1. */
 int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
 
+/* Which family of kernels runs for a valid descriptor (host-only query):
+ *   MLSTM_FAMILY_GENERIC  64-row tiles, float32 row-major chunk states, fp16
+ *                         (bf16 inputs) or fp32 (float32 inputs) operands
+ *   MLSTM_FAMILY_WIDE     bf16 inputs with DHQK in {128, 256} and DHV in
+ *                         {256, 512}, tile_lq 0 or 64 (or 128 when the
+ *                         chunk holds 128 rows): 512-thread intra-chunk
+ *                         workgroups,
+ *                         bf16 operands, chunk states in the packed operand
+ *                         layout
+ *   MLSTM_FAMILY_F64      MLSTM_PREC_F64: fp64 vector-unit kernels
+ * Returns the negated status code for an invalid descriptor. */
+typedef enum { MLSTM_FAMILY_GENERIC = 0, MLSTM_FAMILY_WIDE = 1, MLSTM_FAMILY_F64 = 2 } mlstm_family_t;
+int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
+
 /* Bytes of device workspace that the forward pass needs for `desc`: the
  * stabilised state entering every chunk plus the final state, i.e. N_c + 1
  * states per head of DHQK x DHV values, DHQK normaliser values and one
  * max-state (exp gate), each region 256-byte aligned; 4 bytes per value, 8
- * with MLSTM_PREC_F64.  Returns 0 for
- * an invalid descriptor.  The storage order of the states inside the
- * workspace belongs to the library (it is the operand order of the kernels
- * that read it); mlstm_fw_unpack_states returns them as plain float32. */
+ * with MLSTM_PREC_F64.  For MLSTM_FAMILY_WIDE it also holds per-position gate
+ * terms, written by stage one and read by stage two: 12 bytes per position
+ * and head for the exp gate, 8 for the sig gate (one more 256-aligned
+ * region).  Returns 0 for an invalid descriptor.  The storage order inside
+ * the workspace belongs to the library (the chunk states are kept in the
+ * operand order of the kernels that read them); mlstm_fw_unpack_states
+ * returns the states as plain float32. */
 size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
 
 /* Full forward pass: stage one (states) then stage two (H) on `workspace`.

@@ -69,6 +69,14 @@ def test_valid_descriptor_and_workspace_size():
     assert mt.workspace_bytes(d) == expect
     ds = _desc(gate="sig")
     assert mt.workspace_bytes(ds) == r256(BH * (Nc + 1) * 128 * 64 * 4)
+    # wide-tile family: one more region of per-position gate terms
+    dw = _desc(DHQK=256, DHV=512, chunk_size=256)
+    Ncw = (1000 + 255) // 256
+    expect_w = (r256(BH * (Ncw + 1) * 256 * 512 * 4) + r256(BH * (Ncw + 1) * 256 * 4) + r256(BH * (Ncw + 1) * 4)
+                + r256(BH * 1000 * 4 * 3))
+    assert mt.workspace_bytes(dw) == expect_w
+    dws = _desc(DHQK=256, DHV=512, chunk_size=256, gate="sig")
+    assert mt.workspace_bytes(dws) == r256(BH * (Ncw + 1) * 256 * 512 * 4) + r256(BH * 1000 * 4 * 2)
     assert mt.validate(_desc(S=0)) == 0
     assert mt.num_chunks(_desc(S=0)) == 0
 
@@ -131,6 +139,17 @@ def test_entry_points_refuse_before_launch():
     assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), 1 << 20, wsb - 1, 4096, None, None, None) == 6
     assert lib.mlstm_fw_unpack_states(ctypes.byref(ds), 1 << 20, wsb, None, 4096, None, None) == 5
     assert lib.mlstm_fw_unpack_states(ctypes.byref(d), None, wsb, 4096, None, None, None) == 6
+
+
+def test_kernel_family_query():
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(DHQK=128, DHV=256, chunk_size=128)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=1024, tile_lq=128)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(DHQK=128, DHV=128, chunk_size=128)) == mt.MLSTM_FAMILY_GENERIC
+    assert mt.kernel_family(_desc(DHQK=64, DHV=64, chunk_size=64, qkv_dtype=mt.MLSTM_F32)) == mt.MLSTM_FAMILY_GENERIC
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256, qkv_dtype=mt.MLSTM_F32)) == mt.MLSTM_FAMILY_GENERIC
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256, precision="f64")) == mt.MLSTM_FAMILY_F64
+    assert mt.kernel_family(_desc(DHQK=100)) == -2
 
 
 def test_flops_formula():

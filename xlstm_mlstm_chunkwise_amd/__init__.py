@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmlstm_tfla.so")
 MLSTM_F32, MLSTM_BF16 = 0, 1
 MLSTM_GATE_EXP, MLSTM_GATE_SIG = 0, 1
 MLSTM_PREC_SPLIT, MLSTM_PREC_F16, MLSTM_PREC_F64 = 0, 1, 2
+MLSTM_FAMILY_GENERIC, MLSTM_FAMILY_WIDE, MLSTM_FAMILY_F64 = 0, 1, 2
 _PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16, "f64": MLSTM_PREC_F64}
 _GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
 
@@ -54,6 +55,7 @@ _SYMBOLS = {
     "mlstm_fw_validate": (ctypes.c_int, [ctypes.POINTER(FwDesc)]),
     "mlstm_fw_num_chunks": (ctypes.c_int64, [ctypes.POINTER(FwDesc)]),
     "mlstm_fw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
+    "mlstm_fw_kernel_family": (ctypes.c_int, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_fw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 8
@@ -103,6 +105,11 @@ def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=
 
 def validate(desc: FwDesc) -> int:
     return lib().mlstm_fw_validate(ctypes.byref(desc))
+
+
+def kernel_family(desc: FwDesc) -> int:
+    """MLSTM_FAMILY_* of the kernels that run for `desc` (negated status if invalid)."""
+    return lib().mlstm_fw_kernel_family(ctypes.byref(desc))
 
 
 def workspace_bytes(desc: FwDesc) -> int:

@@ -10,6 +10,7 @@
 
 namespace {
 
+using mlstm::GatesParams;
 using mlstm::HintraParams;
 using mlstm::StatesParams;
 
@@ -53,8 +54,10 @@ int validate_desc(const mlstm_fw_desc_t* d) {
 }
 
 struct WsLayout {
-  size_t c_off, n_off, m_off, total;
+  size_t c_off, n_off, m_off, g_off, total;
 };
+
+bool packed_layout(const mlstm_fw_desc_t* d);
 
 WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   const size_t BH = (size_t)d->B * d->NH;
@@ -67,6 +70,9 @@ WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * el, 256);
   w.m_off = off;
   if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * el, 256);
+  // per-position gate terms shared by the two wide-tile stages
+  w.g_off = off;
+  if (packed_layout(d)) off += round_up(BH * (size_t)d->S * sizeof(float) * (d->gate == MLSTM_GATE_EXP ? 3 : 2), 256);
   w.total = off;
   return w;
 }
@@ -99,6 +105,9 @@ struct WsPtrs {
   float* C;
   float* n;
   float* m;
+  float* gb2;  // gate terms (wide-tile path), else null
+  float* gu2;
+  float* gpm2;
 };
 
 WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
@@ -108,6 +117,13 @@ WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
   r.C = reinterpret_cast<float*>(ws + w.c_off);
   r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
   r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
+  r.gb2 = r.gu2 = r.gpm2 = nullptr;
+  if (packed_layout(d)) {
+    const size_t n = (size_t)d->B * d->NH * d->S;
+    r.gb2 = reinterpret_cast<float*>(ws + w.g_off);
+    r.gu2 = r.gb2 + n;
+    r.gpm2 = d->gate == MLSTM_GATE_EXP ? r.gu2 + n : nullptr;
+  }
   return r;
 }
 
@@ -135,6 +151,9 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   p.C_out = C_out;
   p.n_out = n_out;
   p.m_out = m_out;
+  p.gb2 = ws.gb2;
+  p.gu2 = ws.gu2;
+  p.gpm2 = ws.gpm2;
   p.BH = d->B * d->NH;
   p.S = d->S;
   p.DK = d->DHQK;
@@ -146,7 +165,20 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
   hipError_t e;
   if (d->precision == MLSTM_PREC_F64) e = mlstm::launch_states_f64(p, bf16, sig, stream);
-  else if (packed_layout(d)) e = mlstm::launch_states_wide(p, sig, split, stream);
+  else if (packed_layout(d)) {
+    GatesParams g;
+    g.i_pre = i_pre;
+    g.f_pre = f_pre;
+    g.gb2 = ws.gb2;
+    g.gu2 = ws.gu2;
+    g.gpm2 = ws.gpm2;
+    g.BH = p.BH;
+    g.S = p.S;
+    g.L = p.L;
+    g.Nc = p.Nc;
+    e = mlstm::launch_gates(g, sig, stream);
+    if (e == hipSuccess) e = mlstm::launch_states_wide(p, sig, split, stream);
+  }
   else e = mlstm::launch_states(p, bf16, sig, split, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
@@ -167,6 +199,9 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   p.H = H;
   p.m_rows = m_rows;
   p.den_rows = den_rows;
+  p.gb2 = ws.gb2;
+  p.gu2 = ws.gu2;
+  p.gpm2 = ws.gpm2;
   p.scale = resolve_scale(d);
   p.eps = d->eps;
   p.BH = d->B * d->NH;
@@ -215,6 +250,13 @@ int mlstm_fw_validate(const mlstm_fw_desc_t* desc) { return validate_desc(desc);
 int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc) {
   if (validate_desc(desc) != MLSTM_OK) return -1;
   return ((int64_t)desc->S + desc->chunk_size - 1) / desc->chunk_size;
+}
+
+int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc) {
+  const int st = validate_desc(desc);
+  if (st != MLSTM_OK) return -st;
+  if (desc->precision == MLSTM_PREC_F64) return MLSTM_FAMILY_F64;
+  return packed_layout(desc) ? MLSTM_FAMILY_WIDE : MLSTM_FAMILY_GENERIC;
 }
 
 size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc) {

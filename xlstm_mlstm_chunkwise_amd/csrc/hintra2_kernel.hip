@@ -20,6 +20,8 @@
 //   * the score tile is computed transposed with 16x16x32 tiles (each wave
 //     16 rows), turned into P, and shared through LDS as hi and lo planes.
 // Keys are taken 64 at a time.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -58,10 +60,9 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
   constexpr int NKK = DK / 16;  // 32x32x16 steps over DK
 
-  __shared__ float s_b2[kMaxL];
   __shared__ float s_u2[kMaxL];
-  __shared__ float s_red[W::NW];
-  __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ], s_row_den[TQ], s_den2[TQ];
+  __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ], s_row_den[TQ];
+  __shared__ __align__(16) float s_den2[TQ];
   __shared__ float s_n[DK];
   __shared__ __align__(16) uint16_t s_buf[W::BUF_ELEMS];
   uint16_t* const s_k = s_buf;
@@ -98,8 +99,6 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const uint16_t* Q = static_cast<const uint16_t*>(p.Q) + ((size_t)bh * S + t0) * DK;
   const uint16_t* K = static_cast<const uint16_t*>(p.K) + ((size_t)bh * S + t0) * DK;
   const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV + v0;
-  const float* ig = p.i_pre + (size_t)bh * S + t0;
-  const float* fg = p.f_pre + (size_t)bh * S + t0;
 
   // P.V / Q.C role: rows wr0 .. wr0+63, columns wc0 .. wc0+WC-1.
   const int wr0 = (wave / W::NWC) * 64;
@@ -140,49 +139,22 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
   for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(kk);
 
-  // ---- gates over chunk positions [0, kend): b (inclusive cumsum of log-forget),
-  // u = input term - b (log2 units), prefix max of u.
+  // ---- gate terms of this chunk (log2 units, written by the gates kernel):
+  // u for the keys [0, kend); b and the running max of u for this tile's rows.
   {
-    float b[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      b[e] = pos < kend ? log_sigmoid(fg[pos]) : 0.0f;
-    }
-    block_scan4<false, W::NW>(b, s_red);
-    float u[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      if (pos < kend) {
-        const float it = ig[pos];
-        u[e] = ((SIG ? log_sigmoid(it) : it) - b[e]) * kLog2e;
-        s_b2[pos] = b[e] * kLog2e;
-        s_u2[pos] = u[e];
-      } else {
-        u[e] = -INFINITY;
-      }
-    }
-    if constexpr (!SIG) {
-      block_scan4<true, W::NW>(u, s_red);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = 4 * tid + e;
-        if (pos >= row0 && pos < kend) s_row_m2[pos - row0] = u[e];
-      }
-    }
-    __syncthreads();
+    const float* gu = p.gu2 + (size_t)bh * S + t0;
+    for (int pos = tid; pos < kend; pos += W::NT) s_u2[pos] = gu[pos];
     if (tid < TQ) {
       const int pos = row0 + tid;
       if (pos < kend) {
-        const float b2 = s_b2[pos];
+        const float b2 = p.gb2[(size_t)bh * S + t0 + pos];
         if constexpr (SIG) {
           s_row_r2[tid] = b2;
           s_row_w[tid] = exp2f(b2);
           s_row_m2[tid] = 0.0f;
         } else {
           const float M2 = mprev * kLog2e;
-          const float mx = fmaxf(M2, s_row_m2[tid]);
+          const float mx = fmaxf(M2, p.gpm2[(size_t)bh * S + t0 + pos]);
           s_row_r2[tid] = -mx;
           s_row_w[tid] = exp2f(M2 - mx);
           s_row_m2[tid] = b2 + mx;
@@ -396,25 +368,43 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     }
   }
   __syncthreads();
-  float* Hf = static_cast<float*>(p.H);
-  uint16_t* Hb = static_cast<uint16_t*>(p.H);
-  const size_t hbase = ((size_t)bh * S + t0) * DV + v0;
+  // Each accumulator register holds one row of 32 consecutive columns across
+  // a half-wave, so each store writes two full 128-byte row segments.  Row
+  // offsets are compile-time multiples of DV; only a ragged last tile checks
+  // rows.
+  auto store_h = [&](auto zero, auto ragged) {
+    using OutT = decltype(zero);
+    OutT* const hp = static_cast<OutT*>(p.H) + ((size_t)bh * S + t0 + row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      const int t = row0 + row;
-      if (t >= Lc) continue;
-      const float inv = SIG ? 1.0f : s_den2[row];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rowl = 32 * rb + 8 * r4;  // + 4 * h2 + q: row within the wave's 64
+        float4 inv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if constexpr (!SIG) inv = *reinterpret_cast<const float4*>(s_den2 + wr0 + rowl + 4 * h2);
+        const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
-      for (int cb = 0; cb < W::CB; ++cb) {
-        const float hv = acc[rb][cb][r] * inv;
-        const size_t off = hbase + (size_t)t * DV + wc0 + 32 * cb + l32;
-        if (p.h_bf16) Hb[off] = f32_to_bf16(hv);
-        else Hf[off] = hv;
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (decltype(ragged)::value) {
+            if (row0 + wr0 + rowl + 4 * h2 + q >= Lc) continue;
+          }
+#pragma unroll
+          for (int cb = 0; cb < W::CB; ++cb) {
+            const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
+            OutT* const dst = hp + (size_t)(rowl + q) * DV + 32 * cb;
+            if constexpr (sizeof(OutT) == 2) *dst = f32_to_bf16(hv);
+            else *dst = hv;
+          }
+        }
       }
-    }
+  };
+  const bool full = row0 + wr0 + 64 <= Lc;  // wave-uniform
+  if (p.h_bf16) {
+    if (full) store_h(uint16_t{0}, std::false_type{});
+    else store_h(uint16_t{0}, std::true_type{});
+  } else {
+    if (full) store_h(0.0f, std::false_type{});
+    else store_h(0.0f, std::true_type{});
   }
   if constexpr (!SIG) {
     if (vt == 0 && tid < TQ && row0 + tid < Lc) {

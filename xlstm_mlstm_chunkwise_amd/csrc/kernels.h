@@ -6,6 +6,17 @@
 
 namespace mlstm {
 
+// Per-position gate terms in log2 units, (BH, S) float32 each (the gates
+// kernel writes them; the wide-tile kernels read them).
+struct GatesParams {
+  const float* i_pre;
+  const float* f_pre;
+  float* gb2;   // in-chunk inclusive cumulative sum of log sigmoid(f)
+  float* gu2;   // input term minus gb2
+  float* gpm2;  // running maximum of gu2 within the chunk (exp gate)
+  int BH, S, L, Nc;
+};
+
 struct StatesParams {
   const void* K;
   const void* V;
@@ -20,6 +31,9 @@ struct StatesParams {
   float* C_out;     // may be null
   float* n_out;
   float* m_out;
+  const float* gb2;  // gate terms (wide-tile kernels only)
+  const float* gu2;
+  const float* gpm2;
   int BH, S, DK, DV, L, Nc;
 };
 
@@ -35,6 +49,9 @@ struct HintraParams {
   void* H;
   float* m_rows;    // may be null
   float* den_rows;  // may be null
+  const float* gb2;  // gate terms (wide-tile kernel only)
+  const float* gu2;
+  const float* gpm2;
   float scale;
   float eps;
   int BH, S, DK, DV, L, Nc;
@@ -44,6 +61,7 @@ struct HintraParams {
 };
 
 // Each returns hipSuccess or the launch error.
+hipError_t launch_gates(const GatesParams& p, bool sig, hipStream_t stream);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 

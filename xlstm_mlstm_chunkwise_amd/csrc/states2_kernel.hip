@@ -1,10 +1,12 @@
 // Inter-chunk recurrence, wide-tile version for bf16 inputs (gfx950).
 //
 // Same recurrence as states_kernel.hip (TFLA abstract: chunkwise-parallel
-// form with states carried between chunks):
-//   M' = max(g + M, max_t a_t),  a_t = g - b_t + i_t
-//   C' = e^{g + M - M'} C + sum_t e^{a_t - M'} k_t v_t^T,   n' likewise
-//   (sigmoid gate: C' = e^{g} C + sum_t e^{g - b_t + log sigmoid(i_t)} k_t v_t^T)
+// form with states carried between chunks), in log2 units on the gate terms
+// that gates_kernel.hip leaves per position (b: in-chunk cumulative
+// log-forget sum, u = i~ - b, pm: running max of u):
+//   M' = g + max(M, pm_last),  g = b_last
+//   C' = 2^{g + M - M'} C + sum_t 2^{g + u_t - M'} k_t v_t^T,   n' likewise
+//   (sigmoid gate: no M; C' = 2^{g} C + sum_t 2^{g + u_t} k_t v_t^T)
 // Organisation:
 //   * one workgroup (4 waves) keeps a TK x TV tile of C in 32x32x16 bf16
 //     matrix-core accumulators (float32) for the whole sequence (TK = TV = 64
@@ -38,8 +40,6 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
   static_assert(kTT * KSEG % 256 == 0 && kTT * VSEG % 256 == 0, "staging split");
 
   __shared__ float s_w[kMaxL];
-  __shared__ float s_red[4];
-  __shared__ float s_g;
   __shared__ float s_np[256 / KSEG][TK];
   __shared__ __align__(16) uint16_t s_kh[kTT * LDK];
   __shared__ __align__(16) uint16_t s_kl[kTT * LDK];
@@ -56,8 +56,6 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
   const int wr0 = (wave >> 1) * WR, wc0 = (wave & 1) * WCOL;  // inside the tile
   const uint16_t* K = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK + kt * TK;
   const uint16_t* V = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV + vt * TV;
-  const float* ig = p.i_pre + (size_t)bh * S;
-  const float* fg = p.f_pre + (size_t)bh * S;
   const bool own_n = !SIG && vt == 0;
   const int nseg = tid % KSEG;     // this thread's key segment while staging
   const int nrow = tid / KSEG;     // and its first time row
@@ -75,8 +73,21 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
       }
   float nreg = 0.0f;  // n for key row kt*TK + tid (tid < TK), own_n only
   if (own_n && tid < TK && p.n0) nreg = p.n0[(size_t)bh * DK + kt * TK + tid];
-  float M = 0.0f;
-  if (!SIG && p.m0) M = p.m0[bh];
+  float M2 = 0.0f;  // stabiliser in log2 units
+  if (!SIG && p.m0) M2 = p.m0[bh] * kLog2e;
+  // gate terms of the next chunk: u for positions 4 tid .. 4 tid + 3, then
+  // b and the running max of u at the chunk's last position
+  float gnext[6];
+  auto load_gates = [&](int cc) {
+    const int tc = cc * L;
+    const int Lcc = min(L, S - tc);
+    const float* gu = p.gu2 + (size_t)bh * S + tc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gnext[e] = 4 * tid + e < Lcc ? gu[4 * tid + e] : 0.0f;
+    gnext[4] = p.gb2[(size_t)bh * S + tc + Lcc - 1];
+    gnext[5] = SIG ? 0.0f : p.gpm2[(size_t)bh * S + tc + Lcc - 1];
+  };
+  if (Nc > 0) load_gates(0);
 
   uint4 kpre[KPT], vpre[VPT];
   auto load_kv = [&](int t0, int tb, int Lc) {
@@ -118,52 +129,34 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
           }
         }
       if (own_n && tid < TK) p.n_states[((size_t)bh * (Nc + 1) + c) * DK + kt * TK + tid] = nreg;
-      if (!SIG && kt == 0 && vt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + c] = M;
+      if (!SIG && kt == 0 && vt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + c] = M2 * kLn2;
     }
     if (c == Nc) break;
 
     const int t0 = c * L;
     const int Lc = min(L, S - t0);
-    load_kv(t0, 0, Lc);  // first time block, overlapped with the gates
-    // ---- gates
-    float b[4];
+    load_kv(t0, 0, Lc);  // first time block
+    // ---- gate weights from the per-position gate terms (log2 units), which
+    // were requested one chunk ahead: M' = g + max(M, pm_last),
+    // w_tau = 2^{g + u_tau - M'}, decay of the carried state 2^{g + M - M'}.
+    const float g2 = gnext[4], umax2 = gnext[5];
+    float uc[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      b[e] = pos < Lc ? log_sigmoid(fg[t0 + pos]) : 0.0f;
-    }
-    block_scan4<false, 4>(b, s_red);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * tid + e == Lc - 1) s_g = b[e];
-    __syncthreads();
-    const float gsum = s_g;
-    float a[4];
-    float amax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      if (pos < Lc) {
-        const float it = ig[t0 + pos];
-        a[e] = gsum - b[e] + (SIG ? log_sigmoid(it) : it);
-        amax = fmaxf(amax, a[e]);
-      } else {
-        a[e] = -INFINITY;
-      }
-    }
-    float decay;
+    for (int e = 0; e < 4; ++e) uc[e] = gnext[e];
+    if (c + 1 < Nc) load_gates(c + 1);
+    float decay, Mn2 = 0.0f;
     if constexpr (SIG) {
-      decay = expf(gsum);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? expf(a[e]) : 0.0f;
+      decay = exp2f(g2);
     } else {
-      amax = block_reduce<true, 4>(amax, s_red);
-      const float Mnew = fmaxf(gsum + M, amax);
-      decay = expf(gsum + M - Mnew);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? expf(a[e] - Mnew) : 0.0f;
-      M = Mnew;
+      Mn2 = g2 + fmaxf(M2, umax2);
+      decay = exp2f(g2 + M2 - Mn2);
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = 4 * tid + e;
+      s_w[pos] = pos < Lc ? exp2f(g2 + uc[e] - Mn2) : 0.0f;
+    }
+    M2 = Mn2;
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -249,7 +242,7 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
         }
   }
   if (own_n && p.n_out && tid < TK) p.n_out[(size_t)bh * DK + kt * TK + tid] = nreg;
-  if (!SIG && p.m_out && kt == 0 && vt == 0 && tid == 0) p.m_out[bh] = M;
+  if (!SIG && p.m_out && kt == 0 && vt == 0 && tid == 0) p.m_out[bh] = M2 * kLn2;
 }
 
 template <int T, bool SIG, bool SPLIT>
