@@ -37,11 +37,11 @@ struct Wide {
   static constexpr int NWC = NW / NWR;     // waves along columns
   static constexpr int WC = TV / NWC;      // columns per wave
   static constexpr int CB = WC / 32;       // 32-column blocks per wave
-  // Row strides (elements).  K and P are read along rows (16-byte reads, a
-  // stride of 4 banks mod 64 keeps 16 rows conflict-free); V is read down its
-  // rows with the transposing read (4 rows x 32 bytes per 16 lanes: a stride
-  // of 8 banks mod 64 keeps them apart).
-  static constexpr int LDK = DK + 8, LDV = TV + 16, LDP = TKV + 8, LDQ = DK + 8;
+  // Row strides (elements).  K and P are read along rows with 16-byte reads
+  // (16 lanes, 16 rows: a stride of 4 banks mod 64 keeps them apart).  V is
+  // read down its rows with ds_read_b64_tr_b16, where each half-wave takes
+  // 4 rows x 64 bytes: a stride of 16 banks mod 64 keeps the rows apart.
+  static constexpr int LDK = DK + 8, LDV = TV + 32, LDP = TKV + 8, LDQ = DK + 8;
   static constexpr int K_ELEMS = TKV * LDK;
   static constexpr int P_ELEMS = TQ * LDP;   // one plane
   static constexpr int V_ELEMS = TKV * LDV;
@@ -109,8 +109,30 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const int skb0 = (TQ == 128) ? 0 : 2 * (wave >> 2);
   const int srow = sr * 16 + l16;  // row of this lane in the transposed score tile
   const bool srow_ok = row0 + srow < Lc;
-  // The Q tile (TQ x DK) is requested now, overlapping the gate math, and
-  // staged once in LDS for both the inter-chunk product and the score tile.
+  // Loads in the order they are needed (the memory counter is waited on in
+  // issue order): gate terms and the normaliser, then the Q tile, then the
+  // first chunk-state fragments.
+  constexpr int GPT = (kMaxL + W::NT - 1) / W::NT;  // key positions per thread
+  float gu_r[GPT];
+  const float* gu = p.gu2 + (size_t)bh * S + t0;
+#pragma unroll
+  for (int e = 0; e < GPT; ++e) gu_r[e] = tid + e * W::NT < kend ? gu[tid + e * W::NT] : 0.0f;
+  float gb_r = 0.0f, gpm_r = 0.0f;
+  if (tid < TQ && row0 + tid < kend) {
+    gb_r = p.gb2[(size_t)bh * S + t0 + row0 + tid];
+    if constexpr (!SIG) gpm_r = p.gpm2[(size_t)bh * S + t0 + row0 + tid];
+  }
+  float mprev = 0.0f;
+  if constexpr (!SIG) mprev = p.m_states[(size_t)bh * (Nc + 1) + c];
+  constexpr int NPT = (DK + W::NT - 1) / W::NT;
+  float n_r[NPT];
+  if constexpr (!SIG) {
+    const float* nst = p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) n_r[e] = tid + e * W::NT < DK ? nst[tid + e * W::NT] : 0.0f;
+  }
+  // The Q tile (TQ x DK) is staged once in LDS for both the inter-chunk
+  // product and the score tile.
   constexpr int QPT = TQ * DK / 8 / W::NT;  // 16-byte loads per thread
   static_assert(TQ * DK / 8 % W::NT == 0, "Q tile split");
   uint4 qpre[QPT];
@@ -121,10 +143,8 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     qpre[i] = (row0 + rr < Lc) ? *reinterpret_cast<const uint4*>(Q + (size_t)(row0 + rr) * DK + cc)
                                : make_uint4(0, 0, 0, 0);
   }
-  float mprev = 0.0f;
-  if constexpr (!SIG) mprev = p.m_states[(size_t)bh * (Nc + 1) + c];
 
-  // ---- issue the first state / Q fragment loads before the gate math
+  // ---- first chunk-state fragments
   const uint16_t* Pst = reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
   constexpr int PD = W::CB >= 4 ? 1 : 3;  // k steps loaded ahead
   uint4 bb[NKK][W::CB][2];
@@ -138,23 +158,24 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   };
 #pragma unroll
   for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(kk);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- gate terms of this chunk (log2 units, written by the gates kernel):
   // u for the keys [0, kend); b and the running max of u for this tile's rows.
   {
-    const float* gu = p.gu2 + (size_t)bh * S + t0;
-    for (int pos = tid; pos < kend; pos += W::NT) s_u2[pos] = gu[pos];
+#pragma unroll
+    for (int e = 0; e < GPT; ++e)
+      if (tid + e * W::NT < kend) s_u2[tid + e * W::NT] = gu_r[e];
     if (tid < TQ) {
-      const int pos = row0 + tid;
-      if (pos < kend) {
-        const float b2 = p.gb2[(size_t)bh * S + t0 + pos];
+      if (row0 + tid < kend) {
+        const float b2 = gb_r;
         if constexpr (SIG) {
           s_row_r2[tid] = b2;
           s_row_w[tid] = exp2f(b2);
           s_row_m2[tid] = 0.0f;
         } else {
           const float M2 = mprev * kLog2e;
-          const float mx = fmaxf(M2, p.gpm2[(size_t)bh * S + t0 + pos]);
+          const float mx = fmaxf(M2, gpm_r);
           s_row_r2[tid] = -mx;
           s_row_w[tid] = exp2f(M2 - mx);
           s_row_m2[tid] = b2 + mx;
@@ -166,8 +187,9 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       }
     }
     if constexpr (!SIG) {
-      const float* nst = p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
-      for (int k = tid; k < DK; k += W::NT) s_n[k] = nst[k];
+#pragma unroll
+      for (int e = 0; e < NPT; ++e)
+        if (tid + e * W::NT < DK) s_n[tid + e * W::NT] = n_r[e];
     }
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
@@ -177,12 +199,6 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     }
     __syncthreads();
   }
-  // this lane's Q row as B fragments of the transposed score tile
-  uint4 qs[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qs[ks] = *reinterpret_cast<const uint4*>(s_q + srow * W::LDQ + 32 * ks + 8 * g4);
-
-
   float16_t acc[2][W::CB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -196,6 +212,9 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     if (kk + PD < NKK) load_k(kk + PD);
+    // keep the prefetch ahead of this step's products (the scheduler would
+    // otherwise sink the loads next to their use to save registers)
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8_t qa[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -216,6 +235,10 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       }
     }
   }
+  // this lane's Q row as B fragments of the transposed score tile
+  uint4 qs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qs[ks] = *reinterpret_cast<const uint4*>(s_q + srow * W::LDQ + 32 * ks + 8 * g4);
   __syncthreads();  // the Q tile's LDS is reused for K, P and V below
   // scale row by e^{b + M - m} * s
 #pragma unroll

@@ -20,6 +20,8 @@
 //     and 32-column block, 64 lanes x 8 bf16 values, hi plane then lo plane.
 //     The lane and slot order is the accumulator's own, so the writes are
 //     plain 16-byte stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,8 +35,9 @@ template <int TK, int TV, bool SIG, bool SPLIT>
 __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) {
   constexpr int WR = TK / 2, WCOL = TV / 2;      // wave tile
   constexpr int RB = WR / 32, CB = WCOL / 32;    // 32x32 blocks per wave
-  // row strides of 8 banks mod 64 keep the 4 rows of a transposing read apart
-  constexpr int LDK = TK + 16, LDV = TV + 16;
+  // row strides of 16 banks mod 64 keep apart the 4 rows x 64 bytes that a
+  // half-wave takes in one transposing read
+  constexpr int LDK = TK + 32, LDV = TV + 32;
   constexpr int KSEG = TK / 8, VSEG = TV / 8;    // 16-byte segments per row
   constexpr int KPT = kTT * KSEG / 256, VPT = kTT * VSEG / 256;
   static_assert(kTT * KSEG % 256 == 0 && kTT * VSEG % 256 == 0, "staging split");
@@ -245,6 +248,309 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
   if (!SIG && p.m_out && kt == 0 && vt == 0 && tid == 0) p.m_out[bh] = M2 * kLn2;
 }
 
+// Row-tile variant for many heads: a workgroup of 8 waves keeps a TK x DV
+// tile of C (each wave a 64 x 64 block) for the whole sequence, so each gated
+// key block is staged once for all value columns.  The tiles of one head are
+// placed on one XCD (they read the same V rows at about the same time).
+// Software pipeline over 32-step blocks of the flattened (chunk, step)
+// sequence:
+//   * LDS holds two stages: block j is in the matrix cores while block j+1 is
+//     written, one barrier per block;
+//   * the global loads of block j+2 are in flight meanwhile (two register
+//     sets, issued two blocks ahead);
+//   * each staging thread forms the gate weight of its own time row from the
+//     per-position gate terms; the chunk stabiliser and decay are formed when
+//     a chunk's first block is staged and applied one block later, when the
+//     matrix cores reach it.
+template <int TK, int TV, bool SIG, bool SPLIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void states_rows_kernel(
+    const StatesParams p) {
+  constexpr int NT = 512, NW = 8, TB = 32;
+  constexpr int NWC = TV / 64;
+  static_assert((TK / 64) * NWC == NW, "eight 64x64 wave tiles");
+  constexpr int LDK = TK + 32, LDV = TV + 32;  // 16 banks mod 64 (see above)
+  constexpr int EPT = TB * TK / NT;  // key elements per thread and block
+  constexpr int TPR = TK / EPT;      // staging threads per time row
+  static_assert(TPR == 16 && (EPT == 4 || EPT == 8), "staging split");
+  constexpr int VSEG = TV / 8;
+  constexpr int VPT = TB * VSEG / NT;  // 16-byte V loads per thread and block
+  static_assert(TB * VSEG % NT == 0, "V staging split");
+  constexpr int KBUF = TB * LDK, VBUF = TB * LDV;
+  typedef typename std::conditional<EPT == 4, uint2, uint4>::type KVec;
+
+  __shared__ float s_np[NW][TK];
+  __shared__ __align__(16) uint16_t s_kh[2 * KBUF];
+  __shared__ __align__(16) uint16_t s_kl[SPLIT ? 2 * KBUF : 8];
+  __shared__ __align__(16) uint16_t s_v[2 * VBUF];
+
+  const int NTK = p.DK / TK;
+  const int nblk = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int kt = bid % NTK;
+  const int bh = bid / NTK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int S = p.S, DK = p.DK, L = p.L, Nc = p.Nc;
+  constexpr int DV = TV;
+  const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;  // inside the tile
+  const uint16_t* K = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK + kt * TK;
+  const uint16_t* V = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV;
+  const size_t gbase = (size_t)bh * S;
+  const int krs = tid / TPR, kcs = (tid % TPR) * EPT;  // staging row and columns
+
+  float16_t acc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const int vcol = wc0 + 32 * cb + l32;
+        acc[rb][cb][r] = p.C0 ? p.C0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] : 0.0f;
+      }
+  float nreg = 0.0f;  // n for key row kt * TK + tid (tid < TK)
+  if (!SIG && tid < TK && p.n0) nreg = p.n0[(size_t)bh * DK + kt * TK + tid];
+  float Mst2 = 0.0f;  // stabiliser (log2 units) after the last chunk begun by the staging side
+  if (!SIG && p.m0) Mst2 = p.m0[bh] * kLog2e;
+
+  auto write_state = [&](int entry, float M2) {
+    uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + entry) * DK * DV * 2;
+    constexpr int NB = DV / 32;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
+        const int nb = (wc0 + 32 * cb) / 32;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            split_bf16x2(acc[rb][cb][8 * half + 2 * e], acc[rb][cb][8 * half + 2 * e + 1], hi[e], lo[e]);
+          const size_t blk = ((size_t)(2 * kblk + half) * NB + nb) * 2;
+          *reinterpret_cast<uint4*>(P + (blk + 0) * 512 + lane * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          *reinterpret_cast<uint4*>(P + (blk + 1) * 512 + lane * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+      }
+    if (!SIG && kt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = M2 * kLn2;
+  };
+  write_state(0, Mst2);
+  if (!SIG && tid < TK) p.n_states[((size_t)bh * (Nc + 1)) * DK + kt * TK + tid] = nreg;
+
+  // flattened block sequence: block gi covers steps [tb, tb + TB) of chunk gi / BPC
+  const int BPC = L / TB;
+  const int NBLK = Nc > 0 ? (Nc - 1) * BPC + (S - (Nc - 1) * L + TB - 1) / TB : 0;
+
+  // two register sets of loads in flight
+  KVec kr[2];
+  float ur[2], g2r[2], pmr[2];
+  uint4 vr[2][VPT];
+  auto load_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    const int t0 = c * L, Lc = min(L, S - t0);
+    const int row = tb + krs;
+    if (row < Lc) {
+      kr[s] = *reinterpret_cast<const KVec*>(K + (size_t)(t0 + row) * DK + kcs);
+      ur[s] = p.gu2[gbase + t0 + row];
+    } else {
+      kr[s] = KVec{};
+      ur[s] = -INFINITY;  // weight 0 for rows past the chunk
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / VSEG, sg = idx % VSEG;
+      vr[s][i] = (tb + r < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(t0 + tb + r) * DV + sg * 8)
+                               : make_uint4(0, 0, 0, 0);
+    }
+    if (tb == 0) {
+      g2r[s] = p.gb2[gbase + t0 + Lc - 1];
+      pmr[s] = SIG ? 0.0f : p.gpm2[gbase + t0 + Lc - 1];
+    }
+  };
+
+  // staging side: scalars of the chunk being staged, n partial sums
+  float g2s = 0.0f, Mn2s = 0.0f, dec_s = 1.0f;
+  float dec_pend = 1.0f, M_pend = 0.0f;   // handed to the matrix-core side
+  float np[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) np[e] = 0.0f;
+  bool n_pend = false;
+  float n_dec = 1.0f;
+
+  // n' = decay n + sum_t w_t k_t: reduce the partial sums over the lanes that
+  // share key columns, then (after a barrier) over the waves
+  auto flush_n = [&]() {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      np[e] += __shfl_xor(np[e], 16, 64);
+      np[e] += __shfl_xor(np[e], 32, 64);
+    }
+    if (lane < TPR) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) s_np[wave][kcs + e] = np[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) np[e] = 0.0f;
+    n_pend = true;
+    n_dec = dec_s;
+  };
+  auto finish_n = [&](int entry) {
+    if (tid < TK) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sacc += s_np[w][tid];
+      nreg = nreg * n_dec + sacc;
+      p.n_states[((size_t)bh * (Nc + 1) + entry) * DK + kt * TK + tid] = nreg;
+    }
+    n_pend = false;
+  };
+
+  auto stage_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    if (tb == 0) {
+      if (!SIG && c > 0) flush_n();
+      const float g2 = g2r[s];
+      float Mn2 = 0.0f, dec;
+      if constexpr (SIG) {
+        dec = exp2f(g2);
+      } else {
+        Mn2 = g2 + fmaxf(Mst2, pmr[s]);
+        dec = exp2f(g2 + Mst2 - Mn2);
+        Mst2 = Mn2;
+      }
+      g2s = g2;
+      Mn2s = Mn2;
+      dec_s = dec;
+      dec_pend = dec;
+      M_pend = Mn2;
+    }
+    const float w = exp2f(g2s + ur[s] - Mn2s);
+    uint16_t* kh = s_kh + s * KBUF + krs * LDK + kcs;
+    uint16_t* kl = s_kl + (SPLIT ? s * KBUF + krs * LDK + kcs : 0);
+    uint32_t ww[EPT / 2];
+    __builtin_memcpy(ww, &kr[s], sizeof(ww));
+    uint32_t hi[EPT / 2], lo[EPT / 2];
+#pragma unroll
+    for (int e = 0; e < EPT / 2; ++e) {
+      const float x0 = __uint_as_float(ww[e] << 16) * w;
+      const float x1 = __uint_as_float(ww[e] & 0xffff0000u) * w;
+      np[2 * e] += x0;
+      np[2 * e + 1] += x1;
+      if constexpr (SPLIT) split_bf16x2(x0, x1, hi[e], lo[e]);
+      else hi[e] = round_bf16x2(x0, x1);
+    }
+    if constexpr (EPT == 4) {
+      *reinterpret_cast<uint2*>(kh) = make_uint2(hi[0], hi[1]);
+      if constexpr (SPLIT) *reinterpret_cast<uint2*>(kl) = make_uint2(lo[0], lo[1]);
+    } else {
+      *reinterpret_cast<uint4*>(kh) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      if constexpr (SPLIT) *reinterpret_cast<uint4*>(kl) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / VSEG, sg = idx % VSEG;
+      *reinterpret_cast<uint4*>(s_v + s * VBUF + r * LDV + sg * 8) = vr[s][i];
+    }
+  };
+
+  // matrix-core side
+  float M_mma = Mst2;
+  auto mma_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    if (tb == 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] *= dec_pend;
+      M_mma = M_pend;
+    }
+    const int Lc = min(L, S - c * L);
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ++ks) {
+      if (tb + 16 * ks >= Lc) break;  // uniform: padding only
+      bf16x8_t ah[2], al[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        ah[rb] = as_bf16x8(frag_tr_u(s_kh + s * KBUF, LDK, 16 * ks, wr0 + 32 * rb, lane));
+        if constexpr (SPLIT) al[rb] = as_bf16x8(frag_tr_u(s_kl + s * KBUF, LDK, 16 * ks, wr0 + 32 * rb, lane));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v + s * VBUF, LDV, 16 * ks, wc0 + 32 * cb, lane));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          acc[rb][cb] = mma32b(ah[rb], bv, acc[rb][cb]);
+          if constexpr (SPLIT) acc[rb][cb] = mma32b(al[rb], bv, acc[rb][cb]);
+        }
+      }
+    }
+    if ((gi + 1) % BPC == 0 || gi + 1 == NBLK) write_state(c + 1, M_mma);
+  };
+
+  auto iter = [&](auto par, int gi) {
+    constexpr int P = decltype(par)::value;
+    constexpr int Q = 1 - P;
+    if (n_pend) finish_n(gi / BPC);
+    mma_blk(std::integral_constant<int, P>{}, gi);
+    if (gi + 1 < NBLK) stage_blk(std::integral_constant<int, Q>{}, gi + 1);
+    if (gi + 3 < NBLK) load_blk(std::integral_constant<int, Q>{}, gi + 3);
+    __syncthreads();
+  };
+
+  if (NBLK > 0) {
+    load_blk(std::integral_constant<int, 0>{}, 0);
+    if (NBLK > 1) load_blk(std::integral_constant<int, 1>{}, 1);
+    stage_blk(std::integral_constant<int, 0>{}, 0);
+    if (NBLK > 2) load_blk(std::integral_constant<int, 0>{}, 2);
+    __syncthreads();
+    for (int gi = 0; gi < NBLK; gi += 2) {
+      iter(std::integral_constant<int, 0>{}, gi);
+      if (gi + 1 < NBLK) iter(std::integral_constant<int, 1>{}, gi + 1);
+    }
+    if constexpr (!SIG) {
+      flush_n();
+      __syncthreads();
+      finish_n(Nc);
+    }
+  }
+
+  if (p.C_out) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const int vcol = wc0 + 32 * cb + l32;
+          p.C_out[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] = acc[rb][cb][r];
+        }
+  }
+  if (!SIG && p.n_out && tid < TK) p.n_out[(size_t)bh * DK + kt * TK + tid] = nreg;
+  if (!SIG && p.m_out && kt == 0 && tid == 0) p.m_out[bh] = Mst2 * kLn2;
+}
+
+template <int TK, int TV, bool SIG, bool SPLIT>
+hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)(p.BH * (p.DK / TK)));
+  hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int TK, int TV>
+hipError_t launch_rows_any(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  if (sig) return split ? launch_rows<TK, TV, true, true>(p, stream) : launch_rows<TK, TV, true, false>(p, stream);
+  return split ? launch_rows<TK, TV, false, true>(p, stream) : launch_rows<TK, TV, false, false>(p, stream);
+}
+
 template <int T, bool SIG, bool SPLIT>
 hipError_t launch_t(const StatesParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.BH * (p.DK / T) * (p.DV / T)));
@@ -266,8 +572,14 @@ __global__ __launch_bounds__(256) void unpack_states_kernel(const uint16_t* P, f
 }  // namespace
 
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // Whole-row tiles (TK x DV) when they still give every CU a workgroup.
+  if (p.DV == 512 && (long long)p.BH * (p.DK / 64) >= cus) return launch_rows_any<64, 512>(p, sig, split, stream);
+  if (p.DV == 256 && p.DK % 128 == 0 && (long long)p.BH * (p.DK / 128) >= cus)
+    return launch_rows_any<128, 256>(p, sig, split, stream);
   // 128-wide tiles when they still give at least two workgroups per CU.
-  const bool big = (long long)p.BH * (p.DK / 128) * (p.DV / 128) >= 512;
+  const bool big = (long long)p.BH * (p.DK / 128) * (p.DV / 128) >= 2LL * cus;
   if (big) {
     if (sig) return split ? launch_t<128, true, true>(p, stream) : launch_t<128, true, false>(p, stream);
     return split ? launch_t<128, false, true>(p, stream) : launch_t<128, false, false>(p, stream);
