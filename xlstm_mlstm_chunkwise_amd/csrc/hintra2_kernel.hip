@@ -60,7 +60,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
   constexpr int NKK = DK / 16;  // 32x32x16 steps over DK
 
-  __shared__ float s_u2[kMaxL];
+  __shared__ __align__(16) float s_u2[kMaxL];
   __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ], s_row_den[TQ];
   __shared__ __align__(16) float s_den2[TQ];
   __shared__ float s_n[DK];
@@ -280,19 +280,34 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * TV / 8 % W::NT == 0, "tile split");
   uint4 kpre[KPT], vpre[VPT];
   auto load_kv = [&](int s0) {
+    if (s0 + W::TKV <= Lc) {  // full tile: no row checks
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * W::NT;
-      const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-      kpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(K + (size_t)(s0 + rr) * DK + cc)
-                               : make_uint4(0, 0, 0, 0);
-    }
+      for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+        kpre[i] = *reinterpret_cast<const uint4*>(K + (size_t)(s0 + rr) * DK + cc);
+      }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * W::NT;
-      const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
-      vpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc)
-                               : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < VPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
+        vpre[i] = *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+        kpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(K + (size_t)(s0 + rr) * DK + cc)
+                                 : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
+        vpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc)
+                                 : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   if (ntiles > 0) load_kv(0);
@@ -315,25 +330,48 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     __syncthreads();
 
     // transposed scores for 16 rows x SKB key blocks; P to LDS as hi/lo planes
+    float4_t sacc[W::SKB];
+    bool live[W::SKB];
+    bool all_live = true;
+#pragma unroll
+    for (int kb = 0; kb < W::SKB; ++kb) {
+      const int key0 = s0 + 16 * (skb0 + kb);
+      sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      live[kb] = key0 <= row0 + sr * 16 + 15 && key0 < kend;  // wave-uniform
+      all_live = all_live && live[kb];
+    }
+    if (all_live) {
+      // independent accumulation chains, interleaved
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < W::SKB; ++kb) {
+          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
+          sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < W::SKB; ++kb) {
+        if (!live[kb]) continue;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
+          sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
+        }
+      }
+    }
 #pragma unroll
     for (int kb = 0; kb < W::SKB; ++kb) {
       const int sb = skb0 + kb;
       const int key0 = s0 + 16 * sb;
-      float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const bool live = key0 <= row0 + sr * 16 + 15 && key0 < kend;  // wave-uniform
-      if (live) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * sb + l16) * W::LDK + 32 * ks + 8 * g4);
-          sacc = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc);
-        }
-      }
+      const float4 u4 = *reinterpret_cast<const float4*>(s_u2 + key0 + 4 * g4);
+      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
       float val[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int sg = key0 + 4 * g4 + r;
-        val[r] = 0.0f;
-        if (live && sg <= tau && tau < kend) val[r] = scale * sacc[r] * __builtin_amdgcn_exp2f(r2 + s_u2[sg]);
+        const float pv = scale * sacc[kb][r] * __builtin_amdgcn_exp2f(r2 + uu[r]);
+        val[r] = (live[kb] && sg <= tau && tau < kend) ? pv : 0.0f;
         den_part += val[r];
       }
       uint2 ph, pl;
