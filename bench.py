@@ -44,24 +44,30 @@ def csrc_sha256() -> str:
 
 
 def algorithmic_bytes(w, h_bytes: int) -> dict:
-    """HBM bytes each stage must move at least once per launch.
+    """HBM bytes each stage must move per launch, per token and head, times
+    the B*NH*S units of one launch (the chunk states that pass between the
+    stages are not counted: moving them is a property of the two-stage
+    design, not of the method).
 
-    states: reads K, V and both gate rows (plus the initial state when given)
-            and writes N_c + 1 chunk states of DHQK*DHV + DHQK + 1 values of
-            4 bytes (the packed hi/lo pair of a 16-bit type is 4 bytes too).
-    hintra: reads Q, K, V, the gates and the N_c states entering the chunks,
-            and writes H."""
+    states: reads K, V and both gate rows, plus the initial state when given;
+            writes the final state.
+    hintra: reads Q, K, V and the gate rows; writes H."""
     el = 2 if w.qkv_dtype == "bf16" else 4
-    nc = -(-w.S // w.chunk)
     per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
-    qk = w.BH * w.S * w.DHQK * el
-    vv = w.BH * w.S * w.DHV * el
-    gates = 2 * w.BH * w.S * 4
+    units = w.BH * w.S
     init = w.BH * per_state if w.init_state else 0
     return {
-        "states": qk + vv + gates + init + w.BH * (nc + 1) * per_state,
-        "hintra": 2 * qk + vv + gates + w.BH * nc * per_state + w.BH * w.S * w.DHV * h_bytes,
+        "states": units * ((w.DHQK + w.DHV) * el + 8) + init + w.BH * per_state,
+        "hintra": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes),
     }
+
+
+def chunk_state_bytes(w) -> int:
+    """Bytes of the chunk states the two stages pass through HBM (written by
+    the states stage, read by the intra-chunk stage)."""
+    nc = -(-w.S // w.chunk)
+    per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
+    return w.BH * (nc + 1) * per_state
 
 
 def recorded_traffic(workload: str, kernel: str, tile_lq) -> tuple:
@@ -145,7 +151,10 @@ def path_dtype(mt, desc, precision: str) -> str:
     """Arithmetic of the kernels that run for `desc`: the 16-bit type of the
     matrix-core operands (x2 when the computed operand is split hi + lo) and
     the accumulation type."""
-    wide = mt.kernel_family(desc) == mt.MLSTM_FAMILY_WIDE
+    fam = mt.kernel_family(desc)
+    if fam == mt.MLSTM_FAMILY_F64:
+        return "f64-valu/f64-acc"
+    wide = fam == mt.MLSTM_FAMILY_WIDE
     if desc.qkv_dtype == mt.MLSTM_F32:
         return "f32-mfma/f32-acc"
     t = "bf16" if wide else "f16"
@@ -156,9 +165,9 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_7b_s8192")
-    ap.add_argument("--precision", default="split", choices=["split", "f16"])
+    ap.add_argument("--precision", default="split", choices=["split", "f16", "f64"])
     ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--tile-lq", type=int, default=None, help="override the workload's intra-chunk row tile")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
@@ -305,6 +314,7 @@ def main(argv=None) -> int:
         "wall_ms_per_step": wall_ms,
         "kernels_ms": t_stage,
         "kernels_GBps": {k: abytes[k] / (t_stage[k] * 1e-3) / 1e9 for k in t_stage},
+        "chunk_state_bytes": chunk_state_bytes(w),
         "kernels_TFLOPs": {k: f_stage[k] / (t_stage[k] * 1e-3) / 1e12 for k in t_stage},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
