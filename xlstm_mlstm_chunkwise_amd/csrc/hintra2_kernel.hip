@@ -453,8 +453,10 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           for (int cb = 0; cb < W::CB; ++cb) {
             const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
             OutT* const dst = hp + (size_t)(rowl + q) * DV + 32 * cb;
-            if constexpr (sizeof(OutT) == 2) *dst = f32_to_bf16(hv);
-            else *dst = hv;
+            // H is written once and not read again here: streaming stores
+            // keep the chunk states and K/V tiles the neighbours re-read in L2
+            if constexpr (sizeof(OutT) == 2) __builtin_nontemporal_store(f32_to_bf16(hv), dst);
+            else __builtin_nontemporal_store(hv, dst);
           }
         }
       }

@@ -29,6 +29,7 @@ namespace mlstm {
 namespace {
 
 constexpr int kMaxL = 1024;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kTT = 64;  // time steps per LDS stage
 
 template <int TK, int TV, bool SIG, bool SPLIT>
@@ -331,8 +332,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
           for (int e = 0; e < 4; ++e)
             split_bf16x2(acc[rb][cb][8 * half + 2 * e], acc[rb][cb][8 * half + 2 * e + 1], hi[e], lo[e]);
           const size_t blk = ((size_t)(2 * kblk + half) * NB + nb) * 2;
-          *reinterpret_cast<uint4*>(P + (blk + 0) * 512 + lane * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-          *reinterpret_cast<uint4*>(P + (blk + 1) * 512 + lane * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          // streaming stores: the states are read back by the next kernel,
+          // long after they would have left L2
+          __builtin_nontemporal_store(u32x4_t{hi[0], hi[1], hi[2], hi[3]},
+                                      reinterpret_cast<u32x4_t*>(P + (blk + 0) * 512 + lane * 8));
+          __builtin_nontemporal_store(u32x4_t{lo[0], lo[1], lo[2], lo[3]},
+                                      reinterpret_cast<u32x4_t*>(P + (blk + 1) * 512 + lane * 8));
         }
       }
     if (!SIG && kt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = M2 * kLn2;
@@ -340,8 +345,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   write_state(0, Mst2);
   if (!SIG && tid < TK) p.n_states[((size_t)bh * (Nc + 1)) * DK + kt * TK + tid] = nreg;
 
-  // flattened block sequence: block gi covers steps [tb, tb + TB) of chunk gi / BPC
+  // flattened block sequence: block gi covers steps [tb, tb + TB) of chunk
+  // gi / BPC (BPC = L / TB is a power of two)
   const int BPC = L / TB;
+  const int lbpc = 31 - __builtin_clz(BPC);
   const int NBLK = Nc > 0 ? (Nc - 1) * BPC + (S - (Nc - 1) * L + TB - 1) / TB : 0;
 
   // two register sets of loads in flight
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   uint4 vr[2][VPT];
   auto load_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
     const int row = tb + krs;
     if (row < Lc) {
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   auto stage_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
     if (tb == 0) {
       if (!SIG && c > 0) flush_n();
       const float g2 = g2r[s];
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   float M_mma = Mst2;
   auto mma_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi / BPC, tb = (gi % BPC) * TB;
+    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
     if (tb == 0) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -492,13 +499,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         }
       }
     }
-    if ((gi + 1) % BPC == 0 || gi + 1 == NBLK) write_state(c + 1, M_mma);
+    if (((gi + 1) & (BPC - 1)) == 0 || gi + 1 == NBLK) write_state(c + 1, M_mma);
   };
 
   auto iter = [&](auto par, int gi) {
     constexpr int P = decltype(par)::value;
     constexpr int Q = 1 - P;
-    if (n_pend) finish_n(gi / BPC);
+    if (n_pend) finish_n(gi >> lbpc);
     mma_blk(std::integral_constant<int, P>{}, gi);
     if (gi + 1 < NBLK) stage_blk(std::integral_constant<int, Q>{}, gi + 1);
     if (gi + 3 < NBLK) load_blk(std::integral_constant<int, Q>{}, gi + 3);
