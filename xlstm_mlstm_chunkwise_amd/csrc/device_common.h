@@ -379,6 +379,18 @@ __device__ __forceinline__ uint4 frag_row_u(const uint16_t* X, int ld, int r0, i
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// Raw buffer access: a 128-bit resource (base address, byte extent, 32-bit
+// data format for untyped loads) in scalar registers, a per-lane byte offset
+// and a wave-uniform byte offset.  Reads at or past the extent return zero.
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
 __device__ __forceinline__ float unpack_state_elem_bf16(const uint16_t* P, int k, int v, int DV) {
   const int kk = k >> 4, kr = k & 15, nb = v >> 5, col = v & 31;
   const int h = (kr & 7) >> 2;

@@ -71,98 +71,150 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   uint16_t* const s_v = s_pl + W::P_ELEMS;
   uint16_t* const s_q = s_buf;  // the Q tile, before the key loop
 
-  const int NQT = p.L / TQ;
-  // Workgroups are dealt round-robin to the 8 XCDs; remap so that the tiles
-  // of one chunk (which read the same state, keys and values) are
-  // consecutive on one XCD and share its L2.
-  const int nblk = gridDim.x;
-  int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int vt = bid % NVT;
-  bid /= NVT;
-  const int v0 = vt * TV;
-  const int qt = bid % NQT;
-  bid /= NQT;
-  const int c = bid % p.Nc;
-  const int bh = bid / p.Nc;
   const int S = p.S, L = p.L, Nc = p.Nc;
-  const int t0 = c * L;
-  const int Lc = min(L, S - t0);
-  const int row0 = qt * TQ;
-  if (row0 >= Lc) return;
-  const int kend = min(row0 + TQ, Lc);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, l16 = lane & 15, h2 = lane >> 5, l32 = lane & 31;
+  const int NQT = L / TQ;
   const float scale = p.scale;
+  // Per-lane and per-wave roles.  They are re-derived at the top of every
+  // tile from a laundered thread index, so the compiler rebuilds the offsets
+  // that depend on them instead of keeping them live across the tile loop.
+  int tid, lane, wave, g4, l16, h2, l32;
+  int wr0, wc0;    // P.V / Q.C role: rows wr0 .. wr0+63, columns wc0 .. wc0+WC-1
+  int sr, skb0;    // score-tile role: 16 rows (row block sr) x SKB key blocks
+  int srow;        // row of this lane in the transposed score tile
+  auto set_roles = [&]() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    asm volatile("" : "+s"(w));
+    tid = t;
+    lane = t & 63;
+    wave = w;
+    g4 = lane >> 4;
+    l16 = lane & 15;
+    h2 = lane >> 5;
+    l32 = lane & 31;
+    wr0 = (w / W::NWC) * 64;
+    wc0 = (w % W::NWC) * W::WC;
+    sr = (TQ == 128) ? w : (w & 3);
+    skb0 = (TQ == 128) ? 0 : 2 * (w >> 2);
+    srow = sr * 16 + l16;
+  };
+  set_roles();
 
-  const uint16_t* Q = static_cast<const uint16_t*>(p.Q) + ((size_t)bh * S + t0) * DK;
-  const uint16_t* K = static_cast<const uint16_t*>(p.K) + ((size_t)bh * S + t0) * DK;
-  const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV + v0;
-
-  // P.V / Q.C role: rows wr0 .. wr0+63, columns wc0 .. wc0+WC-1.
-  const int wr0 = (wave / W::NWC) * 64;
-  const int wc0 = (wave % W::NWC) * W::WC;
-
-  // Score-tile role of this wave: 16 rows (row block sr) x SKB key blocks.
-  const int sr = (TQ == 128) ? wave : (wave & 3);
-  const int skb0 = (TQ == 128) ? 0 : 2 * (wave >> 2);
-  const int srow = sr * 16 + l16;  // row of this lane in the transposed score tile
-  const bool srow_ok = row0 + srow < Lc;
-  // Loads in the order they are needed (the memory counter is waited on in
-  // issue order): gate terms and the normaliser, then the Q tile, then the
-  // first chunk-state fragments.
-  constexpr int GPT = (kMaxL + W::NT - 1) / W::NT;  // key positions per thread
-  float gu_r[GPT];
-  const float* gu = p.gu2 + (size_t)bh * S + t0;
-#pragma unroll
-  for (int e = 0; e < GPT; ++e) gu_r[e] = tid + e * W::NT < kend ? gu[tid + e * W::NT] : 0.0f;
-  float gb_r = 0.0f, gpm_r = 0.0f;
-  if (tid < TQ && row0 + tid < kend) {
-    gb_r = p.gb2[(size_t)bh * S + t0 + row0 + tid];
-    if constexpr (!SIG) gpm_r = p.gpm2[(size_t)bh * S + t0 + row0 + tid];
-  }
-  float mprev = 0.0f;
-  if constexpr (!SIG) mprev = p.m_states[(size_t)bh * (Nc + 1) + c];
-  constexpr int NPT = (DK + W::NT - 1) / W::NT;
-  float n_r[NPT];
-  if constexpr (!SIG) {
-    const float* nst = p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
-#pragma unroll
-    for (int e = 0; e < NPT; ++e) n_r[e] = tid + e * W::NT < DK ? nst[tid + e * W::NT] : 0.0f;
-  }
-  // The Q tile (TQ x DK) is staged once in LDS for both the inter-chunk
-  // product and the score tile.
-  constexpr int QPT = TQ * DK / 8 / W::NT;  // 16-byte loads per thread
-  static_assert(TQ * DK / 8 % W::NT == 0, "Q tile split");
-  uint4 qpre[QPT];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = tid + i * W::NT;
-    const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-    qpre[i] = (row0 + rr < Lc) ? *reinterpret_cast<const uint4*>(Q + (size_t)(row0 + rr) * DK + cc)
-                               : make_uint4(0, 0, 0, 0);
-  }
-
-  // ---- first chunk-state fragments
-  const uint16_t* Pst = reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
-  constexpr int PD = W::CB >= 4 ? 1 : 3;  // k steps loaded ahead
-  uint4 bb[NKK][W::CB][2];
-  auto load_k = [&](int kk) {
-#pragma unroll
-    for (int cb = 0; cb < W::CB; ++cb) {
-      const int nb = (v0 + wc0 + 32 * cb) >> 5;
-      bb[kk][cb][0] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 0, DV) + lane * 8);
-      if constexpr (SPLIT) bb[kk][cb][1] = *reinterpret_cast<const uint4*>(Pst + pack_frag_offset(kk, nb, 1, DV) + lane * 8);
+  // ---- persistent schedule.  Tiles are numbered with the column tile
+  // fastest, then the row tile, the chunk and the head, so the tiles of one
+  // chunk (which read the same state, keys and values) are consecutive.
+  // Workgroup b runs on XCD b % 8; each XCD owns a contiguous eighth of the
+  // tiles, and its G workgroups take G consecutive tiles per round (sharing
+  // that XCD's L2), rotated by one each round so no workgroup always gets the
+  // longest (last) row tile of a chunk.
+  const int ntile = p.BH * Nc * NQT * NVT;
+  const int G = gridDim.x;
+  const bool xcd_split = (G & 7) == 0;
+  const int gx = xcd_split ? G >> 3 : G;                  // workgroups per XCD
+  const int x = xcd_split ? (int)blockIdx.x & 7 : 0;
+  const int jw = xcd_split ? (int)blockIdx.x >> 3 : (int)blockIdx.x;
+  const int per_x = xcd_split ? (ntile + 7) >> 3 : ntile;
+  const int tbeg = x * per_x, tend = min(ntile, tbeg + per_x);
+  // tile of round k for this workgroup, or -1 past the end; rows of a
+  // ragged last chunk that hold no data are skipped
+  auto tile_at = [&](int k) -> int {
+    const int t = tbeg + k * gx + (jw + k) % gx;
+    return t < tend ? t : (tbeg + k * gx < tend ? -2 : -1);
+  };
+  auto tile_live = [&](int t) -> bool {
+    const int qt_ = (t / NVT) % NQT;
+    const int c_ = (t / (NVT * NQT)) % Nc;
+    return qt_ * TQ < min(L, S - c_ * L);
+  };
+  int k_round = 0;
+  auto next_tile = [&]() -> int {
+    for (;;) {
+      const int t = tile_at(k_round++);
+      if (t == -1) return -1;
+      if (t >= 0 && tile_live(t)) return t;
     }
   };
-#pragma unroll
-  for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(kk);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- gate terms of this chunk (log2 units, written by the gates kernel):
-  // u for the keys [0, kend); b and the running max of u for this tile's rows.
-  {
+  // ---- requests for one tile, in the order they are needed (the memory
+  // counter is waited on in issue order): gate terms and the normaliser, then
+  // the Q tile.  The first chunk-state fragments follow at the top of the
+  // tile.
+  constexpr int GPT = (kMaxL + W::NT - 1) / W::NT;  // key positions per thread
+  constexpr int NPT = (DK + W::NT - 1) / W::NT;
+  constexpr int QPT = TQ * DK / 8 / W::NT;  // 16-byte Q loads per thread
+  static_assert(TQ * DK / 8 % W::NT == 0, "Q tile split");
+  constexpr int PD = W::CB >= 4 ? 1 : 3;  // k steps of state fragments loaded ahead
+  float gu_r[GPT], n_r[NPT];
+  float gb_r = 0.0f, gpm_r = 0.0f, mprev = 0.0f;
+  uint4 qpre[QPT];
+  uint4 bb[NKK][W::CB][2];
+  auto state_ptr = [&](int bh_, int c_) {
+    return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * (Nc + 1) + c_) * DK * DV * 2;
+  };
+  // Chunk-state fragments through a buffer resource: lane offset and the
+  // wave's first 32-column block in one VGPR, the k step in a scalar offset,
+  // the column block and plane as immediates.
+  auto load_k = [&](__amdgpu_buffer_rsrc_t rs, int v0_, int kk) {
+    const int voff = lane * 16 + ((v0_ + wc0) >> 5) * 2048;
+#pragma unroll
+    for (int cb = 0; cb < W::CB; ++cb) {
+      bb[kk][cb][0] = buf_load16(rs, voff + cb * 2048, kk * DV * 64);
+      if constexpr (SPLIT) bb[kk][cb][1] = buf_load16(rs, voff + cb * 2048 + 1024, kk * DV * 64);
+    }
+  };
+  auto state_rsrc = [&](int bh_, int c_) { return make_rsrc(state_ptr(bh_, c_), (uint32_t)(DK * DV * 4)); };
+  auto request = [&](int t) {
+    const int vt_ = t % NVT, qt_ = (t / NVT) % NQT;
+    const int c_ = (t / (NVT * NQT)) % Nc, bh_ = t / (NVT * NQT * Nc);
+    const int t0_ = c_ * L, Lc_ = min(L, S - t0_), row0_ = qt_ * TQ, kend_ = min(row0_ + TQ, Lc_);
+    const size_t gbase = (size_t)bh_ * S + t0_;
+#pragma unroll
+    for (int e = 0; e < GPT; ++e) gu_r[e] = tid + e * W::NT < kend_ ? p.gu2[gbase + tid + e * W::NT] : 0.0f;
+    gb_r = gpm_r = 0.0f;
+    if (tid < TQ && row0_ + tid < kend_) {
+      gb_r = p.gb2[gbase + row0_ + tid];
+      if constexpr (!SIG) gpm_r = p.gpm2[gbase + row0_ + tid];
+    }
+    if constexpr (!SIG) {
+      mprev = p.m_states[(size_t)bh_ * (Nc + 1) + c_];
+      const float* nst = p.n_states + ((size_t)bh_ * (Nc + 1) + c_) * DK;
+#pragma unroll
+      for (int e = 0; e < NPT; ++e) n_r[e] = tid + e * W::NT < DK ? nst[tid + e * W::NT] : 0.0f;
+    }
+    // the Q tile is contiguous; rows past the chunk read as zero
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.Q) + (gbase + row0_) * DK,
+                                                (uint32_t)((Lc_ - row0_) * DK * 2));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16(rq, tid * 16, i * W::NT * 16);
+  };
+
+  int tile = next_tile();
+  if (tile < 0) return;
+  request(tile);
+
+  for (;;) {
+    __builtin_amdgcn_sched_barrier(0);
+    set_roles();
+    const int vt = tile % NVT;
+    const int qt = (tile / NVT) % NQT;
+    const int c = (tile / (NVT * NQT)) % Nc;
+    const int bh = tile / (NVT * NQT * Nc);
+    const int v0 = vt * TV;
+    const int t0 = c * L;
+    const int Lc = min(L, S - t0);
+    const int row0 = qt * TQ;
+    const int kend = min(row0 + TQ, Lc);
+    const bool srow_ok = row0 + srow < Lc;
+    const uint16_t* K = static_cast<const uint16_t*>(p.K) + ((size_t)bh * S + t0) * DK;
+    const uint16_t* V = static_cast<const uint16_t*>(p.V) + ((size_t)bh * S + t0) * DV + v0;
+    const __amdgpu_buffer_rsrc_t rst = state_rsrc(bh, c);
+#pragma unroll
+    for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(rst, v0, kk);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- gate terms of this chunk (log2 units, written by the gates kernel):
+    // u for the keys [0, kend); b and the running max of u for this tile's rows.
 #pragma unroll
     for (int e = 0; e < GPT; ++e)
       if (tid + e * W::NT < kend) s_u2[tid + e * W::NT] = gu_r[e];
@@ -198,289 +250,282 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       *reinterpret_cast<uint4*>(s_q + rr * W::LDQ + cc) = qpre[i];
     }
     __syncthreads();
-  }
-  float16_t acc[2][W::CB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < W::CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
-  // ---- inter-chunk term: acc = Q . C with the packed state fragments; the Q
-  // rows use the same contraction-slot order as the packed state.
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (kk + PD < NKK) load_k(kk + PD);
-    // keep the prefetch ahead of this step's products (the scheduler would
-    // otherwise sink the loads next to their use to save registers)
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8_t qa[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const uint16_t* qp = s_q + (wr0 + 32 * rb + l32) * W::LDQ + 16 * kk + 4 * h2;
-      const uint2 x0 = *reinterpret_cast<const uint2*>(qp);
-      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 8);
-      qa[rb] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-    }
-#pragma unroll
-    for (int cb = 0; cb < W::CB; ++cb) {
-      const bf16x8_t bh_ = as_bf16x8(bb[kk][cb][0]);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bh_, acc[rb][cb]);
-      if constexpr (SPLIT) {
-        const bf16x8_t bl_ = as_bf16x8(bb[kk][cb][1]);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bl_, acc[rb][cb]);
-      }
-    }
-  }
-  // this lane's Q row as B fragments of the transposed score tile
-  uint4 qs[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qs[ks] = *reinterpret_cast<const uint4*>(s_q + srow * W::LDQ + 32 * ks + 8 * g4);
-  __syncthreads();  // the Q tile's LDS is reused for K, P and V below
-  // scale row by e^{b + M - m} * s
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      const float w = s_row_w[row] * scale;
-#pragma unroll
-      for (int cb = 0; cb < W::CB; ++cb) acc[rb][cb][r] *= w;
-    }
-
-  // normaliser contribution of the state: s e^{b + M - m} q . n
-  float den_part = 0.0f;
-  if constexpr (!SIG) {
-    if (skb0 == 0 && srow_ok) {
-      float d = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 u = qs[ks];
-        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d += __uint_as_float(ww[e] << 16) * s_n[32 * ks + 8 * g4 + 2 * e];
-          d += __uint_as_float(ww[e] & 0xffff0000u) * s_n[32 * ks + 8 * g4 + 2 * e + 1];
-        }
-      }
-      den_part = d * scale * s_row_w[srow];
-    }
-  }
-
-  // ---- intra-chunk term over key tiles [0, kend)
-  const float r2 = s_row_r2[srow];
-  const int tau = row0 + srow;
-  const int ntiles = (kend + W::TKV - 1) / W::TKV;
-  // K and V tiles (64 rows) are prefetched into registers one tile ahead.
-  constexpr int KPT = W::TKV * DK / 8 / W::NT;  // 16-byte K loads per thread
-  constexpr int VPT = W::TKV * TV / 8 / W::NT;  // 16-byte V loads per thread
-  static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * TV / 8 % W::NT == 0, "tile split");
-  uint4 kpre[KPT], vpre[VPT];
-  auto load_kv = [&](int s0) {
-    if (s0 + W::TKV <= Lc) {  // full tile: no row checks
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int idx = tid + i * W::NT;
-        const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-        kpre[i] = *reinterpret_cast<const uint4*>(K + (size_t)(s0 + rr) * DK + cc);
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int idx = tid + i * W::NT;
-        const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
-        vpre[i] = *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int idx = tid + i * W::NT;
-        const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-        kpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(K + (size_t)(s0 + rr) * DK + cc)
-                                 : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int idx = tid + i * W::NT;
-        const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
-        vpre[i] = (s0 + rr < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(s0 + rr) * DV + cc)
-                                 : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  if (ntiles > 0) load_kv(0);
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int s0 = j * W::TKV;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * W::NT;
-      const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-      *reinterpret_cast<uint4*>(s_k + rr * W::LDK + cc) = kpre[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * W::NT;
-      const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
-      *reinterpret_cast<uint4*>(s_v + rr * W::LDV + cc) = vpre[i];
-    }
-    if (j + 1 < ntiles) load_kv(s0 + W::TKV);
-    __syncthreads();
-
-    // transposed scores for 16 rows x SKB key blocks; P to LDS as hi/lo planes
-    float4_t sacc[W::SKB];
-    bool live[W::SKB];
-    bool all_live = true;
-#pragma unroll
-    for (int kb = 0; kb < W::SKB; ++kb) {
-      const int key0 = s0 + 16 * (skb0 + kb);
-      sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      live[kb] = key0 <= row0 + sr * 16 + 15 && key0 < kend;  // wave-uniform
-      all_live = all_live && live[kb];
-    }
-    if (all_live) {
-      // independent accumulation chains, interleaved
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < W::SKB; ++kb) {
-          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
-          sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < W::SKB; ++kb) {
-        if (!live[kb]) continue;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
-          sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < W::SKB; ++kb) {
-      const int sb = skb0 + kb;
-      const int key0 = s0 + 16 * sb;
-      const float4 u4 = *reinterpret_cast<const float4*>(s_u2 + key0 + 4 * g4);
-      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
-      float val[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int sg = key0 + 4 * g4 + r;
-        const float pv = scale * sacc[kb][r] * __builtin_amdgcn_exp2f(r2 + uu[r]);
-        val[r] = (live[kb] && sg <= tau && tau < kend) ? pv : 0.0f;
-        den_part += val[r];
-      }
-      uint2 ph, pl;
-      if constexpr (SPLIT) {
-        split_bf16x2(val[0], val[1], ph.x, pl.x);
-        split_bf16x2(val[2], val[3], ph.y, pl.y);
-        *reinterpret_cast<uint2*>(s_pl + srow * W::LDP + 16 * sb + 4 * g4) = pl;
-      } else {
-        ph.x = round_bf16x2(val[0], val[1]);
-        ph.y = round_bf16x2(val[2], val[3]);
-      }
-      *reinterpret_cast<uint2*>(s_ph + srow * W::LDP + 16 * sb + 4 * g4) = ph;
-    }
-    __syncthreads();
-
-    // acc += P . V over 16-key steps
-#pragma unroll
-    for (int kk = 0; kk < W::TKV / 16; ++kk) {
-      const int key0 = s0 + 16 * kk;
-      if (key0 > row0 + wr0 + 63 || key0 >= kend) continue;  // wave-uniform: all zero
-      uint4 ah[2], al[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        ah[rb] = frag_row_u(s_ph, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
-        if constexpr (SPLIT) al[rb] = frag_row_u(s_pl, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
-      }
-#pragma unroll
-      for (int cb = 0; cb < W::CB; ++cb) {
-        const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, W::LDV, 16 * kk, wc0 + 32 * cb, lane));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          acc[rb][cb] = mma32b(as_bf16x8(ah[rb]), bv, acc[rb][cb]);
-          if constexpr (SPLIT) acc[rb][cb] = mma32b(as_bf16x8(al[rb]), bv, acc[rb][cb]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- normaliser per row, then H
-  if constexpr (!SIG) {
-    den_part += __shfl_xor(den_part, 16, 64);
-    den_part += __shfl_xor(den_part, 32, 64);
-    if (g4 == 0) {
-      if (TQ == 128 || skb0 == 0) s_row_den[srow] = den_part;
-      else s_den2[srow] = den_part;
-    }
-    __syncthreads();
-    if (tid < TQ) {
-      float d = s_row_den[tid];
-      if (TQ != 128) d += s_den2[tid];
-      s_row_den[tid] = d;
-      // reciprocal of the normaliser, reused for every column of the row
-      s_den2[tid] = 1.0f / (fmaxf(fabsf(d), exp2f(-s_row_m2[tid])) + p.eps);
-    }
-  }
-  __syncthreads();
-  // Each accumulator register holds one row of 32 consecutive columns across
-  // a half-wave, so each store writes two full 128-byte row segments.  Row
-  // offsets are compile-time multiples of DV; only a ragged last tile checks
-  // rows.
-  auto store_h = [&](auto zero, auto ragged) {
-    using OutT = decltype(zero);
-    OutT* const hp = static_cast<OutT*>(p.H) + ((size_t)bh * S + t0 + row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32;
+    float16_t acc[2][W::CB];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rowl = 32 * rb + 8 * r4;  // + 4 * h2 + q: row within the wave's 64
-        float4 inv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        if constexpr (!SIG) inv = *reinterpret_cast<const float4*>(s_den2 + wr0 + rowl + 4 * h2);
-        const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
+      for (int cb = 0; cb < W::CB; ++cb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (decltype(ragged)::value) {
-            if (row0 + wr0 + rowl + 4 * h2 + q >= Lc) continue;
+        for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
+
+    // ---- inter-chunk term: acc = Q . C with the packed state fragments; the Q
+    // rows use the same contraction-slot order as the packed state.
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + PD < NKK) load_k(rst, v0, kk + PD);
+      // keep the prefetch ahead of this step's products (the scheduler would
+      // otherwise sink the loads next to their use to save registers)
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t qa[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const uint16_t* qp = s_q + (wr0 + 32 * rb + l32) * W::LDQ + 16 * kk + 4 * h2;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(qp);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 8);
+        qa[rb] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+      }
+#pragma unroll
+      for (int cb = 0; cb < W::CB; ++cb) {
+        const bf16x8_t bh_ = as_bf16x8(bb[kk][cb][0]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bh_, acc[rb][cb]);
+        if constexpr (SPLIT) {
+          const bf16x8_t bl_ = as_bf16x8(bb[kk][cb][1]);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bl_, acc[rb][cb]);
+        }
+      }
+    }
+    // this lane's Q row as B fragments of the transposed score tile
+    uint4 qs[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qs[ks] = *reinterpret_cast<const uint4*>(s_q + srow * W::LDQ + 32 * ks + 8 * g4);
+    __syncthreads();  // the Q tile's LDS is reused for K, P and V below
+    // scale row by e^{b + M - m} * s
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const float w = s_row_w[row] * scale;
+#pragma unroll
+        for (int cb = 0; cb < W::CB; ++cb) acc[rb][cb][r] *= w;
+      }
+
+    // normaliser contribution of the state: s e^{b + M - m} q . n
+    float den_part = 0.0f;
+    if constexpr (!SIG) {
+      if (skb0 == 0 && srow_ok) {
+        float d = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 u = qs[ks];
+          const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d += __uint_as_float(ww[e] << 16) * s_n[32 * ks + 8 * g4 + 2 * e];
+            d += __uint_as_float(ww[e] & 0xffff0000u) * s_n[32 * ks + 8 * g4 + 2 * e + 1];
           }
+        }
+        den_part = d * scale * s_row_w[srow];
+      }
+    }
+
+    // ---- intra-chunk term over key tiles [0, kend)
+    const float r2 = s_row_r2[srow];
+    const int tau = row0 + srow;
+    const int ntiles = (kend + W::TKV - 1) / W::TKV;
+    // K and V tiles (64 rows) are prefetched into registers one tile ahead.
+    constexpr int KPT = W::TKV * DK / 8 / W::NT;  // 16-byte K loads per thread
+    constexpr int VPT = W::TKV * TV / 8 / W::NT;  // 16-byte V loads per thread
+    static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * TV / 8 % W::NT == 0, "tile split");
+    uint4 kpre[KPT], vpre[VPT];
+    // K and V of this chunk through buffer resources: rows past the chunk
+    // read as zero.  One lane offset each; the tile start and the 16-byte
+    // step of the thread's i-th load in scalar offsets.
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, (uint32_t)(Lc * DK * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, (uint32_t)((Lc - 1) * DV * 2 + TV * 2));
+    const int vvoff = (tid / (TV / 8)) * DV * 2 + (tid % (TV / 8)) * 16;
+    auto load_kv = [&](int s0) {
 #pragma unroll
-          for (int cb = 0; cb < W::CB; ++cb) {
-            const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
-            OutT* const dst = hp + (size_t)(rowl + q) * DV + 32 * cb;
-            // H is written once and not read again here: streaming stores
-            // keep the chunk states and K/V tiles the neighbours re-read in L2
-            if constexpr (sizeof(OutT) == 2) __builtin_nontemporal_store(f32_to_bf16(hv), dst);
-            else __builtin_nontemporal_store(hv, dst);
+      for (int i = 0; i < KPT; ++i) kpre[i] = buf_load16(rk, tid * 16, s0 * DK * 2 + i * W::NT * 16);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) vpre[i] = buf_load16(rv, vvoff, (s0 + i * (W::NT / (TV / 8))) * DV * 2);
+    };
+    if (ntiles > 0) load_kv(0);
+
+    for (int j = 0; j < ntiles; ++j) {
+      const int s0 = j * W::TKV;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+        *reinterpret_cast<uint4*>(s_k + rr * W::LDK + cc) = kpre[i];
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int idx = tid + i * W::NT;
+        const int rr = idx / (TV / 8), cc = (idx % (TV / 8)) * 8;
+        *reinterpret_cast<uint4*>(s_v + rr * W::LDV + cc) = vpre[i];
+      }
+      if (j + 1 < ntiles) load_kv(s0 + W::TKV);
+      __syncthreads();
+
+      // transposed scores for 16 rows x SKB key blocks; P to LDS as hi/lo planes
+      float4_t sacc[W::SKB];
+      bool live[W::SKB];
+      bool all_live = true;
+#pragma unroll
+      for (int kb = 0; kb < W::SKB; ++kb) {
+        const int key0 = s0 + 16 * (skb0 + kb);
+        sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        live[kb] = key0 <= row0 + sr * 16 + 15 && key0 < kend;  // wave-uniform
+        all_live = all_live && live[kb];
+      }
+      if (all_live) {
+        // independent accumulation chains, interleaved
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < W::SKB; ++kb) {
+            const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
+            sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < W::SKB; ++kb) {
+          if (!live[kb]) continue;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * (skb0 + kb) + l16) * W::LDK + 32 * ks + 8 * g4);
+            sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs[ks]), sacc[kb]);
           }
         }
       }
-  };
-  const bool full = row0 + wr0 + 64 <= Lc;  // wave-uniform
-  if (p.h_bf16) {
-    if (full) store_h(uint16_t{0}, std::false_type{});
-    else store_h(uint16_t{0}, std::true_type{});
-  } else {
-    if (full) store_h(0.0f, std::false_type{});
-    else store_h(0.0f, std::true_type{});
-  }
-  if constexpr (!SIG) {
-    if (vt == 0 && tid < TQ && row0 + tid < Lc) {
-      const size_t ro = (size_t)bh * S + t0 + row0 + tid;
-      if (p.m_rows) p.m_rows[ro] = s_row_m2[tid] * kLn2;
-      if (p.den_rows) p.den_rows[ro] = s_row_den[tid];
+#pragma unroll
+      for (int kb = 0; kb < W::SKB; ++kb) {
+        const int sb = skb0 + kb;
+        const int key0 = s0 + 16 * sb;
+        const float4 u4 = *reinterpret_cast<const float4*>(s_u2 + key0 + 4 * g4);
+        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+        float val[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sg = key0 + 4 * g4 + r;
+          const float pv = scale * sacc[kb][r] * __builtin_amdgcn_exp2f(r2 + uu[r]);
+          val[r] = (live[kb] && sg <= tau && tau < kend) ? pv : 0.0f;
+          den_part += val[r];
+        }
+        uint2 ph, pl;
+        if constexpr (SPLIT) {
+          split_bf16x2(val[0], val[1], ph.x, pl.x);
+          split_bf16x2(val[2], val[3], ph.y, pl.y);
+          *reinterpret_cast<uint2*>(s_pl + srow * W::LDP + 16 * sb + 4 * g4) = pl;
+        } else {
+          ph.x = round_bf16x2(val[0], val[1]);
+          ph.y = round_bf16x2(val[2], val[3]);
+        }
+        *reinterpret_cast<uint2*>(s_ph + srow * W::LDP + 16 * sb + 4 * g4) = ph;
+      }
+      __syncthreads();
+
+      // acc += P . V over 16-key steps
+#pragma unroll
+      for (int kk = 0; kk < W::TKV / 16; ++kk) {
+        const int key0 = s0 + 16 * kk;
+        if (key0 > row0 + wr0 + 63 || key0 >= kend) continue;  // wave-uniform: all zero
+        uint4 ah[2], al[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          ah[rb] = frag_row_u(s_ph, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
+          if constexpr (SPLIT) al[rb] = frag_row_u(s_pl, W::LDP, wr0 + 32 * rb, 16 * kk, lane);
+        }
+#pragma unroll
+        for (int cb = 0; cb < W::CB; ++cb) {
+          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, W::LDV, 16 * kk, wc0 + 32 * cb, lane));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            acc[rb][cb] = mma32b(as_bf16x8(ah[rb]), bv, acc[rb][cb]);
+            if constexpr (SPLIT) acc[rb][cb] = mma32b(as_bf16x8(al[rb]), bv, acc[rb][cb]);
+          }
+        }
+      }
+      __syncthreads();
     }
+
+    // the next tile's gate terms and Q tile are requested now and land
+    // while this tile's epilogue runs
+    const int next = next_tile();
+    if (next >= 0) request(next);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- normaliser per row, then H
+    if constexpr (!SIG) {
+      den_part += __shfl_xor(den_part, 16, 64);
+      den_part += __shfl_xor(den_part, 32, 64);
+      if (g4 == 0) {
+        if (TQ == 128 || skb0 == 0) s_row_den[srow] = den_part;
+        else s_den2[srow] = den_part;
+      }
+      __syncthreads();
+      if (tid < TQ) {
+        float d = s_row_den[tid];
+        if (TQ != 128) d += s_den2[tid];
+        s_row_den[tid] = d;
+        // reciprocal of the normaliser, reused for every column of the row
+        s_den2[tid] = 1.0f / (fmaxf(fabsf(d), exp2f(-s_row_m2[tid])) + p.eps);
+      }
+    }
+    __syncthreads();
+    // Each accumulator register holds one row of 32 consecutive columns across
+    // a half-wave, so each store writes two full 128-byte row segments.  Row
+    // offsets are compile-time multiples of DV; only a ragged last tile checks
+    // rows.
+    // H through a buffer resource spanning this chunk's rows: stores to rows
+    // past the chunk fall outside it and are dropped.  Each accumulator
+    // register holds one row of 32 consecutive columns across a half-wave, so
+    // each store writes two full 128-byte row segments; the row offsets are
+    // compile-time multiples of DV in scalar offsets.
+    auto store_h = [&](auto esize) {
+      constexpr int E = decltype(esize)::value;
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(static_cast<const char*>(p.H) + ((size_t)bh * S + t0) * DV * E,
+                                                  (uint32_t)(Lc * DV * E));
+      const int hvoff = ((row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32) * E;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rowl = 32 * rb + 8 * r4;  // + 4 * h2 + q: row within the wave's 64
+          float4 inv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          if constexpr (!SIG) inv = *reinterpret_cast<const float4*>(s_den2 + wr0 + rowl + 4 * h2);
+          const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int cb = 0; cb < W::CB; ++cb) {
+              const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
+              if constexpr (E == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 0);
+            }
+          }
+        }
+    };
+    if (p.h_bf16) store_h(std::integral_constant<int, 2>{});
+    else store_h(std::integral_constant<int, 4>{});
+    if constexpr (!SIG) {
+      if (vt == 0 && tid < TQ && row0 + tid < Lc) {
+        const size_t ro = (size_t)bh * S + t0 + row0 + tid;
+        if (p.m_rows) p.m_rows[ro] = s_row_m2[tid] * kLn2;
+        if (p.den_rows) p.den_rows[ro] = s_row_den[tid];
+      }
+    }
+    if (next < 0) break;
+    tile = next;
+    __syncthreads();  // the epilogue's LDS reads precede the next tile's writes
   }
 }
 
 template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT>
 hipError_t launch_t(const HintraParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)(p.BH * p.Nc * (p.L / TQ) * (DV / TV)));
+  // One workgroup per CU walks the tiles (the LDS footprint allows one per
+  // CU); fewer when there are fewer tiles.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long long ntile = (long long)p.BH * p.Nc * (p.L / TQ) * (DV / TV);
+  dim3 grid((unsigned)(ntile < cus ? ntile : cus));
   hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
