@@ -149,9 +149,11 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
  * states per head of DHQK x DHV values, DHQK normaliser values and one
  * max-state (exp gate), each region 256-byte aligned; 4 bytes per value, 8
  * with MLSTM_PREC_F64.  For MLSTM_FAMILY_WIDE it also holds per-position gate
- * terms, written by stage one and read by stage two: 12 bytes per position
- * and head for the exp gate, 8 for the sig gate (one more 256-aligned
- * region).  Returns 0 for an invalid descriptor.  The storage order inside
+ * terms, written by stage one and read by stage two (12 bytes per position
+ * and head for the exp gate, 8 for the sig gate), and 4 bytes per chunk
+ * boundary and head for the stabilisers of sequence segments that stage one
+ * may run side by side (two more 256-aligned regions).  Returns 0 for an
+ * invalid descriptor.  The storage order inside
  * the workspace belongs to the library (the chunk states are kept in the
  * operand order of the kernels that read them); mlstm_fw_unpack_states
  * returns the states as plain float32. */

@@ -69,14 +69,16 @@ def test_valid_descriptor_and_workspace_size():
     assert mt.workspace_bytes(d) == expect
     ds = _desc(gate="sig")
     assert mt.workspace_bytes(ds) == r256(BH * (Nc + 1) * 128 * 64 * 4)
-    # wide-tile family: one more region of per-position gate terms
+    # wide-tile family: regions of per-position gate terms and of the
+    # stabilisers of segment-local state runs
     dw = _desc(DHQK=256, DHV=512, chunk_size=256)
     Ncw = (1000 + 255) // 256
     expect_w = (r256(BH * (Ncw + 1) * 256 * 512 * 4) + r256(BH * (Ncw + 1) * 256 * 4) + r256(BH * (Ncw + 1) * 4)
-                + r256(BH * 1000 * 4 * 3))
+                + r256(BH * 1000 * 4 * 3) + r256(BH * (Ncw + 1) * 4))
     assert mt.workspace_bytes(dw) == expect_w
     dws = _desc(DHQK=256, DHV=512, chunk_size=256, gate="sig")
-    assert mt.workspace_bytes(dws) == r256(BH * (Ncw + 1) * 256 * 512 * 4) + r256(BH * 1000 * 4 * 2)
+    assert mt.workspace_bytes(dws) == (r256(BH * (Ncw + 1) * 256 * 512 * 4) + r256(BH * 1000 * 4 * 2)
+                                       + r256(BH * (Ncw + 1) * 4))
     assert mt.validate(_desc(S=0)) == 0
     assert mt.num_chunks(_desc(S=0)) == 0
 

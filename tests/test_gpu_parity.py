@@ -152,6 +152,9 @@ MANY_HEADS = [
     ("rows_exp_d128_v512", dict(B=16, NH=8, S=130, DHQK=128, DHV=512, chunk=64)),
     ("rows_exp_d256_v256", dict(B=16, NH=8, S=270, DHQK=256, DHV=256, chunk=256, init_state=True)),
     ("rows_sig_d128_v256", dict(gate="sig", B=32, NH=8, S=100, DHQK=128, DHV=256, chunk=64)),
+    # fewer heads: the sequence is cut into segments of several chunks
+    ("segments_exp_d256_v512", dict(B=4, NH=4, S=620, DHQK=256, DHV=512, chunk=64, init_state=True)),
+    ("segments_sig_d128_v256", dict(gate="sig", B=2, NH=16, S=700, DHQK=128, DHV=256, chunk=64)),
 ]
 
 
@@ -248,13 +251,20 @@ def test_bf16_h_output(mt):
     _compare(w, gpu, ref, "bf16 H", h_bf16=True)
 
 
-@pytest.mark.parametrize("shape", [dict(DHQK=128, DHV=128, chunk=128), dict(DHQK=256, DHV=512, chunk=128),
-                                   dict(DHQK=128, DHV=256, chunk=64, gate="sig")],
-                         ids=["rowmajor_states", "packed_states", "packed_states_sig"])
+@pytest.mark.parametrize("shape", [
+    dict(DHQK=128, DHV=128, chunk=128), dict(DHQK=256, DHV=512, chunk=128),
+    dict(DHQK=128, DHV=256, chunk=64, gate="sig"),
+    # enough heads for several chunks per sequence segment (interior joins)
+    dict(B=4, NH=4, S=620, DHQK=256, DHV=512, chunk=64),
+    dict(B=2, NH=16, S=700, DHQK=128, DHV=256, chunk=64, gate="sig")],
+    ids=["rowmajor_states", "packed_states", "packed_states_sig", "segments_exp", "segments_sig"])
 def test_stage_states_match_oracle_chunk_states(mt, shape):
     """Stage one's chunk states (unpacked to float32) against the oracle's."""
+    shape = dict(shape)
     gate = shape.pop("gate", "exp")
-    w = _small_workload(dict(B=1, NH=2, S=450, init_state=True, gate=gate, **shape))
+    base = dict(B=1, NH=2, S=450)
+    base.update(shape)
+    w = _small_workload(dict(init_state=True, gate=gate, **base))
     x = make_inputs(w)
     k, v = _to_dev(x["k"], torch.bfloat16), _to_dev(x["v"], torch.bfloat16)
     q = _to_dev(x["q"], torch.bfloat16)
@@ -267,25 +277,27 @@ def test_stage_states_match_oracle_chunk_states(mt, shape):
     Cst, nst, mst = mt.unpack_states(q, v, ws, chunk_size=w.chunk, gate=gate)
     torch.cuda.synchronize()
     Cst = Cst.cpu().numpy()
-    for h in range(2):
-        args = [x[nm][0, h].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
+    for (b, h) in sorted({(0, 0), (0, 1), (w.B - 1, w.NH - 1), (w.B // 2, w.NH // 2)}):
+        args = [x[nm][b, h].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
         if gate == "exp":
-            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][0, h], x["n0"][0, h], x["m0"][0, h],
+            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][b, h], x["n0"][b, h], x["m0"][b, h],
                                                          chunk_size=w.chunk, return_states=True)
         else:
-            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][0, h], gate="sig",
+            Hr, Cr, nr, mr, (Cs, ns, Ms) = chunkwise_fw(*args, x["C0"][b, h], gate="sig",
                                                          chunk_size=w.chunk, return_states=True)
         Nc = Cs.shape[0]
         assert Cst.shape[2] == Nc + 1
         ref_C = np.concatenate([Cs, Cr[None]], axis=0)
         scale = max(1.0, np.abs(ref_C).max())
-        assert np.abs(Cst[0, h] - ref_C).max() / scale <= TOL_C["bf16"]
-        assert np.abs(C.cpu().numpy()[0, h] - Cr).max() / max(1.0, np.abs(Cr).max()) <= TOL_C["bf16"]
+        assert np.abs(Cst[b, h] - ref_C).max() / scale <= TOL_C["bf16"]
+        assert np.abs(C.cpu().numpy()[b, h] - Cr).max() / max(1.0, np.abs(Cr).max()) <= TOL_C["bf16"]
         if gate == "exp":
             ref_n = np.concatenate([ns, nr[None]], axis=0)
             ref_M = np.concatenate([Ms, [mr]], axis=0)
-            np.testing.assert_allclose(mst.cpu().numpy()[0, h], ref_M, atol=TOL_M["bf16"], rtol=0)
-            assert np.abs(nst.cpu().numpy()[0, h] - ref_n).max() / max(1.0, np.abs(ref_n).max()) <= TOL_C["bf16"]
+            np.testing.assert_allclose(mst.cpu().numpy()[b, h], ref_M, atol=TOL_M["bf16"], rtol=0)
+            assert np.abs(nst.cpu().numpy()[b, h] - ref_n).max() / max(1.0, np.abs(ref_n).max()) <= TOL_C["bf16"]
+            assert abs(m.cpu().numpy()[b, h] - mr) <= TOL_M["bf16"]
+            assert np.abs(n.cpu().numpy()[b, h] - nr).max() / max(1.0, np.abs(nr).max()) <= TOL_C["bf16"]
 
 
 @pytest.mark.parametrize("wide", [False, True], ids=["generic", "wide"])

@@ -54,7 +54,7 @@ int validate_desc(const mlstm_fw_desc_t* d) {
 }
 
 struct WsLayout {
-  size_t c_off, n_off, m_off, g_off, total;
+  size_t c_off, n_off, m_off, g_off, ml_off, total;
 };
 
 bool packed_layout(const mlstm_fw_desc_t* d);
@@ -73,6 +73,9 @@ WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   // per-position gate terms shared by the two wide-tile stages
   w.g_off = off;
   if (packed_layout(d)) off += round_up(BH * (size_t)d->S * sizeof(float) * (d->gate == MLSTM_GATE_EXP ? 3 : 2), 256);
+  // stabilisers of segment-local runs of the states kernel
+  w.ml_off = off;
+  if (packed_layout(d)) off += round_up(BH * Nc1 * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -108,6 +111,7 @@ struct WsPtrs {
   float* gb2;  // gate terms (wide-tile path), else null
   float* gu2;
   float* gpm2;
+  float* m_local;  // segment-local stabilisers (wide-tile path), else null
 };
 
 WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
@@ -117,8 +121,9 @@ WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
   r.C = reinterpret_cast<float*>(ws + w.c_off);
   r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
   r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
-  r.gb2 = r.gu2 = r.gpm2 = nullptr;
+  r.gb2 = r.gu2 = r.gpm2 = r.m_local = nullptr;
   if (packed_layout(d)) {
+    r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
     const size_t n = (size_t)d->B * d->NH * d->S;
     r.gb2 = reinterpret_cast<float*>(ws + w.g_off);
     r.gu2 = r.gb2 + n;
@@ -154,12 +159,15 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   p.gb2 = ws.gb2;
   p.gu2 = ws.gu2;
   p.gpm2 = ws.gpm2;
+  p.m_local = ws.m_local;
   p.BH = d->B * d->NH;
   p.S = d->S;
   p.DK = d->DHQK;
   p.DV = d->DHV;
   p.L = d->chunk_size;
   p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  p.nseg = 1;
+  p.cps = p.Nc;
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
   const bool sig = d->gate == MLSTM_GATE_SIG;
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;

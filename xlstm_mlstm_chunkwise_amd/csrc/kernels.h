@@ -34,7 +34,9 @@ struct StatesParams {
   const float* gb2;  // gate terms (wide-tile kernels only)
   const float* gu2;
   const float* gpm2;
+  float* m_local;    // (BH, Nc + 1) stabiliser of segment-local runs, log2 units (wide family)
   int BH, S, DK, DV, L, Nc;
+  int nseg, cps;     // sequence segments per head and chunks per segment (row-tile kernel)
 };
 
 struct HintraParams {

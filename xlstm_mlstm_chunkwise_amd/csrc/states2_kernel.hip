@@ -289,11 +289,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   int bid = blockIdx.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int kt = bid % NTK;
-  const int bh = bid / NTK;
+  const int seg = (bid / NTK) % p.nseg;
+  const int bh = bid / (NTK * p.nseg);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
   const int S = p.S, DK = p.DK, L = p.L, Nc = p.Nc;
   constexpr int DV = TV;
+  // Chunks [c_beg, c_end) of this head.  With several segments, segment 0 starts
+  // from the initial state and later ones from zero (stabiliser -inf); their
+  // chunk states are local and the join kernels turn them into the true ones.
+  const bool segmented = p.nseg > 1;
+  const int c_beg = seg * p.cps;
+  const int c_end = min(Nc, c_beg + p.cps);
   const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;  // inside the tile
   const uint16_t* K = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK + kt * TK;
   const uint16_t* V = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV;
@@ -309,12 +316,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int r = 0; r < 16; ++r) {
         const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
         const int vcol = wc0 + 32 * cb + l32;
-        acc[rb][cb][r] = p.C0 ? p.C0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] : 0.0f;
+        acc[rb][cb][r] = (p.C0 && seg == 0) ? p.C0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] : 0.0f;
       }
   float nreg = 0.0f;  // n for key row kt * TK + tid (tid < TK)
-  if (!SIG && tid < TK && p.n0) nreg = p.n0[(size_t)bh * DK + kt * TK + tid];
+  if (!SIG && tid < TK && p.n0 && seg == 0) nreg = p.n0[(size_t)bh * DK + kt * TK + tid];
   float Mst2 = 0.0f;  // stabiliser (log2 units) after the last chunk begun by the staging side
   if (!SIG && p.m0) Mst2 = p.m0[bh] * kLog2e;
+  if (!SIG && seg > 0) Mst2 = -INFINITY;
 
   auto write_state = [&](int entry, float M2) {
     uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + entry) * DK * DV * 2;
@@ -340,16 +348,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
                                       reinterpret_cast<u32x4_t*>(P + (blk + 1) * 512 + lane * 8));
         }
       }
-    if (!SIG && kt == 0 && tid == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = M2 * kLn2;
+    if (!SIG && kt == 0 && tid == 0) {
+      if (seg == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = M2 * kLn2;
+      if (segmented) p.m_local[(size_t)bh * (Nc + 1) + entry] = M2;
+    }
   };
-  write_state(0, Mst2);
-  if (!SIG && tid < TK) p.n_states[((size_t)bh * (Nc + 1)) * DK + kt * TK + tid] = nreg;
+  if (seg == 0) {
+    write_state(0, Mst2);
+    if (!SIG && tid < TK) p.n_states[((size_t)bh * (Nc + 1)) * DK + kt * TK + tid] = nreg;
+  }
 
-  // flattened block sequence: block gi covers steps [tb, tb + TB) of chunk
-  // gi / BPC (BPC = L / TB is a power of two)
+  // flattened block sequence over this segment: block gi covers steps
+  // [tb, tb + TB) of chunk c_beg + gi / BPC (BPC = L / TB is a power of two)
   const int BPC = L / TB;
   const int lbpc = 31 - __builtin_clz(BPC);
-  const int NBLK = Nc > 0 ? (Nc - 1) * BPC + (S - (Nc - 1) * L + TB - 1) / TB : 0;
+  const int NBLK = c_end > c_beg ? (c_end - c_beg - 1) * BPC + (min(L, S - (c_end - 1) * L) + TB - 1) / TB : 0;
 
   // two register sets of loads in flight
   KVec kr[2];
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   uint4 vr[2][VPT];
   auto load_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
+    const int c = c_beg + (gi >> lbpc), tb = (gi & (BPC - 1)) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
     const int row = tb + krs;
     if (row < Lc) {
@@ -419,9 +432,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   auto stage_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
+    const int c = c_beg + (gi >> lbpc), tb = (gi & (BPC - 1)) * TB;
     if (tb == 0) {
-      if (!SIG && c > 0) flush_n();
+      if (!SIG && c > c_beg) flush_n();
       const float g2 = g2r[s];
       float Mn2 = 0.0f, dec;
       if constexpr (SIG) {
@@ -471,7 +484,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   float M_mma = Mst2;
   auto mma_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = gi >> lbpc, tb = (gi & (BPC - 1)) * TB;
+    const int c = c_beg + (gi >> lbpc), tb = (gi & (BPC - 1)) * TB;
     if (tb == 0) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   auto iter = [&](auto par, int gi) {
     constexpr int P = decltype(par)::value;
     constexpr int Q = 1 - P;
-    if (n_pend) finish_n(gi >> lbpc);
+    if (n_pend) finish_n(c_beg + (gi >> lbpc));
     mma_blk(std::integral_constant<int, P>{}, gi);
     if (gi + 1 < NBLK) stage_blk(std::integral_constant<int, Q>{}, gi + 1);
     if (gi + 3 < NBLK) load_blk(std::integral_constant<int, Q>{}, gi + 3);
@@ -525,9 +538,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     if constexpr (!SIG) {
       flush_n();
       __syncthreads();
-      finish_n(Nc);
+      finish_n(c_end);
     }
   }
+  if (segmented) return;  // the join kernels write the final state
 
   if (p.C_out) {
 #pragma unroll
@@ -545,10 +559,173 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (!SIG && p.m_out && kt == 0 && tid == 0) p.m_out[bh] = Mst2 * kLn2;
 }
 
+// ---- joining sequence segments
+//
+// A segment s >= 1 ran from a zero state, so its chunk states are local:
+// (C_L, n_L) with stabiliser M_L.  With (C_E, n_E, M_E) the true state at the
+// segment start and G the summed log-forget gates from there (all in log2
+// units), the recurrence being linear in (C, n) with a max-plus stabiliser,
+//   M = max(M_L, M_E + G),  C = C_L 2^{M_L - M} + C_E 2^{M_E + G - M}
+// (n likewise; sigmoid gate: C = C_L + 2^{G} C_E).  One thread owns 8 packed
+// values (one lane slot of a 32 x 32 block, hi and lo planes) of one head,
+// and threads with g < DK also own n[g].
+
+struct JoinView {
+  uint16_t* st;        // packed states of the head
+  const float* nst;    // n states of the head (exp gate)
+  size_t stride;       // elements per packed state (hi and lo planes)
+  size_t hi;           // element offset of this thread's hi slots
+};
+
+__device__ __forceinline__ void join_load(const JoinView& v, int entry, float (&x)[8]) {
+  const uint16_t* q = v.st + (size_t)entry * v.stride + v.hi;
+  const uint4 h = *reinterpret_cast<const uint4*>(q);
+  const uint4 l = *reinterpret_cast<const uint4*>(q + 512);
+  const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16);
+    x[2 * e + 1] = __uint_as_float(hw[e] & 0xffff0000u) + __uint_as_float(lw[e] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void join_store(const JoinView& v, int entry, const float (&x)[8]) {
+  uint16_t* q = v.st + (size_t)entry * v.stride + v.hi;
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16x2(x[2 * e], x[2 * e + 1], hi[e], lo[e]);
+  *reinterpret_cast<uint4*>(q) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4*>(q + 512) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// Summed log2 forget gates of chunks [c0, c1).
+__device__ __forceinline__ float gate_sum2(const StatesParams& p, int bh, int c0, int c1) {
+  float g = 0.0f;
+  for (int c = c0; c < c1; ++c) g += p.gb2[(size_t)bh * p.S + min((c + 1) * p.L, p.S) - 1];
+  return g;
+}
+
+// Segment boundaries, in order: the true state at the end of every segment
+// (it is the start of the next), and the final state outputs.
+template <bool SIG>
+__global__ __launch_bounds__(256) void states_carry_kernel(const StatesParams p) {
+  const int per = p.DK * p.DV / 8;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)p.BH * per) return;
+  const int bh = (int)(gid / per), g = (int)(gid % per);
+  const int Nc = p.Nc;
+  JoinView v;
+  v.stride = (size_t)p.DK * p.DV * 2;
+  v.st = reinterpret_cast<uint16_t*>(p.C_states) + (size_t)bh * (Nc + 1) * v.stride;
+  v.nst = SIG ? nullptr : p.n_states + (size_t)bh * (Nc + 1) * p.DK;
+  v.hi = (size_t)(g >> 6) * 1024 + (g & 63) * 8;
+  const bool own_n = !SIG && g < p.DK;
+  const float* ml = p.m_local + (size_t)bh * (Nc + 1);
+
+  float E[8], En = 0.0f, ME2 = 0.0f;
+  join_load(v, p.cps, E);  // end of segment 0: already true
+  if (own_n) En = v.nst[(size_t)p.cps * p.DK + g];
+  if constexpr (!SIG) ME2 = ml[p.cps];
+  for (int s = 1; s < p.nseg; ++s) {
+    const int c0 = s * p.cps, c1 = min(Nc, c0 + p.cps);
+    const float G2 = gate_sum2(p, bh, c0, c1);
+    float a = 1.0f, b, MT2 = 0.0f;
+    if constexpr (SIG) {
+      b = exp2f(G2);
+    } else {
+      const float ML2 = ml[c1];
+      MT2 = fmaxf(ML2, ME2 + G2);
+      a = exp2f(ML2 - MT2);
+      b = exp2f(ME2 + G2 - MT2);
+    }
+    float Lv[8];
+    join_load(v, c1, Lv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) E[e] = Lv[e] * a + E[e] * b;
+    join_store(v, c1, E);
+    if (own_n) {
+      En = v.nst[(size_t)c1 * p.DK + g] * a + En * b;
+      p.n_states[((size_t)bh * (Nc + 1) + c1) * p.DK + g] = En;
+    }
+    if constexpr (!SIG) {
+      ME2 = MT2;
+      if (g == 0) p.m_states[(size_t)bh * (Nc + 1) + c1] = MT2 * kLn2;
+    }
+  }
+  if (p.C_out) {
+    const int blk = g >> 6, ln = g & 63;
+    const int kk = blk / (p.DV / 32), nb = blk % (p.DV / 32), h = ln >> 5;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * kk + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
+      p.C_out[((size_t)bh * p.DK + k) * p.DV + 32 * nb + (ln & 31)] = E[e];
+    }
+  }
+  if (own_n && p.n_out) p.n_out[(size_t)bh * p.DK + g] = En;
+  if (!SIG && g == 0 && p.m_out) p.m_out[bh] = ME2 * kLn2;
+}
+
+// Interior chunk states of every segment s >= 1, all at once, from the true
+// state at the segment start (fixed by states_carry_kernel).
+template <bool SIG>
+__global__ __launch_bounds__(256) void states_fix_kernel(const StatesParams p) {
+  const int per = p.DK * p.DV / 8;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long ninterior = (long long)(p.nseg - 1) * (p.cps - 1);
+  if (gid >= (long long)p.BH * per * ninterior) return;
+  const int g = (int)(gid % per);
+  const long long rest = gid / per;
+  const int slot = (int)(rest % ninterior);
+  const int bh = (int)(rest / ninterior);
+  const int s = 1 + slot / (p.cps - 1);
+  const int c0 = s * p.cps;
+  const int entry = c0 + 1 + slot % (p.cps - 1);  // interior entries c0+1 .. c1-1
+  const int Nc = p.Nc;
+  const int c1 = min(Nc, c0 + p.cps);
+  if (entry >= c1) return;
+  JoinView v;
+  v.stride = (size_t)p.DK * p.DV * 2;
+  v.st = reinterpret_cast<uint16_t*>(p.C_states) + (size_t)bh * (Nc + 1) * v.stride;
+  v.nst = SIG ? nullptr : p.n_states + (size_t)bh * (Nc + 1) * p.DK;
+  v.hi = (size_t)(g >> 6) * 1024 + (g & 63) * 8;
+  const float G2 = gate_sum2(p, bh, c0, entry);
+  float a = 1.0f, b, MT2 = 0.0f;
+  if constexpr (SIG) {
+    b = exp2f(G2);
+  } else {
+    // the true stabiliser at the segment start (entry c0 ends the previous
+    // segment; segment 0 or states_carry_kernel wrote its true value)
+    const float MEt2 = p.m_states[(size_t)bh * (Nc + 1) + c0] * kLog2e;
+    const float ML2 = p.m_local[(size_t)bh * (Nc + 1) + entry];
+    MT2 = fmaxf(ML2, MEt2 + G2);
+    a = exp2f(ML2 - MT2);
+    b = exp2f(MEt2 + G2 - MT2);
+  }
+  float E[8], Lv[8];
+  join_load(v, c0, E);
+  join_load(v, entry, Lv);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) Lv[e] = Lv[e] * a + E[e] * b;
+  join_store(v, entry, Lv);
+  if (!SIG && g < p.DK) {
+    const float En = v.nst[(size_t)c0 * p.DK + g];
+    p.n_states[((size_t)bh * (Nc + 1) + entry) * p.DK + g] = v.nst[(size_t)entry * p.DK + g] * a + En * b;
+  }
+  if (!SIG && g == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = MT2 * kLn2;
+}
+
 template <int TK, int TV, bool SIG, bool SPLIT>
 hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)(p.BH * (p.DK / TK)));
+  dim3 grid((unsigned)(p.BH * (p.DK / TK) * p.nseg));
   hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nseg <= 1) return e;
+  const long long per = (long long)p.BH * (p.DK * p.DV / 8);
+  hipLaunchKernelGGL((states_carry_kernel<SIG>), dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.cps < 2) return e;
+  const long long nfix = per * (p.nseg - 1) * (p.cps - 1);
+  hipLaunchKernelGGL((states_fix_kernel<SIG>), dim3((unsigned)((nfix + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -582,9 +759,24 @@ hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipSt
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // Whole-row tiles (TK x DV) when they still give every CU a workgroup.
-  if (p.DV == 512 && (long long)p.BH * (p.DK / 64) >= cus) return launch_rows_any<64, 512>(p, sig, split, stream);
-  if (p.DV == 256 && p.DK % 128 == 0 && (long long)p.BH * (p.DK / 128) >= cus)
-    return launch_rows_any<128, 256>(p, sig, split, stream);
+  // Whole-row tiles; with too few heads to fill the CUs the sequence is cut
+  // into segments that run at once and are joined afterwards.
+  const int rows_tk = p.DV == 512 ? 64 : (p.DV == 256 && p.DK % 128 == 0 ? 128 : 0);
+  if (rows_tk) {
+    StatesParams q = p;
+    const long long base = (long long)p.BH * (p.DK / rows_tk);
+    q.nseg = 1;
+    q.cps = p.Nc;
+    if (base < cus && p.Nc >= 2 && p.m_local) {
+      const long long want = (cus + base - 1) / base;
+      q.cps = (int)((p.Nc + want - 1) / want);
+      q.nseg = (p.Nc + q.cps - 1) / q.cps;
+    }
+    if (base >= cus || q.nseg > 1) {
+      if (rows_tk == 64) return launch_rows_any<64, 512>(q, sig, split, stream);
+      return launch_rows_any<128, 256>(q, sig, split, stream);
+    }
+  }
   // 128-wide tiles when they still give at least two workgroups per CU.
   const bool big = (long long)p.BH * (p.DK / 128) * (p.DV / 128) >= 2LL * cus;
   if (big) {
