@@ -383,6 +383,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_ca
 // data format for untyped loads) in scalar registers, a per-lane byte offset
 // and a wave-uniform byte offset.  Reads at or past the extent return zero.
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -368,25 +368,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   KVec kr[2];
   float ur[2], g2r[2], pmr[2];
   uint4 vr[2][VPT];
+  // K, V and the input terms of this head through buffer resources: rows past
+  // the end of the sequence read as zero and get weight zero.  Only the last
+  // chunk can be short, so that bound is also the chunk's.
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, (uint32_t)(((size_t)S * DK - kt * TK) * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, (uint32_t)((size_t)S * DV * 2));
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.gu2 + gbase, (uint32_t)((size_t)S * 4));
+  const int kvoff = (krs * DK + kcs) * 2;
+  const int vvoff = ((tid / VSEG) * DV + (tid % VSEG) * 8) * 2;
   auto load_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
     const int c = c_beg + (gi >> lbpc), tb = (gi & (BPC - 1)) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
-    const int row = tb + krs;
-    if (row < Lc) {
-      kr[s] = *reinterpret_cast<const KVec*>(K + (size_t)(t0 + row) * DK + kcs);
-      ur[s] = p.gu2[gbase + t0 + row];
+    const int trow = t0 + tb;  // first time row of the block
+    if constexpr (EPT == 4) {
+      const v2i32_t k2 = __builtin_amdgcn_raw_buffer_load_b64(rk, kvoff, trow * DK * 2, 0);
+      kr[s] = make_uint2((uint32_t)k2.x, (uint32_t)k2.y);
     } else {
-      kr[s] = KVec{};
-      ur[s] = -INFINITY;  // weight 0 for rows past the chunk
+      kr[s] = buf_load16(rk, kvoff, trow * DK * 2);
     }
+    ur[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, krs * 4, trow * 4, 0));
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / VSEG, sg = idx % VSEG;
-      vr[s][i] = (tb + r < Lc) ? *reinterpret_cast<const uint4*>(V + (size_t)(t0 + tb + r) * DV + sg * 8)
-                               : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < VPT; ++i) vr[s][i] = buf_load16(rv, vvoff, (trow + i * (NT / VSEG)) * DV * 2);
     if (tb == 0) {
       g2r[s] = p.gb2[gbase + t0 + Lc - 1];
       pmr[s] = SIG ? 0.0f : p.gpm2[gbase + t0 + Lc - 1];
@@ -450,7 +453,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       dec_pend = dec;
       M_pend = Mn2;
     }
-    const float w = exp2f(g2s + ur[s] - Mn2s);
+    // weight 0 for rows past the end of the sequence (zero keys; never inf * 0)
+    const float w = c * L + tb + krs < S ? exp2f(g2s + ur[s] - Mn2s) : 0.0f;
     uint16_t* kh = s_kh + s * KBUF + krs * LDK + kcs;
     uint16_t* kl = s_kl + (SPLIT ? s * KBUF + krs * LDK + kcs : 0);
     uint32_t ww[EPT / 2];
