@@ -154,7 +154,7 @@ def path_dtype(mt, desc, precision: str) -> str:
     fam = mt.kernel_family(desc)
     if fam == mt.MLSTM_FAMILY_F64:
         return "f64-valu/f64-acc"
-    wide = fam == mt.MLSTM_FAMILY_WIDE
+    wide = fam in (mt.MLSTM_FAMILY_WIDE, mt.MLSTM_FAMILY_FUSED)
     if desc.qkv_dtype == mt.MLSTM_F32:
         return "f32-mfma/f32-acc"
     t = "bf16" if wide else "f16"

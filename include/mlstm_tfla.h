@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 2
+#define MLSTM_ABI_VERSION 3
 
 typedef enum {
   MLSTM_OK = 0,
@@ -99,6 +99,23 @@ typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
  * instructions. */
 typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } mlstm_prec_t;
 
+/* Which kernels mlstm_chunkwise_fw runs.
+ *   MLSTM_SCHED_TWO_STAGE: the two stages (inter-chunk recurrence writing the
+ *       state entering every chunk to the workspace, then the intra-chunk
+ *       stage reading them back), as mlstm_fw_states + mlstm_fw_hintra.
+ *   MLSTM_SCHED_FUSED: one chunk walker per head and 128-column slice of V
+ *       carries its part of the state from chunk to chunk in registers; no
+ *       chunk state is written (the TFLA page lists avoiding that round trip
+ *       as a planned follow-up of its two-kernel design).  Needs bf16 inputs,
+ *       MLSTM_PREC_SPLIT, DHQK = 256, DHV a multiple of 128 and
+ *       chunk_size <= 512; otherwise MLSTM_E_UNSUPPORTED.  The stage-wise
+ *       calls (mlstm_fw_states, mlstm_fw_hintra, mlstm_fw_unpack_states)
+ *       reject this schedule.
+ *   MLSTM_SCHED_AUTO: the library's choice; currently TWO_STAGE, which is
+ *       the faster of the two on the 7B-shaped workloads.  Stage-wise calls
+ *       run the two stages. */
+typedef enum { MLSTM_SCHED_AUTO = 0, MLSTM_SCHED_TWO_STAGE = 1, MLSTM_SCHED_FUSED = 2 } mlstm_schedule_t;
+
 typedef struct {
   int32_t B, NH;       /* batch, heads: >= 1                                   */
   int32_t S;           /* sequence length: >= 0, need not divide chunk_size   */
@@ -113,7 +130,8 @@ typedef struct {
   float eps;           /* >= 0, added to the normaliser after the max          */
   int32_t tile_lq;     /* rows of the intra-chunk output tile; 0 = library    */
   int32_t tile_lkv;    /* key rows per intra-chunk step; 0 = library          */
-  int32_t reserved[4]; /* must be zero                                        */
+  int32_t schedule;    /* mlstm_schedule_t; 0 = library choice                */
+  int32_t reserved[3]; /* must be zero                                        */
 } mlstm_fw_desc_t;
 
 /* ABI version of the loaded library (MLSTM_ABI_VERSION). */
@@ -130,7 +148,8 @@ int mlstm_fw_validate(const mlstm_fw_desc_t* desc);
  * -1. */
 int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
 
-/* Which family of kernels runs for a valid descriptor (host-only query):
+/* Which family of kernels mlstm_chunkwise_fw runs for a valid descriptor
+ * (host-only query):
  *   MLSTM_FAMILY_GENERIC  64-row tiles, float32 row-major chunk states, fp16
  *                         (bf16 inputs) or fp32 (float32 inputs) operands
  *   MLSTM_FAMILY_WIDE     bf16 inputs with DHQK in {128, 256} and DHV in
@@ -140,8 +159,17 @@ int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
  *                         bf16 operands, chunk states in the packed operand
  *                         layout
  *   MLSTM_FAMILY_F64      MLSTM_PREC_F64: fp64 vector-unit kernels
- * Returns the negated status code for an invalid descriptor. */
-typedef enum { MLSTM_FAMILY_GENERIC = 0, MLSTM_FAMILY_WIDE = 1, MLSTM_FAMILY_F64 = 2 } mlstm_family_t;
+ *   MLSTM_FAMILY_FUSED    the fused chunk walker (see mlstm_schedule_t):
+ *                         bf16 operands, state carried in registers
+ * The stage-wise calls run GENERIC, WIDE or F64 kernels (FUSED descriptors
+ * aside, which they reject).  Returns the negated status code for an invalid
+ * descriptor. */
+typedef enum {
+  MLSTM_FAMILY_GENERIC = 0,
+  MLSTM_FAMILY_WIDE = 1,
+  MLSTM_FAMILY_F64 = 2,
+  MLSTM_FAMILY_FUSED = 3
+} mlstm_family_t;
 int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
 
 /* Bytes of device workspace that the forward pass needs for `desc`: the
@@ -152,14 +180,18 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
  * terms, written by stage one and read by stage two (12 bytes per position
  * and head for the exp gate, 8 for the sig gate), and 4 bytes per chunk
  * boundary and head for the stabilisers of sequence segments that stage one
- * may run side by side (two more 256-aligned regions).  Returns 0 for an
+ * may run side by side (two more 256-aligned regions).  A descriptor whose
+ * schedule is MLSTM_SCHED_FUSED needs only the gate terms (the other regions
+ * are empty); under MLSTM_SCHED_AUTO the gate terms are also present
+ * wherever the fused walker supports the shape.  Returns 0 for an
  * invalid descriptor.  The storage order inside
  * the workspace belongs to the library (the chunk states are kept in the
  * operand order of the kernels that read them); mlstm_fw_unpack_states
  * returns the states as plain float32. */
 size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
 
-/* Full forward pass: stage one (states) then stage two (H) on `workspace`.
+/* Full forward pass: stage one (states) then stage two (H) on `workspace`,
+ * or the fused chunk walker (see mlstm_schedule_t).
  *   C0, n0, m0   may be NULL: zero initial state (m0 = 0).  For the sig gate
  *                n0 and m0 must be NULL.
  *   C_out, n_out, m_out  may be NULL: that final state is not written.  For
@@ -169,7 +201,9 @@ size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
  *   workspace    device buffer of at least mlstm_fw_workspace_bytes(desc)
  *                bytes, 256-byte aligned; it may be NULL only when that size
  *                is 0.  On return it holds the chunk states (see
- *                mlstm_fw_unpack_states).
+ *                mlstm_fw_unpack_states) when the two-stage kernels ran;
+ *                after the fused walker (MLSTM_FAMILY_FUSED) it holds only
+ *                the gate terms, and the chunk states were never formed.
  * With S == 0 the call only copies the initial state to the outputs. */
 int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        const void* Q, const void* K, const void* V,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 2
+    assert mt.abi_version() == 3
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -46,8 +46,9 @@ def test_abi_version_and_status_strings():
 
 
 def test_desc_layout_matches_header():
-    # 14 int/float fields plus reserved[4], all 4 bytes
+    # 15 int/float fields plus reserved[3], all 4 bytes
     assert ctypes.sizeof(mt.FwDesc) == 18 * 4
+    assert mt.FwDesc.schedule.offset == 14 * 4
 
 
 def _desc(**kw):
@@ -152,6 +153,38 @@ def test_kernel_family_query():
     assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256, qkv_dtype=mt.MLSTM_F32)) == mt.MLSTM_FAMILY_GENERIC
     assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256, precision="f64")) == mt.MLSTM_FAMILY_F64
     assert mt.kernel_family(_desc(DHQK=100)) == -2
+
+
+def test_schedule_field():
+    # the automatic schedule keeps the two-stage kernels; the fused walker
+    # runs when asked for on bf16, DHQK 256, DHV a multiple of 128, chunk <= 512
+    big = dict(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
+    assert mt.kernel_family(_desc(**big)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**big, schedule="two_stage")) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**big, schedule="fused")) == mt.MLSTM_FAMILY_FUSED
+    assert mt.kernel_family(_desc(**big, gate="sig", schedule="fused")) == mt.MLSTM_FAMILY_FUSED
+    assert mt.kernel_family(_desc(**dict(big, B=1, NH=1, DHV=128), schedule="fused")) == mt.MLSTM_FAMILY_FUSED
+    assert mt.kernel_family(_desc(**big, precision="f64")) == mt.MLSTM_FAMILY_F64
+    # a forced fused schedule on a shape it does not cover, and unknown values
+    assert mt.validate(_desc(**dict(big, DHQK=128), schedule="fused")) == 5
+    assert mt.validate(_desc(**dict(big, chunk_size=1024), schedule="fused")) == 5
+    assert mt.validate(_desc(**big, qkv_dtype=mt.MLSTM_F32, schedule="fused")) == 5
+    assert mt.validate(_desc(**big, schedule=3)) == 9
+    assert mt.validate(_desc(**big, schedule=-1)) == 9
+    # workspace: the fused schedule needs the gate terms only (12 or 8 bytes per
+    # position and head); auto keeps room for the two-stage kernels as well
+    fused = _desc(**big, schedule="fused")
+    assert mt.workspace_bytes(fused) == 64 * 8192 * 12
+    assert mt.workspace_bytes(_desc(**big, gate="sig", schedule="fused")) == 64 * 8192 * 8
+    auto = mt.workspace_bytes(_desc(**big))
+    assert auto == mt.workspace_bytes(_desc(**big, schedule="two_stage"))
+    assert auto > 64 * 33 * 256 * 512 * 4
+    # the stage-wise calls refuse a fused descriptor before touching pointers
+    lib = mt.lib()
+    wsb = mt.workspace_bytes(fused)
+    assert lib.mlstm_fw_states(ctypes.byref(fused), *([4096] * 7), 1 << 20, wsb, None, None, None, None) == 5
+    assert lib.mlstm_fw_hintra(ctypes.byref(fused), *([4096] * 5), 1 << 20, wsb, 4096, None, None, None) == 5
+    assert lib.mlstm_fw_unpack_states(ctypes.byref(fused), 1 << 20, wsb, 4096, None, None, None) == 5
 
 
 def test_flops_formula():

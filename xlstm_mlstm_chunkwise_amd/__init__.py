@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(PKG_DIR, "libmlstm_tfla.so")
 MLSTM_F32, MLSTM_BF16 = 0, 1
 MLSTM_GATE_EXP, MLSTM_GATE_SIG = 0, 1
 MLSTM_PREC_SPLIT, MLSTM_PREC_F16, MLSTM_PREC_F64 = 0, 1, 2
-MLSTM_FAMILY_GENERIC, MLSTM_FAMILY_WIDE, MLSTM_FAMILY_F64 = 0, 1, 2
+MLSTM_FAMILY_GENERIC, MLSTM_FAMILY_WIDE, MLSTM_FAMILY_F64, MLSTM_FAMILY_FUSED = 0, 1, 2, 3
+MLSTM_SCHED_AUTO, MLSTM_SCHED_TWO_STAGE, MLSTM_SCHED_FUSED = 0, 1, 2
 _PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16, "f64": MLSTM_PREC_F64}
 _GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
+_SCHED = {"auto": MLSTM_SCHED_AUTO, "two_stage": MLSTM_SCHED_TWO_STAGE, "fused": MLSTM_SCHED_FUSED}
 
 STATUS_NAMES = {
     0: "MLSTM_OK", 1: "MLSTM_E_NULLPTR", 2: "MLSTM_E_SHAPE", 3: "MLSTM_E_CHUNK",
@@ -43,8 +45,8 @@ class FwDesc(ctypes.Structure):
         ("DHQK", ctypes.c_int32), ("DHV", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32), ("h_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
         ("precision", ctypes.c_int32), ("qk_scale", ctypes.c_float), ("eps", ctypes.c_float),
-        ("tile_lq", ctypes.c_int32), ("tile_lkv", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("tile_lq", ctypes.c_int32), ("tile_lkv", ctypes.c_int32), ("schedule", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -92,7 +94,8 @@ def status_str(status: int) -> str:
 
 
 def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=MLSTM_F32,
-              gate="exp", precision="split", qk_scale=0.0, eps=0.0, tile_lq=0, tile_lkv=0) -> FwDesc:
+              gate="exp", precision="split", qk_scale=0.0, eps=0.0, tile_lq=0, tile_lkv=0,
+              schedule="auto") -> FwDesc:
     d = FwDesc()
     d.B, d.NH, d.S, d.DHQK, d.DHV, d.chunk_size = B, NH, S, DHQK, DHV, chunk_size
     d.qkv_dtype, d.h_dtype = qkv_dtype, h_dtype
@@ -100,6 +103,7 @@ def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=
     d.precision = _PREC[precision] if isinstance(precision, str) else precision
     d.qk_scale, d.eps = qk_scale, eps
     d.tile_lq, d.tile_lkv = tile_lq, tile_lkv
+    d.schedule = _SCHED[schedule] if isinstance(schedule, str) else schedule
     return d
 
 
@@ -159,7 +163,7 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv):
+def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule="auto"):
     torch = _torch()
     B, NH, S, DK = q.shape
     DV = v.shape[-1]
@@ -167,7 +171,7 @@ def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq
     return make_desc(B, NH, S, DK, DV, chunk_size, qkv_dtype=_dtype_code(q), h_dtype=hcode,
                      gate=gate, precision=precision,
                      qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps),
-                     tile_lq=tile_lq, tile_lkv=tile_lkv)
+                     tile_lq=tile_lq, tile_lkv=tile_lkv, schedule=schedule)
 
 
 def _check_inputs(q, k, v, i_pre, f_pre):
@@ -187,7 +191,7 @@ def _check_inputs(q, k, v, i_pre, f_pre):
 def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
                        gate: str = "exp", h_dtype=None, precision: str = "split",
                        qk_scale: Optional[float] = None, eps: float = 0.0,
-                       tile_lq: int = 0, tile_lkv: int = 0, workspace=None,
+                       tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto", workspace=None,
                        return_final_state: bool = True, out=None):
     """Chunkwise mLSTM forward pass on the GPU.
 
@@ -196,6 +200,7 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     m0 (B, NH) float32 or None (zero state).  Returns (H, C, n, m); n and m
     are None for gate="sig", and the final state is None when
     return_final_state is False.  H is float32 unless h_dtype says otherwise.
+    schedule: "auto", "two_stage" or "fused" (see mlstm_schedule_t).
     """
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
@@ -203,7 +208,7 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     _check(C0, "C0", (B, NH, DK, DV), torch.float32)
     _check(n0, "n0", (B, NH, DK), torch.float32)
     _check(m0, "m0", (B, NH), torch.float32)
-    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv)
+    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_chunkwise_fw")

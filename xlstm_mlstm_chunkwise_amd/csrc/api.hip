@@ -19,14 +19,21 @@ constexpr int kMinChunk = 64;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+bool fused_supported(const mlstm_fw_desc_t* d) {
+  return d->precision == MLSTM_PREC_SPLIT &&
+         mlstm::walk_supported(d->DHQK, d->DHV, d->chunk_size, d->qkv_dtype == MLSTM_BF16, true);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int validate_desc(const mlstm_fw_desc_t* d) {
   if (!d) return MLSTM_E_NULLPTR;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (d->reserved[i] != 0) return MLSTM_E_ARG;
+  if (d->schedule != MLSTM_SCHED_AUTO && d->schedule != MLSTM_SCHED_TWO_STAGE && d->schedule != MLSTM_SCHED_FUSED)
+    return MLSTM_E_ARG;
   if (d->qkv_dtype != MLSTM_F32 && d->qkv_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
   if (d->h_dtype != MLSTM_F32 && d->h_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
   if (d->gate != MLSTM_GATE_EXP && d->gate != MLSTM_GATE_SIG) return MLSTM_E_ARG;
@@ -50,8 +57,14 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   if (BH > (1 << 30)) return MLSTM_E_SHAPE;
   if (BH * Nc * (d->chunk_size / 64) > 0x7fffffffLL) return MLSTM_E_SHAPE;  // grid.x bound
   if ((int64_t)d->S * (int64_t)d->DHV > (1LL << 40)) return MLSTM_E_SHAPE;
+  if (d->schedule == MLSTM_SCHED_FUSED && !fused_supported(d)) return MLSTM_E_UNSUPPORTED;
   return MLSTM_OK;
 }
+
+// Whether mlstm_chunkwise_fw runs the fused walker for a valid descriptor.
+// The automatic schedule keeps the two-stage kernels: on the 7B-shaped
+// workloads they are still the faster pair.
+bool use_fused(const mlstm_fw_desc_t* d) { return d->schedule == MLSTM_SCHED_FUSED; }
 
 struct WsLayout {
   size_t c_off, n_off, m_off, g_off, ml_off, total;
@@ -59,23 +72,26 @@ struct WsLayout {
 
 bool packed_layout(const mlstm_fw_desc_t* d);
 
+// Per-position gate terms: read by both wide-tile stages and by the walker.
+bool needs_gates(const mlstm_fw_desc_t* d) { return packed_layout(d) || fused_supported(d); }
+
 WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   const size_t BH = (size_t)d->B * d->NH;
   const size_t Nc1 = (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
   const size_t el = d->precision == MLSTM_PREC_F64 ? sizeof(double) : sizeof(float);
+  const bool states = d->schedule != MLSTM_SCHED_FUSED;  // chunk states can be formed
   WsLayout w;
   w.c_off = 0;
-  size_t off = round_up(BH * Nc1 * d->DHQK * d->DHV * el, 256);
+  size_t off = states ? round_up(BH * Nc1 * d->DHQK * d->DHV * el, 256) : 0;
   w.n_off = off;
-  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * el, 256);
+  if (states && d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * el, 256);
   w.m_off = off;
-  if (d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * el, 256);
-  // per-position gate terms shared by the two wide-tile stages
+  if (states && d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * el, 256);
   w.g_off = off;
-  if (packed_layout(d)) off += round_up(BH * (size_t)d->S * sizeof(float) * (d->gate == MLSTM_GATE_EXP ? 3 : 2), 256);
+  if (needs_gates(d)) off += round_up(BH * (size_t)d->S * sizeof(float) * (d->gate == MLSTM_GATE_EXP ? 3 : 2), 256);
   // stabilisers of segment-local runs of the states kernel
   w.ml_off = off;
-  if (packed_layout(d)) off += round_up(BH * Nc1 * sizeof(float), 256);
+  if (states && packed_layout(d)) off += round_up(BH * Nc1 * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -122,8 +138,8 @@ WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
   r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
   r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
   r.gb2 = r.gu2 = r.gpm2 = r.m_local = nullptr;
-  if (packed_layout(d)) {
-    r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
+  if (packed_layout(d) && d->schedule != MLSTM_SCHED_FUSED) r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
+  if (needs_gates(d)) {
     const size_t n = (size_t)d->B * d->NH * d->S;
     r.gb2 = reinterpret_cast<float*>(ws + w.g_off);
     r.gu2 = r.gb2 + n;
@@ -137,6 +153,53 @@ int check_workspace(const mlstm_fw_desc_t* d, const void* workspace, size_t work
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MLSTM_E_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
   return MLSTM_OK;
+}
+
+hipError_t run_gates(const mlstm_fw_desc_t* d, const float* i_pre, const float* f_pre, const WsPtrs& ws,
+                     hipStream_t stream) {
+  GatesParams g;
+  g.i_pre = i_pre;
+  g.f_pre = f_pre;
+  g.gb2 = ws.gb2;
+  g.gu2 = ws.gu2;
+  g.gpm2 = ws.gpm2;
+  g.BH = d->B * d->NH;
+  g.S = d->S;
+  g.L = d->chunk_size;
+  g.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  return mlstm::launch_gates(g, d->gate == MLSTM_GATE_SIG, stream);
+}
+
+int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
+              const float* f_pre, const float* C0, const float* n0, const float* m0, const WsPtrs& ws, void* H,
+              float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+  hipError_t e = run_gates(d, i_pre, f_pre, ws, stream);
+  if (e != hipSuccess) return MLSTM_E_HIP;
+  mlstm::WalkParams p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.gb2 = ws.gb2;
+  p.gu2 = ws.gu2;
+  p.gpm2 = ws.gpm2;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.m0 = m0;
+  p.H = H;
+  p.C_out = C_out;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  p.scale = resolve_scale(d);
+  p.eps = d->eps;
+  p.BH = d->B * d->NH;
+  p.S = d->S;
+  p.DK = d->DHQK;
+  p.DV = d->DHV;
+  p.L = d->chunk_size;
+  p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  p.h_bf16 = d->h_dtype == MLSTM_BF16;
+  e = mlstm::launch_walk(p, d->gate == MLSTM_GATE_SIG, stream);
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
 int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const float* i_pre, const float* f_pre,
@@ -174,17 +237,7 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   hipError_t e;
   if (d->precision == MLSTM_PREC_F64) e = mlstm::launch_states_f64(p, bf16, sig, stream);
   else if (packed_layout(d)) {
-    GatesParams g;
-    g.i_pre = i_pre;
-    g.f_pre = f_pre;
-    g.gb2 = ws.gb2;
-    g.gu2 = ws.gu2;
-    g.gpm2 = ws.gpm2;
-    g.BH = p.BH;
-    g.S = p.S;
-    g.L = p.L;
-    g.Nc = p.Nc;
-    e = mlstm::launch_gates(g, sig, stream);
+    e = run_gates(d, i_pre, f_pre, ws, stream);
     if (e == hipSuccess) e = mlstm::launch_states_wide(p, sig, split, stream);
   }
   else e = mlstm::launch_states(p, bf16, sig, split, stream);
@@ -264,6 +317,7 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc) {
   const int st = validate_desc(desc);
   if (st != MLSTM_OK) return -st;
   if (desc->precision == MLSTM_PREC_F64) return MLSTM_FAMILY_F64;
+  if (use_fused(desc)) return MLSTM_FAMILY_FUSED;
   return packed_layout(desc) ? MLSTM_FAMILY_WIDE : MLSTM_FAMILY_GENERIC;
 }
 
@@ -277,6 +331,7 @@ int mlstm_fw_states(const mlstm_fw_desc_t* desc, const void* K, const void* V, c
                     size_t workspace_bytes, float* C_out, float* n_out, float* m_out, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
+  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
   if (desc->S > 0 && (!K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
   if ((K && !aligned(K, 16)) || (V && !aligned(V, 16))) return MLSTM_E_ALIGN;
@@ -291,6 +346,7 @@ int mlstm_fw_hintra(const mlstm_fw_desc_t* desc, const void* Q, const void* K, c
                     float* den_rows, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
+  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, m_rows, den_rows, nullptr, nullptr)) != MLSTM_OK) return st;
   if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
@@ -305,6 +361,7 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, s
                            float* C_states, float* n_states, float* m_states, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
+  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
   if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
   if ((st = check_f32_ptrs({C_states, n_states, m_states})) != MLSTM_OK) return st;
   if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
@@ -347,6 +404,7 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
   const WsPtrs ws = ws_ptrs(desc, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_fused(desc)) return run_fused(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
   st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
   if (st != MLSTM_OK) return st;
   return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);

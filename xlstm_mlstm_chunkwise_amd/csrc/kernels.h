@@ -62,8 +62,34 @@ struct HintraParams {
   int tile_lkv;  // keys per step: 64 or 128
 };
 
+// Fused chunk walker: one workgroup per (head, 128-column slice of V) runs
+// the chunks of its head in order with its part of the state in registers.
+struct WalkParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* gb2;  // gate terms (see GatesParams)
+  const float* gu2;
+  const float* gpm2;
+  const float* C0;  // may be null (zero state)
+  const float* n0;  // may be null
+  const float* m0;  // may be null
+  void* H;
+  float* C_out;  // may be null
+  float* n_out;
+  float* m_out;
+  float scale;
+  float eps;
+  int BH, S, DK, DV, L, Nc;
+  int h_bf16;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gates(const GatesParams& p, bool sig, hipStream_t stream);
+bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split);
+// Workgroups the walker launches for a shape (heads x column slices).
+long long walk_workgroups(int BH, int DV);
+hipError_t launch_walk(const WalkParams& p, bool sig, hipStream_t stream);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 

@@ -1,0 +1,571 @@
+// Fused chunk walker (gfx950): the whole chunkwise forward pass in one launch,
+// with the chunk states kept in registers instead of being written out and
+// read back between two kernels.
+//
+// The chunkwise form ("Tiled Flash Linear Attention: More Efficient Linear RNN
+// and xLSTM Kernels", abstract: an inter-chunk recurrence plus a parallel
+// intra-chunk part with a second level of sequence tiling; the mLSTM cell of
+// "xLSTM: the NX-AI repository behind the extended LSTM architecture",
+// section "Exponential gating, matrix memory, and why the kernels decide
+// everything") computes, for chunk c of a head,
+//   H_c = (inter term Q_c C_{c-1}, rows scaled) + (causal, gate-decayed
+//         Q_c K_c^T) V_c, then the normaliser division (exp gate),
+//   C_c = decay C_{c-1} + K_c^T (w . V_c)       w = per-step gate weights.
+// The TFLA page lists avoiding the HBM round trip of those per-chunk states
+// as a planned follow-up; this kernel is that fused form.
+//
+// Organisation.  One workgroup (4 waves, one per SIMD) owns one head and a
+// 128-column slice of V / H / C and walks the chunks of the head in order.
+// Wave w owns the 32 columns 32w.. of the slice and holds C[:, those columns]
+// (DK x 32 float32) in matrix-core accumulators for the whole run.  Every
+// chunk is processed in 64-row query tiles i; tile i takes the key tiles
+// j <= i:
+//   inter term   H_i  = Q_i . Cbar           (Cbar = C as bf16 hi + lo)
+//   scores       S^T  = K_j . Q_i^T          (each wave one 32 x 32 block)
+//   P = s S decay, shared through LDS as bf16 hi + lo planes
+//   intra term   H_i += P . V_j
+// and the last query tile of the chunk also does the state update
+//   C = decay C + K_j^T (w . V_j)            (w . V_j as bf16 hi + lo)
+// after its inter term has used the old state.  The four column slices of a
+// head compute the same score tiles (that is the price of keeping C
+// on-chip); they are placed on one XCD so their Q and K reads share an L2.
+//
+// State precision.  The state stays in float32 accumulators for the whole
+// walk; at the start of every chunk it is split once into the bf16 hi + lo
+// pair that the Q . Cbar products of all its query tiles read.
+//
+// Contraction order.  The state accumulators hold row m of each 32-row block
+// at k index 32 kb + perm(m), where perm swaps the 4-row groups 1 and 2 of
+// every 16 rows; the K^T operand of the update is read with that column
+// permutation.  With it, the accumulator values a lane holds for a 16-deep k
+// step of Q . Cbar are the k indices 8 (lane / 32) + e in natural order, so Q
+// enters with plain 16-byte row reads.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mlstm {
+namespace {
+
+constexpr int kWalkMaxL = 512;
+constexpr int kWalkSlice = 128;
+
+// K rows are stored unpadded with their 16-byte column groups XOR-swizzled by
+// row, so that both the 16-byte row reads of the scores (16 consecutive rows,
+// one group) and the transposing reads of the update (4 consecutive rows, 4
+// consecutive groups) fall on distinct banks.
+__device__ __forceinline__ int kswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// element offset of K tile element (row r, column c) for a row of DK elements
+template <int DK>
+__device__ __forceinline__ int koff(int r, int c) {
+  return r * DK + (((c >> 3) ^ kswz(r)) << 3) + (c & 7);
+}
+
+template <int DK, bool SIG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void walk_kernel(const WalkParams p) {
+  constexpr int NT = 256, TQ = 64, TKV = 64, TVS = kWalkSlice;
+  constexpr int LDQ = DK + 8;    // 16-byte row reads: 4 banks mod 64
+  constexpr int LDV = TVS + 32;  // transposing reads: 16 banks mod 64
+  constexpr int LDP = TKV + 8;
+  constexpr int NKB = DK / 32;   // 32-row blocks of the state
+  constexpr int NKS = DK / 16;   // 16-deep k steps over DK
+  constexpr int KG = DK / 8;     // 16-byte groups per Q / K row
+  constexpr int QPT = TQ * KG / NT;
+  constexpr int VG = TVS / 8;
+  constexpr int VPT = TKV * VG / NT;
+  constexpr int GPT = kWalkMaxL / NT;
+  static_assert(QPT * NT == TQ * KG && VPT * NT == TKV * VG, "staging split");
+  static_assert(DK <= NT, "one thread per normaliser entry");
+
+  __shared__ __align__(16) uint16_t s_q[TQ * LDQ];
+  __shared__ __align__(16) uint16_t s_k[TKV * DK];
+  __shared__ __align__(16) uint16_t s_v[TKV * LDV];
+  __shared__ __align__(16) uint16_t s_vwh[TKV * LDV];
+  __shared__ __align__(16) uint16_t s_vwl[TKV * LDV];
+  __shared__ __align__(16) uint16_t s_p[2 * TQ * LDP];  // P hi plane, then lo plane
+  __shared__ __align__(16) float s_gu[kWalkMaxL];
+  __shared__ float s_gb[kWalkMaxL];
+  __shared__ float s_gpm[SIG ? 1 : kWalkMaxL];
+  __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ];
+  __shared__ float s_den[4][TQ];  // inter parts (two DK halves), intra parts (two key halves)
+  __shared__ __align__(16) float s_inv[TQ];
+  __shared__ __align__(16) float s_n[DK];
+  uint16_t* const s_ph = s_p;
+  uint16_t* const s_pl = s_p + TQ * LDP;
+  float* const s_np = reinterpret_cast<float*>(s_p);  // n partial sums at the end of a chunk
+
+  // Per-lane roles.  They are re-derived from a laundered thread index at the
+  // top of every loop level, so the compiler rebuilds the LDS offsets that
+  // depend on them instead of keeping dozens of them live across the walk.
+  int tid, lane, wave, h, l32, kh, qh;  // kh, qh: key half, query half of the score block
+  auto set_roles = [&]() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    asm volatile("" : "+s"(w));
+    tid = t;
+    lane = t & 63;
+    wave = w;
+    h = lane >> 5;
+    l32 = lane & 31;
+    kh = w >> 1;
+    qh = w & 1;
+  };
+  set_roles();
+  const int S = p.S, L = p.L, Nc = p.Nc, DV = p.DV;
+  const int NS = DV / TVS;
+  // workgroup -> (head, slice); with BH a multiple of 8 the slices of one
+  // head share blockIdx % 8, i.e. one XCD
+  int slice, bh;
+  {
+    const int bid = blockIdx.x;
+    if ((p.BH & 7) == 0) {
+      const int x = bid & 7, jj = bid >> 3;
+      slice = jj % NS;
+      bh = (jj / NS) * 8 + x;
+    } else {
+      slice = bid % NS;
+      bh = bid / NS;
+    }
+  }
+  const int v0 = slice * TVS;
+  const float scale = p.scale;
+  const float log2_scale = log2f(p.scale);
+  const uint16_t* Qh = static_cast<const uint16_t*>(p.Q) + (size_t)bh * S * DK;
+  const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK;
+  const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV + v0;
+  const size_t gbase = (size_t)bh * S;
+  auto vcol = [&]() { return v0 + 32 * wave + l32; };  // the state / H column of this lane
+
+  // ---- state.  Accumulator register r of block kb holds C[dk][vcol] with
+  // dk = 32 kb + perm(row of r).
+  auto state_row = [&](int kb, int r) {
+    const int j = r >> 2;
+    return 32 * kb + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + (r & 3);
+  };
+  float16_t cacc[NKB];
+  {
+    // a zero-extent resource reads zeros when there is no initial state
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C0 ? p.C0 + (size_t)bh * DK * DV : p.gb2, p.C0 ? (uint32_t)(DK * DV * 4) : 0u);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        cacc[kb][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rc, (state_row(kb, r) * DV + vcol()) * 4, 0, 0));
+  }
+  if (!SIG && tid < DK) s_n[tid] = p.n0 ? p.n0[(size_t)bh * DK + tid] : 0.0f;
+  float M = (!SIG && p.m0) ? p.m0[bh] * kLog2e : 0.0f;  // stabiliser, log2 units
+
+  // ---- global loads, one step ahead.  Q tiles in (chunk, query tile)
+  // order; K / V tiles in (chunk, query tile, key tile <= query tile) order.
+  auto nsub_of = [&](int c) { return (min(L, S - c * L) + TQ - 1) / TQ; };
+  uint4 qpre[QPT], kpre[QPT], vpre[VPT];
+  float gpre_u[GPT], gpre_b[GPT], gpre_pm[GPT];
+  int qc = 0, qi = 0;          // next Q tile to load
+  int kc = 0, ki = 0, kj = 0;  // next K / V tile to load
+  auto load_q = [&]() {
+    if (qc >= Nc) return;
+    const int t0 = qc * L, Lc = min(L, S - t0), r0 = qi * TQ;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (size_t)(t0 + r0) * DK, (uint32_t)((Lc - r0) * DK * 2));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16(rq, tid * 16, i * NT * 16);
+    if (++qi >= nsub_of(qc)) {
+      qi = 0;
+      ++qc;
+    }
+  };
+  auto load_kv = [&]() {
+    if (kc >= Nc) return;
+    const int t0 = kc * L, Lc = min(L, S - t0), k0 = kj * TKV;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)(t0 + k0) * DK, (uint32_t)((Lc - k0) * DK * 2));
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(Vh + (size_t)(t0 + k0) * DV, (uint32_t)(((Lc - k0 - 1) * DV + TVS) * 2));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) kpre[i] = buf_load16(rk, tid * 16, i * NT * 16);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      vpre[i] = buf_load16(rv, ((tid / VG) * DV + (tid % VG) * 8) * 2, i * (NT / VG) * DV * 2);
+    if (++kj > ki) {
+      kj = 0;
+      if (++ki >= nsub_of(kc)) {
+        ki = 0;
+        ++kc;
+      }
+    }
+  };
+  auto load_gates = [&](int c) {
+    if (c >= Nc) return;
+    const int t0 = c * L, Lc = min(L, S - t0);
+#pragma unroll
+    for (int e = 0; e < GPT; ++e) {
+      const int pos = tid + e * NT;
+      const bool ok = pos < Lc;
+      gpre_u[e] = ok ? p.gu2[gbase + t0 + pos] : 0.0f;
+      gpre_b[e] = ok ? p.gb2[gbase + t0 + pos] : 0.0f;
+      gpre_pm[e] = (!SIG && ok) ? p.gpm2[gbase + t0 + pos] : 0.0f;
+    }
+  };
+  load_gates(0);
+  load_q();
+  load_kv();
+
+  float np[8];  // n partial sums of this thread's key columns (exp gate)
+
+  for (int c = 0; c < Nc; ++c) {
+    set_roles();
+    const int t0 = c * L, Lc = min(L, S - t0);
+    const int nsub = (Lc + TQ - 1) / TQ;
+    // u past the end of a short last chunk is -inf: those keys (zero rows)
+    // get weight exactly zero in P
+#pragma unroll
+    for (int e = 0; e < GPT; ++e) {
+      const int pos = tid + e * NT;
+      if (pos < L) {
+        s_gu[pos] = pos < Lc ? gpre_u[e] : -INFINITY;
+        s_gb[pos] = gpre_b[e];
+        if constexpr (!SIG) s_gpm[pos] = gpre_pm[e];
+      }
+    }
+    load_gates(c + 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) np[e] = 0.0f;
+    __syncthreads();
+    // chunk scalars: stabiliser after the chunk, decay of the old state
+    const float g2 = s_gb[Lc - 1];
+    float Mn = 0.0f, dec;
+    if constexpr (SIG) {
+      dec = exp2f(g2);
+    } else {
+      Mn = g2 + fmaxf(M, s_gpm[Lc - 1]);
+      dec = exp2f(g2 + M - Mn);
+    }
+    // the state entering the chunk as bf16 hi + lo words (word q of block kb
+    // packs registers 2q and 2q + 1), read by every query tile's inter term
+    uint32_t chi[NKB][8], clo[NKB][8];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) split_bf16x2(cacc[kb][2 * q], cacc[kb][2 * q + 1], chi[kb][q], clo[kb][q]);
+    // weight of step sigma in the state update
+    auto upd_w = [&](int sigma) -> float {
+      return SIG ? exp2f(g2 + s_gu[sigma]) : exp2f(g2 + s_gu[sigma] - Mn);  // 0 past the chunk end
+    };
+
+    // query tile i; LAST: the chunk's last tile, which also updates the state
+    auto sub_tile = [&](auto last_c, int i) {
+      constexpr bool last = decltype(last_c)::value;
+      set_roles();
+      const int row0 = i * TQ;
+      // per-row terms: exponent offset r2 of the decay, weight of the inter
+      // term, stabiliser m (log2 units)
+      if (tid < TQ) {
+        const int tau = row0 + tid;
+        float r2 = -INFINITY, wr = 0.0f, m2 = 0.0f;
+        if (tau < Lc) {
+          const float b2 = s_gb[tau];
+          if constexpr (SIG) {
+            r2 = b2 + log2_scale;
+            wr = exp2f(b2);
+          } else {
+            const float mx = fmaxf(M, s_gpm[tau]);
+            r2 = log2_scale - mx;
+            wr = exp2f(M - mx);
+            m2 = b2 + mx;
+          }
+        }
+        s_row_r2[tid] = r2;
+        s_row_w[tid] = wr * scale;
+        s_row_m2[tid] = m2;
+      }
+#pragma unroll
+      for (int e = 0; e < QPT; ++e) {
+        const int idx = tid + e * NT;
+        *reinterpret_cast<uint4*>(s_q + (idx / KG) * LDQ + (idx % KG) * 8) = qpre[e];
+      }
+      load_q();
+      __syncthreads();
+
+      // this wave's query half as B fragments of the score blocks (the Q tile
+      // stays in LDS until the next query tile)
+      auto qs = [&](int s) { return *reinterpret_cast<const uint4*>(s_q + (32 * qh + l32) * LDQ + 16 * s + 8 * h); };
+
+      // ---- inter term with the state entering the chunk
+      float16_t hacc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[rb][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        uint4 a[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) a[rb] = *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + 16 * s + 8 * h);
+        const int q0 = 4 * (s & 1);
+        const bf16x8_t bhi = as_bf16x8(make_uint4(chi[s >> 1][q0], chi[s >> 1][q0 + 1], chi[s >> 1][q0 + 2], chi[s >> 1][q0 + 3]));
+        const bf16x8_t blo = as_bf16x8(make_uint4(clo[s >> 1][q0], clo[s >> 1][q0 + 1], clo[s >> 1][q0 + 2], clo[s >> 1][q0 + 3]));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          hacc[rb] = mma32b(as_bf16x8(a[rb]), bhi, hacc[rb]);
+          hacc[rb] = mma32b(as_bf16x8(a[rb]), blo, hacc[rb]);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[rb][r] *= s_row_w[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
+      // normaliser contribution of the state: s e^{M - m} q . n; each wave
+      // takes its query half over one half of DK
+      if constexpr (!SIG) {
+        float d = 0.0f;
+#pragma unroll
+        for (int s0 = 0; s0 < NKS / 2; ++s0) {
+          const int s = kh * (NKS / 2) + s0;
+          const uint4 qv = qs(s);
+          const uint32_t ww[4] = {qv.x, qv.y, qv.z, qv.w};
+          const float4 n0 = *reinterpret_cast<const float4*>(s_n + 16 * s + 8 * h);
+          const float4 n1 = *reinterpret_cast<const float4*>(s_n + 16 * s + 8 * h + 4);
+          d += __uint_as_float(ww[0] << 16) * n0.x + __uint_as_float(ww[0] & 0xffff0000u) * n0.y;
+          d += __uint_as_float(ww[1] << 16) * n0.z + __uint_as_float(ww[1] & 0xffff0000u) * n0.w;
+          d += __uint_as_float(ww[2] << 16) * n1.x + __uint_as_float(ww[2] & 0xffff0000u) * n1.y;
+          d += __uint_as_float(ww[3] << 16) * n1.z + __uint_as_float(ww[3] & 0xffff0000u) * n1.w;
+        }
+        d += __shfl_xor(d, 32, 64);
+        if (h == 0) s_den[kh][32 * qh + l32] = d * s_row_w[32 * qh + l32];
+      }
+      // the last tile decays the old state before accumulating the update
+      if constexpr (last) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cacc[kb][r] *= dec;
+      }
+      float dpart = 0.0f;
+      const int tl = 32 * qh + l32;  // query of this lane in the score block, within the tile
+      const float r2 = s_row_r2[tl];
+
+      // ---- key tiles
+      for (int j = 0; j <= i; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        set_roles();
+        const int key0 = j * TKV;
+        // stage K (swizzled), V and, for the update, w . V as hi / lo planes
+#pragma unroll
+        for (int e = 0; e < QPT; ++e) {
+          const int idx = tid + e * NT;
+          const int rr = idx / KG, cc = (idx % KG) * 8;
+          *reinterpret_cast<uint4*>(s_k + koff<DK>(rr, cc)) = kpre[e];
+          if (!SIG && last) {
+            const float w = upd_w(key0 + rr);
+            const uint32_t ww[4] = {kpre[e].x, kpre[e].y, kpre[e].z, kpre[e].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              np[2 * q] += w * __uint_as_float(ww[q] << 16);
+              np[2 * q + 1] += w * __uint_as_float(ww[q] & 0xffff0000u);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+          const int idx = tid + e * NT;
+          const int rr = idx / VG, cc = (idx % VG) * 8;
+          *reinterpret_cast<uint4*>(s_v + rr * LDV + cc) = vpre[e];
+          if constexpr (last) {
+            const float w = upd_w(key0 + rr);
+            const uint32_t ww[4] = {vpre[e].x, vpre[e].y, vpre[e].z, vpre[e].w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              split_bf16x2(w * __uint_as_float(ww[q] << 16), w * __uint_as_float(ww[q] & 0xffff0000u), hw[q], lw[q]);
+            *reinterpret_cast<uint4*>(s_vwh + rr * LDV + cc) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4*>(s_vwl + rr * LDV + cc) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          }
+        }
+        load_kv();
+        __syncthreads();
+
+        // scores: this wave's 32 keys x 32 queries, then P = s S 2^{r2 + u}
+        // (masked to keys <= query < chunk end) into the P planes
+        if (!(j == i && kh > qh)) {
+          float16_t sacc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            const uint4 a = *reinterpret_cast<const uint4*>(s_k + koff<DK>(32 * kh + l32, 16 * s + 8 * h));
+            sacc = mma32b(as_bf16x8(a), as_bf16x8(qs(s)), sacc);
+          }
+          // rows past the chunk end have r2 = -inf and keys past it u = -inf,
+          // so only the causal mask of the diagonal tile needs a select
+          auto make_p = [&](auto diag_c) {
+            constexpr bool diag = decltype(diag_c)::value;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int kl = 32 * kh + 8 * jj + 4 * h;  // first of this lane's 4 keys, within the tile
+              const float4 u4 = *reinterpret_cast<const float4*>(s_gu + key0 + kl);
+              const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+              float val[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                val[e] = sacc[4 * jj + e] * __builtin_amdgcn_exp2f(r2 + uu[e]);
+                if constexpr (diag) val[e] = (kl + e <= tl) ? val[e] : 0.0f;
+                dpart += val[e];
+              }
+              uint2 ph, pl;
+              split_bf16x2(val[0], val[1], ph.x, pl.x);
+              split_bf16x2(val[2], val[3], ph.y, pl.y);
+              *reinterpret_cast<uint2*>(s_ph + (32 * qh + l32) * LDP + kl) = ph;
+              *reinterpret_cast<uint2*>(s_pl + (32 * qh + l32) * LDP + kl) = pl;
+            }
+          };
+          if (j == i) make_p(std::true_type{});
+          else make_p(std::false_type{});
+        }
+        __syncthreads();
+
+        // intra term: H += P . V over 16-key steps
+#pragma unroll
+        for (int kk = 0; kk < TKV / 16; ++kk) {
+          uint4 ahi[2], alo[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            ahi[rb] = frag_row_u(s_ph, LDP, 32 * rb, 16 * kk, lane);
+            alo[rb] = frag_row_u(s_pl, LDP, 32 * rb, 16 * kk, lane);
+          }
+          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, LDV, 16 * kk, 32 * wave, lane));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            if (j == i && 16 * kk > 32 * rb + 31) continue;  // above the diagonal: P is zero
+            hacc[rb] = mma32b(as_bf16x8(ahi[rb]), bv, hacc[rb]);
+            hacc[rb] = mma32b(as_bf16x8(alo[rb]), bv, hacc[rb]);
+          }
+        }
+        // state update: C[:, this wave's columns] += K^T (w . V)
+        if constexpr (last) {
+          const int grp = lane >> 4, jl = lane & 15;
+          const int pc = 16 * (grp & 1) + 4 * (((jl & 1) << 1) | ((jl >> 1) & 1));  // permuted column group
+#pragma unroll
+          for (int kk = 0; kk < TKV / 16; ++kk) {
+            const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_vwh, LDV, 16 * kk, 32 * wave, lane));
+            const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_vwl, LDV, 16 * kk, 32 * wave, lane));
+            const int kr = 16 * kk + 8 * (grp >> 1) + (jl >> 2);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              const int col = 32 * kb + pc;
+              const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) short4_t*)(s_k + koff<DK>(kr, col)));
+              const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) short4_t*)(s_k + koff<DK>(kr + 4, col)));
+              const uint2 a0 = __builtin_bit_cast(uint2, x0), a1 = __builtin_bit_cast(uint2, x1);
+              const bf16x8_t ak = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+              cacc[kb] = mma32b(ak, bh_, cacc[kb]);
+              cacc[kb] = mma32b(ak, bl_, cacc[kb]);
+            }
+          }
+        }
+        __syncthreads();
+      }
+
+      // ---- normaliser and H for this query tile
+      set_roles();
+      if constexpr (!SIG) {
+        dpart += __shfl_xor(dpart, 32, 64);
+        if (h == 0) s_den[2 + kh][32 * qh + l32] = dpart;
+        __syncthreads();
+        if (tid < TQ) {
+          const float d = s_den[0][tid] + s_den[1][tid] + s_den[2][tid] + s_den[3][tid];
+          s_inv[tid] = 1.0f / (fmaxf(fabsf(d), exp2f(-s_row_m2[tid])) + p.eps);
+        }
+        __syncthreads();
+      }
+      auto store_h = [&](auto esize) {
+        constexpr int E = decltype(esize)::value;
+        const __amdgpu_buffer_rsrc_t rh =
+            make_rsrc(static_cast<const char*>(p.H) + ((gbase + t0 + row0) * DV + v0) * E,
+                      (uint32_t)(((Lc - row0 - 1) * DV + TVS) * E));
+        const int hvoff = (4 * h * DV + 32 * wave + l32) * E;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * rb + 8 * (r >> 2) + (r & 3);  // + 4h
+            float hv = hacc[rb][r];
+            if constexpr (!SIG) {
+              const float4 inv = *reinterpret_cast<const float4*>(s_inv + 32 * rb + 8 * (r >> 2) + 4 * h);
+              hv *= (r & 3) == 0 ? inv.x : (r & 3) == 1 ? inv.y : (r & 3) == 2 ? inv.z : inv.w;
+            }
+            if constexpr (E == 2)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, row * DV * E, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, row * DV * E, 0);
+          }
+      };
+      if (p.h_bf16) store_h(std::integral_constant<int, 2>{});
+      else store_h(std::integral_constant<int, 4>{});
+    };
+    for (int i = 0; i + 1 < nsub; ++i) sub_tile(std::false_type{}, i);
+    sub_tile(std::true_type{}, nsub - 1);
+
+    // ---- normaliser after the chunk: n = decay n + sum_t w_t k_t
+    if constexpr (!SIG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int o = KG; o < 64; o <<= 1) np[e] += __shfl_xor(np[e], o, 64);
+      if (lane < KG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_np[wave * DK + lane * 8 + e] = np[e];
+      }
+      __syncthreads();
+      if (tid < DK) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sum += s_np[w * DK + tid];
+        s_n[tid] = dec * s_n[tid] + sum;
+      }
+      M = Mn;
+      __syncthreads();
+    }
+  }
+
+  // ---- final state
+  if (p.C_out) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p.C_out[(size_t)bh * DK * DV + (size_t)state_row(kb, r) * DV + vcol()] = cacc[kb][r];
+  }
+  if constexpr (!SIG) {
+    if (slice == 0) {
+      if (p.n_out && tid < DK) p.n_out[(size_t)bh * DK + tid] = s_n[tid];
+      if (p.m_out && tid == 0) p.m_out[bh] = M * kLn2;
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(const WalkParams& p, bool sig, hipStream_t stream) {
+  const dim3 grid((unsigned)walk_workgroups(p.BH, p.DV));
+  if (sig) hipLaunchKernelGGL((walk_kernel<DK, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((walk_kernel<DK, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split) {
+  return bf16_inputs && split && DK == 256 && DV % kWalkSlice == 0 && L >= 64 && L <= kWalkMaxL;
+}
+
+long long walk_workgroups(int BH, int DV) { return (long long)BH * (DV / kWalkSlice); }
+
+hipError_t launch_walk(const WalkParams& p, bool sig, hipStream_t stream) {
+  if (p.DK == 256) return launch_dk<256>(p, sig, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mlstm
