@@ -51,7 +51,8 @@ def algorithmic_bytes(w, h_bytes: int) -> dict:
 
     states: reads K, V and both gate rows, plus the initial state when given;
             writes the final state.
-    hintra: reads Q, K, V and the gate rows; writes H."""
+    hintra: reads Q, K, V and the gate rows; writes H.
+    walk:   the fused walker: hintra's bytes plus the initial and final state."""
     el = 2 if w.qkv_dtype == "bf16" else 4
     per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
     units = w.BH * w.S
@@ -59,6 +60,7 @@ def algorithmic_bytes(w, h_bytes: int) -> dict:
     return {
         "states": units * ((w.DHQK + w.DHV) * el + 8) + init + w.BH * per_state,
         "hintra": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes),
+        "walk": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes) + init + w.BH * per_state,
     }
 
 
@@ -170,6 +172,8 @@ def main(argv=None) -> int:
     ap.add_argument("--precision", default="split", choices=["split", "f16", "f64"])
     ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--tile-lq", type=int, default=None, help="override the workload's intra-chunk row tile")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "two_stage", "fused"],
+                    help="kernels of the forward pass (see mlstm_schedule_t)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -228,10 +232,12 @@ def main(argv=None) -> int:
     desc = mt.make_desc(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk,
                         qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
                         h_dtype=mt.MLSTM_BF16 if args.h_dtype == "bf16" else mt.MLSTM_F32,
-                        gate=w.gate, precision=args.precision, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv)
-    ws = torch.empty(mt.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+                        gate=w.gate, precision=args.precision, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv,
+                        schedule=args.schedule)
+    fused = mt.kernel_family(desc) == mt.MLSTM_FAMILY_FUSED
+    ws = torch.empty(max(1, mt.workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     kw = dict(chunk_size=w.chunk, gate=w.gate, h_dtype=h_dtype, precision=args.precision,
-              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, workspace=ws, out=H)
+              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, schedule=args.schedule, workspace=ws, out=H)
 
     def step():
         return mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, **kw)
@@ -251,9 +257,10 @@ def main(argv=None) -> int:
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
     ms = e0.elapsed_time(e1) / args.steps
 
-    # Per-kernel durations: the same two launches, issued through the stage
-    # entry points (on the same workspace) with events between them on the
-    # launch stream.
+    # Per-kernel durations with events on the launch stream.  Two-stage: the
+    # same two launches, issued through the stage entry points (on the same
+    # workspace) with events between them.  Fused: the walker call (its gate
+    # terms pass, about half a percent of it, included).
     import ctypes
     L = mt.lib()
     ws_bytes = ws.numel()
@@ -265,6 +272,10 @@ def main(argv=None) -> int:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for it in range(args.steps):
         ev[it][0].record(stream)
+        if fused:
+            step()
+            ev[it][1].record(stream)
+            continue
         st = L.mlstm_fw_states(ctypes.byref(desc), p(k), p(v), p(i_pre), p(f_pre), p(C0), p(n0), p(m0),
                                p(ws), ws_bytes, None, None, None, sptr)
         ev[it][1].record(stream)
@@ -274,8 +285,8 @@ def main(argv=None) -> int:
         if st or st2:
             raise mt.MlstmError(st or st2, "stage call")
     torch.cuda.synchronize()
-    t_states = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_hintra = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    t_first = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_second = 0.0 if fused else sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
     tokens = w.B * w.S
     flops = mt.flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
@@ -288,8 +299,10 @@ def main(argv=None) -> int:
     # intra = Q.C + causal Q.K^T and P.V
     f_stage = {"states": 2.0 * w.DHQK * w.DHV * w.BH * w.S,
                "hintra": (2.0 * w.DHQK * w.DHV + (w.chunk + 1) * (w.DHQK + w.DHV)) * w.BH * w.S}
-    t_stage = {"states": t_states, "hintra": t_hintra}
-    dominant = "hintra" if t_hintra >= t_states else "states"
+    f_stage["walk"] = f_stage["states"] + f_stage["hintra"]
+    t_stage = {"walk": t_first} if fused else {"states": t_first, "hintra": t_second}
+    f_stage = {k_: f_stage[k_] for k_ in t_stage}
+    dominant = max(t_stage, key=t_stage.get)
     t_dom = t_stage[dominant]
     ach = abytes[dominant] / (t_dom * 1e-3) / 1e9
     traffic, traffic_src = recorded_traffic(w.name, dominant, args.tile_lq)
@@ -308,7 +321,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
                    "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
-                   "precision": args.precision, "tile_lq": w.tile_lq or 64},
+                   "precision": args.precision, "tile_lq": w.tile_lq or 64,
+                   "schedule": "fused" if fused else "two_stage"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "wall_ms_per_step": wall_ms,

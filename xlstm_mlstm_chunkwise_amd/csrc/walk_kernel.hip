@@ -14,16 +14,20 @@
 // The TFLA page lists avoiding the HBM round trip of those per-chunk states
 // as a planned follow-up; this kernel is that fused form.
 //
-// Organisation.  One workgroup (4 waves, one per SIMD) owns one head and a
+// Organisation.  One workgroup (8 waves, two per SIMD) owns one head and a
 // 128-column slice of V / H / C and walks the chunks of the head in order.
-// Wave w owns the 32 columns 32w.. of the slice and holds C[:, those columns]
-// (DK x 32 float32) in matrix-core accumulators for the whole run.  Every
-// chunk is processed in 64-row query tiles i; tile i takes the key tiles
-// j <= i:
-//   inter term   H_i  = Q_i . Cbar           (Cbar = C as bf16 hi + lo)
-//   scores       S^T  = K_j . Q_i^T          (each wave one 32 x 32 block)
+// Wave w = (hf, cb), hf = w / 4, cb = w % 4, holds the state block
+// C[128 hf .. 128 hf + 127][32 cb .. 32 cb + 31] (64 float32 values a lane)
+// in matrix-core accumulators for the whole run.  Every chunk is processed in
+// 64-row query tiles i; tile i takes the key tiles j <= i:
+//   inter term   each wave forms Q_i[:, its DK half] . Cbar[its half, cb]
+//                (Cbar = bf16 hi + lo split of its state block); the two DK
+//                halves are summed through LDS, leaving wave (hf, cb) with
+//                rows 32 hf .. 32 hf + 31, columns cb of H
+//   scores       S^T = K_j . Q_i^T in 16 x 16 blocks: wave w takes queries
+//                16 (w % 4) .. + 15 and keys 32 hf .. + 31
 //   P = s S decay, shared through LDS as bf16 hi + lo planes
-//   intra term   H_i += P . V_j
+//   intra term   H += P . V_j for the wave's rows and columns
 // and the last query tile of the chunk also does the state update
 //   C = decay C + K_j^T (w . V_j)            (w . V_j as bf16 hi + lo)
 // after its inter term has used the old state.  The four column slices of a
@@ -31,8 +35,8 @@
 // on-chip); they are placed on one XCD so their Q and K reads share an L2.
 //
 // State precision.  The state stays in float32 accumulators for the whole
-// walk; at the start of every chunk it is split once into the bf16 hi + lo
-// pair that the Q . Cbar products of all its query tiles read.
+// walk; every query tile splits the wave's block into the bf16 hi + lo pair
+// its Q . Cbar product reads.
 //
 // Contraction order.  The state accumulators hold row m of each 32-row block
 // at k index 32 kb + perm(m), where perm swaps the 4-row groups 1 and 2 of
@@ -64,42 +68,47 @@ __device__ __forceinline__ int koff(int r, int c) {
 }
 
 template <int DK, bool SIG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void walk_kernel(const WalkParams p) {
-  constexpr int NT = 256, TQ = 64, TKV = 64, TVS = kWalkSlice;
+__global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
+  constexpr int NT = 512, TQ = 64, TKV = 64, TVS = kWalkSlice;
   constexpr int LDQ = DK + 8;    // 16-byte row reads: 4 banks mod 64
   constexpr int LDV = TVS + 32;  // transposing reads: 16 banks mod 64
   constexpr int LDP = TKV + 8;
-  constexpr int NKB = DK / 32;   // 32-row blocks of the state
-  constexpr int NKS = DK / 16;   // 16-deep k steps over DK
+  constexpr int DKH = DK / 2;    // DK rows of the state held by one wave
+  constexpr int NKB = DKH / 32;  // its 32-row blocks
+  constexpr int NKS = DKH / 16;  // 16-deep k steps over its half
+  constexpr int NSS = DK / 32;   // 32-deep k steps of the scores
   constexpr int KG = DK / 8;     // 16-byte groups per Q / K row
   constexpr int QPT = TQ * KG / NT;
   constexpr int VG = TVS / 8;
   constexpr int VPT = TKV * VG / NT;
-  constexpr int GPT = kWalkMaxL / NT;
   static_assert(QPT * NT == TQ * KG && VPT * NT == TKV * VG, "staging split");
-  static_assert(DK <= NT, "one thread per normaliser entry");
+  static_assert(kWalkMaxL <= NT && DK <= NT, "one thread per position and per normaliser entry");
+  static_assert(2 * TKV * LDV * 2 >= 8 * 16 * 64 * 4, "the inter-term exchange fits the w . V planes");
 
   __shared__ __align__(16) uint16_t s_q[TQ * LDQ];
   __shared__ __align__(16) uint16_t s_k[TKV * DK];
   __shared__ __align__(16) uint16_t s_v[TKV * LDV];
-  __shared__ __align__(16) uint16_t s_vwh[TKV * LDV];
-  __shared__ __align__(16) uint16_t s_vwl[TKV * LDV];
+  __shared__ __align__(16) uint16_t s_vw[2 * TKV * LDV];  // w . V hi plane, then lo plane
   __shared__ __align__(16) uint16_t s_p[2 * TQ * LDP];  // P hi plane, then lo plane
   __shared__ __align__(16) float s_gu[kWalkMaxL];
   __shared__ float s_gb[kWalkMaxL];
   __shared__ float s_gpm[SIG ? 1 : kWalkMaxL];
   __shared__ float s_row_r2[TQ], s_row_w[TQ], s_row_m2[TQ];
-  __shared__ float s_den[4][TQ];  // inter parts (two DK halves), intra parts (two key halves)
+  __shared__ float s_den[3][TQ];  // inter part, intra parts of the two key halves
   __shared__ __align__(16) float s_inv[TQ];
   __shared__ __align__(16) float s_n[DK];
   uint16_t* const s_ph = s_p;
   uint16_t* const s_pl = s_p + TQ * LDP;
+  uint16_t* const s_vwh = s_vw;
+  uint16_t* const s_vwl = s_vw + TKV * LDV;
   float* const s_np = reinterpret_cast<float*>(s_p);  // n partial sums at the end of a chunk
+  float* const s_x = reinterpret_cast<float*>(s_vw);  // inter-term halves, before the w . V planes are staged
+  static_assert(2 * TQ * LDP * 2 >= 8 * DK * 4, "n partial sums fit the P planes");
 
   // Per-lane roles.  They are re-derived from a laundered thread index at the
   // top of every loop level, so the compiler rebuilds the LDS offsets that
-  // depend on them instead of keeping dozens of them live across the walk.
-  int tid, lane, wave, h, l32, kh, qh;  // kh, qh: key half, query half of the score block
+  // depend on them instead of keeping them live across the walk.
+  int tid, lane, wave, h, l32, l16, g4, hf, cb, qb;
   auto set_roles = [&]() {
     int t = (int)threadIdx.x;
     asm volatile("" : "+v"(t));
@@ -110,8 +119,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wave = w;
     h = lane >> 5;
     l32 = lane & 31;
-    kh = w >> 1;
-    qh = w & 1;
+    l16 = lane & 15;
+    g4 = lane >> 4;
+    hf = w >> 2;
+    cb = w & 3;
+    qb = w & 3;
   };
   set_roles();
   const int S = p.S, L = p.L, Nc = p.Nc, DV = p.DV;
@@ -137,13 +149,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK;
   const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV + v0;
   const size_t gbase = (size_t)bh * S;
-  auto vcol = [&]() { return v0 + 32 * wave + l32; };  // the state / H column of this lane
+  auto vcol = [&]() { return v0 + 32 * cb + l32; };  // the state / H column of this lane
 
   // ---- state.  Accumulator register r of block kb holds C[dk][vcol] with
-  // dk = 32 kb + perm(row of r).
+  // dk = DKH hf + 32 kb + perm(row of r).
   auto state_row = [&](int kb, int r) {
     const int j = r >> 2;
-    return 32 * kb + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + (r & 3);
+    return DKH * hf + 32 * kb + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + (r & 3);
   };
   float16_t cacc[NKB];
   {
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // order; K / V tiles in (chunk, query tile, key tile <= query tile) order.
   auto nsub_of = [&](int c) { return (min(L, S - c * L) + TQ - 1) / TQ; };
   uint4 qpre[QPT], kpre[QPT], vpre[VPT];
-  float gpre_u[GPT], gpre_b[GPT], gpre_pm[GPT];
+  float gpre_u, gpre_b, gpre_pm;
   int qc = 0, qi = 0;          // next Q tile to load
   int kc = 0, ki = 0, kj = 0;  // next K / V tile to load
   auto load_q = [&]() {
@@ -200,14 +212,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto load_gates = [&](int c) {
     if (c >= Nc) return;
     const int t0 = c * L, Lc = min(L, S - t0);
-#pragma unroll
-    for (int e = 0; e < GPT; ++e) {
-      const int pos = tid + e * NT;
-      const bool ok = pos < Lc;
-      gpre_u[e] = ok ? p.gu2[gbase + t0 + pos] : 0.0f;
-      gpre_b[e] = ok ? p.gb2[gbase + t0 + pos] : 0.0f;
-      gpre_pm[e] = (!SIG && ok) ? p.gpm2[gbase + t0 + pos] : 0.0f;
-    }
+    const bool ok = tid < Lc;
+    gpre_u = ok ? p.gu2[gbase + t0 + tid] : 0.0f;
+    gpre_b = ok ? p.gb2[gbase + t0 + tid] : 0.0f;
+    gpre_pm = (!SIG && ok) ? p.gpm2[gbase + t0 + tid] : 0.0f;
   };
   load_gates(0);
   load_q();
@@ -220,15 +228,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int t0 = c * L, Lc = min(L, S - t0);
     const int nsub = (Lc + TQ - 1) / TQ;
     // u past the end of a short last chunk is -inf: those keys (zero rows)
-    // get weight exactly zero in P
-#pragma unroll
-    for (int e = 0; e < GPT; ++e) {
-      const int pos = tid + e * NT;
-      if (pos < L) {
-        s_gu[pos] = pos < Lc ? gpre_u[e] : -INFINITY;
-        s_gb[pos] = gpre_b[e];
-        if constexpr (!SIG) s_gpm[pos] = gpre_pm[e];
-      }
+    // get weight exactly zero
+    if (tid < L) {
+      s_gu[tid] = tid < Lc ? gpre_u : -INFINITY;
+      s_gb[tid] = gpre_b;
+      if constexpr (!SIG) s_gpm[tid] = gpre_pm;
     }
     load_gates(c + 1);
 #pragma unroll
@@ -243,16 +247,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       Mn = g2 + fmaxf(M, s_gpm[Lc - 1]);
       dec = exp2f(g2 + M - Mn);
     }
-    // the state entering the chunk as bf16 hi + lo words (word q of block kb
-    // packs registers 2q and 2q + 1), read by every query tile's inter term
-    uint32_t chi[NKB][8], clo[NKB][8];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) split_bf16x2(cacc[kb][2 * q], cacc[kb][2 * q + 1], chi[kb][q], clo[kb][q]);
-    // weight of step sigma in the state update
+    // weight of step sigma in the state update (0 past the chunk end)
     auto upd_w = [&](int sigma) -> float {
-      return SIG ? exp2f(g2 + s_gu[sigma]) : exp2f(g2 + s_gu[sigma] - Mn);  // 0 past the chunk end
+      return SIG ? exp2f(g2 + s_gu[sigma]) : exp2f(g2 + s_gu[sigma] - Mn);
     };
 
     // query tile i; LAST: the chunk's last tile, which also updates the state
@@ -260,8 +257,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       constexpr bool last = decltype(last_c)::value;
       set_roles();
       const int row0 = i * TQ;
-      // per-row terms: exponent offset r2 of the decay, weight of the inter
-      // term, stabiliser m (log2 units)
+      // per-row terms: exponent offset r2 of P (with log2 s; -inf past the
+      // chunk end), weight of the inter term, stabiliser m (log2 units)
       if (tid < TQ) {
         const int tau = row0 + tid;
         float r2 = -INFINITY, wr = 0.0f, m2 = 0.0f;
@@ -289,62 +286,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       load_q();
       __syncthreads();
 
-      // this wave's query half as B fragments of the score blocks (the Q tile
-      // stays in LDS until the next query tile)
-      auto qs = [&](int s) { return *reinterpret_cast<const uint4*>(s_q + (32 * qh + l32) * LDQ + 16 * s + 8 * h); };
+      // this wave's 16 queries as B fragments of the 16 x 16 x 32 score blocks
+      // (the Q tile stays in LDS until the next query tile)
+      auto qs = [&](int s) { return *reinterpret_cast<const uint4*>(s_q + (16 * qb + l16) * LDQ + 32 * s + 8 * g4); };
 
-      // ---- inter term with the state entering the chunk
-      float16_t hacc[2];
+      // ---- inter term over this wave's DK half, both 32-row halves of the tile
+      float16_t part[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) hacc[rb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) part[rb][r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         uint4 a[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) a[rb] = *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + 16 * s + 8 * h);
-        const int q0 = 4 * (s & 1);
-        const bf16x8_t bhi = as_bf16x8(make_uint4(chi[s >> 1][q0], chi[s >> 1][q0 + 1], chi[s >> 1][q0 + 2], chi[s >> 1][q0 + 3]));
-        const bf16x8_t blo = as_bf16x8(make_uint4(clo[s >> 1][q0], clo[s >> 1][q0 + 1], clo[s >> 1][q0 + 2], clo[s >> 1][q0 + 3]));
+        for (int rb = 0; rb < 2; ++rb)
+          a[rb] = *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + DKH * hf + 16 * s + 8 * h);
+        uint32_t bhw[4], blw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          split_bf16x2(cacc[s >> 1][8 * (s & 1) + 2 * e], cacc[s >> 1][8 * (s & 1) + 2 * e + 1], bhw[e], blw[e]);
+        const bf16x8_t bhi = as_bf16x8(make_uint4(bhw[0], bhw[1], bhw[2], bhw[3]));
+        const bf16x8_t blo = as_bf16x8(make_uint4(blw[0], blw[1], blw[2], blw[3]));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          hacc[rb] = mma32b(as_bf16x8(a[rb]), bhi, hacc[rb]);
-          hacc[rb] = mma32b(as_bf16x8(a[rb]), blo, hacc[rb]);
+          part[rb] = mma32b(as_bf16x8(a[rb]), bhi, part[rb]);
+          part[rb] = mma32b(as_bf16x8(a[rb]), blo, part[rb]);
         }
       }
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) hacc[rb][r] *= s_row_w[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
-      // normaliser contribution of the state: s e^{M - m} q . n; each wave
-      // takes its query half over one half of DK
+      // normaliser contribution of the state, s e^{M - m} q . n: thread t
+      // takes row t / 8 over DK / 8 of the entries
       if constexpr (!SIG) {
+        const int row = tid >> 3, seg = (tid & 7) * (DK / 8);
         float d = 0.0f;
 #pragma unroll
-        for (int s0 = 0; s0 < NKS / 2; ++s0) {
-          const int s = kh * (NKS / 2) + s0;
-          const uint4 qv = qs(s);
-          const uint32_t ww[4] = {qv.x, qv.y, qv.z, qv.w};
-          const float4 n0 = *reinterpret_cast<const float4*>(s_n + 16 * s + 8 * h);
-          const float4 n1 = *reinterpret_cast<const float4*>(s_n + 16 * s + 8 * h + 4);
-          d += __uint_as_float(ww[0] << 16) * n0.x + __uint_as_float(ww[0] & 0xffff0000u) * n0.y;
-          d += __uint_as_float(ww[1] << 16) * n0.z + __uint_as_float(ww[1] & 0xffff0000u) * n0.w;
-          d += __uint_as_float(ww[2] << 16) * n1.x + __uint_as_float(ww[2] & 0xffff0000u) * n1.y;
-          d += __uint_as_float(ww[3] << 16) * n1.z + __uint_as_float(ww[3] & 0xffff0000u) * n1.w;
+        for (int g = 0; g < DK / 64; ++g) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(s_q + row * LDQ + seg + 8 * g);
+          const float4 n0 = *reinterpret_cast<const float4*>(s_n + seg + 8 * g);
+          const float4 n1 = *reinterpret_cast<const float4*>(s_n + seg + 8 * g + 4);
+          d += __uint_as_float(qv.x << 16) * n0.x + __uint_as_float(qv.x & 0xffff0000u) * n0.y;
+          d += __uint_as_float(qv.y << 16) * n0.z + __uint_as_float(qv.y & 0xffff0000u) * n0.w;
+          d += __uint_as_float(qv.z << 16) * n1.x + __uint_as_float(qv.z & 0xffff0000u) * n1.y;
+          d += __uint_as_float(qv.w << 16) * n1.z + __uint_as_float(qv.w & 0xffff0000u) * n1.w;
         }
-        d += __shfl_xor(d, 32, 64);
-        if (h == 0) s_den[kh][32 * qh + l32] = d * s_row_w[32 * qh + l32];
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        d += __shfl_xor(d, 4, 64);
+        if ((tid & 7) == 0) s_den[0][row] = d * s_row_w[row];
       }
-      // the last tile decays the old state before accumulating the update
+      // the other half's rows go to the partner wave (same columns, other DK half)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_x[(wave * 16 + r) * 64 + lane] = part[1 - hf][r];
+      __syncthreads();
+      float16_t hacc = part[hf];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        hacc[r] += s_x[((wave ^ 4) * 16 + r) * 64 + lane];
+        hacc[r] *= s_row_w[32 * hf + 8 * (r >> 2) + 4 * h + (r & 3)];
+      }
       if constexpr (last) {
+        __syncthreads();  // the exchange is read before the w . V planes are staged
+        // the last tile decays the old state before accumulating the update
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) cacc[kb][r] *= dec;
       }
       float dpart = 0.0f;
-      const int tl = 32 * qh + l32;  // query of this lane in the score block, within the tile
+      const int tl = 16 * qb + l16;  // query of this lane in the score block, within the tile
       const float r2 = s_row_r2[tl];
 
       // ---- key tiles
@@ -387,38 +396,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         load_kv();
         __syncthreads();
 
-        // scores: this wave's 32 keys x 32 queries, then P = s S 2^{r2 + u}
-        // (masked to keys <= query < chunk end) into the P planes
-        if (!(j == i && kh > qh)) {
-          float16_t sacc;
+        // scores: keys 32 hf + 16 kb + [0, 16) x this wave's 16 queries, then
+        // P = S 2^{r2 + u} (rows past the chunk end have r2 = -inf and keys
+        // past it u = -inf, so only the diagonal tile needs the causal select)
+        {
+          float4_t sacc[2];
+          bool live[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            const uint4 a = *reinterpret_cast<const uint4*>(s_k + koff<DK>(32 * kh + l32, 16 * s + 8 * h));
-            sacc = mma32b(as_bf16x8(a), as_bf16x8(qs(s)), sacc);
+          for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            live[kb] = !(j == i && 32 * hf + 16 * kb > 16 * qb + 15);  // wave-uniform
           }
-          // rows past the chunk end have r2 = -inf and keys past it u = -inf,
-          // so only the causal mask of the diagonal tile needs a select
+#pragma unroll
+          for (int s = 0; s < NSS; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              if (!live[kb]) continue;
+              const uint4 a = *reinterpret_cast<const uint4*>(s_k + koff<DK>(32 * hf + 16 * kb + l16, 32 * s + 8 * g4));
+              sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs(s)), sacc[kb]);
+            }
           auto make_p = [&](auto diag_c) {
             constexpr bool diag = decltype(diag_c)::value;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int kl = 32 * kh + 8 * jj + 4 * h;  // first of this lane's 4 keys, within the tile
+            for (int kb = 0; kb < 2; ++kb) {
+              const int kl = 32 * hf + 16 * kb + 4 * g4;  // first of this lane's 4 keys, within the tile
+              if (!live[kb]) {
+                // above the diagonal: zero, since P . V reads 32-row pieces
+                *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = make_uint2(0u, 0u);
+                *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = make_uint2(0u, 0u);
+                continue;
+              }
               const float4 u4 = *reinterpret_cast<const float4*>(s_gu + key0 + kl);
               const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
               float val[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                val[e] = sacc[4 * jj + e] * __builtin_amdgcn_exp2f(r2 + uu[e]);
+                val[e] = sacc[kb][e] * __builtin_amdgcn_exp2f(r2 + uu[e]);
                 if constexpr (diag) val[e] = (kl + e <= tl) ? val[e] : 0.0f;
                 dpart += val[e];
               }
               uint2 ph, pl;
               split_bf16x2(val[0], val[1], ph.x, pl.x);
               split_bf16x2(val[2], val[3], ph.y, pl.y);
-              *reinterpret_cast<uint2*>(s_ph + (32 * qh + l32) * LDP + kl) = ph;
-              *reinterpret_cast<uint2*>(s_pl + (32 * qh + l32) * LDP + kl) = pl;
+              *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = ph;
+              *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = pl;
             }
           };
           if (j == i) make_p(std::true_type{});
@@ -426,35 +447,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         __syncthreads();
 
-        // intra term: H += P . V over 16-key steps
+        // intra term: H += P . V over 16-key steps (rows 32 hf.., columns cb)
 #pragma unroll
         for (int kk = 0; kk < TKV / 16; ++kk) {
-          uint4 ahi[2], alo[2];
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            ahi[rb] = frag_row_u(s_ph, LDP, 32 * rb, 16 * kk, lane);
-            alo[rb] = frag_row_u(s_pl, LDP, 32 * rb, 16 * kk, lane);
-          }
-          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, LDV, 16 * kk, 32 * wave, lane));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            if (j == i && 16 * kk > 32 * rb + 31) continue;  // above the diagonal: P is zero
-            hacc[rb] = mma32b(as_bf16x8(ahi[rb]), bv, hacc[rb]);
-            hacc[rb] = mma32b(as_bf16x8(alo[rb]), bv, hacc[rb]);
-          }
+          if (j == i && 16 * kk > 32 * hf + 31) continue;  // above the diagonal: P is zero
+          const uint4 ahi = frag_row_u(s_ph, LDP, 32 * hf, 16 * kk, lane);
+          const uint4 alo = frag_row_u(s_pl, LDP, 32 * hf, 16 * kk, lane);
+          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, LDV, 16 * kk, 32 * cb, lane));
+          hacc = mma32b(as_bf16x8(ahi), bv, hacc);
+          hacc = mma32b(as_bf16x8(alo), bv, hacc);
         }
-        // state update: C[:, this wave's columns] += K^T (w . V)
+        // state update: C[this wave's DK half, cb] += K^T (w . V)
         if constexpr (last) {
           const int grp = lane >> 4, jl = lane & 15;
           const int pc = 16 * (grp & 1) + 4 * (((jl & 1) << 1) | ((jl >> 1) & 1));  // permuted column group
 #pragma unroll
           for (int kk = 0; kk < TKV / 16; ++kk) {
-            const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_vwh, LDV, 16 * kk, 32 * wave, lane));
-            const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_vwl, LDV, 16 * kk, 32 * wave, lane));
+            const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_vwh, LDV, 16 * kk, 32 * cb, lane));
+            const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_vwl, LDV, 16 * kk, 32 * cb, lane));
             const int kr = 16 * kk + 8 * (grp >> 1) + (jl >> 2);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-              const int col = 32 * kb + pc;
+              const int col = DKH * hf + 32 * kb + pc;
               const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (__attribute__((address_space(3))) short4_t*)(s_k + koff<DK>(kr, col)));
               const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -472,11 +486,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // ---- normaliser and H for this query tile
       set_roles();
       if constexpr (!SIG) {
+        dpart += __shfl_xor(dpart, 16, 64);
         dpart += __shfl_xor(dpart, 32, 64);
-        if (h == 0) s_den[2 + kh][32 * qh + l32] = dpart;
+        if (lane < 16) s_den[1 + hf][16 * qb + lane] = dpart;
         __syncthreads();
         if (tid < TQ) {
-          const float d = s_den[0][tid] + s_den[1][tid] + s_den[2][tid] + s_den[3][tid];
+          const float d = s_den[0][tid] + s_den[1][tid] + s_den[2][tid];
           s_inv[tid] = 1.0f / (fmaxf(fabsf(d), exp2f(-s_row_m2[tid])) + p.eps);
         }
         __syncthreads();
@@ -486,22 +501,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const __amdgpu_buffer_rsrc_t rh =
             make_rsrc(static_cast<const char*>(p.H) + ((gbase + t0 + row0) * DV + v0) * E,
                       (uint32_t)(((Lc - row0 - 1) * DV + TVS) * E));
-        const int hvoff = (4 * h * DV + 32 * wave + l32) * E;
+        const int hvoff = ((32 * hf + 4 * h) * DV + 32 * cb + l32) * E;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 inv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          if constexpr (!SIG) inv = *reinterpret_cast<const float4*>(s_inv + 32 * hf + 8 * r4 + 4 * h);
+          const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 32 * rb + 8 * (r >> 2) + (r & 3);  // + 4h
-            float hv = hacc[rb][r];
-            if constexpr (!SIG) {
-              const float4 inv = *reinterpret_cast<const float4*>(s_inv + 32 * rb + 8 * (r >> 2) + 4 * h);
-              hv *= (r & 3) == 0 ? inv.x : (r & 3) == 1 ? inv.y : (r & 3) == 2 ? inv.z : inv.w;
-            }
+          for (int q = 0; q < 4; ++q) {
+            const float hv = hacc[4 * r4 + q] * iv[q];
+            const int soff = (8 * r4 + q) * DV * E;
             if constexpr (E == 2)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, row * DV * E, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 0);
             else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, row * DV * E, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 0);
           }
+        }
       };
       if (p.h_bf16) store_h(std::integral_constant<int, 2>{});
       else store_h(std::integral_constant<int, 4>{});
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (tid < DK) {
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) sum += s_np[w * DK + tid];
+        for (int w = 0; w < 8; ++w) sum += s_np[w * DK + tid];
         s_n[tid] = dec * s_n[tid] + sum;
       }
       M = Mn;
@@ -532,6 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- final state
+  set_roles();
   if (p.C_out) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -550,8 +566,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int DK>
 hipError_t launch_dk(const WalkParams& p, bool sig, hipStream_t stream) {
   const dim3 grid((unsigned)walk_workgroups(p.BH, p.DV));
-  if (sig) hipLaunchKernelGGL((walk_kernel<DK, true>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((walk_kernel<DK, false>), grid, dim3(256), 0, stream, p);
+  if (sig) hipLaunchKernelGGL((walk_kernel<DK, true>), grid, dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((walk_kernel<DK, false>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
