@@ -34,9 +34,12 @@
 // head compute the same score tiles (that is the price of keeping C
 // on-chip); they are placed on one XCD so their Q and K reads share an L2.
 //
-// State precision.  The state stays in float32 accumulators for the whole
-// walk; every query tile splits the wave's block into the bf16 hi + lo pair
-// its Q . Cbar product reads.
+// State precision.  Between chunks a wave holds its state block as bf16
+// hi + lo pairs (about 16 significant bits), the operand form of Q . Cbar;
+// the last query tile of a chunk rebuilds float32 accumulators from them,
+// applies the decay, accumulates the chunk's update on the matrix cores and
+// splits the result again.  The rounding error this adds per chunk is
+// relative 2^-17 of the state, and the decay keeps it from growing.
 //
 // Contraction order.  The state accumulators hold row m of each 32-row block
 // at k index 32 kb + perm(m), where perm swaps the 4-row groups 1 and 2 of
@@ -152,22 +155,39 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
   auto vcol = [&]() { return v0 + 32 * cb + l32; };  // the state / H column of this lane
 
   // ---- state.  Accumulator register r of block kb holds C[dk][vcol] with
-  // dk = DKH hf + 32 kb + perm(row of r).
+  // dk = DKH hf + 32 kb + perm(row of r); chi / clo hold the block as bf16
+  // hi + lo words, word q packing registers 2q (low half) and 2q + 1.
   auto state_row = [&](int kb, int r) {
     const int j = r >> 2;
     return DKH * hf + 32 * kb + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + (r & 3);
   };
-  float16_t cacc[NKB];
-  {
-    // a zero-extent resource reads zeros when there is no initial state
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(p.C0 ? p.C0 + (size_t)bh * DK * DV : p.gb2, p.C0 ? (uint32_t)(DK * DV * 4) : 0u);
+  uint32_t chi[NKB][8], clo[NKB][8];
+  auto split_state = [&](const float16_t* acc) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) split_bf16x2(acc[kb][2 * q], acc[kb][2 * q + 1], chi[kb][q], clo[kb][q]);
+  };
+  auto write_state = [&](const float16_t* acc) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        cacc[kb][r] = __builtin_bit_cast(
+        p.C_out[(size_t)bh * DK * DV + (size_t)state_row(kb, r) * DV + vcol()] = acc[kb][r];
+  };
+  {
+    // a zero-extent resource reads zeros when there is no initial state
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C0 ? p.C0 + (size_t)bh * DK * DV : p.gb2, p.C0 ? (uint32_t)(DK * DV * 4) : 0u);
+    float16_t c0[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        c0[kb][r] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rc, (state_row(kb, r) * DV + vcol()) * 4, 0, 0));
+    if (Nc == 0 && p.C_out) write_state(c0);  // empty sequence: the initial state, exactly
+    split_state(c0);
   }
   if (!SIG && tid < DK) s_n[tid] = p.n0 ? p.n0[(size_t)bh * DK + tid] : 0.0f;
   float M = (!SIG && p.m0) ? p.m0[bh] * kLog2e : 0.0f;  // stabiliser, log2 units
@@ -302,12 +322,11 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           a[rb] = *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + DKH * hf + 16 * s + 8 * h);
-        uint32_t bhw[4], blw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          split_bf16x2(cacc[s >> 1][8 * (s & 1) + 2 * e], cacc[s >> 1][8 * (s & 1) + 2 * e + 1], bhw[e], blw[e]);
-        const bf16x8_t bhi = as_bf16x8(make_uint4(bhw[0], bhw[1], bhw[2], bhw[3]));
-        const bf16x8_t blo = as_bf16x8(make_uint4(blw[0], blw[1], blw[2], blw[3]));
+        const int q0 = 4 * (s & 1);
+        const bf16x8_t bhi =
+            as_bf16x8(make_uint4(chi[s >> 1][q0], chi[s >> 1][q0 + 1], chi[s >> 1][q0 + 2], chi[s >> 1][q0 + 3]));
+        const bf16x8_t blo =
+            as_bf16x8(make_uint4(clo[s >> 1][q0], clo[s >> 1][q0 + 1], clo[s >> 1][q0 + 2], clo[s >> 1][q0 + 3]));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           part[rb] = mma32b(as_bf16x8(a[rb]), bhi, part[rb]);
@@ -344,13 +363,18 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         hacc[r] += s_x[((wave ^ 4) * 16 + r) * 64 + lane];
         hacc[r] *= s_row_w[32 * hf + 8 * (r >> 2) + 4 * h + (r & 3)];
       }
+      // the last tile rebuilds float32 accumulators: decay times the old state
+      float16_t cacc[last ? NKB : 1];
       if constexpr (last) {
         __syncthreads();  // the exchange is read before the w . V planes are staged
-        // the last tile decays the old state before accumulating the update
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) cacc[kb][r] *= dec;
+          for (int q = 0; q < 8; ++q) {
+            cacc[kb][2 * q] = dec * (__uint_as_float(chi[kb][q] << 16) + __uint_as_float(clo[kb][q] << 16));
+            cacc[kb][2 * q + 1] =
+                dec * (__uint_as_float(chi[kb][q] & 0xffff0000u) + __uint_as_float(clo[kb][q] & 0xffff0000u));
+          }
       }
       float dpart = 0.0f;
       const int tl = 16 * qb + l16;  // query of this lane in the score block, within the tile
@@ -362,11 +386,14 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         set_roles();
         const int key0 = j * TKV;
         // stage K (swizzled), V and, for the update, w . V as hi / lo planes
+        // piece e of this thread is row tid / KG + e NT / KG, column group
+        // tid % KG; the swizzle of a row repeats every 16 rows
+        static_assert((NT / KG) % 16 == 0, "swizzle period");
+        const int kst = koff<DK>(tid / KG, (tid % KG) * 8);
 #pragma unroll
         for (int e = 0; e < QPT; ++e) {
-          const int idx = tid + e * NT;
-          const int rr = idx / KG, cc = (idx % KG) * 8;
-          *reinterpret_cast<uint4*>(s_k + koff<DK>(rr, cc)) = kpre[e];
+          const int rr = tid / KG + e * (NT / KG);
+          *reinterpret_cast<uint4*>(s_k + kst + e * (NT / KG) * DK) = kpre[e];
           if (!SIG && last) {
             const float w = upd_w(key0 + rr);
             const uint32_t ww[4] = {kpre[e].x, kpre[e].y, kpre[e].z, kpre[e].w};
@@ -377,11 +404,12 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
             }
           }
         }
+        const int vst = (tid / VG) * LDV + (tid % VG) * 8;
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
-          const int idx = tid + e * NT;
-          const int rr = idx / VG, cc = (idx % VG) * 8;
-          *reinterpret_cast<uint4*>(s_v + rr * LDV + cc) = vpre[e];
+          const int rr = tid / VG + e * (NT / VG);
+          const int vo = vst + e * (NT / VG) * LDV;
+          *reinterpret_cast<uint4*>(s_v + vo) = vpre[e];
           if constexpr (last) {
             const float w = upd_w(key0 + rr);
             const uint32_t ww[4] = {vpre[e].x, vpre[e].y, vpre[e].z, vpre[e].w};
@@ -389,8 +417,8 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               split_bf16x2(w * __uint_as_float(ww[q] << 16), w * __uint_as_float(ww[q] & 0xffff0000u), hw[q], lw[q]);
-            *reinterpret_cast<uint4*>(s_vwh + rr * LDV + cc) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            *reinterpret_cast<uint4*>(s_vwl + rr * LDV + cc) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            *reinterpret_cast<uint4*>(s_vwh + vo) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4*>(s_vwl + vo) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
           }
         }
         load_kv();
@@ -398,52 +426,57 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
 
         // scores: keys 32 hf + 16 kb + [0, 16) x this wave's 16 queries, then
         // P = S 2^{r2 + u} (rows past the chunk end have r2 = -inf and keys
-        // past it u = -inf, so only the diagonal tile needs the causal select)
-        {
+        // past it u = -inf, so only the diagonal tile needs the causal
+        // select).  NLIVE key blocks hold keys at or below some query of the
+        // wave; the others are above the diagonal and written as zero, since
+        // P . V reads 32-row pieces.
+        auto scores = [&](auto nlive_c, auto diag_c) {
+          constexpr int NLIVE = decltype(nlive_c)::value;
+          constexpr bool diag = decltype(diag_c)::value;
           float4_t sacc[2];
-          bool live[2];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            live[kb] = !(j == i && 32 * hf + 16 * kb > 16 * qb + 15);  // wave-uniform
+          for (int kb = 0; kb < NLIVE; ++kb) sacc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < NSS; ++s) {
+            const uint4 b = qs(s);
+#pragma unroll
+            for (int kb = 0; kb < NLIVE; ++kb) {
+              const uint4 a = *reinterpret_cast<const uint4*>(s_k + koff<DK>(32 * hf + 16 * kb + l16, 32 * s + 8 * g4));
+              sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(b), sacc[kb]);
+            }
           }
 #pragma unroll
-          for (int s = 0; s < NSS; ++s)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              if (!live[kb]) continue;
-              const uint4 a = *reinterpret_cast<const uint4*>(s_k + koff<DK>(32 * hf + 16 * kb + l16, 32 * s + 8 * g4));
-              sacc[kb] = mma16b(as_bf16x8(a), as_bf16x8(qs(s)), sacc[kb]);
+          for (int kb = 0; kb < 2; ++kb) {
+            const int kl = 32 * hf + 16 * kb + 4 * g4;  // first of this lane's 4 keys, within the tile
+            if (kb >= NLIVE) {
+              *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = make_uint2(0u, 0u);
+              *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = make_uint2(0u, 0u);
+              continue;
             }
-          auto make_p = [&](auto diag_c) {
-            constexpr bool diag = decltype(diag_c)::value;
+            const float4 u4 = *reinterpret_cast<const float4*>(s_gu + key0 + kl);
+            const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+            float val[4];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const int kl = 32 * hf + 16 * kb + 4 * g4;  // first of this lane's 4 keys, within the tile
-              if (!live[kb]) {
-                // above the diagonal: zero, since P . V reads 32-row pieces
-                *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = make_uint2(0u, 0u);
-                *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = make_uint2(0u, 0u);
-                continue;
-              }
-              const float4 u4 = *reinterpret_cast<const float4*>(s_gu + key0 + kl);
-              const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
-              float val[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                val[e] = sacc[kb][e] * __builtin_amdgcn_exp2f(r2 + uu[e]);
-                if constexpr (diag) val[e] = (kl + e <= tl) ? val[e] : 0.0f;
-                dpart += val[e];
-              }
-              uint2 ph, pl;
-              split_bf16x2(val[0], val[1], ph.x, pl.x);
-              split_bf16x2(val[2], val[3], ph.y, pl.y);
-              *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = ph;
-              *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = pl;
+            for (int e = 0; e < 4; ++e) {
+              val[e] = sacc[kb][e] * __builtin_amdgcn_exp2f(r2 + uu[e]);
+              if constexpr (diag) val[e] = (kl + e <= tl) ? val[e] : 0.0f;
+              dpart += val[e];
             }
-          };
-          if (j == i) make_p(std::true_type{});
-          else make_p(std::false_type{});
+            uint2 ph, pl;
+            split_bf16x2(val[0], val[1], ph.x, pl.x);
+            split_bf16x2(val[2], val[3], ph.y, pl.y);
+            *reinterpret_cast<uint2*>(s_ph + tl * LDP + kl) = ph;
+            *reinterpret_cast<uint2*>(s_pl + tl * LDP + kl) = pl;
+          }
+        };
+        if (j < i) {
+          scores(std::integral_constant<int, 2>{}, std::false_type{});
+        } else if (32 * hf + 16 <= 16 * qb + 15) {
+          scores(std::integral_constant<int, 2>{}, std::true_type{});
+        } else if (32 * hf <= 16 * qb + 15) {
+          scores(std::integral_constant<int, 1>{}, std::true_type{});
+        } else {
+          scores(std::integral_constant<int, 0>{}, std::true_type{});
         }
         __syncthreads();
 
@@ -481,6 +514,10 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
           }
         }
         __syncthreads();
+      }
+      if constexpr (last) {
+        if (c == Nc - 1 && p.C_out) write_state(cacc);
+        split_state(cacc);
       }
 
       // ---- normaliser and H for this query tile
@@ -546,15 +583,9 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
     }
   }
 
-  // ---- final state
+  // ---- final normaliser and stabiliser (the final C was written by the last
+  // chunk's update, or copied from C0 for an empty sequence)
   set_roles();
-  if (p.C_out) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        p.C_out[(size_t)bh * DK * DV + (size_t)state_row(kb, r) * DV + vcol()] = cacc[kb][r];
-  }
   if constexpr (!SIG) {
     if (slice == 0) {
       if (p.n_out && tid < DK) p.n_out[(size_t)bh * DK + tid] = s_n[tid];
