@@ -382,8 +382,6 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
 
       // ---- key tiles
       for (int j = 0; j <= i; ++j) {
-        __builtin_amdgcn_sched_barrier(0);
-        set_roles();
         const int key0 = j * TKV;
         // stage K (swizzled), V and, for the update, w . V as hi / lo planes
         // piece e of this thread is row tid / KG + e NT / KG, column group
@@ -494,18 +492,25 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         if constexpr (last) {
           const int grp = lane >> 4, jl = lane & 15;
           const int pc = 16 * (grp & 1) + 4 * (((jl & 1) << 1) | ((jl >> 1) & 1));  // permuted column group
+          // rows kr0 + 16 kk and kr0 + 4 + 16 kk: the swizzle repeats every 16
+          // rows, so each column block needs two base offsets
+          const int kr0 = 8 * (grp >> 1) + (jl >> 2);
+          int kbase[NKB][2];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            kbase[kb][0] = koff<DK>(kr0, DKH * hf + 32 * kb + pc);
+            kbase[kb][1] = koff<DK>(kr0 + 4, DKH * hf + 32 * kb + pc);
+          }
 #pragma unroll
           for (int kk = 0; kk < TKV / 16; ++kk) {
             const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_vwh, LDV, 16 * kk, 32 * cb, lane));
             const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_vwl, LDV, 16 * kk, 32 * cb, lane));
-            const int kr = 16 * kk + 8 * (grp >> 1) + (jl >> 2);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-              const int col = DKH * hf + 32 * kb + pc;
               const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) short4_t*)(s_k + koff<DK>(kr, col)));
+                  (__attribute__((address_space(3))) short4_t*)(s_k + kbase[kb][0] + 16 * kk * DK));
               const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) short4_t*)(s_k + koff<DK>(kr + 4, col)));
+                  (__attribute__((address_space(3))) short4_t*)(s_k + kbase[kb][1] + 16 * kk * DK));
               const uint2 a0 = __builtin_bit_cast(uint2, x0), a1 = __builtin_bit_cast(uint2, x1);
               const bf16x8_t ak = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
               cacc[kb] = mma32b(ak, bh_, cacc[kb]);
