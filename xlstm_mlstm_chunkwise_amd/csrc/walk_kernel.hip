@@ -29,8 +29,11 @@
 //   P = s S decay, shared through LDS as bf16 hi + lo planes
 //   intra term   H += P . V_j for the wave's rows and columns
 // and the last query tile of the chunk also does the state update
-//   C = decay C + K_j^T (w . V_j)            (w . V_j as bf16 hi + lo)
-// after its inter term has used the old state.  The four column slices of a
+//   C = decay C + K_j^T (w . V_j)            (w . V_j as bf16 hi + lo,
+//                                             formed from the V fragments)
+// after its inter term has used the old state.  K and V tiles are double
+// buffered: while the waves run P . V and the update on tile j, the next tile
+// goes into the other buffers, so a key tile costs two barriers.  The four column slices of a
 // head compute the same score tiles (that is the price of keeping C
 // on-chip); they are placed on one XCD so their Q and K reads share an L2.
 //
@@ -70,11 +73,29 @@ __device__ __forceinline__ int koff(int r, int c) {
   return r * DK + (((c >> 3) ^ kswz(r)) << 3) + (c & 7);
 }
 
+// V tiles (kWalkSlice columns, unpadded): the 16-byte column groups of row r
+// are XOR-ed with 4 (r % 4), which keeps both the 16-byte staging writes (one
+// row, 16 groups) and the transposing reads (4 consecutive rows, 4
+// consecutive groups) on distinct banks.
+__device__ __forceinline__ int voff(int r, int c) {
+  return r * kWalkSlice + (((c >> 3) ^ (4 * (r & 3))) << 3) + (c & 7);
+}
+// Fragment whose contraction axis runs down the rows of a swizzled V tile:
+// lane l gets V[k0 + 8 (l / 32) + e][c0 + l % 32], e = 0..7.
+__device__ __forceinline__ uint4 frag_tr_v(const uint16_t* X, int k0, int c0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const int o = voff(k0 + 8 * (grp >> 1) + (j >> 2), c0 + 16 * (grp & 1) + 4 * (j & 3));
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(X + o));
+  const short4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(X + o + 4 * kWalkSlice));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 template <int DK, bool SIG>
 __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
   constexpr int NT = 512, TQ = 64, TKV = 64, TVS = kWalkSlice;
   constexpr int LDQ = DK + 8;    // 16-byte row reads: 4 banks mod 64
-  constexpr int LDV = TVS + 32;  // transposing reads: 16 banks mod 64
   constexpr int LDP = TKV + 8;
   constexpr int DKH = DK / 2;    // DK rows of the state held by one wave
   constexpr int NKB = DKH / 32;  // its 32-row blocks
@@ -86,13 +107,13 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
   constexpr int VPT = TKV * VG / NT;
   static_assert(QPT * NT == TQ * KG && VPT * NT == TKV * VG, "staging split");
   static_assert(kWalkMaxL <= NT && DK <= NT, "one thread per position and per normaliser entry");
-  static_assert(2 * TKV * LDV * 2 >= 8 * 16 * 64 * 4, "the inter-term exchange fits the w . V planes");
+  static_assert(TKV * DK * 2 >= 8 * 16 * 64 * 4, "the inter-term exchange fits a K buffer");
 
   __shared__ __align__(16) uint16_t s_q[TQ * LDQ];
-  __shared__ __align__(16) uint16_t s_k[TKV * DK];
-  __shared__ __align__(16) uint16_t s_v[TKV * LDV];
-  __shared__ __align__(16) uint16_t s_vw[2 * TKV * LDV];  // w . V hi plane, then lo plane
+  __shared__ __align__(16) uint16_t s_kb[2][TKV * DK];   // K tiles, double buffered
+  __shared__ __align__(16) uint16_t s_vb[2][TKV * TVS];  // V tiles, double buffered
   __shared__ __align__(16) uint16_t s_p[2 * TQ * LDP];  // P hi plane, then lo plane
+  __shared__ __align__(16) float s_w[TKV];               // update weights of the current key tile
   __shared__ __align__(16) float s_gu[kWalkMaxL];
   __shared__ float s_gb[kWalkMaxL];
   __shared__ float s_gpm[SIG ? 1 : kWalkMaxL];
@@ -102,10 +123,7 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
   __shared__ __align__(16) float s_n[DK];
   uint16_t* const s_ph = s_p;
   uint16_t* const s_pl = s_p + TQ * LDP;
-  uint16_t* const s_vwh = s_vw;
-  uint16_t* const s_vwl = s_vw + TKV * LDV;
   float* const s_np = reinterpret_cast<float*>(s_p);  // n partial sums at the end of a chunk
-  float* const s_x = reinterpret_cast<float*>(s_vw);  // inter-term halves, before the w . V planes are staged
   static_assert(2 * TQ * LDP * 2 >= 8 * DK * 4, "n partial sums fit the P planes");
 
   // Per-lane roles.  They are re-derived from a laundered thread index at the
@@ -237,9 +255,33 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
     gpre_b = ok ? p.gb2[gbase + t0 + tid] : 0.0f;
     gpre_pm = (!SIG && ok) ? p.gpm2[gbase + t0 + tid] : 0.0f;
   };
+  // K / V tile n of the (chunk, query tile, key tile) sequence sits in
+  // buffer n % 2; ks counts the tiles consumed.  stage() writes the tile held
+  // in registers into the buffer after the current one and requests the
+  // next; have_kv says whether registers hold a tile.
+  bool have_kv = false;
+  int ks = 0;
+  // piece e of this thread is K row tid / KG + e NT / KG, column group
+  // tid % KG (the swizzle of a row repeats every 16 rows), and V row
+  // tid / VG + e NT / VG, column group tid % VG (period 4)
+  static_assert((NT / KG) % 16 == 0 && (NT / VG) % 4 == 0, "swizzle period");
+  auto stage = [&](int buf) {
+    if (have_kv) {
+      const int kst = koff<DK>(tid / KG, (tid % KG) * 8);
+#pragma unroll
+      for (int e = 0; e < QPT; ++e) *reinterpret_cast<uint4*>(s_kb[buf] + kst + e * (NT / KG) * DK) = kpre[e];
+      const int vst = voff(tid / VG, (tid % VG) * 8);
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) *reinterpret_cast<uint4*>(s_vb[buf] + vst + e * (NT / VG) * TVS) = vpre[e];
+    }
+    have_kv = kc < Nc;
+    load_kv();
+  };
   load_gates(0);
   load_q();
+  have_kv = kc < Nc;
   load_kv();
+  stage(0);
 
   float np[8];  // n partial sums of this thread's key columns (exp gate)
 
@@ -353,7 +395,9 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         d += __shfl_xor(d, 4, 64);
         if ((tid & 7) == 0) s_den[0][row] = d * s_row_w[row];
       }
-      // the other half's rows go to the partner wave (same columns, other DK half)
+      // the other half's rows go to the partner wave (same columns, other DK
+      // half), through the K buffer that does not hold the next tile
+      float* const s_x = reinterpret_cast<float*>(s_kb[(ks & 1) ^ 1]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_x[(wave * 16 + r) * 64 + lane] = part[1 - hf][r];
       __syncthreads();
@@ -366,7 +410,6 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       // the last tile rebuilds float32 accumulators: decay times the old state
       float16_t cacc[last ? NKB : 1];
       if constexpr (last) {
-        __syncthreads();  // the exchange is read before the w . V planes are staged
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -380,47 +423,15 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       const int tl = 16 * qb + l16;  // query of this lane in the score block, within the tile
       const float r2 = s_row_r2[tl];
 
-      // ---- key tiles
+      // ---- key tiles: tile j is in buffers ks % 2 (staged one tile ahead)
       for (int j = 0; j <= i; ++j) {
         const int key0 = j * TKV;
-        // stage K (swizzled), V and, for the update, w . V as hi / lo planes
-        // piece e of this thread is row tid / KG + e NT / KG, column group
-        // tid % KG; the swizzle of a row repeats every 16 rows
-        static_assert((NT / KG) % 16 == 0, "swizzle period");
-        const int kst = koff<DK>(tid / KG, (tid % KG) * 8);
-#pragma unroll
-        for (int e = 0; e < QPT; ++e) {
-          const int rr = tid / KG + e * (NT / KG);
-          *reinterpret_cast<uint4*>(s_k + kst + e * (NT / KG) * DK) = kpre[e];
-          if (!SIG && last) {
-            const float w = upd_w(key0 + rr);
-            const uint32_t ww[4] = {kpre[e].x, kpre[e].y, kpre[e].z, kpre[e].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              np[2 * q] += w * __uint_as_float(ww[q] << 16);
-              np[2 * q + 1] += w * __uint_as_float(ww[q] & 0xffff0000u);
-            }
-          }
+        const int cur = ks & 1;
+        const uint16_t* const s_k = s_kb[cur];
+        const uint16_t* const s_v = s_vb[cur];
+        if constexpr (last) {
+          if (tid < TKV) s_w[tid] = upd_w(key0 + tid);
         }
-        const int vst = (tid / VG) * LDV + (tid % VG) * 8;
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-          const int rr = tid / VG + e * (NT / VG);
-          const int vo = vst + e * (NT / VG) * LDV;
-          *reinterpret_cast<uint4*>(s_v + vo) = vpre[e];
-          if constexpr (last) {
-            const float w = upd_w(key0 + rr);
-            const uint32_t ww[4] = {vpre[e].x, vpre[e].y, vpre[e].z, vpre[e].w};
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              split_bf16x2(w * __uint_as_float(ww[q] << 16), w * __uint_as_float(ww[q] & 0xffff0000u), hw[q], lw[q]);
-            *reinterpret_cast<uint4*>(s_vwh + vo) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            *reinterpret_cast<uint4*>(s_vwl + vo) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-          }
-        }
-        load_kv();
-        __syncthreads();
 
         // scores: keys 32 hf + 16 kb + [0, 16) x this wave's 16 queries, then
         // P = S 2^{r2 + u} (rows past the chunk end have r2 = -inf and keys
@@ -478,33 +489,46 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         }
         __syncthreads();
 
-        // intra term: H += P . V over 16-key steps (rows 32 hf.., columns cb)
-#pragma unroll
-        for (int kk = 0; kk < TKV / 16; ++kk) {
-          if (j == i && 16 * kk > 32 * hf + 31) continue;  // above the diagonal: P is zero
-          const uint4 ahi = frag_row_u(s_ph, LDP, 32 * hf, 16 * kk, lane);
-          const uint4 alo = frag_row_u(s_pl, LDP, 32 * hf, 16 * kk, lane);
-          const bf16x8_t bv = as_bf16x8(frag_tr_u(s_v, LDV, 16 * kk, 32 * cb, lane));
-          hacc = mma32b(as_bf16x8(ahi), bv, hacc);
-          hacc = mma32b(as_bf16x8(alo), bv, hacc);
-        }
-        // state update: C[this wave's DK half, cb] += K^T (w . V)
+        // intra term H += P . V over 16-key steps (rows 32 hf.., columns cb)
+        // and, on the last query tile, the state update C[this wave's DK
+        // half, cb] += K^T (w . V) from the same V fragments
+        [[maybe_unused]] int kbase[NKB][2];
         if constexpr (last) {
           const int grp = lane >> 4, jl = lane & 15;
           const int pc = 16 * (grp & 1) + 4 * (((jl & 1) << 1) | ((jl >> 1) & 1));  // permuted column group
           // rows kr0 + 16 kk and kr0 + 4 + 16 kk: the swizzle repeats every 16
           // rows, so each column block needs two base offsets
           const int kr0 = 8 * (grp >> 1) + (jl >> 2);
-          int kbase[NKB][2];
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
             kbase[kb][0] = koff<DK>(kr0, DKH * hf + 32 * kb + pc);
             kbase[kb][1] = koff<DK>(kr0 + 4, DKH * hf + 32 * kb + pc);
           }
+        }
 #pragma unroll
-          for (int kk = 0; kk < TKV / 16; ++kk) {
-            const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_vwh, LDV, 16 * kk, 32 * cb, lane));
-            const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_vwl, LDV, 16 * kk, 32 * cb, lane));
+        for (int kk = 0; kk < TKV / 16; ++kk) {
+          const bool pv_live = !(j == i && 16 * kk > 32 * hf + 31);  // above the diagonal: P is zero
+          if (!last && !pv_live) continue;
+          const uint4 vraw = frag_tr_v(s_v, 16 * kk, 32 * cb, lane);
+          if (pv_live) {
+            const uint4 ahi = frag_row_u(s_ph, LDP, 32 * hf, 16 * kk, lane);
+            const uint4 alo = frag_row_u(s_pl, LDP, 32 * hf, 16 * kk, lane);
+            hacc = mma32b(as_bf16x8(ahi), as_bf16x8(vraw), hacc);
+            hacc = mma32b(as_bf16x8(alo), as_bf16x8(vraw), hacc);
+          }
+          if constexpr (last) {
+            // w . V for keys 16 kk + 8 (lane / 32) + e as bf16 hi + lo
+            const float4 w0 = *reinterpret_cast<const float4*>(s_w + 16 * kk + 8 * h);
+            const float4 w1 = *reinterpret_cast<const float4*>(s_w + 16 * kk + 8 * h + 4);
+            const uint32_t vv[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
+            const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              split_bf16x2(ww[2 * q] * __uint_as_float(vv[q] << 16), ww[2 * q + 1] * __uint_as_float(vv[q] & 0xffff0000u),
+                           hw[q], lw[q]);
+            const bf16x8_t bh_ = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            const bf16x8_t bl_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
               const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -518,6 +542,26 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
             }
           }
         }
+        // n partial sums (exp gate, last query tile): this thread's K pieces
+        // of the tile, weighted
+        if constexpr (!SIG && last) {
+          const int kst = koff<DK>(tid / KG, (tid % KG) * 8);
+#pragma unroll
+          for (int e = 0; e < QPT; ++e) {
+            const float w = s_w[tid / KG + e * (NT / KG)];
+            const uint4 kv = *reinterpret_cast<const uint4*>(s_k + kst + e * (NT / KG) * DK);
+            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              np[2 * q] += w * __uint_as_float(kw[q] << 16);
+              np[2 * q + 1] += w * __uint_as_float(kw[q] & 0xffff0000u);
+            }
+          }
+        }
+        // the next tile into the other buffers (last read before the previous
+        // barrier)
+        stage(cur ^ 1);
+        ++ks;
         __syncthreads();
       }
       if constexpr (last) {
