@@ -494,11 +494,13 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           for (int q = 0; q < 4; ++q) {
 #pragma unroll
             for (int cb = 0; cb < W::CB; ++cb) {
+              // non-temporal (aux 2): H is not read again here, so it should
+              // not push the state and K/V lines of sibling row tiles out of L2
               const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
               if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 2);
               else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 2);
             }
           }
         }

@@ -597,10 +597,11 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
           for (int q = 0; q < 4; ++q) {
             const float hv = hacc[4 * r4 + q] * iv[q];
             const int soff = (8 * r4 + q) * DV * E;
+            // non-temporal (aux 2): H is written once and never read here
             if constexpr (E == 2)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 2);
             else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 2);
           }
         }
       };
