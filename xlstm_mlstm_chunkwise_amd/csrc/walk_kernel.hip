@@ -275,6 +275,9 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       __syncthreads();  // [G] gate terms
       float g2, Mn, dec;
       chunk_scalars(Lc, M, g2, Mn, dec);
+      float np[8];  // n partial sums of this thread's K column group (exp gate)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) np[e] = 0.0f;
 
       for (int i = 0; i < nsub; ++i) {
         set_roles();
@@ -316,15 +319,20 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         // with the full sum for its query l16
         float dint = 0.0f;
         if constexpr (!SIG) {
-          float4_t dacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          float4_t dacc[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+          uint4 nf[NSS][2];
 #pragma unroll
           for (int s = 0; s < NSS; ++s) {
-            const uint4 nh = *reinterpret_cast<const uint4*>(s_nh + 32 * s + 8 * g4);
-            const uint4 nl = *reinterpret_cast<const uint4*>(s_nl + 32 * s + 8 * g4);
-            dacc = mma16b(as_bf16x8(nh), as_bf16x8(qf[s]), dacc);
-            dacc = mma16b(as_bf16x8(nl), as_bf16x8(qf[s]), dacc);
+            nf[s][0] = *reinterpret_cast<const uint4*>(s_nh + 32 * s + 8 * g4);
+            nf[s][1] = *reinterpret_cast<const uint4*>(s_nl + 32 * s + 8 * g4);
           }
-          dint = dacc[0];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < NSS; ++s) {
+            dacc[0] = mma16b(as_bf16x8(nf[s][0]), as_bf16x8(qf[s]), dacc[0]);
+            dacc[1] = mma16b(as_bf16x8(nf[s][1]), as_bf16x8(qf[s]), dacc[1]);
+          }
+          dint = dacc[0][0] + dacc[1][0];
         }
         float4_t hacc[NCB];
 #pragma unroll
@@ -351,14 +359,39 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int x = 0; x < 2; ++x) sacc[kb][x] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            // K reads in two halves of the DK range, each half's reads all out
+            // before its MFMAs (a scheduling barrier keeps the compiler from
+            // sinking each read to its use)
 #pragma unroll
-            for (int s = 0; s < NSS; ++s)
+            for (int hh = 0; hh < 2; ++hh) {
+              uint4 kf[NSS / 2][2];
 #pragma unroll
-              for (int kb = 0; kb < NLIVE; ++kb) {
-                const uint4 a =
-                    *reinterpret_cast<const uint4*>(s_k + kfa[s & 3] + 128 * (s >> 2) + 16 * kb * DK);
-                sacc[kb][s & 1] = mma16b(as_bf16x8(a), as_bf16x8(qf[s]), sacc[kb][s & 1]);
+              for (int x = 0; x < NSS / 2; ++x)
+#pragma unroll
+                for (int kb = 0; kb < NLIVE; ++kb)
+                  kf[x][kb] = *reinterpret_cast<const uint4*>(s_k + kfa[x] + 128 * hh + 16 * kb * DK);
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int x = 0; x < NSS / 2; ++x)
+#pragma unroll
+                for (int kb = 0; kb < NLIVE; ++kb)
+                  sacc[kb][x & 1] = mma16b(as_bf16x8(kf[x][kb]), as_bf16x8(qf[4 * hh + x]), sacc[kb][x & 1]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            // the V reads of the first four column blocks go out next, so that
+            // they overlap the forming of P
+            const int vb0 = swz<TVS>(4 * g4 + (l16 >> 2), 4 * (l16 & 3));
+            constexpr int NCH = NCB / 2;
+            uint2 vx[NCH][2];
+            auto read_v = [&](int cb0) {
+#pragma unroll
+              for (int x = 0; x < NCH; ++x) {
+                vx[x][0] = lds_tr(s_v + (vb0 ^ ((cb0 + x) << 4)));
+                vx[x][1] = lds_tr(s_v + (vb0 ^ ((cb0 + x) << 4)) + 16 * TVS);
               }
+            };
+            read_v(0);
+            __builtin_amdgcn_sched_barrier(0);
             // P for keys key0 + 16 kb + 4 g + e (slot 4 kb + e of the P.V
             // operand) as bf16 hi / lo words; rows past the chunk end have
             // r2 = -inf and keys past it u = -inf, so only the diagonal block
@@ -389,21 +422,43 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
             // each 16-lane group addresses row 4 g + j / 4 (and 16 rows
             // further), columns 16 cb + 4 (j % 4) ..; the swizzle repeats
             // every 16 rows and moves with cb as an XOR of bits 4..6
-            const int vb0 = swz<TVS>(4 * g4 + (l16 >> 2), 4 * (l16 & 3));
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-              const int o = vb0 ^ (cb << 4);
-              const uint2 x0 = lds_tr(s_v + o);
-              const uint2 x1 = lds_tr(s_v + o + 16 * TVS);
-              const bf16x8_t vf = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-              hacc[cb] = mma16b(ahi, vf, hacc[cb]);
-              hacc[cb] = mma16b(alo, vf, hacc[cb]);
+            for (int hh = 0; hh < 2; ++hh) {
+              if (hh) {
+                read_v(NCH);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+#pragma unroll
+              for (int x = 0; x < NCH; ++x)
+                hacc[NCH * hh + x] = mma16b(
+                    ahi, as_bf16x8(make_uint4(vx[x][0].x, vx[x][0].y, vx[x][1].x, vx[x][1].y)), hacc[NCH * hh + x]);
+#pragma unroll
+              for (int x = 0; x < NCH; ++x)
+                hacc[NCH * hh + x] = mma16b(
+                    alo, as_bf16x8(make_uint4(vx[x][0].x, vx[x][0].y, vx[x][1].x, vx[x][1].y)), hacc[NCH * hh + x]);
             }
           };
           const int qblk = 4 * i + wa;
           if (2 * j + 1 < qblk) block(std::integral_constant<int, 2>{}, std::false_type{});
           else if (2 * j + 1 == qblk) block(std::integral_constant<int, 2>{}, std::true_type{});
           else if (2 * j == qblk) block(std::integral_constant<int, 1>{}, std::true_type{});
+          // n partial sums (exp gate) on the last query tile, which visits
+          // every key tile of the chunk: this thread's K pieces of the tile,
+          // weighted (piece tid + 256 e: row tid / 32 + 8 e, column group tid % 32)
+          if (!SIG && i == nsub - 1) {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+              const int row = tid / KG + e * (NA / KG);
+              const float w = __builtin_amdgcn_exp2f(g2 + s_gu[key0 + row] - Mn);
+              const uint4 kv = *reinterpret_cast<const uint4*>(s_k + kso[e]);
+              const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                np[2 * q] += w * __uint_as_float(kw[q] << 16);
+                np[2 * q + 1] += w * __uint_as_float(kw[q] & 0xffff0000u);
+              }
+            }
+          }
           // the next tile into the other buffers (last read before the previous barrier)
           stage(cur ^ 1);
           ++ks;
@@ -432,10 +487,14 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
               make_rsrc(static_cast<const char*>(p.H) + ((gbase + t0 + row0) * DV + v0) * E,
                         (uint32_t)(((Lc - row0 - 1) * DV + TVS) * E));
           const int hvoff = ((16 * wa + 4 * g4) * DV + l16) * E;
+          float4 xr[NCB];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            xr[cb] = *reinterpret_cast<const float4*>(s_xt + (16 * cb + l16) * LDX + 16 * wa + 4 * g4);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            const float4 x = *reinterpret_cast<const float4*>(s_xt + (16 * cb + l16) * LDX + 16 * wa + 4 * g4);
-            const float xv[4] = {x.x, x.y, x.z, x.w};
+            const float xv[4] = {xr[cb].x, xr[cb].y, xr[cb].z, xr[cb].w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float hv = (hacc[cb][r] + wv[r] * xv[r]) * iv[r];
@@ -450,6 +509,16 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         };
         if (p.h_bf16) store_h(std::integral_constant<int, 2>{});
         else store_h(std::integral_constant<int, 4>{});
+      }
+      // lanes l and l + 32 of a wave share a column group; the four waves'
+      // partial sums go to LDS for the state role
+      if constexpr (!SIG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) np[e] += __shfl_xor(np[e], 32, 64);
+        if (lane < KG) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s_np[wa * DK + lane * 8 + e] = np[e];
+        }
       }
       __syncthreads();  // [N] end of chunk
       M = Mn;
@@ -527,10 +596,6 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       __syncthreads();  // [G] gate terms
       float g2, Mn, dec;
       chunk_scalars(Lc, M, g2, Mn, dec);
-      float np[8];  // n partial sums of this thread's K column group (exp gate)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) np[e] = 0.0f;
-
       // query tile i; LAST: the chunk's last tile, which also updates the state
       auto sub_tile = [&](auto last_c, int i) {
         constexpr bool last = decltype(last_c)::value;
@@ -544,22 +609,37 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
           for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) hq[rb][r] = 0.0f;
+          // Q fragments in batches of four k steps, the next batch's reads in
+          // flight while the current batch is on the matrix cores
+          constexpr int QB = 4;
+          uint4 qa[2][QB][2];
+          auto load_qa = [&](int sb, uint4 (&dst)[QB][2]) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            uint4 a[2];
+            for (int x = 0; x < QB; ++x)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              a[rb] = *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + 16 * s + 8 * h);
-            const int q0 = 4 * (s & 1);
-            const bf16x8_t bhi = as_bf16x8(
-                make_uint4(chi[s >> 1][q0], chi[s >> 1][q0 + 1], chi[s >> 1][q0 + 2], chi[s >> 1][q0 + 3]));
-            const bf16x8_t blo = as_bf16x8(
-                make_uint4(clo[s >> 1][q0], clo[s >> 1][q0 + 1], clo[s >> 1][q0 + 2], clo[s >> 1][q0 + 3]));
+              for (int rb = 0; rb < 2; ++rb)
+                dst[x][rb] =
+                    *reinterpret_cast<const uint4*>(s_q + (32 * rb + l32) * LDQ + 16 * (QB * sb + x) + 8 * h);
+          };
+          load_qa(0, qa[0]);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              hq[rb] = mma32b(as_bf16x8(a[rb]), bhi, hq[rb]);
-              hq[rb] = mma32b(as_bf16x8(a[rb]), blo, hq[rb]);
+          for (int sb = 0; sb < NKS / QB; ++sb) {
+            if (sb + 1 < NKS / QB) load_qa(sb + 1, qa[(sb + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int x = 0; x < QB; ++x) {
+              const int s = QB * sb + x;
+              const int q0 = 4 * (s & 1);
+              const bf16x8_t bhi = as_bf16x8(
+                  make_uint4(chi[s >> 1][q0], chi[s >> 1][q0 + 1], chi[s >> 1][q0 + 2], chi[s >> 1][q0 + 3]));
+              const bf16x8_t blo = as_bf16x8(
+                  make_uint4(clo[s >> 1][q0], clo[s >> 1][q0 + 1], clo[s >> 1][q0 + 2], clo[s >> 1][q0 + 3]));
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) hq[rb] = mma32b(as_bf16x8(qa[sb & 1][x][rb]), bhi, hq[rb]);
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) hq[rb] = mma32b(as_bf16x8(qa[sb & 1][x][rb]), blo, hq[rb]);
             }
+            __builtin_amdgcn_sched_barrier(0);
           }
           // to LDS as [column][row]: column 32 b + lane % 32, rows 32 rb + 8 q + 4 h .. + 3
 #pragma unroll
@@ -606,9 +686,19 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
               const int vc = 32 * wb + 16 * (grp & 1) + 4 * (jl & 3);
               const uint2 v0r = lds_tr(s_v + swz<TVS>(16 * kk + kr0, vc));
               const uint2 v1r = lds_tr(s_v + swz<TVS>(16 * kk + kr0 + 4, vc));
-              const uint32_t vv[4] = {v0r.x, v0r.y, v1r.x, v1r.y};
               const float4 u0 = *reinterpret_cast<const float4*>(s_gu + key0 + 16 * kk + 8 * h);
               const float4 u1 = *reinterpret_cast<const float4*>(s_gu + key0 + 16 * kk + 8 * h + 4);
+              // all K^T reads of the step go out before the arithmetic and the MFMAs
+              uint4 akf[NKB];
+#pragma unroll
+              for (int kb = 0; kb < NKB; ++kb) {
+                const int o = 128 * (kb >> 2) + 16 * kk * DK;
+                const uint2 a0 = lds_tr(s_k + ktb[0][kb & 3] + o);
+                const uint2 a1 = lds_tr(s_k + ktb[1][kb & 3] + o);
+                akf[kb] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+              const uint32_t vv[4] = {v0r.x, v0r.y, v1r.x, v1r.y};
               const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
               float ww[8];
 #pragma unroll
@@ -622,30 +712,9 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
               const bf16x8_t bh_ = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
               const bf16x8_t bl_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
-              for (int kb = 0; kb < NKB; ++kb) {
-                const int o = 128 * (kb >> 2) + 16 * kk * DK;
-                const uint2 a0 = lds_tr(s_k + ktb[0][kb & 3] + o);
-                const uint2 a1 = lds_tr(s_k + ktb[1][kb & 3] + o);
-                const bf16x8_t ak = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-                cacc[kb] = mma32b(ak, bh_, cacc[kb]);
-                cacc[kb] = mma32b(ak, bl_, cacc[kb]);
-              }
-            }
-            // n partial sums (exp gate): this thread's K pieces of the tile,
-            // weighted (piece tb + 256 e: row tb / 32 + 8 e, column group tb % 32)
-            if constexpr (!SIG) {
+              for (int kb = 0; kb < NKB; ++kb) cacc[kb] = mma32b(as_bf16x8(akf[kb]), bh_, cacc[kb]);
 #pragma unroll
-              for (int e = 0; e < KPT; ++e) {
-                const int row = tb / KG + e * (NA / KG);
-                const float w = __builtin_amdgcn_exp2f(g2 + s_gu[key0 + row] - Mn);
-                const uint4 kv = *reinterpret_cast<const uint4*>(s_k + swz<DK>(row, (tb % KG) * 8));
-                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  np[2 * q] += w * __uint_as_float(kw[q] << 16);
-                  np[2 * q + 1] += w * __uint_as_float(kw[q] & 0xffff0000u);
-                }
-              }
+              for (int kb = 0; kb < NKB; ++kb) cacc[kb] = mma32b(as_bf16x8(akf[kb]), bl_, cacc[kb]);
             }
           }
           ++ks;
@@ -659,16 +728,8 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       for (int i = 0; i + 1 < nsub; ++i) sub_tile(std::false_type{}, i);
       sub_tile(std::true_type{}, nsub - 1);
 
-      // ---- normaliser after the chunk: n = decay n + sum_t w_t k_t; lanes
-      // l and l + 32 of a wave share a column group, then the four waves
-      if constexpr (!SIG) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) np[e] += __shfl_xor(np[e], 32, 64);
-        if (lane < KG) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s_np[wb * DK + lane * 8 + e] = np[e];
-        }
-      }
+      // ---- normaliser after the chunk: n = decay n + sum_t w_t k_t, the
+      // sums over the chunk's keys formed by the intra role
       __syncthreads();  // [N] end of chunk
       if constexpr (!SIG) {
         float sum = 0.0f;
