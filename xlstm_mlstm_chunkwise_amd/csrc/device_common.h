@@ -392,6 +392,13 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
+// The same with the non-temporal hint (aux 2), for data read once that should
+// not displace lines other workgroups re-read from L2.
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
 __device__ __forceinline__ float unpack_state_elem_bf16(const uint16_t* P, int k, int v, int DV) {
   const int kk = k >> 4, kr = k & 15, nb = v >> 5, col = v & 31;
   const int h = (kr & 7) >> 2;

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.Q) + (gbase + row0_) * DK,
                                                 (uint32_t)((Lc_ - row0_) * DK * 2));
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16(rq, tid * 16, i * W::NT * 16);
+    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16_nt(rq, tid * 16, i * W::NT * 16);
   };
 
   int tile = next_tile();

@@ -385,7 +385,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       const v2i32_t k2 = __builtin_amdgcn_raw_buffer_load_b64(rk, kvoff, trow * DK * 2, 0);
       kr[s] = make_uint2((uint32_t)k2.x, (uint32_t)k2.y);
     } else {
-      kr[s] = buf_load16(rk, kvoff, trow * DK * 2);
+      kr[s] = buf_load16_nt(rk, kvoff, trow * DK * 2);
     }
     ur[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, krs * 4, trow * 4, 0));
 #pragma unroll
