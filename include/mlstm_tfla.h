@@ -111,9 +111,11 @@ typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } ml
  *       chunk_size <= 512; otherwise MLSTM_E_UNSUPPORTED.  The stage-wise
  *       calls (mlstm_fw_states, mlstm_fw_hintra, mlstm_fw_unpack_states)
  *       reject this schedule.
- *   MLSTM_SCHED_AUTO: the library's choice; currently TWO_STAGE, which is
- *       the faster of the two on the 7B-shaped workloads.  Stage-wise calls
- *       run the two stages. */
+ *   MLSTM_SCHED_AUTO: the library's choice: FUSED where it covers the shape
+ *       and tile_lq and tile_lkv are 0 (it is the faster path on the
+ *       7B-shaped workloads, for both gates), TWO_STAGE otherwise.  The
+ *       workspace size still covers the two stages, and stage-wise calls run
+ *       them. */
 typedef enum { MLSTM_SCHED_AUTO = 0, MLSTM_SCHED_TWO_STAGE = 1, MLSTM_SCHED_FUSED = 2 } mlstm_schedule_t;
 
 typedef struct {
@@ -161,9 +163,11 @@ int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
  *   MLSTM_FAMILY_F64      MLSTM_PREC_F64: fp64 vector-unit kernels
  *   MLSTM_FAMILY_FUSED    the fused chunk walker (see mlstm_schedule_t):
  *                         bf16 operands, state carried in registers
- * The stage-wise calls run GENERIC, WIDE or F64 kernels (FUSED descriptors
- * aside, which they reject).  Returns the negated status code for an invalid
- * descriptor. */
+ * This is the family mlstm_chunkwise_fw runs.  The stage-wise calls run
+ * GENERIC, WIDE or F64 kernels: they reject a descriptor whose schedule is
+ * MLSTM_SCHED_FUSED, and run the two stages for an MLSTM_SCHED_AUTO
+ * descriptor that reports FUSED here.  Returns the negated status code for an
+ * invalid descriptor. */
 typedef enum {
   MLSTM_FAMILY_GENERIC = 0,
   MLSTM_FAMILY_WIDE = 1,

@@ -145,7 +145,9 @@ def test_entry_points_refuse_before_launch():
 
 
 def test_kernel_family_query():
-    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256)) == mt.MLSTM_FAMILY_WIDE
+    # the automatic schedule takes the fused walker where it covers the shape
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256)) == mt.MLSTM_FAMILY_FUSED
+    assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=256, schedule="two_stage")) == mt.MLSTM_FAMILY_WIDE
     assert mt.kernel_family(_desc(DHQK=128, DHV=256, chunk_size=128)) == mt.MLSTM_FAMILY_WIDE
     assert mt.kernel_family(_desc(DHQK=256, DHV=512, chunk_size=1024, tile_lq=128)) == mt.MLSTM_FAMILY_WIDE
     assert mt.kernel_family(_desc(DHQK=128, DHV=128, chunk_size=128)) == mt.MLSTM_FAMILY_GENERIC
@@ -156,10 +158,14 @@ def test_kernel_family_query():
 
 
 def test_schedule_field():
-    # the automatic schedule keeps the two-stage kernels; the fused walker
-    # runs when asked for on bf16, DHQK 256, DHV a multiple of 128, chunk <= 512
+    # the fused walker covers bf16, DHQK 256, DHV a multiple of 128, chunk <=
+    # 512; the automatic schedule takes it there unless tile sizes are given
     big = dict(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
-    assert mt.kernel_family(_desc(**big)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**big)) == mt.MLSTM_FAMILY_FUSED
+    assert mt.kernel_family(_desc(**big, tile_lq=64)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**big, tile_lkv=64)) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**dict(big, chunk_size=1024))) == mt.MLSTM_FAMILY_WIDE
+    assert mt.kernel_family(_desc(**dict(big, DHQK=128))) == mt.MLSTM_FAMILY_WIDE
     assert mt.kernel_family(_desc(**big, schedule="two_stage")) == mt.MLSTM_FAMILY_WIDE
     assert mt.kernel_family(_desc(**big, schedule="fused")) == mt.MLSTM_FAMILY_FUSED
     assert mt.kernel_family(_desc(**big, gate="sig", schedule="fused")) == mt.MLSTM_FAMILY_FUSED
@@ -172,7 +178,8 @@ def test_schedule_field():
     assert mt.validate(_desc(**big, schedule=3)) == 9
     assert mt.validate(_desc(**big, schedule=-1)) == 9
     # workspace: the fused schedule needs the gate terms only (12 or 8 bytes per
-    # position and head); auto keeps room for the two-stage kernels as well
+    # position and head); auto keeps room for the two-stage kernels as well,
+    # which the stage-wise calls run for an auto descriptor
     fused = _desc(**big, schedule="fused")
     assert mt.workspace_bytes(fused) == 64 * 8192 * 12
     assert mt.workspace_bytes(_desc(**big, gate="sig", schedule="fused")) == 64 * 8192 * 8

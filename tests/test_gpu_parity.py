@@ -46,6 +46,9 @@ def _to_dev(x, dtype):
 
 
 def _run_gpu(mt, w: Workload, x, **kw):
+    # the two-stage kernels unless a test names its schedule: the automatic
+    # schedule would send the shapes the fused walker covers to it
+    kw.setdefault("schedule", "two_stage")
     qd = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
     q, k, v = (_to_dev(x[n], qd) for n in ("q", "k", "v"))
     i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
@@ -228,8 +231,8 @@ def test_fused_bf16_h_and_empty_sequence(mt):
 
 @pytest.mark.parametrize("name", ["bf16_7b_s8192", "sig_7b_s8192"])
 def test_fused_schedule_full_size_sampled_heads(mt, name):
-    """The fused walker on the full 7B-shaped workloads (the default schedule
-    runs the two-stage kernels on them)."""
+    """The fused walker on the full 7B-shaped workloads (the path the
+    automatic schedule and bench.py take on them)."""
     w = WORKLOADS[name]
     x = make_inputs(w)
     gpu = _run_gpu(mt, w, x, schedule="fused")
@@ -239,6 +242,31 @@ def test_fused_schedule_full_size_sampled_heads(mt, name):
         g = [None if o is None else o[b, h] for o in gpu]
         worst = max(worst, _compare(w, g, ref, f"fused {name} head {(b, h)}"))
     print(f"\n[{name} fused] max|dH|={worst:.3g}", flush=True)
+
+
+def test_auto_schedule_runs_the_walker_and_stage_calls_still_work(mt):
+    # a shape the walker covers: the automatic schedule gives bit-identical
+    # results to the fused schedule
+    w = _small_workload(dict(B=1, NH=2, S=300, DHQK=256, DHV=256, chunk=128, init_state=True))
+    x = make_inputs(w)
+    fused = _run_gpu(mt, w, x, schedule="fused")
+    auto = _run_gpu(mt, w, x, schedule="auto")
+    for a, f in zip(auto, fused):
+        np.testing.assert_array_equal(a, f)
+    # and the stage-wise calls (automatic schedule) run the two stages on it
+    q, k, v = (_to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
+    C0, n0, m0 = (_to_dev(x[n], torch.float32) for n in ("C0", "n0", "m0"))
+    ws, C, n, m = mt.mlstm_fw_states(k, v, i_pre, f_pre, C0, n0, m0, chunk_size=w.chunk)
+    H = mt.mlstm_fw_hintra(q, k, v, i_pre, f_pre, ws, chunk_size=w.chunk)
+    torch.cuda.synchronize()
+    staged = [t.float().cpu().numpy().astype(np.float64) for t in (H, C, n, m)]
+    ref = [np.zeros_like(g) for g in staged]
+    for h in range(w.NH):
+        r = _oracle(w, x, (0, h))
+        for slot in range(4):
+            ref[slot][0, h] = r[slot]
+    _compare(w, staged, ref, "auto stage calls")
 
 
 FP32_FLOOR = pytest.mark.xfail(

@@ -62,9 +62,13 @@ int validate_desc(const mlstm_fw_desc_t* d) {
 }
 
 // Whether mlstm_chunkwise_fw runs the fused walker for a valid descriptor.
-// The automatic schedule keeps the two-stage kernels: on the 7B-shaped
-// workloads they are still the faster pair.
-bool use_fused(const mlstm_fw_desc_t* d) { return d->schedule == MLSTM_SCHED_FUSED; }
+// The automatic schedule takes it wherever it covers the shape and no tile
+// sizes of the two-stage kernels were asked for: on the 7B-shaped workloads
+// it is the faster path for both gates.
+bool use_fused(const mlstm_fw_desc_t* d) {
+  if (d->schedule == MLSTM_SCHED_FUSED) return true;
+  return d->schedule == MLSTM_SCHED_AUTO && d->tile_lq == 0 && d->tile_lkv == 0 && fused_supported(d);
+}
 
 struct WsLayout {
   size_t c_off, n_off, m_off, g_off, ml_off, total;

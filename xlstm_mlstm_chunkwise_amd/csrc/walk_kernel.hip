@@ -499,11 +499,14 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
             for (int r = 0; r < 4; ++r) {
               const float hv = (hacc[cb][r] + wv[r] * xv[r]) * iv[r];
               const int soff = (r * DV + 16 * cb) * E;
-              // non-temporal (aux 2): H is written once and never read here
+              // plain stores: a store instruction covers 64-byte pieces of
+              // H rows, which L2 merges into whole lines (with the streaming
+              // hint each piece went out on its own and the written bytes
+              // grew by half)
               if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 2);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 0);
               else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 2);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 0);
             }
           }
         };
