@@ -176,6 +176,9 @@ def main(argv=None) -> int:
                     help="kernels of the forward pass (see mlstm_schedule_t)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the recurrent step (one token per head and call) on the workload's heads "
+                         "instead of the forward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times (the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -208,6 +211,8 @@ def main(argv=None) -> int:
         return 0
     mt.lib()  # fail loudly if the HIP library is missing
     w = WORKLOADS[args.workload]
+    if args.decode:
+        return bench_decode(args, w, mt, torch, np)
     if args.tile_lq is not None:
         w = w.replace(tile_lq=args.tile_lq)
     dev = torch.device("cuda", 0)
@@ -337,6 +342,90 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_decode(args, w, mt, torch, np) -> int:
+    """The recurrent step on the workload's heads (B, NH, DHQK, DHV, dtype,
+    gate): one token for each of the B sequences per call, the float32 state
+    updated in place.  Warm: calls back to back, so the 33.5 MB state of the
+    7B-shaped heads can stay in the 256 MB Infinity Cache between calls.
+    Cold: a 512 MiB buffer is overwritten before every timed call, so the
+    state comes from HBM; events bracket each call alone.  The cold time is
+    the headline."""
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(2024)
+    B, NH, DK, DV = w.B, w.NH, w.DHQK, w.DHV
+    sig = w.gate == "sig"
+    qd = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+
+    def up(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+
+    q = up(rng.standard_normal((B, NH, DK)), qd)
+    k = up(rng.standard_normal((B, NH, DK)), qd)
+    v = up(rng.standard_normal((B, NH, DV)), qd)
+    i_pre = up(rng.standard_normal((B, NH)), torch.float32)
+    f_pre = up(2.0 + 4.0 * rng.random((B, NH)), torch.float32)
+    C = up(0.1 * rng.standard_normal((B, NH, DK, DV)), torch.float32)
+    ns = [None, None] if sig else [up(rng.random((B, NH, DK)), torch.float32), torch.empty(B, NH, DK, device=dev)]
+    ms = [None, None] if sig else [up(rng.standard_normal((B, NH)), torch.float32), torch.empty(B, NH, device=dev)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def call():
+        a, b = it[0] & 1, (it[0] + 1) & 1
+        mt.mlstm_recurrent_step(q, k, v, i_pre, f_pre, C, ns[a], ms[a], gate=w.gate, C_out=C, n_out=ns[b],
+                                m_out=ms[b])
+        it[0] += 1
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+    cold = []
+    for _ in range(args.steps):
+        flush.fill_(it[0] & 0xff)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    cold_ms = float(np.median(cold))
+    el = 2 if w.qkv_dtype == "bf16" else 4
+    BH = B * NH
+    abytes = (2 * BH * DK * DV * 4 + (0 if sig else 2 * BH * (DK + 1) * 4) + BH * (2 * DK + DV) * el
+              + BH * DV * 4 + 2 * BH * 4)
+    ach = abytes / (cold_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"mLSTM recurrent step (decode) tokens/s, {w.gate} gate, heads of {w.name}",
+        "value": B / (cold_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": cold_ms,
+        "warm_ms_per_step": warm_ms,
+        "warm_tokens_per_s": B / (warm_ms * 1e-3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"f32-state/{w.qkv_dtype}-qkv",
+        "data": "synthetic",
+        "config": {"workload": f"decode_{w.name}", "B": B, "NH": NH, "DHQK": DK, "DHV": DV, "gate": w.gate,
+                   "qkv_dtype": w.qkv_dtype, "state": "float32, updated in place"},
+        "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes": abytes,
+                     "traffic_source": "not profiled"},
+    }
     print(json.dumps(out), flush=True)
     return 0
 

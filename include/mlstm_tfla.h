@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 3
+#define MLSTM_ABI_VERSION 4
 
 typedef enum {
   MLSTM_OK = 0,
@@ -253,6 +253,36 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc,
                            const void* workspace, size_t workspace_bytes,
                            float* C_states, float* n_states, float* m_states,
                            void* stream);
+
+/* One time step of the recurrence above for every head, the decode step
+ * (the "xLSTM: the NX-AI repository behind the extended LSTM architecture"
+ * page, section "Exponential gating, matrix memory, and why the kernels
+ * decide everything", lists a step kernel beside the chunkwise and sequence
+ * kernels).  `desc` describes a one-token forward pass: S must be 1 (else
+ * MLSTM_E_SHAPE); B, NH, DHQK, DHV, qkv_dtype, h_dtype, gate, qk_scale and
+ * eps are used, the other fields only validated.
+ *   q, k      (B, NH, DHQK)       qkv_dtype, 16-byte aligned
+ *   v         (B, NH, DHV)        qkv_dtype, 16-byte aligned
+ *   i_pre, f_pre (B, NH)          float32
+ *   C_in, n_in, m_in  the state entering the step, in the stabilised
+ *             convention of C_out / n_out / m_out of mlstm_chunkwise_fw (so a
+ *             forward pass's final state continues here); NULL = zero state.
+ *             C_in (B, NH, DHQK, DHV) float32, 16-byte aligned.
+ *   h         (B, NH, DHV)        h_dtype, 16-byte aligned, required
+ *   C_out     (B, NH, DHQK, DHV) float32, 16-byte aligned, required; it may
+ *             be the same buffer as C_in (updated in place).
+ *   n_out, m_out  may be NULL (not written); they must not be the same
+ *             buffers as n_in, m_in (MLSTM_E_ARG): every workgroup of a head
+ *             reads n_in and m_in while one of them writes the new values.
+ * For the sig gate n_in, m_in, n_out and m_out must be NULL.  The call is
+ * bound by memory: it reads and writes the float32 state once. */
+int mlstm_recurrent_step(const mlstm_fw_desc_t* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* i_pre, const float* f_pre,
+                         const float* C_in, const float* n_in, const float* m_in,
+                         void* h,
+                         float* C_out, float* n_out, float* m_out,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 3
+    assert mt.abi_version() == 4
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -192,6 +192,30 @@ def test_schedule_field():
     assert lib.mlstm_fw_states(ctypes.byref(fused), *([4096] * 7), 1 << 20, wsb, None, None, None, None) == 5
     assert lib.mlstm_fw_hintra(ctypes.byref(fused), *([4096] * 5), 1 << 20, wsb, 4096, None, None, None) == 5
     assert lib.mlstm_fw_unpack_states(ctypes.byref(fused), 1 << 20, wsb, 4096, None, None, None) == 5
+
+
+def test_recurrent_step_refuses_before_launch():
+    lib = mt.lib()
+    d1 = _desc(S=1, DHQK=256, DHV=512, chunk_size=64)
+
+    def step(desc, **ptrs):
+        names = ["q", "k", "v", "i", "f", "C_in", "n_in", "m_in", "h", "C_out", "n_out", "m_out"]
+        vals = [ptrs.get(n, 4096 * (j + 1)) for j, n in enumerate(names)]
+        return lib.mlstm_recurrent_step(ctypes.byref(desc) if desc is not None else None, *vals, None)
+
+    assert step(None) == 1
+    assert step(_desc(S=2, chunk_size=64)) == 2          # one token per call
+    assert step(_desc(S=1, DHQK=100, chunk_size=64)) == 2
+    assert step(d1, C_out=None) == 1
+    assert step(d1, h=None) == 1
+    assert step(d1, q=None) == 1
+    assert step(d1, C_in=4096 + 8) == 8                   # the state is read in 16-byte pieces
+    assert step(d1, h=4096 * 9 + 4) == 8
+    assert step(d1, n_out=4096 * 7) == 9                  # n_out may not be n_in
+    assert step(d1, m_out=4096 * 8) == 9                  # m_out may not be m_in
+    ds = _desc(S=1, DHQK=256, DHV=512, chunk_size=64, gate="sig")
+    assert step(ds, n_in=4096, m_in=None, n_out=None, m_out=None) == 5
+    assert step(ds, n_in=None, m_in=None, n_out=4096, m_out=None) == 5
 
 
 def test_flops_formula():

@@ -66,6 +66,7 @@ _SYMBOLS = {
                         + [ctypes.c_size_t] + [ctypes.c_void_p] * 4),
     "mlstm_fw_unpack_states": (ctypes.c_int, [ctypes.POINTER(FwDesc), ctypes.c_void_p, ctypes.c_size_t]
                                + [ctypes.c_void_p] * 4),
+    "mlstm_recurrent_step": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
 }
 
 
@@ -339,3 +340,52 @@ def flops(B, NH, S, DHQK, DHV, chunk_size) -> float:
     """Algorithmic matrix-core FLOPs of one forward pass, causal lower triangle
     only: per token 4*DHQK*DHV (Q.C and K^T.V) + (L+1)*(DHQK+DHV) (Q.K^T and P.V)."""
     return float(B) * NH * S * (4.0 * DHQK * DHV + (chunk_size + 1) * (DHQK + DHV))
+
+
+def mlstm_recurrent_step(q, k, v, i_pre, f_pre, C=None, n=None, m=None, *, gate: str = "exp", h_dtype=None,
+                         qk_scale: Optional[float] = None, eps: float = 0.0, C_out=None, n_out=None,
+                         m_out=None):
+    """One time step of the recurrence for every head (decode) on the GPU.
+
+    q, k: (B, NH, DHQK); v: (B, NH, DHV), bfloat16 or float32; i_pre, f_pre:
+    (B, NH) float32; C (B, NH, DHQK, DHV), n (B, NH, DHQK), m (B, NH) float32
+    or None (zero state): the state entering the step, as returned by
+    mlstm_chunkwise_fw.  Returns (h, C', n', m'); n' and m' are None for
+    gate="sig".  C_out may be C itself (updated in place); n_out / m_out, when
+    given, must be other buffers than n / m.
+    """
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be (B, NH, DHQK)")
+    B, NH, DK = q.shape
+    DV = v.shape[-1]
+    _check(q, "q", (B, NH, DK))
+    _check(k, "k", (B, NH, DK), q.dtype)
+    _check(v, "v", (B, NH, DV), q.dtype)
+    _check(i_pre, "i_pre", (B, NH), torch.float32)
+    _check(f_pre, "f_pre", (B, NH), torch.float32)
+    _check(C, "C", (B, NH, DK, DV), torch.float32)
+    _check(n, "n", (B, NH, DK), torch.float32)
+    _check(m, "m", (B, NH), torch.float32)
+    h_dtype = torch.float32 if h_dtype is None else h_dtype
+    hcode = MLSTM_BF16 if h_dtype == torch.bfloat16 else MLSTM_F32
+    desc = make_desc(B, NH, 1, DK, DV, 64, qkv_dtype=_dtype_code(q), h_dtype=hcode, gate=gate,
+                     qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps))
+    dev = q.device
+    h = torch.empty((B, NH, DV), dtype=h_dtype, device=dev)
+    if C_out is None:
+        C_out = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=dev)
+    _check(C_out, "C_out", (B, NH, DK, DV), torch.float32)
+    if gate != "sig":
+        if n_out is None:
+            n_out = torch.empty((B, NH, DK), dtype=torch.float32, device=dev)
+        if m_out is None:
+            m_out = torch.empty((B, NH), dtype=torch.float32, device=dev)
+    _check(n_out, "n_out", (B, NH, DK), torch.float32)
+    _check(m_out, "m_out", (B, NH), torch.float32)
+    st = lib().mlstm_recurrent_step(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C), _ptr(n), _ptr(m),
+        _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_recurrent_step")
+    return h, C_out, n_out, m_out

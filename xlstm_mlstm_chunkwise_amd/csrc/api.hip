@@ -414,4 +414,43 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);
 }
 
+int mlstm_recurrent_step(const mlstm_fw_desc_t* desc, const void* q, const void* k, const void* v,
+                         const float* i_pre, const float* f_pre, const float* C_in, const float* n_in,
+                         const float* m_in, void* h, float* C_out, float* n_out, float* m_out, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S != 1) return MLSTM_E_SHAPE;
+  if (!q || !k || !v || !i_pre || !f_pre || !h || !C_out) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n_in, m_in, n_out, m_out)) != MLSTM_OK) return st;
+  // every workgroup of a head reads n_in / m_in while one of them writes the
+  // new values: in-place update is allowed for C only
+  if ((n_out && n_out == n_in) || (m_out && m_out == m_in)) return MLSTM_E_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(h, 16) || !aligned(C_out, 16) ||
+      (C_in && !aligned(C_in, 16)))
+    return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, n_in, m_in, n_out, m_out})) != MLSTM_OK) return st;
+  mlstm::StepParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.C_in = C_in;
+  p.n_in = n_in;
+  p.m_in = m_in;
+  p.h = h;
+  p.C_out = C_out;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  p.scale = resolve_scale(desc);
+  p.eps = desc->eps;
+  p.BH = desc->B * desc->NH;
+  p.DK = desc->DHQK;
+  p.DV = desc->DHV;
+  p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
+  p.h_bf16 = desc->h_dtype == MLSTM_BF16;
+  const hipError_t e = mlstm::launch_step(p, desc->gate == MLSTM_GATE_SIG, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
 }  // extern "C"

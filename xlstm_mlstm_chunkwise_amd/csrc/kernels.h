@@ -84,12 +84,33 @@ struct WalkParams {
   int h_bf16;
 };
 
+// One time step of the recurrence for every head (decode).
+struct StepParams {
+  const void* q;  // (BH, DK), bf16 or float32
+  const void* k;
+  const void* v;  // (BH, DV)
+  const float* i_pre;  // (BH)
+  const float* f_pre;
+  const float* C_in;  // (BH, DK, DV) float32, may be null (zero state); may equal C_out
+  const float* n_in;  // (BH, DK), may be null
+  const float* m_in;  // (BH), may be null
+  void* h;            // (BH, DV), bf16 or float32
+  float* C_out;       // required
+  float* n_out;       // may be null; must not alias n_in
+  float* m_out;       // may be null; must not alias m_in
+  float scale;
+  float eps;
+  int BH, DK, DV;
+  int qkv_bf16, h_bf16;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gates(const GatesParams& p, bool sig, hipStream_t stream);
 bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split);
 // Workgroups the walker launches for a shape (heads x column slices).
 long long walk_workgroups(int BH, int DV);
 hipError_t launch_walk(const WalkParams& p, bool sig, hipStream_t stream);
+hipError_t launch_step(const StepParams& p, bool sig, hipStream_t stream);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 

@@ -1,0 +1,167 @@
+// One time step of the mLSTM recurrence for every head (decode), gfx950.
+//
+// The model configuration of "xLSTM: the NX-AI repository behind the extended
+// LSTM architecture" (section "Exponential gating, matrix memory, and why the
+// kernels decide everything") names a step kernel beside the chunkwise and
+// sequence kernels: generation advances the matrix memory one token at a
+// time.  Per head, from the state (C, n, m) entering the step, in the
+// stabilised convention of the forward pass's final state, and the step's
+// q, k, v and gate pre-activations, with lf = log sigmoid(f) and s the query
+// scale:
+//   exp gate:  m' = max(lf + m, i),  a = e^{lf + m - m'},  b = e^{i - m'}
+//              C' = a C + b k v^T,   n' = a n + b k
+//              h  = s C'^T q / (max(|s n' . q|, e^{-m'}) + eps)
+//   sig gate:  C' = sigmoid(f) C + sigmoid(i) k v^T,   h = s C'^T q
+//
+// The step reads and writes the DHQK x DHV float32 state once and does two
+// flops per element besides, so it is bound by memory.  One workgroup (256
+// threads) per (head, 64-column slice of C): thread (row group g, column
+// quad c) streams the 16-byte pieces of rows g, g + 16, ... of its four
+// columns, applies the update, writes them back and accumulates s C'^T q; a
+// reduction over the 16 row groups in LDS gives h.  Every workgroup of a head
+// forms n' and m', which its normaliser needs; the first slice writes them.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mlstm {
+namespace {
+
+constexpr int kStepCols = 64;                    // columns of C per workgroup
+constexpr int kStepThreads = 256;
+constexpr int kStepGroups = kStepThreads / (kStepCols / 4);  // row groups (16)
+
+template <int DK, bool SIG>
+__global__ __launch_bounds__(kStepThreads) void step_kernel(const StepParams p) {
+  constexpr int RPT = DK / kStepGroups;  // rows per thread
+  __shared__ float s_q[DK], s_k[DK];
+  __shared__ float4 s_red[kStepGroups][kStepCols / 4];
+  __shared__ float s_dot[kStepThreads / 64];
+
+  const int DV = p.DV;
+  const int NS = DV / kStepCols;
+  const int bh = blockIdx.x / NS, slice = blockIdx.x % NS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cq = tid % (kStepCols / 4), rg = tid / (kStepCols / 4);
+  const int col = slice * kStepCols + 4 * cq;
+
+  // gate factors of the step (every thread, from two scalars)
+  const float lf = log_sigmoid(p.f_pre[bh]);
+  const float ip = p.i_pre[bh];
+  float a, b, m_new = 0.0f;
+  if constexpr (SIG) {
+    a = expf(lf);
+    b = 1.0f / (1.0f + expf(-ip));
+  } else {
+    const float m_old = p.m_in ? p.m_in[bh] : 0.0f;
+    m_new = fmaxf(lf + m_old, ip);
+    a = expf(lf + m_old - m_new);
+    b = expf(ip - m_new);
+  }
+
+  // q (scaled) and k in LDS as float32; this thread's four values of v
+  auto ld = [&](const void* x, size_t i) -> float {
+    return p.qkv_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
+  };
+  for (int i = tid; i < DK; i += kStepThreads) {
+    s_q[i] = p.scale * ld(p.q, (size_t)bh * DK + i);
+    s_k[i] = ld(p.k, (size_t)bh * DK + i);
+  }
+  float4 v4;
+  if (p.qkv_bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + (size_t)bh * DV + col);
+    v4 = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    v4 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + (size_t)bh * DV + col);
+  }
+  __syncthreads();
+
+  // ---- stream the state: C' = a C + b k v^T, and s C'^T q for four columns
+  const size_t cbase = (size_t)bh * DK * DV + col;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+  for (int r = 0; r < RPT; ++r) {
+    const int row = rg + kStepGroups * r;
+    float4 c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p.C_in) c = *reinterpret_cast<const float4*>(p.C_in + cbase + (size_t)row * DV);
+    const float bk = b * s_k[row], qv = s_q[row];
+    c.x = a * c.x + bk * v4.x;
+    c.y = a * c.y + bk * v4.y;
+    c.z = a * c.z + bk * v4.z;
+    c.w = a * c.w + bk * v4.w;
+    *reinterpret_cast<float4*>(p.C_out + cbase + (size_t)row * DV) = c;
+    acc.x += c.x * qv;
+    acc.y += c.y * qv;
+    acc.z += c.z * qv;
+    acc.w += c.w * qv;
+  }
+  s_red[rg][cq] = acc;
+
+  // ---- normaliser s n' . q (exp gate), n' written by the first slice
+  float den = 0.0f;
+  if constexpr (!SIG) {
+    float d = 0.0f;
+    for (int i = tid; i < DK; i += kStepThreads) {
+      const float n_new = a * (p.n_in ? p.n_in[(size_t)bh * DK + i] : 0.0f) + b * s_k[i];
+      if (slice == 0 && p.n_out) p.n_out[(size_t)bh * DK + i] = n_new;
+      d += n_new * s_q[i];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+    if (lane == 0) s_dot[wave] = d;
+  }
+  __syncthreads();
+  if constexpr (!SIG) {
+#pragma unroll
+    for (int w = 0; w < kStepThreads / 64; ++w) den += s_dot[w];
+    if (slice == 0 && tid == 0 && p.m_out) p.m_out[bh] = m_new;
+  }
+
+  // ---- h for this slice's columns
+  if (rg == 0) {
+    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int g = 0; g < kStepGroups; ++g) {
+      const float4 x = s_red[g][cq];
+      num.x += x.x;
+      num.y += x.y;
+      num.z += x.z;
+      num.w += x.w;
+    }
+    float inv = 1.0f;
+    if constexpr (!SIG) inv = 1.0f / (fmaxf(fabsf(den), expf(-m_new)) + p.eps);
+    const float hv[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
+    if (p.h_bf16) {
+      uint16_t* H = static_cast<uint16_t*>(p.h) + (size_t)bh * DV + col;
+      const uint2 u = make_uint2((uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16),
+                                 (uint32_t)f32_to_bf16(hv[2]) | ((uint32_t)f32_to_bf16(hv[3]) << 16));
+      *reinterpret_cast<uint2*>(H) = u;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.h) + (size_t)bh * DV + col) =
+          make_float4(hv[0], hv[1], hv[2], hv[3]);
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(const StepParams& p, bool sig, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.BH * (p.DV / kStepCols)));
+  if (sig) hipLaunchKernelGGL((step_kernel<DK, true>), grid, dim3(kStepThreads), 0, stream, p);
+  else hipLaunchKernelGGL((step_kernel<DK, false>), grid, dim3(kStepThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepParams& p, bool sig, hipStream_t stream) {
+  if (p.BH == 0) return hipSuccess;
+  switch (p.DK) {
+    case 64: return launch_dk<64>(p, sig, stream);
+    case 128: return launch_dk<128>(p, sig, stream);
+    case 256: return launch_dk<256>(p, sig, stream);
+    case 512: return launch_dk<512>(p, sig, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mlstm
