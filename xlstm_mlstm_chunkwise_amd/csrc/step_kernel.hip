@@ -17,8 +17,9 @@
 // flops per element besides, so it is bound by memory.  One workgroup (256
 // threads) per (head, 64-column slice of C): thread (row group g, column
 // quad c) streams the 16-byte pieces of rows g, g + 16, ... of its four
-// columns, applies the update, writes them back and accumulates s C'^T q; a
-// reduction over the 16 row groups in LDS gives h.  Every workgroup of a head
+// columns (all its loads issued up front), applies the update, writes them
+// back and accumulates s C'^T q; a reduction over the 16 row groups in LDS
+// gives h.  Every workgroup of a head
 // forms n' and m', which its normaliser needs; the first slice writes them.
 #include "device_common.h"
 #include "kernels.h"
@@ -58,6 +59,15 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepParams p) 
     b = expf(ip - m_new);
   }
 
+  // this thread's pieces of the state go out first: they depend on nothing
+  // else, and their latency then overlaps the staging of q and k
+  const size_t cbase = (size_t)bh * DK * DV + col;
+  float4 cr[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+    cr[r] = p.C_in ? *reinterpret_cast<const float4*>(p.C_in + cbase + (size_t)(rg + kStepGroups * r) * DV)
+                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
   // q (scaled) and k in LDS as float32; this thread's four values of v
   auto ld = [&](const void* x, size_t i) -> float {
     return p.qkv_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
@@ -76,14 +86,12 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepParams p) 
   }
   __syncthreads();
 
-  // ---- stream the state: C' = a C + b k v^T, and s C'^T q for four columns
-  const size_t cbase = (size_t)bh * DK * DV + col;
+  // ---- the state update C' = a C + b k v^T, and s C'^T q for four columns
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 8
+#pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int row = rg + kStepGroups * r;
-    float4 c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (p.C_in) c = *reinterpret_cast<const float4*>(p.C_in + cbase + (size_t)row * DV);
+    float4 c = cr[r];
     const float bk = b * s_k[row], qv = s_q[row];
     c.x = a * c.x + bk * v4.x;
     c.y = a * c.y + bk * v4.y;
