@@ -72,10 +72,10 @@ def chunk_state_bytes(w) -> int:
     return w.BH * (nc + 1) * per_state
 
 
-def recorded_traffic(workload: str, kernel: str, tile_lq) -> tuple:
+def recorded_traffic(workload: str, kernel: str, tile_lq, fname: str = None) -> tuple:
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else (None, reason)."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    path = os.path.join(PROFILES, fname or f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None, "no counter summary"
     rec = {}
@@ -83,7 +83,8 @@ def recorded_traffic(workload: str, kernel: str, tile_lq) -> tuple:
         m = re.match(r"\s*traffic-record:\s*(.*)", line)
         if m:
             kv = dict(x.split("=", 1) for x in m.group(1).split())
-            if kv.get("kernel") == kernel and kv.get("tile_lq", "default") == str(tile_lq or "default"):
+            if kv.get("kernel") == kernel and kv.get("tile_lq", "default") == str(tile_lq or "default") \
+                    and kv.get("workload", workload) == workload:
                 rec = kv
     if not rec:
         return None, "kernel not in counter summary"
@@ -348,17 +349,22 @@ def main(argv=None) -> int:
 
 def bench_decode(args, w, mt, torch, np) -> int:
     """The recurrent step on the workload's heads (B, NH, DHQK, DHV, dtype,
-    gate): one token for each of the B sequences per call, the float32 state
-    updated in place.  Warm: calls back to back, so the 33.5 MB state of the
-    7B-shaped heads can stay in the 256 MB Infinity Cache between calls.
-    Cold: a 512 MiB buffer is read (summed) before every timed call, so the
-    state comes from HBM and the caches hold no dirty lines to write back;
-    events bracket each call alone.  The cold time is the headline."""
+    gate): one token for each of the B sequences per call, each state updated
+    in place, calls issued back to back through the C entry point with their
+    arguments built once (so the host issues faster than the device runs).
+    Cold (the headline): the calls cycle through 16 separate states, 540 MB at
+    the 7B-shaped heads, more than the 256 MB Infinity Cache, so each call
+    reads and writes its state in HBM -- one token through 16 layers.  Warm:
+    one state, which can stay in the Infinity Cache between calls.  Isolated:
+    one call after a 512 MiB read, bracketed by events alone (includes the
+    dispatch latency of a lone kernel)."""
+    import ctypes
     dev = torch.device("cuda", 0)
     rng = np.random.default_rng(2024)
     B, NH, DK, DV = w.B, w.NH, w.DHQK, w.DHV
     sig = w.gate == "sig"
     qd = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    NSTATE = 16
 
     def up(a, dt):
         return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
@@ -368,43 +374,61 @@ def bench_decode(args, w, mt, torch, np) -> int:
     v = up(rng.standard_normal((B, NH, DV)), qd)
     i_pre = up(rng.standard_normal((B, NH)), torch.float32)
     f_pre = up(2.0 + 4.0 * rng.random((B, NH)), torch.float32)
-    C = up(0.1 * rng.standard_normal((B, NH, DK, DV)), torch.float32)
-    ns = [None, None] if sig else [up(rng.random((B, NH, DK)), torch.float32), torch.empty(B, NH, DK, device=dev)]
-    ms = [None, None] if sig else [up(rng.standard_normal((B, NH)), torch.float32), torch.empty(B, NH, device=dev)]
+    C0 = up(0.1 * rng.standard_normal((B, NH, DK, DV)), torch.float32)
+    Cs = [C0.clone() for _ in range(NSTATE)]
+    # n and m alternate between two buffers per state (outputs may not alias inputs)
+    ns = [[None, None] if sig else [up(rng.random((B, NH, DK)), torch.float32), torch.empty(B, NH, DK, device=dev)]
+          for _ in range(NSTATE)]
+    ms = [[None, None] if sig else [up(rng.standard_normal((B, NH)), torch.float32), torch.empty(B, NH, device=dev)]
+          for _ in range(NSTATE)]
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    it = [0]
-
-    def call():
-        a, b = it[0] & 1, (it[0] + 1) & 1
-        mt.mlstm_recurrent_step(q, k, v, i_pre, f_pre, C, ns[a], ms[a], gate=w.gate, C_out=C, n_out=ns[b],
-                                m_out=ms[b])
-        it[0] += 1
-
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    h = torch.empty(B, NH, DV, dtype=torch.float32, device=dev)
+    desc = mt.make_desc(B, NH, 1, DK, DV, 64, qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
+                        gate=w.gate)
+    fn = mt.lib().mlstm_recurrent_step
+    P = lambda t: None if t is None else t.data_ptr()
     stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cargs = [[[ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(Cs[j]), P(ns[j][a]), P(ms[j][a]), P(h),
+               P(Cs[j]), P(ns[j][1 - a]), P(ms[j][1 - a]), sp] for a in (0, 1)] for j in range(NSTATE)]
+    it = [0] * NSTATE
+
+    def call(j):
+        st = fn(*cargs[j][it[j] & 1])
+        if st:
+            raise mt.MlstmError(st, "mlstm_recurrent_step")
+        it[j] += 1
+
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = e0.elapsed_time(e1) / args.steps
-    cold = []
+
+    def timed(states):
+        for r in range(args.warmup):
+            call(states[r % len(states)])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for r in range(args.steps):
+            call(states[r % len(states)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    cold_ms = timed(list(range(NSTATE)))
+    warm_ms = timed([0])
+    iso = []
     for _ in range(args.steps):
         flush.sum()
         e0.record(stream)
-        call()
+        call(0)
         e1.record(stream)
         torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    cold_ms = float(np.median(cold))
+        iso.append(e0.elapsed_time(e1))
+    iso_ms = float(np.median(iso))
     el = 2 if w.qkv_dtype == "bf16" else 4
     BH = B * NH
     abytes = (2 * BH * DK * DV * 4 + (0 if sig else 2 * BH * (DK + 1) * 4) + BH * (2 * DK + DV) * el
               + BH * DV * 4 + 2 * BH * 4)
     ach = abytes / (cold_ms * 1e-3) / 1e9
+    traffic, traffic_src = recorded_traffic(f"decode_{w.name}", "step", None, "traffic_decode_7b.md")
     out = {
         "metric": f"mLSTM recurrent step (decode) tokens/s, {w.gate} gate, heads of {w.name}",
         "value": B / (cold_ms * 1e-3),
@@ -415,16 +439,18 @@ def bench_decode(args, w, mt, torch, np) -> int:
         "ms_per_step": cold_ms,
         "warm_ms_per_step": warm_ms,
         "warm_tokens_per_s": B / (warm_ms * 1e-3),
+        "isolated_ms_per_step": iso_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": f"f32-state/{w.qkv_dtype}-qkv",
         "data": "synthetic",
         "config": {"workload": f"decode_{w.name}", "B": B, "NH": NH, "DHQK": DK, "DHV": DV, "gate": w.gate,
-                   "qkv_dtype": w.qkv_dtype, "state": "float32, updated in place"},
+                   "qkv_dtype": w.qkv_dtype, "state": "float32, updated in place",
+                   "states_cycled": NSTATE},
         "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": ach / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes": abytes,
-                     "traffic_source": "not profiled"},
+                     "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes": abytes,
+                     "traffic_source": traffic_src},
     }
     print(json.dumps(out), flush=True)
     return 0
