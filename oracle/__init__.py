@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for the mLSTM forward pass.
+"""Float64 CPU oracle for the mLSTM forward pass and its gradients.
 
 Test infrastructure only: the tests, the package smoke check and the
 benchmark's CPU-baseline leg are the only callers.  The GPU library never
@@ -12,3 +12,4 @@ from .mlstm_oracle import (  # noqa: F401
     quadratic_fw,
     chunkwise_fw,
 )
+from .mlstm_grad import grad_fw, quadratic_fw_torch  # noqa: F401,E402
