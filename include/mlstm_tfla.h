@@ -1,5 +1,6 @@
 /*
- * mlstm_tfla.h - C ABI of the MI355X (gfx950) chunkwise mLSTM forward pass.
+ * mlstm_tfla.h - C ABI of the MI355X (gfx950) chunkwise mLSTM forward pass,
+ * its backward pass and the recurrent (decode) step.
  *
  * What is computed.  The forward pass of the mLSTM cell (matrix memory C
  * updated by an outer product, exponential input gate, normaliser n and
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 4
+#define MLSTM_ABI_VERSION 5
 
 typedef enum {
   MLSTM_OK = 0,
@@ -283,6 +284,53 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc,
                          void* h,
                          float* C_out, float* n_out, float* m_out,
                          void* stream);
+
+/* Bytes of device workspace that mlstm_chunkwise_bw needs for `desc`: the
+ * two-stage forward workspace, the recomputed forward quantities (chunk
+ * states as float32, and for the exp gate H in float32 plus the per-row m and
+ * normaliser), per-position gate terms, and the state gradient after every
+ * chunk (N_c states of DHQK x DHV float32 values per head, plus DHQK values
+ * for the exp gate).  Returns 0 for an invalid descriptor. */
+size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc);
+
+/* Backward pass: the gradients of sum(dH * H) with respect to the inputs of
+ * mlstm_chunkwise_fw, for the same descriptor and inputs.  The pages print no
+ * backward pass; this is the derivative of the forward pass above (the
+ * "xLSTM: the NX-AI repository behind the extended LSTM architecture" page,
+ * section "Exponential gating, matrix memory, and why the kernels decide
+ * everything"), organised in chunks as the "Tiled Flash Linear Attention:
+ * More Efficient Linear RNN and xLSTM Kernels" abstract describes for
+ * training.  The max-state m is held constant: with eps = 0, H does not
+ * depend on m and the gradient is exact; with eps > 0 it is the gradient at
+ * fixed m.
+ *   Q, K, V, i_pre, f_pre, C0, n0, m0   as for mlstm_chunkwise_fw.
+ *   dH        (B, NH, S, DHV)  h_dtype, 16-byte aligned: the incoming gradient.
+ *   dQ, dK    (B, NH, S, DHQK) float32, 16-byte aligned, required.
+ *   dV        (B, NH, S, DHV)  float32, 16-byte aligned, required.
+ *   d_i, d_f  (B, NH, S)       float32, required: gradients of i_pre, f_pre.
+ *   dC0       (B, NH, DHQK, DHV) float32, may be NULL: gradient of C0 (of
+ *             the zero state when C0 is NULL), in C0's stabilised convention.
+ *   dn0       (B, NH, DHQK)    float32, may be NULL (exp gate only).
+ *   dm0       (B, NH)          float32, may be NULL (exp gate only).
+ *   workspace device buffer of at least mlstm_bw_workspace_bytes(desc) bytes,
+ *             256-byte aligned; its contents on return belong to the library.
+ * The forward quantities the gradient needs are recomputed with the two-stage
+ * kernels whatever desc->schedule says (the fused walker forms neither chunk
+ * states nor per-row normalisers); desc->precision applies to that
+ * recomputation.  The gradient kernels compute in float32 on fp32 matrix
+ * cores.  No gradient flows in through the final state.  For the sig gate n0,
+ * m0, dn0 and dm0 must be NULL.  Outputs must not alias inputs.  With S == 0
+ * only dC0, dn0 and dm0 are written (zeros). */
+int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,
+                       const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre,
+                       const float* C0, const float* n0, const float* m0,
+                       const void* dH,
+                       float* dQ, float* dK, float* dV,
+                       float* d_i, float* d_f,
+                       float* dC0, float* dn0, float* dm0,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 #ifdef __cplusplus
 }

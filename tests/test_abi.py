@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 4
+    assert mt.abi_version() == 5
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -216,6 +216,55 @@ def test_recurrent_step_refuses_before_launch():
     ds = _desc(S=1, DHQK=256, DHV=512, chunk_size=64, gate="sig")
     assert step(ds, n_in=4096, m_in=None, n_out=None, m_out=None) == 5
     assert step(ds, n_in=None, m_in=None, n_out=4096, m_out=None) == 5
+
+
+def test_backward_refuses_before_launch():
+    lib = mt.lib()
+    d = _desc(S=300, DHQK=128, DHV=128, chunk_size=64)
+    need = lib.mlstm_bw_workspace_bytes(ctypes.byref(d))
+    assert need > lib.mlstm_fw_workspace_bytes(ctypes.byref(d))
+
+    def bw(desc, ws_bytes=need, **ptrs):
+        names = ["q", "k", "v", "i", "f", "C0", "n0", "m0", "dH", "dQ", "dK", "dV", "d_i", "d_f",
+                 "dC0", "dn0", "dm0", "ws"]
+        vals = [ptrs.get(n, 4096 * (j + 1)) for j, n in enumerate(names)]
+        return lib.mlstm_chunkwise_bw(ctypes.byref(desc) if desc is not None else None, *vals, ws_bytes, None)
+
+    assert bw(None) == 1
+    assert bw(_desc(S=300, DHQK=100, chunk_size=64)) == 2
+    assert bw(d, dH=None) == 1
+    assert bw(d, dQ=None) == 1
+    assert bw(d, d_f=None) == 1
+    assert bw(d, dV=4096 * 12 + 4) == 8                   # gradients are written in 16-byte pieces
+    assert bw(d, dH=4096 * 9 + 8) == 8
+    assert bw(d, d_i=4096 * 13 + 2) == 8
+    assert bw(d, ws=None) == 6
+    assert bw(d, ws_bytes=need - 1) == 6
+    assert bw(d, ws=4096 * 18 + 64) == 6                  # 256-byte aligned workspace
+    ds = _desc(S=300, DHQK=128, DHV=128, chunk_size=64, gate="sig")
+    assert bw(ds, n0=None, m0=None, dm0=None) == 5         # sig gate: no dn0
+    assert bw(ds, n0=None, m0=None, dn0=None) == 5         # sig gate: no dm0
+    assert lib.mlstm_bw_workspace_bytes(None) == 0
+
+
+def test_backward_workspace_formula():
+    """Workspace of the 7B-shaped backward: the forward's two-stage workspace
+    plus float32 chunk states, H, six per-position arrays, the state gradients
+    after each chunk and the initial-state gradients, each region rounded up
+    to 256 bytes."""
+    d = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
+    lib = mt.lib()
+    BH, S, DK, DV, Nc = 64, 8192, 256, 512, 32
+    r = lambda x: (x + 255) // 256 * 256
+    fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(d)))
+    expect = fw + sum(r(x) for x in [
+        BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,   # states
+        BH * S * DV * 4, BH * S * 4, BH * S * 4,                                 # H, m, den
+        BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                          # b, src, 1/z, delta
+        BH * Nc * DK * DV * 4, BH * Nc * DK * 4,                                 # state gradients
+        BH * S * 4, BH * S * 4,                                                  # q.dq, k.dk
+        BH * DK * DV * 4, BH * DK * 4])                                          # dC0, dn0
+    assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
 
 
 def test_flops_formula():

@@ -1,0 +1,161 @@
+"""Parity of the backward pass (mlstm_chunkwise_bw) against the float64
+gradient oracle (needs an MI355X).
+
+Inputs are seeded draws; Q, K, V (and dH where it is bf16) are rounded to
+bf16 and both sides read the same values.  The oracle is torch autograd over
+the quadratic form in float64 (oracle/mlstm_grad.py), pinned on the CPU by
+finite differences of the recurrence.
+
+Tolerance: for every gradient tensor X, max |X_gpu - X_ref| <= tol *
+max(1, max |X_ref|) with tol 1e-3 for bf16 inputs and 1e-4 for float32
+inputs.  The gradient kernels work in float32 throughout (float32 operands on
+fp32 matrix cores); with bf16 inputs they inherit the error of the recomputed
+forward quantities (H, the row normaliser and the chunk states come from the
+split-precision forward, about 1e-3 of the values at worst), which bounds
+the relative error of the normaliser term; measured errors are near 1e-5.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import chunkwise_fw, grad_fw  # noqa: E402
+from workloads import WORKLOADS, head_inputs, round_to_bf16  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-3, "f32": 1e-4}
+KEYS = ("dQ", "dK", "dV", "d_i", "d_f")
+
+
+@pytest.fixture(scope="module")
+def mt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import xlstm_mlstm_chunkwise_amd as m
+    m.lib()
+    return m
+
+
+def _draw(seed, B, NH, S, DK, DV, kind, gate, init, dh_bf16=False):
+    rng = np.random.default_rng(seed)
+    x = dict(q=rng.standard_normal((B, NH, S, DK)), k=rng.standard_normal((B, NH, S, DK)),
+             v=rng.standard_normal((B, NH, S, DV)), i=rng.standard_normal((B, NH, S)),
+             f=2.0 + 4.0 * rng.random((B, NH, S)), dH=rng.standard_normal((B, NH, S, DV)))
+    x = {n: a.astype(np.float32) for n, a in x.items()}
+    if kind == "bf16":
+        for n in ("q", "k", "v"):
+            x[n] = round_to_bf16(x[n])[0]
+    if dh_bf16:
+        x["dH"] = round_to_bf16(x["dH"])[0]
+    if init:
+        x["C0"] = (0.1 * rng.standard_normal((B, NH, DK, DV))).astype(np.float32)
+        if gate == "exp":
+            x["n0"] = rng.random((B, NH, DK)).astype(np.float32)
+            x["m0"] = (0.5 * rng.standard_normal((B, NH))).astype(np.float32)
+    return x
+
+
+def _dev(a, dtype=torch.float32):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda", dtype=dtype)
+
+
+def _gpu(mt, x, kind, gate, L, dh_bf16=False, state_grads=True, **kw):
+    qd = torch.bfloat16 if kind == "bf16" else torch.float32
+    out = mt.mlstm_chunkwise_bw(
+        _dev(x["q"], qd), _dev(x["k"], qd), _dev(x["v"], qd), _dev(x["i"]), _dev(x["f"]),
+        _dev(x["dH"], torch.bfloat16 if dh_bf16 else torch.float32),
+        _dev(x.get("C0")), _dev(x.get("n0")), _dev(x.get("m0")),
+        chunk_size=L, gate=gate, state_grads=state_grads, **kw)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
+
+
+def _ref(x, gate):
+    f64 = {n: a.astype(np.float64) for n, a in x.items()}
+    return grad_fw(f64["q"], f64["k"], f64["v"], f64["i"], f64["f"], f64["dH"], f64.get("C0"),
+                   f64.get("n0") if gate == "exp" else None, f64.get("m0") if gate == "exp" else None,
+                   gate=gate)
+
+
+def _compare(tag, g, r, kind, keys):
+    worst = {}
+    for n in keys:
+        scale = max(1.0, np.abs(r[n]).max())
+        err = np.abs(g[n] - r[n]).max() / scale
+        worst[n] = err
+        assert err <= TOL[kind], f"{tag}: {n} max rel err {err:.3g} > {TOL[kind]} (scale {scale:.3g})"
+    print(f"\n[{tag}] " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()), flush=True)
+
+
+CASES = [
+    # name, B, NH, S, DK, DV, L, kind, gate, init
+    ("exp_bf16_d128_L64_ragged", 1, 2, 300, 128, 128, 64, "bf16", "exp", False),
+    ("exp_bf16_d256x512_L256_init", 1, 2, 520, 256, 512, 256, "bf16", "exp", True),
+    ("sig_bf16_d256x512_L256_init", 1, 2, 520, 256, 512, 256, "bf16", "sig", True),
+    ("exp_f32_d64x192_L64_init", 2, 1, 200, 64, 192, 64, "f32", "exp", True),
+    ("sig_f32_d128x64_L128", 1, 1, 129, 128, 64, 128, "f32", "sig", False),
+    ("exp_bf16_d512x256_L64", 1, 1, 192, 512, 256, 64, "bf16", "exp", False),
+    ("exp_bf16_d64x320_L128_init", 1, 3, 333, 64, 320, 128, "bf16", "exp", True),
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+def test_backward_against_oracle(mt, c):
+    name, B, NH, S, DK, DV, L, kind, gate, init = c
+    x = _draw(100 + CASES.index(c), B, NH, S, DK, DV, kind, gate, init)
+    g = _gpu(mt, x, kind, gate, L)
+    r = _ref(x, gate)
+    keys = KEYS + ("dC0",) + (("dn0", "dm0") if gate == "exp" else ())
+    _compare(name, g, r, kind, keys)
+
+
+def test_backward_bf16_dh_and_one_chunk(mt):
+    x = _draw(21, 1, 2, 64, 128, 256, "bf16", "exp", True, dh_bf16=True)
+    g = _gpu(mt, x, "bf16", "exp", 64, dh_bf16=True)
+    _compare("bf16 dH, one chunk", g, _ref(x, "exp"), "bf16", KEYS + ("dC0", "dn0", "dm0"))
+
+
+def test_backward_without_state_grads_and_empty_sequence(mt):
+    x = _draw(22, 1, 1, 100, 64, 64, "f32", "exp", True)
+    g = _gpu(mt, x, "f32", "exp", 64, state_grads=False)
+    assert "dC0" not in g
+    _compare("no state grads", g, _ref(x, "exp"), "f32", KEYS)
+    e = _draw(23, 1, 2, 0, 64, 64, "f32", "exp", True)
+    g = _gpu(mt, e, "f32", "exp", 64)
+    assert g["dQ"].shape == (1, 2, 0, 64)
+    assert np.all(g["dC0"] == 0) and np.all(g["dn0"] == 0) and np.all(g["dm0"] == 0)
+
+
+@pytest.mark.parametrize("wname", ["bf16_7b_s8192", "sig_7b_s8192"])
+def test_backward_full_size_sampled_heads(mt, wname):
+    """The 7B-shaped workload (B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk
+    256), the whole backward on the GPU.  The oracle checks the last 512
+    positions of two heads: their gradients are those of the tail problem
+    that starts from the exact state at the cut (every later query and key
+    sits in the tail; the prefix enters only through that state), which the
+    float64 chunkwise oracle supplies."""
+    w = WORKLOADS[wname]
+    heads = [(0, 0), (w.B - 1, w.NH - 1)]
+    S, DK, DV, T = w.S, w.DHQK, w.DHV, 512
+    rng = np.random.default_rng(31)
+    dH = rng.standard_normal((w.B, w.NH, S, DV)).astype(np.float32)
+    per = {(b, h): head_inputs(w, b, h) for b in range(w.B) for h in range(w.NH)}
+    stack = lambda key: np.stack([per[(b, h)][key] for b in range(w.B) for h in range(w.NH)]).reshape(
+        (w.B, w.NH) + per[(0, 0)][key].shape)
+    qd = torch.bfloat16
+    g = mt.mlstm_chunkwise_bw(_dev(stack("q"), qd), _dev(stack("k"), qd), _dev(stack("v"), qd),
+                              _dev(stack("i")), _dev(stack("f")), _dev(dH), chunk_size=w.chunk, gate=w.gate)
+    torch.cuda.synchronize()
+    g = {n: t.cpu().numpy().astype(np.float64) for n, t in g.items()}
+    for (b, h) in heads:
+        x = {n: a.astype(np.float64) for n, a in per[(b, h)].items()}
+        t0 = S - T
+        pre = chunkwise_fw(x["q"][None, :t0], x["k"][None, :t0], x["v"][None, :t0], x["i"][None, :t0],
+                           x["f"][None, :t0], gate=w.gate, chunk_size=w.chunk)
+        C, n, m = pre[1], pre[2], pre[3]
+        r = grad_fw(x["q"][None, t0:], x["k"][None, t0:], x["v"][None, t0:], x["i"][None, t0:],
+                    x["f"][None, t0:], dH[b, h][None, t0:].astype(np.float64), C,
+                    n if w.gate == "exp" else None, m if w.gate == "exp" else None, gate=w.gate)
+        gt = {k: g[k][b, h][None, t0:] for k in KEYS}
+        _compare(f"{wname} head {(b, h)} tail {T}", gt, r, "bf16", KEYS)

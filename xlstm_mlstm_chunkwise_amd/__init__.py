@@ -1,4 +1,5 @@
-"""MI355X (gfx950) chunkwise mLSTM forward pass: Python binding of libmlstm_tfla.so.
+"""MI355X (gfx950) chunkwise mLSTM: Python binding of libmlstm_tfla.so (forward
+pass, backward pass and recurrent decode step).
 
 The binding only marshals arguments: it allocates outputs and workspace with
 PyTorch (device memory), passes raw device pointers and the current HIP
@@ -67,6 +68,9 @@ _SYMBOLS = {
     "mlstm_fw_unpack_states": (ctypes.c_int, [ctypes.POINTER(FwDesc), ctypes.c_void_p, ctypes.c_size_t]
                                + [ctypes.c_void_p] * 4),
     "mlstm_recurrent_step": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
+    "mlstm_bw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
+    "mlstm_chunkwise_bw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 18
+                           + [ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -389,3 +393,63 @@ def mlstm_recurrent_step(q, k, v, i_pre, f_pre, C=None, n=None, m=None, *, gate:
     if st:
         raise MlstmError(st, "mlstm_recurrent_step")
     return h, C_out, n_out, m_out
+
+
+def bw_workspace_bytes(desc: FwDesc) -> int:
+    return lib().mlstm_bw_workspace_bytes(ctypes.byref(desc))
+
+
+def mlstm_chunkwise_bw(q, k, v, i_pre, f_pre, dH, C0=None, n0=None, m0=None, *, chunk_size: int,
+                       gate: str = "exp", precision: str = "split", qk_scale: Optional[float] = None,
+                       eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, state_grads: bool = False,
+                       workspace=None):
+    """Backward pass on the GPU: the gradients of sum(dH * H) for the forward
+    pass mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, ...) with the
+    same keyword arguments.  dH has H's shape; its dtype (bfloat16 or
+    float32) is the h_dtype of the descriptor.  Returns a dict with dQ, dK,
+    dV, d_i, d_f (float32) and, with state_grads, dC0 and for the exp gate
+    dn0 and dm0."""
+    torch = _torch()
+    B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
+    if dH.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"dH must be bfloat16 or float32, got {dH.dtype}")
+    _check(dH, "dH", (B, NH, S, DV))
+    _check(C0, "C0", (B, NH, DK, DV), torch.float32)
+    _check(n0, "n0", (B, NH, DK), torch.float32)
+    _check(m0, "m0", (B, NH), torch.float32)
+    desc = _desc_for(q, v, chunk_size, gate, dH.dtype, precision, qk_scale, eps, tile_lq, tile_lkv)
+    st = validate(desc)
+    if st:
+        raise MlstmError(st, "mlstm_chunkwise_bw")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dQ=torch.empty((B, NH, S, DK), **f32), dK=torch.empty((B, NH, S, DK), **f32),
+               dV=torch.empty((B, NH, S, DV), **f32), d_i=torch.empty((B, NH, S), **f32),
+               d_f=torch.empty((B, NH, S), **f32))
+    if state_grads:
+        out["dC0"] = torch.empty((B, NH, DK, DV), **f32)
+        if gate != "sig":
+            out["dn0"] = torch.empty((B, NH, DK), **f32)
+            out["dm0"] = torch.empty((B, NH), **f32)
+    need = bw_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace holds {ws_bytes} bytes, need {need}")
+    st = lib().mlstm_chunkwise_bw(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
+        _ptr(dH), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["d_i"]), _ptr(out["d_f"]),
+        _ptr(out.get("dC0")), _ptr(out.get("dn0")), _ptr(out.get("dm0")), _ptr(workspace), ws_bytes, _stream())
+    if st:
+        raise MlstmError(st, "mlstm_chunkwise_bw")
+    return out
+
+
+def bw_flops(B, NH, S, DHQK, DHV, chunk_size) -> float:
+    """Algorithmic matrix-core FLOPs of one backward pass, causal lower
+    triangle only.  Per token: the five intra-chunk products (scores Q.K^T and
+    dH.V^T, then dS.K, dS^T.Q and P^T.dH), (L+1)(3 DHQK + 2 DHV), plus the
+    four products with a state (C.dn, G.v, G^T.k and the state-gradient
+    update), 8 DHQK DHV."""
+    return float(B) * NH * S * ((chunk_size + 1) * (3.0 * DHQK + 2.0 * DHV) + 8.0 * DHQK * DHV)

@@ -288,6 +288,79 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
+// The chunk states of a two-stage workspace as float32 row-major arrays.
+int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, float* n_states, float* m_states,
+                  hipStream_t s) {
+  const long long n = (long long)d->B * d->NH * ((d->S + d->chunk_size - 1) / d->chunk_size + 1);
+  hipError_t e = hipSuccess;
+  if (d->precision == MLSTM_PREC_F64) {
+    if (C_states) e = mlstm::launch_narrow_f64(ws.C, C_states, n * d->DHQK * d->DHV, s);
+    if (e == hipSuccess && n_states) e = mlstm::launch_narrow_f64(ws.n, n_states, n * d->DHQK, s);
+    if (e == hipSuccess && m_states) e = mlstm::launch_narrow_f64(ws.m, m_states, n, s);
+    return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+  }
+  if (C_states) {
+    if (packed_layout(d)) {
+      e = mlstm::launch_unpack_states(ws.C, C_states, n, d->DHQK, d->DHV, s);
+    } else {
+      e = hipMemcpyAsync(C_states, ws.C, (size_t)n * d->DHQK * d->DHV * sizeof(float), hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (e == hipSuccess && n_states)
+    e = hipMemcpyAsync(n_states, ws.n, (size_t)n * d->DHQK * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && m_states)
+    e = hipMemcpyAsync(m_states, ws.m, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+// ---- backward pass
+// The backward recomputes the forward quantities it needs with the two-stage
+// kernels (the walker forms no chunk states and no per-row normaliser), with
+// H in float32.
+mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
+  mlstm_fw_desc_t r = *d;
+  r.schedule = MLSTM_SCHED_TWO_STAGE;
+  r.h_dtype = MLSTM_F32;
+  return r;
+}
+
+struct BwLayout {
+  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, total;
+};
+
+// Forward workspace first, then the backward's own regions, each 256-byte aligned.
+BwLayout bw_layout(const mlstm_fw_desc_t* d2) {
+  const size_t BH = (size_t)d2->B * d2->NH, S = (size_t)d2->S, DK = d2->DHQK, DV = d2->DHV;
+  const size_t Nc = (S + d2->chunk_size - 1) / d2->chunk_size;
+  const bool ex = d2->gate == MLSTM_GATE_EXP;
+  const size_t f = sizeof(float);
+  BwLayout l;
+  size_t off = round_up(ws_layout(d2).total, 256);
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  l.Cst = take(BH * (Nc + 1) * DK * DV * f);
+  l.nst = take(ex ? BH * (Nc + 1) * DK * f : 0);
+  l.mst = take(ex ? BH * (Nc + 1) * f : 0);
+  l.H = take(ex ? BH * S * DV * f : 0);
+  l.mrows = take(ex ? BH * S * f : 0);
+  l.den = take(ex ? BH * S * f : 0);
+  l.gb = take(BH * S * f);
+  l.gsrc = take(BH * S * f);
+  l.ginvz = take(ex ? BH * S * f : 0);
+  l.gdelta = take(ex ? BH * S * f : 0);
+  l.dC = take(BH * Nc * DK * DV * f);
+  l.dn = take(ex ? BH * Nc * DK * f : 0);
+  l.qdq = take(BH * S * f);
+  l.kdk = take(BH * S * f);
+  l.dC0 = take(BH * DK * DV * f);
+  l.dn0 = take(ex ? BH * DK * f : 0);
+  l.total = off;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -369,29 +442,8 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, s
   if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
   if ((st = check_f32_ptrs({C_states, n_states, m_states})) != MLSTM_OK) return st;
   if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
-  const WsPtrs ws = ws_ptrs(desc, const_cast<void*>(workspace));
-  const long long n = (long long)desc->B * desc->NH * (mlstm_fw_num_chunks(desc) + 1);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (desc->precision == MLSTM_PREC_F64) {
-    if (C_states) e = mlstm::launch_narrow_f64(ws.C, C_states, n * desc->DHQK * desc->DHV, s);
-    if (e == hipSuccess && n_states) e = mlstm::launch_narrow_f64(ws.n, n_states, n * desc->DHQK, s);
-    if (e == hipSuccess && m_states) e = mlstm::launch_narrow_f64(ws.m, m_states, n, s);
-    return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
-  }
-  if (C_states) {
-    if (packed_layout(desc)) {
-      e = mlstm::launch_unpack_states(ws.C, C_states, n, desc->DHQK, desc->DHV, s);
-    } else {
-      e = hipMemcpyAsync(C_states, ws.C, (size_t)n * desc->DHQK * desc->DHV * sizeof(float),
-                         hipMemcpyDeviceToDevice, s);
-    }
-  }
-  if (e == hipSuccess && n_states)
-    e = hipMemcpyAsync(n_states, ws.n, (size_t)n * desc->DHQK * sizeof(float), hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess && m_states)
-    e = hipMemcpyAsync(m_states, ws.m, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, s);
-  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+  return unpack_states(desc, ws_ptrs(desc, const_cast<void*>(workspace)), C_states, n_states, m_states,
+                       static_cast<hipStream_t>(stream));
 }
 
 int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
@@ -450,6 +502,85 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc, const void* q, const void*
   p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
   p.h_bf16 = desc->h_dtype == MLSTM_BF16;
   const hipError_t e = mlstm::launch_step(p, desc->gate == MLSTM_GATE_SIG, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc) {
+  if (validate_desc(desc) != MLSTM_OK) return 0;
+  const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
+  return bw_layout(&d2).total;
+}
+
+int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
+                       float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
+    return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, m0, dn0, dm0)) != MLSTM_OK) return st;
+  for (const void* x : {Q, K, V, dH, static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                        static_cast<const void*>(dV)})
+    if (x && !aligned(x, 16)) return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
+  const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
+  const BwLayout l = bw_layout(&d2);
+  if (!workspace || workspace_bytes < l.total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bool ex = desc->gate == MLSTM_GATE_EXP;
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const WsPtrs fw = ws_ptrs(&d2, workspace);
+  if (desc->S > 0) {
+    st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s);
+    if (st == MLSTM_OK) st = unpack_states(&d2, fw, at(l.Cst), ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
+    if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
+    if (st != MLSTM_OK) return st;
+  }
+  mlstm::BwParams p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.dH = dH;
+  p.H = ex ? at(l.H) : nullptr;
+  p.m_rows = ex ? at(l.mrows) : nullptr;
+  p.den_rows = ex ? at(l.den) : nullptr;
+  p.C_states = at(l.Cst);
+  p.n_states = ex ? at(l.nst) : nullptr;
+  p.m_states = ex ? at(l.mst) : nullptr;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.gb = at(l.gb);
+  p.gsrc = at(l.gsrc);
+  p.ginvz = ex ? at(l.ginvz) : nullptr;
+  p.gdelta = ex ? at(l.gdelta) : nullptr;
+  p.dC_states = at(l.dC);
+  p.dn_states = ex ? at(l.dn) : nullptr;
+  p.qdq = at(l.qdq);
+  p.kdk = at(l.kdk);
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.d_i = d_i;
+  p.d_f = d_f;
+  // dm0 needs dC0 and dn0: the workspace holds them when the caller does not ask
+  p.dC0 = dC0 ? dC0 : (dm0 ? at(l.dC0) : nullptr);
+  p.dn0 = dn0 ? dn0 : (dm0 ? at(l.dn0) : nullptr);
+  p.dm0 = dm0;
+  p.scale = resolve_scale(desc);
+  p.eps = desc->eps;
+  p.BH = desc->B * desc->NH;
+  p.S = desc->S;
+  p.DK = desc->DHQK;
+  p.DV = desc->DHV;
+  p.L = desc->chunk_size;
+  p.Nc = (desc->S + desc->chunk_size - 1) / desc->chunk_size;
+  p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
+  p.dh_bf16 = desc->h_dtype == MLSTM_BF16;
+  const hipError_t e = mlstm::launch_bw(p, !ex, s);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 

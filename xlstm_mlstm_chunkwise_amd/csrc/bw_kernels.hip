@@ -1,0 +1,606 @@
+// Backward pass of the chunkwise mLSTM (gfx950): the gradients of <dH, H>
+// with respect to Q, K, V, both gate pre-activations and the initial state.
+//
+// The pages print no backward pass.  What is computed is the derivative of
+// the forward pass of "xLSTM: the NX-AI repository behind the extended LSTM
+// architecture" (section "Exponential gating, matrix memory, and why the
+// kernels decide everything"), organised chunk by chunk like the forward of
+// "Tiled Flash Linear Attention: More Efficient Linear RNN and xLSTM
+// Kernels" (abstract: chunkwise-parallel training).  The max-state m is a
+// stabiliser and is held constant; with eps = 0 the output does not depend on
+// it, so the gradient is exact.
+//
+// Per head, with s the query scale, b the in-chunk inclusive sum of
+// log sigmoid(f), g its value at the chunk end, src = i (exp gate) or
+// log sigmoid(i) (sig gate), M_c the stabiliser of the state entering chunk
+// c, m_t and den_t the row max-state and stabilised normaliser of the
+// forward pass, and z_t = max(|den_t|, e^{-m_t}) + eps:
+//   dn_t    = dh_t / z_t                                  (sig: dh_t)
+//   delta_t = -(dh_t . h_t) / z_t * sign(den_t) where |den_t| > e^{-m_t}, else 0
+//   w_tj    = e^{b_t - b_j + src_j - m_t}   (j <= t in the same chunk; sig: no m_t)
+//   dP_tj   = dn_t . v_j + delta_t
+//   dq_t    = s sum_j w_tj dP_tj k_j + s e^{b_t + M_c - m_t} (C_c dn_t + delta_t n_c)
+//   dk_j    = s sum_t w_tj dP_tj q_t + e^{g - b_j + src_j - M_{c+1}} (G_c v_j + N_c)
+//   dv_j    = sum_t w_tj s (q_t . k_j) dn_t + e^{g - b_j + src_j - M_{c+1}} G_c^T k_j
+// (C_c, n_c) is the forward state entering chunk c, and (G_c, N_c) the
+// gradient that every later query sends into the state after chunk c, kept
+// relative to that state's stabiliser:
+//   G_{c-1} = e^{M_c + g_c - M_{c+1}} G_c + s sum_{t in c} e^{b_t + M_c - m_t} q_t dn_t^T
+//   N_{c-1} = the same with delta_t in place of dn_t,   (G_{-1}, N_{-1}) = (dC0, dn0)
+// (sig gate: no stabilisers, no N).  Every exponent above is <= 0.  The gate
+// gradients follow from two identities of the exact gradient:
+//   d i_j = k_j . dk_j                 (sig gate: times sigmoid(-i_j))
+//   d f_t = sigmoid(-f_t) sum_{u >= t} (q_u . dq_u - k_u . dk_u)
+// and dm0 = sum(dC0 * C0) + dn0 . n0.
+//
+// Kernels, all on fp32 matrix cores (v_mfma_f32_16x16x4_f32: exact products
+// of float32 operands, fp32 accumulation), 256 threads each:
+//   bw_prep    per position: b, src, 1/z, delta
+//   bw_dstate  the reverse recurrence of (G, N): one workgroup per head and
+//              64 x 64 tile of G, chunks in reverse order; G_c goes to HBM
+//   bw_tiles   dq per 64-query tile, dk and dv per 64-key tile: the inter-
+//              chunk term first, then for each causal partner tile the
+//              64 x 64 score tile (dP or the raw scores), weighted in
+//              registers and fed straight back to the matrix cores as the
+//              operand of the output product
+//   bw_gates   the reverse scan of q.dq - k.dk over the sequence, d_i, dm0
+// Matrix-core fragment of v_mfma_f32_16x16x4_f32: lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; the 16 x 16 accumulator holds in
+// lane l register r the element (4 (l / 16) + r, l % 16).  An accumulator
+// tile is therefore a ready B operand of a product that contracts over its
+// rows: in step r the lanes' slot l / 16 stands for row 4 (l / 16) + r.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mlstm {
+namespace {
+
+constexpr int kT = 64;    // rows of a tile
+constexpr int kLdA = 68;  // LDS row stride (floats) of tiles read with the row on lane % 16
+constexpr int kLdB = 80;  // LDS row stride of tiles read with the row on lane / 16
+
+enum { kModeDQ = 0, kModeDK = 1, kModeDV = 2 };
+
+__device__ __forceinline__ float4_t mma4(float a, float b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid_neg(float x) { return 1.0f / (1.0f + expf(x)); }
+
+// 16 consecutive values at element offset `off` of a bf16 or float32 array.
+__device__ __forceinline__ void load16(const void* base, bool bf16, size_t off, float (&x)[16]) {
+  if (bf16) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint4 a = q[0], b = q[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = q[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// LDS tile dst[r * ld + c] (r, c < 64) = rowscale[r] * src[(row0 + r) * D + col0 + c]
+// for r < nrows, zero below.  256 threads: thread t fills row t / 4,
+// columns 16 (t % 4) .. 16 (t % 4) + 15.
+__device__ __forceinline__ void stage_tile(float* dst, int ld, const void* src, bool bf16, size_t row0, int D,
+                                           int col0, int nrows, const float* rowscale) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  float x[16];
+  if (r < nrows) {
+    load16(src, bf16, (row0 + r) * (size_t)D + col0 + c, x);
+    if (rowscale) {
+      const float sc = rowscale[r];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] *= sc;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+  }
+  float4* d = reinterpret_cast<float4*>(dst + r * ld + c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// Per-position terms: b (in-chunk inclusive sum of log sigmoid(f)), src, and
+// for the exp gate 1/z and delta.  One workgroup per (head, chunk).
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_prep_kernel(const BwParams p) {
+  __shared__ float s_tot[4];
+  const int bh = blockIdx.x / p.Nc, c = blockIdx.x % p.Nc;
+  const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
+  const size_t rb = (size_t)bh * p.S + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pos = 4 * tid + e;
+    v[e] = pos < Lc ? log_sigmoid(p.f_pre[rb + pos]) : 0.0f;
+  }
+  block_scan4<false, 4>(v, s_tot);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pos = 4 * tid + e;
+    if (pos < Lc) {
+      p.gb[rb + pos] = v[e];
+      const float ip = p.i_pre[rb + pos];
+      p.gsrc[rb + pos] = SIG ? log_sigmoid(ip) : ip;
+    }
+  }
+  if constexpr (!SIG) {
+    for (int r = wave; r < Lc; r += 4) {
+      const size_t row = rb + r;
+      float d = 0.0f;
+      for (int e = lane; e < p.DV; e += 64) {
+        const size_t i = row * p.DV + e;
+        const float dh = p.dh_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.dH)[i])
+                                   : static_cast<const float*>(p.dH)[i];
+        d += dh * p.H[i];
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+      if (lane == 0) {
+        const float den = p.den_rows[row], em = expf(-p.m_rows[row]);
+        const float invz = 1.0f / (fmaxf(fabsf(den), em) + p.eps);
+        p.ginvz[row] = invz;
+        p.gdelta[row] = fabsf(den) > em ? (den > 0.0f ? -d * invz : d * invz) : 0.0f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse recurrence of the state gradient (G, N).  Grid (BH, DK/64, DV/64);
+// wave w holds rows 16w .. 16w+15 of the 64 x 64 tile of G.  Entry c of
+// dC_states is G_c (the gradient into the state after chunk c), entry Nc-1 is
+// zero; the value left after chunk 0 is dC0.
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_dstate_kernel(const BwParams p) {
+  __shared__ __align__(16) float s_q[kT * kLdB];  // [t][k]
+  __shared__ __align__(16) float s_b[kT * kLdB];  // [t][v]: weighted dn
+  __shared__ float s_w[kT], s_wd[kT];
+  const int bh = blockIdx.x, kt = blockIdx.y, vt = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const int DK = p.DK, DV = p.DV, Nc = p.Nc;
+  const bool own_n = !SIG && vt == 0;
+  float4_t acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float dn = 0.0f;
+  for (int c = Nc - 1; c >= 0; --c) {
+    float* G = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        G[(size_t)(kt * kT + 16 * wave + 4 * g4 + r) * DV + vt * kT + 16 * nb + l16] = acc[nb][r];
+    if (own_n && tid < kT) p.dn_states[((size_t)bh * Nc + c) * DK + kt * kT + tid] = dn;
+
+    const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
+    const size_t rb = (size_t)bh * p.S + t0;
+    const float g = p.gb[rb + Lc - 1];
+    float Min = 0.0f, decay;
+    if constexpr (SIG) {
+      decay = expf(g);
+    } else {
+      Min = p.m_states[(size_t)bh * (Nc + 1) + c];
+      decay = expf(Min + g - p.m_states[(size_t)bh * (Nc + 1) + c + 1]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] *= decay;
+    dn *= decay;
+
+    for (int ts = 0; ts < Lc; ts += kT) {
+      const int nr = min(kT, Lc - ts);
+      if (tid < kT) {
+        float w = 0.0f, wd = 0.0f;
+        if (tid < nr) {
+          const size_t r = rb + ts + tid;
+          if constexpr (SIG) {
+            w = p.scale * expf(p.gb[r]);
+          } else {
+            const float e = p.scale * expf(p.gb[r] + Min - p.m_rows[r]);
+            w = e * p.ginvz[r];
+            wd = e * p.gdelta[r];
+          }
+        }
+        s_w[tid] = w;
+        s_wd[tid] = wd;
+      }
+      __syncthreads();
+      stage_tile(s_q, kLdB, p.Q, p.qkv_bf16, rb + ts, DK, kt * kT, nr, nullptr);
+      stage_tile(s_b, kLdB, p.dH, p.dh_bf16, rb + ts, DV, vt * kT, nr, s_w);
+      __syncthreads();
+#pragma unroll 4
+      for (int j = 0; j < 16; ++j) {
+        const int t = 4 * j + g4;
+        const float a = s_q[t * kLdB + 16 * wave + l16];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[nb] = mma4(a, s_b[t * kLdB + 16 * nb + l16], acc[nb]);
+      }
+      if (own_n && tid < kT)
+        for (int t = 0; t < nr; ++t) dn += s_wd[t] * s_q[t * kLdB + tid];
+      __syncthreads();
+    }
+  }
+  if (p.dC0) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p.dC0[(size_t)bh * DK * DV + (size_t)(kt * kT + 16 * wave + 4 * g4 + r) * DV + vt * kT + 16 * nb + l16] =
+            acc[nb][r];
+  }
+  if (own_n && p.dn0 && tid < kT) p.dn0[(size_t)bh * DK + kt * kT + tid] = dn;
+}
+
+// ---------------------------------------------------------------------------
+// Gate terms of 64 rows of a chunk (zero past the chunk end).
+struct RowGates {
+  float b[kT], src[kT], m[kT], invz[kT], delta[kT];
+};
+
+template <bool SIG>
+__device__ __forceinline__ void load_rows(RowGates& g, const BwParams& p, size_t rb, int r0, int Lc) {
+  const int t = threadIdx.x;
+  if (t < kT) {
+    const bool ok = r0 + t < Lc;
+    const size_t r = rb + r0 + t;
+    g.b[t] = ok ? p.gb[r] : 0.0f;
+    g.src[t] = ok ? p.gsrc[r] : 0.0f;
+    if constexpr (!SIG) {
+      g.m[t] = ok ? p.m_rows[r] : 0.0f;
+      g.invz[t] = ok ? p.ginvz[r] : 0.0f;
+      g.delta[t] = ok ? p.gdelta[r] : 0.0f;
+    }
+  }
+}
+
+// dq (MODE kModeDQ, own rows = 64 queries), dk (kModeDK) or dv (kModeDV,
+// own rows = 64 keys) for one 64-row tile of one chunk and W = 16 NY output
+// columns.  Wave w owns rows 16w .. 16w+15 of the tile: they are the columns
+// of its accumulators, which hold the transposed output (out^T[y][own]).
+template <int MODE, bool SIG, int NY>
+__global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
+  constexpr int W = 16 * NY;
+  __shared__ __align__(16) float s_x[kT * kLdA];  // partner tile, contraction chunk  [o][x]
+  __shared__ __align__(16) float s_w[kT * kLdA];  // own tile, contraction chunk     [w][x]
+  __shared__ __align__(16) float s_y[kT * kLdB];  // output-side operand chunk
+  __shared__ RowGates g_own, g_oth;
+
+  const int nT = p.L / kT;
+  const int ot = blockIdx.x % nT;
+  const int rest = blockIdx.x / nT;
+  const int c = rest % p.Nc, bh = rest / p.Nc;
+  const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
+  const int own0 = ot * kT;
+  if (own0 >= Lc) return;
+  const int nown = min(kT, Lc - own0);
+  const size_t rb = (size_t)bh * p.S + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const int DK = p.DK, DV = p.DV, Nc = p.Nc;
+  const int DO = MODE == kModeDV ? DV : DK;  // output width
+  const int y0 = blockIdx.y * W;
+  const bool qb = p.qkv_bf16, hb = p.dh_bf16;
+
+  load_rows<SIG>(g_own, p, rb, own0, Lc);
+  __syncthreads();
+  const int w = 16 * wave + l16;  // own row of this lane's accumulator columns
+  const bool own_ok = w < nown;
+  const float ob = g_own.b[w], osrc = g_own.src[w];
+  const float om = SIG ? 0.0f : g_own.m[w];
+  const float odelta = SIG ? 0.0f : g_own.delta[w];
+  const float gc = p.gb[rb + Lc - 1];
+
+  float4_t acc[NY];
+#pragma unroll
+  for (int i = 0; i < NY; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // ---- inter-chunk term
+  if constexpr (MODE == kModeDQ) {
+    // (C_c dn)^T: contraction over v; then times e^{b + M_c - m}, plus delta n_c
+    if (c > 0 || p.C0 || p.n0) {
+      const float* Cst = p.C_states + ((size_t)bh * (Nc + 1) + c) * DK * DV;
+      for (int e0 = 0; e0 < DV; e0 += kT) {
+        __syncthreads();
+        stage_tile(s_w, kLdA, p.dH, hb, rb + own0, DV, e0, nown, SIG ? nullptr : g_own.invz);
+        for (int yc = 0; yc < W / kT; ++yc) {
+          __syncthreads();
+          stage_tile(s_x, kLdA, Cst, false, y0 + yc * kT, DV, e0, kT, nullptr);  // [d][e]
+          __syncthreads();
+#pragma unroll 4
+          for (int j = 0; j < 16; ++j) {
+            const float b = s_w[w * kLdA + 4 * j + g4];
+#pragma unroll
+            for (int yb = 0; yb < 4; ++yb)
+              acc[4 * yc + yb] = mma4(s_x[(16 * yb + l16) * kLdA + 4 * j + g4], b, acc[4 * yc + yb]);
+          }
+        }
+      }
+      float wq;
+      if constexpr (SIG) wq = own_ok ? expf(ob) : 0.0f;
+      else wq = own_ok ? expf(ob + p.m_states[(size_t)bh * (Nc + 1) + c] - om) : 0.0f;
+      const float* nst = SIG ? nullptr : p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
+#pragma unroll
+      for (int yb = 0; yb < NY; ++yb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[yb][r] * wq;
+          if constexpr (!SIG) x += odelta * wq * nst[y0 + 16 * yb + 4 * g4 + r];
+          acc[yb][r] = x;
+        }
+    }
+  } else {
+    if (c < Nc - 1) {
+      // dk: (G v + N)^T, contraction over v;  dv: (G^T k)^T, contraction over k
+      const float* G = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+      const int XD = MODE == kModeDK ? DV : DK;
+      for (int x0 = 0; x0 < XD; x0 += kT) {
+        __syncthreads();
+        if constexpr (MODE == kModeDK) stage_tile(s_w, kLdA, p.V, qb, rb + own0, DV, x0, nown, nullptr);
+        else stage_tile(s_w, kLdA, p.K, qb, rb + own0, DK, x0, nown, nullptr);
+        for (int yc = 0; yc < W / kT; ++yc) {
+          __syncthreads();
+          if constexpr (MODE == kModeDK) stage_tile(s_y, kLdA, G, false, y0 + yc * kT, DV, x0, kT, nullptr);  // [d][v]
+          else stage_tile(s_y, kLdB, G, false, x0, DV, y0 + yc * kT, kT, nullptr);  // [k][e]
+          __syncthreads();
+#pragma unroll 4
+          for (int j = 0; j < 16; ++j) {
+            const float b = s_w[w * kLdA + 4 * j + g4];
+#pragma unroll
+            for (int yb = 0; yb < 4; ++yb) {
+              const float a = MODE == kModeDK ? s_y[(16 * yb + l16) * kLdA + 4 * j + g4]
+                                              : s_y[(4 * j + g4) * kLdB + 16 * yb + l16];
+              acc[4 * yc + yb] = mma4(a, b, acc[4 * yc + yb]);
+            }
+          }
+        }
+      }
+      float wk;
+      const float Mo = SIG ? 0.0f : p.m_states[(size_t)bh * (Nc + 1) + c + 1];
+      wk = own_ok ? expf(gc - ob + osrc - Mo) : 0.0f;
+      if constexpr (MODE == kModeDK) {
+        const float* Nst = SIG ? nullptr : p.dn_states + ((size_t)bh * Nc + c) * DK;
+        const float f = wk / p.scale;
+#pragma unroll
+        for (int yb = 0; yb < NY; ++yb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[yb][r];
+            if constexpr (!SIG) x += Nst[y0 + 16 * yb + 4 * g4 + r];
+            acc[yb][r] = x * f;
+          }
+      } else {
+#pragma unroll
+        for (int yb = 0; yb < NY; ++yb) acc[yb] *= wk;
+      }
+    }
+  }
+
+  // ---- intra-chunk term: every causal partner tile
+  const int lo = MODE == kModeDQ ? 0 : ot;
+  const int hi = MODE == kModeDQ ? ot : (Lc - 1) / kT;
+  for (int xt = lo; xt <= hi; ++xt) {
+    const int x0 = xt * kT, nx = min(kT, Lc - x0);
+    __syncthreads();
+    load_rows<SIG>(g_oth, p, rb, x0, Lc);
+    float4_t sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int XD = MODE == kModeDV ? DK : DV;
+    for (int c0 = 0; c0 < XD; c0 += kT) {
+      __syncthreads();
+      if constexpr (MODE == kModeDQ) {
+        stage_tile(s_x, kLdA, p.V, qb, rb + x0, DV, c0, nx, nullptr);
+        stage_tile(s_w, kLdA, p.dH, hb, rb + own0, DV, c0, nown, SIG ? nullptr : g_own.invz);
+      } else if constexpr (MODE == kModeDK) {
+        stage_tile(s_x, kLdA, p.dH, hb, rb + x0, DV, c0, nx, SIG ? nullptr : g_oth.invz);
+        stage_tile(s_w, kLdA, p.V, qb, rb + own0, DV, c0, nown, nullptr);
+      } else {
+        stage_tile(s_x, kLdA, p.Q, qb, rb + x0, DK, c0, nx, nullptr);
+        stage_tile(s_w, kLdA, p.K, qb, rb + own0, DK, c0, nown, nullptr);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int j = 0; j < 16; ++j) {
+        const float b = s_w[w * kLdA + 4 * j + g4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = mma4(s_x[(16 * i + l16) * kLdA + 4 * j + g4], b, sc[i]);
+      }
+    }
+    // weights: sc[i][r] is the partner row o = 16 i + 4 g4 + r against own row w
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = 16 * i + 4 * g4 + r;
+        float x = 0.0f;
+        if constexpr (MODE == kModeDQ) {
+          // o = key, w = query
+          if (own_ok && o < nx && x0 + o <= own0 + w) {
+            const float ex = ob - g_oth.b[o] + g_oth.src[o] - om;
+            x = expf(ex) * (sc[i][r] + odelta);
+          }
+        } else {
+          // o = query, w = key
+          if (own_ok && o < nx && own0 + w <= x0 + o) {
+            const float ex = g_oth.b[o] - ob + osrc - (SIG ? 0.0f : g_oth.m[o]);
+            if constexpr (MODE == kModeDK) x = expf(ex) * (sc[i][r] + (SIG ? 0.0f : g_oth.delta[o]));
+            else x = expf(ex) * p.scale * sc[i][r];
+          }
+        }
+        sc[i][r] = x;
+      }
+    // output product: out^T[y][w] += sum_o Y[o][y] sc[o][w]
+    for (int yc = 0; yc < W / kT; ++yc) {
+      __syncthreads();
+      if constexpr (MODE == kModeDQ) stage_tile(s_y, kLdA, p.K, qb, rb + x0, DK, y0 + yc * kT, nx, nullptr);
+      else if constexpr (MODE == kModeDK) stage_tile(s_y, kLdA, p.Q, qb, rb + x0, DK, y0 + yc * kT, nx, nullptr);
+      else stage_tile(s_y, kLdA, p.dH, hb, rb + x0, DV, y0 + yc * kT, nx, SIG ? nullptr : g_oth.invz);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int o = 16 * i + 4 * g4 + r;
+#pragma unroll
+          for (int yb = 0; yb < 4; ++yb)
+            acc[4 * yc + yb] = mma4(s_y[o * kLdA + 16 * yb + l16], sc[i][r], acc[4 * yc + yb]);
+        }
+    }
+  }
+
+  // ---- epilogue: scale, store, and q.dq / k.dk for the gate gradients
+  const float fin = MODE == kModeDV ? 1.0f : p.scale;
+  float* out = MODE == kModeDQ ? p.dQ : MODE == kModeDK ? p.dK : p.dV;
+  float dot = 0.0f;
+  if (own_ok) {
+    const size_t orow = rb + own0 + w;
+#pragma unroll
+    for (int yb = 0; yb < NY; ++yb) {
+      const int y = y0 + 16 * yb + 4 * g4;
+      const float4 o4 = make_float4(acc[yb][0] * fin, acc[yb][1] * fin, acc[yb][2] * fin, acc[yb][3] * fin);
+      *reinterpret_cast<float4*>(out + orow * DO + y) = o4;
+      if constexpr (MODE != kModeDV) {
+        const void* src = MODE == kModeDQ ? p.Q : p.K;
+        float x[4];
+        if (qb) {
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + orow * DK + y);
+          x[0] = __uint_as_float(u.x << 16);
+          x[1] = __uint_as_float(u.x & 0xffff0000u);
+          x[2] = __uint_as_float(u.y << 16);
+          x[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + orow * DK + y);
+          x[0] = v.x;
+          x[1] = v.y;
+          x[2] = v.z;
+          x[3] = v.w;
+        }
+        dot += x[0] * o4.x + x[1] * o4.y + x[2] * o4.z + x[3] * o4.w;
+      }
+    }
+  }
+  if constexpr (MODE != kModeDV) {
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    if (g4 == 0 && own_ok) (MODE == kModeDQ ? p.qdq : p.kdk)[rb + own0 + w] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate gradients: one workgroup per head runs the reverse scan of
+// q.dq - k.dk over the sequence in blocks of 1024 positions; dm0.
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_gates_kernel(const BwParams p) {
+  __shared__ float s_tot[4];
+  __shared__ float s_all;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const size_t rb = (size_t)bh * p.S;
+  float carry = 0.0f;
+  for (int blk = (p.S + 1023) / 1024 - 1; blk >= 0; --blk) {
+    float v[4];
+    int pos[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pos[e] = blk * 1024 + 1023 - (4 * tid + e);
+      v[e] = pos[e] < p.S ? p.qdq[rb + pos[e]] - p.kdk[rb + pos[e]] : 0.0f;
+    }
+    block_scan4<false, 4>(v, s_tot);
+    if (tid == 255) s_all = v[3];
+    __syncthreads();
+    const float tot = s_all;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (pos[e] < p.S) {
+        const size_t r = rb + pos[e];
+        p.d_f[r] = sigmoid_neg(p.f_pre[r]) * (v[e] + carry);
+        const float kd = p.kdk[r];
+        p.d_i[r] = SIG ? kd * sigmoid_neg(p.i_pre[r]) : kd;
+      }
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  if constexpr (!SIG) {
+    if (p.dm0) {
+      float a = 0.0f;
+      const size_t n = (size_t)p.DK * p.DV;
+      if (p.C0)
+        for (size_t i = tid; i < n; i += 256) a += p.dC0[(size_t)bh * n + i] * p.C0[(size_t)bh * n + i];
+      if (p.n0)
+        for (int i = tid; i < p.DK; i += 256) a += p.dn0[(size_t)bh * p.DK + i] * p.n0[(size_t)bh * p.DK + i];
+      a = block_reduce<false, 4>(a, s_tot);
+      if (tid == 0) p.dm0[bh] = a;
+    }
+  }
+}
+
+__global__ void bw_zero_kernel(float* x, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.0f;
+}
+
+hipError_t zero(float* x, long long n, hipStream_t s) {
+  if (!x || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n);
+  return hipGetLastError();
+}
+
+template <int MODE, bool SIG>
+hipError_t launch_tiles(const BwParams& p, int W, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)p.BH * p.Nc * (p.L / kT)), (unsigned)((MODE == kModeDV ? p.DV : p.DK) / W));
+  switch (W / 16) {
+    case 4: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 4>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 8>), grid, dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 16>), grid, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 32>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool SIG>
+hipError_t launch_all(const BwParams& p, hipStream_t s) {
+  hipError_t e;
+  hipLaunchKernelGGL((bw_prep_kernel<SIG>), dim3((unsigned)(p.BH * p.Nc)), dim3(256), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bw_dstate_kernel<SIG>), dim3((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT)),
+                     dim3(256), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
+  if ((e = launch_tiles<kModeDK, SIG>(p, p.DK, s)) != hipSuccess) return e;
+  const int Wv = p.DV % 256 == 0 ? 256 : p.DV % 128 == 0 ? 128 : 64;
+  if ((e = launch_tiles<kModeDV, SIG>(p, Wv, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((bw_gates_kernel<SIG>), dim3((unsigned)p.BH), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bw(const BwParams& p, bool sig, hipStream_t stream) {
+  if (p.DK % kT || p.DV % kT || p.L % kT || p.DK > 512 || p.DV > 512 || p.L > 1024) return hipErrorInvalidValue;
+  if (p.S == 0) {
+    // no position reads the initial state: its gradients are zero
+    hipError_t e = zero(p.dC0, (long long)p.BH * p.DK * p.DV, stream);
+    if (e == hipSuccess) e = zero(p.dn0, (long long)p.BH * p.DK, stream);
+    if (e == hipSuccess) e = zero(p.dm0, p.BH, stream);
+    return e;
+  }
+  return sig ? launch_all<true>(p, stream) : launch_all<false>(p, stream);
+}
+
+}  // namespace mlstm

@@ -104,6 +104,46 @@ struct StepParams {
   int qkv_bf16, h_bf16;
 };
 
+// Backward pass: gradients of <dH, H> (bw_kernels.hip).  The forward
+// quantities it reads (row max-state and normaliser, H, the chunk states as
+// float32 row-major) come from a recomputation by the forward kernels.
+struct BwParams {
+  const void* Q;  // (BH, S, DK), bf16 or float32
+  const void* K;
+  const void* V;  // (BH, S, DV)
+  const float* i_pre;  // (BH, S)
+  const float* f_pre;
+  const void* dH;        // (BH, S, DV), bf16 or float32
+  const float* H;        // (BH, S, DV) float32 (exp gate)
+  const float* m_rows;   // (BH, S) exp gate
+  const float* den_rows; // (BH, S) exp gate
+  const float* C_states; // (BH, Nc + 1, DK, DV) float32 row-major: state entering each chunk
+  const float* n_states; // (BH, Nc + 1, DK) exp gate
+  const float* m_states; // (BH, Nc + 1) exp gate
+  const float* C0;       // may be null (for dm0)
+  const float* n0;       // may be null
+  float* gb;             // (BH, S) scratch: in-chunk sum of log sigmoid(f)
+  float* gsrc;           // (BH, S) scratch: i (exp) or log sigmoid(i) (sig)
+  float* ginvz;          // (BH, S) scratch: 1 / z (exp)
+  float* gdelta;         // (BH, S) scratch: normaliser gradient (exp)
+  float* dC_states;      // (BH, Nc, DK, DV) scratch: state gradient after each chunk
+  float* dn_states;      // (BH, Nc, DK) scratch (exp)
+  float* qdq;            // (BH, S) scratch
+  float* kdk;            // (BH, S) scratch
+  float* dQ;             // (BH, S, DK) float32
+  float* dK;
+  float* dV;             // (BH, S, DV) float32
+  float* d_i;            // (BH, S)
+  float* d_f;
+  float* dC0;            // (BH, DK, DV), may be null
+  float* dn0;            // (BH, DK), may be null (exp)
+  float* dm0;            // (BH), may be null (exp); needs dC0 and dn0
+  float scale;
+  float eps;
+  int BH, S, DK, DV, L, Nc;
+  int qkv_bf16, dh_bf16;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gates(const GatesParams& p, bool sig, hipStream_t stream);
 bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split);
@@ -111,6 +151,7 @@ bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split);
 long long walk_workgroups(int BH, int DV);
 hipError_t launch_walk(const WalkParams& p, bool sig, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, bool sig, hipStream_t stream);
+hipError_t launch_bw(const BwParams& p, bool sig, hipStream_t stream);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 
