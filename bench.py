@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 METRIC = "mLSTM chunkwise fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 7B-shaped heads"
 CSRC = os.path.join(ROOT, "xlstm_mlstm_chunkwise_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -180,6 +181,8 @@ def main(argv=None) -> int:
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent step (one token per head and call) on the workload's heads "
                          "instead of the forward pass")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (mlstm_chunkwise_bw) on the workload instead of the forward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times (the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -233,6 +236,8 @@ def main(argv=None) -> int:
     m0 = up(x["m0"], torch.float32) if ("m0" in x and not sig) else None
     del x
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    if args.backward:
+        return bench_backward(args, w, mt, torch, np, (q, k, v, i_pre, f_pre, C0, n0, m0))
     h_dtype = torch.bfloat16 if args.h_dtype == "bf16" else torch.float32
     H = torch.empty((w.B, w.NH, w.S, w.DHV), dtype=h_dtype, device=dev)
     desc = mt.make_desc(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk,
@@ -343,6 +348,127 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_backward(name: str, budget_s: float, S: int = 2048) -> dict:
+    """Time the float64 gradient oracle (torch autograd over the quadratic
+    form) on a bounded sample: heads cut to their first S positions, run one
+    after another in this process on torch's CPU threads (no worker
+    processes: this one already holds the GPU); tokens/s counts NH heads per
+    token.  The quadratic form's cost per token grows with S, so the figure
+    holds for this prefix length only."""
+    import numpy as np
+    import torch
+    from oracle import grad_fw
+    from workloads import WORKLOADS, head_inputs
+    w = WORKLOADS[name]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    torch.set_num_threads(cores)
+    dH = np.random.default_rng(7).standard_normal((1, S, w.DHV))
+    n_heads, t_used = 0, 0.0
+    while n_heads < w.BH and t_used < budget_s:
+        x = head_inputs(w, n_heads // w.NH, n_heads % w.NH)
+        t0 = time.perf_counter()
+        grad_fw(*[x[k][None, :S].astype(np.float64) for k in ("q", "k", "v", "i", "f")], dH, gate=w.gate)
+        t_used += time.perf_counter() - t0
+        n_heads += 1
+    return {"value": n_heads * S / w.NH / t_used, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 gradient oracle (autograd over the quadratic form), {n_heads} of {w.BH} heads "
+                       f"x the first {S} of {w.S} positions ({w.name}), one process on {cores} torch threads; "
+                       f"tokens/s counts {w.NH} heads per token; oracle time {t_used:.1f} s")}
+
+
+def bench_backward(args, w, mt, torch, np, inputs) -> int:
+    """The backward pass on the whole workload: mlstm_chunkwise_bw (forward
+    quantities recomputed, then the gradient kernels) with a float32 dH drawn
+    N(0, 1), timed with HIP events around back-to-back calls; then the two
+    stages apart (mlstm_bw_recompute, mlstm_bw_grads) for the stage times.
+    The roofline prices the gradient stage, whose products all run on fp32
+    matrix cores, against the fp32 dense matrix-core peak."""
+    import ctypes
+    q, k, v, i_pre, f_pre, C0, n0, m0 = inputs
+    dev = q.device
+    sig = w.gate == "sig"
+    dH = torch.randn((w.B, w.NH, w.S, w.DHV), generator=torch.Generator(device=dev).manual_seed(31),
+                     device=dev, dtype=torch.float32)
+    desc = mt.make_desc(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk,
+                        qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
+                        h_dtype=mt.MLSTM_F32, gate=w.gate, precision=args.precision, tile_lq=w.tile_lq,
+                        tile_lkv=w.tile_lkv, schedule="two_stage")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dQ, dK = torch.empty((w.B, w.NH, w.S, w.DHQK), **f32), torch.empty((w.B, w.NH, w.S, w.DHQK), **f32)
+    dV = torch.empty((w.B, w.NH, w.S, w.DHV), **f32)
+    d_i, d_f = torch.empty((w.B, w.NH, w.S), **f32), torch.empty((w.B, w.NH, w.S), **f32)
+    dC0 = torch.empty((w.B, w.NH, w.DHQK, w.DHV), **f32) if C0 is not None else None
+    dn0 = torch.empty((w.B, w.NH, w.DHQK), **f32) if (C0 is not None and not sig) else None
+    dm0 = torch.empty((w.B, w.NH), **f32) if (C0 is not None and not sig) else None
+    ws_bytes = mt.bw_workspace_bytes(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    L = mt.lib()
+    P = lambda t: None if t is None else t.data_ptr()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    grads = (P(dH), P(dQ), P(dK), P(dV), P(d_i), P(d_f), P(dC0), P(dn0), P(dm0))
+
+    def whole():
+        st = L.mlstm_chunkwise_bw(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
+                                  *grads, P(ws), ws_bytes, sp)
+        if st:
+            raise mt.MlstmError(st, "mlstm_chunkwise_bw")
+
+    for _ in range(args.warmup):
+        whole()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        whole()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for it in range(args.steps):
+        ev[it][0].record(stream)
+        st = L.mlstm_bw_recompute(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
+                                  P(ws), ws_bytes, sp)
+        ev[it][1].record(stream)
+        st2 = L.mlstm_bw_grads(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
+                               *grads, P(ws), ws_bytes, sp)
+        ev[it][2].record(stream)
+        if st or st2:
+            raise mt.MlstmError(st or st2, "backward stage call")
+    torch.cuda.synchronize()
+    t_rec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
+    ach = flops / (t_grads * 1e-3) / 1e12
+    out = {
+        "metric": f"mLSTM chunkwise backward tokens/s, {w.gate} gate ({w.name})",
+        "value": w.B * w.S / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32-mfma/f32-acc (gradient kernels); recompute " + path_dtype(mt, desc, args.precision),
+        "data": "synthetic",
+        "config": {"workload": f"backward_{w.name}", "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK,
+                   "DHV": w.DHV, "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "dH": "float32",
+                   "precision": args.precision},
+        "stages_ms": {"recompute": t_rec, "grads": t_grads},
+        "grads_TFLOPs": ach,
+        "roofline": {"kernel": "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_FP32_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops, "traffic_source": "not profiled"},
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU gradient oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_backward(w.name, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -332,6 +332,35 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* The two stages of mlstm_chunkwise_bw, for callers that time or schedule
+ * them apart.  Same arguments as mlstm_chunkwise_bw; the same descriptor,
+ * inputs and initial state must be given to both, and the workspace must not
+ * change in between.
+ *   mlstm_bw_recompute: the forward quantities the gradient needs, into the
+ *       workspace (two-stage forward kernels: chunk states, and for the exp
+ *       gate H in float32 with the per-row m and normaliser).
+ *   mlstm_bw_grads: the gradient kernels on that workspace (float32 on fp32
+ *       matrix cores): per-position gate terms, the state-gradient recurrence
+ *       over the chunks in reverse order, dQ, dK, dV per 64-row tile, and the
+ *       gate gradients by a reverse scan over the sequence.  The workspace's
+ *       forward quantities are only read; its other regions are scratch. */
+int mlstm_bw_recompute(const mlstm_fw_desc_t* desc,
+                       const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre,
+                       const float* C0, const float* n0, const float* m0,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mlstm_bw_grads(const mlstm_fw_desc_t* desc,
+                   const void* Q, const void* K, const void* V,
+                   const float* i_pre, const float* f_pre,
+                   const float* C0, const float* n0,
+                   const void* dH,
+                   float* dQ, float* dK, float* dV,
+                   float* d_i, float* d_f,
+                   float* dC0, float* dn0, float* dm0,
+                   const void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,4 +12,12 @@ from .mlstm_oracle import (  # noqa: F401
     quadratic_fw,
     chunkwise_fw,
 )
-from .mlstm_grad import grad_fw, quadratic_fw_torch  # noqa: F401,E402
+
+
+def __getattr__(name):
+    # The gradient oracle needs torch; it is imported on first use only, so
+    # that the numpy forward oracle stays free of it.
+    if name in ("grad_fw", "quadratic_fw_torch"):
+        from . import mlstm_grad
+        return getattr(mlstm_grad, name)
+    raise AttributeError(name)

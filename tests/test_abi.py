@@ -245,6 +245,21 @@ def test_backward_refuses_before_launch():
     assert bw(ds, n0=None, m0=None, dm0=None) == 5         # sig gate: no dn0
     assert bw(ds, n0=None, m0=None, dn0=None) == 5         # sig gate: no dm0
     assert lib.mlstm_bw_workspace_bytes(None) == 0
+    # the stage calls check the same way
+    rc = lambda desc, **kw: lib.mlstm_bw_recompute(
+        ctypes.byref(desc), *[kw.get(n, 4096 * (j + 1)) for j, n in enumerate(
+            ["q", "k", "v", "i", "f", "C0", "n0", "m0", "ws"])], kw.get("ws_bytes", need), None)
+    assert rc(d, q=None) == 1
+    assert rc(d, ws_bytes=need - 1) == 6
+    assert rc(ds, n0=4096) == 5
+    gr = lambda desc, **kw: lib.mlstm_bw_grads(
+        ctypes.byref(desc), *[kw.get(n, 4096 * (j + 1)) for j, n in enumerate(
+            ["q", "k", "v", "i", "f", "C0", "n0", "dH", "dQ", "dK", "dV", "d_i", "d_f", "dC0", "dn0", "dm0",
+             "ws"])], kw.get("ws_bytes", need), None)
+    assert gr(d, dK=None) == 1
+    assert gr(d, dQ=4096 * 9 + 4) == 8
+    assert gr(d, ws=None) == 6
+    assert gr(ds, n0=None, dn0=None) == 5                 # sig gate: no dm0
 
 
 def test_backward_workspace_formula():

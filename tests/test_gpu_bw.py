@@ -159,3 +159,33 @@ def test_backward_full_size_sampled_heads(mt, wname):
                     n if w.gate == "exp" else None, m if w.gate == "exp" else None, gate=w.gate)
         gt = {k: g[k][b, h][None, t0:] for k in KEYS}
         _compare(f"{wname} head {(b, h)} tail {T}", gt, r, "bf16", KEYS)
+
+
+def test_stage_calls_match_the_whole_backward(mt):
+    """mlstm_bw_recompute then mlstm_bw_grads on one workspace give exactly
+    what mlstm_chunkwise_bw gives."""
+    import ctypes
+    x = _draw(41, 1, 2, 300, 128, 256, "bf16", "exp", True)
+    whole = _gpu(mt, x, "bf16", "exp", 64)
+    qd = torch.bfloat16
+    t = {n: _dev(x[n], qd) for n in ("q", "k", "v")}
+    t.update({n: _dev(x[n]) for n in ("i", "f", "dH", "C0", "n0", "m0")})
+    B, NH, S, DK, DV = 1, 2, 300, 128, 256
+    desc = mt.make_desc(B, NH, S, DK, DV, 64, qkv_dtype=mt.MLSTM_BF16, h_dtype=mt.MLSTM_F32, gate="exp")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = dict(dQ=torch.empty((B, NH, S, DK), **f32), dK=torch.empty((B, NH, S, DK), **f32),
+             dV=torch.empty((B, NH, S, DV), **f32), d_i=torch.empty((B, NH, S), **f32),
+             d_f=torch.empty((B, NH, S), **f32), dC0=torch.empty((B, NH, DK, DV), **f32),
+             dn0=torch.empty((B, NH, DK), **f32), dm0=torch.empty((B, NH), **f32))
+    nb = mt.bw_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    P = lambda a: a.data_ptr()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L = mt.lib()
+    assert L.mlstm_bw_recompute(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]), P(t["i"]), P(t["f"]),
+                                P(t["C0"]), P(t["n0"]), P(t["m0"]), P(ws), nb, s) == 0
+    assert L.mlstm_bw_grads(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]), P(t["i"]), P(t["f"]),
+                            P(t["C0"]), P(t["n0"]), P(t["dH"]), *[P(o[n]) for n in o], P(ws), nb, s) == 0
+    torch.cuda.synchronize()
+    for n in o:
+        np.testing.assert_array_equal(o[n].cpu().numpy().astype(np.float64), whole[n], err_msg=n)

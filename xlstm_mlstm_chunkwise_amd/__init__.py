@@ -71,6 +71,10 @@ _SYMBOLS = {
     "mlstm_bw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_bw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 18
                            + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_bw_recompute": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 9
+                           + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_bw_grads": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 17
+                       + [ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 

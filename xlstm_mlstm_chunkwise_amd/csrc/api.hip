@@ -511,33 +511,50 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc) {
   return bw_layout(&d2).total;
 }
 
-int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
                        const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
-                       const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
-                       float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
-    return MLSTM_E_NULLPTR;
-  if ((st = check_sig_nulls(desc, n0, m0, dn0, dm0)) != MLSTM_OK) return st;
-  for (const void* x : {Q, K, V, dH, static_cast<const void*>(dQ), static_cast<const void*>(dK),
-                        static_cast<const void*>(dV)})
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, m0, nullptr, nullptr)) != MLSTM_OK) return st;
+  for (const void* x : {Q, K, V})
     if (x && !aligned(x, 16)) return MLSTM_E_ALIGN;
-  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0})) != MLSTM_OK) return st;
   const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
   const BwLayout l = bw_layout(&d2);
   if (!workspace || workspace_bytes < l.total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  if (desc->S == 0) return MLSTM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const bool ex = desc->gate == MLSTM_GATE_EXP;
   auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const WsPtrs fw = ws_ptrs(&d2, workspace);
-  if (desc->S > 0) {
-    st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s);
-    if (st == MLSTM_OK) st = unpack_states(&d2, fw, at(l.Cst), ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
-    if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
-    if (st != MLSTM_OK) return st;
-  }
+  st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s);
+  if (st == MLSTM_OK) st = unpack_states(&d2, fw, at(l.Cst), ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
+  if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
+  return st;
+}
+
+int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                   const float* f_pre, const float* C0, const float* n0, const void* dH, float* dQ, float* dK,
+                   float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, const void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
+    return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, dn0, dm0, nullptr)) != MLSTM_OK) return st;
+  for (const void* x : {Q, K, V, dH, static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                        static_cast<const void*>(dV)})
+    if (x && !aligned(x, 16)) return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
+  const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
+  const BwLayout l = bw_layout(&d2);
+  if (!workspace || workspace_bytes < l.total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  const bool ex = desc->gate == MLSTM_GATE_EXP;
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   mlstm::BwParams p;
   p.Q = Q;
   p.K = K;
@@ -580,8 +597,30 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   p.Nc = (desc->S + desc->chunk_size - 1) / desc->chunk_size;
   p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
   p.dh_bf16 = desc->h_dtype == MLSTM_BF16;
-  const hipError_t e = mlstm::launch_bw(p, !ex, s);
+  const hipError_t e = mlstm::launch_bw(p, !ex, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
+                       float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
+  // all checks of both stages before anything is launched
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
+    return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n0, m0, dn0, dm0)) != MLSTM_OK) return st;
+  for (const void* x : {Q, K, V, dH, static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                        static_cast<const void*>(dV)})
+    if (x && !aligned(x, 16)) return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
+  const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
+  if (!workspace || workspace_bytes < bw_layout(&d2).total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  st = mlstm_bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, workspace, workspace_bytes, stream);
+  if (st != MLSTM_OK) return st;
+  return mlstm_bw_grads(desc, Q, K, V, i_pre, f_pre, C0, n0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0, workspace,
+                        workspace_bytes, stream);
 }
 
 }  // extern "C"
