@@ -12,6 +12,7 @@ from .mlstm_oracle import (  # noqa: F401
     quadratic_fw,
     chunkwise_fw,
 )
+from .mlstm_q8 import q8_decode, q8_encode, q8_scaled, recurrent_step_q8  # noqa: F401,E402
 
 
 def __getattr__(name):
