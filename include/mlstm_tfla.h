@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 5
+#define MLSTM_ABI_VERSION 6
 
 typedef enum {
   MLSTM_OK = 0,
@@ -284,6 +284,38 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc,
                          void* h,
                          float* C_out, float* n_out, float* m_out,
                          void* stream);
+
+/* int8 block-quantised memory state for the decode step (the
+ * "flash-xlstm-exp 0.1.0" page, section "Upgrade roadmap", lists a quantised
+ * fp8/int8 state for long-context inference).  C is held as
+ *   Cq (B, NH, DHQK, DHV) int8 codes and
+ *   Cs (B, NH, DHQK, DHV / 64) float32 scales, one per block of 64
+ *      consecutive values of a row;
+ * the block represents Cq * Cs.  A block x encodes as code =
+ * round-half-even(x * 127 / amax), amax = max |x|, with scale amax / 127
+ * (codes and scale 0 when amax = 0); the error is at most half a scale.  n
+ * and m stay float32.
+ *
+ * mlstm_recurrent_step_q8: mlstm_recurrent_step on an encoded state.  The
+ * step decodes the state, updates it in float32, reads h from the updated
+ * values (before they are encoded again) and writes the encoded update.
+ *   Cq_in, Cs_in   both NULL (zero state) or both given; Cq_in 4-byte aligned.
+ *   Cq_out, Cs_out required; they may be Cq_in, Cs_in (updated in place).
+ *   Everything else as for mlstm_recurrent_step.
+ * mlstm_state_q8_encode / _decode: a float32 state (B, NH, DHQK, DHV), such as
+ *   C_out of mlstm_chunkwise_fw, to the encoded form and back (B, NH, DHQK
+ *   and DHV from `desc`, which must be valid; S is not used). */
+int mlstm_recurrent_step_q8(const mlstm_fw_desc_t* desc,
+                            const void* q, const void* k, const void* v,
+                            const float* i_pre, const float* f_pre,
+                            const int8_t* Cq_in, const float* Cs_in,
+                            const float* n_in, const float* m_in,
+                            void* h,
+                            int8_t* Cq_out, float* Cs_out,
+                            float* n_out, float* m_out,
+                            void* stream);
+int mlstm_state_q8_encode(const mlstm_fw_desc_t* desc, const float* C, int8_t* Cq, float* Cs, void* stream);
+int mlstm_state_q8_decode(const mlstm_fw_desc_t* desc, const int8_t* Cq, const float* Cs, float* C, void* stream);
 
 /* Bytes of device workspace that mlstm_chunkwise_bw needs for `desc`: the
  * two-stage forward workspace, the recomputed forward quantities (chunk

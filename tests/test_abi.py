@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 5
+    assert mt.abi_version() == 6
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -280,6 +280,28 @@ def test_backward_workspace_formula():
         BH * S * 4, BH * S * 4,                                                  # q.dq, k.dk
         BH * DK * DV * 4, BH * DK * 4])                                          # dC0, dn0
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
+
+
+def test_q8_step_refuses_before_launch():
+    lib = mt.lib()
+    d1 = _desc(S=1, DHQK=256, DHV=512, chunk_size=64)
+
+    def step(desc, **ptrs):
+        names = ["q", "k", "v", "i", "f", "Cq_in", "Cs_in", "n_in", "m_in", "h", "Cq_out", "Cs_out", "n_out",
+                 "m_out"]
+        vals = [ptrs.get(n, 4096 * (j + 1)) for j, n in enumerate(names)]
+        return lib.mlstm_recurrent_step_q8(ctypes.byref(desc), *vals, None)
+
+    assert step(_desc(S=2, chunk_size=64)) == 2
+    assert step(d1, Cq_out=None) == 1
+    assert step(d1, Cs_out=None) == 1
+    assert step(d1, Cs_in=None) == 1                        # codes without scales
+    assert step(d1, Cq_in=4096 * 6 + 2) == 8                # codes are read in 4-byte pieces
+    assert step(d1, n_out=4096 * 8) == 9                    # n_out may not be n_in
+    ds = _desc(S=1, DHQK=256, DHV=512, chunk_size=64, gate="sig")
+    assert step(ds, n_in=None, m_in=None, n_out=None) == 5
+    assert lib.mlstm_state_q8_encode(ctypes.byref(d1), None, 4096, 8192, None) == 1
+    assert lib.mlstm_state_q8_decode(ctypes.byref(d1), 4096, 8192 + 2, 4096 * 4, None) == 8
 
 
 def test_flops_formula():

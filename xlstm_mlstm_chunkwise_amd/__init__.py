@@ -68,6 +68,9 @@ _SYMBOLS = {
     "mlstm_fw_unpack_states": (ctypes.c_int, [ctypes.POINTER(FwDesc), ctypes.c_void_p, ctypes.c_size_t]
                                + [ctypes.c_void_p] * 4),
     "mlstm_recurrent_step": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
+    "mlstm_recurrent_step_q8": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 15),
+    "mlstm_state_q8_encode": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 4),
+    "mlstm_state_q8_decode": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 4),
     "mlstm_bw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_bw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 18
                            + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -457,3 +460,82 @@ def bw_flops(B, NH, S, DHQK, DHV, chunk_size) -> float:
     four products with a state (C.dn, G.v, G^T.k and the state-gradient
     update), 8 DHQK DHV."""
     return float(B) * NH * S * ((chunk_size + 1) * (3.0 * DHQK + 2.0 * DHV) + 8.0 * DHQK * DHV)
+
+
+def _state_desc(C_like_shape):
+    B, NH, DK, DV = C_like_shape
+    return make_desc(B, NH, 1, DK, DV, 64)
+
+
+def state_q8_encode(C):
+    """float32 state (B, NH, DHQK, DHV) -> (codes int8, scales float32 of
+    shape (B, NH, DHQK, DHV // 64)); see mlstm_state_q8_encode."""
+    torch = _torch()
+    B, NH, DK, DV = C.shape
+    _check(C, "C", (B, NH, DK, DV), torch.float32)
+    Cq = torch.empty((B, NH, DK, DV), dtype=torch.int8, device=C.device)
+    Cs = torch.empty((B, NH, DK, DV // 64), dtype=torch.float32, device=C.device)
+    desc = _state_desc(C.shape)
+    st = lib().mlstm_state_q8_encode(ctypes.byref(desc), _ptr(C), _ptr(Cq), _ptr(Cs), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_state_q8_encode")
+    return Cq, Cs
+
+
+def state_q8_decode(Cq, Cs):
+    """Encoded state -> float32 (B, NH, DHQK, DHV)."""
+    torch = _torch()
+    B, NH, DK, DV = Cq.shape
+    _check(Cq, "Cq", (B, NH, DK, DV), torch.int8)
+    _check(Cs, "Cs", (B, NH, DK, DV // 64), torch.float32)
+    C = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=Cq.device)
+    desc = _state_desc(Cq.shape)
+    st = lib().mlstm_state_q8_decode(ctypes.byref(desc), _ptr(Cq), _ptr(Cs), _ptr(C), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_state_q8_decode")
+    return C
+
+
+def mlstm_recurrent_step_q8(q, k, v, i_pre, f_pre, Cq=None, Cs=None, n=None, m=None, *, gate: str = "exp",
+                            h_dtype=None, qk_scale: Optional[float] = None, eps: float = 0.0, Cq_out=None,
+                            Cs_out=None, n_out=None, m_out=None):
+    """mlstm_recurrent_step on an int8 block-quantised state (Cq, Cs), as
+    state_q8_encode returns it.  Returns (h, Cq', Cs', n', m').  Cq_out /
+    Cs_out may be Cq / Cs (updated in place)."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be (B, NH, DHQK)")
+    B, NH, DK = q.shape
+    DV = v.shape[-1]
+    _check(q, "q", (B, NH, DK))
+    _check(k, "k", (B, NH, DK), q.dtype)
+    _check(v, "v", (B, NH, DV), q.dtype)
+    _check(i_pre, "i_pre", (B, NH), torch.float32)
+    _check(f_pre, "f_pre", (B, NH), torch.float32)
+    _check(Cq, "Cq", (B, NH, DK, DV), torch.int8)
+    _check(Cs, "Cs", (B, NH, DK, DV // 64), torch.float32)
+    _check(n, "n", (B, NH, DK), torch.float32)
+    _check(m, "m", (B, NH), torch.float32)
+    h_dtype = torch.float32 if h_dtype is None else h_dtype
+    hcode = MLSTM_BF16 if h_dtype == torch.bfloat16 else MLSTM_F32
+    desc = make_desc(B, NH, 1, DK, DV, 64, qkv_dtype=_dtype_code(q), h_dtype=hcode, gate=gate,
+                     qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps))
+    dev = q.device
+    h = torch.empty((B, NH, DV), dtype=h_dtype, device=dev)
+    if Cq_out is None:
+        Cq_out = torch.empty((B, NH, DK, DV), dtype=torch.int8, device=dev)
+    if Cs_out is None:
+        Cs_out = torch.empty((B, NH, DK, DV // 64), dtype=torch.float32, device=dev)
+    _check(Cq_out, "Cq_out", (B, NH, DK, DV), torch.int8)
+    _check(Cs_out, "Cs_out", (B, NH, DK, DV // 64), torch.float32)
+    if gate != "sig":
+        if n_out is None:
+            n_out = torch.empty((B, NH, DK), dtype=torch.float32, device=dev)
+        if m_out is None:
+            m_out = torch.empty((B, NH), dtype=torch.float32, device=dev)
+    st = lib().mlstm_recurrent_step_q8(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(Cq), _ptr(Cs), _ptr(n),
+        _ptr(m), _ptr(h), _ptr(Cq_out), _ptr(Cs_out), _ptr(n_out), _ptr(m_out), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_recurrent_step_q8")
+    return h, Cq_out, Cs_out, n_out, m_out

@@ -501,7 +501,76 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc, const void* q, const void*
   p.DV = desc->DHV;
   p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
   p.h_bf16 = desc->h_dtype == MLSTM_BF16;
+  p.Cq_in = nullptr;
+  p.Cs_in = nullptr;
+  p.Cq_out = nullptr;
+  p.Cs_out = nullptr;
+  p.q8 = 0;
   const hipError_t e = mlstm::launch_step(p, desc->gate == MLSTM_GATE_SIG, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+int mlstm_recurrent_step_q8(const mlstm_fw_desc_t* desc, const void* q, const void* k, const void* v,
+                            const float* i_pre, const float* f_pre, const int8_t* Cq_in, const float* Cs_in,
+                            const float* n_in, const float* m_in, void* h, int8_t* Cq_out, float* Cs_out,
+                            float* n_out, float* m_out, void* stream) {
+  int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (desc->S != 1) return MLSTM_E_SHAPE;
+  if (!q || !k || !v || !i_pre || !f_pre || !h || !Cq_out || !Cs_out) return MLSTM_E_NULLPTR;
+  if ((Cq_in == nullptr) != (Cs_in == nullptr)) return MLSTM_E_NULLPTR;
+  if ((st = check_sig_nulls(desc, n_in, m_in, n_out, m_out)) != MLSTM_OK) return st;
+  if ((n_out && n_out == n_in) || (m_out && m_out == m_in)) return MLSTM_E_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(h, 16) || !aligned(Cq_out, 4) ||
+      (Cq_in && !aligned(Cq_in, 4)))
+    return MLSTM_E_ALIGN;
+  if ((st = check_f32_ptrs({i_pre, f_pre, Cs_in, n_in, m_in, Cs_out, n_out, m_out})) != MLSTM_OK) return st;
+  mlstm::StepParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.C_in = nullptr;
+  p.n_in = n_in;
+  p.m_in = m_in;
+  p.h = h;
+  p.C_out = nullptr;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  p.Cq_in = Cq_in;
+  p.Cs_in = Cs_in;
+  p.Cq_out = Cq_out;
+  p.Cs_out = Cs_out;
+  p.q8 = 1;
+  p.scale = resolve_scale(desc);
+  p.eps = desc->eps;
+  p.BH = desc->B * desc->NH;
+  p.DK = desc->DHQK;
+  p.DV = desc->DHV;
+  p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
+  p.h_bf16 = desc->h_dtype == MLSTM_BF16;
+  const hipError_t e = mlstm::launch_step(p, desc->gate == MLSTM_GATE_SIG, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+int mlstm_state_q8_encode(const mlstm_fw_desc_t* desc, const float* C, int8_t* Cq, float* Cs, void* stream) {
+  const int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (!C || !Cq || !Cs) return MLSTM_E_NULLPTR;
+  if (!aligned(C, 4) || !aligned(Cs, 4)) return MLSTM_E_ALIGN;
+  const long long n = (long long)desc->B * desc->NH * desc->DHQK * desc->DHV;
+  const hipError_t e = mlstm::launch_q8_encode(C, Cq, Cs, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
+int mlstm_state_q8_decode(const mlstm_fw_desc_t* desc, const int8_t* Cq, const float* Cs, float* C, void* stream) {
+  const int st = validate_desc(desc);
+  if (st != MLSTM_OK) return st;
+  if (!C || !Cq || !Cs) return MLSTM_E_NULLPTR;
+  if (!aligned(C, 4) || !aligned(Cs, 4)) return MLSTM_E_ALIGN;
+  const long long n = (long long)desc->B * desc->NH * desc->DHQK * desc->DHV;
+  const hipError_t e = mlstm::launch_q8_decode(Cq, Cs, C, n, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 

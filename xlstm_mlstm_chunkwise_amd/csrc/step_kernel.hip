@@ -26,6 +26,16 @@
 // streaming them past the Infinity Cache measured about a quarter faster than
 // ordinary accesses when the states exceed it.  Every workgroup of a head
 // forms n' and m', which its normaliser needs; the first slice writes them.
+//
+// Quantised state (Q8): the "flash-xlstm-exp 0.1.0" page (section "Upgrade
+// roadmap") lists an fp8/int8 memory state for long-context inference.  Here
+// C is held as int8 codes with one float32 scale per block of 64 consecutive
+// values of a row; a block x encodes as code = round-half-even(x * 127 / amax)
+// with scale amax / 127 (all zeros when amax = 0).  The step decodes its
+// pieces, updates them in float32, reads h from the updated values and
+// encodes them again: the 16 threads that hold one block's 64 values find its
+// amax with four lane exchanges.  The state moves in 1 + 1/16 bytes per value
+// instead of 4.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -46,7 +56,17 @@ __device__ __forceinline__ void store_stream(float* a, float4 c) {
   __builtin_nontemporal_store(x, reinterpret_cast<step_f4_t*>(a));
 }
 
-template <int DK, bool SIG, int COLS>
+__device__ __forceinline__ float4 decode4(uint32_t w, float scale) {
+  return make_float4((float)(int8_t)(w & 0xff) * scale, (float)(int8_t)((w >> 8) & 0xff) * scale,
+                     (float)(int8_t)((w >> 16) & 0xff) * scale, (float)(int8_t)(w >> 24) * scale);
+}
+
+__device__ __forceinline__ uint32_t encode1(float x, float inv) {
+  const float r = fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(int)r;
+}
+
+template <int DK, bool SIG, int COLS, bool Q8>
 __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
   constexpr int THREADS = 4 * COLS;      // COLS / 4 column quads x 16 row groups
   constexpr int RPT = DK / kStepGroups;  // rows per thread
@@ -78,13 +98,34 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
   // this thread's pieces of the state go out first: they depend on nothing
   // else, and their latency then overlaps the staging of q and k
   const size_t cbase = (size_t)bh * DK * DV + col;
+  const int NB = DV / 64;  // scale blocks per row
+  const size_t sbase = (size_t)bh * DK * NB + col / 64;
   float4 cr[RPT];
-  if (p.C_in) {
+  uint32_t cw[Q8 ? RPT : 1];
+  float cs[Q8 ? RPT : 1];
+  if constexpr (Q8) {
+    if (p.Cq_in) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) cr[r] = load_stream(p.C_in + cbase + (size_t)(rg + kStepGroups * r) * DV);
+      for (int r = 0; r < RPT; ++r) {
+        const size_t row = rg + kStepGroups * r;
+        cw[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.Cq_in + cbase + row * DV));
+        cs[r] = p.Cs_in[sbase + row * NB];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        cw[r] = 0u;
+        cs[r] = 0.0f;
+      }
+    }
   } else {
+    if (p.C_in) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) cr[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int r = 0; r < RPT; ++r) cr[r] = load_stream(p.C_in + cbase + (size_t)(rg + kStepGroups * r) * DV);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) cr[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   }
 
   // q (scaled) and k in LDS as float32; this thread's four values of v
@@ -110,13 +151,27 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int row = rg + kStepGroups * r;
-    float4 c = cr[r];
+    float4 c;
+    if constexpr (Q8) c = decode4(cw[r], cs[r]);
+    else c = cr[r];
     const float bk = b * s_k[row], qv = s_q[row];
     c.x = a * c.x + bk * v4.x;
     c.y = a * c.y + bk * v4.y;
     c.z = a * c.z + bk * v4.z;
     c.w = a * c.w + bk * v4.w;
-    store_stream(p.C_out + cbase + (size_t)row * DV, c);
+    if constexpr (Q8) {
+      // amax of the 64-value block over its 16 threads (aligned lane groups)
+      float mx = fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
+      const uint32_t w = encode1(c.x, inv) | (encode1(c.y, inv) << 8) | (encode1(c.z, inv) << 16) |
+                         (encode1(c.w, inv) << 24);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.Cq_out + cbase + (size_t)row * DV));
+      if ((cq & 15) == 0) p.Cs_out[sbase + (size_t)row * NB] = mx / 127.0f;
+    } else {
+      store_stream(p.C_out + cbase + (size_t)row * DV, c);
+    }
     acc.x += c.x * qv;
     acc.y += c.y * qv;
     acc.z += c.z * qv;
@@ -173,8 +228,14 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
 template <int DK, int COLS>
 hipError_t launch_cols(const StepParams& p, bool sig, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)p.BH * (p.DV / COLS)));
-  if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS>), grid, dim3(4 * COLS), 0, stream, p);
-  else hipLaunchKernelGGL((step_kernel<DK, false, COLS>), grid, dim3(4 * COLS), 0, stream, p);
+  const dim3 block(4 * COLS);
+  if (p.q8) {
+    if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((step_kernel<DK, false, COLS, true>), grid, block, 0, stream, p);
+  } else {
+    if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((step_kernel<DK, false, COLS, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -183,7 +244,44 @@ hipError_t launch_dk(const StepParams& p, bool sig, hipStream_t stream) {
   return p.DV % 128 == 0 ? launch_cols<DK, 128>(p, sig, stream) : launch_cols<DK, 64>(p, sig, stream);
 }
 
+// Encoding / decoding of a whole float32 state: one wave per 64-value block.
+__global__ __launch_bounds__(256) void q8_encode_kernel(const float* __restrict__ C, int8_t* __restrict__ Cq,
+                                                        float* __restrict__ Cs, long long nblocks) {
+  const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;
+  const int lane = threadIdx.x & 63;
+  const float x = C[blk * 64 + lane];
+  float mx = fabsf(x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
+  Cq[blk * 64 + lane] = (int8_t)(int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
+  if (lane == 0) Cs[blk] = mx / 127.0f;
+}
+
+__global__ __launch_bounds__(256) void q8_decode_kernel(const int8_t* __restrict__ Cq, const float* __restrict__ Cs,
+                                                        float* __restrict__ C, long long nblocks) {
+  const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;
+  const int lane = threadIdx.x & 63;
+  C[blk * 64 + lane] = (float)Cq[blk * 64 + lane] * Cs[blk];
+}
+
 }  // namespace
+
+hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long nvalues, hipStream_t stream) {
+  const long long nb = nvalues / 64;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(q8_encode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, C, Cq, Cs, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long nvalues, hipStream_t stream) {
+  const long long nb = nvalues / 64;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(q8_decode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, Cq, Cs, C, nb);
+  return hipGetLastError();
+}
 
 hipError_t launch_step(const StepParams& p, bool sig, hipStream_t stream) {
   if (p.BH == 0) return hipSuccess;
