@@ -181,6 +181,9 @@ def main(argv=None) -> int:
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent step (one token per head and call) on the workload's heads "
                          "instead of the forward pass")
+    ap.add_argument("--state", default="f32", choices=["f32", "q8"],
+                    help="with --decode: the state format (float32, or int8 codes with a float32 scale per "
+                         "64-value block)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (mlstm_chunkwise_bw) on the workload instead of the forward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -483,7 +486,9 @@ def bench_decode(args, w, mt, torch, np) -> int:
     reads and writes its state in HBM -- one token through 16 layers.  Warm:
     one state, which can stay in the Infinity Cache between calls.  Isolated:
     one call after a 512 MiB read, bracketed by events alone (includes the
-    dispatch latency of a lone kernel)."""
+    dispatch latency of a lone kernel).  --state q8 runs the step on int8
+    codes with a float32 scale per 64-value block (mlstm_recurrent_step_q8);
+    its states are encoded from the same float32 draw."""
     import ctypes
     dev = torch.device("cuda", 0)
     rng = np.random.default_rng(2024)
@@ -501,7 +506,12 @@ def bench_decode(args, w, mt, torch, np) -> int:
     i_pre = up(rng.standard_normal((B, NH)), torch.float32)
     f_pre = up(2.0 + 4.0 * rng.random((B, NH)), torch.float32)
     C0 = up(0.1 * rng.standard_normal((B, NH, DK, DV)), torch.float32)
-    Cs = [C0.clone() for _ in range(NSTATE)]
+    q8 = args.state == "q8"
+    if q8:
+        Cq0, Cs0 = mt.state_q8_encode(C0)
+        Cs = [(Cq0.clone(), Cs0.clone()) for _ in range(NSTATE)]
+    else:
+        Cs = [C0.clone() for _ in range(NSTATE)]
     # n and m alternate between two buffers per state (outputs may not alias inputs)
     ns = [[None, None] if sig else [up(rng.random((B, NH, DK)), torch.float32), torch.empty(B, NH, DK, device=dev)]
           for _ in range(NSTATE)]
@@ -511,12 +521,13 @@ def bench_decode(args, w, mt, torch, np) -> int:
     h = torch.empty(B, NH, DV, dtype=torch.float32, device=dev)
     desc = mt.make_desc(B, NH, 1, DK, DV, 64, qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
                         gate=w.gate)
-    fn = mt.lib().mlstm_recurrent_step
+    fn = mt.lib().mlstm_recurrent_step_q8 if q8 else mt.lib().mlstm_recurrent_step
     P = lambda t: None if t is None else t.data_ptr()
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    cargs = [[[ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(Cs[j]), P(ns[j][a]), P(ms[j][a]), P(h),
-               P(Cs[j]), P(ns[j][1 - a]), P(ms[j][1 - a]), sp] for a in (0, 1)] for j in range(NSTATE)]
+    st_in = (lambda j: [P(Cs[j][0]), P(Cs[j][1])]) if q8 else (lambda j: [P(Cs[j])])
+    cargs = [[[ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre)] + st_in(j) + [P(ns[j][a]), P(ms[j][a]),
+               P(h)] + st_in(j) + [P(ns[j][1 - a]), P(ms[j][1 - a]), sp] for a in (0, 1)] for j in range(NSTATE)]
     it = [0] * NSTATE
 
     def call(j):
@@ -551,12 +562,15 @@ def bench_decode(args, w, mt, torch, np) -> int:
     iso_ms = float(np.median(iso))
     el = 2 if w.qkv_dtype == "bf16" else 4
     BH = B * NH
-    abytes = (2 * BH * DK * DV * 4 + (0 if sig else 2 * BH * (DK + 1) * 4) + BH * (2 * DK + DV) * el
+    state_bytes = BH * DK * DV * (1 + 4 / 64) if q8 else BH * DK * DV * 4
+    abytes = (2 * state_bytes + (0 if sig else 2 * BH * (DK + 1) * 4) + BH * (2 * DK + DV) * el
               + BH * DV * 4 + 2 * BH * 4)
     ach = abytes / (cold_ms * 1e-3) / 1e9
-    traffic, traffic_src = recorded_traffic(f"decode_{w.name}", "step", None, "traffic_decode_7b.md")
+    traffic, traffic_src = recorded_traffic(f"decode_{w.name}", "step_q8" if q8 else "step", None,
+                                            "traffic_decode_7b.md")
     out = {
-        "metric": f"mLSTM recurrent step (decode) tokens/s, {w.gate} gate, heads of {w.name}",
+        "metric": f"mLSTM recurrent step (decode) tokens/s, {w.gate} gate, heads of {w.name}"
+                  + (", int8 block-quantised state" if q8 else ""),
         "value": B / (cold_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -569,10 +583,12 @@ def bench_decode(args, w, mt, torch, np) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"f32-state/{w.qkv_dtype}-qkv",
+        "dtype": ("int8x64-state/f32-update" if q8 else "f32-state") + f"/{w.qkv_dtype}-qkv",
         "data": "synthetic",
-        "config": {"workload": f"decode_{w.name}", "B": B, "NH": NH, "DHQK": DK, "DHV": DV, "gate": w.gate,
-                   "qkv_dtype": w.qkv_dtype, "state": "float32, updated in place",
+        "config": {"workload": f"decode_{w.name}" + ("_q8" if q8 else ""), "B": B, "NH": NH, "DHQK": DK, "DHV": DV, "gate": w.gate,
+                   "qkv_dtype": w.qkv_dtype,
+                   "state": ("int8 codes + float32 scale per 64 values, updated in place" if q8
+                             else "float32, updated in place"),
                    "states_cycled": NSTATE},
         "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes": abytes,

@@ -289,8 +289,10 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc,
  * "flash-xlstm-exp 0.1.0" page, section "Upgrade roadmap", lists a quantised
  * fp8/int8 state for long-context inference).  C is held as
  *   Cq (B, NH, DHQK, DHV) int8 codes and
- *   Cs (B, NH, DHQK, DHV / 64) float32 scales, one per block of 64
- *      consecutive values of a row;
+ *   Cs (B, NH, DHV / 64, DHQK) float32 scales, one per block of 64
+ *      consecutive values of a row: Cs[b][h][j][r] scales
+ *      Cq[b][h][r][64 j .. 64 j + 63] (block-major, so that a run of rows
+ *      moves in 16-byte pieces);
  * the block represents Cq * Cs.  A block x encodes as code =
  * round-half-even(x * 127 / amax), amax = max |x|, with scale amax / 127
  * (codes and scale 0 when amax = 0); the error is at most half a scale.  n
@@ -299,7 +301,8 @@ int mlstm_recurrent_step(const mlstm_fw_desc_t* desc,
  * mlstm_recurrent_step_q8: mlstm_recurrent_step on an encoded state.  The
  * step decodes the state, updates it in float32, reads h from the updated
  * values (before they are encoded again) and writes the encoded update.
- *   Cq_in, Cs_in   both NULL (zero state) or both given; Cq_in 4-byte aligned.
+ *   Cq_in, Cs_in   both NULL (zero state) or both given; Cq_in 4-byte and
+ *                  Cs_in 16-byte aligned (likewise Cq_out, Cs_out).
  *   Cq_out, Cs_out required; they may be Cq_in, Cs_in (updated in place).
  *   Everything else as for mlstm_recurrent_step.
  * mlstm_state_q8_encode / _decode: a float32 state (B, NH, DHQK, DHV), such as

@@ -297,6 +297,7 @@ def test_q8_step_refuses_before_launch():
     assert step(d1, Cs_out=None) == 1
     assert step(d1, Cs_in=None) == 1                        # codes without scales
     assert step(d1, Cq_in=4096 * 6 + 2) == 8                # codes are read in 4-byte pieces
+    assert step(d1, Cs_in=4096 * 7 + 4) == 8                # scales in 16-byte pieces
     assert step(d1, n_out=4096 * 8) == 9                    # n_out may not be n_in
     ds = _desc(S=1, DHQK=256, DHV=512, chunk_size=64, gate="sig")
     assert step(ds, n_in=None, m_in=None, n_out=None) == 5

@@ -9,7 +9,9 @@ from a half-integer, and within +-1 where it does.  Scales: relative 1e-5.
 h: max abs error 2e-2 (bf16 inputs) / 1e-4 (float32 inputs), the forward
 pass's bounds (h is read from the float32 update, before encoding); n, m as
 for the float step.  Inputs are seeded draws; Q, K, V rounded to bf16 for the
-bf16 cases.
+bf16 cases.  The library keeps the scales block-major, (B, NH, DHV/64,
+DHQK); the oracle's are (B, NH, DHQK, DHV/64), and the tests swap the last
+two axes between them.
 """
 import numpy as np
 import pytest
@@ -42,8 +44,17 @@ def _np(t):
     return None if t is None else t.cpu().numpy()
 
 
-def check_codes(tag, codes_gpu, scales_gpu, C_ref):
+def to_lib(scales):
+    return np.ascontiguousarray(np.swapaxes(scales, -1, -2))
+
+
+def from_lib(scales):
+    return np.swapaxes(scales, -1, -2)
+
+
+def check_codes(tag, codes_gpu, scales_lib, C_ref):
     """GPU encoding of the state whose float64 value is C_ref."""
+    scales_gpu = from_lib(scales_lib)
     codes_ref, scales_ref = q8_encode(C_ref)
     scaled = q8_scaled(C_ref)
     near = np.abs(np.abs(scaled - np.trunc(scaled)) - 0.5) < NEAR_TIE
@@ -67,7 +78,7 @@ def _draw(seed, B, NH, DK, DV, kind, gate, zero=False):
     st = {}
     if not zero:
         st["Cq"] = rng.integers(-127, 128, (B, NH, DK, DV)).astype(np.int8)
-        st["Cs"] = (0.1 * rng.random((B, NH, DK, DV // 64)) / 127).astype(np.float32)
+        st["Cs"] = (0.1 * rng.random((B, NH, DK, DV // 64)) / 127).astype(np.float32)   # oracle layout
         if gate == "exp":
             st["n"] = rng.random((B, NH, DK)).astype(np.float32)
             st["m"] = rng.standard_normal((B, NH)).astype(np.float32)
@@ -76,7 +87,8 @@ def _draw(seed, B, NH, DK, DV, kind, gate, zero=False):
 
 def _step(mt, x, st, gate, kind, inplace=False):
     qd = torch.bfloat16 if kind == "bf16" else torch.float32
-    Cq, Cs = _dev(st.get("Cq"), torch.int8), _dev(st.get("Cs"))
+    Cq = _dev(st.get("Cq"), torch.int8)
+    Cs = None if "Cs" not in st else _dev(to_lib(st["Cs"]))
     out = mt.mlstm_recurrent_step_q8(_dev(x["q"], qd), _dev(x["k"], qd), _dev(x["v"], qd), _dev(x["i"]),
                                      _dev(x["f"]), Cq, Cs, _dev(st.get("n")), _dev(st.get("m")), gate=gate,
                                      Cq_out=Cq if inplace else None, Cs_out=Cs if inplace else None)
@@ -131,7 +143,7 @@ def test_q8_encode_decode(mt):
     Cq, Cs = mt.state_q8_encode(_dev(C))
     flips = check_codes("encode", _np(Cq), _np(Cs), C.astype(np.float64))
     back = _np(mt.state_q8_decode(Cq, Cs)).astype(np.float64)
-    np.testing.assert_allclose(back, q8_decode(_np(Cq), _np(Cs).astype(np.float64)), rtol=1e-7, atol=0)
+    np.testing.assert_allclose(back, q8_decode(_np(Cq), from_lib(_np(Cs)).astype(np.float64)), rtol=1e-7, atol=0)
     assert np.all(back[0, 0, 5] == 0)
     print(f"\n[encode] codes at ties={flips}", flush=True)
 
@@ -163,7 +175,7 @@ def test_q8_decode_continues_a_forward_pass(mt, gate):
     worst, drift, hmax = 0.0, 0.0, 0.0
     for t in range(S0, S):
         x = dict(q=q[:, :, t], k=k[:, :, t], v=v[:, :, t], i=i_pre[:, :, t], f=f_pre[:, :, t])
-        st = {"Cq": _np(Cq), "Cs": _np(Cs)}
+        st = {"Cq": _np(Cq), "Cs": from_lib(_np(Cs))}
         if gate == "exp":
             st.update(n=_np(n), m=_np(m))
         h, Cq, Cs, n, m = mt.mlstm_recurrent_step_q8(*(_dev(x[a], qd) for a in ("q", "k", "v")), _dev(x["i"]),

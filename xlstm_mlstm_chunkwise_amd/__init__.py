@@ -469,12 +469,12 @@ def _state_desc(C_like_shape):
 
 def state_q8_encode(C):
     """float32 state (B, NH, DHQK, DHV) -> (codes int8, scales float32 of
-    shape (B, NH, DHQK, DHV // 64)); see mlstm_state_q8_encode."""
+    shape (B, NH, DHV // 64, DHQK), block-major); see mlstm_state_q8_encode."""
     torch = _torch()
     B, NH, DK, DV = C.shape
     _check(C, "C", (B, NH, DK, DV), torch.float32)
     Cq = torch.empty((B, NH, DK, DV), dtype=torch.int8, device=C.device)
-    Cs = torch.empty((B, NH, DK, DV // 64), dtype=torch.float32, device=C.device)
+    Cs = torch.empty((B, NH, DV // 64, DK), dtype=torch.float32, device=C.device)
     desc = _state_desc(C.shape)
     st = lib().mlstm_state_q8_encode(ctypes.byref(desc), _ptr(C), _ptr(Cq), _ptr(Cs), _stream())
     if st:
@@ -487,7 +487,7 @@ def state_q8_decode(Cq, Cs):
     torch = _torch()
     B, NH, DK, DV = Cq.shape
     _check(Cq, "Cq", (B, NH, DK, DV), torch.int8)
-    _check(Cs, "Cs", (B, NH, DK, DV // 64), torch.float32)
+    _check(Cs, "Cs", (B, NH, DV // 64, DK), torch.float32)
     C = torch.empty((B, NH, DK, DV), dtype=torch.float32, device=Cq.device)
     desc = _state_desc(Cq.shape)
     st = lib().mlstm_state_q8_decode(ctypes.byref(desc), _ptr(Cq), _ptr(Cs), _ptr(C), _stream())
@@ -513,7 +513,7 @@ def mlstm_recurrent_step_q8(q, k, v, i_pre, f_pre, Cq=None, Cs=None, n=None, m=N
     _check(i_pre, "i_pre", (B, NH), torch.float32)
     _check(f_pre, "f_pre", (B, NH), torch.float32)
     _check(Cq, "Cq", (B, NH, DK, DV), torch.int8)
-    _check(Cs, "Cs", (B, NH, DK, DV // 64), torch.float32)
+    _check(Cs, "Cs", (B, NH, DV // 64, DK), torch.float32)
     _check(n, "n", (B, NH, DK), torch.float32)
     _check(m, "m", (B, NH), torch.float32)
     h_dtype = torch.float32 if h_dtype is None else h_dtype
@@ -525,9 +525,9 @@ def mlstm_recurrent_step_q8(q, k, v, i_pre, f_pre, Cq=None, Cs=None, n=None, m=N
     if Cq_out is None:
         Cq_out = torch.empty((B, NH, DK, DV), dtype=torch.int8, device=dev)
     if Cs_out is None:
-        Cs_out = torch.empty((B, NH, DK, DV // 64), dtype=torch.float32, device=dev)
+        Cs_out = torch.empty((B, NH, DV // 64, DK), dtype=torch.float32, device=dev)
     _check(Cq_out, "Cq_out", (B, NH, DK, DV), torch.int8)
-    _check(Cs_out, "Cs_out", (B, NH, DK, DV // 64), torch.float32)
+    _check(Cs_out, "Cs_out", (B, NH, DV // 64, DK), torch.float32)
     if gate != "sig":
         if n_out is None:
             n_out = torch.empty((B, NH, DK), dtype=torch.float32, device=dev)

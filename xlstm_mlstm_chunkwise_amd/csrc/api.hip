@@ -522,9 +522,9 @@ int mlstm_recurrent_step_q8(const mlstm_fw_desc_t* desc, const void* q, const vo
   if ((st = check_sig_nulls(desc, n_in, m_in, n_out, m_out)) != MLSTM_OK) return st;
   if ((n_out && n_out == n_in) || (m_out && m_out == m_in)) return MLSTM_E_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(h, 16) || !aligned(Cq_out, 4) ||
-      (Cq_in && !aligned(Cq_in, 4)))
+      (Cq_in && !aligned(Cq_in, 4)) || !aligned(Cs_out, 16) || (Cs_in && !aligned(Cs_in, 16)))
     return MLSTM_E_ALIGN;
-  if ((st = check_f32_ptrs({i_pre, f_pre, Cs_in, n_in, m_in, Cs_out, n_out, m_out})) != MLSTM_OK) return st;
+  if ((st = check_f32_ptrs({i_pre, f_pre, n_in, m_in, n_out, m_out})) != MLSTM_OK) return st;
   mlstm::StepParams p;
   p.q = q;
   p.k = k;
@@ -559,8 +559,8 @@ int mlstm_state_q8_encode(const mlstm_fw_desc_t* desc, const float* C, int8_t* C
   if (st != MLSTM_OK) return st;
   if (!C || !Cq || !Cs) return MLSTM_E_NULLPTR;
   if (!aligned(C, 4) || !aligned(Cs, 4)) return MLSTM_E_ALIGN;
-  const long long n = (long long)desc->B * desc->NH * desc->DHQK * desc->DHV;
-  const hipError_t e = mlstm::launch_q8_encode(C, Cq, Cs, n, static_cast<hipStream_t>(stream));
+  const hipError_t e = mlstm::launch_q8_encode(C, Cq, Cs, (long long)desc->B * desc->NH, desc->DHQK, desc->DHV,
+                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
@@ -569,8 +569,8 @@ int mlstm_state_q8_decode(const mlstm_fw_desc_t* desc, const int8_t* Cq, const f
   if (st != MLSTM_OK) return st;
   if (!C || !Cq || !Cs) return MLSTM_E_NULLPTR;
   if (!aligned(C, 4) || !aligned(Cs, 4)) return MLSTM_E_ALIGN;
-  const long long n = (long long)desc->B * desc->NH * desc->DHQK * desc->DHV;
-  const hipError_t e = mlstm::launch_q8_decode(Cq, Cs, C, n, static_cast<hipStream_t>(stream));
+  const hipError_t e = mlstm::launch_q8_decode(Cq, Cs, C, (long long)desc->B * desc->NH, desc->DHQK, desc->DHV,
+                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 

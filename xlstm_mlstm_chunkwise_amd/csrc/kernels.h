@@ -99,7 +99,8 @@ struct StepParams {
   float* n_out;       // may be null; must not alias n_in
   float* m_out;       // may be null; must not alias m_in
   // int8 block-quantised state (q8 = 1): codes (BH, DK, DV) and one float32
-  // scale per 64 values of a row (BH, DK, DV / 64); C_in / C_out unused
+  // scale per 64 values of a row, block-major (BH, DV / 64, DK); C_in /
+  // C_out unused
   const int8_t* Cq_in;  // may be null (zero state); may equal Cq_out
   const float* Cs_in;   // null exactly when Cq_in is; may equal Cs_out
   int8_t* Cq_out;
@@ -158,9 +159,12 @@ bool walk_supported(int DK, int DV, int L, bool bf16_inputs, bool split);
 long long walk_workgroups(int BH, int DV);
 hipError_t launch_walk(const WalkParams& p, bool sig, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, bool sig, hipStream_t stream);
-// int8 block encoding of a float32 state and back (nvalues a multiple of 64).
-hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long nvalues, hipStream_t stream);
-hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long nvalues, hipStream_t stream);
+// int8 block encoding of a float32 state (BH, DK, DV) and back; scales
+// block-major (BH, DV / 64, DK).
+hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long BH, int DK, int DV,
+                            hipStream_t stream);
+hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long BH, int DK, int DV,
+                            hipStream_t stream);
 hipError_t launch_bw(const BwParams& p, bool sig, hipStream_t stream);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);

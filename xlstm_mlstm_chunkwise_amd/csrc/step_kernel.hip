@@ -33,16 +33,28 @@
 // values of a row; a block x encodes as code = round-half-even(x * 127 / amax)
 // with scale amax / 127 (all zeros when amax = 0).  The step decodes its
 // pieces, updates them in float32, reads h from the updated values and
-// encodes them again: the 16 threads that hold one block's 64 values find its
-// amax with four lane exchanges.  The state moves in 1 + 1/16 bytes per value
-// instead of 4.
+// encodes them again: the 16 threads that hold one block's 64 values (one DPP
+// row of 16 lanes) find its amax with four DPP max steps, and 127 / amax
+// comes from the reciprocal instruction (1 ulp).  In this mode each thread
+// holds a run of DHQK/16 consecutive rows, so the scales, stored block-major
+// (BH, DHV/64, DHQK), move in 16-byte pieces.  The state moves in 1 + 1/16
+// bytes per value instead of 4.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace mlstm {
 namespace {
 
-constexpr int kStepGroups = 16;  // row groups per workgroup
+constexpr int kStepGroups = 16;  // row groups per workgroup (float state)
+constexpr int kQ8Groups = 32;    // row groups per workgroup (quantised state), at most
+constexpr int kQ8Cols = 128;     // columns per workgroup (quantised state), at most
+
+// Row groups of a workgroup: the quantised state keeps runs of at least four
+// rows per thread (its scales move in 16-byte pieces).
+template <int DK, bool Q8>
+constexpr int step_groups() {
+  return Q8 ? (DK / 4 < kQ8Groups ? DK / 4 : kQ8Groups) : kStepGroups;
+}
 
 typedef float step_f4_t __attribute__((ext_vector_type(4)));
 
@@ -56,22 +68,39 @@ __device__ __forceinline__ void store_stream(float* a, float4 c) {
   __builtin_nontemporal_store(x, reinterpret_cast<step_f4_t*>(a));
 }
 
-__device__ __forceinline__ float4 decode4(uint32_t w, float scale) {
-  return make_float4((float)(int8_t)(w & 0xff) * scale, (float)(int8_t)((w >> 8) & 0xff) * scale,
-                     (float)(int8_t)((w >> 16) & 0xff) * scale, (float)(int8_t)(w >> 24) * scale);
+// The code of x as the low byte of fma(x, inv, 1.5 * 2^23): for |x * inv| <
+// 2^22 the sum lies where floats are spaced by one, so the single rounding of
+// the fma is round-half-even of x * inv, and the low mantissa bits hold it in
+// two's complement.  |x * inv| <= 127 (1 + 2^-21) for |x| <= amax, which
+// rounds into [-127, 127].
+__device__ __forceinline__ uint32_t encode_bits(float x, float inv) {
+  return __float_as_uint(fmaf(x, inv, 12582912.0f));
 }
 
-__device__ __forceinline__ uint32_t encode1(float x, float inv) {
-  const float r = fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
-  return (uint32_t)(uint8_t)(int8_t)(int)r;
+// Low bytes of four words into one word (byte i from word i).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// max over the 16 lanes of a DPP row: swap lanes within quads (xor 1, xor 2),
+// then mirror within half-rows and within the row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+  return x;
 }
 
 template <int DK, bool SIG, int COLS, bool Q8>
-__global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
-  constexpr int THREADS = 4 * COLS;      // COLS / 4 column quads x 16 row groups
-  constexpr int RPT = DK / kStepGroups;  // rows per thread
+__global__ __launch_bounds__((COLS / 4 * step_groups<DK, Q8>())) void step_kernel(const StepParams p) {
+  constexpr int RG = step_groups<DK, Q8>();         // row groups
+  constexpr int THREADS = COLS / 4 * RG;            // COLS / 4 column quads x RG row groups
+  constexpr int RPT = DK / RG;                      // rows per thread
   __shared__ float s_q[DK], s_k[DK];
-  __shared__ float4 s_red[kStepGroups][COLS / 4];
+  __shared__ float4 s_red[RG][COLS / 4];
   __shared__ float s_dot[THREADS / 64];
 
   const int DV = p.DV;
@@ -98,18 +127,28 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
   // this thread's pieces of the state go out first: they depend on nothing
   // else, and their latency then overlaps the staging of q and k
   const size_t cbase = (size_t)bh * DK * DV + col;
-  const int NB = DV / 64;  // scale blocks per row
-  const size_t sbase = (size_t)bh * DK * NB + col / 64;
+  // row of this thread's r-th piece: strided for the float state, a run of
+  // RPT consecutive rows for the quantised one
+  auto row_of = [&](int r) { return Q8 ? rg * RPT + r : rg + RG * r; };
+  // scales of this thread's block, block-major: (BH, DV/64, DK)
+  const size_t sbase = ((size_t)bh * (DV / 64) + col / 64) * DK + (size_t)rg * RPT;
   float4 cr[RPT];
   uint32_t cw[Q8 ? RPT : 1];
   float cs[Q8 ? RPT : 1];
   if constexpr (Q8) {
+    static_assert(RPT % 4 == 0, "scales move in groups of four rows");
     if (p.Cq_in) {
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const size_t row = rg + kStepGroups * r;
-        cw[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.Cq_in + cbase + row * DV));
-        cs[r] = p.Cs_in[sbase + row * NB];
+      for (int r = 0; r < RPT; ++r)
+        cw[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(p.Cq_in + cbase + (size_t)row_of(r) * DV));
+#pragma unroll
+      for (int r = 0; r < RPT; r += 4) {
+        const float4 s4 = *reinterpret_cast<const float4*>(p.Cs_in + sbase + r);
+        cs[r] = s4.x;
+        cs[r + 1] = s4.y;
+        cs[r + 2] = s4.z;
+        cs[r + 3] = s4.w;
       }
     } else {
 #pragma unroll
@@ -148,27 +187,37 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
 
   // ---- the state update C' = a C + b k v^T, and s C'^T q for four columns
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float smax[Q8 ? RPT : 1];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    const int row = rg + kStepGroups * r;
+    const int row = row_of(r);
     float4 c;
-    if constexpr (Q8) c = decode4(cw[r], cs[r]);
-    else c = cr[r];
     const float bk = b * s_k[row], qv = s_q[row];
-    c.x = a * c.x + bk * v4.x;
-    c.y = a * c.y + bk * v4.y;
-    c.z = a * c.z + bk * v4.z;
-    c.w = a * c.w + bk * v4.w;
     if constexpr (Q8) {
-      // amax of the 64-value block over its 16 threads (aligned lane groups)
-      float mx = fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)));
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
-      const uint32_t w = encode1(c.x, inv) | (encode1(c.y, inv) << 8) | (encode1(c.z, inv) << 16) |
-                         (encode1(c.w, inv) << 24);
+      // a (code * scale) + bk v with the code read as the unsigned byte
+      // code + 128: (code + 128) (a scale) + (bk v - 128 a scale)
+      const uint32_t u = cw[r] ^ 0x80808080u;
+      const float as = a * cs[r], nb = -128.0f * as;
+      c.x = fmaf((float)(u & 0xffu), as, fmaf(bk, v4.x, nb));
+      c.y = fmaf((float)((u >> 8) & 0xffu), as, fmaf(bk, v4.y, nb));
+      c.z = fmaf((float)((u >> 16) & 0xffu), as, fmaf(bk, v4.z, nb));
+      c.w = fmaf((float)(u >> 24), as, fmaf(bk, v4.w, nb));
+    } else {
+      c = cr[r];
+      c.x = a * c.x + bk * v4.x;
+      c.y = a * c.y + bk * v4.y;
+      c.z = a * c.z + bk * v4.z;
+      c.w = a * c.w + bk * v4.w;
+    }
+    if constexpr (Q8) {
+      // amax of the 64-value block over its 16 threads (one DPP row)
+      const float mx = row16_max(fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+      const float inv = mx >= 1.17549435e-38f ? 127.0f * __builtin_amdgcn_rcpf(mx)
+                                              : (mx > 0.0f ? 127.0f / mx : 0.0f);
+      const uint32_t w = pack_low_bytes(encode_bits(c.x, inv), encode_bits(c.y, inv), encode_bits(c.z, inv),
+                                        encode_bits(c.w, inv));
       __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.Cq_out + cbase + (size_t)row * DV));
-      if ((cq & 15) == 0) p.Cs_out[sbase + (size_t)row * NB] = mx / 127.0f;
+      smax[r] = mx;
     } else {
       store_stream(p.C_out + cbase + (size_t)row * DV, c);
     }
@@ -176,6 +225,15 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
     acc.y += c.y * qv;
     acc.z += c.z * qv;
     acc.w += c.w * qv;
+  }
+  if constexpr (Q8) {
+    if ((cq & 15) == 0) {
+      constexpr float k127 = 1.0f / 127.0f;
+#pragma unroll
+      for (int r = 0; r < RPT; r += 4)
+        *reinterpret_cast<float4*>(p.Cs_out + sbase + r) =
+            make_float4(smax[r] * k127, smax[r + 1] * k127, smax[r + 2] * k127, smax[r + 3] * k127);
+    }
   }
   s_red[rg][cq] = acc;
 
@@ -203,7 +261,7 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
   if (rg == 0) {
     float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-    for (int g = 0; g < kStepGroups; ++g) {
+    for (int g = 0; g < RG; ++g) {
       const float4 x = s_red[g][cq];
       num.x += x.x;
       num.y += x.y;
@@ -225,28 +283,34 @@ __global__ __launch_bounds__(4 * COLS) void step_kernel(const StepParams p) {
   }
 }
 
-template <int DK, int COLS>
+template <int DK, int COLS, bool Q8>
 hipError_t launch_cols(const StepParams& p, bool sig, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)p.BH * (p.DV / COLS)));
-  const dim3 block(4 * COLS);
-  if (p.q8) {
-    if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((step_kernel<DK, false, COLS, true>), grid, block, 0, stream, p);
-  } else {
-    if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((step_kernel<DK, false, COLS, false>), grid, block, 0, stream, p);
-  }
+  const dim3 block(COLS / 4 * step_groups<DK, Q8>());
+  if (sig) hipLaunchKernelGGL((step_kernel<DK, true, COLS, Q8>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((step_kernel<DK, false, COLS, Q8>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <int DK>
 hipError_t launch_dk(const StepParams& p, bool sig, hipStream_t stream) {
-  return p.DV % 128 == 0 ? launch_cols<DK, 128>(p, sig, stream) : launch_cols<DK, 64>(p, sig, stream);
+  if (p.q8) {
+    if (kQ8Cols == 128 && p.DV % 128 == 0) return launch_cols<DK, 128, true>(p, sig, stream);
+    return launch_cols<DK, 64, true>(p, sig, stream);
+  }
+  return p.DV % 128 == 0 ? launch_cols<DK, 128, false>(p, sig, stream) : launch_cols<DK, 64, false>(p, sig, stream);
 }
 
-// Encoding / decoding of a whole float32 state: one wave per 64-value block.
+// Encoding / decoding of a whole float32 state (BH, DK, DV): one wave per
+// 64-value block; block b of row r of head bh has its scale at
+// ((bh * DV/64) + b) * DK + r.
+__device__ __forceinline__ long long scale_index(long long blk, int DK, int NB) {
+  const long long row = blk / NB;  // bh * DK + r
+  return ((row / DK) * NB + blk % NB) * DK + row % DK;
+}
+
 __global__ __launch_bounds__(256) void q8_encode_kernel(const float* __restrict__ C, int8_t* __restrict__ Cq,
-                                                        float* __restrict__ Cs, long long nblocks) {
+                                                        float* __restrict__ Cs, long long nblocks, int DK, int NB) {
   const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;
   const int lane = threadIdx.x & 63;
@@ -255,31 +319,35 @@ __global__ __launch_bounds__(256) void q8_encode_kernel(const float* __restrict_
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
-  Cq[blk * 64 + lane] = (int8_t)(int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
-  if (lane == 0) Cs[blk] = mx / 127.0f;
+  Cq[blk * 64 + lane] = (int8_t)(int)rintf(x * inv);
+  if (lane == 0) Cs[scale_index(blk, DK, NB)] = mx / 127.0f;
 }
 
 __global__ __launch_bounds__(256) void q8_decode_kernel(const int8_t* __restrict__ Cq, const float* __restrict__ Cs,
-                                                        float* __restrict__ C, long long nblocks) {
+                                                        float* __restrict__ C, long long nblocks, int DK, int NB) {
   const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;
   const int lane = threadIdx.x & 63;
-  C[blk * 64 + lane] = (float)Cq[blk * 64 + lane] * Cs[blk];
+  C[blk * 64 + lane] = (float)Cq[blk * 64 + lane] * Cs[scale_index(blk, DK, NB)];
 }
 
 }  // namespace
 
-hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long nvalues, hipStream_t stream) {
-  const long long nb = nvalues / 64;
+hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long BH, int DK, int DV,
+                            hipStream_t stream) {
+  const long long nb = BH * DK * (DV / 64);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(q8_encode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, C, Cq, Cs, nb);
+  hipLaunchKernelGGL(q8_encode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, C, Cq, Cs, nb, DK,
+                     DV / 64);
   return hipGetLastError();
 }
 
-hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long nvalues, hipStream_t stream) {
-  const long long nb = nvalues / 64;
+hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long BH, int DK, int DV,
+                            hipStream_t stream) {
+  const long long nb = BH * DK * (DV / 64);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(q8_decode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, Cq, Cs, C, nb);
+  hipLaunchKernelGGL(q8_decode_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, Cq, Cs, C, nb, DK,
+                     DV / 64);
   return hipGetLastError();
 }
 
