@@ -32,15 +32,29 @@ CSRC = os.path.join(ROOT, "xlstm_mlstm_chunkwise_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def csrc_sha256() -> str:
-    """Hash of every kernel source file (name and bytes, sorted by name)."""
+# The source files whose bytes decide each profiled kernel's code: its own
+# file (kernel and launch), the gate-terms kernel it reads from, and the
+# shared device helpers.
+KERNEL_SOURCES = {
+    "walk": ("walk_kernel.hip", "gates_kernel.hip", "device_common.h"),
+    "states": ("states2_kernel.hip", "gates_kernel.hip", "device_common.h"),
+    "hintra": ("hintra2_kernel.hip", "device_common.h"),
+    "step": ("step_kernel.hip", "device_common.h"),
+    "step_q8": ("step_kernel.hip", "device_common.h"),
+}
+
+
+def csrc_sha256(kernel: str = None) -> str:
+    """Hash of the kernel's source files (name and bytes, in a fixed order),
+    or of every source file when no kernel is named."""
     import hashlib
+    names = KERNEL_SOURCES[kernel] if kernel else sorted(
+        n for n in os.listdir(CSRC) if n.endswith((".hip", ".h")))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as fh:
-                h.update(fh.read())
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -89,7 +103,7 @@ def recorded_traffic(workload: str, kernel: str, tile_lq, fname: str = None) -> 
                 rec = kv
     if not rec:
         return None, "kernel not in counter summary"
-    if rec.get("source_sha256") != csrc_sha256():
+    if rec.get("source_sha256") != csrc_sha256(kernel):
         return None, "kernel sources changed since the counters were taken"
     b = float(rec["fetch_kib"]) * 1024 * float(rec["fetch_scale"]) + \
         float(rec["write_kib"]) * 1024 * float(rec["write_scale"])
