@@ -502,6 +502,339 @@ __global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The same three modes for bf16 inputs on bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 (l / 16) + e] and
+// B[8 (l / 16) + e][l % 16], e = 0..7).  Q, K and V enter unchanged; every
+// operand computed in float32 (dH / z, the states, the weighted score tiles)
+// is carried as a bf16 hi + lo pair, so a product with one computed side
+// takes two passes and one with two computed sides three (hi.hi + hi.lo +
+// lo.hi).  LDS tiles hold bf16 bits, row stride kLd16.  The output product
+// reads its A operand from a transposed tile [y][partner row]; its B operand
+// is the pair of score accumulators (partner blocks 2p, 2p+1) split to bf16:
+// slot e stands for partner row 32 p + 16 (e / 4) + 4 (l / 16) + e % 4.
+constexpr int kLd16 = 72;
+
+// dst rows (row-major, contraction along the row): r < nrows from src, else 0.
+// With `split` the value (times rowscale) is carried as hi + lo; without it
+// the source must be bf16 and is copied bit for bit.
+__device__ __forceinline__ void stage_rows16(uint16_t* hi, uint16_t* lo, const void* src, bool bf16, size_t row0,
+                                             int D, int col0, int nrows, const float* rowscale) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  uint4 h0, h1, l0 = make_uint4(0, 0, 0, 0), l1 = make_uint4(0, 0, 0, 0);
+  if (r >= nrows) {
+    h0 = h1 = make_uint4(0, 0, 0, 0);
+  } else if (!lo) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (row0 + r) * (size_t)D +
+                                                    col0 + c);
+    h0 = q[0];
+    h1 = q[1];
+  } else {
+    float x[16];
+    load16(src, bf16, (row0 + r) * (size_t)D + col0 + c, x);
+    const float sc = rowscale ? rowscale[r] : 1.0f;
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16x2(x[2 * i] * sc, x[2 * i + 1] * sc, hw[i], lw[i]);
+    h0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    h1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    l0 = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    l1 = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  }
+  uint4* dh = reinterpret_cast<uint4*>(hi + r * kLd16 + c);
+  dh[0] = h0;
+  dh[1] = h1;
+  if (lo) {
+    uint4* dl = reinterpret_cast<uint4*>(lo + r * kLd16 + c);
+    dl[0] = l0;
+    dl[1] = l1;
+  }
+}
+
+// The transpose: dst[c * kLd16 + r] for source row r, column c.
+__device__ __forceinline__ void stage_cols16(uint16_t* hi, uint16_t* lo, const void* src, bool bf16, size_t row0,
+                                             int D, int col0, int nrows, const float* rowscale) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  float x[16];
+  if (r < nrows) {
+    load16(src, bf16, (row0 + r) * (size_t)D + col0 + c, x);
+    const float sc = rowscale ? rowscale[r] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] *= sc;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t hw, lw;
+    split_bf16x2(x[i], x[i + 1], hw, lw);
+    hi[(c + i) * kLd16 + r] = (uint16_t)(hw & 0xffff);
+    hi[(c + i + 1) * kLd16 + r] = (uint16_t)(hw >> 16);
+    if (lo) {
+      lo[(c + i) * kLd16 + r] = (uint16_t)(lw & 0xffff);
+      lo[(c + i + 1) * kLd16 + r] = (uint16_t)(lw >> 16);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8_t frag16(const uint16_t* t, int row, int k0) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(t + row * kLd16 + k0));
+}
+
+// A fragment of the output product from a transposed tile: row y, slots
+// e = 0..3 at partner rows o0 .. o0+3 and e = 4..7 at o0+16 .. o0+19.
+__device__ __forceinline__ bf16x8_t frag16_pair(const uint16_t* t, int y, int o0) {
+  const uint2 a = *reinterpret_cast<const uint2*>(t + y * kLd16 + o0);
+  const uint2 b = *reinterpret_cast<const uint2*>(t + y * kLd16 + o0 + 16);
+  return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+template <int MODE, bool SIG, int NY>
+__global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
+  constexpr int W = 16 * NY;
+  __shared__ __align__(16) uint16_t s_x[2][kT * kLd16];  // partner tile [o][x] (hi, lo)
+  __shared__ __align__(16) uint16_t s_w[2][kT * kLd16];  // own tile [w][x] (hi, lo)
+  __shared__ __align__(16) uint16_t s_y[2][kT * kLd16];  // output-side operand, transposed (hi, lo)
+  __shared__ RowGates g_own, g_oth;
+
+  const int nT = p.L / kT;
+  const int ot = blockIdx.x % nT;
+  const int rest = blockIdx.x / nT;
+  const int c = rest % p.Nc, bh = rest / p.Nc;
+  const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
+  const int own0 = ot * kT;
+  if (own0 >= Lc) return;
+  const int nown = min(kT, Lc - own0);
+  const size_t rb = (size_t)bh * p.S + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const int DK = p.DK, DV = p.DV, Nc = p.Nc;
+  const int DO = MODE == kModeDV ? DV : DK;
+  const int y0 = blockIdx.y * W;
+  const bool hb = p.dh_bf16;
+
+  load_rows<SIG>(g_own, p, rb, own0, Lc);
+  __syncthreads();
+  const int w = 16 * wave + l16;
+  const bool own_ok = w < nown;
+  const float ob = g_own.b[w], osrc = g_own.src[w];
+  const float om = SIG ? 0.0f : g_own.m[w];
+  const float odelta = SIG ? 0.0f : g_own.delta[w];
+  const float gc = p.gb[rb + Lc - 1];
+
+  float4_t acc[NY];
+#pragma unroll
+  for (int i = 0; i < NY; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // ---- inter-chunk term: out^T[y][w] = sum_x A[y][x] B[w][x]
+  {
+    bool run;
+    const float* St;  // the state: rows k, columns v
+    if constexpr (MODE == kModeDQ) {
+      run = c > 0 || p.C0 || p.n0;
+      St = p.C_states + ((size_t)bh * (Nc + 1) + c) * DK * DV;
+    } else {
+      run = c < Nc - 1;
+      St = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+    }
+    if (run) {
+      const int XD = MODE == kModeDV ? DK : DV;
+      constexpr bool own_split = MODE == kModeDQ;  // dH / z; V and K enter raw
+      for (int x0 = 0; x0 < XD; x0 += kT) {
+        __syncthreads();
+        if constexpr (MODE == kModeDQ)
+          stage_rows16(s_w[0], s_w[1], p.dH, hb, rb + own0, DV, x0, nown, SIG ? nullptr : g_own.invz);
+        else if constexpr (MODE == kModeDK)
+          stage_rows16(s_w[0], nullptr, p.V, true, rb + own0, DV, x0, nown, nullptr);
+        else
+          stage_rows16(s_w[0], nullptr, p.K, true, rb + own0, DK, x0, nown, nullptr);
+        for (int yc = 0; yc < W / kT; ++yc) {
+          __syncthreads();
+          if constexpr (MODE == kModeDV)
+            stage_cols16(s_y[0], s_y[1], St, false, x0, DV, y0 + yc * kT, kT, nullptr);   // [e][k]
+          else
+            stage_rows16(s_y[0], s_y[1], St, false, y0 + yc * kT, DV, x0, kT, nullptr);   // [k][v]
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int k0 = 32 * j + 8 * g4;
+            const bf16x8_t bh_ = frag16(s_w[0], w, k0);
+            bf16x8_t bl_;
+            if constexpr (own_split) bl_ = frag16(s_w[1], w, k0);
+#pragma unroll
+            for (int yb = 0; yb < 4; ++yb) {
+              const bf16x8_t ah = frag16(s_y[0], 16 * yb + l16, k0);
+              const bf16x8_t al = frag16(s_y[1], 16 * yb + l16, k0);
+              float4_t a_ = acc[4 * yc + yb];
+              a_ = mma16b(ah, bh_, a_);
+              a_ = mma16b(al, bh_, a_);
+              if constexpr (own_split) a_ = mma16b(ah, bl_, a_);
+              acc[4 * yc + yb] = a_;
+            }
+          }
+        }
+      }
+      if constexpr (MODE == kModeDQ) {
+        float wq;
+        if constexpr (SIG) wq = own_ok ? expf(ob) : 0.0f;
+        else wq = own_ok ? expf(ob + p.m_states[(size_t)bh * (Nc + 1) + c] - om) : 0.0f;
+        const float* nst = SIG ? nullptr : p.n_states + ((size_t)bh * (Nc + 1) + c) * DK;
+#pragma unroll
+        for (int yb = 0; yb < NY; ++yb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[yb][r] * wq;
+            if constexpr (!SIG) x += odelta * wq * nst[y0 + 16 * yb + 4 * g4 + r];
+            acc[yb][r] = x;
+          }
+      } else {
+        const float Mo = SIG ? 0.0f : p.m_states[(size_t)bh * (Nc + 1) + c + 1];
+        const float wk = own_ok ? expf(gc - ob + osrc - Mo) : 0.0f;
+        if constexpr (MODE == kModeDK) {
+          const float* Nst = SIG ? nullptr : p.dn_states + ((size_t)bh * Nc + c) * DK;
+          const float f = wk / p.scale;
+#pragma unroll
+          for (int yb = 0; yb < NY; ++yb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float x = acc[yb][r];
+              if constexpr (!SIG) x += Nst[y0 + 16 * yb + 4 * g4 + r];
+              acc[yb][r] = x * f;
+            }
+        } else {
+#pragma unroll
+          for (int yb = 0; yb < NY; ++yb) acc[yb] *= wk;
+        }
+      }
+    }
+  }
+
+  // ---- intra-chunk term
+  const int lo = MODE == kModeDQ ? 0 : ot;
+  const int hi = MODE == kModeDQ ? ot : (Lc - 1) / kT;
+  for (int xt = lo; xt <= hi; ++xt) {
+    const int x0 = xt * kT, nx = min(kT, Lc - x0);
+    __syncthreads();
+    load_rows<SIG>(g_oth, p, rb, x0, Lc);
+    float4_t sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int XD = MODE == kModeDV ? DK : DV;
+    // which side of the score product is computed (dH / z)
+    constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
+    for (int c0 = 0; c0 < XD; c0 += kT) {
+      __syncthreads();
+      if constexpr (MODE == kModeDQ) {
+        stage_rows16(s_x[0], nullptr, p.V, true, rb + x0, DV, c0, nx, nullptr);
+        stage_rows16(s_w[0], s_w[1], p.dH, hb, rb + own0, DV, c0, nown, SIG ? nullptr : g_own.invz);
+      } else if constexpr (MODE == kModeDK) {
+        stage_rows16(s_x[0], s_x[1], p.dH, hb, rb + x0, DV, c0, nx, SIG ? nullptr : g_oth.invz);
+        stage_rows16(s_w[0], nullptr, p.V, true, rb + own0, DV, c0, nown, nullptr);
+      } else {
+        stage_rows16(s_x[0], nullptr, p.Q, true, rb + x0, DK, c0, nx, nullptr);
+        stage_rows16(s_w[0], nullptr, p.K, true, rb + own0, DK, c0, nown, nullptr);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k0 = 32 * j + 8 * g4;
+        const bf16x8_t bh_ = frag16(s_w[0], w, k0);
+        bf16x8_t bl_;
+        if constexpr (w_split) bl_ = frag16(s_w[1], w, k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t ah = frag16(s_x[0], 16 * i + l16, k0);
+          float4_t a_ = mma16b(ah, bh_, sc[i]);
+          if constexpr (w_split) a_ = mma16b(ah, bl_, a_);
+          if constexpr (x_split) a_ = mma16b(frag16(s_x[1], 16 * i + l16, k0), bh_, a_);
+          sc[i] = a_;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = 16 * i + 4 * g4 + r;
+        float x = 0.0f;
+        if constexpr (MODE == kModeDQ) {
+          if (own_ok && o < nx && x0 + o <= own0 + w) {
+            const float ex = ob - g_oth.b[o] + g_oth.src[o] - om;
+            x = expf(ex) * (sc[i][r] + odelta);
+          }
+        } else {
+          if (own_ok && o < nx && own0 + w <= x0 + o) {
+            const float ex = g_oth.b[o] - ob + osrc - (SIG ? 0.0f : g_oth.m[o]);
+            if constexpr (MODE == kModeDK) x = expf(ex) * (sc[i][r] + (SIG ? 0.0f : g_oth.delta[o]));
+            else x = expf(ex) * p.scale * sc[i][r];
+          }
+        }
+        sc[i][r] = x;
+      }
+    // the weighted tile as bf16 hi + lo B fragments, one per 32 partner rows
+    bf16x8_t bsh[2], bsl[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t hw[4], lw[4];
+      split_bf16x2(sc[2 * q][0], sc[2 * q][1], hw[0], lw[0]);
+      split_bf16x2(sc[2 * q][2], sc[2 * q][3], hw[1], lw[1]);
+      split_bf16x2(sc[2 * q + 1][0], sc[2 * q + 1][1], hw[2], lw[2]);
+      split_bf16x2(sc[2 * q + 1][2], sc[2 * q + 1][3], hw[3], lw[3]);
+      bsh[q] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      bsl[q] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    }
+    // output product: out^T[y][w] += sum_o Y[o][y] sc[o][w]
+    constexpr bool y_split = MODE == kModeDV;  // dH / z; K and Q enter raw
+    for (int yc = 0; yc < W / kT; ++yc) {
+      __syncthreads();
+      if constexpr (MODE == kModeDQ)
+        stage_cols16(s_y[0], nullptr, p.K, true, rb + x0, DK, y0 + yc * kT, nx, nullptr);
+      else if constexpr (MODE == kModeDK)
+        stage_cols16(s_y[0], nullptr, p.Q, true, rb + x0, DK, y0 + yc * kT, nx, nullptr);
+      else
+        stage_cols16(s_y[0], s_y[1], p.dH, hb, rb + x0, DV, y0 + yc * kT, nx, SIG ? nullptr : g_oth.invz);
+      __syncthreads();
+#pragma unroll
+      for (int yb = 0; yb < 4; ++yb) {
+        float4_t a_ = acc[4 * yc + yb];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8_t ah = frag16_pair(s_y[0], 16 * yb + l16, 32 * q + 4 * g4);
+          a_ = mma16b(ah, bsh[q], a_);
+          a_ = mma16b(ah, bsl[q], a_);
+          if constexpr (y_split) a_ = mma16b(frag16_pair(s_y[1], 16 * yb + l16, 32 * q + 4 * g4), bsh[q], a_);
+        }
+        acc[4 * yc + yb] = a_;
+      }
+    }
+  }
+
+  // ---- epilogue (as the float32 kernel)
+  const float fin = MODE == kModeDV ? 1.0f : p.scale;
+  float* out = MODE == kModeDQ ? p.dQ : MODE == kModeDK ? p.dK : p.dV;
+  float dot = 0.0f;
+  if (own_ok) {
+    const size_t orow = rb + own0 + w;
+#pragma unroll
+    for (int yb = 0; yb < NY; ++yb) {
+      const int y = y0 + 16 * yb + 4 * g4;
+      const float4 o4 = make_float4(acc[yb][0] * fin, acc[yb][1] * fin, acc[yb][2] * fin, acc[yb][3] * fin);
+      *reinterpret_cast<float4*>(out + orow * DO + y) = o4;
+      if constexpr (MODE != kModeDV) {
+        const uint16_t* src = static_cast<const uint16_t*>(MODE == kModeDQ ? p.Q : p.K);
+        const uint2 u = *reinterpret_cast<const uint2*>(src + orow * DK + y);
+        dot += __uint_as_float(u.x << 16) * o4.x + __uint_as_float(u.x & 0xffff0000u) * o4.y +
+               __uint_as_float(u.y << 16) * o4.z + __uint_as_float(u.y & 0xffff0000u) * o4.w;
+      }
+    }
+  }
+  if constexpr (MODE != kModeDV) {
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    if (g4 == 0 && own_ok) (MODE == kModeDQ ? p.qdq : p.kdk)[rb + own0 + w] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Gate gradients: one workgroup per head runs the reverse scan of
 // q.dq - k.dk over the sequence in blocks of 1024 positions; dm0.
 template <bool SIG>
@@ -560,14 +893,20 @@ hipError_t zero(float* x, long long n, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int MODE, bool SIG, int NY>
+void launch_tiles_ny(const BwParams& p, dim3 grid, hipStream_t s) {
+  if (p.qkv_bf16) hipLaunchKernelGGL((bw_tiles16_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
+}
+
 template <int MODE, bool SIG>
 hipError_t launch_tiles(const BwParams& p, int W, hipStream_t s) {
   const dim3 grid((unsigned)((long long)p.BH * p.Nc * (p.L / kT)), (unsigned)((MODE == kModeDV ? p.DV : p.DK) / W));
   switch (W / 16) {
-    case 4: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 4>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 8>), grid, dim3(256), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 16>), grid, dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, 32>), grid, dim3(256), 0, s, p); break;
+    case 4: launch_tiles_ny<MODE, SIG, 4>(p, grid, s); break;
+    case 8: launch_tiles_ny<MODE, SIG, 8>(p, grid, s); break;
+    case 16: launch_tiles_ny<MODE, SIG, 16>(p, grid, s); break;
+    case 32: launch_tiles_ny<MODE, SIG, 32>(p, grid, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
