@@ -402,8 +402,10 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     quantities recomputed, then the gradient kernels) with a float32 dH drawn
     N(0, 1), timed with HIP events around back-to-back calls; then the two
     stages apart (mlstm_bw_recompute, mlstm_bw_grads) for the stage times.
-    The roofline prices the gradient stage, whose products all run on fp32
-    matrix cores, against the fp32 dense matrix-core peak."""
+    The roofline prices the gradient stage's algorithmic FLOPs against the
+    dense peak of the matrix cores it runs on: bf16 for bf16 inputs (the
+    computed operands go as hi + lo pairs, so 2-3 passes per product), fp32
+    for float32 inputs."""
     import ctypes
     q, k, v, i_pre, f_pre, C0, n0, m0 = inputs
     dev = q.device
@@ -461,6 +463,11 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
     ach = flops / (t_grads * 1e-3) / 1e12
+    # bf16 inputs: bf16 matrix cores (computed operands as hi + lo pairs);
+    # float32 inputs: fp32 matrix cores.  Each is priced at its own peak.
+    bf16_path = w.qkv_dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16_path else PEAK_FP32_TFLOPS
+    grads_dtype = "bf16x2-mfma/f32-acc" if bf16_path else "f32-mfma/f32-acc"
     out = {
         "metric": f"mLSTM chunkwise backward tokens/s, {w.gate} gate ({w.name})",
         "value": w.B * w.S / (ms * 1e-3),
@@ -472,7 +479,7 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32-mfma/f32-acc (gradient kernels); recompute " + path_dtype(mt, desc, args.precision),
+        "dtype": grads_dtype + " (gradient kernels); recompute " + path_dtype(mt, desc, args.precision),
         "data": "synthetic",
         "config": {"workload": f"backward_{w.name}", "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK,
                    "DHV": w.DHV, "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "dH": "float32",
@@ -480,7 +487,7 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "stages_ms": {"recompute": t_rec, "grads": t_grads},
         "grads_TFLOPs": ach,
         "roofline": {"kernel": "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
-                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_FP32_TFLOPS, "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
                      "algorithmic_flops": flops, "traffic_source": "not profiled"},
     }
     if not args.no_cpu_baseline:

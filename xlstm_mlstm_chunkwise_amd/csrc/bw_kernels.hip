@@ -33,8 +33,9 @@
 //   d f_t = sigmoid(-f_t) sum_{u >= t} (q_u . dq_u - k_u . dk_u)
 // and dm0 = sum(dC0 * C0) + dn0 . n0.
 //
-// Kernels, all on fp32 matrix cores (v_mfma_f32_16x16x4_f32: exact products
-// of float32 operands, fp32 accumulation), 256 threads each:
+// Kernels, 256 threads each; with float32 inputs on fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: exact products of float32 operands), with bf16
+// inputs on bf16 matrix cores with computed operands split (below):
 //   bw_prep    per position: b, src, 1/z, delta
 //   bw_dstate  the reverse recurrence of (G, N): one workgroup per head and
 //              64 x 64 tile of G, chunks in reverse order; G_c goes to HBM
@@ -589,6 +590,93 @@ __device__ __forceinline__ bf16x8_t frag16_pair(const uint16_t* t, int y, int o0
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// The state-gradient recurrence on bf16 matrix cores (bf16 inputs): per
+// 64-position stage, G[k][v] += sum_t Q[t][k] W[t][v] with W = s e^{b + M - m}
+// dn the computed operand; both sides are staged transposed ([k][t] and
+// [v][t], W as hi + lo), so the contraction over t runs along LDS rows.
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
+  __shared__ __align__(16) uint16_t s_qt[kT * kLd16];     // Q^T [k][t]
+  __shared__ __align__(16) uint16_t s_wt[2][kT * kLd16];  // W^T [v][t] (hi, lo)
+  __shared__ float s_w[kT], s_wd[kT];
+  const int bh = blockIdx.x, kt = blockIdx.y, vt = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const int DK = p.DK, DV = p.DV, Nc = p.Nc;
+  const bool own_n = !SIG && vt == 0;
+  float4_t acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float dn = 0.0f;
+  for (int c = Nc - 1; c >= 0; --c) {
+    float* G = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        G[(size_t)(kt * kT + 16 * wave + 4 * g4 + r) * DV + vt * kT + 16 * nb + l16] = acc[nb][r];
+    if (own_n && tid < kT) p.dn_states[((size_t)bh * Nc + c) * DK + kt * kT + tid] = dn;
+
+    const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
+    const size_t rb = (size_t)bh * p.S + t0;
+    const float g = p.gb[rb + Lc - 1];
+    float Min = 0.0f, decay;
+    if constexpr (SIG) {
+      decay = expf(g);
+    } else {
+      Min = p.m_states[(size_t)bh * (Nc + 1) + c];
+      decay = expf(Min + g - p.m_states[(size_t)bh * (Nc + 1) + c + 1]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] *= decay;
+    dn *= decay;
+
+    for (int ts = 0; ts < Lc; ts += kT) {
+      const int nr = min(kT, Lc - ts);
+      if (tid < kT) {
+        float w = 0.0f, wd = 0.0f;
+        if (tid < nr) {
+          const size_t r = rb + ts + tid;
+          if constexpr (SIG) {
+            w = p.scale * expf(p.gb[r]);
+          } else {
+            const float e = p.scale * expf(p.gb[r] + Min - p.m_rows[r]);
+            w = e * p.ginvz[r];
+            wd = e * p.gdelta[r];
+          }
+        }
+        s_w[tid] = w;
+        s_wd[tid] = wd;
+      }
+      __syncthreads();
+      stage_cols16(s_qt, nullptr, p.Q, true, rb + ts, DK, kt * kT, nr, nullptr);
+      stage_cols16(s_wt[0], s_wt[1], p.dH, p.dh_bf16, rb + ts, DV, vt * kT, nr, s_w);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k0 = 32 * j + 8 * g4;
+        const bf16x8_t a = frag16(s_qt, 16 * wave + l16, k0);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          acc[nb] = mma16b(a, frag16(s_wt[0], 16 * nb + l16, k0), acc[nb]);
+          acc[nb] = mma16b(a, frag16(s_wt[1], 16 * nb + l16, k0), acc[nb]);
+        }
+      }
+      if (own_n && tid < kT)
+        for (int t = 0; t < nr; ++t) dn += s_wd[t] * __uint_as_float((uint32_t)s_qt[tid * kLd16 + t] << 16);
+      __syncthreads();
+    }
+  }
+  if (p.dC0) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p.dC0[(size_t)bh * DK * DV + (size_t)(kt * kT + 16 * wave + 4 * g4 + r) * DV + vt * kT + 16 * nb + l16] =
+            acc[nb][r];
+  }
+  if (own_n && p.dn0 && tid < kT) p.dn0[(size_t)bh * DK + kt * kT + tid] = dn;
+}
+
 template <int MODE, bool SIG, int NY>
 __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   constexpr int W = 16 * NY;
@@ -917,8 +1005,9 @@ hipError_t launch_all(const BwParams& p, hipStream_t s) {
   hipError_t e;
   hipLaunchKernelGGL((bw_prep_kernel<SIG>), dim3((unsigned)(p.BH * p.Nc)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bw_dstate_kernel<SIG>), dim3((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT)),
-                     dim3(256), 0, s, p);
+  const dim3 gs((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT));
+  if (p.qkv_bf16) hipLaunchKernelGGL((bw_dstate16_kernel<SIG>), gs, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((bw_dstate_kernel<SIG>), gs, dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
   if ((e = launch_tiles<kModeDK, SIG>(p, p.DK, s)) != hipSuccess) return e;

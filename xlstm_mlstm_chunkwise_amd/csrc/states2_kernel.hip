@@ -746,17 +746,6 @@ hipError_t launch_t(const StatesParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Packed state -> float32 (B, NH, N_c + 1, DK, DV).
-__global__ __launch_bounds__(256) void unpack_states_kernel(const uint16_t* P, float* C, long long total, int DK,
-                                                            int DV) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const long long per = (long long)DK * DV;
-  const long long s = i / per;
-  const int k = (int)((i % per) / DV), v = (int)(i % DV);
-  C[i] = unpack_state_elem_bf16(P + s * per * 2, k, v, DV);
-}
-
 }  // namespace
 
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
@@ -789,16 +778,6 @@ hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipSt
   }
   if (sig) return split ? launch_t<64, true, true>(p, stream) : launch_t<64, true, false>(p, stream);
   return split ? launch_t<64, false, true>(p, stream) : launch_t<64, false, false>(p, stream);
-}
-
-hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
-                                hipStream_t stream) {
-  const long long total = n_states * DK * DV;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(unpack_states_kernel, dim3(blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(packed), C, total, DK, DV);
-  return hipGetLastError();
 }
 
 }  // namespace mlstm

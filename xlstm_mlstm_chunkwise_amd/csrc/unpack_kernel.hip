@@ -1,0 +1,49 @@
+// Packed chunk states -> float32 row-major (n_states, DK, DV).
+//
+// The wide kernels keep each state as bf16 hi + lo fragments of 16 rows x 32
+// columns (device_common.h, packed chunk-state layout): lane l of a fragment
+// holds column 32 nb + l % 32 and, in its eight slots e, rows
+// 16 kk + (e < 4 ? 0 : 8) + 4 (l / 32) + e % 4.  One thread per fragment lane
+// reads its 16-byte hi and lo pieces and writes the eight values; the 32
+// lanes of a half-wave write 128 contiguous bytes of a row each time.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mlstm {
+namespace {
+
+__global__ __launch_bounds__(256) void unpack_states_kernel(const uint16_t* __restrict__ P, float* __restrict__ C,
+                                                            long long nfrag_lanes, int DK, int DV) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nfrag_lanes) return;
+  const int lane = (int)(i & 63);
+  const long long frag = i >> 6;                 // (state, kk, nb)
+  const int nfr = (DK / 16) * (DV / 32);         // fragments per state
+  const long long st = frag / nfr;
+  const int f = (int)(frag % nfr), kk = f / (DV / 32), nb = f % (DV / 32);
+  const uint16_t* src = P + st * (long long)DK * DV * 2;
+  const uint4 hi = *reinterpret_cast<const uint4*>(src + pack_frag_offset(kk, nb, 0, DV) + lane * 8);
+  const uint4 lo = *reinterpret_cast<const uint4*>(src + pack_frag_offset(kk, nb, 1, DV) + lane * 8);
+  const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+  float* dst = C + st * (long long)DK * DV + (size_t)(32 * nb + (lane & 31));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = e & 1 ? hw[e >> 1] & 0xffff0000u : hw[e >> 1] << 16;
+    const uint32_t l = e & 1 ? lw[e >> 1] & 0xffff0000u : lw[e >> 1] << 16;
+    const int k = 16 * kk + (e < 4 ? 0 : 8) + 4 * (lane >> 5) + (e & 3);
+    dst[(size_t)k * DV] = __uint_as_float(h) + __uint_as_float(l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
+                                hipStream_t stream) {
+  const long long lanes = n_states * (DK / 16) * (DV / 32) * 64;
+  if (lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(unpack_states_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(packed), C, lanes, DK, DV);
+  return hipGetLastError();
+}
+
+}  // namespace mlstm
