@@ -677,6 +677,54 @@ __global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
   if (own_n && p.dn0 && tid < kT) p.dn0[(size_t)bh * DK + kt * kT + tid] = dn;
 }
 
+// Staging in two halves, so that the global loads of the next tile are in
+// flight while the matrix cores work on the current one: pre16 loads this
+// thread's 16 values of a tile into registers, put_rows / put_cols write them
+// to LDS (row-major or transposed) as bf16, split into hi + lo where a lo
+// plane is given (a raw bf16 value converts exactly).
+__device__ __forceinline__ void pre16(float (&x)[16], const void* src, bool bf16, size_t row0, int D, int col0,
+                                      int nrows) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  if (r < nrows) {
+    load16(src, bf16, (row0 + r) * (size_t)D + col0 + c, x);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+  }
+}
+
+__device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo, const float (&x)[16], const float* rowscale) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  const float sc = rowscale ? rowscale[r] : 1.0f;
+  uint32_t hw[8], lw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split_bf16x2(x[2 * i] * sc, x[2 * i + 1] * sc, hw[i], lw[i]);
+  uint4* dh = reinterpret_cast<uint4*>(hi + r * kLd16 + c);
+  dh[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  dh[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+  if (lo) {
+    uint4* dl = reinterpret_cast<uint4*>(lo + r * kLd16 + c);
+    dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  }
+}
+
+__device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo, const float (&x)[16], const float* rowscale) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  const float sc = rowscale ? rowscale[r] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t hw, lw;
+    split_bf16x2(x[i] * sc, x[i + 1] * sc, hw, lw);
+    hi[(c + i) * kLd16 + r] = (uint16_t)(hw & 0xffff);
+    hi[(c + i + 1) * kLd16 + r] = (uint16_t)(hw >> 16);
+    if (lo) {
+      lo[(c + i) * kLd16 + r] = (uint16_t)(lw & 0xffff);
+      lo[(c + i + 1) * kLd16 + r] = (uint16_t)(lw >> 16);
+    }
+  }
+}
+
 template <int MODE, bool SIG, int NY>
 __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   constexpr int W = 16 * NY;
@@ -713,7 +761,13 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
 #pragma unroll
   for (int i = 0; i < NY; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- inter-chunk term: out^T[y][w] = sum_x A[y][x] B[w][x]
+  // the own tile's operand of a contraction chunk: dH (dq), V (dk), K (dv)
+  const void* own_src = MODE == kModeDQ ? p.dH : MODE == kModeDK ? p.V : p.K;
+  const bool own_bf16 = MODE == kModeDQ ? hb : true;
+  const int own_D = MODE == kModeDV ? DK : DV;
+  constexpr bool own_split = MODE == kModeDQ;
+
+  // ---- inter-chunk term: out^T[y][w] = sum_x A[y][x] B[w][x], over (x chunk, y chunk) pairs
   {
     bool run;
     const float* St;  // the state: rows k, columns v
@@ -725,40 +779,47 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
       St = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
     }
     if (run) {
-      const int XD = MODE == kModeDV ? DK : DV;
-      constexpr bool own_split = MODE == kModeDQ;  // dH / z; V and K enter raw
-      for (int x0 = 0; x0 < XD; x0 += kT) {
+      constexpr int NYC = W / kT;
+      const int nxc = own_D / kT;
+      // state tile of (x chunk, y chunk): [k][v] for dq/dk, transposed to [v][k] for dv
+      auto pre_state = [&](float (&x)[16], int xi, int yc) {
+        if constexpr (MODE == kModeDV) pre16(x, St, false, xi * kT, DV, y0 + yc * kT, kT);
+        else pre16(x, St, false, y0 + yc * kT, DV, xi * kT, kT);
+      };
+      float pw[16], py[16];
+      pre16(pw, own_src, own_bf16, rb + own0, own_D, 0, nown);
+      pre_state(py, 0, 0);
+      for (int xi = 0; xi < nxc; ++xi) {
+#pragma unroll
+        for (int yc = 0; yc < NYC; ++yc) {
         __syncthreads();
-        if constexpr (MODE == kModeDQ)
-          stage_rows16(s_w[0], s_w[1], p.dH, hb, rb + own0, DV, x0, nown, SIG ? nullptr : g_own.invz);
-        else if constexpr (MODE == kModeDK)
-          stage_rows16(s_w[0], nullptr, p.V, true, rb + own0, DV, x0, nown, nullptr);
-        else
-          stage_rows16(s_w[0], nullptr, p.K, true, rb + own0, DK, x0, nown, nullptr);
-        for (int yc = 0; yc < W / kT; ++yc) {
-          __syncthreads();
-          if constexpr (MODE == kModeDV)
-            stage_cols16(s_y[0], s_y[1], St, false, x0, DV, y0 + yc * kT, kT, nullptr);   // [e][k]
-          else
-            stage_rows16(s_y[0], s_y[1], St, false, y0 + yc * kT, DV, x0, kT, nullptr);   // [k][v]
-          __syncthreads();
+        if (yc == 0) put_rows(s_w[0], own_split ? s_w[1] : nullptr, pw, own_split && !SIG ? g_own.invz : nullptr);
+        if constexpr (MODE == kModeDV) put_cols(s_y[0], s_y[1], py, nullptr);
+        else put_rows(s_y[0], s_y[1], py, nullptr);
+        __syncthreads();
+        if (yc + 1 < NYC) {
+          pre_state(py, xi, yc + 1);
+        } else if (xi + 1 < nxc) {
+          pre16(pw, own_src, own_bf16, rb + own0, own_D, (xi + 1) * kT, nown);
+          pre_state(py, xi + 1, 0);
+        }
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int k0 = 32 * j + 8 * g4;
-            const bf16x8_t bh_ = frag16(s_w[0], w, k0);
-            bf16x8_t bl_;
-            if constexpr (own_split) bl_ = frag16(s_w[1], w, k0);
+        for (int j = 0; j < 2; ++j) {
+          const int k0 = 32 * j + 8 * g4;
+          const bf16x8_t bh_ = frag16(s_w[0], w, k0);
+          bf16x8_t bl_;
+          if constexpr (own_split) bl_ = frag16(s_w[1], w, k0);
 #pragma unroll
-            for (int yb = 0; yb < 4; ++yb) {
-              const bf16x8_t ah = frag16(s_y[0], 16 * yb + l16, k0);
-              const bf16x8_t al = frag16(s_y[1], 16 * yb + l16, k0);
-              float4_t a_ = acc[4 * yc + yb];
-              a_ = mma16b(ah, bh_, a_);
-              a_ = mma16b(al, bh_, a_);
-              if constexpr (own_split) a_ = mma16b(ah, bl_, a_);
-              acc[4 * yc + yb] = a_;
-            }
+          for (int yb = 0; yb < 4; ++yb) {
+            const bf16x8_t ah = frag16(s_y[0], 16 * yb + l16, k0);
+            const bf16x8_t al = frag16(s_y[1], 16 * yb + l16, k0);
+            float4_t a_ = acc[4 * yc + yb];
+            a_ = mma16b(ah, bh_, a_);
+            a_ = mma16b(al, bh_, a_);
+            if constexpr (own_split) a_ = mma16b(ah, bl_, a_);
+            acc[4 * yc + yb] = a_;
           }
+        }
         }
       }
       if constexpr (MODE == kModeDQ) {
@@ -799,6 +860,15 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   // ---- intra-chunk term
   const int lo = MODE == kModeDQ ? 0 : ot;
   const int hi = MODE == kModeDQ ? ot : (Lc - 1) / kT;
+  // the partner tile's operand of the score contraction: V (dq), dH (dk), Q (dv)
+  const void* x_src = MODE == kModeDQ ? p.V : MODE == kModeDK ? p.dH : p.Q;
+  const bool x_bf16 = MODE == kModeDK ? hb : true;
+  constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
+  // the partner tile's operand of the output product: K (dq), Q (dk), dH (dv)
+  const void* y_src = MODE == kModeDQ ? p.K : MODE == kModeDK ? p.Q : p.dH;
+  const bool y_bf16 = MODE == kModeDV ? hb : true;
+  const int y_D = MODE == kModeDV ? DV : DK;
+  constexpr bool y_split = MODE == kModeDV;
   for (int xt = lo; xt <= hi; ++xt) {
     const int x0 = xt * kT, nx = min(kT, Lc - x0);
     __syncthreads();
@@ -806,22 +876,19 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
     float4_t sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int XD = MODE == kModeDV ? DK : DV;
-    // which side of the score product is computed (dH / z)
-    constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
-    for (int c0 = 0; c0 < XD; c0 += kT) {
+    const int nc = own_D / kT;  // contraction chunks (the own tile's width)
+    float px[16], pw[16];
+    pre16(px, x_src, x_bf16, rb + x0, own_D, 0, nx);
+    pre16(pw, own_src, own_bf16, rb + own0, own_D, 0, nown);
+    for (int ci = 0; ci < nc; ++ci) {
       __syncthreads();
-      if constexpr (MODE == kModeDQ) {
-        stage_rows16(s_x[0], nullptr, p.V, true, rb + x0, DV, c0, nx, nullptr);
-        stage_rows16(s_w[0], s_w[1], p.dH, hb, rb + own0, DV, c0, nown, SIG ? nullptr : g_own.invz);
-      } else if constexpr (MODE == kModeDK) {
-        stage_rows16(s_x[0], s_x[1], p.dH, hb, rb + x0, DV, c0, nx, SIG ? nullptr : g_oth.invz);
-        stage_rows16(s_w[0], nullptr, p.V, true, rb + own0, DV, c0, nown, nullptr);
-      } else {
-        stage_rows16(s_x[0], nullptr, p.Q, true, rb + x0, DK, c0, nx, nullptr);
-        stage_rows16(s_w[0], nullptr, p.K, true, rb + own0, DK, c0, nown, nullptr);
+      put_rows(s_x[0], x_split ? s_x[1] : nullptr, px, x_split && !SIG ? g_oth.invz : nullptr);
+      put_rows(s_w[0], w_split ? s_w[1] : nullptr, pw, w_split && !SIG ? g_own.invz : nullptr);
+      __syncthreads();
+      if (ci + 1 < nc) {
+        pre16(px, x_src, x_bf16, rb + x0, own_D, (ci + 1) * kT, nx);
+        pre16(pw, own_src, own_bf16, rb + own0, own_D, (ci + 1) * kT, nown);
       }
-      __syncthreads();
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int k0 = 32 * j + 8 * g4;
@@ -838,6 +905,9 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
         }
       }
     }
+    // first output-side tile in flight during the weighting
+    float py[16];
+    pre16(py, y_src, y_bf16, rb + x0, y_D, y0, nx);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -871,16 +941,13 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
       bsl[q] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
     // output product: out^T[y][w] += sum_o Y[o][y] sc[o][w]
-    constexpr bool y_split = MODE == kModeDV;  // dH / z; K and Q enter raw
-    for (int yc = 0; yc < W / kT; ++yc) {
+    constexpr int NYC = W / kT;
+#pragma unroll
+    for (int yc = 0; yc < NYC; ++yc) {
       __syncthreads();
-      if constexpr (MODE == kModeDQ)
-        stage_cols16(s_y[0], nullptr, p.K, true, rb + x0, DK, y0 + yc * kT, nx, nullptr);
-      else if constexpr (MODE == kModeDK)
-        stage_cols16(s_y[0], nullptr, p.Q, true, rb + x0, DK, y0 + yc * kT, nx, nullptr);
-      else
-        stage_cols16(s_y[0], s_y[1], p.dH, hb, rb + x0, DV, y0 + yc * kT, nx, SIG ? nullptr : g_oth.invz);
+      put_cols(s_y[0], y_split ? s_y[1] : nullptr, py, y_split && !SIG ? g_oth.invz : nullptr);
       __syncthreads();
+      if (yc + 1 < NYC) pre16(py, y_src, y_bf16, rb + x0, y_D, y0 + (yc + 1) * kT, nx);
 #pragma unroll
       for (int yb = 0; yb < 4; ++yb) {
         float4_t a_ = acc[4 * yc + yb];
