@@ -205,7 +205,7 @@ def main(argv=None) -> int:
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
 
