@@ -393,7 +393,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc,
                    float* dQ, float* dK, float* dV,
                    float* d_i, float* d_f,
                    float* dC0, float* dn0, float* dm0,
-                   const void* workspace, size_t workspace_bytes,
+                   void* workspace, size_t workspace_bytes,
                    void* stream);
 
 #ifdef __cplusplus

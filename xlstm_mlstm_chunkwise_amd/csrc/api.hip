@@ -607,7 +607,7 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
 
 int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
                    const float* f_pre, const float* C0, const float* n0, const void* dH, float* dQ, float* dK,
-                   float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, const void* workspace,
+                   float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, void* workspace,
                    size_t workspace_bytes, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
@@ -621,7 +621,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
   const BwLayout l = bw_layout(&d2);
   if (!workspace || workspace_bytes < l.total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
-  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  char* ws = static_cast<char*>(workspace);
   const bool ex = desc->gate == MLSTM_GATE_EXP;
   auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   mlstm::BwParams p;

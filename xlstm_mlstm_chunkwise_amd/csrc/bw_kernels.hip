@@ -515,42 +515,6 @@ __global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
 // slot e stands for partner row 32 p + 16 (e / 4) + 4 (l / 16) + e % 4.
 constexpr int kLd16 = 72;
 
-// dst rows (row-major, contraction along the row): r < nrows from src, else 0.
-// With `split` the value (times rowscale) is carried as hi + lo; without it
-// the source must be bf16 and is copied bit for bit.
-__device__ __forceinline__ void stage_rows16(uint16_t* hi, uint16_t* lo, const void* src, bool bf16, size_t row0,
-                                             int D, int col0, int nrows, const float* rowscale) {
-  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
-  uint4 h0, h1, l0 = make_uint4(0, 0, 0, 0), l1 = make_uint4(0, 0, 0, 0);
-  if (r >= nrows) {
-    h0 = h1 = make_uint4(0, 0, 0, 0);
-  } else if (!lo) {
-    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (row0 + r) * (size_t)D +
-                                                    col0 + c);
-    h0 = q[0];
-    h1 = q[1];
-  } else {
-    float x[16];
-    load16(src, bf16, (row0 + r) * (size_t)D + col0 + c, x);
-    const float sc = rowscale ? rowscale[r] : 1.0f;
-    uint32_t hw[8], lw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) split_bf16x2(x[2 * i] * sc, x[2 * i + 1] * sc, hw[i], lw[i]);
-    h0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    h1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-    l0 = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    l1 = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-  }
-  uint4* dh = reinterpret_cast<uint4*>(hi + r * kLd16 + c);
-  dh[0] = h0;
-  dh[1] = h1;
-  if (lo) {
-    uint4* dl = reinterpret_cast<uint4*>(lo + r * kLd16 + c);
-    dl[0] = l0;
-    dl[1] = l1;
-  }
-}
-
 // The transpose: dst[c * kLd16 + r] for source row r, column c.
 __device__ __forceinline__ void stage_cols16(uint16_t* hi, uint16_t* lo, const void* src, bool bf16, size_t row0,
                                              int D, int col0, int nrows, const float* rowscale) {
