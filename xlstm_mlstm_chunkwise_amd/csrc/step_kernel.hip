@@ -84,15 +84,9 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// max over the 16 lanes of a DPP row: swap lanes within quads (xor 1, xor 2),
-// then mirror within half-rows and within the row.
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
-  return x;
-}
+// DPP controls for the block maximum over the 16 lanes of a DPP row: swap
+// within quads (0xB1: xor 1, 0x4E: xor 2), then mirror within half-rows
+// (0x141) and within the row (0x140).
 
 template <int DK, bool SIG, int COLS, bool Q8>
 __global__ __launch_bounds__((COLS / 4 * step_groups<DK, Q8>())) void step_kernel(const StepParams p) {
@@ -187,52 +181,77 @@ __global__ __launch_bounds__((COLS / 4 * step_groups<DK, Q8>())) void step_kerne
 
   // ---- the state update C' = a C + b k v^T, and s C'^T q for four columns
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float smax[Q8 ? RPT : 1];
+  if constexpr (Q8) {
+    // in phases over the thread's rows, so that the block maxima of all rows
+    // go through the DPP steps side by side
+    float4 cn[RPT];
+    float mx[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int row = row_of(r);
-    float4 c;
-    const float bk = b * s_k[row], qv = s_q[row];
-    if constexpr (Q8) {
+    for (int r = 0; r < RPT; ++r) {
+      const int row = row_of(r);
+      const float bk = b * s_k[row], qv = s_q[row];
       // a (code * scale) + bk v with the code read as the unsigned byte
       // code + 128: (code + 128) (a scale) + (bk v - 128 a scale)
       const uint32_t u = cw[r] ^ 0x80808080u;
       const float as = a * cs[r], nb = -128.0f * as;
+      float4 c;
       c.x = fmaf((float)(u & 0xffu), as, fmaf(bk, v4.x, nb));
       c.y = fmaf((float)((u >> 8) & 0xffu), as, fmaf(bk, v4.y, nb));
       c.z = fmaf((float)((u >> 16) & 0xffu), as, fmaf(bk, v4.z, nb));
       c.w = fmaf((float)(u >> 24), as, fmaf(bk, v4.w, nb));
-    } else {
-      c = cr[r];
-      c.x = a * c.x + bk * v4.x;
-      c.y = a * c.y + bk * v4.y;
-      c.z = a * c.z + bk * v4.z;
-      c.w = a * c.w + bk * v4.w;
+      acc.x += c.x * qv;
+      acc.y += c.y * qv;
+      acc.z += c.z * qv;
+      acc.w += c.w * qv;
+      cn[r] = c;
+      mx[r] = fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)));
     }
-    if constexpr (Q8) {
-      // amax of the 64-value block over its 16 threads (one DPP row)
-      const float mx = row16_max(fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
-      const float inv = mx >= 1.17549435e-38f ? 127.0f * __builtin_amdgcn_rcpf(mx)
-                                              : (mx > 0.0f ? 127.0f / mx : 0.0f);
+    // amax of each 64-value block over its 16 threads (one DPP row); the
+    // values are >= 0, whose bit patterns order as unsigned integers
+    uint32_t mb[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mb[r] = __float_as_uint(mx[r]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mb[r] = max(mb[r], (uint32_t)__builtin_amdgcn_mov_dpp((int)mb[r], 0xB1, 0xF, 0xF, true));
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mb[r] = max(mb[r], (uint32_t)__builtin_amdgcn_mov_dpp((int)mb[r], 0x4E, 0xF, 0xF, true));
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mb[r] = max(mb[r], (uint32_t)__builtin_amdgcn_mov_dpp((int)mb[r], 0x141, 0xF, 0xF, true));
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mb[r] = max(mb[r], (uint32_t)__builtin_amdgcn_mov_dpp((int)mb[r], 0x140, 0xF, 0xF, true));
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) mx[r] = __uint_as_float(mb[r]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const float m = mx[r];
+      const float inv = m >= 1.17549435e-38f ? 127.0f * __builtin_amdgcn_rcpf(m) : (m > 0.0f ? 127.0f / m : 0.0f);
+      const float4 c = cn[r];
       const uint32_t w = pack_low_bytes(encode_bits(c.x, inv), encode_bits(c.y, inv), encode_bits(c.z, inv),
                                         encode_bits(c.w, inv));
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.Cq_out + cbase + (size_t)row * DV));
-      smax[r] = mx;
-    } else {
-      store_stream(p.C_out + cbase + (size_t)row * DV, c);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.Cq_out + cbase + (size_t)row_of(r) * DV));
     }
-    acc.x += c.x * qv;
-    acc.y += c.y * qv;
-    acc.z += c.z * qv;
-    acc.w += c.w * qv;
-  }
-  if constexpr (Q8) {
     if ((cq & 15) == 0) {
       constexpr float k127 = 1.0f / 127.0f;
 #pragma unroll
       for (int r = 0; r < RPT; r += 4)
         *reinterpret_cast<float4*>(p.Cs_out + sbase + r) =
-            make_float4(smax[r] * k127, smax[r + 1] * k127, smax[r + 2] * k127, smax[r + 3] * k127);
+            make_float4(mx[r] * k127, mx[r + 1] * k127, mx[r + 2] * k127, mx[r + 3] * k127);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = row_of(r);
+      const float bk = b * s_k[row], qv = s_q[row];
+      float4 c = cr[r];
+      c.x = a * c.x + bk * v4.x;
+      c.y = a * c.y + bk * v4.y;
+      c.z = a * c.z + bk * v4.z;
+      c.w = a * c.w + bk * v4.w;
+      store_stream(p.C_out + cbase + (size_t)row * DV, c);
+      acc.x += c.x * qv;
+      acc.y += c.y * qv;
+      acc.z += c.z * qv;
+      acc.w += c.w * qv;
     }
   }
   s_red[rg][cq] = acc;
