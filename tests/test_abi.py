@@ -265,8 +265,9 @@ def test_backward_refuses_before_launch():
 def test_backward_workspace_formula():
     """Workspace of the 7B-shaped backward: the forward's two-stage workspace
     plus float32 chunk states, H, six per-position arrays, the state gradients
-    after each chunk and the initial-state gradients, each region rounded up
-    to 256 bytes."""
+    after each chunk, the initial-state gradients and (bf16 inputs) the
+    weighted dS tiles that the dk pass hands to the dq pass, each region
+    rounded up to 256 bytes."""
     d = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
     lib = mt.lib()
     BH, S, DK, DV, Nc = 64, 8192, 256, 512, 32
@@ -278,7 +279,8 @@ def test_backward_workspace_formula():
         BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                          # b, src, 1/z, delta
         BH * Nc * DK * DV * 4, BH * Nc * DK * 4,                                 # state gradients
         BH * S * 4, BH * S * 4,                                                  # q.dq, k.dk
-        BH * DK * DV * 4, BH * DK * 4])                                          # dC0, dn0
+        BH * DK * DV * 4, BH * DK * 4,                                           # dC0, dn0
+        BH * Nc * 10 * 64 * 64 * 4])                  # weighted dS of the 10 tile pairs per chunk
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
 
 

@@ -325,7 +325,7 @@ mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
 }
 
 struct BwLayout {
-  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, total;
+  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, dS, total;
 };
 
 // Forward workspace first, then the backward's own regions, each 256-byte aligned.
@@ -357,6 +357,8 @@ BwLayout bw_layout(const mlstm_fw_desc_t* d2) {
   l.kdk = take(BH * S * f);
   l.dC0 = take(BH * DK * DV * f);
   l.dn0 = take(ex ? BH * DK * f : 0);
+  const size_t nT = (size_t)d2->chunk_size / 64;
+  l.dS = take(d2->qkv_dtype == MLSTM_BF16 ? BH * Nc * (nT * (nT + 1) / 2) * 64 * 64 * f : 0);
   l.total = off;
   return l;
 }
@@ -647,6 +649,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.dn_states = ex ? at(l.dn) : nullptr;
   p.qdq = at(l.qdq);
   p.kdk = at(l.kdk);
+  p.dS_tiles = desc->qkv_dtype == MLSTM_BF16 ? at(l.dS) : nullptr;
   p.dQ = dQ;
   p.dK = dK;
   p.dV = dV;

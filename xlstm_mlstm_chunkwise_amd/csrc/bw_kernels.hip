@@ -833,11 +833,24 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   const bool y_bf16 = MODE == kModeDV ? hb : true;
   const int y_D = MODE == kModeDV ? DV : DK;
   constexpr bool y_split = MODE == kModeDV;
+  // the weighted dS tiles of the chunk's (query tile, key tile) pairs: the dk
+  // pass writes them, the dq pass (launched after it) reads them
+  float* dS_chunk = p.dS_tiles + ((size_t)bh * Nc + c) * (size_t)(nT * (nT + 1) / 2) * kT * kT;
   for (int xt = lo; xt <= hi; ++xt) {
     const int x0 = xt * kT, nx = min(kT, Lc - x0);
+    float4_t sc[4];
+    if constexpr (MODE == kModeDQ) {
+      // dS[own query w][partner keys 16 i + 4 g4 + 0..3], weighted and masked
+      const float* t = dS_chunk + ((size_t)(ot * (ot + 1) / 2 + xt) * kT + w) * kT + 4 * g4;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(t + 16 * i);
+        sc[i] = float4_t{v.x, v.y, v.z, v.w};
+      }
+    } else {
     __syncthreads();
     load_rows<SIG>(g_oth, p, rb, x0, Lc);
-    float4_t sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int nc = own_D / kT;  // contraction chunks (the own tile's width)
@@ -869,29 +882,32 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
         }
       }
     }
-    // first output-side tile in flight during the weighting
-    float py[16];
-    pre16(py, y_src, y_bf16, rb + x0, y_D, y0, nx);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int o = 16 * i + 4 * g4 + r;
         float x = 0.0f;
-        if constexpr (MODE == kModeDQ) {
-          if (own_ok && o < nx && x0 + o <= own0 + w) {
-            const float ex = ob - g_oth.b[o] + g_oth.src[o] - om;
-            x = expf(ex) * (sc[i][r] + odelta);
-          }
-        } else {
-          if (own_ok && o < nx && own0 + w <= x0 + o) {
-            const float ex = g_oth.b[o] - ob + osrc - (SIG ? 0.0f : g_oth.m[o]);
-            if constexpr (MODE == kModeDK) x = expf(ex) * (sc[i][r] + (SIG ? 0.0f : g_oth.delta[o]));
-            else x = expf(ex) * p.scale * sc[i][r];
-          }
+        // o = query, w = key
+        if (own_ok && o < nx && own0 + w <= x0 + o) {
+          const float ex = g_oth.b[o] - ob + osrc - (SIG ? 0.0f : g_oth.m[o]);
+          if constexpr (MODE == kModeDK) x = expf(ex) * (sc[i][r] + (SIG ? 0.0f : g_oth.delta[o]));
+          else x = expf(ex) * p.scale * sc[i][r];
         }
         sc[i][r] = x;
       }
+    if constexpr (MODE == kModeDK) {
+      // dS[partner query o][own key w] for the dq pass
+      float* t = dS_chunk + ((size_t)(xt * (xt + 1) / 2 + ot) * kT) * kT + w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * g4 + r) * kT] = sc[i][r];
+    }
+    }
+    // first output-side tile (loads in flight during the split below)
+    float py[16];
+    pre16(py, y_src, y_bf16, rb + x0, y_D, y0, nx);
     // the weighted tile as bf16 hi + lo B fragments, one per 32 partner rows
     bf16x8_t bsh[2], bsl[2];
 #pragma unroll
@@ -1040,8 +1056,9 @@ hipError_t launch_all(const BwParams& p, hipStream_t s) {
   if (p.qkv_bf16) hipLaunchKernelGGL((bw_dstate16_kernel<SIG>), gs, dim3(256), 0, s, p);
   else hipLaunchKernelGGL((bw_dstate_kernel<SIG>), gs, dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
+  // dk first: with bf16 inputs it leaves the weighted dS tiles that dq reads
   if ((e = launch_tiles<kModeDK, SIG>(p, p.DK, s)) != hipSuccess) return e;
+  if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
   const int Wv = p.DV % 256 == 0 ? 256 : p.DV % 128 == 0 ? 128 : 64;
   if ((e = launch_tiles<kModeDV, SIG>(p, Wv, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((bw_gates_kernel<SIG>), dim3((unsigned)p.BH), dim3(256), 0, s, p);

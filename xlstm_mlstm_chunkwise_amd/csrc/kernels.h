@@ -138,6 +138,8 @@ struct BwParams {
   float* dn_states;      // (BH, Nc, DK) scratch (exp)
   float* qdq;            // (BH, S) scratch
   float* kdk;            // (BH, S) scratch
+  float* dS_tiles;       // (BH, Nc, L/64 (L/64 + 1) / 2, 64, 64) scratch: weighted dS of every
+                         // (query tile, key tile <= it) pair, written by the dk pass, read by dq
   float* dQ;             // (BH, S, DK) float32
   float* dK;
   float* dV;             // (BH, S, DV) float32
