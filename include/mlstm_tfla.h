@@ -323,9 +323,11 @@ int mlstm_state_q8_decode(const mlstm_fw_desc_t* desc, const int8_t* Cq, const f
 /* Bytes of device workspace that mlstm_chunkwise_bw needs for `desc`: the
  * two-stage forward workspace, the recomputed forward quantities (chunk
  * states as float32, and for the exp gate H in float32 plus the per-row m and
- * normaliser), per-position gate terms, and the state gradient after every
+ * normaliser), per-position gate terms, the state gradient after every
  * chunk (N_c states of DHQK x DHV float32 values per head, plus DHQK values
- * for the exp gate).  Returns 0 for an invalid descriptor. */
+ * for the exp gate) and, for bf16 inputs, the weighted score gradients of
+ * every pair of 64-row tiles in a chunk (64 x 64 float32 each), which one
+ * gradient kernel hands to another.  Returns 0 for an invalid descriptor. */
 size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc);
 
 /* Backward pass: the gradients of sum(dH * H) with respect to the inputs of
