@@ -189,3 +189,24 @@ def test_stage_calls_match_the_whole_backward(mt):
     torch.cuda.synchronize()
     for n in o:
         np.testing.assert_array_equal(o[n].cpu().numpy().astype(np.float64), whole[n], err_msg=n)
+
+
+@pytest.mark.parametrize("precision", ["f64", "f16"])
+def test_backward_with_other_recompute_precisions(mt, precision):
+    """The forward quantities recomputed in fp64 (the parity mode of the
+    input-gate-spike workload) or with single-rounded fp16 operands; the
+    gradient kernels are the same."""
+    x = _draw(71, 1, 2, 200, 128, 128, "bf16", "exp", True)
+    g = _gpu(mt, x, "bf16", "exp", 64, precision=precision)
+    _compare(f"recompute {precision}", g, _ref(x, "exp"), "bf16", KEYS + ("dC0", "dn0", "dm0"))
+
+
+def test_backward_with_eps_and_tile_sizes(mt):
+    """eps > 0 (the gradient at fixed max-state, as the oracle takes it) and
+    explicit 128-row tiles for the recomputed intra-chunk stage."""
+    x = _draw(72, 1, 2, 384, 128, 256, "bf16", "exp", True)
+    g = _gpu(mt, x, "bf16", "exp", 128, eps=0.5, tile_lq=128, tile_lkv=128)
+    f64 = {n: a.astype(np.float64) for n, a in x.items()}
+    r = grad_fw(f64["q"], f64["k"], f64["v"], f64["i"], f64["f"], f64["dH"], f64["C0"], f64["n0"], f64["m0"],
+                gate="exp", eps=0.5)
+    _compare("eps 0.5, tiles 128", g, r, "bf16", KEYS + ("dC0", "dn0", "dm0"))

@@ -113,6 +113,19 @@ def test_step_against_oracle(mt, name, c):
     print(f"\n[{name}] max|dh|={e:.3g}", flush=True)
 
 
+def test_step_with_eps(mt):
+    x, st = _draw(16, 2, 2, 128, 128, "f32", "exp")
+    qd = torch.float32
+    out = mt.mlstm_recurrent_step(*(_dev(x[n][:, :, 0], qd) for n in ("q", "k", "v")), _dev(x["i"][:, :, 0], qd),
+                                  _dev(x["f"][:, :, 0], qd), _dev(st["C"], qd), _dev(st["n"], qd),
+                                  _dev(st["m"], qd), gate="exp", eps=0.25)
+    torch.cuda.synchronize()
+    gpu = [o.float().cpu().numpy().astype(np.float64) for o in out]
+    args = [x[n][:, :, :1].astype(np.float64) for n in ("q", "k", "v", "i", "f")]
+    ref = recurrent_fw(*args, st["C"], st["n"], st["m"], gate="exp", eps=0.25)
+    _check("eps 0.25", "f32", "exp", gpu, ref)
+
+
 def test_step_zero_state_in_place_and_bf16_h(mt):
     x, st = _draw(12, 2, 2, 128, 256, "bf16", "exp", with_state=False)
     gpu = _step_gpu(mt, x, st, "exp", 0, "bf16")
