@@ -127,10 +127,12 @@ def test_backward_without_state_grads_and_empty_sequence(mt):
     assert np.all(g["dC0"] == 0) and np.all(g["dn0"] == 0) and np.all(g["dm0"] == 0)
 
 
-@pytest.mark.parametrize("wname", ["bf16_7b_s8192", "sig_7b_s8192"])
+@pytest.mark.parametrize("wname", ["bf16_7b_s8192", "sig_7b_s8192", "bf16_7b_s65536"])
 def test_backward_full_size_sampled_heads(mt, wname):
-    """The 7B-shaped workload (B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk
-    256), the whole backward on the GPU.  The oracle checks the last 512
+    """The 7B-shaped workloads (B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk
+    256; and the long-context one, B=1, NH=8, S=65536, chunk 1024, 128-row
+    tiles, with an initial state), the whole backward on the GPU.  The
+    oracle checks the last 512
     positions of two heads: their gradients are those of the tail problem
     that starts from the exact state at the cut (every later query and key
     sits in the tail; the prefix enters only through that state), which the
@@ -144,15 +146,22 @@ def test_backward_full_size_sampled_heads(mt, wname):
     stack = lambda key: np.stack([per[(b, h)][key] for b in range(w.B) for h in range(w.NH)]).reshape(
         (w.B, w.NH) + per[(0, 0)][key].shape)
     qd = torch.bfloat16
+    init = {}
+    if w.init_state:
+        init = dict(C0=_dev(stack("C0")), n0=_dev(stack("n0")), m0=_dev(stack("m0")))
     g = mt.mlstm_chunkwise_bw(_dev(stack("q"), qd), _dev(stack("k"), qd), _dev(stack("v"), qd),
-                              _dev(stack("i")), _dev(stack("f")), _dev(dH), chunk_size=w.chunk, gate=w.gate)
+                              _dev(stack("i")), _dev(stack("f")), _dev(dH), chunk_size=w.chunk, gate=w.gate,
+                              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, **init)
     torch.cuda.synchronize()
     g = {n: t.cpu().numpy().astype(np.float64) for n, t in g.items()}
     for (b, h) in heads:
         x = {n: a.astype(np.float64) for n, a in per[(b, h)].items()}
         t0 = S - T
+        st0 = {}
+        if w.init_state:
+            st0 = dict(C0=x["C0"][None], n0=x["n0"][None], m0=np.asarray(x["m0"])[None])
         pre = chunkwise_fw(x["q"][None, :t0], x["k"][None, :t0], x["v"][None, :t0], x["i"][None, :t0],
-                           x["f"][None, :t0], gate=w.gate, chunk_size=w.chunk)
+                           x["f"][None, :t0], gate=w.gate, chunk_size=w.chunk, **st0)
         C, n, m = pre[1], pre[2], pre[3]
         r = grad_fw(x["q"][None, t0:], x["k"][None, t0:], x["v"][None, t0:], x["i"][None, t0:],
                     x["f"][None, t0:], dH[b, h][None, t0:].astype(np.float64), C,
