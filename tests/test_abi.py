@@ -37,6 +37,34 @@ def test_library_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+def _declared_prototypes():
+    """name -> list of parameter declarations, from the header's prototypes."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(mlstm_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).replace("\n", " ").split(",")]
+        protos[m.group(1)] = [] if params == ["void"] or params == [""] else params
+    return protos
+
+
+def test_binding_signatures_match_the_header():
+    """Every binding's argument count equals the prototype's, pointer
+    parameters are passed as pointers and size_t as size_t."""
+    protos = _declared_prototypes()
+    assert set(protos) == set(_declared_functions())
+    for name, (restype, argtypes) in mt._SYMBOLS.items():
+        params = protos[name]
+        assert len(argtypes) == len(params), (name, len(argtypes), len(params))
+        for decl, at in zip(params, argtypes):
+            if "*" in decl:
+                assert at in (ctypes.c_void_p, ctypes.c_char_p) or issubclass(at, ctypes._Pointer), (name, decl)
+            elif decl.startswith("size_t"):
+                assert at is ctypes.c_size_t, (name, decl)
+            else:
+                assert at in (ctypes.c_int, ctypes.c_int32), (name, decl)
+    assert set(mt._SYMBOLS) == set(protos), set(protos) ^ set(mt._SYMBOLS)
+
+
 def test_abi_version_and_status_strings():
     assert mt.abi_version() == 6
     assert mt.status_str(0) == "ok"
