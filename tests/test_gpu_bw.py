@@ -219,3 +219,23 @@ def test_backward_with_eps_and_tile_sizes(mt):
     r = grad_fw(f64["q"], f64["k"], f64["v"], f64["i"], f64["f"], f64["dH"], f64["C0"], f64["n0"], f64["m0"],
                 gate="exp", eps=0.5)
     _compare("eps 0.5, tiles 128", g, r, "bf16", KEYS + ("dC0", "dn0", "dm0"))
+
+
+def test_autograd_function_against_oracle(mt):
+    """mlstm_chunkwise as a torch autograd function: loss = sum(dH * H),
+    gradients from loss.backward() against the oracle."""
+    x = _draw(81, 1, 2, 260, 128, 256, "bf16", "exp", True)
+    qd = torch.bfloat16
+    t = {n: _dev(x[n], qd).requires_grad_(True) for n in ("q", "k", "v")}
+    t.update({n: _dev(x[n]).requires_grad_(True) for n in ("i", "f", "C0", "n0", "m0")})
+    H = mt.mlstm_chunkwise(t["q"], t["k"], t["v"], t["i"], t["f"], t["C0"], t["n0"], t["m0"], chunk_size=64)
+    (H * _dev(x["dH"])).sum().backward()
+    torch.cuda.synchronize()
+    r = _ref(x, "exp")
+    names = {"q": "dQ", "k": "dK", "v": "dV", "i": "d_i", "f": "d_f", "C0": "dC0", "n0": "dn0", "m0": "dm0"}
+    g = {names[n]: t[n].grad.float().cpu().numpy().astype(np.float64) for n in names}
+    # Q, K, V gradients come back in bf16 (the inputs' dtype): allow its rounding
+    for n in ("dQ", "dK", "dV"):
+        scale = max(1.0, np.abs(r[n]).max())
+        assert np.abs(g[n] - r[n]).max() / scale <= 2 ** -8, n
+    _compare("autograd", g, r, "bf16", ("d_i", "d_f", "dC0", "dn0", "dm0"))

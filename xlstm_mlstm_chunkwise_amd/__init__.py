@@ -539,3 +539,36 @@ def mlstm_recurrent_step_q8(q, k, v, i_pre, f_pre, Cq=None, Cs=None, n=None, m=N
     if st:
         raise MlstmError(st, "mlstm_recurrent_step_q8")
     return h, Cq_out, Cs_out, n_out, m_out
+
+
+def mlstm_chunkwise(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int, gate: str = "exp",
+                    precision: str = "split", qk_scale: Optional[float] = None, eps: float = 0.0,
+                    tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto"):
+    """H of the forward pass as a torch autograd function: the forward runs
+    mlstm_chunkwise_fw, the backward mlstm_chunkwise_bw (gradients for q, k,
+    v, i_pre, f_pre and, when given, C0, n0, m0).  H is float32.  The final
+    state is not returned here: no gradient enters through it."""
+    torch = _torch()
+    kw = dict(chunk_size=chunk_size, gate=gate, precision=precision, qk_scale=qk_scale, eps=eps,
+              tile_lq=tile_lq, tile_lkv=tile_lkv)
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_, i_, f_, C0_, n0_, m0_):
+            H = mlstm_chunkwise_fw(q_, k_, v_, i_, f_, C0_, n0_, m0_, schedule=schedule, return_final_state=False,
+                                   **kw)[0]
+            ctx.save_for_backward(q_, k_, v_, i_, f_, C0_, n0_, m0_)
+            return H
+
+        @staticmethod
+        def backward(ctx, dH):
+            q_, k_, v_, i_, f_, C0_, n0_, m0_ = ctx.saved_tensors
+            want_state = any(ctx.needs_input_grad[5:])
+            g = mlstm_chunkwise_bw(q_, k_, v_, i_, f_, dH.contiguous().float(), C0_, n0_, m0_,
+                                   state_grads=want_state, **kw)
+            cast = lambda t, like: None if t is None else t.to(like.dtype)
+            return (cast(g["dQ"], q_), cast(g["dK"], k_), cast(g["dV"], v_), g["d_i"], g["d_f"],
+                    g.get("dC0") if C0_ is not None else None, g.get("dn0") if n0_ is not None else None,
+                    g.get("dm0") if m0_ is not None else None)
+
+    return _Fn.apply(q, k, v, i_pre, f_pre, C0, n0, m0)
