@@ -641,6 +641,313 @@ __global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
   if (own_n && p.dn0 && tid < kT) p.dn0[(size_t)bh * DK + kt * kT + tid] = dn;
 }
 
+// Row-tile form of the (G, N) recurrence for bf16 Q: a workgroup of eight
+// waves keeps a TK x DV tile of G (each wave a 64 x 64 block on the 32x32x16
+// matrix cores) while it walks the chunks from last to first.  Each block of
+// 32 weighted dH rows is then staged once for all TK key rows, and each Q
+// block once for all value columns.  Per chunk c: G and N leave for slot c,
+// are decayed by the chunk's gate and gain the chunk's sums
+//   G += Q^T (w . dH),  N += Q^T wd,
+// w_t = s e^{b_t + M_c - m_t} / z_t and wd_t the same with delta_t (sig gate:
+// w_t = s e^{b_t}, no N).  Q enters the matrix cores as raw bf16 (exact);
+// w . dH is split into bf16 hi + lo.  Software pipeline over TB-row blocks
+// of the flattened (chunk, block) sequence, as in the forward state kernel:
+// two LDS stages and one barrier per block, global loads two blocks ahead.
+// A block of float32 dH is 16 rows, so that both register sets of its loads
+// fit beside the accumulators: a spilled register would be reloaded through
+// the same in-order counter as the loads in flight, and wait for them.
+// Staging: the lanes of wave x are split evenly over its time rows
+// (TB / 8 rows each; a row's owner lanes hold its Q pieces and gate terms),
+// and the same wave stages those rows of dH, taking each row's weight from
+// the row's first owner lane.
+template <int TK, int TV, int TB, bool SIG, bool DHB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bw_dstate_rows_kernel(
+    const BwParams p) {
+  constexpr int NT = 512, NW = 8;
+  constexpr int NWC = TV / 64;
+  static_assert((TK / 64) * NWC == NW, "eight 64x64 wave tiles");
+  constexpr int LDK = TK + 32, LDV = TV + 32;  // transposing reads: 16 banks mod 64
+  constexpr int RW = TB / NW;                  // time rows per wave
+  constexpr int EPT = TB * TK / NT;            // Q elements per thread and block
+  constexpr int TPR = TK / EPT;                // staging lanes per time row
+  static_assert((TB == 16 || TB == 32) && RW * TPR == 64, "staging split");
+  static_assert(EPT == 2 || EPT == 4 || EPT == 8, "Q pieces of 4, 8 or 16 bytes");
+  constexpr int VE = DHB ? 8 : 4;       // dH elements per 16-byte load
+  constexpr int VSEG = TV / VE;         // 16-byte pieces per dH row
+  constexpr int VPT = RW * VSEG / 64;   // pieces per lane and block
+  static_assert(VPT * 64 == RW * VSEG && VPT >= 1, "dH staging split");
+  constexpr int QBUF = TB * LDK, WBUF = TB * LDV;
+  typedef typename std::conditional<EPT == 2, uint32_t, typename std::conditional<EPT == 4, uint2, uint4>::type>::type
+      QVec;
+
+  __shared__ float s_np[NW][TK];
+  __shared__ __align__(16) uint16_t s_q[2 * QBUF];
+  __shared__ __align__(16) uint16_t s_wh[2 * WBUF];
+  __shared__ __align__(16) uint16_t s_wl[2 * WBUF];
+
+  const int NTK = p.DK / TK;
+  const int nblk = gridDim.x;
+  int bid = blockIdx.x;
+  // the row tiles of one head on one XCD: they read the same dH rows
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int kt = bid % NTK;
+  const int bh = bid / NTK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int S = p.S, DK = p.DK, L = p.L, Nc = p.Nc;
+  constexpr int DV = TV;
+  const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;
+  const size_t gbase = (size_t)bh * S;
+  const int krs = tid / TPR, kcs = (tid % TPR) * EPT;  // own time row (RW wave + lane / TPR) and columns
+
+  float16_t acc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
+  float nreg = 0.0f;  // N for key row kt * TK + tid (tid < TK)
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.Q) + gbase * DK + kt * TK,
+                                              (uint32_t)(((size_t)S * DK - kt * TK) * 2));
+  const __amdgpu_buffer_rsrc_t rd =
+      make_rsrc(static_cast<const char*>(p.dH) + gbase * DV * (DHB ? 2 : 4), (uint32_t)((size_t)S * DV * (DHB ? 2 : 4)));
+  const int qvoff = (krs * DK + kcs) * 2;
+
+  // block gi: chunk Nc - 1 - gi / BPC, rows [tb, tb + TB) of it; blocks past
+  // the end of a short last chunk read zeros and carry weight zero
+  const int BPC = L / TB;
+  const int NBLK = Nc * BPC;
+
+  QVec qr[2];
+  uint4 dr[2][VPT];
+  float gbr[2], mr[2], izr[2], dlr[2];  // own row's gate terms
+  float glr[2], Mcr[2], Mnr[2];         // chunk scalars (first block of a chunk)
+  auto load_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    const int t0 = c * L, Lc = min(L, S - t0);
+    const int trow = t0 + tb;
+    if constexpr (EPT == 2) {
+      qr[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rq, qvoff, trow * DK * 2, 0);
+    } else if constexpr (EPT == 4) {
+      const v2i32_t q2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qvoff, trow * DK * 2, 0);
+      qr[s] = make_uint2((uint32_t)q2.x, (uint32_t)q2.y);
+    } else {
+      qr[s] = buf_load16(rq, qvoff, trow * DK * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int f = i * 64 + lane, row = RW * wave + f / VSEG, seg = f % VSEG;
+      dr[s][i] = buf_load16_nt(rd, (row * DV + seg * VE) * (DHB ? 2 : 4), trow * DV * (DHB ? 2 : 4));
+    }
+    const int t = trow + krs;
+    const bool ok = t < S;
+    gbr[s] = ok ? p.gb[gbase + t] : 0.0f;
+    if constexpr (!SIG) {
+      mr[s] = ok ? p.m_rows[gbase + t] : 0.0f;
+      izr[s] = ok ? p.ginvz[gbase + t] : 0.0f;
+      dlr[s] = ok ? p.gdelta[gbase + t] : 0.0f;
+    }
+    if (tb == 0) {
+      glr[s] = p.gb[gbase + t0 + Lc - 1];
+      if constexpr (!SIG) {
+        Mcr[s] = p.m_states[(size_t)bh * (Nc + 1) + c];
+        Mnr[s] = p.m_states[(size_t)bh * (Nc + 1) + c + 1];
+      }
+    }
+  };
+
+  // N: partial sums of the staging lanes, reduced over the lanes that share
+  // key columns, then (after a barrier) over the waves
+  float np[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) np[e] = 0.0f;
+  bool n_pend = false;
+  float n_dec = 1.0f;
+  float Mc_s = 0.0f, dec_s = 1.0f;  // scalars of the chunk being staged
+  float dec_pend = 1.0f;            // handed to the matrix-core side
+  auto flush_n = [&]() {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+#pragma unroll
+      for (int o = TPR; o < 64; o <<= 1) np[e] += __shfl_xor(np[e], o, 64);
+    }
+    if (lane < TPR) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) s_np[wave][kcs + e] = np[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) np[e] = 0.0f;
+    n_pend = true;
+    n_dec = dec_s;
+  };
+  auto finish_n = [&](float* dst) {
+    if (tid < TK) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sacc += s_np[w][tid];
+      nreg = nreg * n_dec + sacc;
+      if (dst) dst[kt * TK + tid] = nreg;
+    }
+    n_pend = false;
+  };
+
+  auto stage_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    if (tb == 0) {
+      if (!SIG && gi > 0) flush_n();
+      if constexpr (SIG) {
+        dec_s = expf(glr[s]);
+      } else {
+        Mc_s = Mcr[s];
+        dec_s = expf(Mc_s + glr[s] - Mnr[s]);
+      }
+      dec_pend = dec_s;
+    }
+    const bool ok = c * L + tb + krs < S;
+    float w = 0.0f, wd = 0.0f;
+    if (ok) {
+      if constexpr (SIG) {
+        w = p.scale * expf(gbr[s]);
+      } else {
+        const float e = p.scale * expf(gbr[s] + Mc_s - mr[s]);
+        w = e * izr[s];
+        wd = e * dlr[s];
+      }
+    }
+    // Q as raw bf16; N partial sums
+    *reinterpret_cast<QVec*>(s_q + s * QBUF + krs * LDK + kcs) = qr[s];
+    if constexpr (!SIG) {
+      uint32_t qw[EPT / 2];
+      __builtin_memcpy(qw, &qr[s], sizeof(qw));
+#pragma unroll
+      for (int e = 0; e < EPT / 2; ++e) {
+        np[2 * e] += wd * __uint_as_float(qw[e] << 16);
+        np[2 * e + 1] += wd * __uint_as_float(qw[e] & 0xffff0000u);
+      }
+    }
+    // w . dH as bf16 hi + lo; the row's weight from its owner lanes
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int f = i * 64 + lane, rw = f / VSEG, seg = f % VSEG;
+      float wi;
+      if constexpr (VSEG % 64 == 0) {
+        wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), TPR * ((i * 64) / VSEG)));
+      } else {
+        wi = __shfl(w, TPR * rw, 64);
+      }
+      float x[VE];
+      const uint32_t u[4] = {dr[s][i].x, dr[s][i].y, dr[s][i].z, dr[s][i].w};
+      if constexpr (DHB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(u[e] << 16) * wi;
+          x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u) * wi;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(u[e]) * wi;
+      }
+      uint32_t hw[VE / 2], lw[VE / 2];
+#pragma unroll
+      for (int e = 0; e < VE / 2; ++e) split_bf16x2(x[2 * e], x[2 * e + 1], hw[e], lw[e]);
+      const int o = s * WBUF + (RW * wave + rw) * LDV + seg * VE;
+      if constexpr (DHB) {
+        *reinterpret_cast<uint4*>(s_wh + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(s_wl + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      } else {
+        *reinterpret_cast<uint2*>(s_wh + o) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(s_wl + o) = make_uint2(lw[0], lw[1]);
+      }
+    }
+  };
+
+  // matrix-core side
+  auto write_g = [&](int c) {
+    float* G = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const int vcol = wc0 + 32 * cb + l32;
+          __builtin_nontemporal_store(acc[rb][cb][r], G + (size_t)krow * DV + vcol);
+        }
+  };
+  auto mma_blk = [&](auto set, int gi) {
+    constexpr int s = decltype(set)::value;
+    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    if (tb == 0) {
+      write_g(c);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] *= dec_pend;
+    }
+    const int Lc = min(L, S - c * L);
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ++ks) {
+      if (tb + 16 * ks >= Lc) break;  // uniform: padding only
+      bf16x8_t a[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a[rb] = as_bf16x8(frag_tr_u(s_q + s * QBUF, LDK, 16 * ks, wr0 + 32 * rb, lane));
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const bf16x8_t bh_ = as_bf16x8(frag_tr_u(s_wh + s * WBUF, LDV, 16 * ks, wc0 + 32 * cb, lane));
+        const bf16x8_t bl_ = as_bf16x8(frag_tr_u(s_wl + s * WBUF, LDV, 16 * ks, wc0 + 32 * cb, lane));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          acc[rb][cb] = mma32b(a[rb], bh_, acc[rb][cb]);
+          acc[rb][cb] = mma32b(a[rb], bl_, acc[rb][cb]);
+        }
+      }
+    }
+  };
+
+  auto iter = [&](auto par, int gi) {
+    constexpr int P = decltype(par)::value;
+    constexpr int Qs = 1 - P;
+    if (n_pend) finish_n(p.dn_states + ((size_t)bh * Nc + (Nc - 1 - gi / BPC)) * DK);
+    mma_blk(std::integral_constant<int, P>{}, gi);
+    if (gi + 1 < NBLK) stage_blk(std::integral_constant<int, Qs>{}, gi + 1);
+    if (gi + 3 < NBLK) load_blk(std::integral_constant<int, Qs>{}, gi + 3);
+    __syncthreads();
+  };
+
+  if (!SIG && tid < TK) p.dn_states[((size_t)bh * Nc + Nc - 1) * DK + kt * TK + tid] = 0.0f;
+  load_blk(std::integral_constant<int, 0>{}, 0);
+  if (NBLK > 1) load_blk(std::integral_constant<int, 1>{}, 1);
+  stage_blk(std::integral_constant<int, 0>{}, 0);
+  if (NBLK > 2) load_blk(std::integral_constant<int, 0>{}, 2);
+  __syncthreads();
+  for (int gi = 0; gi < NBLK; gi += 2) {
+    iter(std::integral_constant<int, 0>{}, gi);
+    if (gi + 1 < NBLK) iter(std::integral_constant<int, 1>{}, gi + 1);
+  }
+  if constexpr (!SIG) {
+    flush_n();
+    __syncthreads();
+    finish_n(p.dn0 ? p.dn0 + (size_t)bh * DK : nullptr);
+  }
+  if (p.dC0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const int vcol = wc0 + 32 * cb + l32;
+          p.dC0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] = acc[rb][cb][r];
+        }
+  }
+}
+
 // Staging in two halves, so that the global loads of the next tile are in
 // flight while the matrix cores work on the current one: pre16 loads this
 // thread's 16 values of a tile into registers, put_rows / put_cols write them
@@ -1053,7 +1360,16 @@ hipError_t launch_all(const BwParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bw_prep_kernel<SIG>), dim3((unsigned)(p.BH * p.Nc)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gs((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT));
-  if (p.qkv_bf16) hipLaunchKernelGGL((bw_dstate16_kernel<SIG>), gs, dim3(256), 0, s, p);
+  const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK / (p.DV == 512 ? 64 : 128));
+  if (p.qkv_bf16 && p.DV == 512 && p.dh_bf16)
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 32, SIG, true>), dim3(rows), dim3(512), 0, s, p);
+  else if (p.qkv_bf16 && p.DV == 512)
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 16, SIG, false>), dim3(rows), dim3(512), 0, s, p);
+  else if (p.qkv_bf16 && p.DV == 256 && p.DK % 128 == 0 && p.dh_bf16)
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<128, 256, 32, SIG, true>), dim3(rows), dim3(512), 0, s, p);
+  else if (p.qkv_bf16 && p.DV == 256 && p.DK % 128 == 0)
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<128, 256, 16, SIG, false>), dim3(rows), dim3(512), 0, s, p);
+  else if (p.qkv_bf16) hipLaunchKernelGGL((bw_dstate16_kernel<SIG>), gs, dim3(256), 0, s, p);
   else hipLaunchKernelGGL((bw_dstate_kernel<SIG>), gs, dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // dk first: with bf16 inputs it leaves the weighted dS tiles that dq reads
