@@ -121,7 +121,8 @@ typedef enum { MLSTM_SCHED_AUTO = 0, MLSTM_SCHED_TWO_STAGE = 1, MLSTM_SCHED_FUSE
 
 typedef struct {
   int32_t B, NH;       /* batch, heads: >= 1                                   */
-  int32_t S;           /* sequence length: >= 0, need not divide chunk_size   */
+  int32_t S;           /* sequence length: >= 0, need not divide chunk_size;
+                          S * max(DHQK, DHV) < 2^29 (else MLSTM_E_SHAPE)     */
   int32_t DHQK, DHV;   /* head dims: multiples of 64, at most 512 (float32
                           inputs: DHQK at most 256)                           */
   int32_t chunk_size;  /* L: power of two, 64..1024                           */

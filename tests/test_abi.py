@@ -110,10 +110,13 @@ def test_valid_descriptor_and_workspace_size():
                                        + r256(BH * (Ncw + 1) * 4))
     assert mt.validate(_desc(S=0)) == 0
     assert mt.num_chunks(_desc(S=0)) == 0
+    # the longest head the 32-bit buffer offsets allow
+    assert mt.validate(_desc(S=(1 << 20) - 1, DHQK=64, DHV=512)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 2), (dict(NH=-1), 2), (dict(S=-5), 2),
+    (dict(S=1 << 20, DHQK=64, DHV=512), 2), (dict(S=1 << 21, DHQK=256, DHV=256), 2),
     (dict(DHQK=96), 2), (dict(DHQK=1024), 2), (dict(DHV=32), 2), (dict(DHV=576), 2),
     (dict(chunk_size=96), 3), (dict(chunk_size=32), 3), (dict(chunk_size=2048), 3),
     (dict(tile_lq=48), 3), (dict(tile_lkv=256), 3),

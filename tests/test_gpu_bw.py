@@ -116,6 +116,26 @@ def test_backward_bf16_dh_and_one_chunk(mt):
     _compare("bf16 dH, one chunk", g, _ref(x, "exp"), "bf16", KEYS + ("dC0", "dn0", "dm0"))
 
 
+ROW_TILE_CASES = [
+    # name, B, NH, S, DK, DV, L, gate, init, dh_bf16: the instances of the
+    # row-tile state-gradient kernel (64 key rows x 512 value columns, or
+    # 128 x 256; 16-row blocks for float32 dH, 32-row blocks for bf16 dH)
+    ("exp_d256x512_bf16dh_L128_ragged", 1, 2, 300, 256, 512, 128, "exp", True, True),
+    ("sig_d128x512_bf16dh_L64", 1, 2, 200, 128, 512, 64, "sig", False, True),
+    ("sig_d256x256_f32dh_L64_init", 1, 1, 333, 256, 256, 64, "sig", True, False),
+    ("sig_d128x256_bf16dh_L64_ragged", 2, 1, 150, 128, 256, 64, "sig", True, True),
+]
+
+
+@pytest.mark.parametrize("c", ROW_TILE_CASES, ids=[c[0] for c in ROW_TILE_CASES])
+def test_backward_row_tile_state_kernel(mt, c):
+    name, B, NH, S, DK, DV, L, gate, init, dh_bf16 = c
+    x = _draw(300 + ROW_TILE_CASES.index(c), B, NH, S, DK, DV, "bf16", gate, init, dh_bf16=dh_bf16)
+    g = _gpu(mt, x, "bf16", gate, L, dh_bf16=dh_bf16)
+    keys = KEYS + ("dC0",) + (("dn0", "dm0") if gate == "exp" else ())
+    _compare(name, g, _ref(x, gate), "bf16", keys)
+
+
 def test_backward_without_state_grads_and_empty_sequence(mt):
     x = _draw(22, 1, 1, 100, 64, 64, "f32", "exp", True)
     g = _gpu(mt, x, "f32", "exp", 64, state_grads=False)

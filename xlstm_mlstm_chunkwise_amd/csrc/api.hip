@@ -56,7 +56,9 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   const int64_t Nc = ((int64_t)d->S + d->chunk_size - 1) / d->chunk_size;
   if (BH > (1 << 30)) return MLSTM_E_SHAPE;
   if (BH * Nc * (d->chunk_size / 64) > 0x7fffffffLL) return MLSTM_E_SHAPE;  // grid.x bound
-  if ((int64_t)d->S * (int64_t)d->DHV > (1LL << 40)) return MLSTM_E_SHAPE;
+  // Per-head byte extents and row offsets of the buffer-resource kernels are
+  // 32-bit: a head's largest float32 row block stays below 2 GiB.
+  if ((int64_t)d->S * (int64_t)(d->DHQK > d->DHV ? d->DHQK : d->DHV) >= (1LL << 29)) return MLSTM_E_SHAPE;
   if (d->schedule == MLSTM_SCHED_FUSED && !fused_supported(d)) return MLSTM_E_UNSUPPORTED;
   return MLSTM_OK;
 }
