@@ -66,6 +66,21 @@ __device__ __forceinline__ float4_t mma4(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Tile index (x, y) of this workgroup, placed so that neighbouring tiles (the
+// row tiles of one chunk, and the column slices of one tile, y fastest) run
+// on one XCD at about the same time: they stage the same partner tiles,
+// which that XCD's L2 then serves.  The hardware deals workgroups to the
+// eight XCDs round-robin in launch order.
+struct TileIdx {
+  int x, y;
+};
+__device__ __forceinline__ TileIdx xcd_tile() {
+  const unsigned long long gy = gridDim.y, n = (unsigned long long)gridDim.x * gy;
+  unsigned long long lin = blockIdx.x + blockIdx.y * (unsigned long long)gridDim.x;
+  if ((n & 7) == 0) lin = (lin & 7) * (n >> 3) + (lin >> 3);
+  return {(int)(lin / gy), (int)(lin % gy)};
+}
+
 __device__ __forceinline__ float sigmoid_neg(float x) { return 1.0f / (1.0f + expf(x)); }
 
 // 16 consecutive values at element offset `off` of a bf16 or float32 array.
@@ -283,8 +298,9 @@ __global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
   __shared__ RowGates g_own, g_oth;
 
   const int nT = p.L / kT;
-  const int ot = blockIdx.x % nT;
-  const int rest = blockIdx.x / nT;
+  const TileIdx ti = xcd_tile();
+  const int ot = ti.x % nT;
+  const int rest = ti.x / nT;
   const int c = rest % p.Nc, bh = rest / p.Nc;
   const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
   const int own0 = ot * kT;
@@ -294,7 +310,7 @@ __global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
   const int DK = p.DK, DV = p.DV, Nc = p.Nc;
   const int DO = MODE == kModeDV ? DV : DK;  // output width
-  const int y0 = blockIdx.y * W;
+  const int y0 = ti.y * W;
   const bool qb = p.qkv_bf16, hb = p.dh_bf16;
 
   load_rows<SIG>(g_own, p, rb, own0, Lc);
@@ -1005,8 +1021,9 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   __shared__ RowGates g_own, g_oth;
 
   const int nT = p.L / kT;
-  const int ot = blockIdx.x % nT;
-  const int rest = blockIdx.x / nT;
+  const TileIdx ti = xcd_tile();
+  const int ot = ti.x % nT;
+  const int rest = ti.x / nT;
   const int c = rest % p.Nc, bh = rest / p.Nc;
   const int t0 = c * p.L, Lc = min(p.L, p.S - t0);
   const int own0 = ot * kT;
@@ -1016,7 +1033,7 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
   const int DK = p.DK, DV = p.DV, Nc = p.Nc;
   const int DO = MODE == kModeDV ? DV : DK;
-  const int y0 = blockIdx.y * W;
+  const int y0 = ti.y * W;
   const bool hb = p.dh_bf16;
 
   load_rows<SIG>(g_own, p, rb, own0, Lc);
