@@ -51,6 +51,7 @@
 // tile is therefore a ready B operand of a product that contracts over its
 // rows: in step r the lanes' slot l / 16 stands for row 4 (l / 16) + r.
 #include "device_common.h"
+#include "tile_order.h"
 #include "kernels.h"
 
 namespace mlstm {
@@ -64,21 +65,6 @@ enum { kModeDQ = 0, kModeDK = 1, kModeDV = 2 };
 
 __device__ __forceinline__ float4_t mma4(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Tile index (x, y) of this workgroup, placed so that neighbouring tiles (the
-// row tiles of one chunk, and the column slices of one tile, y fastest) run
-// on one XCD at about the same time: they stage the same partner tiles,
-// which that XCD's L2 then serves.  The hardware deals workgroups to the
-// eight XCDs round-robin in launch order.
-struct TileIdx {
-  int x, y;
-};
-__device__ __forceinline__ TileIdx xcd_tile() {
-  const unsigned long long gy = gridDim.y, n = (unsigned long long)gridDim.x * gy;
-  unsigned long long lin = blockIdx.x + blockIdx.y * (unsigned long long)gridDim.x;
-  if ((n & 7) == 0) lin = (lin & 7) * (n >> 3) + (lin >> 3);
-  return {(int)(lin / gy), (int)(lin % gy)};
 }
 
 __device__ __forceinline__ float sigmoid_neg(float x) { return 1.0f / (1.0f + expf(x)); }

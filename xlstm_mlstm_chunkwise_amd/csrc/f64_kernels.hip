@@ -9,6 +9,7 @@
 // (kept in fp64 in the workspace).  Each thread owns a 4 x 4 register block;
 // operands are staged through LDS in 64-wide tiles.
 #include "device_common.h"
+#include "tile_order.h"
 #include "kernels.h"
 
 namespace mlstm {
@@ -196,12 +197,13 @@ __global__ __launch_bounds__(256) void hintra_f64_kernel(const HintraParams p) {
   __shared__ double s_row_r[64], s_row_w[64], s_row_m[64], s_row_den[64];
 
   const int NQT = p.L / 64;
-  int bid = blockIdx.x;
+  const TileIdx ti = xcd_tile();
+  int bid = ti.x;
   const int qt = bid % NQT;
   bid /= NQT;
   const int c = bid % p.Nc;
   const int bh = bid / p.Nc;
-  const int vt = blockIdx.y;
+  const int vt = ti.y;
   const int S = p.S, DK = p.DK, DV = p.DV, L = p.L, Nc = p.Nc;
   const int t0 = c * L, Lc = min(L, S - t0), row0 = qt * 64;
   if (row0 >= Lc) return;

@@ -27,6 +27,7 @@
 // the P.V product directly (the contraction slots are permuted consistently
 // on the V side), with no trip through LDS.
 #include "device_common.h"
+#include "tile_order.h"
 #include "kernels.h"
 
 namespace mlstm {
@@ -55,12 +56,13 @@ __global__ __launch_bounds__(kTQ * 4) void hintra_kernel(const HintraParams p) {
   __shared__ __align__(16) float s_ct[kTV][64 + 4];        // state slice [v][k]
 
   const int NQT = p.L / kTQ;
-  int bid = blockIdx.x;
+  const TileIdx ti = xcd_tile();
+  int bid = ti.x;
   const int qt = bid % NQT;
   bid /= NQT;
   const int c = bid % p.Nc;
   const int bh = bid / p.Nc;
-  const int vt = blockIdx.y;
+  const int vt = ti.y;
   const int S = p.S, DV = p.DV, L = p.L, Nc = p.Nc;
   const int t0 = c * L;
   const int Lc = min(L, S - t0);
