@@ -208,9 +208,11 @@ int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
+// C_plain (packed layout only): also deliver the chunk states as float32
+// row-major; plain_only: no intra-chunk kernel will read the packed copy.
 int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const float* i_pre, const float* f_pre,
                const float* C0, const float* n0, const float* m0, const WsPtrs& ws, float* C_out, float* n_out,
-               float* m_out, hipStream_t stream) {
+               float* m_out, hipStream_t stream, float* C_plain = nullptr, bool plain_only = false) {
   StatesParams p;
   p.K = K;
   p.V = V;
@@ -243,6 +245,8 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   hipError_t e;
   if (d->precision == MLSTM_PREC_F64) e = mlstm::launch_states_f64(p, bf16, sig, stream);
   else if (packed_layout(d)) {
+    p.C_plain = C_plain;
+    p.plain_only = C_plain && plain_only;
     e = run_gates(d, i_pre, f_pre, ws, stream);
     if (e == hipSuccess) e = mlstm::launch_states_wide(p, sig, split, stream);
   }
@@ -584,6 +588,14 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc) {
   return bw_layout(&d2).total;
 }
 
+// Where the recompute leaves the float32 chunk states: the backward's own
+// region (written by the wide states kernel, or narrowed from float64), or,
+// for the generic kernels, their float32 workspace states themselves.
+float* bw_states_f32(const mlstm_fw_desc_t* d2, void* workspace, float* region) {
+  if (packed_layout(d2) || d2->precision == MLSTM_PREC_F64) return region;
+  return ws_ptrs(d2, workspace).C;
+}
+
 int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
                        const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -603,8 +615,18 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   const bool ex = desc->gate == MLSTM_GATE_EXP;
   auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const WsPtrs fw = ws_ptrs(&d2, workspace);
-  st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s);
-  if (st == MLSTM_OK) st = unpack_states(&d2, fw, at(l.Cst), ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
+  // Float32 chunk states for the gradient stage.  Sig gate on the wide
+  // kernels: no intra-chunk kernel runs, so the states kernel writes them as
+  // float32 directly instead of packed.  Exp gate: the packed states feed the
+  // intra-chunk recompute and are unpacked after it.  Float64: narrowed.  The
+  // generic kernels' float32 states are read in place (bw_states_f32).
+  const bool packed = packed_layout(&d2);
+  const bool direct = packed && !ex;
+  st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s, direct ? at(l.Cst) : nullptr,
+                  true);
+  const bool convert = (packed && !direct) || d2.precision == MLSTM_PREC_F64;
+  if (st == MLSTM_OK)
+    st = unpack_states(&d2, fw, convert ? at(l.Cst) : nullptr, ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
   if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
   return st;
 }
@@ -638,7 +660,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.H = ex ? at(l.H) : nullptr;
   p.m_rows = ex ? at(l.mrows) : nullptr;
   p.den_rows = ex ? at(l.den) : nullptr;
-  p.C_states = at(l.Cst);
+  p.C_states = bw_states_f32(&d2, workspace, at(l.Cst));
   p.n_states = ex ? at(l.nst) : nullptr;
   p.m_states = ex ? at(l.mst) : nullptr;
   p.C0 = C0;

@@ -37,6 +37,11 @@ struct StatesParams {
   float* m_local;    // (BH, Nc + 1) stabiliser of segment-local runs, log2 units (wide family)
   int BH, S, DK, DV, L, Nc;
   int nseg, cps;     // sequence segments per head and chunks per segment (row-tile kernel)
+  // Wide family only: also deliver the chunk states as float32 row-major
+  // (BH, Nc + 1, DK, DV); with plain_only the packed copy may be skipped
+  // (no intra-chunk kernel reads it).
+  float* C_plain = nullptr;
+  int plain_only = 0;
 };
 
 struct HintraParams {

@@ -263,7 +263,9 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
 //     per-position gate terms; the chunk stabiliser and decay are formed when
 //     a chunk's first block is staged and applied one block later, when the
 //     matrix cores reach it.
-template <int TK, int TV, bool SIG, bool SPLIT>
+// PLAIN: the states go out as float32 row-major (StatesParams::C_plain)
+// instead of packed, for a reader other than the intra-chunk kernel.
+template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void states_rows_kernel(
     const StatesParams p) {
   constexpr int NT = 512, NW = 8, TB = 32;
@@ -325,10 +327,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (!SIG && seg > 0) Mst2 = -INFINITY;
 
   auto write_state = [&](int entry, float M2) {
+    if constexpr (PLAIN) {
+      // float32 row-major copy: a half-wave stores 128 contiguous bytes of a row
+      float* Pl = p.C_plain + ((size_t)bh * (Nc + 1) + entry) * DK * DV;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            __builtin_nontemporal_store(acc[rb][cb][r], Pl + (size_t)krow * DV + wc0 + 32 * cb + l32);
+          }
+    }
     uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + entry) * DK * DV * 2;
     constexpr int NB = DV / 32;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2 && !PLAIN; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
@@ -718,10 +733,10 @@ __global__ __launch_bounds__(256) void states_fix_kernel(const StatesParams p) {
   if (!SIG && g == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = MT2 * kLn2;
 }
 
-template <int TK, int TV, bool SIG, bool SPLIT>
+template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false>
 hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.BH * (p.DK / TK) * p.nseg));
-  hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT, PLAIN>), grid, dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nseg <= 1) return e;
   const long long per = (long long)p.BH * (p.DK * p.DV / 8);
@@ -735,6 +750,8 @@ hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
 
 template <int TK, int TV>
 hipError_t launch_rows_any(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  if (p.C_plain)  // float32 states only: one segment, split operands
+    return sig ? launch_rows<TK, TV, true, true, true>(p, stream) : launch_rows<TK, TV, false, true, true>(p, stream);
   if (sig) return split ? launch_rows<TK, TV, true, true>(p, stream) : launch_rows<TK, TV, true, false>(p, stream);
   return split ? launch_rows<TK, TV, false, true>(p, stream) : launch_rows<TK, TV, false, false>(p, stream);
 }
@@ -766,9 +783,27 @@ hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipSt
       q.nseg = (p.Nc + q.cps - 1) / q.cps;
     }
     if (base >= cus || q.nseg > 1) {
-      if (rows_tk == 64) return launch_rows_any<64, 512>(q, sig, split, stream);
-      return launch_rows_any<128, 256>(q, sig, split, stream);
+      // segment-local states are joined afterwards: the plain copy then
+      // comes from the joined packed states
+      if (q.nseg > 1 || !split || !q.plain_only) {
+        q.C_plain = nullptr;
+        q.plain_only = 0;
+      }
+      hipError_t e = rows_tk == 64 ? launch_rows_any<64, 512>(q, sig, split, stream)
+                                   : launch_rows_any<128, 256>(q, sig, split, stream);
+      if (e == hipSuccess && p.C_plain && !q.C_plain)
+        e = launch_unpack_states(p.C_states, p.C_plain, (long long)p.BH * (p.Nc + 1), p.DK, p.DV, stream);
+      return e;
     }
+  }
+  if (p.C_plain) {
+    StatesParams q = p;
+    q.C_plain = nullptr;
+    q.plain_only = 0;
+    hipError_t e = launch_states_wide(q, sig, split, stream);
+    if (e == hipSuccess)
+      e = launch_unpack_states(p.C_states, p.C_plain, (long long)p.BH * (p.Nc + 1), p.DK, p.DV, stream);
+    return e;
   }
   // 128-wide tiles when they still give at least two workgroups per CU.
   const bool big = (long long)p.BH * (p.DK / 128) * (p.DV / 128) >= 2LL * cus;
