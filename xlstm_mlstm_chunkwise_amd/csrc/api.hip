@@ -589,8 +589,10 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc) {
 }
 
 // Where the recompute leaves the float32 chunk states: the backward's own
-// region (written by the wide states kernel, or narrowed from float64), or,
-// for the generic kernels, their float32 workspace states themselves.
+// region (written by the sig-gate wide states kernel, or narrowed from
+// float64), or, for the generic kernels, their float32 workspace states
+// themselves.  (Exp gate on the wide kernels: the dq pass reads the packed
+// states, and this region stays unused.)
 float* bw_states_f32(const mlstm_fw_desc_t* d2, void* workspace, float* region) {
   if (packed_layout(d2) || d2->precision == MLSTM_PREC_F64) return region;
   return ws_ptrs(d2, workspace).C;
@@ -615,16 +617,17 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   const bool ex = desc->gate == MLSTM_GATE_EXP;
   auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const WsPtrs fw = ws_ptrs(&d2, workspace);
-  // Float32 chunk states for the gradient stage.  Sig gate on the wide
-  // kernels: no intra-chunk kernel runs, so the states kernel writes them as
-  // float32 directly instead of packed.  Exp gate: the packed states feed the
-  // intra-chunk recompute and are unpacked after it.  Float64: narrowed.  The
-  // generic kernels' float32 states are read in place (bw_states_f32).
+  // Chunk states for the gradient stage.  Exp gate on the wide kernels: the
+  // packed states feed the intra-chunk recompute, and the dq pass reads them
+  // packed too.  Sig gate on the wide kernels: no intra-chunk kernel runs,
+  // so the states kernel writes them as float32 directly instead.  Float64:
+  // narrowed to float32.  The generic kernels' float32 states are read in
+  // place (bw_states_f32).
   const bool packed = packed_layout(&d2);
   const bool direct = packed && !ex;
   st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s, direct ? at(l.Cst) : nullptr,
                   true);
-  const bool convert = (packed && !direct) || d2.precision == MLSTM_PREC_F64;
+  const bool convert = d2.precision == MLSTM_PREC_F64;
   if (st == MLSTM_OK)
     st = unpack_states(&d2, fw, convert ? at(l.Cst) : nullptr, ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
   if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
@@ -661,6 +664,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.m_rows = ex ? at(l.mrows) : nullptr;
   p.den_rows = ex ? at(l.den) : nullptr;
   p.C_states = bw_states_f32(&d2, workspace, at(l.Cst));
+  p.C_packed = packed_layout(&d2) && ex ? reinterpret_cast<const uint16_t*>(ws_ptrs(&d2, workspace).C) : nullptr;
   p.n_states = ex ? at(l.nst) : nullptr;
   p.m_states = ex ? at(l.mst) : nullptr;
   p.C0 = C0;

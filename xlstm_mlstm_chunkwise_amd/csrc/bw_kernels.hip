@@ -998,6 +998,45 @@ __device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo, const float
   }
 }
 
+// A 64 x 64 tile of a packed chunk state (16-row steps kk0 .. kk0 + 3,
+// 32-column blocks nb0, nb0 + 1; layout in device_common.h) as [k][v] bf16 hi
+// and lo planes.  Thread t owns fragment lanes t and t + 256: its four
+// 16-byte pieces (hi, lo of each) travel in x's registers.  The planes are
+// the split of the float32 state already (hi + lo is exact in float32).
+__device__ __forceinline__ void pre_packed(float (&x)[16], const uint16_t* P, int DV, int kk0, int nb0) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = threadIdx.x + 256 * j, f = idx >> 6, lane = idx & 63;
+#pragma unroll
+    for (int plane = 0; plane < 2; ++plane) {
+      const uint4 u = *reinterpret_cast<const uint4*>(P + pack_frag_offset(kk0 + (f >> 1), nb0 + (f & 1), plane, DV) +
+                                                      lane * 8);
+      x[8 * j + 4 * plane + 0] = __uint_as_float(u.x);
+      x[8 * j + 4 * plane + 1] = __uint_as_float(u.y);
+      x[8 * j + 4 * plane + 2] = __uint_as_float(u.z);
+      x[8 * j + 4 * plane + 3] = __uint_as_float(u.w);
+    }
+  }
+}
+
+__device__ __forceinline__ void put_packed(uint16_t* hi, uint16_t* lo, const float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = threadIdx.x + 256 * j, f = idx >> 6, lane = idx & 63;
+    const int v = 32 * (f & 1) + (lane & 31);
+#pragma unroll
+    for (int plane = 0; plane < 2; ++plane) {
+      uint16_t* dst = plane ? lo : hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = __float_as_uint(x[8 * j + 4 * plane + (e >> 1)]);
+        const int k = 16 * (f >> 1) + (e < 4 ? 0 : 8) + 4 * (lane >> 5) + (e & 3);
+        dst[k * kLd16 + v] = (uint16_t)(e & 1 ? w >> 16 : w & 0xffff);
+      }
+    }
+  }
+}
+
 template <int MODE, bool SIG, int NY>
 __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   constexpr int W = 16 * NY;
@@ -1056,7 +1095,14 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
       constexpr int NYC = W / kT;
       const int nxc = own_D / kT;
       // state tile of (x chunk, y chunk): [k][v] for dq/dk, transposed to [v][k] for dv
+      const uint16_t* Pk = nullptr;  // dq: packed states, rows k, columns v
+      if constexpr (MODE == kModeDQ)
+        if (p.C_packed) Pk = p.C_packed + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
       auto pre_state = [&](float (&x)[16], int xi, int yc) {
+        if (Pk) {
+          pre_packed(x, Pk, DV, (y0 + yc * kT) / 16, xi * 2);
+          return;
+        }
         if constexpr (MODE == kModeDV) pre16(x, St, false, xi * kT, DV, y0 + yc * kT, kT);
         else pre16(x, St, false, y0 + yc * kT, DV, xi * kT, kT);
       };
@@ -1069,6 +1115,7 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
         __syncthreads();
         if (yc == 0) put_rows(s_w[0], own_split ? s_w[1] : nullptr, pw, own_split && !SIG ? g_own.invz : nullptr);
         if constexpr (MODE == kModeDV) put_cols(s_y[0], s_y[1], py, nullptr);
+        else if (Pk) put_packed(s_y[0], s_y[1], py);
         else put_rows(s_y[0], s_y[1], py, nullptr);
         __syncthreads();
         if (yc + 1 < NYC) {

@@ -131,6 +131,8 @@ struct BwParams {
   const float* m_rows;   // (BH, S) exp gate
   const float* den_rows; // (BH, S) exp gate
   const float* C_states; // (BH, Nc + 1, DK, DV) float32 row-major: state entering each chunk
+  const uint16_t* C_packed;  // the same states in the packed bf16 hi + lo layout, or null; the
+                             // bf16 dq pass then reads these instead of C_states
   const float* n_states; // (BH, Nc + 1, DK) exp gate
   const float* m_states; // (BH, Nc + 1) exp gate
   const float* C0;       // may be null (for dm0)
