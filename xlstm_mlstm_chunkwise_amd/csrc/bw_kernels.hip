@@ -143,14 +143,26 @@ __global__ __launch_bounds__(256) void bw_prep_kernel(const BwParams p) {
     }
   }
   if constexpr (!SIG) {
+    // float32 dH on 16-byte boundaries: 16-byte loads, the row's pieces all
+    // in flight at once
+    const bool vec = !p.dh_bf16 && (p.DV & 255) == 0 && (reinterpret_cast<uintptr_t>(p.dH) & 15) == 0;
     for (int r = wave; r < Lc; r += 4) {
       const size_t row = rb + r;
       float d = 0.0f;
-      for (int e = lane; e < p.DV; e += 64) {
-        const size_t i = row * p.DV + e;
-        const float dh = p.dh_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.dH)[i])
-                                   : static_cast<const float*>(p.dH)[i];
-        d += dh * p.H[i];
+      if (vec) {
+        const float4* a = reinterpret_cast<const float4*>(static_cast<const float*>(p.dH) + row * p.DV);
+        const float4* b = reinterpret_cast<const float4*>(p.H + row * p.DV);
+        for (int e = lane; e < p.DV / 4; e += 64) {
+          const float4 x = a[e], y = b[e];
+          d += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        }
+      } else {
+        for (int e = lane; e < p.DV; e += 64) {
+          const size_t i = row * p.DV + e;
+          const float dh = p.dh_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.dH)[i])
+                                     : static_cast<const float*>(p.dH)[i];
+          d += dh * p.H[i];
+        }
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
