@@ -377,8 +377,9 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,
  *   mlstm_bw_recompute: the forward quantities the gradient needs, into the
  *       workspace (two-stage forward kernels: chunk states, and for the exp
  *       gate H in float32 with the per-row m and normaliser).
- *   mlstm_bw_grads: the gradient kernels on that workspace (float32 on fp32
- *       matrix cores): per-position gate terms, the state-gradient recurrence
+ *   mlstm_bw_grads: the gradient kernels on that workspace (bf16 inputs:
+ *       bf16 matrix cores, computed operands as bf16 hi + lo pairs; float32
+ *       inputs: fp32 matrix cores): per-position gate terms, the state-gradient recurrence
  *       over the chunks in reverse order, dQ, dK, dV per 64-row tile, and the
  *       gate gradients by a reverse scan over the sequence.  The workspace's
  *       forward quantities are only read; its other regions are scratch. */
