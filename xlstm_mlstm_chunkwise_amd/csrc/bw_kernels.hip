@@ -524,7 +524,8 @@ __global__ __launch_bounds__(256) void bw_tiles_kernel(const BwParams p) {
 // is carried as a bf16 hi + lo pair, so a product with one computed side
 // takes two passes and one with two computed sides three (hi.hi + hi.lo +
 // lo.hi).  LDS tiles hold bf16 bits, row stride kLd16.  The output product
-// reads its A operand from a transposed tile [y][partner row]; its B operand
+// reads its A operand from a row-major tile [partner row][y] with transposing
+// reads (frag16_tr); its B operand
 // is the pair of score accumulators (partner blocks 2p, 2p+1) split to bf16:
 // slot e stands for partner row 32 p + 16 (e / 4) + 4 (l / 16) + e % 4.
 constexpr int kLd16 = 72;
@@ -560,11 +561,21 @@ __device__ __forceinline__ bf16x8_t frag16(const uint16_t* t, int row, int k0) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(t + row * kLd16 + k0));
 }
 
-// A fragment of the output product from a transposed tile: row y, slots
-// e = 0..3 at partner rows o0 .. o0+3 and e = 4..7 at o0+16 .. o0+19.
-__device__ __forceinline__ bf16x8_t frag16_pair(const uint16_t* t, int y, int o0) {
-  const uint2 a = *reinterpret_cast<const uint2*>(t + y * kLd16 + o0);
-  const uint2 b = *reinterpret_cast<const uint2*>(t + y * kLd16 + o0 + 16);
+// A fragment (lane l supplies row l % 16 of A, slots e = 0..7) read from a
+// row-major LDS tile X whose rows run along A's contraction axis: slots 0..3
+// from rows r0 .. r0+3 and slots 4..7 from rows r0+dr .. r0+dr+3, all at
+// column c0 + l % 16 (r0 carries the lane group's offset).  Two transposing
+// reads, ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element e from address a_{i/4 + 4e} + i % 4, a_j the address lane j gives;
+// lane j gives row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3.  So the tile
+// is written with row stores (16 bytes) rather than transposing ones.
+__device__ __forceinline__ bf16x8_t frag16_tr(const uint16_t* X, int r0, int dr, int c0) {
+  const int j = threadIdx.x & 15;
+  const uint16_t* base = X + (r0 + (j >> 2)) * kLd16 + c0 + 4 * (j & 3);
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(base));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(base + dr * kLd16));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
@@ -964,9 +975,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // Staging in two halves, so that the global loads of the next tile are in
 // flight while the matrix cores work on the current one: pre16 loads this
-// thread's 16 values of a tile into registers, put_rows / put_cols write them
-// to LDS (row-major or transposed) as bf16, split into hi + lo where a lo
-// plane is given (a raw bf16 value converts exactly).
+// thread's 16 values of a tile into registers, put_rows writes them to LDS
+// row-major as bf16, split into hi + lo where a lo plane is given (a raw bf16
+// value converts exactly).
 __device__ __forceinline__ void pre16(float (&x)[16], const void* src, bool bf16, size_t row0, int D, int col0,
                                       int nrows) {
   const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
@@ -991,22 +1002,6 @@ __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo, const float
     uint4* dl = reinterpret_cast<uint4*>(lo + r * kLd16 + c);
     dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-  }
-}
-
-__device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo, const float (&x)[16], const float* rowscale) {
-  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
-  const float sc = rowscale ? rowscale[r] : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    uint32_t hw, lw;
-    split_bf16x2(x[i] * sc, x[i + 1] * sc, hw, lw);
-    hi[(c + i) * kLd16 + r] = (uint16_t)(hw & 0xffff);
-    hi[(c + i + 1) * kLd16 + r] = (uint16_t)(hw >> 16);
-    if (lo) {
-      lo[(c + i) * kLd16 + r] = (uint16_t)(lw & 0xffff);
-      lo[(c + i + 1) * kLd16 + r] = (uint16_t)(lw >> 16);
-    }
   }
 }
 
@@ -1054,7 +1049,7 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   constexpr int W = 16 * NY;
   __shared__ __align__(16) uint16_t s_x[2][kT * kLd16];  // partner tile [o][x] (hi, lo)
   __shared__ __align__(16) uint16_t s_w[2][kT * kLd16];  // own tile [w][x] (hi, lo)
-  __shared__ __align__(16) uint16_t s_y[2][kT * kLd16];  // output-side operand, transposed (hi, lo)
+  __shared__ __align__(16) uint16_t s_y[2][kT * kLd16];  // output-side operand (hi, lo)
   __shared__ RowGates g_own, g_oth;
 
   const int nT = p.L / kT;
@@ -1106,7 +1101,7 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
     if (run) {
       constexpr int NYC = W / kT;
       const int nxc = own_D / kT;
-      // state tile of (x chunk, y chunk): [k][v] for dq/dk, transposed to [v][k] for dv
+      // state tile of (x chunk, y chunk): [k][v] for every mode (dv reads it transposed)
       const uint16_t* Pk = nullptr;  // dq: packed states, rows k, columns v
       if constexpr (MODE == kModeDQ)
         if (p.C_packed) Pk = p.C_packed + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
@@ -1126,8 +1121,7 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
         for (int yc = 0; yc < NYC; ++yc) {
         __syncthreads();
         if (yc == 0) put_rows(s_w[0], own_split ? s_w[1] : nullptr, pw, own_split && !SIG ? g_own.invz : nullptr);
-        if constexpr (MODE == kModeDV) put_cols(s_y[0], s_y[1], py, nullptr);
-        else if (Pk) put_packed(s_y[0], s_y[1], py);
+        if (Pk) put_packed(s_y[0], s_y[1], py);
         else put_rows(s_y[0], s_y[1], py, nullptr);
         __syncthreads();
         if (yc + 1 < NYC) {
@@ -1144,8 +1138,9 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
           if constexpr (own_split) bl_ = frag16(s_w[1], w, k0);
 #pragma unroll
           for (int yb = 0; yb < 4; ++yb) {
-            const bf16x8_t ah = frag16(s_y[0], 16 * yb + l16, k0);
-            const bf16x8_t al = frag16(s_y[1], 16 * yb + l16, k0);
+            // dv: the state tile is [k][v] in LDS (row stores); read transposed
+            const bf16x8_t ah = MODE == kModeDV ? frag16_tr(s_y[0], k0, 4, 16 * yb) : frag16(s_y[0], 16 * yb + l16, k0);
+            const bf16x8_t al = MODE == kModeDV ? frag16_tr(s_y[1], k0, 4, 16 * yb) : frag16(s_y[1], 16 * yb + l16, k0);
             float4_t a_ = acc[4 * yc + yb];
             a_ = mma16b(ah, bh_, a_);
             a_ = mma16b(al, bh_, a_);
@@ -1294,7 +1289,8 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
 #pragma unroll
     for (int yc = 0; yc < NYC; ++yc) {
       __syncthreads();
-      put_cols(s_y[0], y_split ? s_y[1] : nullptr, py, y_split && !SIG ? g_oth.invz : nullptr);
+      // Y stays [o][y] in LDS (row stores) and is read transposed
+      put_rows(s_y[0], y_split ? s_y[1] : nullptr, py, y_split && !SIG ? g_oth.invz : nullptr);
       __syncthreads();
       if (yc + 1 < NYC) pre16(py, y_src, y_bf16, rb + x0, y_D, y0 + (yc + 1) * kT, nx);
 #pragma unroll
@@ -1302,10 +1298,10 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
         float4_t a_ = acc[4 * yc + yb];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const bf16x8_t ah = frag16_pair(s_y[0], 16 * yb + l16, 32 * q + 4 * g4);
+          const bf16x8_t ah = frag16_tr(s_y[0], 32 * q + 4 * g4, 16, 16 * yb);
           a_ = mma16b(ah, bsh[q], a_);
           a_ = mma16b(ah, bsl[q], a_);
-          if constexpr (y_split) a_ = mma16b(frag16_pair(s_y[1], 16 * yb + l16, 32 * q + 4 * g4), bsh[q], a_);
+          if constexpr (y_split) a_ = mma16b(frag16_tr(s_y[1], 32 * q + 4 * g4, 16, 16 * yb), bsh[q], a_);
         }
         acc[4 * yc + yb] = a_;
       }
