@@ -734,6 +734,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
   float nreg = 0.0f;  // N for key row kt * TK + tid (tid < TK)
 
+  // Q and dH of this head through buffer resources; a block's first row is
+  // added to the lane offset, so rows past the sequence fall outside the
+  // range check and read as zero.
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.Q) + gbase * DK + kt * TK,
                                               (uint32_t)(((size_t)S * DK - kt * TK) * 2));
   const __amdgpu_buffer_rsrc_t rd =
@@ -754,18 +757,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
     const int trow = t0 + tb;
+    const int qo = qvoff + trow * DK * 2;
     if constexpr (EPT == 2) {
-      qr[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rq, qvoff, trow * DK * 2, 0);
+      qr[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rq, qo, 0, 0);
     } else if constexpr (EPT == 4) {
-      const v2i32_t q2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qvoff, trow * DK * 2, 0);
+      const v2i32_t q2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qo, 0, 0);
       qr[s] = make_uint2((uint32_t)q2.x, (uint32_t)q2.y);
     } else {
-      qr[s] = buf_load16(rq, qvoff, trow * DK * 2);
+      qr[s] = buf_load16(rq, qo);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int f = i * 64 + lane, row = RW * wave + f / VSEG, seg = f % VSEG;
-      dr[s][i] = buf_load16_nt(rd, (row * DV + seg * VE) * (DHB ? 2 : 4), trow * DV * (DHB ? 2 : 4));
+      dr[s][i] = buf_load16_nt(rd, ((trow + row) * DV + seg * VE) * (DHB ? 2 : 4));
     }
     const int t = trow + krs;
     const bool ok = t < S;

@@ -380,22 +380,40 @@ __device__ __forceinline__ uint4 frag_row_u(const uint16_t* X, int ld, int r0, i
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // Raw buffer access: a 128-bit resource (base address, byte extent, 32-bit
-// data format for untyped loads) in scalar registers, a per-lane byte offset
-// and a wave-uniform byte offset.  Reads at or past the extent return zero.
+// data format for untyped loads) in scalar registers and a per-lane byte
+// offset.  The hardware range check covers the lane offset and the
+// instruction's immediate offset, not the scalar offset operand, so these
+// helpers use no scalar offset where a row can lie past the data: a
+// wave-uniform offset (a row block, a tile start) is folded into the resource
+// by make_rsrc_at instead, which moves the base and shrinks the extent, and
+// the steps inside a tile go in the lane offset.  Reads at or past the extent return
+// zero and stores there are dropped.
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+// The bytes [off, extent) of the range at `base`, as a resource starting at
+// base + off (empty when off >= extent).  off must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_at(const void* base, uint32_t extent, uint32_t off) {
+  return make_rsrc(static_cast<const char*>(base) + off, off < extent ? extent - off : 0u);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
 // The same with the non-temporal hint (aux 2), for data read once that should
 // not displace lines other workgroups re-read from L2.
-__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, int voff) {
+  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+// A load with a scalar offset, for a resource every byte of which the
+// kernel reads whole (a complete chunk state): soff + voff is in range by
+// construction, so the unchecked scalar offset cannot reach past the data.
+__device__ __forceinline__ uint4 buf_load16_whole(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4i32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 

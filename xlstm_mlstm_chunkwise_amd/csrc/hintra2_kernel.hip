@@ -153,14 +153,15 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * (Nc + 1) + c_) * DK * DV * 2;
   };
   // Chunk-state fragments through a buffer resource: lane offset and the
-  // wave's first 32-column block in one VGPR, the k step in a scalar offset,
-  // the column block and plane as immediates.
+  // wave's first 32-column block in one VGPR, the k step in a scalar offset
+  // (a state is read whole, so every offset is in range), the column block
+  // and plane as immediates.
   auto load_k = [&](__amdgpu_buffer_rsrc_t rs, int v0_, int kk) {
     const int voff = lane * 16 + ((v0_ + wc0) >> 5) * 2048;
 #pragma unroll
     for (int cb = 0; cb < W::CB; ++cb) {
-      bb[kk][cb][0] = buf_load16(rs, voff + cb * 2048, kk * DV * 64);
-      if constexpr (SPLIT) bb[kk][cb][1] = buf_load16(rs, voff + cb * 2048 + 1024, kk * DV * 64);
+      bb[kk][cb][0] = buf_load16_whole(rs, voff + cb * 2048, kk * DV * 64);
+      if constexpr (SPLIT) bb[kk][cb][1] = buf_load16_whole(rs, voff + cb * 2048 + 1024, kk * DV * 64);
     }
   };
   auto state_rsrc = [&](int bh_, int c_) { return make_rsrc(state_ptr(bh_, c_), (uint32_t)(DK * DV * 4)); };
@@ -182,11 +183,12 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
       for (int e = 0; e < NPT; ++e) n_r[e] = tid + e * W::NT < DK ? nst[tid + e * W::NT] : 0.0f;
     }
-    // the Q tile is contiguous; rows past the chunk read as zero
+    // the Q tile is contiguous; rows past the chunk read as zero (the step of
+    // each load is in the lane offset, which the range check covers)
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.Q) + (gbase + row0_) * DK,
                                                 (uint32_t)((Lc_ - row0_) * DK * 2));
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16_nt(rq, tid * 16, i * W::NT * 16);
+    for (int i = 0; i < QPT; ++i) qpre[i] = buf_load16_nt(rq, tid * 16 + i * W::NT * 16);
   };
 
   int tile = next_tile();
@@ -332,16 +334,18 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     static_assert(W::TKV * DK / 8 % W::NT == 0 && W::TKV * TV / 8 % W::NT == 0, "tile split");
     uint4 kpre[KPT], vpre[VPT];
     // K and V of this chunk through buffer resources: rows past the chunk
-    // read as zero.  One lane offset each; the tile start and the 16-byte
-    // step of the thread's i-th load in scalar offsets.
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, (uint32_t)(Lc * DK * 2));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, (uint32_t)((Lc - 1) * DV * 2 + TV * 2));
+    // read as zero.  The tile start moves each resource's base; the step of
+    // the thread's i-th load is in its lane offset.
+    const uint32_t kext = (uint32_t)(Lc * DK * 2);
+    const uint32_t vext = (uint32_t)((Lc - 1) * DV * 2 + TV * 2);
     const int vvoff = (tid / (TV / 8)) * DV * 2 + (tid % (TV / 8)) * 16;
     auto load_kv = [&](int s0) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(K, kext, s0 * DK * 2);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(V, vext, s0 * DV * 2);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) kpre[i] = buf_load16(rk, tid * 16, s0 * DK * 2 + i * W::NT * 16);
+      for (int i = 0; i < KPT; ++i) kpre[i] = buf_load16(rk, tid * 16 + i * W::NT * 16);
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) vpre[i] = buf_load16(rv, vvoff, (s0 + i * (W::NT / (TV / 8))) * DV * 2);
+      for (int i = 0; i < VPT; ++i) vpre[i] = buf_load16(rv, vvoff + i * (W::NT / (TV / 8)) * DV * 2);
     };
     if (ntiles > 0) load_kv(0);
 
@@ -468,15 +472,11 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       }
     }
     __syncthreads();
-    // Each accumulator register holds one row of 32 consecutive columns across
-    // a half-wave, so each store writes two full 128-byte row segments.  Row
-    // offsets are compile-time multiples of DV; only a ragged last tile checks
-    // rows.
     // H through a buffer resource spanning this chunk's rows: stores to rows
     // past the chunk fall outside it and are dropped.  Each accumulator
     // register holds one row of 32 consecutive columns across a half-wave, so
     // each store writes two full 128-byte row segments; the row offsets are
-    // compile-time multiples of DV in scalar offsets.
+    // compile-time multiples of DV added to the lane offset.
     auto store_h = [&](auto esize) {
       constexpr int E = decltype(esize)::value;
       const __amdgpu_buffer_rsrc_t rh = make_rsrc(static_cast<const char*>(p.H) + ((size_t)bh * S + t0) * DV * E,
@@ -492,15 +492,16 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const int hro = hvoff + (rowl + q) * DV * E;
 #pragma unroll
             for (int cb = 0; cb < W::CB; ++cb) {
               // non-temporal (aux 2): H is not read again here, so it should
               // not push the state and K/V lines of sibling row tiles out of L2
               const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
               if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 2);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hro + 32 * cb * E, 0, 2);
               else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff + 32 * cb * E, (rowl + q) * DV * E, 2);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hro + 32 * cb * E, 0, 2);
             }
           }
         }

@@ -385,10 +385,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   uint4 vr[2][VPT];
   // K, V and the input terms of this head through buffer resources: rows past
   // the end of the sequence read as zero and get weight zero.  Only the last
-  // chunk can be short, so that bound is also the chunk's.
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, (uint32_t)(((size_t)S * DK - kt * TK) * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, (uint32_t)((size_t)S * DV * 2));
-  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.gu2 + gbase, (uint32_t)((size_t)S * 4));
+  // chunk can be short, so that bound is also the chunk's.  The block's first
+  // row moves each resource's base and the steps inside the block are in the
+  // lane offset (the range check does not see a scalar offset).
+  const uint32_t kext = (uint32_t)(((size_t)S * DK - kt * TK) * 2);
+  const uint32_t vext = (uint32_t)((size_t)S * DV * 2);
+  const uint32_t uext = (uint32_t)((size_t)S * 4);
   const int kvoff = (krs * DK + kcs) * 2;
   const int vvoff = ((tid / VSEG) * DV + (tid % VSEG) * 8) * 2;
   auto load_blk = [&](auto set, int gi) {
@@ -396,15 +398,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int c = c_beg + (gi >> lbpc), tb = (gi & (BPC - 1)) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
     const int trow = t0 + tb;  // first time row of the block
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(K, kext, trow * DK * 2);
     if constexpr (EPT == 4) {
-      const v2i32_t k2 = __builtin_amdgcn_raw_buffer_load_b64(rk, kvoff, trow * DK * 2, 0);
+      const v2i32_t k2 = __builtin_amdgcn_raw_buffer_load_b64(rk, kvoff, 0, 0);
       kr[s] = make_uint2((uint32_t)k2.x, (uint32_t)k2.y);
     } else {
-      kr[s] = buf_load16_nt(rk, kvoff, trow * DK * 2);
+      kr[s] = buf_load16_nt(rk, kvoff);
     }
-    ur[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, krs * 4, trow * 4, 0));
+    ur[s] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc_at(p.gu2 + gbase, uext, trow * 4), krs * 4, 0, 0));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(V, vext, trow * DV * 2);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) vr[s][i] = buf_load16(rv, vvoff, (trow + i * (NT / VSEG)) * DV * 2);
+    for (int i = 0; i < VPT; ++i) vr[s][i] = buf_load16(rv, vvoff + i * (NT / VSEG) * DV * 2);
     if (tb == 0) {
       g2r[s] = p.gb2[gbase + t0 + Lc - 1];
       pmr[s] = SIG ? 0.0f : p.gpm2[gbase + t0 + Lc - 1];

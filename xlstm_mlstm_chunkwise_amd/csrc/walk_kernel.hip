@@ -190,9 +190,11 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
     auto load_q = [&]() {
       if (qc >= Nc) return;
       const int t0 = qc * L, Lc = chunk_len(qc), r0 = qi * TQ;
+      // rows past the chunk read as zero: the load steps are in the lane
+      // offset, which the range check covers
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (size_t)(t0 + r0) * DK, (uint32_t)((Lc - r0) * DK * 2));
 #pragma unroll
-      for (int e = 0; e < QPT; ++e) qpre[e] = buf_load16(rq, tid * 16, e * NA * 16);
+      for (int e = 0; e < QPT; ++e) qpre[e] = buf_load16(rq, tid * 16 + e * NA * 16);
       if (++qi >= nsub_of(Lc)) {
         qi = 0;
         ++qc;
@@ -205,10 +207,10 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       const __amdgpu_buffer_rsrc_t rv =
           make_rsrc(Vh + (size_t)(t0 + k0) * DV, (uint32_t)(((Lc - k0 - 1) * DV + TVS) * 2));
 #pragma unroll
-      for (int e = 0; e < KPT; ++e) kpre[e] = buf_load16(rk, tid * 16, e * NA * 16);
+      for (int e = 0; e < KPT; ++e) kpre[e] = buf_load16(rk, tid * 16 + e * NA * 16);
 #pragma unroll
       for (int e = 0; e < VPT; ++e)
-        vpre[e] = buf_load16(rv, ((tid / VG) * DV + (tid % VG) * 8) * 2, e * (NA / VG) * DV * 2);
+        vpre[e] = buf_load16(rv, ((tid / VG) * DV + (tid % VG) * 8) * 2 + e * (NA / VG) * DV * 2);
       if (++kj >= nkt_of(Lc, ki)) {
         kj = 0;
         if (++ki >= nsub_of(Lc)) {
@@ -483,6 +485,8 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         }
         auto store_h = [&](auto esize) {
           constexpr int E = decltype(esize)::value;
+          // rows past the chunk fall outside the resource and are dropped (the
+          // row and column steps are in the lane offset)
           const __amdgpu_buffer_rsrc_t rh =
               make_rsrc(static_cast<const char*>(p.H) + ((gbase + t0 + row0) * DV + v0) * E,
                         (uint32_t)(((Lc - row0 - 1) * DV + TVS) * E));
@@ -498,15 +502,15 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float hv = (hacc[cb][r] + wv[r] * xv[r]) * iv[r];
-              const int soff = (r * DV + 16 * cb) * E;
+              const int hro = hvoff + (r * DV + 16 * cb) * E;
               // plain stores: a store instruction covers 64-byte pieces of
               // H rows, which L2 merges into whole lines (with the streaming
               // hint each piece went out on its own and the written bytes
               // grew by half)
               if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hvoff, soff, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hro, 0, 0);
               else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hvoff, soff, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hro, 0, 0);
             }
           }
         };
