@@ -39,8 +39,10 @@
  *        H         (B, NH, S, DHV)    h_dtype
  *     Q, K, V and H must be 16-byte aligned; everything else 4-byte aligned.
  *   - The caller owns every buffer, including the workspace.  The library
- *     allocates no device memory and keeps no mutable global state.  Inputs
- *     are never written.  Outputs must not alias inputs.
+ *     allocates no device memory and keeps no mutable global state, except
+ *     for mlstm_chunkwise_fw_noalloc's static workspace (one array per GPU,
+ *     part of the loaded code object).  Inputs are never written.  Outputs
+ *     must not alias inputs.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Results are ready when the stream has finished.
  *   - Every call validates all arguments on the host before it launches
@@ -219,6 +221,34 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        float* C_out, float* n_out, float* m_out,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Size of the static workspace of mlstm_chunkwise_fw_noalloc (64 MiB). */
+#define MLSTM_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+/* mlstm_chunkwise_fw for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same forward pass, same arguments without the workspace,
+ * which comes from a static device array of MLSTM_NOALLOC_WORKSPACE_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * The call allocates nothing.  When the workspace of the kernels that run
+ * exceeds that size the call is refused with MLSTM_E_WORKSPACE before
+ * anything is launched: where the fused walker runs (schedule FUSED, or AUTO
+ * on a shape it covers) that is only its gate terms, 12 bytes per position
+ * and head for the exp gate (B * NH * S up to 5.5 M positions); the
+ * two-stage kernels need mlstm_fw_workspace_bytes(desc), mostly chunk
+ * states, so they fit for small problems only.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give wrong results; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start at zero (every region a kernel
+ * reads is written earlier in the same call).  The first call on a device
+ * looks up the array's device address (MLSTM_E_HIP if that fails). */
+int mlstm_chunkwise_fw_noalloc(const mlstm_fw_desc_t* desc,
+                               const void* Q, const void* K, const void* V,
+                               const float* i_pre, const float* f_pre,
+                               const float* C0, const float* n0, const float* m0,
+                               void* H,
+                               float* C_out, float* n_out, float* m_out,
+                               void* stream);
 
 /* Stage one, the inter-chunk recurrence: writes into `workspace` the
  * stabilised state entering each chunk c = 0..N_c-1 (entry 0 is the initial

@@ -342,3 +342,29 @@ def test_flops_formula():
     # 7B-shaped heads, S=8192, chunk 256: 378.4 GFLOP
     f = mt.flops(8, 8, 8192, 256, 512, 256)
     assert abs(f / 1e9 - 378.4) < 0.1
+
+
+def test_noalloc_entry_point_refuses_before_launch():
+    """mlstm_chunkwise_fw_noalloc checks its arguments, then the size of the
+    workspace the chosen kernels need against its static array, before any
+    device call."""
+    lib = mt.lib()
+    names = ["Q", "K", "V", "i", "f", "C0", "n0", "m0", "H", "C_out", "n_out", "m_out"]
+
+    def call(desc, **ptrs):
+        vals = [ptrs.get(n, 4096) for n in names]
+        return lib.mlstm_chunkwise_fw_noalloc(ctypes.byref(desc) if desc is not None else None, *vals, None)
+
+    d = _desc()
+    assert call(None) == 1
+    assert call(d, Q=None) == 1
+    assert call(d, H=4096 + 8) == 8
+    assert call(_desc(DHQK=100)) == 2
+    assert call(_desc(gate="sig"), n0=4096) == 5
+    # two-stage kernels at the 7B-shaped heads: 1.1 GB of chunk states
+    big = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256, schedule=mt.MLSTM_SCHED_TWO_STAGE)
+    assert mt.workspace_bytes(big) > mt.NOALLOC_WORKSPACE_BYTES
+    assert call(big) == 6
+    # the walker's gate terms beyond the array: 64 * 2^17 positions x 12 bytes
+    huge = _desc(B=64, NH=1, S=1 << 17, DHQK=256, DHV=512, chunk_size=256)
+    assert call(huge) == 6

@@ -61,6 +61,7 @@ _SYMBOLS = {
     "mlstm_fw_kernel_family": (ctypes.c_int, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_fw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_chunkwise_fw_noalloc": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
     "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 8
                         + [ctypes.c_size_t] + [ctypes.c_void_p] * 4),
     "mlstm_fw_hintra": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 6
@@ -245,6 +246,37 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     if st:
         raise MlstmError(st, "mlstm_chunkwise_fw")
+    return H, C_out, n_out, m_out
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20   # MLSTM_NOALLOC_WORKSPACE_BYTES
+
+
+def mlstm_chunkwise_fw_noalloc(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
+                               gate: str = "exp", precision: str = "split", qk_scale: Optional[float] = None,
+                               eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto",
+                               out=None, C_out=None, n_out=None, m_out=None):
+    """mlstm_chunkwise_fw on the library's static workspace
+    (mlstm_chunkwise_fw_noalloc): no workspace argument, and nothing is
+    allocated when every output is given (out = H, whose dtype is the H
+    dtype; C_out, n_out, m_out may be None: not written).  Returns
+    (H, C_out, n_out, m_out).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
+    _check(C0, "C0", (B, NH, DK, DV), torch.float32)
+    _check(n0, "n0", (B, NH, DK), torch.float32)
+    _check(m0, "m0", (B, NH), torch.float32)
+    H = out if out is not None else torch.empty((B, NH, S, DV), dtype=torch.float32, device=q.device)
+    _check(H, "H", (B, NH, S, DV))
+    _check(C_out, "C_out", (B, NH, DK, DV), torch.float32)
+    _check(n_out, "n_out", (B, NH, DK), torch.float32)
+    _check(m_out, "m_out", (B, NH), torch.float32)
+    desc = _desc_for(q, v, chunk_size, gate, H.dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule)
+    st = lib().mlstm_chunkwise_fw_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
+        _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
+    if st:
+        raise MlstmError(st, "mlstm_chunkwise_fw_noalloc")
     return H, C_out, n_out, m_out
 
 

@@ -3,6 +3,7 @@
 // contract of every entry point.
 #include <math.h>
 #include <initializer_list>
+#include <mutex>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -454,24 +455,89 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, s
                        static_cast<hipStream_t>(stream));
 }
 
-int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
-                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
-                       void* H, float* C_out, float* n_out, float* m_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of the forward pass's arguments other than the workspace.
+int check_fw_args(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                  const float* f_pre, const float* C0, const float* n0, const float* m0, const void* H,
+                  const float* C_out, const float* n_out, const float* m_out) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
   if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
     return MLSTM_E_ALIGN;
-  if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, C_out, n_out, m_out})) != MLSTM_OK) return st;
-  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  return check_f32_ptrs({i_pre, f_pre, C0, n0, m0, C_out, n_out, m_out});
+}
+
+// The forward pass on a checked workspace.
+int run_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+           const float* f_pre, const float* C0, const float* n0, const float* m0, void* H, float* C_out,
+           float* n_out, float* m_out, void* workspace, hipStream_t s) {
   const WsPtrs ws = ws_ptrs(desc, workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_fused(desc)) return run_fused(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
-  st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
+  const int st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
   if (st != MLSTM_OK) return st;
   return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);
+}
+
+// ---- workspace of the allocation-free forward pass: a static device array
+// (each GPU that loads the library holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel: on the host it
+// is only a stand-in, so its device address is looked up once per device
+// with that device current, and that address is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[MLSTM_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLSTM_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLSTM_E_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MLSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       void* H, float* C_out, float* n_out, float* m_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = check_fw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out);
+  if (st != MLSTM_OK) return st;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  return run_fw(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, workspace,
+                static_cast<hipStream_t>(stream));
+}
+
+int mlstm_chunkwise_fw_noalloc(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                               const float* i_pre, const float* f_pre, const float* C0, const float* n0,
+                               const float* m0, void* H, float* C_out, float* n_out, float* m_out,
+                               void* stream) {
+  int st = check_fw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out);
+  if (st != MLSTM_OK) return st;
+  // the workspace of the kernels that run: where the automatic schedule
+  // picks the fused walker, only its gate terms
+  mlstm_fw_desc_t d = *desc;
+  if (use_fused(&d)) d.schedule = MLSTM_SCHED_FUSED;
+  const size_t need = ws_layout(&d).total;
+  if (need > (size_t)MLSTM_NOALLOC_WORKSPACE_BYTES) return MLSTM_E_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_address(&ws)) != MLSTM_OK) return st;
+  return run_fw(&d, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, ws,
+                static_cast<hipStream_t>(stream));
 }
 
 int mlstm_recurrent_step(const mlstm_fw_desc_t* desc, const void* q, const void* k, const void* v,
