@@ -128,6 +128,25 @@ def _oracle_head(args):
     return time.perf_counter() - t0
 
 
+# Worker processes of the CPU baseline: every core of this process's
+# affinity set, up to 16 (a one-GPU machine's share of its host's cores).
+MAX_CPU_WORKERS = 16
+
+
+def host_cpu() -> dict:
+    """The host's CPU model (from /proc/cpuinfo) and its affinity core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(name: str, budget_s: float) -> dict:
     """Time the float64 recurrent oracle on a bounded sample of the workload.
 
@@ -136,7 +155,7 @@ def cpu_baseline(name: str, budget_s: float) -> dict:
     single head exceeds the budget); tokens/s counts NH heads per token."""
     from workloads import WORKLOADS
     w = WORKLOADS[name]
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
     # probe the per-step cost on a short prefix
     probe_steps = min(w.S, 256)
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
@@ -161,8 +180,9 @@ def cpu_baseline(name: str, budget_s: float) -> dict:
     used = min(cores, n_heads)
     return {"value": tokens / wall, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": (f"float64 recurrent oracle, {n_heads} of {w.BH} heads x {steps} of {w.S} steps "
-                       f"({w.name}), {used} worker processes with 1 BLAS thread each; "
-                       f"tokens/s counts {w.NH} heads per token; wall {wall:.1f} s")}
+                       f"({w.name}), {used} worker processes with 1 BLAS thread each (affinity cores "
+                       f"up to {MAX_CPU_WORKERS}); tokens/s counts {w.NH} heads per token; wall {wall:.1f} s"),
+            **host_cpu()}
 
 
 def path_dtype(mt, desc, precision: str) -> str:
@@ -172,11 +192,9 @@ def path_dtype(mt, desc, precision: str) -> str:
     fam = mt.kernel_family(desc)
     if fam == mt.MLSTM_FAMILY_F64:
         return "f64-valu/f64-acc"
-    wide = fam in (mt.MLSTM_FAMILY_WIDE, mt.MLSTM_FAMILY_FUSED)
     if desc.qkv_dtype == mt.MLSTM_F32:
         return "f32-mfma/f32-acc"
-    t = "bf16" if wide else "f16"
-    return f"{t}x2-mfma/f32-acc" if precision == "split" else f"{t}-mfma/f32-acc"
+    return "bf16x2-mfma/f32-acc" if precision == "split" else "bf16-mfma/f32-acc"
 
 
 def main(argv=None) -> int:
@@ -381,7 +399,7 @@ def cpu_baseline_backward(name: str, budget_s: float, S: int = 2048) -> dict:
     from oracle import grad_fw
     from workloads import WORKLOADS, head_inputs
     w = WORKLOADS[name]
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
     torch.set_num_threads(cores)
     dH = np.random.default_rng(7).standard_normal((1, S, w.DHV))
     n_heads, t_used = 0, 0.0
@@ -394,7 +412,7 @@ def cpu_baseline_backward(name: str, budget_s: float, S: int = 2048) -> dict:
     return {"value": n_heads * S / w.NH / t_used, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"float64 gradient oracle (autograd over the quadratic form), {n_heads} of {w.BH} heads "
                        f"x the first {S} of {w.S} positions ({w.name}), one process on {cores} torch threads; "
-                       f"tokens/s counts {w.NH} heads per token; oracle time {t_used:.1f} s")}
+                       f"tokens/s counts {w.NH} heads per token; oracle time {t_used:.1f} s"), **host_cpu()}
 
 
 def bench_backward(args, w, mt, torch, np, inputs) -> int:

@@ -86,14 +86,10 @@ typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
  * keys in K^T.V).  With bf16 inputs the raw Q, K, V enter the matrix cores
  * unchanged; the computed operand is rounded to nearest-even in one of two
  * ways, and every product accumulates in fp32:
- *   MLSTM_PREC_SPLIT: the operand is carried as a hi + lo pair of 16-bit
- *                     values (two MFMA passes).  The head shapes with
- *                     DHQK in {128, 256} and DHV in {256, 512} use bf16
- *                     pairs (about 16 significant bits); the other shapes
- *                     use fp16 pairs (about 21 bits, Q, K, V converted
- *                     to fp16, which is exact for bf16 values of magnitude
- *                     in [2^-14, 65504]).  Default.
- *   MLSTM_PREC_F16:   a single 16-bit rounding of the operand (one pass).
+ *   MLSTM_PREC_SPLIT: the operand is carried as a hi + lo pair of bf16
+ *                     values (two MFMA passes, about 16 significant bits).
+ *                     Default.
+ *   MLSTM_PREC_F16:   a single bf16 rounding of the operand (one pass).
  *   MLSTM_PREC_F64:   everything (gates, scores, contractions, chunk states)
  *                     in fp64 on the vector units; for rows whose sums cancel
  *                     too strongly for fp32 accumulation.  Workspace states
@@ -127,7 +123,8 @@ typedef struct {
                           S * max(DHQK, DHV) < 2^29 (else MLSTM_E_SHAPE)     */
   int32_t DHQK, DHV;   /* head dims: multiples of 64, at most 512 (float32
                           inputs: DHQK at most 256)                           */
-  int32_t chunk_size;  /* L: power of two, 64..1024                           */
+  int32_t chunk_size;  /* L: power of two, 16..1024 (16 and 32: the generic
+                          and float64 kernels, one tile per chunk)          */
   int32_t qkv_dtype;   /* mlstm_dtype_t of Q, K, V                             */
   int32_t h_dtype;     /* mlstm_dtype_t of H                                   */
   int32_t gate;        /* mlstm_gate_t                                         */
@@ -156,7 +153,7 @@ int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
 
 /* Which family of kernels mlstm_chunkwise_fw runs for a valid descriptor
  * (host-only query):
- *   MLSTM_FAMILY_GENERIC  64-row tiles, float32 row-major chunk states, fp16
+ *   MLSTM_FAMILY_GENERIC  64-row tiles, float32 row-major chunk states, bf16
  *                         (bf16 inputs) or fp32 (float32 inputs) operands
  *   MLSTM_FAMILY_WIDE     bf16 inputs with DHQK in {128, 256} and DHV in
  *                         {256, 512}, tile_lq 0 or 64 (or 128 when the
@@ -385,8 +382,10 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc);
  * The forward quantities the gradient needs are recomputed with the two-stage
  * kernels whatever desc->schedule says (the fused walker forms neither chunk
  * states nor per-row normalisers); desc->precision applies to that
- * recomputation.  The gradient kernels compute in float32 on fp32 matrix
- * cores.  No gradient flows in through the final state.  For the sig gate n0,
+ * recomputation.  The gradient kernels accumulate in float32: with bf16
+ * inputs on bf16 matrix cores (Q, K, V raw, every computed operand as a bf16
+ * hi + lo pair), with float32 inputs on fp32 matrix cores.  No gradient
+ * flows in through the final state.  For the sig gate n0,
  * m0, dn0 and dm0 must be NULL.  Outputs must not alias inputs.  With S == 0
  * only dC0, dn0 and dm0 are written (zeros). */
 int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,

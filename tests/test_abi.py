@@ -118,7 +118,7 @@ def test_valid_descriptor_and_workspace_size():
     (dict(B=0), 2), (dict(NH=-1), 2), (dict(S=-5), 2),
     (dict(S=1 << 20, DHQK=64, DHV=512), 2), (dict(S=1 << 21, DHQK=256, DHV=256), 2),
     (dict(DHQK=96), 2), (dict(DHQK=1024), 2), (dict(DHV=32), 2), (dict(DHV=576), 2),
-    (dict(chunk_size=96), 3), (dict(chunk_size=32), 3), (dict(chunk_size=2048), 3),
+    (dict(chunk_size=96), 3), (dict(chunk_size=8), 3), (dict(chunk_size=2048), 3),
     (dict(tile_lq=48), 3), (dict(tile_lkv=256), 3),
     (dict(qkv_dtype=7), 4), (dict(h_dtype=-1), 4),
     (dict(gate=2), 9), (dict(precision=5), 9), (dict(eps=-1.0), 9), (dict(eps=float("nan")), 9),
@@ -368,3 +368,20 @@ def test_noalloc_entry_point_refuses_before_launch():
     # the walker's gate terms beyond the array: 64 * 2^17 positions x 12 bytes
     huge = _desc(B=64, NH=1, S=1 << 17, DHQK=256, DHV=512, chunk_size=256)
     assert call(huge) == 6
+
+
+def test_short_chunks_run_on_the_generic_kernels():
+    """Chunks of 16 and 32 rows are valid: the generic (and float64) kernels
+    take one tile per chunk; the backward runs its kernels on chunks of 64
+    (its result does not depend on the chunking), so its workspace is that
+    of chunk 64."""
+    for L in (16, 32):
+        for kw in (dict(), dict(DHQK=256, DHV=512), dict(qkv_dtype=mt.MLSTM_F32)):
+            d = _desc(chunk_size=L, **kw)
+            assert mt.validate(d) == 0
+            assert mt.kernel_family(d) == mt.MLSTM_FAMILY_GENERIC
+            assert mt.num_chunks(d) == (1000 + L - 1) // L
+            assert mt.bw_workspace_bytes(d) == mt.bw_workspace_bytes(_desc(chunk_size=64, **kw))
+        assert mt.validate(_desc(chunk_size=L, tile_lq=64)) == 3
+        assert mt.kernel_family(_desc(chunk_size=L, precision="f64")) == mt.MLSTM_FAMILY_F64
+        assert mt.validate(_desc(chunk_size=L, DHQK=256, DHV=512, schedule="fused")) == 5

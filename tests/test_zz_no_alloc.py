@@ -14,6 +14,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+from f32_chunkwise import accumulation_bound  # noqa: E402
 from oracle import recurrent_fw  # noqa: E402
 from workloads import WORKLOADS, make_inputs  # noqa: E402
 
@@ -79,9 +80,15 @@ def _check_against_oracle(w, x, o, tag):
             args = [x[nm][b, h].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
             init = [x[nm][b, h] if (w.init_state and (nm == "C0" or w.gate == "exp")) else None
                     for nm in ("C0", "n0", "m0")]
-            r = recurrent_fw(*args, *init, gate=w.gate)
+            r = recurrent_fw(*args, *init, gate=w.gate, return_rows=w.gate == "exp")
             err = np.abs(H[b, h] - r[0])
-            bound = tol + (1e-5 * np.abs(r[0]) if w.qkv_dtype == "f32" else 0.0)
+            bound = tol
+            if w.qkv_dtype == "f32":
+                # float32 accumulation bound from the row's conditioning
+                bound = accumulation_bound(*[x[nm][b, h] for nm in ("q", "k", "v", "i", "f")], *init,
+                                           chunk_size=w.chunk, gate=w.gate, H_ref=r[0],
+                                           m_rows=r[4] if w.gate == "exp" else None,
+                                           den_rows=r[5] if w.gate == "exp" else None)[0]
             assert np.all(err <= bound), f"{tag} head {(b, h)}: max|dH| {err.max():.3g}"
 
 

@@ -16,7 +16,7 @@ using mlstm::HintraParams;
 using mlstm::StatesParams;
 
 constexpr int kMaxChunk = 1024;
-constexpr int kMinChunk = 64;
+constexpr int kMinChunk = 16;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -56,7 +56,7 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   const int64_t BH = (int64_t)d->B * d->NH;
   const int64_t Nc = ((int64_t)d->S + d->chunk_size - 1) / d->chunk_size;
   if (BH > (1 << 30)) return MLSTM_E_SHAPE;
-  if (BH * Nc * (d->chunk_size / 64) > 0x7fffffffLL) return MLSTM_E_SHAPE;  // grid.x bound
+  if (BH * Nc * (d->chunk_size > 64 ? d->chunk_size / 64 : 1) > 0x7fffffffLL) return MLSTM_E_SHAPE;  // grid.x bound
   // Per-head byte extents and row offsets of the buffer-resource kernels are
   // 32-bit: a head's largest float32 row block stays below 2 GiB.
   if ((int64_t)d->S * (int64_t)(d->DHQK > d->DHV ? d->DHQK : d->DHV) >= (1LL << 29)) return MLSTM_E_SHAPE;
@@ -324,10 +324,14 @@ int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, f
 // The backward recomputes the forward quantities it needs with the two-stage
 // kernels (the walker forms no chunk states and no per-row normaliser), with
 // H in float32.
+// Chunks below 64 rows run as chunks of 64: the gradient does not depend on
+// how the sequence is cut into chunks, and the gradient kernels work in
+// 64-row tiles.
 mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
   mlstm_fw_desc_t r = *d;
   r.schedule = MLSTM_SCHED_TWO_STAGE;
   r.h_dtype = MLSTM_F32;
+  if (r.chunk_size < 64) r.chunk_size = 64;
   return r;
 }
 
@@ -759,8 +763,8 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.S = desc->S;
   p.DK = desc->DHQK;
   p.DV = desc->DHV;
-  p.L = desc->chunk_size;
-  p.Nc = (desc->S + desc->chunk_size - 1) / desc->chunk_size;
+  p.L = d2.chunk_size;
+  p.Nc = (d2.S + d2.chunk_size - 1) / d2.chunk_size;
   p.qkv_bf16 = desc->qkv_dtype == MLSTM_BF16;
   p.dh_bf16 = desc->h_dtype == MLSTM_BF16;
   const hipError_t e = mlstm::launch_bw(p, !ex, static_cast<hipStream_t>(stream));

@@ -1,7 +1,7 @@
 // Device helpers shared by the gfx950 mLSTM kernels: operand fragments for
 // the 16x16 matrix-core tiles, dtype conversion, gate math and block scans.
 //
-// Matrix-core fragment convention (v_mfma_f32_16x16x32_f16 and, for float32
+// Matrix-core fragment convention (v_mfma_f32_16x16x32_bf16 and, for float32
 // inputs, eight v_mfma_f32_16x16x4_f32 steps): a fragment is the eight
 // contraction-axis values one lane contributes to a 16 x 16 x 32 product.
 // Lane l works on row / column (l % 16) of its operand and on contraction
@@ -51,36 +51,42 @@ __device__ __forceinline__ float log_sigmoid(float x) {
 template <typename TIn>
 struct Ops;
 
-// bf16 inputs: fp16 matrix-core operands (bf16 -> fp16 is exact for
-// magnitudes in [2^-14, 65504]).
+// bf16 inputs: bf16 matrix-core operands.  Q, K, V enter unchanged (every
+// bf16 value, of any magnitude, is exact); an operand computed in float32 is
+// rounded to bf16, or carried as a bf16 hi + lo pair (about 16 significant
+// bits).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 template <>
 struct Ops<bf16_t> {
-  typedef half8_t frag;
-  typedef _Float16 lds_t;  // element type of staged input tiles
+  typedef bf16x8_t frag;
+  typedef __bf16 lds_t;  // element type of staged input tiles
   static constexpr bool kSplitCapable = true;
 
   __device__ static __forceinline__ float4_t mma(const frag& a, const frag& b, float4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ frag round(const float (&x)[8]) {
     frag f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = static_cast<_Float16>(x[e]);
+    for (int e = 0; e < 8; ++e) f[e] = static_cast<__bf16>(x[e]);
     return f;
   }
-  // x ~= hi + lo with hi = fp16(x), lo = fp16(x - hi).
+  // x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi).
   __device__ static __forceinline__ void split(const float (&x)[8], frag& hi, frag& lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      _Float16 h = static_cast<_Float16>(x[e]);
+      const __bf16 h = static_cast<__bf16>(x[e]);
       hi[e] = h;
-      lo[e] = static_cast<_Float16>(x[e] - static_cast<float>(h));
+      lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
     }
   }
-  __device__ static __forceinline__ lds_t to_lds(float x) { return static_cast<_Float16>(x); }
+  __device__ static __forceinline__ lds_t to_lds(float x) { return static_cast<__bf16>(x); }
   // Store 8 floats as operand elements at p[0..7] (16-byte aligned).
   __device__ static __forceinline__ void store8(lds_t* p, const float (&x)[8]) {
-    *reinterpret_cast<half8_t*>(p) = round(x);
+    *reinterpret_cast<bf16x8_t*>(p) = round(x);
   }
   // Load 8 consecutive inputs (16 bytes) and widen to float.
   __device__ static __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
@@ -94,13 +100,12 @@ struct Ops<bf16_t> {
   }
   // Read a fragment of 8 staged elements at p[0..7] (16-byte aligned).
   __device__ static __forceinline__ frag lds_frag(const lds_t* p) {
-    return *reinterpret_cast<const half8_t*>(p);
+    return *reinterpret_cast<const bf16x8_t*>(p);
   }
   // Fragment from two runs of 4 staged elements (8-byte aligned each).
   __device__ static __forceinline__ frag lds_frag2(const lds_t* p0, const lds_t* p1) {
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    half4_t a = *reinterpret_cast<const half4_t*>(p0);
-    half4_t b = *reinterpret_cast<const half4_t*>(p1);
+    const bf16x4_t a = *reinterpret_cast<const bf16x4_t*>(p0);
+    const bf16x4_t b = *reinterpret_cast<const bf16x4_t*>(p1);
     frag f;
     f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
     f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
@@ -333,9 +338,6 @@ __device__ __forceinline__ half4_t bf16x4_to_f16x4(uint2 u) {
 // bf16 matrix-core operands (wide kernels).  Inputs Q, K, V feed the bf16
 // MFMAs unchanged; a value computed in float32 is carried as a bf16 hi + lo
 // pair (hi = RNE(x), lo = RNE(x - hi)), about 16 significant bits.
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float16_t mma32b(const bf16x8_t& a, const bf16x8_t& b, float16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void hintra_f64_kernel(const HintraParams p) {
   __shared__ double s_vt[64][65];
   __shared__ double s_row_r[64], s_row_w[64], s_row_m[64], s_row_den[64];
 
-  const int NQT = p.L / 64;
+  const int NQT = p.L > 64 ? p.L / 64 : 1;  // chunks below 64 rows: one tile
   const TileIdx ti = xcd_tile();
   int bid = ti.x;
   const int qt = bid % NQT;
@@ -412,7 +412,7 @@ hipError_t launch_states_f64(const StatesParams& p, bool bf16_inputs, bool sig, 
 }
 
 hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream) {
-  dim3 grid((unsigned)(p.BH * p.Nc * (p.L / 64)), p.DV / 64);
+  dim3 grid((unsigned)(p.BH * p.Nc * (p.L > 64 ? p.L / 64 : 1)), p.DV / 64);
   if (bf16_inputs) {
     if (sig) hipLaunchKernelGGL((hintra_f64_kernel<bf16_t, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((hintra_f64_kernel<bf16_t, false>), grid, dim3(256), 0, stream, p);

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kTQ * 4) void hintra_kernel(const HintraParams p) {
   __shared__ __align__(16) lds_t s_vt[kTV][kTKV + kPad];   // values [v][sigma]
   __shared__ __align__(16) float s_ct[kTV][64 + 4];        // state slice [v][k]
 
-  const int NQT = p.L / kTQ;
+  const int NQT = p.L > kTQ ? p.L / kTQ : 1;  // chunks below one tile: one tile
   const TileIdx ti = xcd_tile();
   int bid = ti.x;
   const int qt = bid % NQT;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kTQ * 4) void hintra_kernel(const HintraParams p) {
 
 template <typename TIn, bool SIG, bool SPLIT, int DK, int TQ, int TKV>
 hipError_t launch_t(const HintraParams& p, hipStream_t stream) {
-  const int NQT = p.L / TQ;
+  const int NQT = p.L > TQ ? p.L / TQ : 1;
   dim3 grid((unsigned)(p.BH * p.Nc * NQT), p.DV / kTV);
   hipLaunchKernelGGL((hintra_kernel<TIn, SIG, SPLIT, DK, TQ, TKV>), grid, dim3(TQ * 4), 0, stream, p);
   return hipGetLastError();
