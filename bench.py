@@ -67,7 +67,9 @@ def algorithmic_bytes(w, h_bytes: int) -> dict:
     states: reads K, V and both gate rows, plus the initial state when given;
             writes the final state.
     hintra: reads Q, K, V and the gate rows; writes H.
-    walk:   the fused walker: hintra's bytes plus the initial and final state."""
+    walk:   the fused walker: hintra's bytes plus the initial and final state.
+    blocked: the whole blocked-schedule call (both stages per block of
+            chunks), the same algorithmic bytes as the walker."""
     el = 2 if w.qkv_dtype == "bf16" else 4
     per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
     units = w.BH * w.S
@@ -76,6 +78,7 @@ def algorithmic_bytes(w, h_bytes: int) -> dict:
         "states": units * ((w.DHQK + w.DHV) * el + 8) + init + w.BH * per_state,
         "hintra": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes),
         "walk": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes) + init + w.BH * per_state,
+        "blocked": units * ((2 * w.DHQK + w.DHV) * el + 8 + w.DHV * h_bytes) + init + w.BH * per_state,
     }
 
 
@@ -206,8 +209,10 @@ def main(argv=None) -> int:
     ap.add_argument("--precision", default="split", choices=["split", "f16", "f64"])
     ap.add_argument("--h-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--tile-lq", type=int, default=None, help="override the workload's intra-chunk row tile")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "two_stage", "fused"],
+    ap.add_argument("--schedule", default="auto", choices=["auto", "two_stage", "fused", "blocked"],
                     help="kernels of the forward pass (see mlstm_schedule_t)")
+    ap.add_argument("--block-chunks", type=int, default=0,
+                    help="chunks per block of the blocked schedule (0: the library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
@@ -279,11 +284,14 @@ def main(argv=None) -> int:
                         qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
                         h_dtype=mt.MLSTM_BF16 if args.h_dtype == "bf16" else mt.MLSTM_F32,
                         gate=w.gate, precision=args.precision, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv,
-                        schedule=args.schedule)
-    fused = mt.kernel_family(desc) == mt.MLSTM_FAMILY_FUSED
+                        schedule=args.schedule, block_chunks=args.block_chunks)
+    family = mt.kernel_family(desc)
+    fused = family in (mt.MLSTM_FAMILY_FUSED, mt.MLSTM_FAMILY_BLOCKED)
+    one_call = "blocked" if family == mt.MLSTM_FAMILY_BLOCKED else "walk"
     ws = torch.empty(max(1, mt.workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     kw = dict(chunk_size=w.chunk, gate=w.gate, h_dtype=h_dtype, precision=args.precision,
-              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, schedule=args.schedule, workspace=ws, out=H)
+              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, schedule=args.schedule, workspace=ws, out=H,
+              block_chunks=args.block_chunks)
 
     def step():
         return mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, **kw)
@@ -345,8 +353,8 @@ def main(argv=None) -> int:
     # intra = Q.C + causal Q.K^T and P.V
     f_stage = {"states": 2.0 * w.DHQK * w.DHV * w.BH * w.S,
                "hintra": (2.0 * w.DHQK * w.DHV + (w.chunk + 1) * (w.DHQK + w.DHV)) * w.BH * w.S}
-    f_stage["walk"] = f_stage["states"] + f_stage["hintra"]
-    t_stage = {"walk": t_first} if fused else {"states": t_first, "hintra": t_second}
+    f_stage["walk"] = f_stage["blocked"] = f_stage["states"] + f_stage["hintra"]
+    t_stage = {one_call: t_first} if fused else {"states": t_first, "hintra": t_second}
     f_stage = {k_: f_stage[k_] for k_ in t_stage}
     dominant = max(t_stage, key=t_stage.get)
     t_dom = t_stage[dominant]
@@ -368,7 +376,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
                    "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
                    "precision": args.precision, "tile_lq": w.tile_lq or 64,
-                   "schedule": "fused" if fused else "two_stage"},
+                   "schedule": {"walk": "fused", "blocked": "blocked"}[one_call] if fused else "two_stage"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "wall_ms_per_step": wall_ms,

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 6
+#define MLSTM_ABI_VERSION 7
 
 typedef enum {
   MLSTM_OK = 0,
@@ -115,7 +115,12 @@ typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } ml
  *       7B-shaped workloads, for both gates), TWO_STAGE otherwise.  The
  *       workspace size still covers the two stages, and stage-wise calls run
  *       them. */
-typedef enum { MLSTM_SCHED_AUTO = 0, MLSTM_SCHED_TWO_STAGE = 1, MLSTM_SCHED_FUSED = 2 } mlstm_schedule_t;
+typedef enum {
+  MLSTM_SCHED_AUTO = 0,
+  MLSTM_SCHED_TWO_STAGE = 1,
+  MLSTM_SCHED_FUSED = 2,
+  MLSTM_SCHED_BLOCKED = 3
+} mlstm_schedule_t;
 
 typedef struct {
   int32_t B, NH;       /* batch, heads: >= 1                                   */
@@ -134,7 +139,10 @@ typedef struct {
   int32_t tile_lq;     /* rows of the intra-chunk output tile; 0 = library    */
   int32_t tile_lkv;    /* key rows per intra-chunk step; 0 = library          */
   int32_t schedule;    /* mlstm_schedule_t; 0 = library choice                */
-  int32_t reserved[3]; /* must be zero                                        */
+  int32_t block_chunks; /* MLSTM_SCHED_BLOCKED: chunks per block, >= 0; 0 =
+                           library (a block's chunk states fill half of the
+                           256 MB Infinity Cache); ignored otherwise        */
+  int32_t reserved[2]; /* must be zero                                        */
 } mlstm_fw_desc_t;
 
 /* ABI version of the loaded library (MLSTM_ABI_VERSION). */
@@ -173,7 +181,8 @@ typedef enum {
   MLSTM_FAMILY_GENERIC = 0,
   MLSTM_FAMILY_WIDE = 1,
   MLSTM_FAMILY_F64 = 2,
-  MLSTM_FAMILY_FUSED = 3
+  MLSTM_FAMILY_FUSED = 3,
+  MLSTM_FAMILY_BLOCKED = 4
 } mlstm_family_t;
 int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
 

@@ -66,7 +66,7 @@ def test_binding_signatures_match_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 6
+    assert mt.abi_version() == 7
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -74,9 +74,10 @@ def test_abi_version_and_status_strings():
 
 
 def test_desc_layout_matches_header():
-    # 15 int/float fields plus reserved[3], all 4 bytes
+    # 16 int/float fields plus reserved[2], all 4 bytes
     assert ctypes.sizeof(mt.FwDesc) == 18 * 4
     assert mt.FwDesc.schedule.offset == 14 * 4
+    assert mt.FwDesc.block_chunks.offset == 15 * 4
 
 
 def _desc(**kw):
@@ -134,7 +135,10 @@ def test_validation_errors(kw, code):
 
 def test_reserved_fields_must_be_zero():
     d = _desc()
-    d.reserved[2] = 1
+    d.reserved[1] = 1
+    assert mt.validate(d) == 9
+    d = _desc()
+    d.block_chunks = -1
     assert mt.validate(d) == 9
 
 
@@ -206,7 +210,7 @@ def test_schedule_field():
     assert mt.validate(_desc(**dict(big, DHQK=128), schedule="fused")) == 5
     assert mt.validate(_desc(**dict(big, chunk_size=1024), schedule="fused")) == 5
     assert mt.validate(_desc(**big, qkv_dtype=mt.MLSTM_F32, schedule="fused")) == 5
-    assert mt.validate(_desc(**big, schedule=3)) == 9
+    assert mt.validate(_desc(**big, schedule=4)) == 9
     assert mt.validate(_desc(**big, schedule=-1)) == 9
     # workspace: the fused schedule needs the gate terms only (12 or 8 bytes per
     # position and head); auto keeps room for the two-stage kernels as well,
@@ -385,3 +389,30 @@ def test_short_chunks_run_on_the_generic_kernels():
         assert mt.validate(_desc(chunk_size=L, tile_lq=64)) == 3
         assert mt.kernel_family(_desc(chunk_size=L, precision="f64")) == mt.MLSTM_FAMILY_F64
         assert mt.validate(_desc(chunk_size=L, DHQK=256, DHV=512, schedule="fused")) == 5
+
+
+def test_blocked_schedule():
+    """The blocked schedule: the wide kernels with the row-tile states kernel,
+    run per block of chunks; its workspace holds one block's chunk states
+    (block_chunks + 1 per head) and the state passed between blocks, twice;
+    the stage-wise calls refuse it."""
+    big = dict(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
+    d = _desc(**big, schedule="blocked")
+    assert mt.validate(d) == 0
+    assert mt.kernel_family(d) == mt.MLSTM_FAMILY_BLOCKED
+    BH, DK, DV, S = 64, 256, 512, 8192
+    r = lambda x: (x + 255) // 256 * 256
+    for k in (0, 1, 3):
+        dk = _desc(**big, schedule="blocked", block_chunks=k)
+        kk = k or (128 << 20) // (BH * DK * DV * 4)       # half the Infinity Cache: 4 chunks here
+        want = (r(BH * (kk + 1) * DK * DV * 4) + r(BH * (kk + 1) * DK * 4) + r(BH * (kk + 1) * 4)
+                + r(BH * S * 12) + 2 * (r(BH * DK * DV * 4) + r(BH * DK * 4) + r(BH * 4)))
+        assert mt.workspace_bytes(dk) == want, k
+    # shapes outside the row-tile states kernel, fp64 and float32 inputs refuse it
+    assert mt.validate(_desc(B=2, NH=2, S=1000, DHQK=128, DHV=128, chunk_size=128, schedule="blocked")) == 5
+    assert mt.validate(_desc(**big, schedule="blocked", precision="f64")) == 5
+    assert mt.validate(_desc(**big, schedule="blocked", qkv_dtype=mt.MLSTM_F32)) == 5
+    lib = mt.lib()
+    wsb = mt.workspace_bytes(d)
+    assert lib.mlstm_fw_states(ctypes.byref(d), *([4096] * 7), 1 << 20, wsb, None, None, None, None) == 5
+    assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), 1 << 20, wsb, 4096, None, None, None) == 5

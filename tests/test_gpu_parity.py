@@ -592,3 +592,61 @@ def test_bf16_inputs_beyond_the_fp16_range(mt, name, over, schedule):
              None if mb is None else mb[0, h]]
         assert np.all(np.isfinite(g[0]))
         _compare(w, g, r, f"{name} large Q, small K head {h}")
+
+
+# The blocked schedule: both stages per block of chunks over all heads, the
+# state handed from block to block.  Small shapes force short blocks (1 to 3
+# chunks) so that several hand-offs, a ragged last block and a ragged last
+# chunk all occur; both row-tile shapes of the states kernel (64 x 512 and
+# 128 x 256), both gates, initial states, 128-row intra tiles.
+BLOCKED = [
+    ("blk1_exp_v512_init", dict(B=1, NH=2, S=333, DHQK=256, DHV=512, chunk=64, init_state=True), 1),
+    ("blk2_exp_v512", dict(B=2, NH=1, S=700, DHQK=256, DHV=512, chunk=128), 2),
+    ("blk3_sig_v512_init", dict(gate="sig", B=1, NH=2, S=900, DHQK=128, DHV=512, chunk=64, init_state=True), 3),
+    ("blk2_exp_v256_dk128", dict(B=1, NH=3, S=500, DHQK=128, DHV=256, chunk=64, init_state=True), 2),
+    ("blk1_sig_v256_dk256", dict(gate="sig", B=1, NH=2, S=300, DHQK=256, DHV=256, chunk=128), 1),
+    ("blk2_exp_tq128", dict(B=1, NH=2, S=1100, DHQK=256, DHV=512, chunk=256, tile_lq=128, init_state=True), 2),
+    ("blk_one_block", dict(B=1, NH=2, S=260, DHQK=256, DHV=512, chunk=64), 0),
+    ("blk_empty", dict(B=1, NH=2, S=0, DHQK=256, DHV=512, chunk=64, init_state=True), 2),
+]
+
+
+@pytest.mark.parametrize("name,over,k", BLOCKED, ids=[c[0] for c in BLOCKED])
+def test_blocked_schedule_parity(mt, name, over, k):
+    w = _small_workload(over)
+    x = make_inputs(w)
+    print(f"\n[{name}] block_chunks {k}", flush=True)
+    gpu = _run_gpu(mt, w, x, schedule="blocked", block_chunks=k)
+    if w.S == 0:
+        np.testing.assert_array_equal(gpu[1], x["C0"])
+        np.testing.assert_array_equal(gpu[2], x["n0"])
+        np.testing.assert_array_equal(gpu[3], x["m0"])
+        return
+    ref = [np.zeros_like(g) if g is not None else None for g in gpu]
+    for b in range(w.B):
+        for h in range(w.NH):
+            r = _oracle(w, x, (b, h), fn="recurrent")
+            for slot in range(4):
+                if r[slot] is not None:
+                    ref[slot][b, h] = r[slot]
+    e = _compare(w, gpu, ref, name)
+    # the same kernels as the two-stage schedule, cut at chunk boundaries:
+    # H within rounding of the two-stage result
+    two = _run_gpu(mt, w, x, schedule="two_stage")
+    assert np.abs(gpu[0] - two[0]).max() <= 1e-3 * max(1.0, np.abs(two[0]).max())
+    print(f"[{name}] max|H|={np.abs(ref[0]).max():.3g} max|dH|={e:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["bf16_7b_s8192", "sig_7b_s8192"])
+def test_blocked_schedule_full_size_sampled_heads(mt, name):
+    """The blocked schedule on the full 7B-shaped workloads (its default block
+    of chunks: 4 chunks of all 64 heads, 128 MB of chunk states)."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    gpu = _run_gpu(mt, w, x, schedule="blocked")
+    worst = 0.0
+    for (b, h) in [(0, 0), (w.B // 2, 3), (w.B - 1, w.NH - 1)]:
+        ref = _oracle(w, x, (b, h))
+        g = [None if o is None else o[b, h] for o in gpu]
+        worst = max(worst, _compare(w, g, ref, f"blocked {name} head {(b, h)}"))
+    print(f"\n[{name} blocked] max|dH|={worst:.3g}", flush=True)

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(PKG_DIR, "libmlstm_tfla.so")
 MLSTM_F32, MLSTM_BF16 = 0, 1
 MLSTM_GATE_EXP, MLSTM_GATE_SIG = 0, 1
 MLSTM_PREC_SPLIT, MLSTM_PREC_F16, MLSTM_PREC_F64 = 0, 1, 2
-MLSTM_FAMILY_GENERIC, MLSTM_FAMILY_WIDE, MLSTM_FAMILY_F64, MLSTM_FAMILY_FUSED = 0, 1, 2, 3
-MLSTM_SCHED_AUTO, MLSTM_SCHED_TWO_STAGE, MLSTM_SCHED_FUSED = 0, 1, 2
+MLSTM_FAMILY_GENERIC, MLSTM_FAMILY_WIDE, MLSTM_FAMILY_F64, MLSTM_FAMILY_FUSED, MLSTM_FAMILY_BLOCKED = 0, 1, 2, 3, 4
+MLSTM_SCHED_AUTO, MLSTM_SCHED_TWO_STAGE, MLSTM_SCHED_FUSED, MLSTM_SCHED_BLOCKED = 0, 1, 2, 3
 _PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16, "f64": MLSTM_PREC_F64}
 _GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
-_SCHED = {"auto": MLSTM_SCHED_AUTO, "two_stage": MLSTM_SCHED_TWO_STAGE, "fused": MLSTM_SCHED_FUSED}
+_SCHED = {"auto": MLSTM_SCHED_AUTO, "two_stage": MLSTM_SCHED_TWO_STAGE, "fused": MLSTM_SCHED_FUSED,
+          "blocked": MLSTM_SCHED_BLOCKED}
 
 STATUS_NAMES = {
     0: "MLSTM_OK", 1: "MLSTM_E_NULLPTR", 2: "MLSTM_E_SHAPE", 3: "MLSTM_E_CHUNK",
@@ -47,7 +48,7 @@ class FwDesc(ctypes.Structure):
         ("qkv_dtype", ctypes.c_int32), ("h_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
         ("precision", ctypes.c_int32), ("qk_scale", ctypes.c_float), ("eps", ctypes.c_float),
         ("tile_lq", ctypes.c_int32), ("tile_lkv", ctypes.c_int32), ("schedule", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("block_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -108,7 +109,7 @@ def status_str(status: int) -> str:
 
 def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=MLSTM_F32,
               gate="exp", precision="split", qk_scale=0.0, eps=0.0, tile_lq=0, tile_lkv=0,
-              schedule="auto") -> FwDesc:
+              schedule="auto", block_chunks=0) -> FwDesc:
     d = FwDesc()
     d.B, d.NH, d.S, d.DHQK, d.DHV, d.chunk_size = B, NH, S, DHQK, DHV, chunk_size
     d.qkv_dtype, d.h_dtype = qkv_dtype, h_dtype
@@ -117,6 +118,7 @@ def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=
     d.qk_scale, d.eps = qk_scale, eps
     d.tile_lq, d.tile_lkv = tile_lq, tile_lkv
     d.schedule = _SCHED[schedule] if isinstance(schedule, str) else schedule
+    d.block_chunks = block_chunks
     return d
 
 
@@ -176,7 +178,8 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule="auto"):
+def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule="auto",
+              block_chunks=0):
     torch = _torch()
     B, NH, S, DK = q.shape
     DV = v.shape[-1]
@@ -184,7 +187,7 @@ def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq
     return make_desc(B, NH, S, DK, DV, chunk_size, qkv_dtype=_dtype_code(q), h_dtype=hcode,
                      gate=gate, precision=precision,
                      qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps),
-                     tile_lq=tile_lq, tile_lkv=tile_lkv, schedule=schedule)
+                     tile_lq=tile_lq, tile_lkv=tile_lkv, schedule=schedule, block_chunks=block_chunks)
 
 
 def _check_inputs(q, k, v, i_pre, f_pre):
@@ -205,7 +208,7 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
                        gate: str = "exp", h_dtype=None, precision: str = "split",
                        qk_scale: Optional[float] = None, eps: float = 0.0,
                        tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto", workspace=None,
-                       return_final_state: bool = True, out=None):
+                       return_final_state: bool = True, out=None, block_chunks: int = 0):
     """Chunkwise mLSTM forward pass on the GPU.
 
     q, k: (B, NH, S, DHQK); v: (B, NH, S, DHV), bfloat16 or float32;
@@ -213,7 +216,9 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     m0 (B, NH) float32 or None (zero state).  Returns (H, C, n, m); n and m
     are None for gate="sig", and the final state is None when
     return_final_state is False.  H is float32 unless h_dtype says otherwise.
-    schedule: "auto", "two_stage" or "fused" (see mlstm_schedule_t).
+    schedule: "auto", "two_stage", "fused" or "blocked" (see
+    mlstm_schedule_t); block_chunks: chunks per block of the blocked
+    schedule (0: the library's choice).
     """
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
@@ -221,7 +226,8 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     _check(C0, "C0", (B, NH, DK, DV), torch.float32)
     _check(n0, "n0", (B, NH, DK), torch.float32)
     _check(m0, "m0", (B, NH), torch.float32)
-    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule)
+    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule,
+                     block_chunks)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_chunkwise_fw")
@@ -255,7 +261,7 @@ NOALLOC_WORKSPACE_BYTES = 64 << 20   # MLSTM_NOALLOC_WORKSPACE_BYTES
 def mlstm_chunkwise_fw_noalloc(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
                                gate: str = "exp", precision: str = "split", qk_scale: Optional[float] = None,
                                eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto",
-                               out=None, C_out=None, n_out=None, m_out=None):
+                               out=None, C_out=None, n_out=None, m_out=None, block_chunks: int = 0):
     """mlstm_chunkwise_fw on the library's static workspace
     (mlstm_chunkwise_fw_noalloc): no workspace argument, and nothing is
     allocated when every output is given (out = H, whose dtype is the H
@@ -271,7 +277,8 @@ def mlstm_chunkwise_fw_noalloc(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None,
     _check(C_out, "C_out", (B, NH, DK, DV), torch.float32)
     _check(n_out, "n_out", (B, NH, DK), torch.float32)
     _check(m_out, "m_out", (B, NH), torch.float32)
-    desc = _desc_for(q, v, chunk_size, gate, H.dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule)
+    desc = _desc_for(q, v, chunk_size, gate, H.dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule,
+                     block_chunks)
     st = lib().mlstm_chunkwise_fw_noalloc(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
         _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())

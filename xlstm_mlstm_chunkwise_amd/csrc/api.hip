@@ -27,13 +27,38 @@ bool fused_supported(const mlstm_fw_desc_t* d) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+bool packed_layout(const mlstm_fw_desc_t* d);
+
+// The blocked schedule runs the wide kernels with the row-tile states kernel
+// (one workgroup per head and row tile of the state, all value columns).
+bool blocked_supported(const mlstm_fw_desc_t* d) {
+  return d->precision != MLSTM_PREC_F64 && packed_layout(d) && mlstm::rows_tile_rows(d->DHQK, d->DHV) > 0;
+}
+
+// Chunk states of one block of the blocked schedule, over all heads: half the
+// 256 MB Infinity Cache, so that a block's states, written by the states
+// kernel, are still there when the intra-chunk kernel reads them.
+constexpr size_t kBlockStateBytes = size_t(128) << 20;
+
+// Chunks per block of the blocked schedule (at least one).
+int block_chunks(const mlstm_fw_desc_t* d) {
+  const int Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  const size_t per_chunk = (size_t)d->B * d->NH * d->DHQK * d->DHV * sizeof(float);
+  size_t k = d->block_chunks > 0 ? (size_t)d->block_chunks : kBlockStateBytes / per_chunk;
+  if (k < 1) k = 1;
+  if (k > (size_t)(Nc > 1 ? Nc : 1)) k = Nc > 1 ? Nc : 1;
+  return (int)k;
+}
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int validate_desc(const mlstm_fw_desc_t* d) {
   if (!d) return MLSTM_E_NULLPTR;
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
     if (d->reserved[i] != 0) return MLSTM_E_ARG;
-  if (d->schedule != MLSTM_SCHED_AUTO && d->schedule != MLSTM_SCHED_TWO_STAGE && d->schedule != MLSTM_SCHED_FUSED)
+  if (d->block_chunks < 0) return MLSTM_E_ARG;
+  if (d->schedule != MLSTM_SCHED_AUTO && d->schedule != MLSTM_SCHED_TWO_STAGE && d->schedule != MLSTM_SCHED_FUSED &&
+      d->schedule != MLSTM_SCHED_BLOCKED)
     return MLSTM_E_ARG;
   if (d->qkv_dtype != MLSTM_F32 && d->qkv_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
   if (d->h_dtype != MLSTM_F32 && d->h_dtype != MLSTM_BF16) return MLSTM_E_DTYPE;
@@ -61,6 +86,7 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   // 32-bit: a head's largest float32 row block stays below 2 GiB.
   if ((int64_t)d->S * (int64_t)(d->DHQK > d->DHV ? d->DHQK : d->DHV) >= (1LL << 29)) return MLSTM_E_SHAPE;
   if (d->schedule == MLSTM_SCHED_FUSED && !fused_supported(d)) return MLSTM_E_UNSUPPORTED;
+  if (d->schedule == MLSTM_SCHED_BLOCKED && !blocked_supported(d)) return MLSTM_E_UNSUPPORTED;
   return MLSTM_OK;
 }
 
@@ -74,17 +100,18 @@ bool use_fused(const mlstm_fw_desc_t* d) {
 }
 
 struct WsLayout {
-  size_t c_off, n_off, m_off, g_off, ml_off, total;
+  size_t c_off, n_off, m_off, g_off, ml_off, cy_off, total;
 };
-
-bool packed_layout(const mlstm_fw_desc_t* d);
 
 // Per-position gate terms: read by both wide-tile stages and by the walker.
 bool needs_gates(const mlstm_fw_desc_t* d) { return packed_layout(d) || fused_supported(d); }
 
 WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   const size_t BH = (size_t)d->B * d->NH;
-  const size_t Nc1 = (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
+  const bool blocked = d->schedule == MLSTM_SCHED_BLOCKED;
+  // chunk-state slots per head: every chunk boundary, or one block's
+  const size_t Nc1 = blocked ? (size_t)block_chunks(d) + 1
+                             : (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
   const size_t el = d->precision == MLSTM_PREC_F64 ? sizeof(double) : sizeof(float);
   const bool states = d->schedule != MLSTM_SCHED_FUSED;  // chunk states can be formed
   WsLayout w;
@@ -98,7 +125,13 @@ WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   if (needs_gates(d)) off += round_up(BH * (size_t)d->S * sizeof(float) * (d->gate == MLSTM_GATE_EXP ? 3 : 2), 256);
   // stabilisers of segment-local runs of the states kernel
   w.ml_off = off;
-  if (states && packed_layout(d)) off += round_up(BH * Nc1 * sizeof(float), 256);
+  if (states && !blocked && packed_layout(d)) off += round_up(BH * Nc1 * sizeof(float), 256);
+  // blocked schedule: the state handed from one block to the next, twice
+  // (read by one block while the next is written): C, n, m as float32
+  w.cy_off = off;
+  if (blocked)
+    off += 2 * (round_up(BH * d->DHQK * d->DHV * sizeof(float), 256) + round_up(BH * d->DHQK * sizeof(float), 256) +
+                round_up(BH * sizeof(float), 256));
   w.total = off;
   return w;
 }
@@ -135,6 +168,9 @@ struct WsPtrs {
   float* gu2;
   float* gpm2;
   float* m_local;  // segment-local stabilisers (wide-tile path), else null
+  float* cy_C[2];  // blocked schedule: the state between blocks, else null
+  float* cy_n[2];
+  float* cy_m[2];
 };
 
 WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
@@ -145,7 +181,22 @@ WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
   r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
   r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
   r.gb2 = r.gu2 = r.gpm2 = r.m_local = nullptr;
-  if (packed_layout(d) && d->schedule != MLSTM_SCHED_FUSED) r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
+  const bool blocked = d->schedule == MLSTM_SCHED_BLOCKED;
+  if (packed_layout(d) && d->schedule != MLSTM_SCHED_FUSED && !blocked)
+    r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
+  for (int i = 0; i < 2; ++i) r.cy_C[i] = r.cy_n[i] = r.cy_m[i] = nullptr;
+  if (blocked) {
+    const size_t BH = (size_t)d->B * d->NH;
+    const size_t cb = round_up(BH * d->DHQK * d->DHV * sizeof(float), 256);
+    const size_t nb = round_up(BH * d->DHQK * sizeof(float), 256), mb = round_up(BH * sizeof(float), 256);
+    char* c = ws + w.cy_off;
+    for (int i = 0; i < 2; ++i) {
+      r.cy_C[i] = reinterpret_cast<float*>(c);
+      r.cy_n[i] = reinterpret_cast<float*>(c + cb);
+      r.cy_m[i] = reinterpret_cast<float*>(c + cb + nb);
+      c += cb + nb + mb;
+    }
+  }
   if (needs_gates(d)) {
     const size_t n = (size_t)d->B * d->NH * d->S;
     r.gb2 = reinterpret_cast<float*>(ws + w.g_off);
@@ -295,6 +346,88 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
+// Blocked schedule: the two stages per block of chunks, over all heads.  The
+// states kernel starts each block from the state the previous block ended
+// in (the initial state for the first) and writes the block's chunk states
+// with plain stores; the intra-chunk kernel reads them back while they are
+// still in the Infinity Cache.  The last block ends in the final state.
+int run_blocked(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
+                const float* f_pre, const float* C0, const float* n0, const float* m0, const WsPtrs& ws, void* H,
+                float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+  const int Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
+  const int k = block_chunks(d);
+  const bool sig = d->gate == MLSTM_GATE_SIG;
+  const bool split = d->precision == MLSTM_PREC_SPLIT;
+  hipError_t e = hipSuccess;
+  if (d->S > 0) e = run_gates(d, i_pre, f_pre, ws, stream);
+  const int nblk = Nc > 0 ? (Nc + k - 1) / k : 1;
+  for (int b = 0; b < nblk && e == hipSuccess; ++b) {
+    const int c_lo = b * k, c_hi = Nc < c_lo + k ? Nc : c_lo + k;
+    const bool last = b + 1 == nblk;
+    StatesParams p;
+    p.K = K;
+    p.V = V;
+    p.i_pre = i_pre;
+    p.f_pre = f_pre;
+    p.C0 = b == 0 ? C0 : ws.cy_C[b & 1];
+    p.n0 = b == 0 ? n0 : ws.cy_n[b & 1];
+    p.m0 = b == 0 ? m0 : ws.cy_m[b & 1];
+    p.C_states = ws.C;
+    p.n_states = ws.n;
+    p.m_states = ws.m;
+    p.C_out = last ? C_out : ws.cy_C[(b + 1) & 1];
+    p.n_out = last ? n_out : (sig ? nullptr : ws.cy_n[(b + 1) & 1]);
+    p.m_out = last ? m_out : (sig ? nullptr : ws.cy_m[(b + 1) & 1]);
+    p.gb2 = ws.gb2;
+    p.gu2 = ws.gu2;
+    p.gpm2 = ws.gpm2;
+    p.m_local = nullptr;
+    p.BH = d->B * d->NH;
+    p.S = d->S;
+    p.DK = d->DHQK;
+    p.DV = d->DHV;
+    p.L = d->chunk_size;
+    p.Nc = Nc;
+    p.c_lo = c_lo;
+    p.c_hi = c_hi;
+    p.slots = k + 1;
+    p.nt_states = 0;
+    e = mlstm::launch_states_rows_range(p, sig, split, stream);
+    if (e != hipSuccess || d->S == 0) break;
+    HintraParams h;
+    h.Q = Q;
+    h.K = K;
+    h.V = V;
+    h.i_pre = i_pre;
+    h.f_pre = f_pre;
+    h.C_states = ws.C;
+    h.n_states = ws.n;
+    h.m_states = ws.m;
+    h.H = H;
+    h.m_rows = nullptr;
+    h.den_rows = nullptr;
+    h.gb2 = ws.gb2;
+    h.gu2 = ws.gu2;
+    h.gpm2 = ws.gpm2;
+    h.scale = resolve_scale(d);
+    h.eps = d->eps;
+    h.BH = d->B * d->NH;
+    h.S = d->S;
+    h.DK = d->DHQK;
+    h.DV = d->DHV;
+    h.L = d->chunk_size;
+    h.Nc = Nc;
+    h.h_bf16 = d->h_dtype == MLSTM_BF16;
+    h.tile_lq = d->tile_lq ? d->tile_lq : 64;
+    h.tile_lkv = d->tile_lkv ? d->tile_lkv : 64;
+    h.c_lo = c_lo;
+    h.c_hi = c_hi;
+    h.slots = k + 1;
+    e = mlstm::launch_hintra_wide(h, sig, split, stream);
+  }
+  return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
+}
+
 // The chunk states of a two-stage workspace as float32 row-major arrays.
 int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, float* n_states, float* m_states,
                   hipStream_t s) {
@@ -408,6 +541,7 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc) {
   if (st != MLSTM_OK) return -st;
   if (desc->precision == MLSTM_PREC_F64) return MLSTM_FAMILY_F64;
   if (use_fused(desc)) return MLSTM_FAMILY_FUSED;
+  if (desc->schedule == MLSTM_SCHED_BLOCKED) return MLSTM_FAMILY_BLOCKED;
   return packed_layout(desc) ? MLSTM_FAMILY_WIDE : MLSTM_FAMILY_GENERIC;
 }
 
@@ -421,7 +555,7 @@ int mlstm_fw_states(const mlstm_fw_desc_t* desc, const void* K, const void* V, c
                     size_t workspace_bytes, float* C_out, float* n_out, float* m_out, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
+  if (desc->schedule == MLSTM_SCHED_FUSED || desc->schedule == MLSTM_SCHED_BLOCKED) return MLSTM_E_UNSUPPORTED;
   if (desc->S > 0 && (!K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, n0, m0, n_out, m_out)) != MLSTM_OK) return st;
   if ((K && !aligned(K, 16)) || (V && !aligned(V, 16))) return MLSTM_E_ALIGN;
@@ -436,7 +570,7 @@ int mlstm_fw_hintra(const mlstm_fw_desc_t* desc, const void* Q, const void* K, c
                     float* den_rows, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
+  if (desc->schedule == MLSTM_SCHED_FUSED || desc->schedule == MLSTM_SCHED_BLOCKED) return MLSTM_E_UNSUPPORTED;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !H)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, m_rows, den_rows, nullptr, nullptr)) != MLSTM_OK) return st;
   if ((Q && !aligned(Q, 16)) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || (H && !aligned(H, 16)))
@@ -451,7 +585,7 @@ int mlstm_fw_unpack_states(const mlstm_fw_desc_t* desc, const void* workspace, s
                            float* C_states, float* n_states, float* m_states, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->schedule == MLSTM_SCHED_FUSED) return MLSTM_E_UNSUPPORTED;
+  if (desc->schedule == MLSTM_SCHED_FUSED || desc->schedule == MLSTM_SCHED_BLOCKED) return MLSTM_E_UNSUPPORTED;
   if ((st = check_sig_nulls(desc, n_states, m_states, nullptr, nullptr)) != MLSTM_OK) return st;
   if ((st = check_f32_ptrs({C_states, n_states, m_states})) != MLSTM_OK) return st;
   if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
@@ -482,6 +616,8 @@ int run_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void
            float* n_out, float* m_out, void* workspace, hipStream_t s) {
   const WsPtrs ws = ws_ptrs(desc, workspace);
   if (use_fused(desc)) return run_fused(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
+  if (desc->schedule == MLSTM_SCHED_BLOCKED)
+    return run_blocked(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
   const int st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
   if (st != MLSTM_OK) return st;
   return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);

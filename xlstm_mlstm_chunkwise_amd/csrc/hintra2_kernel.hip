@@ -71,9 +71,14 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   uint16_t* const s_v = s_pl + W::P_ELEMS;
   uint16_t* const s_q = s_buf;  // the Q tile, before the key loop
 
-  const int S = p.S, L = p.L, Nc = p.Nc;
+  const int S = p.S, L = p.L;
   const int NQT = L / TQ;
   const float scale = p.scale;
+  // chunks [c_lo, c_lo + NCB) of this launch; the state entering chunk c sits
+  // at slot c - c_lo of the head's SL slots
+  const int c_lo = p.c_lo;
+  const int NCB = (p.c_hi < 0 ? p.Nc : p.c_hi) - c_lo;
+  const int SL = p.slots ? p.slots : p.Nc + 1;
   // Per-lane and per-wave roles.  They are re-derived at the top of every
   // tile from a laundered thread index, so the compiler rebuilds the offsets
   // that depend on them instead of keeping them live across the tile loop.
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   // tiles, and its G workgroups take G consecutive tiles per round (sharing
   // that XCD's L2), rotated by one each round so no workgroup always gets the
   // longest (last) row tile of a chunk.
-  const int ntile = p.BH * Nc * NQT * NVT;
+  const int ntile = p.BH * NCB * NQT * NVT;
   const int G = gridDim.x;
   const bool xcd_split = (G & 7) == 0;
   const int gx = xcd_split ? G >> 3 : G;                  // workgroups per XCD
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   };
   auto tile_live = [&](int t) -> bool {
     const int qt_ = (t / NVT) % NQT;
-    const int c_ = (t / (NVT * NQT)) % Nc;
+    const int c_ = c_lo + (t / (NVT * NQT)) % NCB;
     return qt_ * TQ < min(L, S - c_ * L);
   };
   int k_round = 0;
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   uint4 qpre[QPT];
   uint4 bb[NKK][W::CB][2];
   auto state_ptr = [&](int bh_, int c_) {
-    return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * (Nc + 1) + c_) * DK * DV * 2;
+    return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * SL + c_ - c_lo) * DK * DV * 2;
   };
   // Chunk-state fragments through a buffer resource: lane offset and the
   // wave's first 32-column block in one VGPR, the k step in a scalar offset
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   auto state_rsrc = [&](int bh_, int c_) { return make_rsrc(state_ptr(bh_, c_), (uint32_t)(DK * DV * 4)); };
   auto request = [&](int t) {
     const int vt_ = t % NVT, qt_ = (t / NVT) % NQT;
-    const int c_ = (t / (NVT * NQT)) % Nc, bh_ = t / (NVT * NQT * Nc);
+    const int c_ = c_lo + (t / (NVT * NQT)) % NCB, bh_ = t / (NVT * NQT * NCB);
     const int t0_ = c_ * L, Lc_ = min(L, S - t0_), row0_ = qt_ * TQ, kend_ = min(row0_ + TQ, Lc_);
     const size_t gbase = (size_t)bh_ * S + t0_;
 #pragma unroll
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       if constexpr (!SIG) gpm_r = p.gpm2[gbase + row0_ + tid];
     }
     if constexpr (!SIG) {
-      mprev = p.m_states[(size_t)bh_ * (Nc + 1) + c_];
-      const float* nst = p.n_states + ((size_t)bh_ * (Nc + 1) + c_) * DK;
+      mprev = p.m_states[(size_t)bh_ * SL + c_ - c_lo];
+      const float* nst = p.n_states + ((size_t)bh_ * SL + c_ - c_lo) * DK;
 #pragma unroll
       for (int e = 0; e < NPT; ++e) n_r[e] = tid + e * W::NT < DK ? nst[tid + e * W::NT] : 0.0f;
     }
@@ -200,8 +205,8 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
     set_roles();
     const int vt = tile % NVT;
     const int qt = (tile / NVT) % NQT;
-    const int c = (tile / (NVT * NQT)) % Nc;
-    const int bh = tile / (NVT * NQT * Nc);
+    const int c = c_lo + (tile / (NVT * NQT)) % NCB;
+    const int bh = tile / (NVT * NQT * NCB);
     const int v0 = vt * TV;
     const int t0 = c * L;
     const int Lc = min(L, S - t0);
@@ -527,7 +532,7 @@ hipError_t launch_t(const HintraParams& p, hipStream_t stream) {
   // CU); fewer when there are fewer tiles.
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const long long ntile = (long long)p.BH * p.Nc * (p.L / TQ) * (DV / TV);
+  const long long ntile = (long long)p.BH * ((p.c_hi < 0 ? p.Nc : p.c_hi) - p.c_lo) * (p.L / TQ) * (DV / TV);
   dim3 grid((unsigned)(ntile < cus ? ntile : cus));
   hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();

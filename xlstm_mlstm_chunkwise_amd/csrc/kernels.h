@@ -42,6 +42,13 @@ struct StatesParams {
   // (no intra-chunk kernel reads it).
   float* C_plain = nullptr;
   int plain_only = 0;
+  // Chunk range [c_lo, c_hi) of this launch (c_hi < 0: Nc) and the chunk-state
+  // slots per head (0: Nc + 1): the state entering chunk c sits at slot
+  // c - c_lo, the one after the last chunk at slot c_hi - c_lo.  A launch over
+  // part of the chunks starts from C0, n0, m0 and ends in C_out, n_out,
+  // m_out (row-tile states kernel, one segment).
+  int c_lo = 0, c_hi = -1, slots = 0;
+  int nt_states = 1;  // non-temporal stores of the packed chunk states
 };
 
 struct HintraParams {
@@ -65,6 +72,8 @@ struct HintraParams {
   int h_bf16;    // 1: H is bf16, 0: float32
   int tile_lq;   // rows per workgroup: 64 or 128
   int tile_lkv;  // keys per step: 64 or 128
+  // Chunk range and state slots as in StatesParams (wide kernel only).
+  int c_lo = 0, c_hi = -1, slots = 0;
 };
 
 // Fused chunk walker: one workgroup per (head, 128-column slice of V) runs
@@ -186,6 +195,10 @@ hipError_t launch_hintra_wide(const HintraParams& p, bool sig, bool split, hipSt
 // Wide-tile states kernel: writes the chunk states in the packed fragment
 // layout read by the wide intra-chunk kernel.
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream);
+// Row-tile states kernel over the chunk range of p, one segment (the blocked
+// forward schedule); rows_tile_rows(DK, DV) > 0 where it covers the shape.
+int rows_tile_rows(int DK, int DV);
+hipError_t launch_states_rows_range(const StatesParams& p, bool sig, bool split, hipStream_t stream);
 // Float64 precision mode: both stages in fp64, states kept in fp64.
 hipError_t launch_states_f64(const StatesParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
 hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream);

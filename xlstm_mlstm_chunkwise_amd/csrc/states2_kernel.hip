@@ -301,8 +301,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // from the initial state and later ones from zero (stabiliser -inf); their
   // chunk states are local and the join kernels turn them into the true ones.
   const bool segmented = p.nseg > 1;
-  const int c_beg = seg * p.cps;
-  const int c_end = min(Nc, c_beg + p.cps);
+  // Chunks [c_lo, c_hi) of this launch (all of them unless the forward runs
+  // in blocks of chunks); the state entering chunk c sits at slot c - c_lo of
+  // the head's SL slots.
+  const int c_hi = p.c_hi < 0 ? Nc : p.c_hi;
+  const int SL = p.slots ? p.slots : Nc + 1;
+  const int c_beg = p.c_lo + seg * p.cps;
+  const int c_end = min(c_hi, c_beg + p.cps);
   const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;  // inside the tile
   const uint16_t* K = static_cast<const uint16_t*>(p.K) + (size_t)bh * S * DK + kt * TK;
   const uint16_t* V = static_cast<const uint16_t*>(p.V) + (size_t)bh * S * DV;
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   auto write_state = [&](int entry, float M2) {
     if constexpr (PLAIN) {
       // float32 row-major copy: a half-wave stores 128 contiguous bytes of a row
-      float* Pl = p.C_plain + ((size_t)bh * (Nc + 1) + entry) * DK * DV;
+      float* Pl = p.C_plain + ((size_t)bh * SL + entry - p.c_lo) * DK * DV;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             __builtin_nontemporal_store(acc[rb][cb][r], Pl + (size_t)krow * DV + wc0 + 32 * cb + l32);
           }
     }
-    uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * (Nc + 1) + entry) * DK * DV * 2;
+    uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV * 2;
     constexpr int NB = DV / 32;
 #pragma unroll
     for (int rb = 0; rb < 2 && !PLAIN; ++rb)
@@ -355,22 +360,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
           for (int e = 0; e < 4; ++e)
             split_bf16x2(acc[rb][cb][8 * half + 2 * e], acc[rb][cb][8 * half + 2 * e + 1], hi[e], lo[e]);
           const size_t blk = ((size_t)(2 * kblk + half) * NB + nb) * 2;
-          // streaming stores: the states are read back by the next kernel,
-          // long after they would have left L2
-          __builtin_nontemporal_store(u32x4_t{hi[0], hi[1], hi[2], hi[3]},
-                                      reinterpret_cast<u32x4_t*>(P + (blk + 0) * 512 + lane * 8));
-          __builtin_nontemporal_store(u32x4_t{lo[0], lo[1], lo[2], lo[3]},
-                                      reinterpret_cast<u32x4_t*>(P + (blk + 1) * 512 + lane * 8));
+          u32x4_t* dh = reinterpret_cast<u32x4_t*>(P + (blk + 0) * 512 + lane * 8);
+          u32x4_t* dl = reinterpret_cast<u32x4_t*>(P + (blk + 1) * 512 + lane * 8);
+          if (p.nt_states) {
+            // streaming stores: the states are read back by the next kernel,
+            // long after they would have left L2
+            __builtin_nontemporal_store(u32x4_t{hi[0], hi[1], hi[2], hi[3]}, dh);
+            __builtin_nontemporal_store(u32x4_t{lo[0], lo[1], lo[2], lo[3]}, dl);
+          } else {
+            // plain stores: a block of chunk states is read back right away,
+            // from the Infinity Cache
+            *dh = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+            *dl = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+          }
         }
       }
     if (!SIG && kt == 0 && tid == 0) {
-      if (seg == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = M2 * kLn2;
+      if (seg == 0) p.m_states[(size_t)bh * SL + entry - p.c_lo] = M2 * kLn2;
       if (segmented) p.m_local[(size_t)bh * (Nc + 1) + entry] = M2;
     }
   };
   if (seg == 0) {
-    write_state(0, Mst2);
-    if (!SIG && tid < TK) p.n_states[((size_t)bh * (Nc + 1)) * DK + kt * TK + tid] = nreg;
+    write_state(p.c_lo, Mst2);
+    if (!SIG && tid < TK) p.n_states[((size_t)bh * SL) * DK + kt * TK + tid] = nreg;
   }
 
   // flattened block sequence over this segment: block gi covers steps
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
       for (int w = 0; w < NW; ++w) sacc += s_np[w][tid];
       nreg = nreg * n_dec + sacc;
-      p.n_states[((size_t)bh * (Nc + 1) + entry) * DK + kt * TK + tid] = nreg;
+      p.n_states[((size_t)bh * SL + entry - p.c_lo) * DK + kt * TK + tid] = nreg;
     }
     n_pend = false;
   };
@@ -770,13 +782,28 @@ hipError_t launch_t(const StatesParams& p, hipStream_t stream) {
 
 }  // namespace
 
+int rows_tile_rows(int DK, int DV) { return DV == 512 ? 64 : (DV == 256 && DK % 128 == 0 ? 128 : 0); }
+
+hipError_t launch_states_rows_range(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  StatesParams q = p;
+  q.nseg = 1;
+  q.cps = (p.c_hi < 0 ? p.Nc : p.c_hi) - p.c_lo;
+  q.C_plain = nullptr;
+  q.plain_only = 0;
+  q.m_local = nullptr;
+  const int tk = rows_tile_rows(p.DK, p.DV);
+  if (tk == 64) return launch_rows_any<64, 512>(q, sig, split, stream);
+  if (tk == 128) return launch_rows_any<128, 256>(q, sig, split, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // Whole-row tiles (TK x DV) when they still give every CU a workgroup.
   // Whole-row tiles; with too few heads to fill the CUs the sequence is cut
   // into segments that run at once and are joined afterwards.
-  const int rows_tk = p.DV == 512 ? 64 : (p.DV == 256 && p.DK % 128 == 0 ? 128 : 0);
+  const int rows_tk = rows_tile_rows(p.DK, p.DV);
   if (rows_tk) {
     StatesParams q = p;
     const long long base = (long long)p.BH * (p.DK / rows_tk);
