@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "walk": ("walk_kernel.hip", "gates_kernel.hip", "device_common.h"),
     "states": ("states2_kernel.hip", "gates_kernel.hip", "device_common.h"),
     "hintra": ("hintra2_kernel.hip", "device_common.h"),
+    "blocked": ("states2_kernel.hip", "hintra2_kernel.hip", "gates_kernel.hip", "device_common.h"),
     "step": ("step_kernel.hip", "device_common.h"),
     "step_q8": ("step_kernel.hip", "device_common.h"),
 }
