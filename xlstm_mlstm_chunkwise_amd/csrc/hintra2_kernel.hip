@@ -112,7 +112,11 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   // Workgroup b runs on XCD b % 8; each XCD owns a contiguous eighth of the
   // tiles, and its G workgroups take G consecutive tiles per round (sharing
   // that XCD's L2), rotated by one each round so no workgroup always gets the
-  // longest (last) row tile of a chunk.
+  // longest (last) row tile of a chunk.  With pair_tiles a workgroup instead
+  // takes row tiles p and NQT-1-p of one chunk in two consecutive rounds:
+  // every such pair covers the same number of key tiles, so the workgroups
+  // of an XCD stay on the same few chunks and share their keys and values
+  // in L2 instead of drifting apart.
   const int ntile = p.BH * NCB * NQT * NVT;
   const int G = gridDim.x;
   const bool xcd_split = (G & 7) == 0;
@@ -123,7 +127,21 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   const int tbeg = x * per_x, tend = min(ntile, tbeg + per_x);
   // tile of round k for this workgroup, or -1 past the end; rows of a
   // ragged last chunk that hold no data are skipped
+  const bool paired = p.pair_tiles && (NQT % 2) == 0;
+  const int NPAIR = NQT / 2;
+  const int nitem = ntile / 2;
+  const int per_xi = xcd_split ? (nitem + 7) >> 3 : nitem;
+  const int ibeg = x * per_xi, iend = min(nitem, ibeg + per_xi);
   auto tile_at = [&](int k) -> int {
+    if (paired) {
+      // work item = row tiles p and NQT-1-p of one (head, chunk, column
+      // tile), in consecutive rounds: every item has the same key range
+      const int it = ibeg + (k >> 1) * gx + jw;
+      if (it >= iend) return -1;
+      const int vt_ = it % NVT, pp = (it / NVT) % NPAIR, rest = it / (NVT * NPAIR);
+      const int qt_ = (k & 1) ? NQT - 1 - pp : pp;
+      return (rest * NQT + qt_) * NVT + vt_;
+    }
     const int t = tbeg + k * gx + (jw + k) % gx;
     return t < tend ? t : (tbeg + k * gx < tend ? -2 : -1);
   };
@@ -527,7 +545,13 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 }
 
 template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT>
-hipError_t launch_t(const HintraParams& p, hipStream_t stream) {
+hipError_t launch_t(const HintraParams& p0, hipStream_t stream) {
+  // Long chunks (8 or more row tiles) pair their row tiles: measured on the
+  // long-context workload (chunk 1024, 128-row tiles) the L2 re-fetch of K
+  // and V halves (6.45 -> 3.85 GB per launch) and the kernel gains 4 %; with
+  // 4 row tiles per chunk the unpaired rotation is faster.
+  HintraParams p = p0;
+  p.pair_tiles = p.L / TQ >= 8;
   // One workgroup per CU walks the tiles (the LDS footprint allows one per
   // CU); fewer when there are fewer tiles.
   int dev = 0, cus = 256;

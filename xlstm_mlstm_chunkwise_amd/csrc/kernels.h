@@ -74,6 +74,7 @@ struct HintraParams {
   int tile_lkv;  // keys per step: 64 or 128
   // Chunk range and state slots as in StatesParams (wide kernel only).
   int c_lo = 0, c_hi = -1, slots = 0;
+  int pair_tiles = 0;  // wide kernel: schedule row tiles p and NQT-1-p together
 };
 
 // Fused chunk walker: one workgroup per (head, 128-column slice of V) runs
