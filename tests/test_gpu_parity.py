@@ -342,6 +342,16 @@ F64_SMALL = [
     ("f64_bf16_spikes", dict(B=1, NH=2, S=600, DHQK=128, DHV=128, chunk=128, i_dist=("normal", 0.0, 2.0),
                             i_spike_prob=0.02)),
     ("f64_bf16_l16", dict(B=1, NH=2, S=90, DHQK=64, DHV=64, chunk=16, init_state=True)),
+    # matrix-core kernels: 256-wide keys with 128- and 64-column tiles, float32
+    # inputs at 256 (64-column tiles only), a 1024 chunk with a ragged second
+    # chunk; 512-wide keys take the vector-unit kernel
+    ("f64_bf16_d256_v512", dict(B=1, NH=1, S=300, DHQK=256, DHV=512, chunk=256, init_state=True)),
+    ("f64_bf16_d256_v192_sig", dict(gate="sig", B=1, NH=1, S=170, DHQK=256, DHV=192, chunk=128)),
+    ("f64_f32_d256_v128_sig", dict(qkv_dtype="f32", gate="sig", B=1, NH=1, S=200, DHQK=256, DHV=128,
+                                   chunk=128, init_state=True)),
+    ("f64_f32_d128_v256", dict(qkv_dtype="f32", B=1, NH=2, S=150, DHQK=128, DHV=256, chunk=64)),
+    ("f64_bf16_l1024", dict(B=1, NH=1, S=1100, DHQK=64, DHV=128, chunk=1024)),
+    ("f64_bf16_d512", dict(B=1, NH=1, S=130, DHQK=512, DHV=128, chunk=64, init_state=True)),
 ]
 
 

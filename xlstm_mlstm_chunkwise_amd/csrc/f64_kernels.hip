@@ -1,185 +1,23 @@
-// Float64 evaluation of both stages of the chunkwise mLSTM forward pass
-// (precision mode MLSTM_PREC_F64), for inputs whose rows are too
-// ill-conditioned for float32 accumulation.
+// Float64 evaluation of the intra-chunk stage of the chunkwise mLSTM forward
+// pass (precision mode MLSTM_PREC_F64) on the vector ALUs, for the key widths
+// the matrix-core kernels (f64_mfma_kernels.hip) do not take (512), and the
+// narrowing of the fp64 chunk states to float32.
 //
 // The arithmetic is the chunkwise form used by the other kernels (TFLA
 // abstract: chunkwise-parallel recurrence with intra-chunk tiling; mLSTM
-// normaliser and max-state), carried out entirely in fp64 on the vector
-// ALUs: gate sums, exponentials, scores, contractions and the chunk states
-// (kept in fp64 in the workspace).  Each thread owns a 4 x 4 register block;
-// operands are staged through LDS in 64-wide tiles.
+// normaliser and max-state), carried out entirely in fp64: gate sums,
+// exponentials, scores and contractions, against chunk states kept in fp64
+// in the workspace.  Each thread owns a 4 x 4 register block; operands are
+// staged through LDS in 64-wide tiles.
 #include "device_common.h"
+#include "f64_common.h"
 #include "tile_order.h"
 #include "kernels.h"
 
 namespace mlstm {
 namespace {
 
-constexpr int kMaxL = 1024;
-
-__device__ __forceinline__ double log_sigmoid_d(double x) { return fmin(x, 0.0) - log1p(exp(-fabs(x))); }
-
-template <typename TIn>
-__device__ __forceinline__ double load_in(const TIn* p, size_t i);
-template <>
-__device__ __forceinline__ double load_in<float>(const float* p, size_t i) {
-  return static_cast<double>(p[i]);
-}
-template <>
-__device__ __forceinline__ double load_in<bf16_t>(const bf16_t* p, size_t i) {
-  return static_cast<double>(bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]));
-}
-
-// Block-wide inclusive scan (sum or max) of 4 doubles per thread; 256 threads.
-template <bool IS_MAX>
-__device__ void block_scan4_d(double (&v)[4], double* tot) {
-  const double ident = IS_MAX ? -INFINITY : 0.0;
-  for (int e = 1; e < 4; ++e) v[e] = IS_MAX ? fmax(v[e - 1], v[e]) : v[e - 1] + v[e];
-  const int tid = threadIdx.x;
-  tot[tid] = v[3];
-  __syncthreads();
-  // Hillis-Steele over the 256 thread totals (double buffer in tot[0..511]).
-  double* a = tot;
-  double* b = tot + 256;
-  for (int off = 1; off < 256; off <<= 1) {
-    const double x = a[tid];
-    const double y = tid >= off ? a[tid - off] : ident;
-    b[tid] = IS_MAX ? fmax(x, y) : x + y;
-    __syncthreads();
-    double* t = a;
-    a = b;
-    b = t;
-  }
-  const double pre = tid > 0 ? a[tid - 1] : ident;
-  __syncthreads();
-  for (int e = 0; e < 4; ++e) v[e] = IS_MAX ? fmax(pre, v[e]) : pre + v[e];
-}
-
-__device__ double block_max_d(double x, double* scratch) {
-  const int tid = threadIdx.x;
-  scratch[tid] = x;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) scratch[tid] = fmax(scratch[tid], scratch[tid + off]);
-    __syncthreads();
-  }
-  const double r = scratch[0];
-  __syncthreads();
-  return r;
-}
-
-// ---------------------------------------------------------------------------
-// Stage one: 64 x 64 tile of C per workgroup, thread t owns rows 4*(t/16)..+3
-// and columns 4*(t%16)..+3 of the tile.
-
-template <typename TIn, bool SIG>
-__global__ __launch_bounds__(256) void states_f64_kernel(const StatesParams p) {
-  __shared__ double s_w[kMaxL];
-  __shared__ double s_tot[512];
-  __shared__ double s_g;
-  __shared__ double s_k[32][65];
-  __shared__ double s_vv[32][65];
-
-  const int bh = blockIdx.x, kt = blockIdx.y, vt = blockIdx.z;
-  const int tid = threadIdx.x, kq = tid >> 4, vq = tid & 15;
-  const int S = p.S, DK = p.DK, DV = p.DV, L = p.L, Nc = p.Nc;
-  const TIn* K = static_cast<const TIn*>(p.K) + (size_t)bh * S * DK;
-  const TIn* V = static_cast<const TIn*>(p.V) + (size_t)bh * S * DV;
-  const float* ig = p.i_pre + (size_t)bh * S;
-  const float* fg = p.f_pre + (size_t)bh * S;
-  const bool own_n = !SIG && vt == 0;
-  double* Cs = reinterpret_cast<double*>(p.C_states);
-  double* ns = reinterpret_cast<double*>(p.n_states);
-  double* ms = reinterpret_cast<double*>(p.m_states);
-
-  double acc[4][4];
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) {
-      const int kr = kt * 64 + 4 * kq + i, vc = vt * 64 + 4 * vq + j;
-      acc[i][j] = p.C0 ? (double)p.C0[(size_t)bh * DK * DV + (size_t)kr * DV + vc] : 0.0;
-    }
-  double nreg = 0.0;
-  if (own_n && tid < 64 && p.n0) nreg = p.n0[(size_t)bh * DK + kt * 64 + tid];
-  double M = (!SIG && p.m0) ? (double)p.m0[bh] : 0.0;
-
-  for (int c = 0; c <= Nc; ++c) {
-    double* Cst = Cs + ((size_t)bh * (Nc + 1) + c) * DK * DV;
-    for (int i = 0; i < 4; ++i)
-      for (int j = 0; j < 4; ++j) Cst[(size_t)(kt * 64 + 4 * kq + i) * DV + vt * 64 + 4 * vq + j] = acc[i][j];
-    if (own_n && tid < 64) ns[((size_t)bh * (Nc + 1) + c) * DK + kt * 64 + tid] = nreg;
-    if (!SIG && kt == 0 && vt == 0 && tid == 0) ms[(size_t)bh * (Nc + 1) + c] = M;
-    if (c == Nc) break;
-
-    const int t0 = c * L, Lc = min(L, S - t0);
-    double b[4];
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      b[e] = pos < Lc ? log_sigmoid_d((double)fg[t0 + pos]) : 0.0;
-    }
-    block_scan4_d<false>(b, s_tot);
-    for (int e = 0; e < 4; ++e)
-      if (4 * tid + e == Lc - 1) s_g = b[e];
-    __syncthreads();
-    const double g = s_g;
-    double a[4], amax = -INFINITY;
-    for (int e = 0; e < 4; ++e) {
-      const int pos = 4 * tid + e;
-      if (pos < Lc) {
-        const double it = (double)ig[t0 + pos];
-        a[e] = g - b[e] + (SIG ? log_sigmoid_d(it) : it);
-        amax = fmax(amax, a[e]);
-      } else {
-        a[e] = -INFINITY;
-      }
-    }
-    double decay;
-    if constexpr (SIG) {
-      decay = exp(g);
-      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? exp(a[e]) : 0.0;
-    } else {
-      amax = block_max_d(amax, s_tot);
-      const double Mn = fmax(g + M, amax);
-      decay = exp(g + M - Mn);
-      for (int e = 0; e < 4; ++e) s_w[4 * tid + e] = (4 * tid + e < Lc) ? exp(a[e] - Mn) : 0.0;
-      M = Mn;
-    }
-    __syncthreads();
-    for (int i = 0; i < 4; ++i)
-      for (int j = 0; j < 4; ++j) acc[i][j] *= decay;
-    nreg *= decay;
-
-    for (int tb = 0; tb < Lc; tb += 32) {
-      for (int idx = tid; idx < 32 * 64; idx += 256) {
-        const int t = idx >> 6, col = idx & 63;
-        const bool ok = tb + t < Lc;
-        s_k[t][col] = ok ? load_in<TIn>(K, (size_t)(t0 + tb + t) * DK + kt * 64 + col) * s_w[tb + t] : 0.0;
-        s_vv[t][col] = ok ? load_in<TIn>(V, (size_t)(t0 + tb + t) * DV + vt * 64 + col) : 0.0;
-      }
-      __syncthreads();
-      if (own_n && tid < 64) {
-        double sacc = 0.0;
-        for (int t = 0; t < 32; ++t) sacc += s_k[t][tid];
-        nreg += sacc;
-      }
-#pragma unroll 2
-      for (int t = 0; t < 32; ++t) {
-        double kk[4], vv[4];
-        for (int i = 0; i < 4; ++i) kk[i] = s_k[t][4 * kq + i];
-        for (int j = 0; j < 4; ++j) vv[j] = s_vv[t][4 * vq + j];
-        for (int i = 0; i < 4; ++i)
-          for (int j = 0; j < 4; ++j) acc[i][j] = fma(kk[i], vv[j], acc[i][j]);
-      }
-      __syncthreads();
-    }
-  }
-  if (p.C_out)
-    for (int i = 0; i < 4; ++i)
-      for (int j = 0; j < 4; ++j)
-        p.C_out[(size_t)bh * DK * DV + (size_t)(kt * 64 + 4 * kq + i) * DV + vt * 64 + 4 * vq + j] =
-            (float)acc[i][j];
-  if (own_n && p.n_out && tid < 64) p.n_out[(size_t)bh * DK + kt * 64 + tid] = (float)nreg;
-  if (!SIG && p.m_out && kt == 0 && vt == 0 && tid == 0) p.m_out[bh] = (float)M;
-}
+using namespace f64;
 
 // ---------------------------------------------------------------------------
 // Stage two: 64 rows x 64 columns of H per workgroup; thread t owns rows
@@ -399,19 +237,8 @@ __global__ __launch_bounds__(256) void narrow_f64_kernel(const double* src, floa
 
 }  // namespace
 
-hipError_t launch_states_f64(const StatesParams& p, bool bf16_inputs, bool sig, hipStream_t stream) {
-  dim3 grid(p.BH, p.DK / 64, p.DV / 64);
-  if (bf16_inputs) {
-    if (sig) hipLaunchKernelGGL((states_f64_kernel<bf16_t, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((states_f64_kernel<bf16_t, false>), grid, dim3(256), 0, stream, p);
-  } else {
-    if (sig) hipLaunchKernelGGL((states_f64_kernel<float, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((states_f64_kernel<float, false>), grid, dim3(256), 0, stream, p);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream) {
+  if (hintra_f64m_supported(p.DK)) return launch_hintra_f64m(p, bf16_inputs, sig, stream);
   dim3 grid((unsigned)(p.BH * p.Nc * (p.L > 64 ? p.L / 64 : 1)), p.DV / 64);
   if (bf16_inputs) {
     if (sig) hipLaunchKernelGGL((hintra_f64_kernel<bf16_t, true>), grid, dim3(256), 0, stream, p);

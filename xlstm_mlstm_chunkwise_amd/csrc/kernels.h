@@ -200,10 +200,14 @@ hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipSt
 // forward schedule); rows_tile_rows(DK, DV) > 0 where it covers the shape.
 int rows_tile_rows(int DK, int DV);
 hipError_t launch_states_rows_range(const StatesParams& p, bool sig, bool split, hipStream_t stream);
-// Float64 precision mode: both stages in fp64, states kept in fp64.
+// Float64 precision mode: both stages in fp64, states kept in fp64.  The
+// states stage runs on the fp64 matrix cores; the intra-chunk stage does for
+// DK of 64, 128 or 256 (launch_hintra_f64m) and on the vector ALUs otherwise.
 hipError_t launch_states_f64(const StatesParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
 hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
 hipError_t launch_narrow_f64(const void* src, float* dst, long long n, hipStream_t stream);
+bool hintra_f64m_supported(int DK);
+hipError_t launch_hintra_f64m(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
 // Packed states (n_states x DK x DV) -> float32.
 hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
                                 hipStream_t stream);
