@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 7
+#define MLSTM_ABI_VERSION 8
 
 typedef enum {
   MLSTM_OK = 0,
@@ -102,10 +102,12 @@ typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } ml
  *   MLSTM_SCHED_TWO_STAGE: the two stages (inter-chunk recurrence writing the
  *       state entering every chunk to the workspace, then the intra-chunk
  *       stage reading them back), as mlstm_fw_states + mlstm_fw_hintra.
- *   MLSTM_SCHED_FUSED: one chunk walker per head and 128-column slice of V
- *       carries its part of the state from chunk to chunk in registers; no
- *       chunk state is written (the TFLA page lists avoiding that round trip
- *       as a planned follow-up of its two-kernel design).  Needs bf16 inputs,
+ *   MLSTM_SCHED_FUSED: one launch: a chunk walker per head and 128-column
+ *       slice of V carries its part of the state from chunk to chunk in
+ *       registers and forms the gate terms of each chunk from i_pre and
+ *       f_pre itself; no chunk state is written and no workspace is used
+ *       (the TFLA page lists avoiding the states' round trip as a planned
+ *       follow-up of its two-kernel design).  Needs bf16 inputs,
  *       MLSTM_PREC_SPLIT, DHQK = 256, DHV a multiple of 128 and
  *       chunk_size <= 512; otherwise MLSTM_E_UNSUPPORTED.  The stage-wise
  *       calls (mlstm_fw_states, mlstm_fw_hintra, mlstm_fw_unpack_states)
@@ -195,10 +197,9 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
  * and head for the exp gate, 8 for the sig gate), and 4 bytes per chunk
  * boundary and head for the stabilisers of sequence segments that stage one
  * may run side by side (two more 256-aligned regions).  A descriptor whose
- * schedule is MLSTM_SCHED_FUSED needs only the gate terms (the other regions
- * are empty); under MLSTM_SCHED_AUTO the gate terms are also present
- * wherever the fused walker supports the shape.  Returns 0 for an
- * invalid descriptor.  The storage order inside
+ * schedule is MLSTM_SCHED_FUSED needs no workspace (0 bytes); under
+ * MLSTM_SCHED_AUTO the size covers the two stages even where the fused
+ * walker runs.  Returns 0 for an invalid descriptor.  The storage order inside
  * the workspace belongs to the library (the chunk states are kept in the
  * operand order of the kernels that read them); mlstm_fw_unpack_states
  * returns the states as plain float32. */
@@ -216,8 +217,8 @@ size_t mlstm_fw_workspace_bytes(const mlstm_fw_desc_t* desc);
  *                bytes, 256-byte aligned; it may be NULL only when that size
  *                is 0.  On return it holds the chunk states (see
  *                mlstm_fw_unpack_states) when the two-stage kernels ran;
- *                after the fused walker (MLSTM_FAMILY_FUSED) it holds only
- *                the gate terms, and the chunk states were never formed.
+ *                the fused walker (MLSTM_FAMILY_FUSED) leaves it untouched:
+ *                the chunk states were never formed.
  * With S == 0 the call only copies the initial state to the outputs. */
 int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        const void* Q, const void* K, const void* V,
@@ -239,10 +240,9 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
  * The call allocates nothing.  When the workspace of the kernels that run
  * exceeds that size the call is refused with MLSTM_E_WORKSPACE before
  * anything is launched: where the fused walker runs (schedule FUSED, or AUTO
- * on a shape it covers) that is only its gate terms, 12 bytes per position
- * and head for the exp gate (B * NH * S up to 5.5 M positions); the
- * two-stage kernels need mlstm_fw_workspace_bytes(desc), mostly chunk
- * states, so they fit for small problems only.  Every call on one GPU shares that GPU's
+ * on a shape it covers) it uses none, so every size fits; the two-stage
+ * kernels need mlstm_fw_workspace_bytes(desc), mostly chunk states, so they
+ * fit for small problems only.  Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (two streams, two host
  * threads) race and give wrong results; calls ordered on one stream are
  * safe.  Nothing in the array needs to start at zero (every region a kernel

@@ -134,7 +134,7 @@ def test_noalloc_refuses_a_workspace_beyond_the_static_array(mt):
     assert e.value.status == 6
     torch.cuda.synchronize()
     assert bool(torch.all(H == 7.0))      # nothing was launched
-    # the automatic schedule runs the walker there, whose gate terms fit
+    # the automatic schedule runs the walker there, which needs no workspace
     mt.mlstm_chunkwise_fw_noalloc(q, q, v, g, g, chunk_size=w.chunk, out=H)
     torch.cuda.synchronize()
     assert bool(torch.all(H == 0.0))      # zero keys and values give zero H

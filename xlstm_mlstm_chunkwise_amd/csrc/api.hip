@@ -103,8 +103,9 @@ struct WsLayout {
   size_t c_off, n_off, m_off, g_off, ml_off, cy_off, total;
 };
 
-// Per-position gate terms: read by both wide-tile stages and by the walker.
-bool needs_gates(const mlstm_fw_desc_t* d) { return packed_layout(d) || fused_supported(d); }
+// Per-position gate terms: read by both wide-tile stages (the walker forms
+// its own).
+bool needs_gates(const mlstm_fw_desc_t* d) { return packed_layout(d) && d->schedule != MLSTM_SCHED_FUSED; }
 
 WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   const size_t BH = (size_t)d->B * d->NH;
@@ -231,15 +232,13 @@ hipError_t run_gates(const mlstm_fw_desc_t* d, const float* i_pre, const float* 
 int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
               const float* f_pre, const float* C0, const float* n0, const float* m0, const WsPtrs& ws, void* H,
               float* C_out, float* n_out, float* m_out, hipStream_t stream) {
-  hipError_t e = run_gates(d, i_pre, f_pre, ws, stream);
-  if (e != hipSuccess) return MLSTM_E_HIP;
+  (void)ws;
   mlstm::WalkParams p;
   p.Q = Q;
   p.K = K;
   p.V = V;
-  p.gb2 = ws.gb2;
-  p.gu2 = ws.gu2;
-  p.gpm2 = ws.gpm2;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
   p.C0 = C0;
   p.n0 = n0;
   p.m0 = m0;
@@ -256,7 +255,7 @@ int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void
   p.L = d->chunk_size;
   p.Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
   p.h_bf16 = d->h_dtype == MLSTM_BF16;
-  e = mlstm::launch_walk(p, d->gate == MLSTM_GATE_SIG, stream);
+  const hipError_t e = mlstm::launch_walk(p, d->gate == MLSTM_GATE_SIG, stream);
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 

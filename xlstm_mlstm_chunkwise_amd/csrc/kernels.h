@@ -83,9 +83,8 @@ struct WalkParams {
   const void* Q;
   const void* K;
   const void* V;
-  const float* gb2;  // gate terms (see GatesParams)
-  const float* gu2;
-  const float* gpm2;
+  const float* i_pre;  // (BH, S) gate pre-activations; the walker forms the gate terms
+  const float* f_pre;
   const float* C0;  // may be null (zero state)
   const float* n0;  // may be null
   const float* m0;  // may be null

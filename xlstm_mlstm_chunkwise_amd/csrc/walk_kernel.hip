@@ -26,7 +26,8 @@
 //                      those registers (the score accumulators already have
 //                      the layout of the P.V operand, with the keys taken in a
 //                      permuted order that the V reads follow).  These waves
-//                      also stage every Q, K and V tile and the gate terms.
+//                      also stage every Q, K and V tile and form the gate
+//                      terms of each chunk from the raw gate inputs.
 //   state waves 4..7   wave 4 + b holds the state block C[0 .. DK-1][32 b ..
 //                      32 b + 31] for the whole walk, forms the inter term
 //                      Q C for its columns at the start of every query tile
@@ -35,7 +36,18 @@
 //                      C = decay C + K^T (w . V) from the same key tiles.
 // Each role runs its own loop nest; both pass the same workgroup barriers in
 // the same order: one per chunk for the gate terms [G], one per query tile
-// for Q [Q], one per key tile [R] and one at the end of the chunk [N].  The
+// for Q [Q], one per key tile [R] and one at the end of the chunk [N].
+//
+// Gate terms.  With lf = log sigmoid(f) and i~ = i (exp gate) or
+// log sigmoid(i) (sig gate), the chunk needs, in log2 units, the in-chunk
+// inclusive sums b_t = lf_0 + ... + lf_t, u_t = i~_t - b_t and (exp gate)
+// the running maximum pm_t = max(u_0 .. u_t).  Before [G] each intra wave
+// scans its 64-position segments (positions 64 s .. 64 s + 63 of the chunk,
+// s = 4 e + wave) with lane shuffles and posts the segment's sum and the
+// maximum of its local u; after [G] each thread adds the sums of the earlier
+// segments to its own positions (u moves down by the same amount, the running
+// maximum takes the earlier segments' maxima) and the finished terms are read
+// after [Q].  No separate pass or workspace is needed.  The
 // four column slices of a head compute the same score tiles (the price of
 // keeping C on-chip); they are placed on one XCD so their Q and K reads share
 // an L2.
@@ -86,6 +98,18 @@ __device__ __forceinline__ int swz_base(int r, int c0, int x) {
   return r * W + 32 * (x ^ (k >> 2)) + 8 * (((c0 >> 3) ^ k) & 3) + (c0 & 7);
 }
 
+// Inclusive scan (sum or max) over the 64 lanes of a wave.
+template <bool IS_MAX>
+__device__ __forceinline__ float wave_scan(float x) {
+  const int lane = (int)threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x = scan_op<IS_MAX>(x, y);
+  }
+  return x;
+}
+
 __device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
   const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
   return __builtin_bit_cast(uint2, v);
@@ -117,6 +141,7 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
   __shared__ __align__(16) float s_gu[kWalkMaxL];
   __shared__ __align__(16) float s_gb[kWalkMaxL];
   __shared__ __align__(16) float s_gpm[SIG ? 4 : kWalkMaxL];
+  __shared__ float s_segT[kWalkMaxL / 64], s_segX[kWalkMaxL / 64];  // per-segment sum of lf, max of local u
   __shared__ __align__(16) uint16_t s_nh[DK], s_nl[DK];  // normaliser as bf16 hi / lo
   __shared__ __align__(16) float s_np[SIG ? 4 : 4 * DK];
 
@@ -184,7 +209,7 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
     // order; K / V tiles in (chunk, query tile, key tile) order.  Piece e of
     // a thread is piece tid + 256 e of the tile (16 bytes, row-major groups).
     uint4 qpre[QPT], kpre[KPT], vpre[VPT];
-    float gpre_u[GPT], gpre_b[GPT], gpre_pm[GPT];
+    float gpre_f[GPT], gpre_i[GPT];
     int qc = 0, qi = 0;          // next Q tile to load
     int kc = 0, ki = 0, kj = 0;  // next K / V tile to load
     auto load_q = [&]() {
@@ -226,9 +251,8 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       for (int e = 0; e < GPT; ++e) {
         const int t = tid + e * NA;
         const bool ok = t < Lc;
-        gpre_u[e] = ok ? p.gu2[gbase + t0 + t] : 0.0f;
-        gpre_b[e] = ok ? p.gb2[gbase + t0 + t] : 0.0f;
-        gpre_pm[e] = (!SIG && ok) ? p.gpm2[gbase + t0 + t] : 0.0f;
+        gpre_f[e] = ok ? p.f_pre[gbase + t0 + t] : 0.0f;
+        gpre_i[e] = ok ? p.i_pre[gbase + t0 + t] : 0.0f;
       }
     };
     // LDS offsets of this thread's K and V pieces (rows tid / 32 + 8 e and
@@ -262,21 +286,38 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       set_roles();
       const int t0 = c * L, Lc = chunk_len(c);
       const int nsub = nsub_of(Lc);
-      // u past the end of a short last chunk is -inf: those keys (zero rows)
-      // get weight exactly zero
+      // segment-local gate terms of this thread's positions; u past the end
+      // of a short last chunk is -inf, so those keys (zero rows) get weight
+      // exactly zero
+      float lb[GPT], lu[GPT], lpm[GPT];
 #pragma unroll
       for (int e = 0; e < GPT; ++e) {
         const int t = tid + e * NA;
-        if (t < L) {
-          s_gu[t] = t < Lc ? gpre_u[e] : -INFINITY;
-          s_gb[t] = gpre_b[e];
-          if constexpr (!SIG) s_gpm[t] = gpre_pm[e];
+        const bool ok = t < Lc;
+        lb[e] = wave_scan<false>(ok ? log_sigmoid(gpre_f[e]) * kLog2e : 0.0f);
+        lu[e] = ok ? (SIG ? log_sigmoid(gpre_i[e]) : gpre_i[e]) * kLog2e - lb[e] : -INFINITY;
+        lpm[e] = SIG ? 0.0f : wave_scan<true>(lu[e]);
+        if (lane == 63) {
+          s_segT[t >> 6] = lb[e];
+          s_segX[t >> 6] = lpm[e];
         }
       }
       load_gates(c + 1);
       __syncthreads();  // [G] gate terms
-      float g2, Mn, dec;
-      chunk_scalars(Lc, M, g2, Mn, dec);
+      // add the earlier segments (uniform per wave) to this thread's positions
+#pragma unroll
+      for (int e = 0; e < GPT; ++e) {
+        const int t = tid + e * NA;
+        float B = 0.0f, P = -INFINITY;
+        for (int sg = 0; sg < (t >> 6); ++sg) {
+          if constexpr (!SIG) P = fmaxf(P, s_segX[sg] - B);
+          B += s_segT[sg];
+        }
+        s_gb[t] = lb[e] + B;
+        s_gu[t] = lu[e] - B;
+        if constexpr (!SIG) s_gpm[t] = fmaxf(P, lpm[e] - B);
+      }
+      float g2, Mn, dec;  // set after the first [Q] of the chunk
       float np[8];  // n partial sums of this thread's K column group (exp gate)
 #pragma unroll
       for (int e = 0; e < 8; ++e) np[e] = 0.0f;
@@ -292,6 +333,7 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
         load_q();
         __syncthreads();  // [Q] query tile
         set_roles();
+        if (i == 0) chunk_scalars(Lc, M, g2, Mn, dec);
         // this wave's 16 queries as B fragments of the 16x16x32 score blocks
         uint4 qf[NSS];
 #pragma unroll
@@ -573,7 +615,7 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
     {
       // a zero-extent resource reads zeros when there is no initial state
       const __amdgpu_buffer_rsrc_t rc =
-          make_rsrc(p.C0 ? p.C0 + (size_t)bh * DK * DV : p.gb2, p.C0 ? (uint32_t)(DK * DV * 4) : 0u);
+          make_rsrc(p.C0 ? p.C0 + (size_t)bh * DK * DV : p.f_pre, p.C0 ? (uint32_t)(DK * DV * 4) : 0u);
       float16_t c0[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -601,14 +643,14 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
       const int Lc = chunk_len(c);
       const int nsub = nsub_of(Lc);
       __syncthreads();  // [G] gate terms
-      float g2, Mn, dec;
-      chunk_scalars(Lc, M, g2, Mn, dec);
+      float g2, Mn, dec;  // set after the first [Q] of the chunk
       // query tile i; LAST: the chunk's last tile, which also updates the state
       auto sub_tile = [&](auto last_c, int i) {
         constexpr bool last = decltype(last_c)::value;
         set_roles();
         __syncthreads();  // [Q] query tile
         set_roles();
+        if (i == 0) chunk_scalars(Lc, M, g2, Mn, dec);
         // ---- inter term Q C for this wave's columns, both 32-row halves
         {
           float16_t hq[2];
