@@ -498,7 +498,7 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     for it in range(args.steps):
         ev[it][0].record(stream)
         st = L.mlstm_bw_recompute(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
-                                  P(ws), ws_bytes, sp)
+                                  P(dH), P(ws), ws_bytes, sp)
         ev[it][1].record(stream)
         st2 = L.mlstm_bw_grads(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
                                *grads, P(ws), ws_bytes, sp)

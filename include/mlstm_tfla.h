@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 8
+#define MLSTM_ABI_VERSION 9
 
 typedef enum {
   MLSTM_OK = 0,
@@ -414,7 +414,13 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,
  * change in between.
  *   mlstm_bw_recompute: the forward quantities the gradient needs, into the
  *       workspace (two-stage forward kernels: chunk states, and for the exp
- *       gate H in float32 with the per-row m and normaliser).
+ *       gate the per-row m and normaliser, with the row terms of the
+ *       gradient that read dH: 1/z and delta = -(dh . h) / z * sign(den)
+ *       where |den| > e^{-m}, else 0).  On the wide kernels (bf16 inputs,
+ *       DHQK 128 or 256, DHV 256 or 512) the intra-chunk kernel forms those
+ *       row terms in its epilogue and H is never stored; elsewhere H is
+ *       stored in float32 and the gradient stage forms them.  dH is
+ *       required (as in mlstm_chunkwise_bw).
  *   mlstm_bw_grads: the gradient kernels on that workspace (bf16 inputs:
  *       bf16 matrix cores, computed operands as bf16 hi + lo pairs; float32
  *       inputs: fp32 matrix cores): per-position gate terms, the state-gradient recurrence
@@ -425,6 +431,7 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc,
                        const void* Q, const void* K, const void* V,
                        const float* i_pre, const float* f_pre,
                        const float* C0, const float* n0, const float* m0,
+                       const void* dH,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
 int mlstm_bw_grads(const mlstm_fw_desc_t* desc,

@@ -66,7 +66,7 @@ def test_binding_signatures_match_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 8
+    assert mt.abi_version() == 9
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -283,8 +283,10 @@ def test_backward_refuses_before_launch():
     # the stage calls check the same way
     rc = lambda desc, **kw: lib.mlstm_bw_recompute(
         ctypes.byref(desc), *[kw.get(n, 4096 * (j + 1)) for j, n in enumerate(
-            ["q", "k", "v", "i", "f", "C0", "n0", "m0", "ws"])], kw.get("ws_bytes", need), None)
+            ["q", "k", "v", "i", "f", "C0", "n0", "m0", "dH", "ws"])], kw.get("ws_bytes", need), None)
     assert rc(d, q=None) == 1
+    assert rc(d, dH=None) == 1
+    assert rc(d, dH=4096 * 9 + 4) == 8
     assert rc(d, ws_bytes=need - 1) == 6
     assert rc(ds, n0=4096) == 5
     gr = lambda desc, **kw: lib.mlstm_bw_grads(
@@ -299,24 +301,39 @@ def test_backward_refuses_before_launch():
 
 def test_backward_workspace_formula():
     """Workspace of the 7B-shaped backward: the forward's two-stage workspace
-    plus float32 chunk states, H, six per-position arrays, the state gradients
-    after each chunk, the initial-state gradients and (bf16 inputs) the
-    weighted dS tiles that the dk pass hands to the dq pass, each region
-    rounded up to 256 bytes."""
+    plus float32 chunk states, six per-position arrays (the recompute forms
+    1/z and delta in the intra-chunk kernel, so H is not kept on these
+    shapes), the state gradients after each chunk, the initial-state
+    gradients and (bf16 inputs) the weighted dS tiles that the dk pass hands
+    to the dq pass, each region rounded up to 256 bytes.  The generic shapes
+    (here DHQK 64) keep H."""
     d = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
     lib = mt.lib()
     BH, S, DK, DV, Nc = 64, 8192, 256, 512, 32
     r = lambda x: (x + 255) // 256 * 256
     fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(d)))
+    rest = [BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                     # b, src, 1/z, delta
+            BH * Nc * DK * DV * 4, BH * Nc * DK * 4,                            # state gradients
+            BH * S * 4, BH * S * 4,                                             # q.dq, k.dk
+            BH * DK * DV * 4, BH * DK * 4]                                      # dC0, dn0
     expect = fw + sum(r(x) for x in [
         BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,   # states
-        BH * S * DV * 4, BH * S * 4, BH * S * 4,                                 # H, m, den
-        BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                          # b, src, 1/z, delta
-        BH * Nc * DK * DV * 4, BH * Nc * DK * 4,                                 # state gradients
-        BH * S * 4, BH * S * 4,                                                  # q.dq, k.dk
-        BH * DK * DV * 4, BH * DK * 4,                                           # dC0, dn0
+        0, BH * S * 4, BH * S * 4,                                               # (no H), m, den
+        *rest,
         BH * Nc * 10 * 64 * 64 * 4])                  # weighted dS of the 10 tile pairs per chunk
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
+    # generic kernels (DHQK 64): H in float32 as well
+    DK = 64
+    dg = _desc(B=8, NH=8, S=8192, DHQK=DK, DHV=512, chunk_size=256)
+    fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(dg)))
+    rest[4:6] = [BH * Nc * DK * DV * 4, BH * Nc * DK * 4]
+    rest[8:10] = [BH * DK * DV * 4, BH * DK * 4]
+    expect = fw + sum(r(x) for x in [
+        BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,
+        BH * S * DV * 4, BH * S * 4, BH * S * 4,                                 # H, m, den
+        *rest,
+        BH * Nc * 10 * 64 * 64 * 4])
+    assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dg)) == expect
 
 
 def test_q8_step_refuses_before_launch():

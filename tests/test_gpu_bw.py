@@ -224,7 +224,7 @@ def test_stage_calls_match_the_whole_backward(mt):
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     L = mt.lib()
     assert L.mlstm_bw_recompute(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]), P(t["i"]), P(t["f"]),
-                                P(t["C0"]), P(t["n0"]), P(t["m0"]), P(ws), nb, s) == 0
+                                P(t["C0"]), P(t["n0"]), P(t["m0"]), P(t["dH"]), P(ws), nb, s) == 0
     assert L.mlstm_bw_grads(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]), P(t["i"]), P(t["f"]),
                             P(t["C0"]), P(t["n0"]), P(t["dH"]), *[P(o[n]) for n in o], P(ws), nb, s) == 0
     torch.cuda.synchronize()

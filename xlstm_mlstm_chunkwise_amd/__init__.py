@@ -76,7 +76,7 @@ _SYMBOLS = {
     "mlstm_bw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_bw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 18
                            + [ctypes.c_size_t, ctypes.c_void_p]),
-    "mlstm_bw_recompute": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 9
+    "mlstm_bw_recompute": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 10
                            + [ctypes.c_size_t, ctypes.c_void_p]),
     "mlstm_bw_grads": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 17
                        + [ctypes.c_size_t, ctypes.c_void_p]),

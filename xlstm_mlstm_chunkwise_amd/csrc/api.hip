@@ -307,7 +307,8 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
 
 int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
                const float* f_pre, const WsPtrs& ws, void* H, float* m_rows, float* den_rows,
-               hipStream_t stream) {
+               hipStream_t stream, const void* dH = nullptr, bool dh_bf16 = false, float* ginvz = nullptr,
+               float* gdelta = nullptr) {
   if (d->S == 0) return MLSTM_OK;
   HintraParams p;
   p.Q = Q;
@@ -335,6 +336,12 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   p.h_bf16 = d->h_dtype == MLSTM_BF16;
   p.tile_lq = d->tile_lq ? d->tile_lq : 64;
   p.tile_lkv = d->tile_lkv ? d->tile_lkv : 64;
+  // backward recompute: the row terms of the gradient instead of H (wide
+  // kernel; dH is float32 or bf16 as h_dtype of the caller's descriptor says)
+  p.dH = dH;
+  p.dh_bf16 = dh_bf16;
+  p.ginvz = ginvz;
+  p.gdelta = gdelta;
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
   const bool sig = d->gate == MLSTM_GATE_SIG;
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
@@ -464,7 +471,17 @@ mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
   r.schedule = MLSTM_SCHED_TWO_STAGE;
   r.h_dtype = MLSTM_F32;
   if (r.chunk_size < 64) r.chunk_size = 64;
+  // the library's own tiles (64-row intra-chunk tiles hold whole rows, which
+  // the row terms of the gradient need); the result does not depend on them
+  r.tile_lq = r.tile_lkv = 0;
   return r;
+}
+
+// Exp gate on the wide kernels: the recompute forms the row terms of the
+// gradient (1/z and delta) in the intra-chunk kernel's epilogue from dH, and
+// H is never stored; elsewhere it stores H for the gradient stage.
+bool bw_delta_in_recompute(const mlstm_fw_desc_t* d2) {
+  return d2->gate == MLSTM_GATE_EXP && packed_layout(d2);
 }
 
 struct BwLayout {
@@ -487,7 +504,7 @@ BwLayout bw_layout(const mlstm_fw_desc_t* d2) {
   l.Cst = take(BH * (Nc + 1) * DK * DV * f);
   l.nst = take(ex ? BH * (Nc + 1) * DK * f : 0);
   l.mst = take(ex ? BH * (Nc + 1) * f : 0);
-  l.H = take(ex ? BH * S * DV * f : 0);
+  l.H = take(ex && !bw_delta_in_recompute(d2) ? BH * S * DV * f : 0);
   l.mrows = take(ex ? BH * S * f : 0);
   l.den = take(ex ? BH * S * f : 0);
   l.gb = take(BH * S * f);
@@ -805,12 +822,12 @@ float* bw_states_f32(const mlstm_fw_desc_t* d2, void* workspace, float* region) 
 
 int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
                        const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       const void* dH, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
-  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre)) return MLSTM_E_NULLPTR;
+  if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH)) return MLSTM_E_NULLPTR;
   if ((st = check_sig_nulls(desc, n0, m0, nullptr, nullptr)) != MLSTM_OK) return st;
-  for (const void* x : {Q, K, V})
+  for (const void* x : {Q, K, V, dH})
     if (x && !aligned(x, 16)) return MLSTM_E_ALIGN;
   if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0})) != MLSTM_OK) return st;
   const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
@@ -835,7 +852,13 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   const bool convert = d2.precision == MLSTM_PREC_F64;
   if (st == MLSTM_OK)
     st = unpack_states(&d2, fw, convert ? at(l.Cst) : nullptr, ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
-  if (st == MLSTM_OK && ex) st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
+  if (st == MLSTM_OK && ex) {
+    if (bw_delta_in_recompute(&d2))
+      st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, nullptr, at(l.mrows), at(l.den), s, dH,
+                      desc->h_dtype == MLSTM_BF16, at(l.ginvz), at(l.gdelta));
+    else
+      st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, at(l.H), at(l.mrows), at(l.den), s);
+  }
   return st;
 }
 
@@ -865,7 +888,8 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.i_pre = i_pre;
   p.f_pre = f_pre;
   p.dH = dH;
-  p.H = ex ? at(l.H) : nullptr;
+  p.delta_ready = bw_delta_in_recompute(&d2);
+  p.H = ex && !p.delta_ready ? at(l.H) : nullptr;
   p.m_rows = ex ? at(l.mrows) : nullptr;
   p.den_rows = ex ? at(l.den) : nullptr;
   p.C_states = bw_states_f32(&d2, workspace, at(l.Cst));
@@ -922,7 +946,7 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
   const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
   if (!workspace || workspace_bytes < bw_layout(&d2).total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
-  st = mlstm_bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, workspace, workspace_bytes, stream);
+  st = mlstm_bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, workspace, workspace_bytes, stream);
   if (st != MLSTM_OK) return st;
   return mlstm_bw_grads(desc, Q, K, V, i_pre, f_pre, C0, n0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0, workspace,
                         workspace_bytes, stream);

@@ -142,7 +142,8 @@ __global__ __launch_bounds__(256) void bw_prep_kernel(const BwParams p) {
       p.gsrc[rb + pos] = SIG ? log_sigmoid(ip) : ip;
     }
   }
-  if constexpr (!SIG) {
+  // exp gate: 1/z and delta, unless the recompute formed them
+  if (!SIG && !p.delta_ready) {
     // float32 dH on 16-byte boundaries: 16-byte loads, the row's pieces all
     // in flight at once
     const bool vec = !p.dh_bf16 && (p.DV & 255) == 0 && (reinterpret_cast<uintptr_t>(p.dH) & 15) == 0;

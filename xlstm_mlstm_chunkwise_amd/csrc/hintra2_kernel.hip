@@ -53,8 +53,9 @@ struct Wide {
   static_assert(DK % 32 == 0, "DHQK must be a multiple of 32");
 };
 
-template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT>
+template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT, bool DELTA = false>
 __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) {
+  static_assert(!DELTA || (!SIG && TV == DV), "the row terms of the gradient need whole rows (exp gate)");
   typedef Wide<DK, TV, TQ> W;
   constexpr int NVT = DV / TV;
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
@@ -529,8 +530,75 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           }
         }
     };
-    if (p.h_bf16) store_h(std::integral_constant<int, 2>{});
-    else store_h(std::integral_constant<int, 4>{});
+    // Backward recompute (exp gate, whole rows per workgroup): instead of H,
+    // the row terms of the gradient, from dh . h with h = acc / z.
+    auto store_delta = [&](auto dsize) {
+      constexpr int E = decltype(dsize)::value;  // bytes per dH element
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const char*>(p.dH) + ((size_t)bh * S + t0) * DV * E,
+                                                  (uint32_t)(Lc * DV * E));
+      const int dvoff = ((row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32) * E;
+      // this lane's partial sums over its columns, slot j = 16 rb + 4 r4 + q
+      // for row wr0 + 32 rb + 8 r4 + 4 h2 + q
+      float part[32];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rowl = 32 * rb + 8 * r4;
+          const float4 inv = *reinterpret_cast<const float4*>(s_den2 + wr0 + rowl + 4 * h2);
+          const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int dro = dvoff + (rowl + q) * DV * E;
+            float d = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < W::CB; ++cb) {
+              float dh;
+              if constexpr (E == 2)
+                dh = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rd, dro + 32 * cb * E, 0, 0) << 16);
+              else
+                dh = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, dro + 32 * cb * E, 0, 0));
+              d += dh * acc[rb][cb][4 * r4 + q];
+            }
+            part[16 * rb + 4 * r4 + q] = d * invq[q];
+          }
+        }
+      // butterfly over the 32 lanes of each half-wave: after the step with
+      // offset o, a lane keeps the half of its slots whose bit o matches its
+      // lane bit; at the end lane l32 holds the sum of slot l32
+#pragma unroll
+      for (int n = 32, o = 16; o >= 1; n >>= 1, o >>= 1) {
+        const bool up = (l32 & o) != 0;
+#pragma unroll
+        for (int j = 0; j < n / 2; ++j) {
+          const float send = up ? part[j] : part[j + n / 2];
+          const float keep = up ? part[j + n / 2] : part[j];
+          part[j] = keep + __shfl_xor(send, o, 64);
+        }
+      }
+      // slot l32 = 16 rb + 4 r4 + q: row wr0 + 32 rb + 8 r4 + 4 h2 + q
+      const int rl = wr0 + 32 * (l32 >> 4) + 8 * ((l32 >> 2) & 3) + 4 * h2 + (l32 & 3);
+      float* const s_dp = reinterpret_cast<float*>(s_buf);  // [column wave][row], the K/P/V space is free
+      s_dp[(wave % W::NWC) * TQ + rl] = part[0];
+      __syncthreads();
+      if (tid < TQ && row0 + tid < Lc) {
+        float d = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W::NWC; ++w) d += s_dp[w * TQ + tid];
+        const float den = s_row_den[tid], invz = s_den2[tid];
+        const size_t ro = (size_t)bh * S + t0 + row0 + tid;
+        p.ginvz[ro] = invz;
+        p.gdelta[ro] = fabsf(den) > exp2f(-s_row_m2[tid]) ? (den > 0.0f ? -d * invz : d * invz) : 0.0f;
+      }
+    };
+    if constexpr (DELTA) {
+      if (p.dh_bf16) store_delta(std::integral_constant<int, 2>{});
+      else store_delta(std::integral_constant<int, 4>{});
+    } else if (p.h_bf16) {
+      store_h(std::integral_constant<int, 2>{});
+    } else {
+      store_h(std::integral_constant<int, 4>{});
+    }
     if constexpr (!SIG) {
       if (vt == 0 && tid < TQ && row0 + tid < Lc) {
         const size_t ro = (size_t)bh * S + t0 + row0 + tid;
@@ -558,6 +626,13 @@ hipError_t launch_t(const HintraParams& p0, hipStream_t stream) {
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const long long ntile = (long long)p.BH * ((p.c_hi < 0 ? p.Nc : p.c_hi) - p.c_lo) * (p.L / TQ) * (DV / TV);
   dim3 grid((unsigned)(ntile < cus ? ntile : cus));
+  if constexpr (!SIG && TV == DV) {
+    if (p.dH) {
+      hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT, true>), grid, dim3(512), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.dH) return hipErrorInvalidValue;  // the row terms need whole rows and the exp gate
   hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }

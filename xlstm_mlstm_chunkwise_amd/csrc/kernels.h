@@ -75,6 +75,13 @@ struct HintraParams {
   // Chunk range and state slots as in StatesParams (wide kernel only).
   int c_lo = 0, c_hi = -1, slots = 0;
   int pair_tiles = 0;  // wide kernel: schedule row tiles p and NQT-1-p together
+  // Backward recompute (wide kernel, exp gate, 64-row tiles): with dH set,
+  // H is not stored; per row the kernel writes ginvz = 1 / (max(|den|, e^-m)
+  // + eps) and gdelta = -(dh . h) ginvz sign(den) where |den| > e^-m, else 0.
+  const void* dH = nullptr;
+  int dh_bf16 = 0;
+  float* ginvz = nullptr;
+  float* gdelta = nullptr;
 };
 
 // Fused chunk walker: one workgroup per (head, 128-column slice of V) runs
@@ -136,7 +143,8 @@ struct BwParams {
   const float* i_pre;  // (BH, S)
   const float* f_pre;
   const void* dH;        // (BH, S, DV), bf16 or float32
-  const float* H;        // (BH, S, DV) float32 (exp gate)
+  const float* H;        // (BH, S, DV) float32 (exp gate), or null when delta_ready
+  int delta_ready;       // exp gate: the recompute already wrote ginvz and gdelta
   const float* m_rows;   // (BH, S) exp gate
   const float* den_rows; // (BH, S) exp gate
   const float* C_states; // (BH, Nc + 1, DK, DV) float32 row-major: state entering each chunk
