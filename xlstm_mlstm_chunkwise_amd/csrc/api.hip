@@ -889,6 +889,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.f_pre = f_pre;
   p.dH = dH;
   p.delta_ready = bw_delta_in_recompute(&d2);
+  p.G_packed = nullptr;  // set by the launcher where the row-tile recurrence runs
   p.H = ex && !p.delta_ready ? at(l.H) : nullptr;
   p.m_rows = ex ? at(l.mrows) : nullptr;
   p.den_rows = ex ? at(l.den) : nullptr;

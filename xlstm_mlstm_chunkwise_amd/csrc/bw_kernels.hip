@@ -36,9 +36,12 @@
 // Kernels, 256 threads each; with float32 inputs on fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: exact products of float32 operands), with bf16
 // inputs on bf16 matrix cores with computed operands split (below):
-//   bw_prep    per position: b, src, 1/z, delta
+//   bw_prep    per position: b, src, and 1/z, delta unless the recompute
+//              formed them
 //   bw_dstate  the reverse recurrence of (G, N): one workgroup per head and
 //              64 x 64 tile of G, chunks in reverse order; G_c goes to HBM
+//              (the row-tile variant writes it in the packed bf16 hi + lo
+//              layout of the chunk states, which dk and dv then stage as is)
 //   bw_tiles   dq per 64-query tile, dk and dv per 64-key tile: the inter-
 //              chunk term first, then for each causal partner tile the
 //              64 x 64 score tile (dP or the raw scores), weighted in
@@ -671,8 +674,8 @@ __global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
 // waves keeps a TK x DV tile of G (each wave a 64 x 64 block on the 32x32x16
 // matrix cores) while it walks the chunks from last to first.  Each block of
 // 32 weighted dH rows is then staged once for all TK key rows, and each Q
-// block once for all value columns.  Per chunk c: G and N leave for slot c,
-// are decayed by the chunk's gate and gain the chunk's sums
+// block once for all value columns.  Per chunk c: G (packed hi + lo) and N
+// leave for slot c, are decayed by the chunk's gate and gain the chunk's sums
 //   G += Q^T (w . dH),  N += Q^T wd,
 // w_t = s e^{b_t + M_c - m_t} / z_t and wd_t the same with delta_t (sig gate:
 // w_t = s e^{b_t}, no N).  Q enters the matrix cores as raw bf16 (exact);
@@ -896,17 +899,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   };
 
   // matrix-core side
+  // G_c in the packed hi + lo layout of the chunk states: each half of a
+  // 32 x 32 accumulator is one fragment (16-row k step, 32-column block)
   auto write_g = [&](int c) {
-    float* G = p.dC_states + ((size_t)bh * Nc + c) * DK * DV;
+    uint16_t* P = p.G_packed + ((size_t)bh * Nc + c) * DK * DV * 2;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          const int vcol = wc0 + 32 * cb + l32;
-          __builtin_nontemporal_store(acc[rb][cb][r], G + (size_t)krow * DV + vcol);
+        for (int half = 0; half < 2; ++half) {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            split_bf16x2(acc[rb][cb][8 * half + 2 * q], acc[rb][cb][8 * half + 2 * q + 1], hw[q], lw[q]);
+          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (wc0 + 32 * cb) / 32;
+          typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(u32x4_t{hw[0], hw[1], hw[2], hw[3]},
+                                      reinterpret_cast<u32x4_t*>(P + pack_frag_offset(kk, nb, 0, DV) + lane * 8));
+          __builtin_nontemporal_store(u32x4_t{lw[0], lw[1], lw[2], lw[3]},
+                                      reinterpret_cast<u32x4_t*>(P + pack_frag_offset(kk, nb, 1, DV) + lane * 8));
         }
   };
   auto mma_blk = [&](auto set, int gi) {
@@ -1107,12 +1119,19 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
       constexpr int NYC = W / kT;
       const int nxc = own_D / kT;
       // state tile of (x chunk, y chunk): [k][v] for every mode (dv reads it transposed)
-      const uint16_t* Pk = nullptr;  // dq: packed states, rows k, columns v
-      if constexpr (MODE == kModeDQ)
+      // packed states (dq: C; dk, dv: G), rows k, columns v
+      const uint16_t* Pk = nullptr;
+      if constexpr (MODE == kModeDQ) {
         if (p.C_packed) Pk = p.C_packed + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
+      } else {
+        if (p.G_packed) Pk = p.G_packed + ((size_t)bh * Nc + c) * DK * DV * 2;
+      }
       auto pre_state = [&](float (&x)[16], int xi, int yc) {
         if (Pk) {
-          pre_packed(x, Pk, DV, (y0 + yc * kT) / 16, xi * 2);
+          // the 64 x 64 tile of rows k, columns v: dq and dk take k = y,
+          // v = x; dv takes k = x, v = y
+          if constexpr (MODE == kModeDV) pre_packed(x, Pk, DV, xi * 4, (y0 + yc * kT) / 32);
+          else pre_packed(x, Pk, DV, (y0 + yc * kT) / 16, xi * 2);
           return;
         }
         if constexpr (MODE == kModeDV) pre16(x, St, false, xi * kT, DV, y0 + yc * kT, kT);
@@ -1418,8 +1437,13 @@ hipError_t launch_tiles(const BwParams& p, int W, hipStream_t s) {
 }
 
 template <bool SIG>
-hipError_t launch_all(const BwParams& p, hipStream_t s) {
+hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   hipError_t e;
+  // The row-tile state recurrence (bf16 inputs, DHV 512 or 256) leaves the
+  // state gradients packed, for the dk and dv passes to stage as they are.
+  BwParams p = p0;
+  const bool rows_kernel = p.qkv_bf16 && (p.DV == 512 || (p.DV == 256 && p.DK % 128 == 0));
+  p.G_packed = rows_kernel ? reinterpret_cast<uint16_t*>(p.dC_states) : nullptr;
   hipLaunchKernelGGL((bw_prep_kernel<SIG>), dim3((unsigned)(p.BH * p.Nc)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gs((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT));

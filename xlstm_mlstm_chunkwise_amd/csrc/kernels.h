@@ -145,6 +145,8 @@ struct BwParams {
   const void* dH;        // (BH, S, DV), bf16 or float32
   const float* H;        // (BH, S, DV) float32 (exp gate), or null when delta_ready
   int delta_ready;       // exp gate: the recompute already wrote ginvz and gdelta
+  uint16_t* G_packed;    // the state gradients in the packed bf16 hi + lo layout of the chunk
+                         // states (row-tile recurrence), in dC_states' space, or null
   const float* m_rows;   // (BH, S) exp gate
   const float* den_rows; // (BH, S) exp gate
   const float* C_states; // (BH, Nc + 1, DK, DV) float32 row-major: state entering each chunk
