@@ -136,7 +136,7 @@ def _oracle_head(args):
 
 
 # Worker processes of the CPU baseline: every core of this process's
-# affinity set, up to 16 (a one-GPU machine's share of its host's cores).
+# affinity set, up to 16 (the host cores that come with one GPU).
 MAX_CPU_WORKERS = 16
 
 
