@@ -8,7 +8,8 @@ float64 forms (no GPU needed).
    single bf16 rounding, fp8 e4m3 with a scale per 64 values and int8 with
    a scale per 64 values each move H by more than the 2e-2 bound: the state
    alone needs about 16 significant bits, so the hand-off stays a hi + lo
-   pair (4 bytes per value).
+   pair (4 bytes per value).  int16 codes with a scale per 64 values (2
+   bytes, 16 bits) meet the bound.
 2. The int8 decode state.  Over 512 decoded tokens after a 256-token
    prefill, h read from the int8 block state drifts from h of the float
    state by a bounded few percent of max |h| (the forget gate decays old
@@ -50,6 +51,16 @@ def _int8_blocks(x):
     return q8_decode(*q8_encode(x))
 
 
+def _int16_blocks(x, blk=64):
+    """int16 codes with one scale amax / 32767 per 64 consecutive values of a
+    row (round half to even)."""
+    DK, DV = x.shape
+    xb = x.reshape(DK, DV // blk, blk)
+    amax = np.abs(xb).max(axis=2, keepdims=True)
+    sc = np.where(amax > 0, amax / 32767.0, 1.0)
+    return (np.round(xb / sc) * sc).reshape(DK, DV)
+
+
 def _handoff_errors(x, L, quantisers):
     """max |dH| of the exp gate when the inter-chunk term reads a quantised
     copy of the chunk-boundary state (float64 chunkwise form otherwise)."""
@@ -83,11 +94,14 @@ def _handoff_errors(x, L, quantisers):
 def test_chunk_state_handoff_needs_sixteen_bits():
     w = WORKLOADS["bf16_7b_s8192"]
     err = _handoff_errors(head_inputs(w, 0, 0), w.chunk, {"hilo": _hilo, "bf16": _bf16, "e4m3": _e4m3_blocks,
-                                                        "int8": _int8_blocks})
+                                                        "int8": _int8_blocks, "int16": _int16_blocks})
     print("\n" + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
     assert err["hilo"] < 1e-3
     for name in ("bf16", "e4m3", "int8"):
         assert err[name] > 2e-2, (name, err[name])
+    # a 2-byte hand-off that keeps 16 bits (int16 codes, a scale per 64
+    # values) meets the bound with a wide margin
+    assert err["int16"] < 3e-3, err["int16"]
 
 
 def test_int8_decode_state_drift_is_bounded():
