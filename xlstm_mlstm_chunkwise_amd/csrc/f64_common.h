@@ -23,40 +23,41 @@ __device__ __forceinline__ double load_in<bf16_t>(const bf16_t* p, size_t i) {
   return static_cast<double>(bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-// Block-wide inclusive scan (sum or max) of 4 doubles per thread; 256 threads.
+// Block-wide inclusive scan (sum or max) of 4 doubles per thread; 256
+// threads (4 waves).  Each thread scans its 4 values, each wave scans its 64
+// thread totals with lane shuffles, and the waves' totals go through LDS
+// (`tot`, at least 4 doubles): two barriers in all.
 template <bool IS_MAX>
 __device__ inline void block_scan4_d(double (&v)[4], double* tot) {
   const double ident = IS_MAX ? -INFINITY : 0.0;
   for (int e = 1; e < 4; ++e) v[e] = IS_MAX ? fmax(v[e - 1], v[e]) : v[e - 1] + v[e];
-  const int tid = threadIdx.x;
-  tot[tid] = v[3];
-  __syncthreads();
-  // Hillis-Steele over the 256 thread totals (double buffer in tot[0..511]).
-  double* a = tot;
-  double* b = tot + 256;
-  for (int off = 1; off < 256; off <<= 1) {
-    const double x = a[tid];
-    const double y = tid >= off ? a[tid - off] : ident;
-    b[tid] = IS_MAX ? fmax(x, y) : x + y;
-    __syncthreads();
-    double* t = a;
-    a = b;
-    b = t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double x = v[3];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off, 64);
+    if (lane >= off) x = IS_MAX ? fmax(x, y) : x + y;
   }
-  const double pre = tid > 0 ? a[tid - 1] : ident;
+  if (lane == 63) tot[wave] = x;
   __syncthreads();
+  double pre = ident;
+  for (int w = 0; w < wave; ++w) pre = IS_MAX ? fmax(pre, tot[w]) : pre + tot[w];
+  double ex = __shfl_up(x, 1, 64);  // this wave's total before this thread
+  if (lane == 0) ex = ident;
+  pre = IS_MAX ? fmax(pre, ex) : pre + ex;
+  __syncthreads();  // tot is free again
   for (int e = 0; e < 4; ++e) v[e] = IS_MAX ? fmax(pre, v[e]) : pre + v[e];
 }
 
+// Maximum over the block (256 threads): lane shuffles within each wave, the
+// four wave maxima through LDS (`scratch`, at least 4 doubles).
 __device__ inline double block_max_d(double x, double* scratch) {
-  const int tid = threadIdx.x;
-  scratch[tid] = x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off, 64));
+  if (lane == 0) scratch[wave] = x;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) scratch[tid] = fmax(scratch[tid], scratch[tid + off]);
-    __syncthreads();
-  }
-  const double r = scratch[0];
+  const double r = fmax(fmax(scratch[0], scratch[1]), fmax(scratch[2], scratch[3]));
   __syncthreads();
   return r;
 }

@@ -27,7 +27,7 @@ template <typename TIn, bool SIG>
 __global__ __launch_bounds__(256) void hintra_f64_kernel(const HintraParams p) {
   __shared__ double s_b[kMaxL];
   __shared__ double s_u[kMaxL];
-  __shared__ double s_tot[512];
+  __shared__ double s_tot[4];  // wave totals of the block scans
   __shared__ double s_q[64][33];
   __shared__ double s_x[64][33];  // key rows [sigma][k], or state block [k][v] as [v][k]
   __shared__ double s_pv[64][65]; // P tile [tau][sigma], then values [sigma][v]

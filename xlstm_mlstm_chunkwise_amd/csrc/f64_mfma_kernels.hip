@@ -118,7 +118,7 @@ __device__ __forceinline__ void widen8<float>(const uint4 (&u)[2], double (&x)[8
 template <typename TIn, bool SIG>
 __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) {
   __shared__ double s_w[kMaxL];
-  __shared__ double s_tot[512];
+  __shared__ double s_tot[4];  // wave totals of the block scans
   __shared__ double s_g;
   __shared__ __align__(32) double s_kwt[64 * kSLD];  // [state row][step]
   __shared__ __align__(32) double s_vt[64 * kSLD];   // [column][step]
@@ -287,10 +287,10 @@ struct F64mLayout {
   static constexpr int V_BYTES = TV * LDV * (int)sizeof(TIn);
   // One region holds, phase by phase, the gate sums b (kMaxL doubles), the
   // state blocks of the inter-chunk term and the key tiles; the scan scratch
-  // (512 doubles) of the gate phase lives in the value tile's space.
+  // (4 doubles) of the gate phase lives in the value tile's space.
   static constexpr int A_BYTES = K_BYTES > C_BYTES ? (K_BYTES > kMaxL * 8 ? K_BYTES : kMaxL * 8)
                                                    : (C_BYTES > kMaxL * 8 ? C_BYTES : kMaxL * 8);
-  static_assert(V_BYTES >= 512 * 8, "scan scratch must fit in the value tile");
+  static_assert(V_BYTES >= 4 * 8, "scan scratch must fit in the value tile");
 };
 
 template <typename TIn, bool SIG, int DK, int TV>
