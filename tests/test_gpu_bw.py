@@ -160,18 +160,20 @@ def test_backward_without_state_grads_and_empty_sequence(mt):
 def test_backward_full_size_sampled_heads(mt, wname):
     """The 7B-shaped workloads (B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk
     256; and the long-context one, B=1, NH=8, S=65536, chunk 1024, 128-row
-    tiles, with an initial state), the whole backward on the GPU.  The
-    oracle checks the last T positions of two heads, T = 4 chunks at chunk
-    256 and 3 chunks at chunk 1024, so the reverse state-gradient recurrence
-    crosses three or more chunk boundaries inside the checked span and the
-    inter-chunk terms of dQ, dK, dV are checked there.  Their gradients are
-    those of the tail problem that starts from the exact state at the cut
-    (every later query and key sits in the tail; the prefix enters only
-    through that state), which the float64 chunkwise oracle supplies."""
+    tiles, with an initial state), the whole backward on the GPU, checked on
+    two heads.  At 8192 tokens the oracle takes each head whole (every
+    position, all 32 chunk boundaries of the reverse state-gradient
+    recurrence, and the initial-state gradients).  At 65536 tokens the
+    quadratic form of a whole head does not fit in host memory, so the
+    oracle checks the last 8 chunks (8192 positions, seven chunk boundaries
+    inside the span): their gradients are those of the tail problem that
+    starts from the exact state at the cut (every later query and key sits
+    in the tail; the prefix enters only through that state), which the
+    float64 chunkwise oracle supplies."""
     w = WORKLOADS[wname]
     heads = [(0, 0), (w.B - 1, w.NH - 1)]
     S, DK, DV = w.S, w.DHQK, w.DHV
-    T = 4 * w.chunk if w.chunk <= 256 else 3 * w.chunk
+    T = min(S, 8192)
     rng = np.random.default_rng(31)
     dH = rng.standard_normal((w.B, w.NH, S, DV)).astype(np.float32)
     per = {(b, h): head_inputs(w, b, h) for b in range(w.B) for h in range(w.NH)}
@@ -183,7 +185,7 @@ def test_backward_full_size_sampled_heads(mt, wname):
         init = dict(C0=_dev(stack("C0")), n0=_dev(stack("n0")), m0=_dev(stack("m0")))
     g = mt.mlstm_chunkwise_bw(_dev(stack("q"), qd), _dev(stack("k"), qd), _dev(stack("v"), qd),
                               _dev(stack("i")), _dev(stack("f")), _dev(dH), chunk_size=w.chunk, gate=w.gate,
-                              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, **init)
+                              tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, state_grads=True, **init)
     torch.cuda.synchronize()
     g = {n: t.cpu().numpy().astype(np.float64) for n, t in g.items()}
     for (b, h) in heads:
@@ -192,14 +194,21 @@ def test_backward_full_size_sampled_heads(mt, wname):
         st0 = {}
         if w.init_state:
             st0 = dict(C0=x["C0"][None], n0=x["n0"][None], m0=np.asarray(x["m0"])[None])
-        pre = chunkwise_fw(x["q"][None, :t0], x["k"][None, :t0], x["v"][None, :t0], x["i"][None, :t0],
-                           x["f"][None, :t0], gate=w.gate, chunk_size=w.chunk, **st0)
-        C, n, m = pre[1], pre[2], pre[3]
+        if t0 == 0:
+            C, n, m = st0.get("C0"), st0.get("n0"), st0.get("m0")
+        else:
+            pre = chunkwise_fw(x["q"][None, :t0], x["k"][None, :t0], x["v"][None, :t0], x["i"][None, :t0],
+                               x["f"][None, :t0], gate=w.gate, chunk_size=w.chunk, **st0)
+            C, n, m = pre[1], pre[2], pre[3]
         r = grad_fw(x["q"][None, t0:], x["k"][None, t0:], x["v"][None, t0:], x["i"][None, t0:],
                     x["f"][None, t0:], dH[b, h][None, t0:].astype(np.float64), C,
                     n if w.gate == "exp" else None, m if w.gate == "exp" else None, gate=w.gate)
-        gt = {k: g[k][b, h][None, t0:] for k in KEYS}
-        _compare(f"{wname} head {(b, h)} tail {T}", gt, r, "bf16", KEYS)
+        keys = KEYS
+        if t0 == 0:
+            # the whole head: the initial-state gradients are the GPU's too
+            keys = KEYS + (("dC0", "dn0") if w.gate == "exp" else ("dC0",))
+        gt = {k: g[k][b, h][None, t0:] if k in KEYS else g[k][b, h][None] for k in keys}
+        _compare(f"{wname} head {(b, h)} " + ("whole" if t0 == 0 else f"tail {T}"), gt, r, "bf16", keys)
 
 
 def test_stage_calls_match_the_whole_backward(mt):
