@@ -43,6 +43,8 @@ KERNEL_SOURCES = {
     "blocked": ("states2_kernel.hip", "hintra2_kernel.hip", "gates_kernel.hip", "device_common.h"),
     "step": ("step_kernel.hip", "device_common.h"),
     "step_q8": ("step_kernel.hip", "device_common.h"),
+    "states_int16": ("states2_kernel.hip", "gates_kernel.hip", "device_common.h"),
+    "hintra_int16": ("hintra2_kernel.hip", "device_common.h"),
     "states_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
     "hintra_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
 }
@@ -86,11 +88,13 @@ def algorithmic_bytes(w, h_bytes: int) -> dict:
     }
 
 
-def chunk_state_bytes(w) -> int:
+def chunk_state_bytes(w, codes: str = "split") -> int:
     """Bytes of the chunk states the two stages pass through HBM (written by
-    the states stage, read by the intra-chunk stage)."""
+    the states stage, read by the intra-chunk stage): 4 bytes a value, or
+    with int16 codes 2 bytes a value plus a 4-byte scale per 512 values."""
     nc = -(-w.S // w.chunk)
-    per_state = (w.DHQK * w.DHV + (0 if w.gate == "sig" else w.DHQK + 1)) * 4
+    c_bytes = w.DHQK * w.DHV * 4 if codes == "split" else w.DHQK * w.DHV * 2 + (w.DHQK * w.DHV // 512) * 4
+    per_state = c_bytes + (0 if w.gate == "sig" else (w.DHQK + 1) * 4)
     return w.BH * (nc + 1) * per_state
 
 
@@ -220,6 +224,8 @@ def main(argv=None) -> int:
     ap.add_argument("--tile-lq", type=int, default=None, help="override the workload's intra-chunk row tile")
     ap.add_argument("--schedule", default="auto", choices=["auto", "two_stage", "fused", "blocked"],
                     help="kernels of the forward pass (see mlstm_schedule_t)")
+    ap.add_argument("--state-codes", default="split", choices=["split", "int16"],
+                    help="chunk-state hand-off of the two stages (see mlstm_state_codes_t)")
     ap.add_argument("--block-chunks", type=int, default=0,
                     help="chunks per block of the blocked schedule (0: the library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
@@ -293,14 +299,14 @@ def main(argv=None) -> int:
                         qkv_dtype=mt.MLSTM_BF16 if w.qkv_dtype == "bf16" else mt.MLSTM_F32,
                         h_dtype=mt.MLSTM_BF16 if args.h_dtype == "bf16" else mt.MLSTM_F32,
                         gate=w.gate, precision=args.precision, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv,
-                        schedule=args.schedule, block_chunks=args.block_chunks)
+                        schedule=args.schedule, block_chunks=args.block_chunks, state_codes=args.state_codes)
     family = mt.kernel_family(desc)
     fused = family in (mt.MLSTM_FAMILY_FUSED, mt.MLSTM_FAMILY_BLOCKED)
     one_call = "blocked" if family == mt.MLSTM_FAMILY_BLOCKED else "walk"
     ws = torch.empty(max(1, mt.workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     kw = dict(chunk_size=w.chunk, gate=w.gate, h_dtype=h_dtype, precision=args.precision,
               tile_lq=w.tile_lq, tile_lkv=w.tile_lkv, schedule=args.schedule, workspace=ws, out=H,
-              block_chunks=args.block_chunks)
+              block_chunks=args.block_chunks, state_codes=args.state_codes)
 
     def step():
         return mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, **kw)
@@ -368,7 +374,9 @@ def main(argv=None) -> int:
     dominant = max(t_stage, key=t_stage.get)
     t_dom = t_stage[dominant]
     f64_mode = mt.kernel_family(desc) == mt.MLSTM_FAMILY_F64
-    traffic, traffic_src = recorded_traffic(w.name, dominant + ("_f64" if f64_mode else ""), args.tile_lq)
+    codes = args.state_codes if not fused else "split"
+    traffic, traffic_src = recorded_traffic(
+        w.name, dominant + ("_f64" if f64_mode else "") + ("_int16" if codes == "int16" else ""), args.tile_lq)
     if f64_mode:
         # The float64 kernels do about 50 FLOP per algorithmic byte, above the
         # fp64 ridge point (78.6 TFLOP/s over 8 TB/s, ~10 FLOP/byte): they are
@@ -399,13 +407,14 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK, "DHV": w.DHV,
                    "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "h_dtype": args.h_dtype,
                    "precision": args.precision, "tile_lq": w.tile_lq or 64,
-                   "schedule": {"walk": "fused", "blocked": "blocked"}[one_call] if fused else "two_stage"},
+                   "schedule": {"walk": "fused", "blocked": "blocked"}[one_call] if fused else "two_stage",
+                   "state_codes": codes},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "wall_ms_per_step": wall_ms,
         "kernels_ms": t_stage,
         "kernels_GBps": {k: abytes[k] / (t_stage[k] * 1e-3) / 1e9 for k in t_stage},
-        "chunk_state_bytes": chunk_state_bytes(w),
+        "chunk_state_bytes": chunk_state_bytes(w, codes),
         "kernels_TFLOPs": {k: f_stage[k] / (t_stage[k] * 1e-3) / 1e12 for k in t_stage},
         "roofline": roof,
     }

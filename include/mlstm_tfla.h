@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 9
+#define MLSTM_ABI_VERSION 10
 
 typedef enum {
   MLSTM_OK = 0,
@@ -91,9 +91,10 @@ typedef enum { MLSTM_GATE_EXP = 0, MLSTM_GATE_SIG = 1 } mlstm_gate_t;
  *                     Default.
  *   MLSTM_PREC_F16:   a single bf16 rounding of the operand (one pass).
  *   MLSTM_PREC_F64:   everything (gates, scores, contractions, chunk states)
- *                     in fp64 on the vector units; for rows whose sums cancel
- *                     too strongly for fp32 accumulation.  Workspace states
- *                     take 8 bytes per value.
+ *                     in fp64, on the fp64 matrix cores (the intra-chunk
+ *                     stage at DHQK 512 on the vector units); for rows whose
+ *                     sums cancel too strongly for fp32 accumulation.
+ *                     Workspace states take 8 bytes per value.
  * SPLIT and F16 are the same for float32 inputs, which use fp32 matrix-core
  * instructions. */
 typedef enum { MLSTM_PREC_SPLIT = 0, MLSTM_PREC_F16 = 1, MLSTM_PREC_F64 = 2 } mlstm_prec_t;
@@ -124,6 +125,27 @@ typedef enum {
   MLSTM_SCHED_BLOCKED = 3
 } mlstm_schedule_t;
 
+/* How the two-stage schedule hands the chunk states from stage one to stage
+ * two (the quantised-state follow-up on the "flash-xlstm-exp 0.1.0" page,
+ * "Upgrade roadmap", item 3, applied to the hand-off):
+ *   MLSTM_STATES_SPLIT: each value as a bf16 hi + lo pair, 4 bytes, the
+ *       split the intra-chunk kernel feeds to the matrix cores.  Default.
+ *   MLSTM_STATES_I16:   int16 codes, 2 bytes a value, with one
+ *       power-of-two float32 scale per 16 x 32 block of the state (its
+ *       largest magnitude over 32767, rounded up; codes round half to even).
+ *       The intra-chunk kernel turns each code into the exact hi + lo pair
+ *       of code * scale, so the only added error is the coding step, at most
+ *       half a scale per value: max |dH| 3e-3 on the 7B-shaped exp workload
+ *       (CPU measurement), inside the 2e-2 bound.  Needs bf16 inputs,
+ *       MLSTM_PREC_SPLIT, the wide family with DHQK 128 or 256 and DHV 256
+ *       or 512, and a schedule other than MLSTM_SCHED_FUSED and
+ *       MLSTM_SCHED_BLOCKED (else MLSTM_E_UNSUPPORTED).  Stage one then runs
+ *       its row-tile kernel in one sequence segment.  It halves the chunk
+ *       states of the workspace.  Under MLSTM_SCHED_AUTO the field applies
+ *       where the two stages run (the fused walker hands no states over).
+ *       The backward pass ignores it. */
+typedef enum { MLSTM_STATES_SPLIT = 0, MLSTM_STATES_I16 = 1 } mlstm_state_codes_t;
+
 typedef struct {
   int32_t B, NH;       /* batch, heads: >= 1                                   */
   int32_t S;           /* sequence length: >= 0, need not divide chunk_size;
@@ -144,7 +166,8 @@ typedef struct {
   int32_t block_chunks; /* MLSTM_SCHED_BLOCKED: chunks per block, >= 0; 0 =
                            library (a block's chunk states fill half of the
                            256 MB Infinity Cache); ignored otherwise        */
-  int32_t reserved[2]; /* must be zero                                        */
+  int32_t state_codes; /* mlstm_state_codes_t; 0 = bf16 hi + lo pairs       */
+  int32_t reserved;    /* must be zero                                        */
 } mlstm_fw_desc_t;
 
 /* ABI version of the loaded library (MLSTM_ABI_VERSION). */
@@ -171,7 +194,9 @@ int64_t mlstm_fw_num_chunks(const mlstm_fw_desc_t* desc);
  *                         workgroups,
  *                         bf16 operands, chunk states in the packed operand
  *                         layout
- *   MLSTM_FAMILY_F64      MLSTM_PREC_F64: fp64 vector-unit kernels
+ *   MLSTM_FAMILY_F64      MLSTM_PREC_F64: fp64 kernels on the fp64 matrix
+ *                         cores (the intra-chunk stage at DHQK 512 on the
+ *                         vector units)
  *   MLSTM_FAMILY_FUSED    the fused chunk walker (see mlstm_schedule_t):
  *                         bf16 operands, state carried in registers
  * This is the family mlstm_chunkwise_fw runs.  The stage-wise calls run
@@ -192,7 +217,9 @@ int mlstm_fw_kernel_family(const mlstm_fw_desc_t* desc);
  * stabilised state entering every chunk plus the final state, i.e. N_c + 1
  * states per head of DHQK x DHV values, DHQK normaliser values and one
  * max-state (exp gate), each region 256-byte aligned; 4 bytes per value, 8
- * with MLSTM_PREC_F64.  For MLSTM_FAMILY_WIDE it also holds per-position gate
+ * with MLSTM_PREC_F64; with MLSTM_STATES_I16 the chunk states take 2 bytes
+ * per value plus one more region of 4 bytes per 16 x 32 block of each state
+ * (its scale).  For MLSTM_FAMILY_WIDE it also holds per-position gate
  * terms, written by stage one and read by stage two (12 bytes per position
  * and head for the exp gate, 8 for the sig gate), and 4 bytes per chunk
  * boundary and head for the stabilisers of sequence segments that stage one

@@ -66,7 +66,7 @@ def test_binding_signatures_match_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 9
+    assert mt.abi_version() == 10
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -74,10 +74,11 @@ def test_abi_version_and_status_strings():
 
 
 def test_desc_layout_matches_header():
-    # 16 int/float fields plus reserved[2], all 4 bytes
+    # 17 int/float fields plus reserved, all 4 bytes
     assert ctypes.sizeof(mt.FwDesc) == 18 * 4
     assert mt.FwDesc.schedule.offset == 14 * 4
     assert mt.FwDesc.block_chunks.offset == 15 * 4
+    assert mt.FwDesc.state_codes.offset == 16 * 4
 
 
 def _desc(**kw):
@@ -135,7 +136,10 @@ def test_validation_errors(kw, code):
 
 def test_reserved_fields_must_be_zero():
     d = _desc()
-    d.reserved[1] = 1
+    d.reserved = 1
+    assert mt.validate(d) == 9
+    d = _desc()
+    d.state_codes = 2
     assert mt.validate(d) == 9
     d = _desc()
     d.block_chunks = -1
@@ -434,3 +438,35 @@ def test_blocked_schedule():
     wsb = mt.workspace_bytes(d)
     assert lib.mlstm_fw_states(ctypes.byref(d), *([4096] * 7), 1 << 20, wsb, None, None, None, None) == 5
     assert lib.mlstm_fw_hintra(ctypes.byref(d), *([4096] * 5), 1 << 20, wsb, 4096, None, None, None) == 5
+
+
+def test_int16_state_codes():
+    """int16-coded chunk states: the wide family with split operands and a
+    row-tile shape, on the two-stage schedule; the chunk states take 2 bytes
+    a value plus one float32 scale per 16 x 32 block."""
+    def r256(x):
+        return (x + 255) // 256 * 256
+    BH = 6
+    for DK, DV in ((256, 512), (128, 512), (256, 256), (128, 256)):
+        for sched in ("auto", "two_stage"):
+            d = _desc(DHQK=DK, DHV=DV, chunk_size=256, schedule=sched, state_codes="int16")
+            assert mt.validate(d) == 0, (DK, DV, sched)
+            Nc = (1000 + 255) // 256
+            expect = (r256(BH * (Nc + 1) * DK * DV * 2) + r256(BH * (Nc + 1) * DK * 4) + r256(BH * (Nc + 1) * 4)
+                      + r256(BH * 1000 * 4 * 3) + r256(BH * (Nc + 1) * 4)
+                      + r256(BH * (Nc + 1) * (DK // 16) * (DV // 32) * 4))
+            assert mt.workspace_bytes(d) == expect, (DK, DV, sched)
+    # sig gate: no normaliser or stabiliser regions
+    ds = _desc(DHQK=256, DHV=512, chunk_size=256, schedule="two_stage", state_codes="int16", gate="sig")
+    Nc = 4
+    assert mt.workspace_bytes(ds) == (r256(BH * (Nc + 1) * 256 * 512 * 2) + r256(BH * 1000 * 4 * 2)
+                                      + r256(BH * (Nc + 1) * 4) + r256(BH * (Nc + 1) * 16 * 16 * 4))
+    for kw in (dict(DHQK=128, DHV=64),                                   # generic family
+               dict(DHQK=256, DHV=512, chunk_size=256, precision="f16"),   # single-rounded operands
+               dict(DHQK=256, DHV=512, chunk_size=256, precision="f64"),
+               dict(DHQK=256, DHV=512, chunk_size=256, qkv_dtype=mt.MLSTM_F32),
+               dict(DHQK=256, DHV=512, chunk_size=256, schedule="fused"),
+               dict(DHQK=256, DHV=512, chunk_size=256, schedule="blocked")):
+        d = _desc(state_codes="int16", **kw)
+        assert mt.validate(d) == 5, kw
+        assert mt.workspace_bytes(d) == 0

@@ -233,6 +233,62 @@ def test_fused_parity_against_recurrent_oracle(mt, name, over):
     print(f"[{name}] max|dH|={e:.3g}", flush=True)
 
 
+# int16-coded chunk-state hand-off of the two-stage schedule: the row-tile
+# states kernel writes int16 codes with one power-of-two scale per 16 x 32
+# block, the wide intra-chunk kernel turns them back into exact bf16 hi + lo
+# pairs.  Every head against the recurrent oracle at the bf16 bound; also the
+# largest difference to the pair hand-off on the same inputs.
+CODES = [
+    ("int16_exp_d256_v512_l64_init", dict(B=1, NH=2, S=333, DHQK=256, DHV=512, chunk=64, init_state=True)),
+    ("int16_sig_d256_v512_l256", dict(gate="sig", B=1, NH=2, S=520, DHQK=256, DHV=512, chunk=256)),
+    ("int16_exp_d128_v256", dict(B=2, NH=1, S=300, DHQK=128, DHV=256, chunk=128)),
+    ("int16_exp_d256_v256_tq128_init", dict(B=1, NH=1, S=700, DHQK=256, DHV=256, chunk=256, tile_lq=128,
+                                            tile_lkv=128, init_state=True)),
+    ("int16_sig_d128_v512_l512_init", dict(gate="sig", B=1, NH=1, S=1100, DHQK=128, DHV=512, chunk=512,
+                                           init_state=True)),
+    ("int16_exp_l1024_tq128_init", dict(B=1, NH=1, S=1500, DHQK=256, DHV=512, chunk=1024, tile_lq=128,
+                                        tile_lkv=128, init_state=True)),
+    ("int16_exp_spikes", dict(B=1, NH=2, S=520, DHQK=256, DHV=512, chunk=128, i_dist=("normal", 0.0, 2.0),
+                              i_spike_prob=0.01)),
+    ("int16_exp_bf16_h", dict(B=1, NH=1, S=300, DHQK=128, DHV=512, chunk=64)),
+]
+
+
+@pytest.mark.parametrize("name,over", CODES, ids=[s[0] for s in CODES])
+def test_int16_state_codes_parity(mt, name, over):
+    w = _small_workload(over)
+    x = make_inputs(w)
+    h_bf16 = name.endswith("bf16_h")
+    kw = dict(h_dtype=torch.bfloat16) if h_bf16 else {}
+    gpu = _run_gpu(mt, w, x, state_codes="int16", **kw)
+    pair = _run_gpu(mt, w, x, **kw)
+    ref = [np.zeros_like(g) if g is not None else None for g in gpu]
+    for b in range(w.B):
+        for h in range(w.NH):
+            r = _oracle(w, x, (b, h), fn="recurrent")
+            for slot in range(4):
+                if r[slot] is not None:
+                    ref[slot][b, h] = r[slot]
+    e = _compare(w, gpu, ref, name, h_bf16=h_bf16)
+    print(f"\n[{name}] max|dH|={e:.3g} max|H|={np.abs(ref[0]).max():.3g} "
+          f"max|H_int16 - H_pair|={np.abs(gpu[0] - pair[0]).max():.3g}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["bf16_7b_s8192", "sig_7b_s8192"])
+def test_int16_state_codes_full_size_sampled_heads(mt, name):
+    """The two-stage schedule with int16-coded chunk states on the full
+    7B-shaped workloads."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    gpu = _run_gpu(mt, w, x, state_codes="int16")
+    worst = 0.0
+    for (b, h) in [(0, 0), (w.B - 1, w.NH - 1)]:
+        ref = _oracle(w, x, (b, h))
+        g = [None if o is None else o[b, h] for o in gpu]
+        worst = max(worst, _compare(w, g, ref, f"int16 {name} head {(b, h)}"))
+    print(f"\n[{name} int16 states] max|dH|={worst:.3g}", flush=True)
+
+
 def test_fused_bf16_h_and_empty_sequence(mt):
     w = _small_workload(dict(B=1, NH=2, S=300, DHQK=256, DHV=256, chunk=128))
     x = make_inputs(w)
@@ -390,12 +446,18 @@ def test_bf16_h_output(mt):
     dict(DHQK=128, DHV=256, chunk=64, gate="sig"),
     # enough heads for several chunks per sequence segment (interior joins)
     dict(B=4, NH=4, S=620, DHQK=256, DHV=512, chunk=64),
-    dict(B=2, NH=16, S=700, DHQK=128, DHV=256, chunk=64, gate="sig")],
-    ids=["rowmajor_states", "packed_states", "packed_states_sig", "segments_exp", "segments_sig"])
+    dict(B=2, NH=16, S=700, DHQK=128, DHV=256, chunk=64, gate="sig"),
+    # int16-coded states (one segment); their coding step is at most half a
+    # scale, 2^-16 of the block's largest magnitude
+    dict(DHQK=256, DHV=512, chunk=128, codes="int16"),
+    dict(B=4, NH=4, S=620, DHQK=128, DHV=256, chunk=64, gate="sig", codes="int16")],
+    ids=["rowmajor_states", "packed_states", "packed_states_sig", "segments_exp", "segments_sig",
+         "int16_states", "int16_states_sig_few_heads"])
 def test_stage_states_match_oracle_chunk_states(mt, shape):
     """Stage one's chunk states (unpacked to float32) against the oracle's."""
     shape = dict(shape)
     gate = shape.pop("gate", "exp")
+    codes = shape.pop("codes", "split")
     base = dict(B=1, NH=2, S=450)
     base.update(shape)
     w = _small_workload(dict(init_state=True, gate=gate, **base))
@@ -407,8 +469,9 @@ def test_stage_states_match_oracle_chunk_states(mt, shape):
     n0 = m0 = None
     if gate == "exp":
         n0, m0 = _to_dev(x["n0"], torch.float32), _to_dev(x["m0"], torch.float32)
-    ws, C, n, m = mt.mlstm_fw_states(k, v, i_pre, f_pre, C0, n0, m0, chunk_size=w.chunk, gate=gate)
-    Cst, nst, mst = mt.unpack_states(q, v, ws, chunk_size=w.chunk, gate=gate)
+    ws, C, n, m = mt.mlstm_fw_states(k, v, i_pre, f_pre, C0, n0, m0, chunk_size=w.chunk, gate=gate,
+                                     state_codes=codes)
+    Cst, nst, mst = mt.unpack_states(q, v, ws, chunk_size=w.chunk, gate=gate, state_codes=codes)
     torch.cuda.synchronize()
     Cst = Cst.cpu().numpy()
     for (b, h) in sorted({(0, 0), (0, 1), (w.B - 1, w.NH - 1), (w.B // 2, w.NH // 2)}):

@@ -9,7 +9,8 @@ float64 forms (no GPU needed).
    a scale per 64 values each move H by more than the 2e-2 bound: the state
    alone needs about 16 significant bits, so the hand-off stays a hi + lo
    pair (4 bytes per value).  int16 codes with a scale per 64 values (2
-   bytes, 16 bits) meet the bound.
+   bytes, 16 bits) meet the bound, and so do int16 codes with a power-of-two
+   scale per 16 x 32 block (the library's MLSTM_STATES_I16 hand-off).
 2. The int8 decode state.  Over 512 decoded tokens after a 256-token
    prefill, h read from the int8 block state drifts from h of the float
    state by a bounded few percent of max |h| (the forget gate decays old
@@ -61,6 +62,18 @@ def _int16_blocks(x, blk=64):
     return (np.round(xb / sc) * sc).reshape(DK, DV)
 
 
+def _int16_frag_p2(x):
+    """int16 codes with one power-of-two scale per 16 x 32 block (16 rows of
+    DHQK, 32 columns of DHV: one matrix-core fragment of the packed layout),
+    the smallest power of two at or above amax / 32767 (round half to even)."""
+    DK, DV = x.shape
+    xb = x.reshape(DK // 16, 16, DV // 32, 32)
+    amax = np.abs(xb).max(axis=(1, 3), keepdims=True)
+    e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / 32767.0)), 0.0)
+    sc = np.exp2(e)
+    return (np.round(xb / sc) * sc).reshape(DK, DV)
+
+
 def _handoff_errors(x, L, quantisers):
     """max |dH| of the exp gate when the inter-chunk term reads a quantised
     copy of the chunk-boundary state (float64 chunkwise form otherwise)."""
@@ -94,7 +107,8 @@ def _handoff_errors(x, L, quantisers):
 def test_chunk_state_handoff_needs_sixteen_bits():
     w = WORKLOADS["bf16_7b_s8192"]
     err = _handoff_errors(head_inputs(w, 0, 0), w.chunk, {"hilo": _hilo, "bf16": _bf16, "e4m3": _e4m3_blocks,
-                                                        "int8": _int8_blocks, "int16": _int16_blocks})
+                                                        "int8": _int8_blocks, "int16": _int16_blocks,
+                                                        "int16_frag": _int16_frag_p2})
     print("\n" + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
     assert err["hilo"] < 1e-3
     for name in ("bf16", "e4m3", "int8"):
@@ -102,6 +116,10 @@ def test_chunk_state_handoff_needs_sixteen_bits():
     # a 2-byte hand-off that keeps 16 bits (int16 codes, a scale per 64
     # values) meets the bound with a wide margin
     assert err["int16"] < 3e-3, err["int16"]
+    # the form the library builds (mlstm_state_codes_t MLSTM_STATES_I16): a
+    # power-of-two scale per 16 x 32 fragment, up to twice the step of an
+    # exact per-64 scale, still 7x inside the bound
+    assert err["int16_frag"] < 5e-3, err["int16_frag"]
 
 
 def test_int8_decode_state_drift_is_bounded():

@@ -26,6 +26,8 @@ _PREC = {"split": MLSTM_PREC_SPLIT, "f16": MLSTM_PREC_F16, "f64": MLSTM_PREC_F64
 _GATE = {"exp": MLSTM_GATE_EXP, "sig": MLSTM_GATE_SIG}
 _SCHED = {"auto": MLSTM_SCHED_AUTO, "two_stage": MLSTM_SCHED_TWO_STAGE, "fused": MLSTM_SCHED_FUSED,
           "blocked": MLSTM_SCHED_BLOCKED}
+MLSTM_STATES_SPLIT, MLSTM_STATES_I16 = 0, 1
+_CODES = {"split": MLSTM_STATES_SPLIT, "int16": MLSTM_STATES_I16}
 
 STATUS_NAMES = {
     0: "MLSTM_OK", 1: "MLSTM_E_NULLPTR", 2: "MLSTM_E_SHAPE", 3: "MLSTM_E_CHUNK",
@@ -48,7 +50,7 @@ class FwDesc(ctypes.Structure):
         ("qkv_dtype", ctypes.c_int32), ("h_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
         ("precision", ctypes.c_int32), ("qk_scale", ctypes.c_float), ("eps", ctypes.c_float),
         ("tile_lq", ctypes.c_int32), ("tile_lkv", ctypes.c_int32), ("schedule", ctypes.c_int32),
-        ("block_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+        ("block_chunks", ctypes.c_int32), ("state_codes", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -109,7 +111,7 @@ def status_str(status: int) -> str:
 
 def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=MLSTM_F32,
               gate="exp", precision="split", qk_scale=0.0, eps=0.0, tile_lq=0, tile_lkv=0,
-              schedule="auto", block_chunks=0) -> FwDesc:
+              schedule="auto", block_chunks=0, state_codes="split") -> FwDesc:
     d = FwDesc()
     d.B, d.NH, d.S, d.DHQK, d.DHV, d.chunk_size = B, NH, S, DHQK, DHV, chunk_size
     d.qkv_dtype, d.h_dtype = qkv_dtype, h_dtype
@@ -119,6 +121,7 @@ def make_desc(B, NH, S, DHQK, DHV, chunk_size, *, qkv_dtype=MLSTM_BF16, h_dtype=
     d.tile_lq, d.tile_lkv = tile_lq, tile_lkv
     d.schedule = _SCHED[schedule] if isinstance(schedule, str) else schedule
     d.block_chunks = block_chunks
+    d.state_codes = _CODES[state_codes] if isinstance(state_codes, str) else state_codes
     return d
 
 
@@ -179,7 +182,7 @@ def _stream():
 
 
 def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule="auto",
-              block_chunks=0):
+              block_chunks=0, state_codes="split"):
     torch = _torch()
     B, NH, S, DK = q.shape
     DV = v.shape[-1]
@@ -187,7 +190,8 @@ def _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq
     return make_desc(B, NH, S, DK, DV, chunk_size, qkv_dtype=_dtype_code(q), h_dtype=hcode,
                      gate=gate, precision=precision,
                      qk_scale=0.0 if qk_scale is None else float(qk_scale), eps=float(eps),
-                     tile_lq=tile_lq, tile_lkv=tile_lkv, schedule=schedule, block_chunks=block_chunks)
+                     tile_lq=tile_lq, tile_lkv=tile_lkv, schedule=schedule, block_chunks=block_chunks,
+                     state_codes=state_codes)
 
 
 def _check_inputs(q, k, v, i_pre, f_pre):
@@ -208,7 +212,8 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
                        gate: str = "exp", h_dtype=None, precision: str = "split",
                        qk_scale: Optional[float] = None, eps: float = 0.0,
                        tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto", workspace=None,
-                       return_final_state: bool = True, out=None, block_chunks: int = 0):
+                       return_final_state: bool = True, out=None, block_chunks: int = 0,
+                       state_codes: str = "split"):
     """Chunkwise mLSTM forward pass on the GPU.
 
     q, k: (B, NH, S, DHQK); v: (B, NH, S, DHV), bfloat16 or float32;
@@ -218,7 +223,8 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     return_final_state is False.  H is float32 unless h_dtype says otherwise.
     schedule: "auto", "two_stage", "fused" or "blocked" (see
     mlstm_schedule_t); block_chunks: chunks per block of the blocked
-    schedule (0: the library's choice).
+    schedule (0: the library's choice); state_codes: "split" or "int16", how
+    the two stages hand the chunk states over (see mlstm_state_codes_t).
     """
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
@@ -227,7 +233,7 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     _check(n0, "n0", (B, NH, DK), torch.float32)
     _check(m0, "m0", (B, NH), torch.float32)
     desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule,
-                     block_chunks)
+                     block_chunks, state_codes)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_chunkwise_fw")
@@ -261,7 +267,8 @@ NOALLOC_WORKSPACE_BYTES = 64 << 20   # MLSTM_NOALLOC_WORKSPACE_BYTES
 def mlstm_chunkwise_fw_noalloc(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
                                gate: str = "exp", precision: str = "split", qk_scale: Optional[float] = None,
                                eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto",
-                               out=None, C_out=None, n_out=None, m_out=None, block_chunks: int = 0):
+                               out=None, C_out=None, n_out=None, m_out=None, block_chunks: int = 0,
+                               state_codes: str = "split"):
     """mlstm_chunkwise_fw on the library's static workspace
     (mlstm_chunkwise_fw_noalloc): no workspace argument, and nothing is
     allocated when every output is given (out = H, whose dtype is the H
@@ -278,7 +285,7 @@ def mlstm_chunkwise_fw_noalloc(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None,
     _check(n_out, "n_out", (B, NH, DK), torch.float32)
     _check(m_out, "m_out", (B, NH), torch.float32)
     desc = _desc_for(q, v, chunk_size, gate, H.dtype, precision, qk_scale, eps, tile_lq, tile_lkv, schedule,
-                     block_chunks)
+                     block_chunks, state_codes)
     st = lib().mlstm_chunkwise_fw_noalloc(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
         _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out), _stream())
@@ -299,13 +306,14 @@ def _workspace(desc, workspace, dev):
 
 def mlstm_fw_states(k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size: int,
                     gate: str = "exp", precision: str = "split", tile_lq: int = 0, tile_lkv: int = 0,
-                    workspace=None, return_final_state: bool = True):
+                    workspace=None, return_final_state: bool = True, state_codes: str = "split"):
     """Stage one alone.  Returns (workspace, C, n, m): the workspace now holds
     the chunk states (read them with unpack_states); C, n, m are the final
     state (None where not requested or not defined for the gate)."""
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(k, k, v, i_pre, f_pre)
-    desc = _desc_for(k, v, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv)
+    desc = _desc_for(k, v, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv,
+                     state_codes=state_codes)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_fw_states")
@@ -331,14 +339,16 @@ def mlstm_fw_states(k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_size
 
 def mlstm_fw_hintra(q, k, v, i_pre, f_pre, workspace, *, chunk_size: int, gate: str = "exp",
                     h_dtype=None, precision: str = "split", qk_scale: Optional[float] = None,
-                    eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, return_rows: bool = False):
+                    eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, return_rows: bool = False,
+                    state_codes: str = "split"):
     """Stage two alone: H (and, with return_rows, the per-row m and stabilised
     normaliser) from the chunk states that mlstm_fw_states left in workspace.
     The descriptor arguments must match the ones given to mlstm_fw_states."""
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
     h_dtype = torch.float32 if h_dtype is None else h_dtype
-    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv)
+    desc = _desc_for(q, v, chunk_size, gate, h_dtype, precision, qk_scale, eps, tile_lq, tile_lkv,
+                     state_codes=state_codes)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_fw_hintra")
@@ -360,13 +370,14 @@ def mlstm_fw_hintra(q, k, v, i_pre, f_pre, workspace, *, chunk_size: int, gate: 
 
 
 def unpack_states(q_like, v_like, workspace, *, chunk_size: int, gate: str = "exp",
-                  precision: str = "split", tile_lq: int = 0, tile_lkv: int = 0):
+                  precision: str = "split", tile_lq: int = 0, tile_lkv: int = 0, state_codes: str = "split"):
     """The chunk states in workspace as float32 tensors (C_states, n_states,
     m_states) of shapes (B, NH, N_c+1, DHQK, DHV), (B, NH, N_c+1, DHQK),
     (B, NH, N_c+1); entry c is the state entering chunk c.  q_like / v_like
     only supply the shapes and the input dtype."""
     torch = _torch()
-    desc = _desc_for(q_like, v_like, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv)
+    desc = _desc_for(q_like, v_like, chunk_size, gate, torch.float32, precision, None, 0.0, tile_lq, tile_lkv,
+                     state_codes=state_codes)
     st = validate(desc)
     if st:
         raise MlstmError(st, "mlstm_fw_unpack_states")

@@ -35,6 +35,15 @@ bool blocked_supported(const mlstm_fw_desc_t* d) {
   return d->precision != MLSTM_PREC_F64 && packed_layout(d) && mlstm::rows_tile_rows(d->DHQK, d->DHV) > 0;
 }
 
+// int16-coded chunk states: written by the row-tile states kernel in one
+// segment and read by the wide intra-chunk kernel, so the wide family with
+// split operands and a row-tile shape, on the two-stage schedule (the fused
+// walker hands no states over; the blocked schedule keeps the pair form).
+bool codes_supported(const mlstm_fw_desc_t* d) {
+  return d->precision == MLSTM_PREC_SPLIT && packed_layout(d) && mlstm::rows_tile_rows(d->DHQK, d->DHV) > 0 &&
+         d->schedule != MLSTM_SCHED_FUSED && d->schedule != MLSTM_SCHED_BLOCKED;
+}
+
 // Chunk states of one block of the blocked schedule, over all heads: half the
 // 256 MB Infinity Cache, so that a block's states, written by the states
 // kernel, are still there when the intra-chunk kernel reads them.
@@ -54,8 +63,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int validate_desc(const mlstm_fw_desc_t* d) {
   if (!d) return MLSTM_E_NULLPTR;
-  for (int i = 0; i < 2; ++i)
-    if (d->reserved[i] != 0) return MLSTM_E_ARG;
+  if (d->reserved != 0) return MLSTM_E_ARG;
+  if (d->state_codes != MLSTM_STATES_SPLIT && d->state_codes != MLSTM_STATES_I16) return MLSTM_E_ARG;
   if (d->block_chunks < 0) return MLSTM_E_ARG;
   if (d->schedule != MLSTM_SCHED_AUTO && d->schedule != MLSTM_SCHED_TWO_STAGE && d->schedule != MLSTM_SCHED_FUSED &&
       d->schedule != MLSTM_SCHED_BLOCKED)
@@ -87,6 +96,7 @@ int validate_desc(const mlstm_fw_desc_t* d) {
   if ((int64_t)d->S * (int64_t)(d->DHQK > d->DHV ? d->DHQK : d->DHV) >= (1LL << 29)) return MLSTM_E_SHAPE;
   if (d->schedule == MLSTM_SCHED_FUSED && !fused_supported(d)) return MLSTM_E_UNSUPPORTED;
   if (d->schedule == MLSTM_SCHED_BLOCKED && !blocked_supported(d)) return MLSTM_E_UNSUPPORTED;
+  if (d->state_codes == MLSTM_STATES_I16 && !codes_supported(d)) return MLSTM_E_UNSUPPORTED;
   return MLSTM_OK;
 }
 
@@ -100,7 +110,7 @@ bool use_fused(const mlstm_fw_desc_t* d) {
 }
 
 struct WsLayout {
-  size_t c_off, n_off, m_off, g_off, ml_off, cy_off, total;
+  size_t c_off, n_off, m_off, g_off, ml_off, cy_off, cs_off, total;
 };
 
 // Per-position gate terms: read by both wide-tile stages (the walker forms
@@ -115,9 +125,10 @@ WsLayout ws_layout(const mlstm_fw_desc_t* d) {
                              : (size_t)((d->S + d->chunk_size - 1) / d->chunk_size) + 1;
   const size_t el = d->precision == MLSTM_PREC_F64 ? sizeof(double) : sizeof(float);
   const bool states = d->schedule != MLSTM_SCHED_FUSED;  // chunk states can be formed
+  const bool codes = d->state_codes == MLSTM_STATES_I16;
   WsLayout w;
   w.c_off = 0;
-  size_t off = states ? round_up(BH * Nc1 * d->DHQK * d->DHV * el, 256) : 0;
+  size_t off = states ? round_up(BH * Nc1 * d->DHQK * d->DHV * (codes ? sizeof(int16_t) : el), 256) : 0;
   w.n_off = off;
   if (states && d->gate == MLSTM_GATE_EXP) off += round_up(BH * Nc1 * d->DHQK * el, 256);
   w.m_off = off;
@@ -133,6 +144,9 @@ WsLayout ws_layout(const mlstm_fw_desc_t* d) {
   if (blocked)
     off += 2 * (round_up(BH * d->DHQK * d->DHV * sizeof(float), 256) + round_up(BH * d->DHQK * sizeof(float), 256) +
                 round_up(BH * sizeof(float), 256));
+  // int16-coded states: one float32 scale per 16 x 32 fragment
+  w.cs_off = off;
+  if (states && codes) off += round_up(BH * Nc1 * (d->DHQK / 16) * (d->DHV / 32) * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -172,6 +186,7 @@ struct WsPtrs {
   float* cy_C[2];  // blocked schedule: the state between blocks, else null
   float* cy_n[2];
   float* cy_m[2];
+  float* C_scales;  // int16-coded states: fragment scales, else null (C then holds the codes)
 };
 
 WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
@@ -182,6 +197,9 @@ WsPtrs ws_ptrs(const mlstm_fw_desc_t* d, void* workspace) {
   r.n = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.n_off) : nullptr;
   r.m = d->gate == MLSTM_GATE_EXP ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
   r.gb2 = r.gu2 = r.gpm2 = r.m_local = nullptr;
+  r.C_scales = d->state_codes == MLSTM_STATES_I16 && d->schedule != MLSTM_SCHED_FUSED
+                   ? reinterpret_cast<float*>(ws + w.cs_off)
+                   : nullptr;
   const bool blocked = d->schedule == MLSTM_SCHED_BLOCKED;
   if (packed_layout(d) && d->schedule != MLSTM_SCHED_FUSED && !blocked)
     r.m_local = reinterpret_cast<float*>(ws + w.ml_off);
@@ -298,6 +316,7 @@ int run_states(const mlstm_fw_desc_t* d, const void* K, const void* V, const flo
   else if (packed_layout(d)) {
     p.C_plain = C_plain;
     p.plain_only = C_plain && plain_only;
+    p.C_scales = ws.C_scales;
     e = run_gates(d, i_pre, f_pre, ws, stream);
     if (e == hipSuccess) e = mlstm::launch_states_wide(p, sig, split, stream);
   }
@@ -342,6 +361,7 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
   p.dh_bf16 = dh_bf16;
   p.ginvz = ginvz;
   p.gdelta = gdelta;
+  p.C_scales = ws.C_scales;
   const bool bf16 = d->qkv_dtype == MLSTM_BF16;
   const bool sig = d->gate == MLSTM_GATE_SIG;
   const bool split = bf16 && d->precision == MLSTM_PREC_SPLIT;
@@ -447,7 +467,7 @@ int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, f
   }
   if (C_states) {
     if (packed_layout(d)) {
-      e = mlstm::launch_unpack_states(ws.C, C_states, n, d->DHQK, d->DHV, s);
+      e = mlstm::launch_unpack_states(ws.C, C_states, n, d->DHQK, d->DHV, s, ws.C_scales);
     } else {
       e = hipMemcpyAsync(C_states, ws.C, (size_t)n * d->DHQK * d->DHV * sizeof(float), hipMemcpyDeviceToDevice, s);
     }
@@ -468,6 +488,7 @@ int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, f
 // 64-row tiles.
 mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
   mlstm_fw_desc_t r = *d;
+  r.state_codes = MLSTM_STATES_SPLIT;  // the recompute keeps its states as hi + lo pairs
   r.schedule = MLSTM_SCHED_TWO_STAGE;
   r.h_dtype = MLSTM_F32;
   if (r.chunk_size < 64) r.chunk_size = 64;

@@ -53,9 +53,14 @@ struct Wide {
   static_assert(DK % 32 == 0, "DHQK must be a multiple of 32");
 };
 
-template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT, bool DELTA = false>
+// CODES: the chunk states arrive as int16 codes with one power-of-two scale
+// per fragment (HintraParams::C_scales); each lane turns its eight codes of a
+// fragment into the bf16 hi + lo pair of code * scale, which is exact (a
+// code has at most 15 significant bits), right before the products.
+template <int DK, int DV, int TQ, int TV, bool SIG, bool SPLIT, bool DELTA = false, bool CODES = false>
 __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) {
   static_assert(!DELTA || (!SIG && TV == DV), "the row terms of the gradient need whole rows (exp gate)");
+  static_assert(!CODES || (SPLIT && !DELTA), "int16-coded states feed the split forward");
   typedef Wide<DK, TV, TQ> W;
   constexpr int NVT = DV / TV;
   constexpr int NKS = DK / 32;  // 16x16x32 steps over DK
@@ -173,14 +178,23 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
   float gb_r = 0.0f, gpm_r = 0.0f, mprev = 0.0f;
   uint4 qpre[QPT];
   uint4 bb[NKK][W::CB][2];
+  // elements (bf16 words or int16 codes) per state
+  constexpr size_t kStateElems = (size_t)DK * DV * (CODES ? 1 : 2);
   auto state_ptr = [&](int bh_, int c_) {
-    return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * SL + c_ - c_lo) * DK * DV * 2;
+    return reinterpret_cast<const uint16_t*>(p.C_states) + ((size_t)bh_ * SL + c_ - c_lo) * kStateElems;
   };
   // Chunk-state fragments through a buffer resource: lane offset and the
   // wave's first 32-column block in one VGPR, the k step in a scalar offset
   // (a state is read whole, so every offset is in range), the column block
   // and plane as immediates.
   auto load_k = [&](__amdgpu_buffer_rsrc_t rs, int v0_, int kk) {
+    if constexpr (CODES) {
+      // fragment kk * (DV / 32) + nb at byte 1024 times that index
+      const int voff = lane * 16 + ((v0_ + wc0) >> 5) * 1024;
+#pragma unroll
+      for (int cb = 0; cb < W::CB; ++cb) bb[kk][cb][0] = buf_load16_whole(rs, voff + cb * 1024, kk * DV * 32);
+      return;
+    }
     const int voff = lane * 16 + ((v0_ + wc0) >> 5) * 2048;
 #pragma unroll
     for (int cb = 0; cb < W::CB; ++cb) {
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       if constexpr (SPLIT) bb[kk][cb][1] = buf_load16_whole(rs, voff + cb * 2048 + 1024, kk * DV * 64);
     }
   };
-  auto state_rsrc = [&](int bh_, int c_) { return make_rsrc(state_ptr(bh_, c_), (uint32_t)(DK * DV * 4)); };
+  auto state_rsrc = [&](int bh_, int c_) { return make_rsrc(state_ptr(bh_, c_), (uint32_t)(kStateElems * 2)); };
   auto request = [&](int t) {
     const int vt_ = t % NVT, qt_ = (t / NVT) % NQT;
     const int c_ = c_lo + (t / (NVT * NQT)) % NCB, bh_ = t / (NVT * NQT * NCB);
@@ -238,6 +252,16 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
 #pragma unroll
     for (int kk = 0; kk < PD && kk < NKK; ++kk) load_k(rst, v0, kk);
     __builtin_amdgcn_sched_barrier(0);
+    // scales of this wave's fragments (int16-coded states): wave-uniform
+    float scl[CODES ? NKK : 1][CODES ? W::CB : 1];
+    if constexpr (CODES) {
+      const int f0 = __builtin_amdgcn_readfirstlane(
+          (int)(((size_t)bh * SL + c - c_lo) * (DK / 16) * (DV / 32)) + ((v0 + wc0) >> 5));
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < W::CB; ++cb) scl[kk][cb] = p.C_scales[f0 + kk * (DV / 32) + cb];
+    }
 
     // ---- gate terms of this chunk (log2 units, written by the gates kernel):
     // u for the keys [0, kend); b and the running max of u for this tile's rows.
@@ -303,11 +327,23 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       }
 #pragma unroll
       for (int cb = 0; cb < W::CB; ++cb) {
-        const bf16x8_t bh_ = as_bf16x8(bb[kk][cb][0]);
+        uint4 ph = bb[kk][cb][0], pl;
+        if constexpr (!CODES && SPLIT) pl = bb[kk][cb][1];
+        if constexpr (CODES) {
+          const uint32_t cw[4] = {ph.x, ph.y, ph.z, ph.w};
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            split_bf16x2((float)((int)(cw[q] << 16) >> 16) * scl[kk][cb], (float)((int)cw[q] >> 16) * scl[kk][cb],
+                         hw[q], lw[q]);
+          ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        const bf16x8_t bh_ = as_bf16x8(ph);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bh_, acc[rb][cb]);
         if constexpr (SPLIT) {
-          const bf16x8_t bl_ = as_bf16x8(bb[kk][cb][1]);
+          const bf16x8_t bl_ = as_bf16x8(pl);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mma32b(qa[rb], bl_, acc[rb][cb]);
         }
@@ -633,6 +669,14 @@ hipError_t launch_t(const HintraParams& p0, hipStream_t stream) {
     }
   }
   if (p.dH) return hipErrorInvalidValue;  // the row terms need whole rows and the exp gate
+  if (p.C_scales) {
+    if constexpr (SPLIT) {
+      hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT, false, true>), grid, dim3(512), 0, stream,
+                         p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;  // int16-coded states feed the split forward only
+  }
   hipLaunchKernelGGL((hintra_wide_kernel<DK, DV, TQ, TV, SIG, SPLIT>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }

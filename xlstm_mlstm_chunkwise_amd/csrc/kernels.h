@@ -49,6 +49,11 @@ struct StatesParams {
   // m_out (row-tile states kernel, one segment).
   int c_lo = 0, c_hi = -1, slots = 0;
   int nt_states = 1;  // non-temporal stores of the packed chunk states
+  // Packed states as int16 codes (row-tile kernel, one segment) when set:
+  // C_states then holds one code per value in the packed fragment order,
+  // DK * DV int16 per state, and C_scales one power-of-two float32 scale per
+  // 16 x 32 fragment, (DK / 16) * (DV / 32) per state (value = code * scale).
+  float* C_scales = nullptr;
 };
 
 struct HintraParams {
@@ -75,6 +80,8 @@ struct HintraParams {
   // Chunk range and state slots as in StatesParams (wide kernel only).
   int c_lo = 0, c_hi = -1, slots = 0;
   int pair_tiles = 0;  // wide kernel: schedule row tiles p and NQT-1-p together
+  // int16-coded chunk states (wide kernel; layout as in StatesParams) when set
+  const float* C_scales = nullptr;
   // Backward recompute (wide kernel, exp gate, 64-row tiles): with dH set,
   // H is not stored; per row the kernel writes ginvz = 1 / (max(|den|, e^-m)
   // + eps) and gdelta = -(dh . h) ginvz sign(den) where |den| > e^-m, else 0.
@@ -203,7 +210,8 @@ bool hintra_wide_supported(int DK, int DV, int L, int tile_lq, bool bf16_inputs)
 hipError_t launch_hintra_wide(const HintraParams& p, bool sig, bool split, hipStream_t stream);
 
 // Wide-tile states kernel: writes the chunk states in the packed fragment
-// layout read by the wide intra-chunk kernel.
+// layout read by the wide intra-chunk kernel (as int16 codes when
+// p.C_scales is set: row-tile kernel only, one segment).
 hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipStream_t stream);
 // Row-tile states kernel over the chunk range of p, one segment (the blocked
 // forward schedule); rows_tile_rows(DK, DV) > 0 where it covers the shape.
@@ -217,8 +225,9 @@ hipError_t launch_hintra_f64(const HintraParams& p, bool bf16_inputs, bool sig, 
 hipError_t launch_narrow_f64(const void* src, float* dst, long long n, hipStream_t stream);
 bool hintra_f64m_supported(int DK);
 hipError_t launch_hintra_f64m(const HintraParams& p, bool bf16_inputs, bool sig, hipStream_t stream);
-// Packed states (n_states x DK x DV) -> float32.
+// Packed states (n_states x DK x DV) -> float32; scales non-null: the
+// states are int16 codes with one scale per fragment (StatesParams::C_scales).
 hipError_t launch_unpack_states(const void* packed, float* C, long long n_states, int DK, int DV,
-                                hipStream_t stream);
+                                hipStream_t stream, const float* scales = nullptr);
 
 }  // namespace mlstm

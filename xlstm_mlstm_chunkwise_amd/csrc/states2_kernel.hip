@@ -265,7 +265,10 @@ __global__ __launch_bounds__(256) void states_wide_kernel(const StatesParams p) 
 //     matrix cores reach it.
 // PLAIN: the states go out as float32 row-major (StatesParams::C_plain)
 // instead of packed, for a reader other than the intra-chunk kernel.
-template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false>
+// CODES: the packed states go out as int16 codes with one power-of-two scale
+// per 16 x 32 fragment (StatesParams::C_scales), half the bytes of the hi +
+// lo pair.
+template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false, bool CODES = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void states_rows_kernel(
     const StatesParams p) {
   constexpr int NT = 512, NW = 8, TB = 32;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (!SIG && p.m0) Mst2 = p.m0[bh] * kLog2e;
   if (!SIG && seg > 0) Mst2 = -INFINITY;
 
-  auto write_state = [&](int entry, float M2) {
+  auto write_state = [&](int entry, float M2) __attribute__((always_inline)) {
     if constexpr (PLAIN) {
       // float32 row-major copy: a half-wave stores 128 contiguous bytes of a row
       float* Pl = p.C_plain + ((size_t)bh * SL + entry - p.c_lo) * DK * DV;
@@ -345,10 +348,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             __builtin_nontemporal_store(acc[rb][cb][r], Pl + (size_t)krow * DV + wc0 + 32 * cb + l32);
           }
     }
-    uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV * 2;
     constexpr int NB = DV / 32;
+    if constexpr (CODES) {
+      // Fragment f = 2 kblk + half, nb holds exactly this wave's eight values
+      // per lane of one (rb, cb, half): its scale is the wave's maximum
+      // magnitude over 32767, rounded up to a power of two, so that every
+      // code (round half to even) fits in int16 and code * scale is the
+      // value to within half a scale step.
+      int16_t* P = reinterpret_cast<int16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV;
+      float* Sc = p.C_scales + ((size_t)bh * SL + entry - p.c_lo) * (DK / 16) * NB;
 #pragma unroll
-    for (int rb = 0; rb < 2 && !PLAIN; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
+          const int nb = (wc0 + 32 * cb) / 32;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(acc[rb][cb][8 * half + e]));
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+            int ex = 0;
+            if (amax > 0.0f) (void)frexpf(amax * (1.0f / 32767.0f), &ex);
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c0 = (int)fminf(fmaxf(rintf(ldexpf(acc[rb][cb][8 * half + 2 * q], -ex)), -32767.0f), 32767.0f);
+              const int c1 =
+                  (int)fminf(fmaxf(rintf(ldexpf(acc[rb][cb][8 * half + 2 * q + 1], -ex)), -32767.0f), 32767.0f);
+              w[q] = ((uint32_t)c0 & 0xffffu) | ((uint32_t)c1 << 16);
+            }
+            const int f = (2 * kblk + half) * NB + nb;
+            u32x4_t* d = reinterpret_cast<u32x4_t*>(P + (size_t)f * 512 + lane * 8);
+            if (p.nt_states) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, d);
+            else *d = u32x4_t{w[0], w[1], w[2], w[3]};
+            if (lane == 0) Sc[f] = ldexpf(1.0f, ex);
+          }
+        }
+    }
+    uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV * 2;
+#pragma unroll
+    for (int rb = 0; rb < 2 && !PLAIN && !CODES; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
@@ -750,10 +792,10 @@ __global__ __launch_bounds__(256) void states_fix_kernel(const StatesParams p) {
   if (!SIG && g == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = MT2 * kLn2;
 }
 
-template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false>
+template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false, bool CODES = false>
 hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.BH * (p.DK / TK) * p.nseg));
-  hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT, PLAIN>), grid, dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((states_rows_kernel<TK, TV, SIG, SPLIT, PLAIN, CODES>), grid, dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nseg <= 1) return e;
   const long long per = (long long)p.BH * (p.DK * p.DV / 8);
@@ -767,6 +809,11 @@ hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
 
 template <int TK, int TV>
 hipError_t launch_rows_any(const StatesParams& p, bool sig, bool split, hipStream_t stream) {
+  if (p.C_scales) {  // int16 codes: one segment, split operands
+    if (p.nseg != 1 || p.C_plain || !split) return hipErrorInvalidValue;
+    return sig ? launch_rows<TK, TV, true, true, false, true>(p, stream)
+               : launch_rows<TK, TV, false, true, false, true>(p, stream);
+  }
   if (p.C_plain)  // float32 states only: one segment, split operands
     return sig ? launch_rows<TK, TV, true, true, true>(p, stream) : launch_rows<TK, TV, false, true, true>(p, stream);
   if (sig) return split ? launch_rows<TK, TV, true, true>(p, stream) : launch_rows<TK, TV, true, false>(p, stream);
@@ -804,6 +851,16 @@ hipError_t launch_states_wide(const StatesParams& p, bool sig, bool split, hipSt
   // Whole-row tiles; with too few heads to fill the CUs the sequence is cut
   // into segments that run at once and are joined afterwards.
   const int rows_tk = rows_tile_rows(p.DK, p.DV);
+  if (p.C_scales) {
+    // int16 codes: the row-tile kernel in one segment (the joins work on the
+    // hi + lo form)
+    if (!rows_tk || p.C_plain) return hipErrorInvalidValue;
+    StatesParams q = p;
+    q.nseg = 1;
+    q.cps = p.Nc;
+    return rows_tk == 64 ? launch_rows_any<64, 512>(q, sig, split, stream)
+                         : launch_rows_any<128, 256>(q, sig, split, stream);
+  }
   if (rows_tk) {
     StatesParams q = p;
     const long long base = (long long)p.BH * (p.DK / rows_tk);
