@@ -131,8 +131,9 @@ typedef enum {
  *   MLSTM_STATES_SPLIT: each value as a bf16 hi + lo pair, 4 bytes, the
  *       split the intra-chunk kernel feeds to the matrix cores.  Default.
  *   MLSTM_STATES_I16:   int16 codes, 2 bytes a value, with one
- *       power-of-two float32 scale per 16 x 32 block of the state (its
- *       largest magnitude over 32767, rounded up; codes round half to even).
+ *       power-of-two float32 scale per 16 x 32 block of the state (between
+ *       its largest magnitude over 32767 and twice that; codes round half to
+ *       even).
  *       The intra-chunk kernel turns each code into the exact hi + lo pair
  *       of code * scale, so the only added error is the coding step, at most
  *       half a scale per value: max |dH| 3e-3 on the 7B-shaped exp workload

@@ -351,42 +351,53 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     constexpr int NB = DV / 32;
     if constexpr (CODES) {
       // Fragment f = 2 kblk + half, nb holds exactly this wave's eight values
-      // per lane of one (rb, cb, half): its scale is the wave's maximum
-      // magnitude over 32767, rounded up to a power of two, so that every
-      // code (round half to even) fits in int16 and code * scale is the
-      // value to within half a scale step.
+      // per lane of one (rb, cb, half): its scale is a power of two between
+      // its largest magnitude over 32767 and twice that, so that every code
+      // (round half to even) fits in int16 and code * scale is the value to
+      // within half a scale step.  The eight fragments' maxima go through
+      // the lane reduction side by side.
       int16_t* P = reinterpret_cast<int16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV;
       float* Sc = p.C_scales + ((size_t)bh * SL + entry - p.c_lo) * (DK / 16) * NB;
+      float amax[8];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int j = 0; j < 8; ++j) {
+        const int rb = j >> 2, cb = (j >> 1) & 1, half = j & 1;
+        float a = 0.0f;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
-          const int nb = (wc0 + 32 * cb) / 32;
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(acc[rb][cb][8 * half + e]));
+        amax[j] = a;
+      }
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            float amax = 0.0f;
+      for (int off = 32; off > 0; off >>= 1)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(acc[rb][cb][8 * half + e]));
+        for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], off, 64));
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-            int ex = 0;
-            if (amax > 0.0f) (void)frexpf(amax * (1.0f / 32767.0f), &ex);
-            uint32_t w[4];
+      for (int j = 0; j < 8; ++j) {
+        const int rb = j >> 2, cb = (j >> 1) & 1, half = j & 1;
+        const int kblk = (kt * TK + wr0 + 32 * rb) / 32;
+        const int nb = (wc0 + 32 * cb) / 32;
+        // scale 2^(e - 14) with e the exponent of amax (1 + 2^-15): then
+        // amax / scale < 2^15 / (1 + 2^-15), so every code rounds into
+        // [-32767, 32767]; both powers of two are built from their exponent
+        // fields.  Blocks below 2^-112 (zero or subnormal) take scale 1 and
+        // code 0.
+        const int E = (int)((__float_as_uint(amax[j] * 1.000030517578125f) >> 23) & 0xffu);
+        const bool tiny = E < 15;
+        const float inv = tiny ? 1.0f : __uint_as_float((uint32_t)(268 - E) << 23);
+        const float sc = tiny ? 1.0f : __uint_as_float((uint32_t)(E - 14) << 23);
+        uint32_t w[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int c0 = (int)fminf(fmaxf(rintf(ldexpf(acc[rb][cb][8 * half + 2 * q], -ex)), -32767.0f), 32767.0f);
-              const int c1 =
-                  (int)fminf(fmaxf(rintf(ldexpf(acc[rb][cb][8 * half + 2 * q + 1], -ex)), -32767.0f), 32767.0f);
-              w[q] = ((uint32_t)c0 & 0xffffu) | ((uint32_t)c1 << 16);
-            }
-            const int f = (2 * kblk + half) * NB + nb;
-            u32x4_t* d = reinterpret_cast<u32x4_t*>(P + (size_t)f * 512 + lane * 8);
-            if (p.nt_states) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, d);
-            else *d = u32x4_t{w[0], w[1], w[2], w[3]};
-            if (lane == 0) Sc[f] = ldexpf(1.0f, ex);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = (int)rintf(acc[rb][cb][8 * half + 2 * q] * inv);
+          const int c1 = (int)rintf(acc[rb][cb][8 * half + 2 * q + 1] * inv);
+          w[q] = ((uint32_t)c0 & 0xffffu) | ((uint32_t)c1 << 16);
         }
+        const int f = (2 * kblk + half) * NB + nb;
+        u32x4_t* d = reinterpret_cast<u32x4_t*>(P + (size_t)f * 512 + lane * 8);
+        if (p.nt_states) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, d);
+        else *d = u32x4_t{w[0], w[1], w[2], w[3]};
+        if (lane == 0) Sc[f] = sc;
+      }
     }
     uint16_t* P = reinterpret_cast<uint16_t*>(p.C_states) + ((size_t)bh * SL + entry - p.c_lo) * DK * DV * 2;
 #pragma unroll
