@@ -69,6 +69,9 @@ PAIRS = [
      dict(B=1, NH=2, S=200, DHQK=128, DHV=256, chunk=64), "two_stage"),
     ("two_stage_generic_f32", dict(qkv_dtype="f32", B=2, NH=2, S=400, DHQK=128, DHV=128, chunk=128),
      dict(qkv_dtype="f32", B=1, NH=1, S=90, DHQK=64, DHV=64, chunk=64, init_state=True), "two_stage"),
+    # int16-coded chunk states on the static array
+    ("two_stage_int16", dict(B=1, NH=4, S=600, DHQK=256, DHV=512, chunk=128, init_state=True),
+     dict(gate="sig", B=1, NH=2, S=200, DHQK=128, DHV=256, chunk=64), "two_stage:int16"),
 ]
 
 
@@ -94,6 +97,8 @@ def _check_against_oracle(w, x, o, tag):
 
 @pytest.mark.parametrize("name,first,second,schedule", PAIRS, ids=[p[0] for p in PAIRS])
 def test_noalloc_matches_workspace_entry_point(mt, name, first, second, schedule):
+    schedule, _, codes = schedule.partition(":")
+    codes = codes or "split"
     runs = []
     for over in (first, second):
         w = _workload(**over)
@@ -105,13 +110,15 @@ def test_noalloc_matches_workspace_entry_point(mt, name, first, second, schedule
               flush=True)
         mt.mlstm_chunkwise_fw_noalloc(d["q"], d["k"], d["v"], d["i"], d["f"], d.get("C0"), d.get("n0"),
                                       d.get("m0"), chunk_size=w.chunk, gate=w.gate, schedule=schedule,
-                                      out=o["H"], C_out=o["C"], n_out=o.get("n"), m_out=o.get("m"))
+                                      state_codes=codes, out=o["H"], C_out=o["C"], n_out=o.get("n"),
+                                      m_out=o.get("m"))
         torch.cuda.synchronize()
         assert torch.cuda.memory_allocated() == before
         runs.append((w, x, d, o, o_ref))
     for w, x, d, o, o_ref in runs:
         H, C, n, m = mt.mlstm_chunkwise_fw(d["q"], d["k"], d["v"], d["i"], d["f"], d.get("C0"), d.get("n0"),
-                                           d.get("m0"), chunk_size=w.chunk, gate=w.gate, schedule=schedule)
+                                           d.get("m0"), chunk_size=w.chunk, gate=w.gate, schedule=schedule,
+                                           state_codes=codes)
         torch.cuda.synchronize()
         assert torch.equal(o["H"], H), f"{name}: H differs from the workspace entry point"
         assert torch.equal(o["C"], C)
