@@ -73,10 +73,10 @@ struct Vec16 {
 };
 
 // ---------------------------------------------------------------------------
-// Stage one: a 64 x 64 tile of C per workgroup, walking the chunks of its head.
-// Wave w owns state rows 16 w .. 16 w + 15 of the tile and its four 16-column
-// blocks (accumulator register r of block cb: row 16 w + 4 r + l / 16,
-// column 16 cb + l % 16).  Per chunk the gated keys (K w, fp64) and the values
+// Stage one: a 64 x TVC tile of C per workgroup (TVC = 64 or 32), walking the
+// chunks of its head.  Wave w owns state rows 16 w .. 16 w + 15 of the tile
+// and its TVC / 16 column blocks (accumulator register r of block cb: row
+// 16 w + 4 r + l / 16, column 16 cb + l % 16).  Per chunk the gated keys (K w, fp64) and the values
 // are staged transposed, 32 steps at a time, and C += (K w)^T V runs on the
 // matrix cores.
 
@@ -115,8 +115,11 @@ __device__ __forceinline__ void widen8<float>(const uint4 (&u)[2], double (&x)[8
   }
 }
 
-template <typename TIn, bool SIG>
+// TVC: columns of the C tile (64, or 32 to give heads with few tiles twice
+// the workgroups: two per CU instead of one).
+template <typename TIn, bool SIG, int TVC>
 __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) {
+  constexpr int NCB = TVC / 16;  // 16-column blocks of a wave
   __shared__ double s_w[kMaxL];
   __shared__ double s_tot[4];  // wave totals of the block scans
   __shared__ double s_g;
@@ -135,28 +138,32 @@ __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) 
   double* ns = reinterpret_cast<double*>(p.n_states);
   double* ms = reinterpret_cast<double*>(p.m_states);
   auto krow = [&](int r) { return kt * 64 + 16 * w + 4 * r + g; };
-  auto vcol = [&](int cb) { return vt * 64 + 16 * cb + l16; };
+  auto vcol = [&](int cb) { return vt * TVC + 16 * cb + l16; };
 
   const int st_t = tid & 31, st_c = 8 * (tid >> 5);  // this thread's staging step and columns
+  const bool st_v = st_c < TVC;  // this thread also stages values
   StageRegs<TIn> cur;
   auto load_block = [&](int t0, int Lc, int tb, StageRegs<TIn>& sr) {
     // steps past the chunk read row t0 (in bounds) and are zeroed after
     const bool ok = tb + st_t < Lc;
     const size_t row = (size_t)t0 + (ok ? tb + st_t : 0);
     const uint4* kp = reinterpret_cast<const uint4*>(K + row * DK + kt * 64 + st_c);
-    const uint4* vp = reinterpret_cast<const uint4*>(V + row * DV + vt * 64 + st_c);
+    const uint4* vp = reinterpret_cast<const uint4*>(V + row * DV + vt * TVC + (st_v ? st_c : 0));
     const uint32_t keep = ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int i = 0; i < StageRegs<TIn>::NV; ++i) {
-      const uint4 a = kp[i], b = vp[i];
+      const uint4 a = kp[i];
       sr.k[i] = make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
-      sr.v[i] = make_uint4(b.x & keep, b.y & keep, b.z & keep, b.w & keep);
+      if (st_v) {
+        const uint4 b = vp[i];
+        sr.v[i] = make_uint4(b.x & keep, b.y & keep, b.z & keep, b.w & keep);
+      }
     }
   };
 
-  double4_t acc[4];
+  double4_t acc[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       acc[cb][r] = p.C0 ? (double)p.C0[(size_t)bh * DK * DV + (size_t)krow(r) * DV + vcol(cb)] : 0.0;
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) 
     // the state entering chunk c (c == Nc: the final state)
     double* Cst = Cs + ((size_t)bh * (Nc + 1) + c) * DK * DV;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) Cst[(size_t)krow(r) * DV + vcol(cb)] = acc[cb][r];
     if (own_n && tid < 64) ns[((size_t)bh * (Nc + 1) + c) * DK + kt * 64 + tid] = nreg;
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) 
     }
     __syncthreads();
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[cb] *= decay;
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] *= decay;
     nreg *= decay;
 
     for (int tb = 0; tb < Lc; tb += kSTB) {
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           s_kwt[(st_c + e) * kSLD + st_t] = kx[e] * wt;
-          s_vt[(st_c + e) * kSLD + st_t] = vx[e];
+          if (st_v) s_vt[(st_c + e) * kSLD + st_t] = vx[e];
         }
       }
       if (tb + kSTB < Lc) load_block(t0, Lc, tb + kSTB, cur);
@@ -247,21 +254,21 @@ __global__ __launch_bounds__(256) void states_f64m_kernel(const StatesParams p) 
 #pragma unroll
       for (int s0 = 0; s0 < kSTB; s0 += 16) {
         const double4_t ka = *reinterpret_cast<const double4_t*>(s_kwt + (16 * w + l16) * kSLD + s0 + 4 * g);
-        double4_t vb[4];
+        double4_t vb[NCB];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
           vb[cb] = *reinterpret_cast<const double4_t*>(s_vt + (16 * cb + l16) * kSLD + s0 + 4 * g);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[cb] = mma_f64(ka[s], vb[cb][s], acc[cb]);
+          for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma_f64(ka[s], vb[cb][s], acc[cb]);
       }
       __syncthreads();
     }
   }
   if (p.C_out)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         p.C_out[(size_t)bh * DK * DV + (size_t)krow(r) * DV + vcol(cb)] = (float)acc[cb][r];
@@ -540,8 +547,16 @@ __global__ __launch_bounds__(256) void hintra_f64m_kernel(const HintraParams p) 
 
 template <typename TIn, bool SIG>
 hipError_t launch_states_t(const StatesParams& p, hipStream_t stream) {
-  dim3 grid(p.BH, p.DK / 64, p.DV / 64);
-  hipLaunchKernelGGL((states_f64m_kernel<TIn, SIG>), grid, dim3(256), 0, stream, p);
+  // 32-column tiles when 64-column ones leave fewer than two workgroups per CU
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if ((long long)p.BH * (p.DK / 64) * (p.DV / 64) < 2LL * cus) {
+    dim3 grid(p.BH, p.DK / 64, p.DV / 32);
+    hipLaunchKernelGGL((states_f64m_kernel<TIn, SIG, 32>), grid, dim3(256), 0, stream, p);
+  } else {
+    dim3 grid(p.BH, p.DK / 64, p.DV / 64);
+    hipLaunchKernelGGL((states_f64m_kernel<TIn, SIG, 64>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
