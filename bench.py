@@ -517,7 +517,10 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     torch.cuda.synchronize()
     t_rec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, w.chunk)
+    # the backward cuts the sequence into chunks of min(max(chunk, 64), 256)
+    # rows (mlstm_chunkwise_bw): its algorithmic FLOPs are those of that cut
+    bw_chunk = min(max(w.chunk, 64), 256)
+    flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, bw_chunk)
     ach = flops / (t_grads * 1e-3) / 1e12
     # bf16 inputs: bf16 matrix cores (computed operands as hi + lo pairs);
     # float32 inputs: fp32 matrix cores.  Each is priced at its own peak.
@@ -538,8 +541,8 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "dtype": grads_dtype + " (gradient kernels); recompute " + path_dtype(mt, desc, args.precision),
         "data": "synthetic",
         "config": {"workload": f"backward_{w.name}", "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK,
-                   "DHV": w.DHV, "chunk": w.chunk, "gate": w.gate, "qkv_dtype": w.qkv_dtype, "dH": "float32",
-                   "precision": args.precision},
+                   "DHV": w.DHV, "chunk": w.chunk, "backward_chunk": bw_chunk, "gate": w.gate,
+                   "qkv_dtype": w.qkv_dtype, "dH": "float32", "precision": args.precision},
         "stages_ms": {"recompute": t_rec, "grads": t_grads},
         "grads_TFLOPs": ach,
         "roofline": {"kernel": "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,

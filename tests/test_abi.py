@@ -338,6 +338,11 @@ def test_backward_workspace_formula():
         *rest,
         BH * Nc * 10 * 64 * 64 * 4])
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dg)) == expect
+    # the backward cuts the sequence into chunks of at most 256 rows whatever
+    # the forward's chunk: its workspace is that of chunk 256
+    for L in (512, 1024):
+        dl = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=L, tile_lq=128, tile_lkv=128)
+        assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dl)) == lib.mlstm_bw_workspace_bytes(ctypes.byref(d))
 
 
 def test_q8_step_refuses_before_launch():

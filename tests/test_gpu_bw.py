@@ -165,8 +165,8 @@ def test_backward_full_size_sampled_heads(mt, wname):
     position, all 32 chunk boundaries of the reverse state-gradient
     recurrence, and the initial-state gradients).  At 65536 tokens the
     quadratic form of a whole head does not fit in host memory, so the
-    oracle checks the last 8 chunks (8192 positions, seven chunk boundaries
-    inside the span): their gradients are those of the tail problem that
+    oracle checks the last 8192 positions (the backward cuts them into 32
+    chunks of 256): their gradients are those of the tail problem that
     starts from the exact state at the cut (every later query and key sits
     in the tail; the prefix enters only through that state), which the
     float64 chunkwise oracle supplies."""
