@@ -517,9 +517,10 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     torch.cuda.synchronize()
     t_rec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    # the backward cuts the sequence into chunks of min(max(chunk, 64), 256)
-    # rows (mlstm_chunkwise_bw): its algorithmic FLOPs are those of that cut
-    bw_chunk = min(max(w.chunk, 64), 256)
+    # the backward cuts the sequence into chunks of min(max(chunk, 64), Lmax)
+    # rows, Lmax = 128 when B NH DHQK / 64 >= 256, else 256
+    # (mlstm_chunkwise_bw): its algorithmic FLOPs are those of that cut
+    bw_chunk = min(max(w.chunk, 64), 128 if w.B * w.NH * (w.DHQK // 64) >= 256 else 256)
     flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, bw_chunk)
     ach = flops / (t_grads * 1e-3) / 1e12
     # bf16 inputs: bf16 matrix cores (computed operands as hi + lo pairs);

@@ -421,8 +421,11 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc);
  * states nor per-row normalisers); desc->precision applies to that
  * recomputation.  The gradient does not depend on how the sequence is cut
  * into chunks, so the backward picks its own: chunks of
- * min(max(chunk_size, 64), 256) rows (at 65536 tokens and chunk 1024, chunks
- * of 256 take 13.0 ms against 16.9 ms; the results agree to rounding).  The gradient kernels accumulate in float32: with bf16
+ * min(max(chunk_size, 64), Lmax) rows, Lmax = 128 when B * NH * DHQK / 64 is
+ * at least 256 (the chip's CU count) and 256 otherwise; the results agree
+ * with those of any other cut to rounding.  (At 65536 tokens, 8 heads and
+ * chunk 1024 the cut at 256 takes 13.0 ms against 16.9 ms; at the 7B-shaped
+ * 64 heads the cut at 128 takes 6.9 ms against 7.4 ms at 256.)  The gradient kernels accumulate in float32: with bf16
  * inputs on bf16 matrix cores (Q, K, V raw, every computed operand as a bf16
  * hi + lo pair), with float32 inputs on fp32 matrix cores.  No gradient
  * flows in through the final state.  For the sig gate n0,

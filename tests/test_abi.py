@@ -310,10 +310,12 @@ def test_backward_workspace_formula():
     shapes), the state gradients after each chunk, the initial-state
     gradients and (bf16 inputs) the weighted dS tiles that the dk pass hands
     to the dq pass, each region rounded up to 256 bytes.  The generic shapes
-    (here DHQK 64) keep H."""
-    d = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
+    (here DHQK 64) keep H.  (The 7B-shaped heads fill the CUs, so the
+    backward cuts them into chunks of 128: two 64-row tiles, three tile
+    pairs per chunk.)"""
+    d = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=128)
     lib = mt.lib()
-    BH, S, DK, DV, Nc = 64, 8192, 256, 512, 32
+    BH, S, DK, DV, Nc = 64, 8192, 256, 512, 64
     r = lambda x: (x + 255) // 256 * 256
     fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(d)))
     rest = [BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                     # b, src, 1/z, delta
@@ -324,10 +326,11 @@ def test_backward_workspace_formula():
         BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,   # states
         0, BH * S * 4, BH * S * 4,                                               # (no H), m, den
         *rest,
-        BH * Nc * 10 * 64 * 64 * 4])                  # weighted dS of the 10 tile pairs per chunk
+        BH * Nc * 3 * 64 * 64 * 4])                   # weighted dS of the 3 tile pairs per chunk
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
-    # generic kernels (DHQK 64): H in float32 as well
-    DK = 64
+    # generic kernels (DHQK 64, one row tile per head: chunks of 256 stay):
+    # H in float32 as well
+    DK, Nc = 64, 32
     dg = _desc(B=8, NH=8, S=8192, DHQK=DK, DHV=512, chunk_size=256)
     fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(dg)))
     rest[4:6] = [BH * Nc * DK * DV * 4, BH * Nc * DK * 4]
@@ -338,11 +341,15 @@ def test_backward_workspace_formula():
         *rest,
         BH * Nc * 10 * 64 * 64 * 4])
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dg)) == expect
-    # the backward cuts the sequence into chunks of at most 256 rows whatever
-    # the forward's chunk: its workspace is that of chunk 256
-    for L in (512, 1024):
+    # the backward picks its own cut: chunks of at most 128 rows when the
+    # heads fill the CUs (64 heads x 4 row tiles here), else 256
+    for L in (256, 512, 1024):
         dl = _desc(B=8, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=L, tile_lq=128, tile_lkv=128)
         assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dl)) == lib.mlstm_bw_workspace_bytes(ctypes.byref(d))
+    few = _desc(B=1, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=256)
+    for L in (512, 1024):
+        dl = _desc(B=1, NH=8, S=8192, DHQK=256, DHV=512, chunk_size=L, tile_lq=128, tile_lkv=128)
+        assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dl)) == lib.mlstm_bw_workspace_bytes(ctypes.byref(few))
 
 
 def test_q8_step_refuses_before_launch():

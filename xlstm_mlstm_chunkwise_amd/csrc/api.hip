@@ -485,10 +485,16 @@ int unpack_states(const mlstm_fw_desc_t* d, const WsPtrs& ws, float* C_states, f
 // H in float32.
 // The gradient does not depend on how the sequence is cut into chunks, so
 // the backward picks its own: chunks below 64 rows run as chunks of 64 (the
-// gradient kernels work in 64-row tiles), chunks above 256 rows as chunks of
-// 256 (the intra-chunk gradient tiles grow with the chunk length; at 65536
-// tokens chunks of 256 take 13.0 ms against 16.9 ms at 1024).
-constexpr int kBwMaxChunk = 256;
+// gradient kernels work in 64-row tiles), longer ones as chunks of at most
+// 256 rows, or 128 when the heads alone give the row-tile state-gradient
+// kernel a workgroup per CU (BH * DHQK / 64 >= 256 CUs).  The intra-chunk
+// gradient tiles grow with the chunk length, the sequential state-gradient
+// recurrence with the number of chunks: at 65536 tokens and 8 heads chunks of
+// 256 take 13.0 ms (16.9 at 1024, 13.8 at 128); at 8192 tokens and 64 heads
+// chunks of 128 take 6.9 ms (7.4 at 256, 7.8 at 64).
+int bw_max_chunk(const mlstm_fw_desc_t* d) {
+  return (int64_t)d->B * d->NH * (d->DHQK / 64) >= 256 ? 128 : 256;
+}
 
 mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
   mlstm_fw_desc_t r = *d;
@@ -496,7 +502,7 @@ mlstm_fw_desc_t bw_fw_desc(const mlstm_fw_desc_t* d) {
   r.schedule = MLSTM_SCHED_TWO_STAGE;
   r.h_dtype = MLSTM_F32;
   if (r.chunk_size < 64) r.chunk_size = 64;
-  if (r.chunk_size > kBwMaxChunk) r.chunk_size = kBwMaxChunk;
+  if (r.chunk_size > bw_max_chunk(d)) r.chunk_size = bw_max_chunk(d);
   // the library's own tiles (64-row intra-chunk tiles hold whole rows, which
   // the row terms of the gradient need); the result does not depend on them
   r.tile_lq = r.tile_lkv = 0;
