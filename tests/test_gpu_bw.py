@@ -106,6 +106,11 @@ CASES = [
     # chunks below 64 rows: the backward runs on chunks of 64
     ("exp_bf16_d128x128_L16_init", 1, 2, 150, 128, 128, 16, "bf16", "exp", True),
     ("sig_f32_d64x64_L32", 1, 1, 100, 64, 64, 32, "f32", "sig", False),
+    # long chunks: the backward cuts them into chunks of 256 (few heads) or
+    # 128 (B NH DHQK / 64 >= 256: the heads fill the CUs)
+    ("exp_bf16_d256x512_L1024_init", 1, 1, 1500, 256, 512, 1024, "bf16", "exp", True),
+    ("sig_bf16_d256x256_L512_manyheads", 16, 4, 150, 256, 256, 512, "bf16", "sig", True),
+    ("exp_bf16_d256x512_L256_manyheads", 8, 8, 140, 256, 512, 256, "bf16", "exp", False),
 ]
 
 
