@@ -329,7 +329,9 @@ def test_backward_workspace_formula():
         BH * Nc * 3 * 64 * 64 * 4])                   # weighted dS of the 3 tile pairs per chunk
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(d)) == expect
     # generic kernels (DHQK 64, one row tile per head: chunks of 256 stay):
-    # H in float32 as well
+    # H in float32 as well.  64 row tiles fill a quarter of the 256 CUs, so
+    # the state-gradient recurrence runs as 4 sequence segments of 8 chunks,
+    # each leaving its own gradient (and normaliser gradient) for the joins.
     DK, Nc = 64, 32
     dg = _desc(B=8, NH=8, S=8192, DHQK=DK, DHV=512, chunk_size=256)
     fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(dg)))
@@ -339,7 +341,8 @@ def test_backward_workspace_formula():
         BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,
         BH * S * DV * 4, BH * S * 4, BH * S * 4,                                 # H, m, den
         *rest,
-        BH * Nc * 10 * 64 * 64 * 4])
+        BH * Nc * 10 * 64 * 64 * 4,
+        BH * 4 * DK * DV * 4, BH * 4 * DK * 4])                                  # segments
     assert lib.mlstm_bw_workspace_bytes(ctypes.byref(dg)) == expect
     # the backward picks its own cut: chunks of at most 128 rows when the
     # heads fill the CUs (64 heads x 4 row tiles here), else 256

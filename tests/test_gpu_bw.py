@@ -138,6 +138,12 @@ ROW_TILE_CASES = [
     ("sig_d128x512_bf16dh_L64", 1, 2, 200, 128, 512, 64, "sig", False, True),
     ("sig_d256x256_f32dh_L64_init", 1, 1, 333, 256, 256, 64, "sig", True, False),
     ("sig_d128x256_bf16dh_L64_ragged", 2, 1, 150, 128, 256, 64, "sig", True, True),
+    # fewer row tiles than CUs: the recurrence runs as sequence segments that
+    # start from zero and are joined afterwards.  32 heads x 4 tiles, 7
+    # chunks: 2 segments of 4 and 3 chunks; 32 heads x 2 tiles, 10 chunks:
+    # 4 segments of 3, 3, 3 and 1 chunks
+    ("exp_d256x512_bf16dh_L64_segments", 4, 8, 414, 256, 512, 64, "exp", True, True),
+    ("sig_d256x256_f32dh_L64_segments", 2, 16, 593, 256, 256, 64, "sig", True, False),
 ]
 
 

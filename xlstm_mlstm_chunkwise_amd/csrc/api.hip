@@ -517,7 +517,8 @@ bool bw_delta_in_recompute(const mlstm_fw_desc_t* d2) {
 }
 
 struct BwLayout {
-  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, dS, total;
+  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, dS, seg, segn, total;
+  int nseg, cps;  // sequence segments of the state-gradient recurrence
 };
 
 // Forward workspace first, then the backward's own regions, each 256-byte aligned.
@@ -551,6 +552,9 @@ BwLayout bw_layout(const mlstm_fw_desc_t* d2) {
   l.dn0 = take(ex ? BH * DK * f : 0);
   const size_t nT = (size_t)d2->chunk_size / 64;
   l.dS = take(d2->qkv_dtype == MLSTM_BF16 ? BH * Nc * (nT * (nT + 1) / 2) * 64 * 64 * f : 0);
+  l.nseg = mlstm::bw_dstate_segments((int)BH, (int)DK, (int)DV, (int)Nc, d2->qkv_dtype == MLSTM_BF16, &l.cps);
+  l.seg = take(l.nseg > 1 ? BH * l.nseg * DK * DV * f : 0);
+  l.segn = take(l.nseg > 1 && ex ? BH * l.nseg * DK * f : 0);
   l.total = off;
   return l;
 }
@@ -940,6 +944,10 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.qdq = at(l.qdq);
   p.kdk = at(l.kdk);
   p.dS_tiles = desc->qkv_dtype == MLSTM_BF16 ? at(l.dS) : nullptr;
+  p.nseg = l.nseg;
+  p.cps = l.cps;
+  p.seg_C = l.nseg > 1 ? at(l.seg) : nullptr;
+  p.seg_n = l.nseg > 1 && ex ? at(l.segn) : nullptr;
   p.dQ = dQ;
   p.dK = dK;
   p.dV = dV;

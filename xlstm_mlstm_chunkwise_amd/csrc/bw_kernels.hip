@@ -717,13 +717,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int NTK = p.DK / TK;
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
-  // the row tiles of one head on one XCD: they read the same dH rows
+  // the row tiles of one head (and segment) on one XCD: they read the same
+  // dH rows
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int kt = bid % NTK;
-  const int bh = bid / NTK;
+  const int seg = (bid / NTK) % p.nseg;
+  const int bh = bid / (NTK * p.nseg);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
   const int S = p.S, DK = p.DK, L = p.L, Nc = p.Nc;
+  // chunks [c_beg, c_end) of this segment, walked from the last; a segment
+  // other than the last starts from a zero state gradient and the join
+  // kernels add what enters it from the later segments
+  const int c_beg = p.nseg > 1 ? seg * p.cps : 0;
+  const int c_end = p.nseg > 1 ? min(Nc, c_beg + p.cps) : Nc;
   constexpr int DV = TV;
   const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;
   const size_t gbase = (size_t)bh * S;
@@ -747,10 +754,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       make_rsrc(static_cast<const char*>(p.dH) + gbase * DV * (DHB ? 2 : 4), (uint32_t)((size_t)S * DV * (DHB ? 2 : 4)));
   const int qvoff = (krs * DK + kcs) * 2;
 
-  // block gi: chunk Nc - 1 - gi / BPC, rows [tb, tb + TB) of it; blocks past
-  // the end of a short last chunk read zeros and carry weight zero
+  // block gi: chunk c_end - 1 - gi / BPC, rows [tb, tb + TB) of it; blocks
+  // past the end of a short last chunk read zeros and carry weight zero
   const int BPC = L / TB;
-  const int NBLK = Nc * BPC;
+  const int NBLK = (c_end - c_beg) * BPC;
 
   QVec qr[2];
   uint4 dr[2][VPT];
@@ -758,7 +765,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   float glr[2], Mcr[2], Mnr[2];         // chunk scalars (first block of a chunk)
   auto load_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    const int c = c_end - 1 - gi / BPC, tb = (gi % BPC) * TB;
     const int t0 = c * L, Lc = min(L, S - t0);
     const int trow = t0 + tb;
     const int qo = qvoff + trow * DK * 2;
@@ -829,7 +836,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   auto stage_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    const int c = c_end - 1 - gi / BPC, tb = (gi % BPC) * TB;
     if (tb == 0) {
       if (!SIG && gi > 0) flush_n();
       if constexpr (SIG) {
@@ -923,7 +930,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   };
   auto mma_blk = [&](auto set, int gi) {
     constexpr int s = decltype(set)::value;
-    const int c = Nc - 1 - gi / BPC, tb = (gi % BPC) * TB;
+    const int c = c_end - 1 - gi / BPC, tb = (gi % BPC) * TB;
     if (tb == 0) {
       write_g(c);
 #pragma unroll
@@ -954,14 +961,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   auto iter = [&](auto par, int gi) {
     constexpr int P = decltype(par)::value;
     constexpr int Qs = 1 - P;
-    if (n_pend) finish_n(p.dn_states + ((size_t)bh * Nc + (Nc - 1 - gi / BPC)) * DK);
+    if (n_pend) finish_n(p.dn_states + ((size_t)bh * Nc + (c_end - 1 - gi / BPC)) * DK);
     mma_blk(std::integral_constant<int, P>{}, gi);
     if (gi + 1 < NBLK) stage_blk(std::integral_constant<int, Qs>{}, gi + 1);
     if (gi + 3 < NBLK) load_blk(std::integral_constant<int, Qs>{}, gi + 3);
     __syncthreads();
   };
 
-  if (!SIG && tid < TK) p.dn_states[((size_t)bh * Nc + Nc - 1) * DK + kt * TK + tid] = 0.0f;
+  if (!SIG && tid < TK) p.dn_states[((size_t)bh * Nc + c_end - 1) * DK + kt * TK + tid] = 0.0f;
   load_blk(std::integral_constant<int, 0>{}, 0);
   if (NBLK > 1) load_blk(std::integral_constant<int, 1>{}, 1);
   stage_blk(std::integral_constant<int, 0>{}, 0);
@@ -970,6 +977,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   for (int gi = 0; gi < NBLK; gi += 2) {
     iter(std::integral_constant<int, 0>{}, gi);
     if (gi + 1 < NBLK) iter(std::integral_constant<int, 1>{}, gi + 1);
+  }
+  if (p.nseg > 1) {
+    // the segment's own state gradient at its first chunk, for the joins:
+    // fragment-lane order (8 values a lane per 16 x 32 fragment)
+    if constexpr (!SIG) {
+      flush_n();
+      __syncthreads();
+      finish_n(p.seg_n + ((size_t)bh * p.nseg + seg) * DK);
+    }
+    float* sc = p.seg_C + ((size_t)bh * p.nseg + seg) * DK * DV;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (wc0 + 32 * cb) / 32;
+          float4* d = reinterpret_cast<float4*>(sc + ((size_t)(kk * (DV / 32) + nb) * 64 + lane) * 8);
+          d[0] = make_float4(acc[rb][cb][8 * half], acc[rb][cb][8 * half + 1], acc[rb][cb][8 * half + 2],
+                             acc[rb][cb][8 * half + 3]);
+          d[1] = make_float4(acc[rb][cb][8 * half + 4], acc[rb][cb][8 * half + 5], acc[rb][cb][8 * half + 6],
+                             acc[rb][cb][8 * half + 7]);
+        }
+    return;
   }
   if constexpr (!SIG) {
     flush_n();
@@ -987,6 +1018,106 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           const int vcol = wc0 + 32 * cb + l32;
           p.dC0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] = acc[rb][cb][r];
         }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Joins of the segmented state-gradient recurrence.  With the decay of chunk
+// c, d_c = e^{M_c + g_c - M_{c+1}} (sig gate: e^{g_c}), the recurrence
+// A_c = d_c A_{c+1} + U_c (A_Nc = 0; slot c holds A_{c+1}) splits over
+// segments [c0, c1): A_c = A^loc_c + (d_c ... d_{c1-1}) A_{c1}, where A^loc
+// is the segment's own run from zero.  The carry kernel walks the segments
+// from the last, writes the true A_{c1} into each segment's top slot c1 - 1
+// (whose own value is zero) and the initial-state gradients; the fix kernel
+// then adds the decayed A_{c1} to every other slot of the segment.  Values
+// are handled in pieces of one fragment lane: 8 values of the packed layout.
+
+// decay of chunk c of head bh
+template <bool SIG>
+__device__ __forceinline__ float chunk_decay(const BwParams& p, int bh, int c) {
+  const float g = p.gb[(size_t)bh * p.S + min((c + 1) * p.L, p.S) - 1];
+  if constexpr (SIG) return expf(g);
+  const float* M = p.m_states + (size_t)bh * (p.Nc + 1);
+  return expf(M[c] + g - M[c + 1]);
+}
+
+// piece g (fragment g / 64, lane g % 64) of slot c of the packed gradients
+__device__ __forceinline__ void g_piece_load(const BwParams& p, int bh, int c, int g, float (&x)[8]) {
+  const uint16_t* P = p.G_packed + ((size_t)bh * p.Nc + c) * p.DK * p.DV * 2 + (size_t)(g >> 6) * 1024 + (g & 63) * 8;
+  const uint4 h = *reinterpret_cast<const uint4*>(P), l = *reinterpret_cast<const uint4*>(P + 512);
+  const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    x[e] = __uint_as_float(e & 1 ? hw[e >> 1] & 0xffff0000u : hw[e >> 1] << 16) +
+           __uint_as_float(e & 1 ? lw[e >> 1] & 0xffff0000u : lw[e >> 1] << 16);
+}
+__device__ __forceinline__ void g_piece_store(const BwParams& p, int bh, int c, int g, const float (&x)[8]) {
+  uint16_t* P = p.G_packed + ((size_t)bh * p.Nc + c) * p.DK * p.DV * 2 + (size_t)(g >> 6) * 1024 + (g & 63) * 8;
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_bf16x2(x[2 * q], x[2 * q + 1], hw[q], lw[q]);
+  *reinterpret_cast<uint4*>(P) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  *reinterpret_cast<uint4*>(P + 512) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_dstate_carry_kernel(const BwParams p) {
+  const int per = p.DK * p.DV / 8;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)p.BH * per) return;
+  const int bh = (int)(gid / per), g = (int)(gid % per);
+  const int Nc = p.Nc, DK = p.DK, DV = p.DV;
+  const bool own_n = !SIG && g < DK;  // normaliser entry g
+  float A[8], An = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) A[e] = 0.0f;
+  for (int s = p.nseg - 1; s >= 0; --s) {
+    const int c0 = s * p.cps, c1 = min(Nc, c0 + p.cps);
+    if (s < p.nseg - 1) {
+      g_piece_store(p, bh, c1 - 1, g, A);
+      if (own_n) p.dn_states[((size_t)bh * Nc + c1 - 1) * DK + g] = An;
+    }
+    float P = 1.0f;
+    for (int c = c0; c < c1; ++c) P *= chunk_decay<SIG>(p, bh, c);
+    const float* sc = p.seg_C + ((size_t)bh * p.nseg + s) * DK * DV + (size_t)g * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) A[e] = sc[e] + P * A[e];
+    if (own_n) An = p.seg_n[((size_t)bh * p.nseg + s) * DK + g] + P * An;
+  }
+  if (p.dC0) {
+    const int f = g >> 6, ln = g & 63, kk = f / (DV / 32), nb = f % (DV / 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * kk + (e < 4 ? 0 : 8) + 4 * (ln >> 5) + (e & 3);
+      p.dC0[((size_t)bh * DK + k) * DV + 32 * nb + (ln & 31)] = A[e];
+    }
+  }
+  if (own_n && p.dn0) p.dn0[(size_t)bh * DK + g] = An;
+}
+
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_dstate_fix_kernel(const BwParams p) {
+  const int per = p.DK * p.DV / 8;
+  const long long interior = (long long)(p.nseg - 1) * (p.cps - 1);  // slots below each segment's top
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)p.BH * interior * per) return;
+  const int g = (int)(gid % per);
+  const long long rest = gid / per;
+  const int slot = (int)(rest % interior), bh = (int)(rest / interior);
+  const int s = slot / (p.cps - 1);
+  const int c1 = (s + 1) * p.cps;                // segments before the last are whole
+  const int c = s * p.cps + slot % (p.cps - 1);  // c <= c1 - 2
+  float F = 1.0f;
+  for (int k = c + 1; k < c1; ++k) F *= chunk_decay<SIG>(p, bh, k);
+  float top[8], x[8];
+  g_piece_load(p, bh, c1 - 1, g, top);
+  g_piece_load(p, bh, c, g, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] += F * top[e];
+  g_piece_store(p, bh, c, g, x);
+  if (!SIG && g < p.DK) {
+    float* dn = p.dn_states + (size_t)bh * p.Nc * p.DK;
+    dn[(size_t)c * p.DK + g] += F * dn[(size_t)(c1 - 1) * p.DK + g];
   }
 }
 
@@ -1447,7 +1578,8 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   hipLaunchKernelGGL((bw_prep_kernel<SIG>), dim3((unsigned)(p.BH * p.Nc)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gs((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT));
-  const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK / (p.DV == 512 ? 64 : 128));
+  if (!rows_kernel || !p.seg_C || (!SIG && !p.seg_n) || p.cps < 1) p.nseg = 1;
+  const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK / (p.DV == 512 ? 64 : 128)) * (unsigned)p.nseg;
   if (p.qkv_bf16 && p.DV == 512 && p.dh_bf16)
     hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 32, SIG, true>), dim3(rows), dim3(512), 0, s, p);
   else if (p.qkv_bf16 && p.DV == 512)
@@ -1459,6 +1591,16 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   else if (p.qkv_bf16) hipLaunchKernelGGL((bw_dstate16_kernel<SIG>), gs, dim3(256), 0, s, p);
   else hipLaunchKernelGGL((bw_dstate_kernel<SIG>), gs, dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.nseg > 1) {
+    const long long per = (long long)p.BH * (p.DK * p.DV / 8);
+    hipLaunchKernelGGL((bw_dstate_carry_kernel<SIG>), dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.cps >= 2) {
+      const long long nfix = per * (p.nseg - 1) * (p.cps - 1);
+      hipLaunchKernelGGL((bw_dstate_fix_kernel<SIG>), dim3((unsigned)((nfix + 255) / 256)), dim3(256), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
   // dk first: with bf16 inputs it leaves the weighted dS tiles that dq reads
   if ((e = launch_tiles<kModeDK, SIG>(p, p.DK, s)) != hipSuccess) return e;
   if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
@@ -1469,6 +1611,21 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
 }
 
 }  // namespace
+
+int bw_dstate_segments(int BH, int DK, int DV, int Nc, bool bf16_inputs, int* cps) {
+  // the row-tile recurrence: one workgroup per head and TK key rows; with
+  // fewer than one per CU (256 CUs) the sequence is cut into segments
+  const bool rows = bf16_inputs && (DV == 512 || (DV == 256 && DK % 128 == 0));
+  const long long base = (long long)BH * (DK / (DV == 512 ? 64 : 128));
+  if (!rows || base >= 256 || Nc < 2) {
+    if (cps) *cps = Nc;
+    return 1;
+  }
+  const long long want = (256 + base - 1) / base;
+  const int c = (int)((Nc + want - 1) / want);
+  if (cps) *cps = c;
+  return (Nc + c - 1) / c;
+}
 
 hipError_t launch_bw(const BwParams& p, bool sig, hipStream_t stream) {
   if (p.DK % kT || p.DV % kT || p.L % kT || p.DK > 512 || p.DV > 512 || p.L > 1024) return hipErrorInvalidValue;

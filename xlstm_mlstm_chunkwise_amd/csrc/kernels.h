@@ -185,6 +185,14 @@ struct BwParams {
   float eps;
   int BH, S, DK, DV, L, Nc;
   int qkv_bf16, dh_bf16;
+  // Sequence segments of the row-tile state-gradient recurrence
+  // (bw_dstate_segments): segment s walks chunks [s cps, (s + 1) cps) from
+  // zero and leaves its state gradient at the segment's first chunk in
+  // seg_C ((BH, nseg, DK * DV) float32, packed fragment-lane order) and
+  // seg_n ((BH, nseg, DK), exp gate); the join kernels make them true.
+  int nseg = 1, cps = 0;
+  float* seg_C = nullptr;
+  float* seg_n = nullptr;
 };
 
 // Each returns hipSuccess or the launch error.
@@ -201,6 +209,10 @@ hipError_t launch_q8_encode(const float* C, int8_t* Cq, float* Cs, long long BH,
 hipError_t launch_q8_decode(const int8_t* Cq, const float* Cs, float* C, long long BH, int DK, int DV,
                             hipStream_t stream);
 hipError_t launch_bw(const BwParams& p, bool sig, hipStream_t stream);
+// Segments of the backward's row-tile state-gradient recurrence for a shape
+// (1 when its heads alone fill the CUs, or when another kernel runs it);
+// *cps receives the chunks per segment.
+int bw_dstate_segments(int BH, int DK, int DV, int Nc, bool bf16_inputs, int* cps);
 hipError_t launch_states(const StatesParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 hipError_t launch_hintra(const HintraParams& p, bool bf16_inputs, bool sig, bool split, hipStream_t stream);
 
