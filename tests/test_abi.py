@@ -321,6 +321,7 @@ def test_backward_workspace_formula():
     rest = [BH * S * 4, BH * S * 4, BH * S * 4, BH * S * 4,                     # b, src, 1/z, delta
             BH * Nc * DK * DV * 4, BH * Nc * DK * 4,                            # state gradients
             BH * S * 4, BH * S * 4,                                             # q.dq, k.dk
+            BH * (S // 1024 + 32) * 4,                                          # gate sums, dm0 partial sums
             BH * DK * DV * 4, BH * DK * 4]                                      # dC0, dn0
     expect = fw + sum(r(x) for x in [
         BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,   # states
@@ -336,7 +337,7 @@ def test_backward_workspace_formula():
     dg = _desc(B=8, NH=8, S=8192, DHQK=DK, DHV=512, chunk_size=256)
     fw = r(lib.mlstm_fw_workspace_bytes(ctypes.byref(dg)))
     rest[4:6] = [BH * Nc * DK * DV * 4, BH * Nc * DK * 4]
-    rest[8:10] = [BH * DK * DV * 4, BH * DK * 4]
+    rest[9:11] = [BH * DK * DV * 4, BH * DK * 4]
     expect = fw + sum(r(x) for x in [
         BH * (Nc + 1) * DK * DV * 4, BH * (Nc + 1) * DK * 4, BH * (Nc + 1) * 4,
         BH * S * DV * 4, BH * S * 4, BH * S * 4,                                 # H, m, den

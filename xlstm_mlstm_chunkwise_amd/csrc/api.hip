@@ -517,7 +517,7 @@ bool bw_delta_in_recompute(const mlstm_fw_desc_t* d2) {
 }
 
 struct BwLayout {
-  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, dC0, dn0, dS, seg, segn, total;
+  size_t Cst, nst, mst, H, mrows, den, gb, gsrc, ginvz, gdelta, dC, dn, qdq, kdk, gtot, dC0, dn0, dS, seg, segn, total;
   int nseg, cps;  // sequence segments of the state-gradient recurrence
 };
 
@@ -548,6 +548,7 @@ BwLayout bw_layout(const mlstm_fw_desc_t* d2) {
   l.dn = take(ex ? BH * Nc * DK * f : 0);
   l.qdq = take(BH * S * f);
   l.kdk = take(BH * S * f);
+  l.gtot = take(BH * ((S + 1023) / 1024 + 32) * f);
   l.dC0 = take(BH * DK * DV * f);
   l.dn0 = take(ex ? BH * DK * f : 0);
   const size_t nT = (size_t)d2->chunk_size / 64;
@@ -943,6 +944,7 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.dn_states = ex ? at(l.dn) : nullptr;
   p.qdq = at(l.qdq);
   p.kdk = at(l.kdk);
+  p.gate_tot = at(l.gtot);
   p.dS_tiles = desc->qkv_dtype == MLSTM_BF16 ? at(l.dS) : nullptr;
   p.nseg = l.nseg;
   p.cps = l.cps;

@@ -1095,29 +1095,31 @@ __global__ __launch_bounds__(256) void bw_dstate_carry_kernel(const BwParams p) 
   if (own_n && p.dn0) p.dn0[(size_t)bh * DK + g] = An;
 }
 
+// One thread per (head, segment before the last, piece): the segment's top
+// slot is read once, and the decay product grows as the walk goes down.
 template <bool SIG>
 __global__ __launch_bounds__(256) void bw_dstate_fix_kernel(const BwParams p) {
   const int per = p.DK * p.DV / 8;
-  const long long interior = (long long)(p.nseg - 1) * (p.cps - 1);  // slots below each segment's top
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (long long)p.BH * interior * per) return;
+  if (gid >= (long long)p.BH * (p.nseg - 1) * per) return;
   const int g = (int)(gid % per);
   const long long rest = gid / per;
-  const int slot = (int)(rest % interior), bh = (int)(rest / interior);
-  const int s = slot / (p.cps - 1);
-  const int c1 = (s + 1) * p.cps;                // segments before the last are whole
-  const int c = s * p.cps + slot % (p.cps - 1);  // c <= c1 - 2
-  float F = 1.0f;
-  for (int k = c + 1; k < c1; ++k) F *= chunk_decay<SIG>(p, bh, k);
-  float top[8], x[8];
+  const int s = (int)(rest % (p.nseg - 1)), bh = (int)(rest / (p.nseg - 1));
+  const int c0 = s * p.cps, c1 = c0 + p.cps;  // segments before the last are whole
+  float top[8];
   g_piece_load(p, bh, c1 - 1, g, top);
-  g_piece_load(p, bh, c, g, x);
+  const bool own_n = !SIG && g < p.DK;
+  float* dn = own_n ? p.dn_states + (size_t)bh * p.Nc * p.DK + g : nullptr;
+  const float topn = own_n ? dn[(size_t)(c1 - 1) * p.DK] : 0.0f;
+  float F = 1.0f;
+  for (int c = c1 - 2; c >= c0; --c) {
+    F *= chunk_decay<SIG>(p, bh, c + 1);
+    float x[8];
+    g_piece_load(p, bh, c, g, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] += F * top[e];
-  g_piece_store(p, bh, c, g, x);
-  if (!SIG && g < p.DK) {
-    float* dn = p.dn_states + (size_t)bh * p.Nc * p.DK;
-    dn[(size_t)c * p.DK + g] += F * dn[(size_t)(c1 - 1) * p.DK + g];
+    for (int e = 0; e < 8; ++e) x[e] += F * top[e];
+    g_piece_store(p, bh, c, g, x);
+    if (own_n) dn[(size_t)c * p.DK] += F * topn;
   }
 }
 
@@ -1490,49 +1492,72 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate gradients: one workgroup per head runs the reverse scan of
-// q.dq - k.dk over the sequence in blocks of 1024 positions; dm0.
-template <bool SIG>
-__global__ __launch_bounds__(256) void bw_gates_kernel(const BwParams p) {
-  __shared__ float s_tot[4];
-  __shared__ float s_all;
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const size_t rb = (size_t)bh * p.S;
-  float carry = 0.0f;
-  for (int blk = (p.S + 1023) / 1024 - 1; blk >= 0; --blk) {
-    float v[4];
-    int pos[4];
+// Gate gradients: the reverse (suffix) sum of q.dq - k.dk over the sequence,
+// in blocks of 1024 positions: first every block's total, then each block's
+// own scan plus the totals of the blocks after it; dm0.
+constexpr int kGateBlk = 1024;
+constexpr int kDm0Slices = 32;  // partial sums of dC0 . C0 per head
+
+// Workgroups y < nblk: the total of block y; y >= nblk (exp gate, dm0
+// asked): slice y - nblk of sum(dC0 * C0), beside the block totals.
+__global__ __launch_bounds__(256) void bw_gate_totals_kernel(const BwParams p, int nblk) {
+  __shared__ float s_w[4];
+  const int blk = blockIdx.y, bh = blockIdx.x, tid = threadIdx.x;
+  float a = 0.0f;
+  if (blk < nblk) {
+    const size_t rb = (size_t)bh * p.S;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pos[e] = blk * 1024 + 1023 - (4 * tid + e);
-      v[e] = pos[e] < p.S ? p.qdq[rb + pos[e]] - p.kdk[rb + pos[e]] : 0.0f;
+      const int pos = blk * kGateBlk + 4 * tid + e;
+      if (pos < p.S) a += p.qdq[rb + pos] - p.kdk[rb + pos];
     }
-    block_scan4<false, 4>(v, s_tot);
-    if (tid == 255) s_all = v[3];
-    __syncthreads();
-    const float tot = s_all;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (pos[e] < p.S) {
-        const size_t r = rb + pos[e];
-        p.d_f[r] = sigmoid_neg(p.f_pre[r]) * (v[e] + carry);
-        const float kd = p.kdk[r];
-        p.d_i[r] = SIG ? kd * sigmoid_neg(p.i_pre[r]) : kd;
-      }
-    }
-    carry += tot;
-    __syncthreads();
+  } else if (p.C0) {
+    // C0 and dC0 may be the caller's, 4-byte aligned only: float loads
+    const size_t n = (size_t)p.DK * p.DV, len = n / kDm0Slices;  // DK DV is a multiple of 64 * 64
+    const float* dc = p.dC0 + (size_t)bh * n + (blk - nblk) * len;
+    const float* c0 = p.C0 + (size_t)bh * n + (blk - nblk) * len;
+#pragma unroll 4
+    for (size_t i = tid; i < len; i += 256) a += dc[i] * c0[i];
   }
-  if constexpr (!SIG) {
-    if (p.dm0) {
-      float a = 0.0f;
-      const size_t n = (size_t)p.DK * p.DV;
-      if (p.C0)
-        for (size_t i = tid; i < n; i += 256) a += p.dC0[(size_t)bh * n + i] * p.C0[(size_t)bh * n + i];
+  a = block_reduce<false, 4>(a, s_w);
+  if (tid == 0) p.gate_tot[(size_t)bh * (nblk + kDm0Slices) + blk] = a;
+}
+
+template <bool SIG>
+__global__ __launch_bounds__(256) void bw_gates_kernel(const BwParams p, int nblk) {
+  __shared__ float s_tot[4];
+  const int blk = blockIdx.y, bh = blockIdx.x, tid = threadIdx.x;
+  const float* tot = p.gate_tot + (size_t)bh * (nblk + kDm0Slices);
+  if (blk == nblk) {
+    // dm0: the initial stabiliser enters through C0 and n0 scaled by e^{m0}
+    if constexpr (!SIG) {
+      float a = p.C0 && tid < kDm0Slices ? tot[nblk + tid] : 0.0f;
       if (p.n0)
         for (int i = tid; i < p.DK; i += 256) a += p.dn0[(size_t)bh * p.DK + i] * p.n0[(size_t)bh * p.DK + i];
       a = block_reduce<false, 4>(a, s_tot);
       if (tid == 0) p.dm0[bh] = a;
+    }
+    return;
+  }
+  const size_t rb = (size_t)bh * p.S;
+  float carry = 0.0f;  // the blocks after this one
+  for (int b = blk + 1 + tid; b < nblk; b += 256) carry += tot[b];
+  carry = block_reduce<false, 4>(carry, s_tot);
+  float v[4];
+  int pos[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pos[e] = blk * kGateBlk + kGateBlk - 1 - (4 * tid + e);
+    v[e] = pos[e] < p.S ? p.qdq[rb + pos[e]] - p.kdk[rb + pos[e]] : 0.0f;
+  }
+  block_scan4<false, 4>(v, s_tot);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (pos[e] < p.S) {
+      const size_t r = rb + pos[e];
+      p.d_f[r] = sigmoid_neg(p.f_pre[r]) * (v[e] + carry);
+      const float kd = p.kdk[r];
+      p.d_i[r] = SIG ? kd * sigmoid_neg(p.i_pre[r]) : kd;
     }
   }
 }
@@ -1596,7 +1621,7 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
     hipLaunchKernelGGL((bw_dstate_carry_kernel<SIG>), dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.cps >= 2) {
-      const long long nfix = per * (p.nseg - 1) * (p.cps - 1);
+      const long long nfix = per * (p.nseg - 1);
       hipLaunchKernelGGL((bw_dstate_fix_kernel<SIG>), dim3((unsigned)((nfix + 255) / 256)), dim3(256), 0, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1606,7 +1631,13 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   if ((e = launch_tiles<kModeDQ, SIG>(p, p.DK, s)) != hipSuccess) return e;
   const int Wv = p.DV % 256 == 0 ? 256 : p.DV % 128 == 0 ? 128 : 64;
   if ((e = launch_tiles<kModeDV, SIG>(p, Wv, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bw_gates_kernel<SIG>), dim3((unsigned)p.BH), dim3(256), 0, s, p);
+  const int nblk = (p.S + kGateBlk - 1) / kGateBlk;
+  const bool dm0 = !SIG && p.dm0;
+  hipLaunchKernelGGL(bw_gate_totals_kernel, dim3((unsigned)p.BH, (unsigned)(nblk + (dm0 ? kDm0Slices : 0))),
+                     dim3(256), 0, s, p, nblk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned gy = (unsigned)nblk + (dm0 ? 1u : 0u);
+  hipLaunchKernelGGL((bw_gates_kernel<SIG>), dim3((unsigned)p.BH, gy), dim3(256), 0, s, p, nblk);
   return hipGetLastError();
 }
 

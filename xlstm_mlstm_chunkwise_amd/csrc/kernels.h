@@ -171,6 +171,8 @@ struct BwParams {
   float* dn_states;      // (BH, Nc, DK) scratch (exp)
   float* qdq;            // (BH, S) scratch
   float* kdk;            // (BH, S) scratch
+  float* gate_tot;       // (BH, ceil(S / 1024) + 32) scratch: sums of q.dq - k.dk over blocks of
+                         // positions, then 32 partial sums of dC0 . C0
   float* dS_tiles;       // (BH, Nc, L/64 (L/64 + 1) / 2, 64, 64) scratch: weighted dS of every
                          // (query tile, key tile <= it) pair, written by the dk pass, read by dq
   float* dQ;             // (BH, S, DK) float32
