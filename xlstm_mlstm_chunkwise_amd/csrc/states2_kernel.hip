@@ -754,53 +754,56 @@ __global__ __launch_bounds__(256) void states_carry_kernel(const StatesParams p)
   if (!SIG && g == 0 && p.m_out) p.m_out[bh] = ME2 * kLn2;
 }
 
-// Interior chunk states of every segment s >= 1, all at once, from the true
-// state at the segment start (fixed by states_carry_kernel).
+// Interior chunk states of every segment s >= 1 from the true state at the
+// segment start (fixed by states_carry_kernel): one thread per (head,
+// segment, 8 packed values), which reads the start once and walks up the
+// segment's entries with the running gate sum.
 template <bool SIG>
 __global__ __launch_bounds__(256) void states_fix_kernel(const StatesParams p) {
   const int per = p.DK * p.DV / 8;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long ninterior = (long long)(p.nseg - 1) * (p.cps - 1);
-  if (gid >= (long long)p.BH * per * ninterior) return;
+  if (gid >= (long long)p.BH * per * (p.nseg - 1)) return;
   const int g = (int)(gid % per);
   const long long rest = gid / per;
-  const int slot = (int)(rest % ninterior);
-  const int bh = (int)(rest / ninterior);
-  const int s = 1 + slot / (p.cps - 1);
-  const int c0 = s * p.cps;
-  const int entry = c0 + 1 + slot % (p.cps - 1);  // interior entries c0+1 .. c1-1
+  const int s = 1 + (int)(rest % (p.nseg - 1));
+  const int bh = (int)(rest / (p.nseg - 1));
   const int Nc = p.Nc;
-  const int c1 = min(Nc, c0 + p.cps);
-  if (entry >= c1) return;
+  const int c0 = s * p.cps, c1 = min(Nc, c0 + p.cps);
   JoinView v;
   v.stride = (size_t)p.DK * p.DV * 2;
   v.st = reinterpret_cast<uint16_t*>(p.C_states) + (size_t)bh * (Nc + 1) * v.stride;
   v.nst = SIG ? nullptr : p.n_states + (size_t)bh * (Nc + 1) * p.DK;
   v.hi = (size_t)(g >> 6) * 1024 + (g & 63) * 8;
-  const float G2 = gate_sum2(p, bh, c0, entry);
-  float a = 1.0f, b, MT2 = 0.0f;
-  if constexpr (SIG) {
-    b = exp2f(G2);
-  } else {
-    // the true stabiliser at the segment start (entry c0 ends the previous
-    // segment; segment 0 or states_carry_kernel wrote its true value)
-    const float MEt2 = p.m_states[(size_t)bh * (Nc + 1) + c0] * kLog2e;
-    const float ML2 = p.m_local[(size_t)bh * (Nc + 1) + entry];
-    MT2 = fmaxf(ML2, MEt2 + G2);
-    a = exp2f(ML2 - MT2);
-    b = exp2f(MEt2 + G2 - MT2);
-  }
-  float E[8], Lv[8];
+  const bool own_n = !SIG && g < p.DK;
+  float E[8];
   join_load(v, c0, E);
-  join_load(v, entry, Lv);
+  const float En = own_n ? v.nst[(size_t)c0 * p.DK + g] : 0.0f;
+  // the true stabiliser at the segment start (entry c0 ends the previous
+  // segment; segment 0 or states_carry_kernel wrote its true value)
+  const float MEt2 = SIG ? 0.0f : p.m_states[(size_t)bh * (Nc + 1) + c0] * kLog2e;
+  float G2 = 0.0f;  // summed log2 forget gates of chunks [c0, entry)
+  for (int entry = c0 + 1; entry < c1; ++entry) {
+    G2 += p.gb2[(size_t)bh * p.S + min(entry * p.L, p.S) - 1];
+    float a = 1.0f, b, MT2 = 0.0f;
+    if constexpr (SIG) {
+      b = exp2f(G2);
+    } else {
+      const float ML2 = p.m_local[(size_t)bh * (Nc + 1) + entry];
+      MT2 = fmaxf(ML2, MEt2 + G2);
+      a = exp2f(ML2 - MT2);
+      b = exp2f(MEt2 + G2 - MT2);
+    }
+    float Lv[8];
+    join_load(v, entry, Lv);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) Lv[e] = Lv[e] * a + E[e] * b;
-  join_store(v, entry, Lv);
-  if (!SIG && g < p.DK) {
-    const float En = v.nst[(size_t)c0 * p.DK + g];
-    p.n_states[((size_t)bh * (Nc + 1) + entry) * p.DK + g] = v.nst[(size_t)entry * p.DK + g] * a + En * b;
+    for (int e = 0; e < 8; ++e) Lv[e] = Lv[e] * a + E[e] * b;
+    join_store(v, entry, Lv);
+    if (own_n) {
+      float* n = p.n_states + ((size_t)bh * (Nc + 1) + entry) * p.DK + g;
+      *n = *n * a + En * b;
+    }
+    if (!SIG && g == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = MT2 * kLn2;
   }
-  if (!SIG && g == 0) p.m_states[(size_t)bh * (Nc + 1) + entry] = MT2 * kLn2;
 }
 
 template <int TK, int TV, bool SIG, bool SPLIT, bool PLAIN = false, bool CODES = false>
@@ -813,7 +816,7 @@ hipError_t launch_rows(const StatesParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((states_carry_kernel<SIG>), dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.cps < 2) return e;
-  const long long nfix = per * (p.nseg - 1) * (p.cps - 1);
+  const long long nfix = per * (p.nseg - 1);
   hipLaunchKernelGGL((states_fix_kernel<SIG>), dim3((unsigned)((nfix + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
