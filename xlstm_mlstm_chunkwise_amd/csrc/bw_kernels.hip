@@ -1195,11 +1195,19 @@ __device__ __forceinline__ void put_packed(uint16_t* hi, uint16_t* lo, const flo
 }
 
 template <int MODE, bool SIG, int NY>
-__global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
+__device__ __forceinline__ void tiles16_body(const BwParams& p) {
   constexpr int W = 16 * NY;
-  __shared__ __align__(16) uint16_t s_x[2][kT * kLd16];  // partner tile [o][x] (hi, lo)
-  __shared__ __align__(16) uint16_t s_w[2][kT * kLd16];  // own tile [w][x] (hi, lo)
-  __shared__ __align__(16) uint16_t s_y[2][kT * kLd16];  // output-side operand (hi, lo)
+  // LDS planes of 64 x kLd16 bf16, only those the mode uses (a lo plane
+  // where the operand is split), so that three workgroups fit a CU:
+  // partner tile [o][x] (dk: hi, lo; dv: hi; dq reads the dS tiles instead),
+  // own tile [w][x] (dq: hi, lo; else hi), output-side operand (hi, lo)
+  constexpr int kPl = kT * kLd16;
+  constexpr int NXP = MODE == kModeDQ ? 0 : MODE == kModeDK ? 2 : 1;
+  constexpr int NWP = MODE == kModeDQ ? 2 : 1;
+  __shared__ __align__(16) uint16_t s_buf[(NXP + NWP + 2) * kPl];
+  uint16_t* const s_x[2] = {s_buf, s_buf + (NXP > 1 ? kPl : 0)};
+  uint16_t* const s_w[2] = {s_buf + NXP * kPl, s_buf + (NXP + NWP - 1) * kPl};
+  uint16_t* const s_y[2] = {s_buf + (NXP + NWP) * kPl, s_buf + (NXP + NWP + 1) * kPl};
   __shared__ RowGates g_own, g_oth;
 
   const int nT = p.L / kT;
@@ -1491,6 +1499,18 @@ __global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
   }
 }
 
+// Two workgroups per CU by registers; the dq and dv passes also come in a
+// variant held to three (dq fits without spills, dv spills a few registers
+// in its epilogue; dk would spill its accumulators).
+template <int MODE, bool SIG, int NY>
+__global__ __launch_bounds__(256) void bw_tiles16_kernel(const BwParams p) {
+  tiles16_body<MODE, SIG, NY>(p);
+}
+template <int MODE, bool SIG, int NY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bw_tiles16_w3_kernel(const BwParams p) {
+  tiles16_body<MODE, SIG, NY>(p);
+}
+
 // ---------------------------------------------------------------------------
 // Gate gradients: the reverse (suffix) sum of q.dq - k.dk over the sequence,
 // in blocks of 1024 positions: first every block's total, then each block's
@@ -1575,8 +1595,9 @@ hipError_t zero(float* x, long long n, hipStream_t s) {
 
 template <int MODE, bool SIG, int NY>
 void launch_tiles_ny(const BwParams& p, dim3 grid, hipStream_t s) {
-  if (p.qkv_bf16) hipLaunchKernelGGL((bw_tiles16_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
+  if (!p.qkv_bf16) hipLaunchKernelGGL((bw_tiles_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
+  else if constexpr (MODE != kModeDK) hipLaunchKernelGGL((bw_tiles16_w3_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((bw_tiles16_kernel<MODE, SIG, NY>), grid, dim3(256), 0, s, p);
 }
 
 template <int MODE, bool SIG>
