@@ -1156,8 +1156,8 @@ __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo, const float
 }
 
 // A 64 x 64 tile of a packed chunk state (16-row steps kk0 .. kk0 + 3,
-// 32-column blocks nb0, nb0 + 1; layout in device_common.h) as [k][v] bf16 hi
-// and lo planes.  Thread t owns fragment lanes t and t + 256: its four
+// 32-column blocks nb0, nb0 + 1; layout in device_common.h), as bf16 hi and
+// lo planes for put_packed_vk.  Thread t owns fragment lanes t and t + 256: its four
 // 16-byte pieces (hi, lo of each) travel in x's registers.  The planes are
 // the split of the float32 state already (hi + lo is exact in float32).
 __device__ __forceinline__ void pre_packed(float (&x)[16], const uint16_t* P, int DV, int kk0, int nb0) {
@@ -1176,21 +1176,35 @@ __device__ __forceinline__ void pre_packed(float (&x)[16], const uint16_t* P, in
   }
 }
 
-__device__ __forceinline__ void put_packed(uint16_t* hi, uint16_t* lo, const float (&x)[16]) {
+// The tile of pre_packed as [v][k] hi and lo planes: each fragment lane's
+// 8 values are two runs of 4 consecutive k at one v, one 8-byte store each.
+__device__ __forceinline__ void put_packed_vk(uint16_t* hi, uint16_t* lo, const float (&x)[16]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int idx = threadIdx.x + 256 * j, f = idx >> 6, lane = idx & 63;
-    const int v = 32 * (f & 1) + (lane & 31);
+    const int v = 32 * (f & 1) + (lane & 31), k = 16 * (f >> 1) + 4 * (lane >> 5);
 #pragma unroll
     for (int plane = 0; plane < 2; ++plane) {
-      uint16_t* dst = plane ? lo : hi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = __float_as_uint(x[8 * j + 4 * plane + (e >> 1)]);
-        const int k = 16 * (f >> 1) + (e < 4 ? 0 : 8) + 4 * (lane >> 5) + (e & 3);
-        dst[k * kLd16 + v] = (uint16_t)(e & 1 ? w >> 16 : w & 0xffff);
-      }
+      uint16_t* dst = (plane ? lo : hi) + v * kLd16 + k;
+      const float* w = x + 8 * j + 4 * plane;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(__float_as_uint(w[0]), __float_as_uint(w[1]));
+      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(__float_as_uint(w[2]), __float_as_uint(w[3]));
     }
+  }
+}
+
+// The values of pre16 (row r = thread / 4, columns 16 (thread % 4) + i)
+// transposed, dst[c * kLd16 + r], as bf16 hi + lo.
+__device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo, const float (&x)[16]) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t hw, lw;
+    split_bf16x2(x[i], x[i + 1], hw, lw);
+    hi[(c + i) * kLd16 + r] = (uint16_t)(hw & 0xffff);
+    hi[(c + i + 1) * kLd16 + r] = (uint16_t)(hw >> 16);
+    lo[(c + i) * kLd16 + r] = (uint16_t)(lw & 0xffff);
+    lo[(c + i + 1) * kLd16 + r] = (uint16_t)(lw >> 16);
   }
 }
 
@@ -1259,8 +1273,9 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
     if (run) {
       constexpr int NYC = W / kT;
       const int nxc = own_D / kT;
-      // state tile of (x chunk, y chunk): [k][v] for every mode (dv reads it transposed)
-      // packed states (dq: C; dk, dv: G), rows k, columns v
+      // state tile of (x chunk, y chunk), held in LDS as [v][k] in every
+      // mode: dq and dk (rows y = k) read it transposed, dv (rows y = v)
+      // directly; packed states (dq: C; dk, dv: G)
       const uint16_t* Pk = nullptr;
       if constexpr (MODE == kModeDQ) {
         if (p.C_packed) Pk = p.C_packed + ((size_t)bh * (Nc + 1) + c) * DK * DV * 2;
@@ -1286,8 +1301,8 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
         for (int yc = 0; yc < NYC; ++yc) {
         __syncthreads();
         if (yc == 0) put_rows(s_w[0], own_split ? s_w[1] : nullptr, pw, own_split && !SIG ? g_own.invz : nullptr);
-        if (Pk) put_packed(s_y[0], s_y[1], py);
-        else put_rows(s_y[0], s_y[1], py, nullptr);
+        if (Pk) put_packed_vk(s_y[0], s_y[1], py);
+        else put_cols(s_y[0], s_y[1], py);
         __syncthreads();
         if (yc + 1 < NYC) {
           pre_state(py, xi, yc + 1);
@@ -1303,9 +1318,9 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
           if constexpr (own_split) bl_ = frag16(s_w[1], w, k0);
 #pragma unroll
           for (int yb = 0; yb < 4; ++yb) {
-            // dv: the state tile is [k][v] in LDS (row stores); read transposed
-            const bf16x8_t ah = MODE == kModeDV ? frag16_tr(s_y[0], k0, 4, 16 * yb) : frag16(s_y[0], 16 * yb + l16, k0);
-            const bf16x8_t al = MODE == kModeDV ? frag16_tr(s_y[1], k0, 4, 16 * yb) : frag16(s_y[1], 16 * yb + l16, k0);
+            // the state tile is [v][k] in LDS: dq and dk read it transposed
+            const bf16x8_t ah = MODE == kModeDV ? frag16(s_y[0], 16 * yb + l16, k0) : frag16_tr(s_y[0], k0, 4, 16 * yb);
+            const bf16x8_t al = MODE == kModeDV ? frag16(s_y[1], 16 * yb + l16, k0) : frag16_tr(s_y[1], k0, 4, 16 * yb);
             float4_t a_ = acc[4 * yc + yb];
             a_ = mma16b(ah, bh_, a_);
             a_ = mma16b(al, bh_, a_);
