@@ -111,6 +111,8 @@ CASES = [
     ("exp_bf16_d256x512_L1024_init", 1, 1, 1500, 256, 512, 1024, "bf16", "exp", True),
     ("sig_bf16_d256x256_L512_manyheads", 16, 4, 150, 256, 256, 512, "bf16", "sig", True),
     ("exp_bf16_d256x512_L256_manyheads", 8, 8, 140, 256, 512, 256, "bf16", "exp", False),
+    # two 256-row key tiles of the state-gradient recurrence per head
+    ("exp_bf16_d512x512_L128_init", 1, 2, 300, 512, 512, 128, "bf16", "exp", True),
 ]
 
 
@@ -133,8 +135,11 @@ def test_backward_bf16_dh_and_one_chunk(mt):
 ROW_TILE_CASES = [
     # name, B, NH, S, DK, DV, L, gate, init, dh_bf16: the instances of the
     # row-tile state-gradient kernel (64 key rows x 512 value columns, or
-    # 128 x 256; 16-row blocks for float32 dH, 32-row blocks for bf16 dH)
+    # 128 x 256; 16-row blocks for float32 dH, 32-row blocks for bf16 dH;
+    # 256 x 128 for float32 dH when DHV is 512 and DHQK a multiple of 256,
+    # which the shapes of the cases above reach)
     ("exp_d256x512_bf16dh_L128_ragged", 1, 2, 300, 256, 512, 128, "exp", True, True),
+    ("exp_d128x512_f32dh_L64_init", 1, 2, 200, 128, 512, 64, "exp", True, False),
     ("sig_d128x512_bf16dh_L64", 1, 2, 200, 128, 512, 64, "sig", False, True),
     ("sig_d256x256_f32dh_L64_init", 1, 1, 333, 256, 256, 64, "sig", True, False),
     ("sig_d128x256_bf16dh_L64_ragged", 2, 1, 150, 128, 256, 64, "sig", True, True),

@@ -671,10 +671,12 @@ __global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
 }
 
 // Row-tile form of the (G, N) recurrence for bf16 Q: a workgroup of eight
-// waves keeps a TK x DV tile of G (each wave a 64 x 64 block on the 32x32x16
+// waves keeps a TK x TV tile of G (each wave a 64 x 64 block on the 32x32x16
 // matrix cores) while it walks the chunks from last to first.  Each block of
-// 32 weighted dH rows is then staged once for all TK key rows, and each Q
-// block once for all value columns.  Per chunk c: G (packed hi + lo) and N
+// weighted dH rows is then staged once for all TK key rows, and each Q block
+// once for all TV value columns.  With TV < DHV (256 x 128 tiles for float32
+// dH) every workgroup reads only its own columns of dH, the largest input,
+// and the workgroups of a head share the Q rows instead.  Per chunk c: G (packed hi + lo) and N
 // leave for slot c, are decayed by the chunk's gate and gain the chunk's sums
 //   G += Q^T (w . dH),  N += Q^T wd,
 // w_t = s e^{b_t + M_c - m_t} / z_t and wd_t the same with delta_t (sig gate:
@@ -714,15 +716,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   __shared__ __align__(16) uint16_t s_wh[2 * WBUF];
   __shared__ __align__(16) uint16_t s_wl[2 * WBUF];
 
-  const int NTK = p.DK / TK;
+  const int NTK = p.DK / TK, NTV = p.DV / TV;
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
-  // the row tiles of one head (and segment) on one XCD: they read the same
+  // the tiles of one head (and segment) on one XCD: they read the same Q or
   // dH rows
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int kt = bid % NTK;
-  const int seg = (bid / NTK) % p.nseg;
-  const int bh = bid / (NTK * p.nseg);
+  const int vt = bid % NTV;
+  const int kt = (bid / NTV) % NTK;
+  const int seg = (bid / (NTV * NTK)) % p.nseg;
+  const int bh = bid / (NTV * NTK * p.nseg);
+  const bool n_out = vt == 0;  // N is the same for every column slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
   const int S = p.S, DK = p.DK, L = p.L, Nc = p.Nc;
@@ -731,8 +735,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   // kernels add what enters it from the later segments
   const int c_beg = p.nseg > 1 ? seg * p.cps : 0;
   const int c_end = p.nseg > 1 ? min(Nc, c_beg + p.cps) : Nc;
-  constexpr int DV = TV;
+  const int DV = p.DV;
   const int wr0 = (wave / NWC) * 64, wc0 = (wave % NWC) * 64;
+  const int vc0 = vt * TV;  // first value column of the slice
   const size_t gbase = (size_t)bh * S;
   const int krs = tid / TPR, kcs = (tid % TPR) * EPT;  // own time row (RW wave + lane / TPR) and columns
 
@@ -780,7 +785,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int f = i * 64 + lane, row = RW * wave + f / VSEG, seg = f % VSEG;
-      dr[s][i] = buf_load16_nt(rd, ((trow + row) * DV + seg * VE) * (DHB ? 2 : 4));
+      dr[s][i] = buf_load16_nt(rd, ((trow + row) * DV + vc0 + seg * VE) * (DHB ? 2 : 4));
     }
     const int t = trow + krs;
     const bool ok = t < S;
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int w = 0; w < NW; ++w) sacc += s_np[w][tid];
       nreg = nreg * n_dec + sacc;
-      if (dst) dst[kt * TK + tid] = nreg;
+      if (dst && n_out) dst[kt * TK + tid] = nreg;
     }
     n_pend = false;
   };
@@ -920,7 +925,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             split_bf16x2(acc[rb][cb][8 * half + 2 * q], acc[rb][cb][8 * half + 2 * q + 1], hw[q], lw[q]);
-          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (wc0 + 32 * cb) / 32;
+          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (vc0 + wc0 + 32 * cb) / 32;
           typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
           __builtin_nontemporal_store(u32x4_t{hw[0], hw[1], hw[2], hw[3]},
                                       reinterpret_cast<u32x4_t*>(P + pack_frag_offset(kk, nb, 0, DV) + lane * 8));
@@ -968,7 +973,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     __syncthreads();
   };
 
-  if (!SIG && tid < TK) p.dn_states[((size_t)bh * Nc + c_end - 1) * DK + kt * TK + tid] = 0.0f;
+  if (!SIG && n_out && tid < TK) p.dn_states[((size_t)bh * Nc + c_end - 1) * DK + kt * TK + tid] = 0.0f;
   load_blk(std::integral_constant<int, 0>{}, 0);
   if (NBLK > 1) load_blk(std::integral_constant<int, 1>{}, 1);
   stage_blk(std::integral_constant<int, 0>{}, 0);
@@ -993,7 +998,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (wc0 + 32 * cb) / 32;
+          const int kk = (kt * TK + wr0 + 32 * rb) / 16 + half, nb = (vc0 + wc0 + 32 * cb) / 32;
           float4* d = reinterpret_cast<float4*>(sc + ((size_t)(kk * (DV / 32) + nb) * 64 + lane) * 8);
           d[0] = make_float4(acc[rb][cb][8 * half], acc[rb][cb][8 * half + 1], acc[rb][cb][8 * half + 2],
                              acc[rb][cb][8 * half + 3]);
@@ -1015,7 +1020,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int krow = kt * TK + wr0 + 32 * rb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          const int vcol = wc0 + 32 * cb + l32;
+          const int vcol = vc0 + wc0 + 32 * cb + l32;
           p.dC0[(size_t)bh * DK * DV + (size_t)krow * DV + vcol] = acc[rb][cb][r];
         }
   }
@@ -1640,8 +1645,11 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gs((unsigned)p.BH, (unsigned)(p.DK / kT), (unsigned)(p.DV / kT));
   if (!rows_kernel || !p.seg_C || (!SIG && !p.seg_n) || p.cps < 1) p.nseg = 1;
-  const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK / (p.DV == 512 ? 64 : 128)) * (unsigned)p.nseg;
-  if (p.qkv_bf16 && p.DV == 512 && p.dh_bf16)
+  // tiles of 64 x 512, 256 x 128 (float32 dH) or 128 x 256: DHQK DHV / 32768 of them per head
+  const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK * p.DV / 32768) * (unsigned)p.nseg;
+  if (p.qkv_bf16 && p.DV == 512 && !p.dh_bf16 && p.DK % 256 == 0)
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<256, 128, 16, SIG, false>), dim3(rows), dim3(512), 0, s, p);
+  else if (p.qkv_bf16 && p.DV == 512 && p.dh_bf16)
     hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 32, SIG, true>), dim3(rows), dim3(512), 0, s, p);
   else if (p.qkv_bf16 && p.DV == 512)
     hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 16, SIG, false>), dim3(rows), dim3(512), 0, s, p);
@@ -1683,7 +1691,7 @@ int bw_dstate_segments(int BH, int DK, int DV, int Nc, bool bf16_inputs, int* cp
   // the row-tile recurrence: one workgroup per head and TK key rows; with
   // fewer than one per CU (256 CUs) the sequence is cut into segments
   const bool rows = bf16_inputs && (DV == 512 || (DV == 256 && DK % 128 == 0));
-  const long long base = (long long)BH * (DK / (DV == 512 ? 64 : 128));
+  const long long base = (long long)BH * DK * DV / 32768;  // tiles of 32768 entries
   if (!rows || base >= 256 || Nc < 2) {
     if (cps) *cps = Nc;
     return 1;
