@@ -1263,6 +1263,21 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
   const bool own_bf16 = MODE == kModeDQ ? hb : true;
   const int own_D = MODE == kModeDV ? DK : DV;
   constexpr bool own_split = MODE == kModeDQ;
+  // the partner tile's operand of the score contraction: V (dq), dH (dk), Q (dv)
+  const void* x_src = MODE == kModeDQ ? p.V : MODE == kModeDK ? p.dH : p.Q;
+  const bool x_bf16 = MODE == kModeDK ? hb : true;
+  constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
+  // dk: the scores against the diagonal partner (the own rows' tile as the
+  // partner) ride on the inter-chunk loop, which stages the own tile's
+  // contraction chunks anyway: each chunk's partner tile goes in at the
+  // loop's second state tile, and the score products join those of that
+  // step (output slices of at least two 64-column state tiles).  Not dv:
+  // held to three waves, the extra accumulators spill there.
+  constexpr bool FUSE = MODE == kModeDK && W >= 2 * kT;
+  bool fused = false;
+  float4_t scd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) scd[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // ---- inter-chunk term: out^T[y][w] = sum_x A[y][x] B[w][x], over (x chunk, y chunk) pairs
   {
@@ -1277,6 +1292,7 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
     }
     if (run) {
       constexpr int NYC = W / kT;
+      fused = FUSE;
       const int nxc = own_D / kT;
       // state tile of (x chunk, y chunk), held in LDS as [v][k] in every
       // mode: dq and dk (rows y = k) read it transposed, dv (rows y = v)
@@ -1298,7 +1314,7 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
         if constexpr (MODE == kModeDV) pre16(x, St, false, xi * kT, DV, y0 + yc * kT, kT);
         else pre16(x, St, false, y0 + yc * kT, DV, xi * kT, kT);
       };
-      float pw[16], py[16];
+      float pw[16], py[16], px[16];
       pre16(pw, own_src, own_bf16, rb + own0, own_D, 0, nown);
       pre_state(py, 0, 0);
       for (int xi = 0; xi < nxc; ++xi) {
@@ -1306,6 +1322,7 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
         for (int yc = 0; yc < NYC; ++yc) {
         __syncthreads();
         if (yc == 0) put_rows(s_w[0], own_split ? s_w[1] : nullptr, pw, own_split && !SIG ? g_own.invz : nullptr);
+        if (FUSE && yc == 1) put_rows(s_x[0], x_split ? s_x[1] : nullptr, px, x_split && !SIG ? g_own.invz : nullptr);
         if (Pk) put_packed_vk(s_y[0], s_y[1], py);
         else put_cols(s_y[0], s_y[1], py);
         __syncthreads();
@@ -1314,6 +1331,20 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
         } else if (xi + 1 < nxc) {
           pre16(pw, own_src, own_bf16, rb + own0, own_D, (xi + 1) * kT, nown);
           pre_state(py, xi + 1, 0);
+        }
+        if (FUSE && yc == 0) pre16(px, x_src, x_bf16, rb + own0, own_D, xi * kT, nown);
+        if (FUSE && yc == 1) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int k0 = 32 * j + 8 * g4;
+            const bf16x8_t bh_ = frag16(s_w[0], w, k0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float4_t a_ = mma16b(frag16(s_x[0], 16 * i + l16, k0), bh_, scd[i]);
+              if constexpr (x_split) a_ = mma16b(frag16(s_x[1], 16 * i + l16, k0), bh_, a_);
+              scd[i] = a_;
+            }
+          }
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1373,10 +1404,6 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
   // ---- intra-chunk term
   const int lo = MODE == kModeDQ ? 0 : ot;
   const int hi = MODE == kModeDQ ? ot : (Lc - 1) / kT;
-  // the partner tile's operand of the score contraction: V (dq), dH (dk), Q (dv)
-  const void* x_src = MODE == kModeDQ ? p.V : MODE == kModeDK ? p.dH : p.Q;
-  const bool x_bf16 = MODE == kModeDK ? hb : true;
-  constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
   // the partner tile's operand of the output product: K (dq), Q (dk), dH (dv)
   const void* y_src = MODE == kModeDQ ? p.K : MODE == kModeDK ? p.Q : p.dH;
   const bool y_bf16 = MODE == kModeDV ? hb : true;
@@ -1400,6 +1427,11 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
     } else {
     __syncthreads();
     load_rows<SIG>(g_oth, p, rb, x0, Lc);
+    if (fused && xt == ot) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = scd[i];
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int nc = own_D / kT;  // contraction chunks (the own tile's width)
@@ -1430,6 +1462,7 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
           sc[i] = a_;
         }
       }
+    }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
