@@ -1181,6 +1181,29 @@ __device__ __forceinline__ void pre_packed(float (&x)[16], const uint16_t* P, in
   }
 }
 
+// The same two halves for a source that is bf16 by construction and enters
+// unsplit and unscaled: the raw bf16 pairs stay packed in 8 registers (a
+// raw bf16 value is its own hi part, with a zero lo part).
+__device__ __forceinline__ void pre16(uint32_t (&x)[8], const void* src, bool, size_t row0, int D, int col0,
+                                      int nrows) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+  if (r < nrows) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (row0 + r) * (size_t)D + col0 + c);
+    a = q[0];
+    b = q[1];
+  }
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t*, const uint32_t (&x)[8], const float*) {
+  const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;
+  uint4* dh = reinterpret_cast<uint4*>(hi + r * kLd16 + c);
+  dh[0] = make_uint4(x[0], x[1], x[2], x[3]);
+  dh[1] = make_uint4(x[4], x[5], x[6], x[7]);
+}
+
 // The tile of pre_packed as [v][k] hi and lo planes: each fragment lane's
 // 8 values are two runs of 4 consecutive k at one v, one 8-byte store each.
 __device__ __forceinline__ void put_packed_vk(uint16_t* hi, uint16_t* lo, const float (&x)[16]) {
@@ -1267,6 +1290,11 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
   const void* x_src = MODE == kModeDQ ? p.V : MODE == kModeDK ? p.dH : p.Q;
   const bool x_bf16 = MODE == kModeDK ? hb : true;
   constexpr bool x_split = MODE == kModeDK, w_split = MODE == kModeDQ;
+  // staging registers: packed raw bf16 for the own tile (dk, dv: V, K), the
+  // partner of the scores (dv: Q) and the output side (dq, dk: K, Q)
+  typedef typename std::conditional<MODE != kModeDQ, uint32_t[8], float[16]>::type OwnBuf;
+  typedef typename std::conditional<MODE == kModeDV, uint32_t[8], float[16]>::type XBuf;
+  typedef typename std::conditional<MODE != kModeDV, uint32_t[8], float[16]>::type YBuf;
   // dk: the scores against the diagonal partner (the own rows' tile as the
   // partner) ride on the inter-chunk loop, which stages the own tile's
   // contraction chunks anyway: each chunk's partner tile goes in at the
@@ -1314,7 +1342,9 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
         if constexpr (MODE == kModeDV) pre16(x, St, false, xi * kT, DV, y0 + yc * kT, kT);
         else pre16(x, St, false, y0 + yc * kT, DV, xi * kT, kT);
       };
-      float pw[16], py[16], px[16];
+      OwnBuf pw;
+      XBuf px;
+      float py[16];
       pre16(pw, own_src, own_bf16, rb + own0, own_D, 0, nown);
       pre_state(py, 0, 0);
       for (int xi = 0; xi < nxc; ++xi) {
@@ -1435,7 +1465,8 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int nc = own_D / kT;  // contraction chunks (the own tile's width)
-    float px[16], pw[16];
+    XBuf px;
+    OwnBuf pw;
     pre16(px, x_src, x_bf16, rb + x0, own_D, 0, nx);
     pre16(pw, own_src, own_bf16, rb + own0, own_D, 0, nown);
     for (int ci = 0; ci < nc; ++ci) {
@@ -1488,7 +1519,7 @@ __device__ __forceinline__ void tiles16_body(const BwParams& p) {
     }
     }
     // first output-side tile (loads in flight during the split below)
-    float py[16];
+    YBuf py;
     pre16(py, y_src, y_bf16, rb + x0, y_D, y0, nx);
     // the weighted tile as bf16 hi + lo B fragments, one per 32 partner rows
     bf16x8_t bsh[2], bsl[2];
