@@ -238,6 +238,10 @@ def main(argv=None) -> int:
                          "64-value block)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (mlstm_chunkwise_bw) on the workload instead of the forward pass")
+    ap.add_argument("--saved-forward", action="store_true",
+                    help="with --backward (exp gate): time mlstm_chunkwise_bw_saved, which takes the forward's H "
+                         "and per-row m and normaliser (from one untimed mlstm_chunkwise_fw_rows call) instead "
+                         "of recomputing the intra-chunk pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times (the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -487,11 +491,24 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     sp = ctypes.c_void_p(stream.cuda_stream)
     grads = (P(dH), P(dQ), P(dK), P(dV), P(d_i), P(d_f), P(dC0), P(dn0), P(dm0))
 
+    saved = args.saved_forward and not sig
+    if saved:
+        # the forward's outputs, once, untimed (the automatic schedule: the
+        # fused walker where it covers the shape)
+        H, _, _, _, m_rows, den_rows = mt.mlstm_chunkwise_fw(
+            q, k, v, i_pre, f_pre, C0, n0, m0, chunk_size=w.chunk, gate=w.gate, precision=args.precision,
+            tile_lq=w.tile_lq or 0, tile_lkv=w.tile_lkv or 0, return_final_state=False, return_rows=True)
+        torch.cuda.synchronize()
+
     def whole():
-        st = L.mlstm_chunkwise_bw(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
-                                  *grads, P(ws), ws_bytes, sp)
+        if saved:
+            st = L.mlstm_chunkwise_bw_saved(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
+                                            P(m0), P(H), P(m_rows), P(den_rows), *grads, P(ws), ws_bytes, sp)
+        else:
+            st = L.mlstm_chunkwise_bw(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
+                                      P(m0), *grads, P(ws), ws_bytes, sp)
         if st:
-            raise mt.MlstmError(st, "mlstm_chunkwise_bw")
+            raise mt.MlstmError(st, "mlstm_chunkwise_bw_saved" if saved else "mlstm_chunkwise_bw")
 
     for _ in range(args.warmup):
         whole()
@@ -529,7 +546,8 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     peak = PEAK_BF16_TFLOPS if bf16_path else PEAK_FP32_TFLOPS
     grads_dtype = "bf16x2-mfma/f32-acc" if bf16_path else "f32-mfma/f32-acc"
     out = {
-        "metric": f"mLSTM chunkwise backward tokens/s, {w.gate} gate ({w.name})",
+        "metric": f"mLSTM chunkwise backward tokens/s, {w.gate} gate ({w.name})"
+                  + (", from the forward's saved H and rows" if saved else ""),
         "value": w.B * w.S / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -544,7 +562,10 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "config": {"workload": f"backward_{w.name}", "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK,
                    "DHV": w.DHV, "chunk": w.chunk, "backward_chunk": bw_chunk, "gate": w.gate,
                    "qkv_dtype": w.qkv_dtype, "dH": "float32", "precision": args.precision},
+        # saved: the stage split is that of mlstm_chunkwise_bw (the saved call
+        # skips the intra-chunk part of the recompute)
         "stages_ms": {"recompute": t_rec, "grads": t_grads},
+        "saved_forward": saved,
         "grads_TFLOPs": ach,
         "roofline": {"kernel": "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
                      "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,

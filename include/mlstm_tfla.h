@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 10
+#define MLSTM_ABI_VERSION 11
 
 typedef enum {
   MLSTM_OK = 0,
@@ -257,6 +257,28 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* mlstm_chunkwise_fw that also writes the per-row quantities of the
+ * normalisation ("xLSTM: the NX-AI repository behind the extended LSTM
+ * architecture", section "Exponential gating, matrix memory, and why the
+ * kernels decide everything": the max-state m and the normaliser; the
+ * "flash-xlstm-exp 0.1.0" page, section "Usage", lists per-row n and m among
+ * the parallel stage's outputs), for mlstm_chunkwise_bw_saved:
+ *   m_rows   (B, NH, S) float32, may be NULL: the max-state m_t
+ *   den_rows (B, NH, S) float32, may be NULL: the stabilised normaliser
+ *            s n_t . q_t before the max with e^{-m_t}
+ * Exp gate only (with the sig gate both must be NULL: MLSTM_E_UNSUPPORTED).
+ * Every schedule writes them, the fused walker included; other arguments,
+ * checks and errors as mlstm_chunkwise_fw. */
+int mlstm_chunkwise_fw_rows(const mlstm_fw_desc_t* desc,
+                            const void* Q, const void* K, const void* V,
+                            const float* i_pre, const float* f_pre,
+                            const float* C0, const float* n0, const float* m0,
+                            void* H,
+                            float* C_out, float* n_out, float* m_out,
+                            float* m_rows, float* den_rows,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Size of the static workspace of mlstm_chunkwise_fw_noalloc (64 MiB). */
 #define MLSTM_NOALLOC_WORKSPACE_BYTES (64u << 20)
 
@@ -424,8 +446,9 @@ size_t mlstm_bw_workspace_bytes(const mlstm_fw_desc_t* desc);
  * min(max(chunk_size, 64), Lmax) rows, Lmax = 128 when B * NH * DHQK / 64 is
  * at least 256 (the chip's CU count) and 256 otherwise; the results agree
  * with those of any other cut to rounding.  (At 65536 tokens, 8 heads and
- * chunk 1024 the cut at 256 takes 13.0 ms against 16.9 ms; at the 7B-shaped
- * 64 heads the cut at 128 takes 6.9 ms against 7.4 ms at 256.)  The gradient kernels accumulate in float32: with bf16
+ * chunk 1024 the cut at 256 is 6 % faster than at 128 and 10 % faster than
+ * at 512; at the 7B-shaped 64 heads the cut at 128 is 7 % faster than at
+ * 512.)  The gradient kernels accumulate in float32: with bf16
  * inputs on bf16 matrix cores (Q, K, V raw, every computed operand as a bf16
  * hi + lo pair), with float32 inputs on fp32 matrix cores.  No gradient
  * flows in through the final state.  For the sig gate n0,
@@ -441,6 +464,32 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc,
                        float* dC0, float* dn0, float* dm0,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* mlstm_chunkwise_bw from the forward's own outputs: the gradient's row
+ * terms (1/z and delta) come from H, m_rows and den_rows as
+ * mlstm_chunkwise_fw_rows wrote them for the same descriptor and inputs,
+ * so of the forward only the chunk states are recomputed (the intra-chunk
+ * recompute is skipped).  Exp gate: desc->h_dtype must be MLSTM_F32
+ * (MLSTM_E_UNSUPPORTED otherwise; H is read as float32, dH is float32 too);
+ *   H        (B, NH, S, DHV) float32, 16-byte aligned, required
+ *   m_rows   (B, NH, S) float32, required
+ *   den_rows (B, NH, S) float32, required
+ * Sig gate: the gradient has no normaliser terms, the three must be NULL
+ * (MLSTM_E_UNSUPPORTED otherwise) and the call is mlstm_chunkwise_bw.  The
+ * gradient agrees with mlstm_chunkwise_bw's to rounding (the row terms are
+ * formed from the stored H instead of the recomputed one).  Other
+ * arguments, workspace size, checks and errors as mlstm_chunkwise_bw. */
+int mlstm_chunkwise_bw_saved(const mlstm_fw_desc_t* desc,
+                             const void* Q, const void* K, const void* V,
+                             const float* i_pre, const float* f_pre,
+                             const float* C0, const float* n0, const float* m0,
+                             const float* H, const float* m_rows, const float* den_rows,
+                             const void* dH,
+                             float* dQ, float* dK, float* dV,
+                             float* d_i, float* d_f,
+                             float* dC0, float* dn0, float* dm0,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* The two stages of mlstm_chunkwise_bw, for callers that time or schedule
  * them apart.  Same arguments as mlstm_chunkwise_bw; the same descriptor,

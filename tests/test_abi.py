@@ -66,7 +66,7 @@ def test_binding_signatures_match_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert mt.abi_version() == 10
+    assert mt.abi_version() == 11
     assert mt.status_str(0) == "ok"
     for code in range(1, 10):
         assert mt.status_str(code) not in ("ok", "unknown status")
@@ -301,6 +301,47 @@ def test_backward_refuses_before_launch():
     assert gr(d, dQ=4096 * 9 + 4) == 8
     assert gr(d, ws=None) == 6
     assert gr(ds, n0=None, dn0=None) == 5                 # sig gate: no dm0
+
+
+def test_saved_forward_entry_points_refuse_before_launch():
+    """mlstm_chunkwise_fw_rows and mlstm_chunkwise_bw_saved check their extra
+    arguments (the forward's H and per-row m and normaliser) before any
+    launch, besides those of mlstm_chunkwise_fw and mlstm_chunkwise_bw."""
+    lib = mt.lib()
+    d = _desc(S=300, DHQK=128, DHV=128, chunk_size=64)
+    need = lib.mlstm_bw_workspace_bytes(ctypes.byref(d))
+
+    def sb(desc, ws_bytes=need, **ptrs):
+        names = ["q", "k", "v", "i", "f", "C0", "n0", "m0", "H", "m_rows", "den_rows", "dH", "dQ", "dK", "dV",
+                 "d_i", "d_f", "dC0", "dn0", "dm0", "ws"]
+        vals = [ptrs.get(n, 4096 * (j + 1)) for j, n in enumerate(names)]
+        return lib.mlstm_chunkwise_bw_saved(ctypes.byref(desc), *vals, ws_bytes, None)
+
+    assert sb(d, H=None) == 1                             # exp gate: H, m_rows, den_rows required
+    assert sb(d, m_rows=None) == 1
+    assert sb(d, den_rows=None) == 1
+    assert sb(d, H=4096 * 9 + 4) == 8                     # H in 16-byte pieces
+    assert sb(d, den_rows=4096 * 11 + 2) == 8
+    assert sb(d, dQ=None) == 1                            # the checks of mlstm_chunkwise_bw
+    assert sb(d, ws_bytes=need - 1) == 6
+    assert sb(_desc(S=300, DHQK=128, DHV=128, chunk_size=64, h_dtype=mt.MLSTM_BF16)) == 5  # H is float32
+    ds = _desc(S=300, DHQK=128, DHV=128, chunk_size=64, gate="sig")
+    assert sb(ds, n0=None, m0=None, dn0=None, dm0=None) == 5            # sig gate: no row terms
+    assert sb(ds, n0=None, m0=None, dn0=None, dm0=None, H=None, m_rows=None) == 5
+
+    wsb = mt.workspace_bytes(d)
+
+    def fr(desc, **ptrs):
+        names = ["q", "k", "v", "i", "f", "C0", "n0", "m0", "H", "C_out", "n_out", "m_out", "m_rows", "den_rows"]
+        vals = [ptrs.get(n, 4096 * (j + 1)) for j, n in enumerate(names)]
+        return lib.mlstm_chunkwise_fw_rows(ctypes.byref(desc), *vals, ptrs.get("ws", 1 << 20),
+                                           ptrs.get("ws_bytes", wsb), None)
+
+    assert fr(d, q=None) == 1
+    assert fr(d, m_rows=4096 * 13 + 2) == 8
+    assert fr(d, ws_bytes=wsb - 1) == 6
+    assert fr(ds, n0=None, m0=None, n_out=None, m_out=None) == 5       # sig gate: no rows
+    assert fr(ds, n0=None, m0=None, n_out=None, m_out=None, m_rows=None) == 5
 
 
 def test_backward_workspace_formula():

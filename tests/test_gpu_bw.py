@@ -161,6 +161,40 @@ def test_backward_row_tile_state_kernel(mt, c):
     _compare(name, g, _ref(x, gate), "bf16", keys)
 
 
+SAVED_CASES = [
+    # name, B, NH, S, DK, DV, L, kind, init: the forward that keeps H and the
+    # per-row m and normaliser runs the fused walker (bf16, DHQK 256, chunk
+    # <= 512), the wide two-stage kernels, or the generic ones
+    ("walker_d256x512_L256_init", 1, 2, 520, 256, 512, 256, "bf16", True),
+    ("wide_d128x256_L128_ragged", 1, 2, 300, 128, 256, 128, "bf16", False),
+    ("generic_f32_d64x192_L64_init", 2, 1, 200, 64, 192, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("c", SAVED_CASES, ids=[c[0] for c in SAVED_CASES])
+def test_backward_from_saved_forward(mt, c):
+    """mlstm_chunkwise_bw_saved: the row terms come from the forward's own
+    H, m_rows and den_rows (mlstm_chunkwise_fw_rows), only the chunk states
+    are recomputed; against the gradient oracle, and to rounding the same
+    as the backward that recomputes everything."""
+    name, B, NH, S, DK, DV, L, kind, init = c
+    x = _draw(400 + SAVED_CASES.index(c), B, NH, S, DK, DV, kind, "exp", init)
+    qd = torch.bfloat16 if kind == "bf16" else torch.float32
+    args = [_dev(x["q"], qd), _dev(x["k"], qd), _dev(x["v"], qd), _dev(x["i"]), _dev(x["f"])]
+    init_args = [_dev(x.get("C0")), _dev(x.get("n0")), _dev(x.get("m0"))]
+    H, _, _, _, m_rows, den_rows = mt.mlstm_chunkwise_fw(*args, *init_args, chunk_size=L, return_rows=True)
+    out = mt.mlstm_chunkwise_bw(*args, _dev(x["dH"]), *init_args, chunk_size=L, state_grads=True,
+                                saved=(H, m_rows, den_rows))
+    torch.cuda.synchronize()
+    g = {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
+    keys = KEYS + ("dC0", "dn0", "dm0")
+    _compare(name + " saved", g, _ref(x, "exp"), kind, keys)
+    full = _gpu(mt, x, kind, "exp", L)
+    for n in keys:
+        scale = max(1.0, np.abs(full[n]).max())
+        assert np.abs(g[n] - full[n]).max() / scale <= TOL[kind], n
+
+
 def test_backward_without_state_grads_and_empty_sequence(mt):
     x = _draw(22, 1, 1, 100, 64, 64, "f32", "exp", True)
     g = _gpu(mt, x, "f32", "exp", 64, state_grads=False)

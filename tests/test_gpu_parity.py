@@ -523,6 +523,29 @@ def test_hintra_rows_match_recurrent_rows(mt, wide):
     assert np.all(derr <= bden), f"den_rows: max err/bound {(derr / bden).max():.3g}"
 
 
+@pytest.mark.parametrize("schedule", ["fused", "two_stage"])
+def test_forward_rows_match_recurrent_rows(mt, schedule):
+    """mlstm_chunkwise_fw_rows: the per-row max-state m and normaliser that
+    the fused walker and the two-stage kernels write for a backward pass,
+    against the recurrent oracle's (same bounds as the intra-chunk stage's
+    rows above)."""
+    w = _small_workload(dict(B=1, NH=1, S=300, DHQK=256, DHV=256, chunk=128))
+    x = make_inputs(w)
+    q, k, v = (_to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
+    H, _, _, _, m_rows, den_rows = mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, chunk_size=128,
+                                                         schedule=schedule, return_rows=True)
+    torch.cuda.synchronize()
+    args = [x[nm][0, 0].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
+    Hr, _, _, _, rm, rden = recurrent_fw(*args, return_rows=True)
+    np.testing.assert_allclose(H.cpu().numpy()[0, 0], Hr, atol=2e-2, rtol=0)
+    np.testing.assert_allclose(m_rows.cpu().numpy()[0, 0], rm, atol=1e-5, rtol=0)
+    _, bden = accumulation_bound(*[x[nm][0, 0] for nm in ("q", "k", "v", "i", "f")], chunk_size=128, H_ref=Hr,
+                                 m_rows=rm, den_rows=rden)
+    derr = np.abs(den_rows.cpu().numpy()[0, 0] - rden)
+    assert np.all(derr <= bden), f"den_rows: max err/bound {(derr / bden).max():.3g}"
+
+
 def test_empty_sequence_copies_initial_state(mt):
     w = _small_workload(dict(B=1, NH=2, S=0, DHQK=64, DHV=64, chunk=64, init_state=True))
     x = make_inputs(w)

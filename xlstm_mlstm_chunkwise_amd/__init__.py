@@ -64,6 +64,8 @@ _SYMBOLS = {
     "mlstm_fw_kernel_family": (ctypes.c_int, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_fw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 12
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_chunkwise_fw_rows": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 14
+                                + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mlstm_chunkwise_fw_noalloc": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 13),
     "mlstm_fw_states": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 8
                         + [ctypes.c_size_t] + [ctypes.c_void_p] * 4),
@@ -78,6 +80,8 @@ _SYMBOLS = {
     "mlstm_bw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwDesc)]),
     "mlstm_chunkwise_bw": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 18
                            + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mlstm_chunkwise_bw_saved": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 21
+                                 + [ctypes.c_size_t, ctypes.c_void_p]),
     "mlstm_bw_recompute": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 10
                            + [ctypes.c_size_t, ctypes.c_void_p]),
     "mlstm_bw_grads": (ctypes.c_int, [ctypes.POINTER(FwDesc)] + [ctypes.c_void_p] * 17
@@ -213,7 +217,7 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
                        qk_scale: Optional[float] = None, eps: float = 0.0,
                        tile_lq: int = 0, tile_lkv: int = 0, schedule: str = "auto", workspace=None,
                        return_final_state: bool = True, out=None, block_chunks: int = 0,
-                       state_codes: str = "split"):
+                       state_codes: str = "split", return_rows: bool = False):
     """Chunkwise mLSTM forward pass on the GPU.
 
     q, k: (B, NH, S, DHQK); v: (B, NH, S, DHV), bfloat16 or float32;
@@ -225,6 +229,9 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
     mlstm_schedule_t); block_chunks: chunks per block of the blocked
     schedule (0: the library's choice); state_codes: "split" or "int16", how
     the two stages hand the chunk states over (see mlstm_state_codes_t).
+    return_rows (exp gate): also return the per-row max-state m and
+    normaliser, (B, NH, S) float32 each, as (H, C, n, m, m_rows, den_rows)
+    (mlstm_chunkwise_fw_rows), for mlstm_chunkwise_bw(saved=...).
     """
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
@@ -252,6 +259,18 @@ def mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chun
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {need}")
+    if return_rows:
+        if sig:
+            raise ValueError("return_rows: the sig gate has no per-row normaliser")
+        m_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
+        den_rows = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
+        st = lib().mlstm_chunkwise_fw_rows(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre),
+            _ptr(C0), _ptr(n0), _ptr(m0), _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out), _ptr(m_rows),
+            _ptr(den_rows), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+        if st:
+            raise MlstmError(st, "mlstm_chunkwise_fw_rows")
+        return H, C_out, n_out, m_out, m_rows, den_rows
     st = lib().mlstm_chunkwise_fw(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre),
         _ptr(C0), _ptr(n0), _ptr(m0), _ptr(H), _ptr(C_out), _ptr(n_out), _ptr(m_out),
@@ -459,13 +478,15 @@ def bw_workspace_bytes(desc: FwDesc) -> int:
 def mlstm_chunkwise_bw(q, k, v, i_pre, f_pre, dH, C0=None, n0=None, m0=None, *, chunk_size: int,
                        gate: str = "exp", precision: str = "split", qk_scale: Optional[float] = None,
                        eps: float = 0.0, tile_lq: int = 0, tile_lkv: int = 0, state_grads: bool = False,
-                       workspace=None):
+                       workspace=None, saved=None):
     """Backward pass on the GPU: the gradients of sum(dH * H) for the forward
     pass mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, C0, n0, m0, ...) with the
     same keyword arguments.  dH has H's shape; its dtype (bfloat16 or
     float32) is the h_dtype of the descriptor.  Returns a dict with dQ, dK,
     dV, d_i, d_f (float32) and, with state_grads, dC0 and for the exp gate
-    dn0 and dm0."""
+    dn0 and dm0.  saved (exp gate, float32 dH): the forward's (H, m_rows,
+    den_rows) from mlstm_chunkwise_fw(return_rows=True), so that only the
+    chunk states are recomputed (mlstm_chunkwise_bw_saved)."""
     torch = _torch()
     B, NH, S, DK, DV = _check_inputs(q, k, v, i_pre, f_pre)
     if dH.dtype not in (torch.float32, torch.bfloat16):
@@ -494,6 +515,21 @@ def mlstm_chunkwise_bw(q, k, v, i_pre, f_pre, dH, C0=None, n0=None, m0=None, *, 
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < need:
         raise ValueError(f"workspace holds {ws_bytes} bytes, need {need}")
+    if saved is not None:
+        if gate == "sig":
+            raise ValueError("saved: the sig gate has no per-row normaliser")
+        H, m_rows, den_rows = saved
+        _check(H, "H", (B, NH, S, DV), torch.float32)
+        _check(m_rows, "m_rows", (B, NH, S), torch.float32)
+        _check(den_rows, "den_rows", (B, NH, S), torch.float32)
+        st = lib().mlstm_chunkwise_bw_saved(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0),
+            _ptr(m0), _ptr(H), _ptr(m_rows), _ptr(den_rows), _ptr(dH), _ptr(out["dQ"]), _ptr(out["dK"]),
+            _ptr(out["dV"]), _ptr(out["d_i"]), _ptr(out["d_f"]), _ptr(out.get("dC0")), _ptr(out.get("dn0")),
+            _ptr(out.get("dm0")), _ptr(workspace), ws_bytes, _stream())
+        if st:
+            raise MlstmError(st, "mlstm_chunkwise_bw_saved")
+        return out
     st = lib().mlstm_chunkwise_bw(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(C0), _ptr(n0), _ptr(m0),
         _ptr(dH), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["d_i"]), _ptr(out["d_f"]),
@@ -597,7 +633,10 @@ def mlstm_chunkwise(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_s
     """H of the forward pass as a torch autograd function: the forward runs
     mlstm_chunkwise_fw, the backward mlstm_chunkwise_bw (gradients for q, k,
     v, i_pre, f_pre and, when given, C0, n0, m0).  H is float32.  The final
-    state is not returned here: no gradient enters through it."""
+    state is not returned here: no gradient enters through it.  With the exp
+    gate the forward also keeps the per-row m and normaliser, and the
+    backward takes them with H instead of recomputing the intra-chunk pass
+    (mlstm_chunkwise_bw_saved)."""
     torch = _torch()
     kw = dict(chunk_size=chunk_size, gate=gate, precision=precision, qk_scale=qk_scale, eps=eps,
               tile_lq=tile_lq, tile_lkv=tile_lkv)
@@ -605,17 +644,24 @@ def mlstm_chunkwise(q, k, v, i_pre, f_pre, C0=None, n0=None, m0=None, *, chunk_s
     class _Fn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q_, k_, v_, i_, f_, C0_, n0_, m0_):
-            H = mlstm_chunkwise_fw(q_, k_, v_, i_, f_, C0_, n0_, m0_, schedule=schedule, return_final_state=False,
-                                   **kw)[0]
-            ctx.save_for_backward(q_, k_, v_, i_, f_, C0_, n0_, m0_)
+            if gate == "sig":
+                H = mlstm_chunkwise_fw(q_, k_, v_, i_, f_, C0_, n0_, m0_, schedule=schedule,
+                                       return_final_state=False, **kw)[0]
+                ctx.save_for_backward(q_, k_, v_, i_, f_, C0_, n0_, m0_)
+            else:
+                H, _, _, _, m_rows, den_rows = mlstm_chunkwise_fw(q_, k_, v_, i_, f_, C0_, n0_, m0_,
+                                                                  schedule=schedule, return_final_state=False,
+                                                                  return_rows=True, **kw)
+                ctx.save_for_backward(q_, k_, v_, i_, f_, C0_, n0_, m0_, H, m_rows, den_rows)
             return H
 
         @staticmethod
         def backward(ctx, dH):
-            q_, k_, v_, i_, f_, C0_, n0_, m0_ = ctx.saved_tensors
+            q_, k_, v_, i_, f_, C0_, n0_, m0_ = ctx.saved_tensors[:8]
+            saved = tuple(ctx.saved_tensors[8:]) or None
             want_state = any(ctx.needs_input_grad[5:])
             g = mlstm_chunkwise_bw(q_, k_, v_, i_, f_, dH.contiguous().float(), C0_, n0_, m0_,
-                                   state_grads=want_state, **kw)
+                                   state_grads=want_state, saved=saved, **kw)
             cast = lambda t, like: None if t is None else t.to(like.dtype)
             return (cast(g["dQ"], q_), cast(g["dK"], k_), cast(g["dV"], v_), g["d_i"], g["d_f"],
                     g.get("dC0") if C0_ is not None else None, g.get("dn0") if n0_ is not None else None,

@@ -249,7 +249,7 @@ hipError_t run_gates(const mlstm_fw_desc_t* d, const float* i_pre, const float* 
 
 int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
               const float* f_pre, const float* C0, const float* n0, const float* m0, const WsPtrs& ws, void* H,
-              float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+              float* C_out, float* n_out, float* m_out, float* m_rows, float* den_rows, hipStream_t stream) {
   (void)ws;
   mlstm::WalkParams p;
   p.Q = Q;
@@ -264,6 +264,8 @@ int run_fused(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void
   p.C_out = C_out;
   p.n_out = n_out;
   p.m_out = m_out;
+  p.m_rows = m_rows;
+  p.den_rows = den_rows;
   p.scale = resolve_scale(d);
   p.eps = d->eps;
   p.BH = d->B * d->NH;
@@ -379,7 +381,7 @@ int run_hintra(const mlstm_fw_desc_t* d, const void* Q, const void* K, const voi
 // still in the Infinity Cache.  The last block ends in the final state.
 int run_blocked(const mlstm_fw_desc_t* d, const void* Q, const void* K, const void* V, const float* i_pre,
                 const float* f_pre, const float* C0, const float* n0, const float* m0, const WsPtrs& ws, void* H,
-                float* C_out, float* n_out, float* m_out, hipStream_t stream) {
+                float* C_out, float* n_out, float* m_out, float* m_rows, float* den_rows, hipStream_t stream) {
   const int Nc = (d->S + d->chunk_size - 1) / d->chunk_size;
   const int k = block_chunks(d);
   const bool sig = d->gate == MLSTM_GATE_SIG;
@@ -430,8 +432,8 @@ int run_blocked(const mlstm_fw_desc_t* d, const void* Q, const void* K, const vo
     h.n_states = ws.n;
     h.m_states = ws.m;
     h.H = H;
-    h.m_rows = nullptr;
-    h.den_rows = nullptr;
+    h.m_rows = m_rows;
+    h.den_rows = den_rows;
     h.gb2 = ws.gb2;
     h.gu2 = ws.gu2;
     h.gpm2 = ws.gpm2;
@@ -666,14 +668,15 @@ int check_fw_args(const mlstm_fw_desc_t* desc, const void* Q, const void* K, con
 // The forward pass on a checked workspace.
 int run_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
            const float* f_pre, const float* C0, const float* n0, const float* m0, void* H, float* C_out,
-           float* n_out, float* m_out, void* workspace, hipStream_t s) {
+           float* n_out, float* m_out, float* m_rows, float* den_rows, void* workspace, hipStream_t s) {
   const WsPtrs ws = ws_ptrs(desc, workspace);
-  if (use_fused(desc)) return run_fused(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
+  if (use_fused(desc))
+    return run_fused(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, m_rows, den_rows, s);
   if (desc->schedule == MLSTM_SCHED_BLOCKED)
-    return run_blocked(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, s);
+    return run_blocked(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, ws, H, C_out, n_out, m_out, m_rows, den_rows, s);
   const int st = run_states(desc, K, V, i_pre, f_pre, C0, n0, m0, ws, C_out, n_out, m_out, s);
   if (st != MLSTM_OK) return st;
-  return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, nullptr, nullptr, s);
+  return run_hintra(desc, Q, K, V, i_pre, f_pre, ws, H, m_rows, den_rows, s);
 }
 
 // ---- workspace of the allocation-free forward pass: a static device array
@@ -711,7 +714,20 @@ int mlstm_chunkwise_fw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   int st = check_fw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out);
   if (st != MLSTM_OK) return st;
   if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
-  return run_fw(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, workspace,
+  return run_fw(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, nullptr, nullptr, workspace,
+                static_cast<hipStream_t>(stream));
+}
+
+int mlstm_chunkwise_fw_rows(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                            const float* i_pre, const float* f_pre, const float* C0, const float* n0,
+                            const float* m0, void* H, float* C_out, float* n_out, float* m_out, float* m_rows,
+                            float* den_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out);
+  if (st != MLSTM_OK) return st;
+  if (desc->gate == MLSTM_GATE_SIG && (m_rows || den_rows)) return MLSTM_E_UNSUPPORTED;
+  if ((st = check_f32_ptrs({m_rows, den_rows})) != MLSTM_OK) return st;
+  if ((st = check_workspace(desc, workspace, workspace_bytes)) != MLSTM_OK) return st;
+  return run_fw(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, m_rows, den_rows, workspace,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -729,7 +745,7 @@ int mlstm_chunkwise_fw_noalloc(const mlstm_fw_desc_t* desc, const void* Q, const
   if (need > (size_t)MLSTM_NOALLOC_WORKSPACE_BYTES) return MLSTM_E_WORKSPACE;
   void* ws = nullptr;
   if (need > 0 && (st = scratch_address(&ws)) != MLSTM_OK) return st;
-  return run_fw(&d, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, ws,
+  return run_fw(&d, Q, K, V, i_pre, f_pre, C0, n0, m0, H, C_out, n_out, m_out, nullptr, nullptr, ws,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -857,9 +873,15 @@ float* bw_states_f32(const mlstm_fw_desc_t* d2, void* workspace, float* region) 
   return ws_ptrs(d2, workspace).C;
 }
 
-int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
-                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
-                       const void* dH, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// saved: the caller holds the forward's H and per-row m and normaliser, so
+// only the chunk states are recomputed.
+int bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                 const float* f_pre, const float* C0, const float* n0, const float* m0, const void* dH,
+                 void* workspace, size_t workspace_bytes, void* stream, bool saved) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH)) return MLSTM_E_NULLPTR;
@@ -889,7 +911,7 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   const bool convert = d2.precision == MLSTM_PREC_F64;
   if (st == MLSTM_OK)
     st = unpack_states(&d2, fw, convert ? at(l.Cst) : nullptr, ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
-  if (st == MLSTM_OK && ex) {
+  if (st == MLSTM_OK && ex && !saved) {
     if (bw_delta_in_recompute(&d2))
       st = run_hintra(&d2, Q, K, V, i_pre, f_pre, fw, nullptr, at(l.mrows), at(l.den), s, dH,
                       desc->h_dtype == MLSTM_BF16, at(l.ginvz), at(l.gdelta));
@@ -899,10 +921,12 @@ int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   return st;
 }
 
-int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
-                   const float* f_pre, const float* C0, const float* n0, const void* dH, float* dQ, float* dK,
-                   float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// H_saved, m_saved, den_saved: the forward's H and per-row m and normaliser
+// (saved recompute), or null (the recompute's own).
+int bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+             const float* f_pre, const float* C0, const float* n0, const void* dH, float* dQ, float* dK, float* dV,
+             float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, void* workspace, size_t workspace_bytes,
+             void* stream, const float* H_saved, const float* m_saved, const float* den_saved) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
@@ -925,11 +949,12 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   p.i_pre = i_pre;
   p.f_pre = f_pre;
   p.dH = dH;
-  p.delta_ready = bw_delta_in_recompute(&d2);
+  const bool saved = ex && H_saved;
+  p.delta_ready = !saved && bw_delta_in_recompute(&d2);
   p.G_packed = nullptr;  // set by the launcher where the row-tile recurrence runs
-  p.H = ex && !p.delta_ready ? at(l.H) : nullptr;
-  p.m_rows = ex ? at(l.mrows) : nullptr;
-  p.den_rows = ex ? at(l.den) : nullptr;
+  p.H = saved ? H_saved : (ex && !p.delta_ready ? at(l.H) : nullptr);
+  p.m_rows = saved ? m_saved : (ex ? at(l.mrows) : nullptr);
+  p.den_rows = saved ? den_saved : (ex ? at(l.den) : nullptr);
   p.C_states = bw_states_f32(&d2, workspace, at(l.Cst));
   p.C_packed = packed_layout(&d2) && ex ? reinterpret_cast<const uint16_t*>(ws_ptrs(&d2, workspace).C) : nullptr;
   p.n_states = ex ? at(l.nst) : nullptr;
@@ -973,11 +998,11 @@ int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, co
   return e == hipSuccess ? MLSTM_OK : MLSTM_E_HIP;
 }
 
-int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
-                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
-                       const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
-                       float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
-  // all checks of both stages before anything is launched
+// The checks of mlstm_chunkwise_bw, before anything is launched.
+int check_bw_args(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                  const float* f_pre, const float* C0, const float* n0, const float* m0, const void* dH, float* dQ,
+                  float* dK, float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0,
+                  void* workspace, size_t workspace_bytes) {
   int st = validate_desc(desc);
   if (st != MLSTM_OK) return st;
   if (desc->S > 0 && (!Q || !K || !V || !i_pre || !f_pre || !dH || !dQ || !dK || !dV || !d_i || !d_f))
@@ -989,6 +1014,58 @@ int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K
   if ((st = check_f32_ptrs({i_pre, f_pre, C0, n0, m0, d_i, d_f, dC0, dn0, dm0})) != MLSTM_OK) return st;
   const mlstm_fw_desc_t d2 = bw_fw_desc(desc);
   if (!workspace || workspace_bytes < bw_layout(&d2).total || !aligned(workspace, 256)) return MLSTM_E_WORKSPACE;
+  return MLSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       const void* dH, void* workspace, size_t workspace_bytes, void* stream) {
+  return bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, workspace, workspace_bytes, stream, false);
+}
+
+int mlstm_bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V, const float* i_pre,
+                   const float* f_pre, const float* C0, const float* n0, const void* dH, float* dQ, float* dK,
+                   float* dV, float* d_i, float* d_f, float* dC0, float* dn0, float* dm0, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bw_grads(desc, Q, K, V, i_pre, f_pre, C0, n0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0, workspace,
+                  workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+int mlstm_chunkwise_bw_saved(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                             const float* i_pre, const float* f_pre, const float* C0, const float* n0,
+                             const float* m0, const float* H, const float* m_rows, const float* den_rows,
+                             const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
+                             float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_bw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0,
+                         workspace, workspace_bytes);
+  if (st != MLSTM_OK) return st;
+  const bool ex = desc->gate == MLSTM_GATE_EXP;
+  if (ex) {
+    if (desc->h_dtype != MLSTM_F32) return MLSTM_E_UNSUPPORTED;  // H is read as float32
+    if (desc->S > 0 && (!H || !m_rows || !den_rows)) return MLSTM_E_NULLPTR;
+    if (H && !aligned(H, 16)) return MLSTM_E_ALIGN;
+    if ((st = check_f32_ptrs({m_rows, den_rows})) != MLSTM_OK) return st;
+  } else if (H || m_rows || den_rows) {
+    return MLSTM_E_UNSUPPORTED;  // the sig gate has no normaliser terms
+  }
+  st = bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, workspace, workspace_bytes, stream, true);
+  if (st != MLSTM_OK) return st;
+  return bw_grads(desc, Q, K, V, i_pre, f_pre, C0, n0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0, workspace,
+                  workspace_bytes, stream, ex ? H : nullptr, m_rows, den_rows);
+}
+
+int mlstm_chunkwise_bw(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const void* V,
+                       const float* i_pre, const float* f_pre, const float* C0, const float* n0, const float* m0,
+                       const void* dH, float* dQ, float* dK, float* dV, float* d_i, float* d_f, float* dC0,
+                       float* dn0, float* dm0, void* workspace, size_t workspace_bytes, void* stream) {
+  // all checks of both stages before anything is launched
+  int st = check_bw_args(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0,
+                         workspace, workspace_bytes);
+  if (st != MLSTM_OK) return st;
   st = mlstm_bw_recompute(desc, Q, K, V, i_pre, f_pre, C0, n0, m0, dH, workspace, workspace_bytes, stream);
   if (st != MLSTM_OK) return st;
   return mlstm_bw_grads(desc, Q, K, V, i_pre, f_pre, C0, n0, dH, dQ, dK, dV, d_i, d_f, dC0, dn0, dm0, workspace,

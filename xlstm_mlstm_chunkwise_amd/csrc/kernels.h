@@ -106,6 +106,8 @@ struct WalkParams {
   float* C_out;  // may be null
   float* n_out;
   float* m_out;
+  float* m_rows = nullptr;    // (BH, S) per-row max-state m, may be null (exp gate)
+  float* den_rows = nullptr;  // (BH, S) per-row normaliser before the max with e^{-m}, may be null
   float scale;
   float eps;
   int BH, S, DK, DV, L, Nc;

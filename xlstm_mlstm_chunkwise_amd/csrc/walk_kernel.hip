@@ -518,6 +518,13 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
           dpart += __shfl_xor(dpart, 32, 64);
           const float d = dint * wrq + dpart;
           inv = 1.0f / (fmaxf(fabsf(d), exp2f(-m2q)) + p.eps);
+          // per-row m and normaliser for a backward pass, from the first
+          // column slice (lanes 0..15 hold queries 0..15 of the wave)
+          const int tau = row0 + 16 * wa + l16;
+          if (v0 == 0 && g4 == 0 && tau < Lc) {
+            if (p.m_rows) p.m_rows[gbase + t0 + tau] = m2q * kLn2;
+            if (p.den_rows) p.den_rows[gbase + t0 + tau] = d;
+          }
         }
         float iv[4], wv[4];
 #pragma unroll
