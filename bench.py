@@ -520,26 +520,30 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for it in range(args.steps):
-        ev[it][0].record(stream)
-        st = L.mlstm_bw_recompute(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
-                                  P(dH), P(ws), ws_bytes, sp)
-        ev[it][1].record(stream)
-        st2 = L.mlstm_bw_grads(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
-                               *grads, P(ws), ws_bytes, sp)
-        ev[it][2].record(stream)
-        if st or st2:
-            raise mt.MlstmError(st or st2, "backward stage call")
-    torch.cuda.synchronize()
-    t_rec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    t_rec = t_grads = None
+    if not saved:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for it in range(args.steps):
+            ev[it][0].record(stream)
+            st = L.mlstm_bw_recompute(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0), P(m0),
+                                      P(dH), P(ws), ws_bytes, sp)
+            ev[it][1].record(stream)
+            st2 = L.mlstm_bw_grads(ctypes.byref(desc), P(q), P(k), P(v), P(i_pre), P(f_pre), P(C0), P(n0),
+                                   *grads, P(ws), ws_bytes, sp)
+            ev[it][2].record(stream)
+            if st or st2:
+                raise mt.MlstmError(st or st2, "backward stage call")
+        torch.cuda.synchronize()
+        t_rec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        t_grads = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     # the backward cuts the sequence into chunks of min(max(chunk, 64), Lmax)
     # rows, Lmax = 128 when B NH DHQK / 64 >= 256, else 256
     # (mlstm_chunkwise_bw): its algorithmic FLOPs are those of that cut
     bw_chunk = min(max(w.chunk, 64), 128 if w.B * w.NH * (w.DHQK // 64) >= 256 else 256)
     flops = mt.bw_flops(w.B, w.NH, w.S, w.DHQK, w.DHV, bw_chunk)
-    ach = flops / (t_grads * 1e-3) / 1e12
+    # the gradient stage alone; from saved forward outputs there is no stage
+    # call of its own, so the whole call is priced
+    ach = flops / ((ms if saved else t_grads) * 1e-3) / 1e12
     # bf16 inputs: bf16 matrix cores (computed operands as hi + lo pairs);
     # float32 inputs: fp32 matrix cores.  Each is priced at its own peak.
     bf16_path = w.qkv_dtype == "bf16"
@@ -562,12 +566,12 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "config": {"workload": f"backward_{w.name}", "B": w.B, "NH": w.NH, "S": w.S, "DHQK": w.DHQK,
                    "DHV": w.DHV, "chunk": w.chunk, "backward_chunk": bw_chunk, "gate": w.gate,
                    "qkv_dtype": w.qkv_dtype, "dH": "float32", "precision": args.precision},
-        # saved: the stage split is that of mlstm_chunkwise_bw (the saved call
-        # skips the intra-chunk part of the recompute)
-        "stages_ms": {"recompute": t_rec, "grads": t_grads},
+        # the stage calls of mlstm_chunkwise_bw (the saved call has none)
+        "stages_ms": None if saved else {"recompute": t_rec, "grads": t_grads},
         "saved_forward": saved,
         "grads_TFLOPs": ach,
-        "roofline": {"kernel": "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
+        "roofline": {"kernel": "whole backward from saved forward outputs (mlstm_chunkwise_bw_saved)" if saved
+                     else "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
                      "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
                      "algorithmic_flops": flops, "traffic_source": "not profiled"},
     }
