@@ -684,9 +684,10 @@ __global__ __launch_bounds__(256) void bw_dstate16_kernel(const BwParams p) {
 // w . dH is split into bf16 hi + lo.  Software pipeline over TB-row blocks
 // of the flattened (chunk, block) sequence, as in the forward state kernel:
 // two LDS stages and one barrier per block, global loads two blocks ahead.
-// A block of float32 dH is 16 rows, so that both register sets of its loads
-// fit beside the accumulators: a spilled register would be reloaded through
-// the same in-order counter as the loads in flight, and wait for them.
+// A block of float32 dH is 16 rows on the 512-column tiles, so that both
+// register sets of its loads fit beside the accumulators (a spilled
+// register would be reloaded through the same in-order counter as the loads
+// in flight, and wait for them); on the 128-column tiles 32 rows fit.
 // Staging: the lanes of wave x are split evenly over its time rows
 // (TB / 8 rows each; a row's owner lanes hold its Q pieces and gate terms),
 // and the same wave stages those rows of dH, taking each row's weight from
@@ -702,13 +703,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   constexpr int EPT = TB * TK / NT;            // Q elements per thread and block
   constexpr int TPR = TK / EPT;                // staging lanes per time row
   static_assert((TB == 16 || TB == 32) && RW * TPR == 64, "staging split");
-  static_assert(EPT == 2 || EPT == 4 || EPT == 8, "Q pieces of 4, 8 or 16 bytes");
+  static_assert(EPT == 2 || EPT == 4 || EPT == 8 || EPT == 16, "Q pieces of 4, 8, 16 or 32 bytes");
   constexpr int VE = DHB ? 8 : 4;       // dH elements per 16-byte load
   constexpr int VSEG = TV / VE;         // 16-byte pieces per dH row
   constexpr int VPT = RW * VSEG / 64;   // pieces per lane and block
   static_assert(VPT * 64 == RW * VSEG && VPT >= 1, "dH staging split");
   constexpr int QBUF = TB * LDK, WBUF = TB * LDV;
-  typedef typename std::conditional<EPT == 2, uint32_t, typename std::conditional<EPT == 4, uint2, uint4>::type>::type
+  struct alignas(16) Uint4x2 {
+    uint4 a, b;
+  };
+  typedef typename std::conditional<
+      EPT == 2, uint32_t,
+      typename std::conditional<EPT == 4, uint2, typename std::conditional<EPT == 8, uint4, Uint4x2>::type>::type>::type
       QVec;
 
   __shared__ float s_np[NW][TK];
@@ -779,8 +785,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     } else if constexpr (EPT == 4) {
       const v2i32_t q2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qo, 0, 0);
       qr[s] = make_uint2((uint32_t)q2.x, (uint32_t)q2.y);
-    } else {
+    } else if constexpr (EPT == 8) {
       qr[s] = buf_load16(rq, qo);
+    } else {
+      qr[s].a = buf_load16(rq, qo);
+      qr[s].b = buf_load16(rq, qo + 16);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -864,7 +873,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       }
     }
     // Q as raw bf16; N partial sums
-    *reinterpret_cast<QVec*>(s_q + s * QBUF + krs * LDK + kcs) = qr[s];
+    if constexpr (EPT == 16) {
+      *reinterpret_cast<uint4*>(s_q + s * QBUF + krs * LDK + kcs) = qr[s].a;
+      *reinterpret_cast<uint4*>(s_q + s * QBUF + krs * LDK + kcs + 8) = qr[s].b;
+    } else {
+      *reinterpret_cast<QVec*>(s_q + s * QBUF + krs * LDK + kcs) = qr[s];
+    }
     if constexpr (!SIG) {
       uint32_t qw[EPT / 2];
       __builtin_memcpy(qw, &qr[s], sizeof(qw));
@@ -1712,7 +1726,7 @@ hipError_t launch_all(const BwParams& p0, hipStream_t s) {
   // tiles of 64 x 512, 256 x 128 (float32 dH) or 128 x 256: DHQK DHV / 32768 of them per head
   const unsigned rows = (unsigned)p.BH * (unsigned)(p.DK * p.DV / 32768) * (unsigned)p.nseg;
   if (p.qkv_bf16 && p.DV == 512 && !p.dh_bf16 && p.DK % 256 == 0)
-    hipLaunchKernelGGL((bw_dstate_rows_kernel<256, 128, 16, SIG, false>), dim3(rows), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((bw_dstate_rows_kernel<256, 128, 32, SIG, false>), dim3(rows), dim3(512), 0, s, p);
   else if (p.qkv_bf16 && p.DV == 512 && p.dh_bf16)
     hipLaunchKernelGGL((bw_dstate_rows_kernel<64, 512, 32, SIG, true>), dim3(rows), dim3(512), 0, s, p);
   else if (p.qkv_bf16 && p.DV == 512)
