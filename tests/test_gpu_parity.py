@@ -523,18 +523,20 @@ def test_hintra_rows_match_recurrent_rows(mt, wide):
     assert np.all(derr <= bden), f"den_rows: max err/bound {(derr / bden).max():.3g}"
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage"])
-def test_forward_rows_match_recurrent_rows(mt, schedule):
+@pytest.mark.parametrize("schedule,codes", [("fused", "split"), ("two_stage", "split"), ("blocked", "split"),
+                                          ("two_stage", "int16")])
+def test_forward_rows_match_recurrent_rows(mt, schedule, codes):
     """mlstm_chunkwise_fw_rows: the per-row max-state m and normaliser that
-    the fused walker and the two-stage kernels write for a backward pass,
-    against the recurrent oracle's (same bounds as the intra-chunk stage's
-    rows above)."""
+    the fused walker, the two-stage kernels (chunk states as pairs or int16
+    codes) and the blocked schedule write for a backward pass, against the
+    recurrent oracle's (same bounds as the intra-chunk stage's rows above;
+    n and m stay float32 under int16 codes)."""
     w = _small_workload(dict(B=1, NH=1, S=300, DHQK=256, DHV=256, chunk=128))
     x = make_inputs(w)
     q, k, v = (_to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
     i_pre, f_pre = _to_dev(x["i"], torch.float32), _to_dev(x["f"], torch.float32)
     H, _, _, _, m_rows, den_rows = mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, chunk_size=128,
-                                                         schedule=schedule, return_rows=True)
+                                                         schedule=schedule, state_codes=codes, return_rows=True)
     torch.cuda.synchronize()
     args = [x[nm][0, 0].astype(np.float64) for nm in ("q", "k", "v", "i", "f")]
     Hr, _, _, _, rm, rden = recurrent_fw(*args, return_rows=True)
