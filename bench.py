@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "hintra_int16": ("hintra2_kernel.hip", "device_common.h"),
     "states_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
     "hintra_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
+    "grads": ("bw_kernels.hip", "kernels.h", "tile_order.h", "device_common.h"),
 }
 
 
@@ -548,6 +549,11 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
     # float32 inputs: fp32 matrix cores.  Each is priced at its own peak.
     bf16_path = w.qkv_dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16_path else PEAK_FP32_TFLOPS
+    # HBM bytes of the gradient stage per call, from the committed counter
+    # summary while it matches the current sources (the saved call has no
+    # stage of its own to price)
+    traffic, traffic_src = (None, "no stage of its own") if saved else recorded_traffic(
+        f"backward_{w.name}", "grads", None, fname="traffic_backward_7b.md")
     grads_dtype = "bf16x2-mfma/f32-acc" if bf16_path else "f32-mfma/f32-acc"
     out = {
         "metric": f"mLSTM chunkwise backward tokens/s, {w.gate} gate ({w.name})"
@@ -572,8 +578,8 @@ def bench_backward(args, w, mt, torch, np, inputs) -> int:
         "grads_TFLOPs": ach,
         "roofline": {"kernel": "whole backward from saved forward outputs (mlstm_chunkwise_bw_saved)" if saved
                      else "gradient stage (mlstm_bw_grads)", "bound": "mfma", "achieved": ach,
-                     "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
-                     "algorithmic_flops": flops, "traffic_source": "not profiled"},
+                     "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
+                     "algorithmic_flops": flops, "traffic_source": traffic_src},
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU gradient oracle", file=sys.stderr, flush=True)
