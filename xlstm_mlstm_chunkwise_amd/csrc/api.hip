@@ -898,16 +898,11 @@ int bw_recompute(const mlstm_fw_desc_t* desc, const void* Q, const void* K, cons
   const bool ex = desc->gate == MLSTM_GATE_EXP;
   auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const WsPtrs fw = ws_ptrs(&d2, workspace);
-  // Chunk states for the gradient stage.  Exp gate on the wide kernels: the
-  // packed states feed the intra-chunk recompute, and the dq pass reads them
-  // packed too.  Sig gate on the wide kernels: no intra-chunk kernel runs,
-  // so the states kernel writes them as float32 directly instead.  Float64:
-  // narrowed to float32.  The generic kernels' float32 states are read in
-  // place (bw_states_f32).
-  const bool packed = packed_layout(&d2);
-  const bool direct = packed && !ex;
-  st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s, direct ? at(l.Cst) : nullptr,
-                  true);
+  // Chunk states for the gradient stage.  On the wide kernels the packed
+  // states feed the intra-chunk recompute (exp gate), and the dq pass reads
+  // them packed too (both gates).  Float64: narrowed to float32.  The
+  // generic kernels' float32 states are read in place (bw_states_f32).
+  st = run_states(&d2, K, V, i_pre, f_pre, C0, n0, m0, fw, nullptr, nullptr, nullptr, s, nullptr, true);
   const bool convert = d2.precision == MLSTM_PREC_F64;
   if (st == MLSTM_OK)
     st = unpack_states(&d2, fw, convert ? at(l.Cst) : nullptr, ex ? at(l.nst) : nullptr, ex ? at(l.mst) : nullptr, s);
@@ -956,7 +951,7 @@ int bw_grads(const mlstm_fw_desc_t* desc, const void* Q, const void* K, const vo
   p.m_rows = saved ? m_saved : (ex ? at(l.mrows) : nullptr);
   p.den_rows = saved ? den_saved : (ex ? at(l.den) : nullptr);
   p.C_states = bw_states_f32(&d2, workspace, at(l.Cst));
-  p.C_packed = packed_layout(&d2) && ex ? reinterpret_cast<const uint16_t*>(ws_ptrs(&d2, workspace).C) : nullptr;
+  p.C_packed = packed_layout(&d2) ? reinterpret_cast<const uint16_t*>(ws_ptrs(&d2, workspace).C) : nullptr;
   p.n_states = ex ? at(l.nst) : nullptr;
   p.m_states = ex ? at(l.mst) : nullptr;
   p.C0 = C0;
