@@ -541,7 +541,15 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
       constexpr int E = decltype(esize)::value;
       const __amdgpu_buffer_rsrc_t rh = make_rsrc(static_cast<const char*>(p.H) + ((size_t)bh * S + t0) * DV * E,
                                                   (uint32_t)(Lc * DV * E));
-      const int hvoff = ((row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32) * E;
+      // float32: one value per lane and store.  bf16: lane pairs (l32 even,
+      // odd) swap values so that each lane holds two adjacent columns of one
+      // row (the even lane rows q = 0, 2, the odd lane rows 1, 3), rounded
+      // together and stored as one word (measured 3 % faster than one 2-byte
+      // store per value; the same exchange with 8-byte float32 stores was 6 %
+      // slower)
+      const bool odd = (l32 & 1) != 0;
+      const int hvoff = E == 2 ? ((row0 + wr0 + 4 * h2 + (odd ? 1 : 0)) * DV + v0 + wc0 + (l32 & ~1)) * E
+                               : ((row0 + wr0 + 4 * h2) * DV + v0 + wc0 + l32) * E;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -550,18 +558,29 @@ __global__ __launch_bounds__(512) void hintra_wide_kernel(const HintraParams p) 
           float4 inv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
           if constexpr (!SIG) inv = *reinterpret_cast<const float4*>(s_den2 + wr0 + rowl + 4 * h2);
           const float invq[4] = {inv.x, inv.y, inv.z, inv.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int hro = hvoff + (rowl + q) * DV * E;
+          // non-temporal (aux 2): H is not read again here, so it should not
+          // push the state and K/V lines of sibling row tiles out of L2
+          if constexpr (E == 2) {
 #pragma unroll
             for (int cb = 0; cb < W::CB; ++cb) {
-              // non-temporal (aux 2): H is not read again here, so it should
-              // not push the state and K/V lines of sibling row tiles out of L2
-              const float hv = acc[rb][cb][4 * r4 + q] * invq[q];
-              if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hro + 32 * cb * E, 0, 2);
-              else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hro + 32 * cb * E, 0, 2);
+              float hv[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) hv[q] = acc[rb][cb][4 * r4 + q] * invq[q];
+#pragma unroll
+              for (int qp = 0; qp < 2; ++qp) {
+                const float2 pr = pair_rows_to_cols(hv[2 * qp], hv[2 * qp + 1], odd);
+                __builtin_amdgcn_raw_buffer_store_b32(round_bf16x2(pr.x, pr.y), rh,
+                                                      hvoff + ((rowl + 2 * qp) * DV + 32 * cb) * E, 0, 2);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int hro = hvoff + (rowl + q) * DV * E;
+#pragma unroll
+              for (int cb = 0; cb < W::CB; ++cb)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][cb][4 * r4 + q] * invq[q]), rh,
+                                                      hro + 32 * cb * E, 0, 2);
             }
           }
         }

@@ -539,27 +539,40 @@ __global__ __launch_bounds__(512) void walk_kernel(const WalkParams p) {
           const __amdgpu_buffer_rsrc_t rh =
               make_rsrc(static_cast<const char*>(p.H) + ((gbase + t0 + row0) * DV + v0) * E,
                         (uint32_t)(((Lc - row0 - 1) * DV + TVS) * E));
-          const int hvoff = ((16 * wa + 4 * g4) * DV + l16) * E;
           float4 xr[NCB];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
             xr[cb] = *reinterpret_cast<const float4*>(s_xt + (16 * cb + l16) * LDX + 16 * wa + 4 * g4);
           __builtin_amdgcn_sched_barrier(0);
+          // Plain stores: a store instruction covers 64-byte (float32) or
+          // 32-byte (bf16) pieces of H rows, which L2 merges into whole lines
+          // (with the streaming hint each piece went out on its own and the
+          // written bytes grew by half).  float32: one value per lane and
+          // store.  bf16: lane pairs (l16 even, odd) swap values so that the
+          // even lane holds rows 0 and 2 of its quad and the odd lane rows 1
+          // and 3, each as two adjacent columns, rounded together and stored
+          // as one word (measured 4-5 % faster than one 2-byte store per value;
+          // the same exchange with 8-byte float32 stores was 3-4 % slower).
+          const bool odd = (l16 & 1) != 0;
+          const int hvoff = E == 2 ? ((16 * wa + 4 * g4 + (odd ? 1 : 0)) * DV + (l16 & ~1)) * E
+                                   : ((16 * wa + 4 * g4) * DV + l16) * E;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             const float xv[4] = {xr[cb].x, xr[cb].y, xr[cb].z, xr[cb].w};
+            float hv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float hv = (hacc[cb][r] + wv[r] * xv[r]) * iv[r];
-              const int hro = hvoff + (r * DV + 16 * cb) * E;
-              // plain stores: a store instruction covers 64-byte pieces of
-              // H rows, which L2 merges into whole lines (with the streaming
-              // hint each piece went out on its own and the written bytes
-              // grew by half)
-              if constexpr (E == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(hv), rh, hro, 0, 0);
-              else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), rh, hro, 0, 0);
+            for (int r = 0; r < 4; ++r) hv[r] = (hacc[cb][r] + wv[r] * xv[r]) * iv[r];
+            if constexpr (E == 2) {
+#pragma unroll
+              for (int rp = 0; rp < 2; ++rp) {
+                const float2 pr = pair_rows_to_cols(hv[2 * rp], hv[2 * rp + 1], odd);
+                __builtin_amdgcn_raw_buffer_store_b32(round_bf16x2(pr.x, pr.y), rh,
+                                                      hvoff + (2 * rp * DV + 16 * cb) * E, 0, 0);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv[r]), rh, hvoff + (r * DV + 16 * cb) * E, 0, 0);
             }
           }
         };
