@@ -37,14 +37,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 # file (kernel and launch), the gate-terms kernel it reads from, and the
 # shared device helpers.
 KERNEL_SOURCES = {
-    "walk": ("walk_kernel.hip", "gates_kernel.hip", "device_common.h"),
+    "walk": ("walk_kernel.hip", "gates_kernel.hip", "device_common.h", "pair_store.h"),
     "states": ("states2_kernel.hip", "gates_kernel.hip", "device_common.h"),
-    "hintra": ("hintra2_kernel.hip", "device_common.h"),
-    "blocked": ("states2_kernel.hip", "hintra2_kernel.hip", "gates_kernel.hip", "device_common.h"),
+    "hintra": ("hintra2_kernel.hip", "device_common.h", "pair_store.h"),
+    "blocked": ("states2_kernel.hip", "hintra2_kernel.hip", "gates_kernel.hip", "device_common.h", "pair_store.h"),
     "step": ("step_kernel.hip", "device_common.h"),
     "step_q8": ("step_kernel.hip", "device_common.h"),
     "states_int16": ("states2_kernel.hip", "gates_kernel.hip", "device_common.h"),
-    "hintra_int16": ("hintra2_kernel.hip", "device_common.h"),
+    "hintra_int16": ("hintra2_kernel.hip", "device_common.h", "pair_store.h"),
     "states_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
     "hintra_f64": ("f64_mfma_kernels.hip", "f64_common.h", "device_common.h"),
     "grads": ("bw_kernels.hip", "kernels.h", "tile_order.h", "device_common.h"),

@@ -13,6 +13,9 @@ The kernels covered are the ones that address their rows through buffer
 resources: the wide states and intra-chunk kernels (both tile heights), the
 fused walker, and the backward's state-gradient kernel (Q and dH); the
 generic and float64 kernels, which check every row explicitly, run too.
+bf16 H, which the walker and the wide intra-chunk kernel store as pairs of
+adjacent columns after a lane exchange, is checked the same way and value for
+value against the float32 H of the same call, rounded to bf16.
 """
 import numpy as np
 import pytest
@@ -114,6 +117,61 @@ def test_forward_ragged_tail_reads_nothing_past_the_rows(mt, name, over, schedul
             if w.gate == "exp":
                 assert np.isfinite(m.cpu().numpy()[b, h]) and abs(m.cpu().numpy()[b, h] - r[3]) <= 1e-3
                 assert np.abs(n.cpu().numpy()[b, h] - r[2]).max() / max(1.0, np.abs(r[2]).max()) <= 1e-3
+
+
+BF16_H = [
+    # name, workload overrides, schedule
+    ("fused_exp_bf16h", dict(B=1, NH=2, S=300, DHQK=256, DHV=512, chunk=256), "fused"),
+    ("fused_sig_bf16h_init", dict(gate="sig", B=1, NH=2, S=333, DHQK=256, DHV=256, chunk=128, init_state=True),
+     "fused"),
+    ("wide_exp_tq64_bf16h", dict(B=1, NH=2, S=300, DHQK=256, DHV=512, chunk=256), "two_stage"),
+    ("wide_exp_tq128_bf16h", dict(B=1, NH=2, S=700, DHQK=256, DHV=512, chunk=256, tile_lq=128, tile_lkv=128),
+     "two_stage"),
+    ("generic_bf16h", dict(B=1, NH=2, S=200, DHQK=64, DHV=128, chunk=64), "two_stage"),
+]
+
+
+@pytest.mark.parametrize("name,over,schedule", BF16_H, ids=[c[0] for c in BF16_H])
+def test_bf16_h_is_the_rounded_float32_h_and_stays_in_the_rows(mt, name, over, schedule):
+    """bf16 H (lane pairs swap values and store two adjacent columns of a
+    row as one word in the walker and the wide intra-chunk kernel) is, value
+    for value, the round-to-nearest-even bf16 of the float32 H of the same
+    call, and no store lands past the last row."""
+    w = _workload(**over)
+    x = make_inputs(w)
+    DK, DV = w.DHQK, w.DHV
+    q, k = _nan_tail(x["q"], torch.bfloat16, DK), _nan_tail(x["k"], torch.bfloat16, DK)
+    v = _nan_tail(x["v"], torch.bfloat16, DV)
+    i_pre, f_pre = _nan_tail(x["i"], torch.float32, 1), _nan_tail(x["f"], torch.float32, 1)
+    st = {}
+    if w.init_state:
+        st["C0"] = _nan_tail(x["C0"], torch.float32, DV)
+        if w.gate == "exp":
+            st["n0"] = _nan_tail(x["n0"], torch.float32, 1)
+            st["m0"] = _nan_tail(x["m0"], torch.float32, 1)
+    shape = (w.B, w.NH, w.S, DV)
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        flat, H = _sentinel_out(shape, dt, DV)
+        print(f"\n[{name}] schedule {schedule}, H {dt}", flush=True)
+        mt.mlstm_chunkwise_fw(q, k, v, i_pre, f_pre, st.get("C0"), st.get("n0"), st.get("m0"),
+                              chunk_size=w.chunk, gate=w.gate, tile_lq=w.tile_lq, tile_lkv=w.tile_lkv,
+                              schedule=schedule, h_dtype=dt, out=H)
+        torch.cuda.synchronize()
+        tail = flat[H.numel():].cpu()
+        sent = torch.full_like(tail, SENTINEL)
+        assert torch.equal(tail, sent), f"{name}: {dt} H stores past the last row"
+        outs[dt] = H.cpu()
+    want = outs[torch.float32].to(torch.bfloat16).view(torch.int16)
+    got = outs[torch.bfloat16].view(torch.int16)
+    bad = int((want != got).sum())
+    assert bad == 0, f"{name}: {bad} bf16 H values differ from the rounded float32 H"
+    r = recurrent_fw(*[x[nm][0, 0].astype(np.float64) for nm in ("q", "k", "v", "i", "f")],
+                     x["C0"][0, 0] if w.init_state else None,
+                     x["n0"][0, 0] if (w.init_state and w.gate == "exp") else None,
+                     x["m0"][0, 0] if (w.init_state and w.gate == "exp") else None, gate=w.gate)
+    err = np.abs(outs[torch.float32].numpy()[0, 0].astype(np.float64) - r[0]).max()
+    assert err <= 2e-2, f"{name}: float32 H max|dH| {err:.3g}"
 
 
 BACKWARD = [

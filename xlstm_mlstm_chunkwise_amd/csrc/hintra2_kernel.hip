@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "pair_store.h"
 
 namespace mlstm {
 namespace {

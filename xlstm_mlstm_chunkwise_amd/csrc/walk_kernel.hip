@@ -69,6 +69,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "pair_store.h"
 
 namespace mlstm {
 namespace {
